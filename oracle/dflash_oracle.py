@@ -1,0 +1,299 @@
+"""Plain fp64 CPU oracle for the DFlash KV-injection attention layer.
+
+TEST INFRASTRUCTURE.  Only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import this module.  The GPU library never calls it, and it
+imports nothing from the GPU package: the two share no code.
+
+Sources (cited by page title and section):
+  [W]  "DFlash KV Injection Walkthrough": Step 2 (projection and norm),
+       Step 4.1-4.5 (Q projection, dual-stream K/V, RoPE alignment, attention,
+       output projection), Step 6-7 (acceptance, state update).
+  [S]  "DFlash源码导读二 Qwen3DFlashAttention注意力实现全解析": section 1 (QKV
+       projection, QK-RMSNorm, head_dim, GQA groups), 2 (dual-stream K/V),
+       3 (RoPE window), 4 (KV cache update and crop), 5 (sliding window), and the
+       non-causal key design.
+  [T]  "KV Cache + Speculative Decoding 面试 Cheat Sheet": section 4.2 and 6.3
+       (GQA: each K/V head serves a contiguous group of query heads).
+
+Everything is float64.  Inputs arrive as float32 arrays holding exact bf16 or
+fp32 values and are upcast without any rounding afterwards.  Library routines
+used as steps: numpy matmul, sqrt, exp, cos, sin.
+
+Readings taken where the pages leave a step open (the numbers refer to the list
+of readings kept with the design notes):
+  R2  W_fc is stored [d, k*d] (output x input); a context row is raw_row . W_fc^T.
+  R3  RMSNorm(x) = x / sqrt(mean(x^2) + eps) * gamma over the normalised axis
+      (d for hidden_norm, d_h for the per-head Q/K norms, gains shared by heads).
+  R4  no biases in q/k/v/o projections.
+  R5  RoPE pairs element i with i + d_h/2 (rotate_half), w_i = theta^(-2i/d_h).
+  R6  the RoPE window of a round covers positions [L, L + n + B); cached keys keep
+      the rotation they got when appended.
+  R7  block rows are appended too, then the caller crops to L + n.
+  R10 query head h reads K/V head h // (n_h / n_kv).
+  R12 sliding layers: key j is visible to query i iff pos_i - pos_j < window
+      (no upper bound: still non-causal inside the block).
+  R14 layer stacks chain H_{l+1} = H_l + out_l (the decoder MLP is not on the
+      pages).  parity unpinned: this chaining is a builder choice.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+def f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# norms and the context projection
+# --------------------------------------------------------------------------
+
+def rms_norm(x, gamma, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis (reading R3).  [W] Step 2 names hidden_norm as
+    an RMSNorm over d; [S] section 1 names the per-head q_norm/k_norm over d_h."""
+    x = f64(x)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * f64(gamma)
+
+
+def ctx_project(x_raw, w_fc, gamma_h, eps: float) -> np.ndarray:
+    """Context C = hidden_norm(fc(raw)), [W] Step 2.
+
+    x_raw [T, k*d]: each row is the k target-layer vectors of one position,
+    concatenated in layer order ([W] Step 1).  w_fc is stored [d, k*d]
+    (reading R2: only raw_row . W_fc^T is dimensionally consistent with the
+    stated 1536 x 512 shape).  fc has no bias."""
+    u = f64(x_raw) @ f64(w_fc).T
+    return rms_norm(u, gamma_h, eps)
+
+
+# --------------------------------------------------------------------------
+# rotary position embedding
+# --------------------------------------------------------------------------
+
+def rope_inv_freq(d_h: int, theta: float) -> np.ndarray:
+    """w_i = theta^(-2i/d_h), i < d_h/2 (reading R5)."""
+    i = np.arange(d_h // 2, dtype=np.float64)
+    return np.power(float(theta), -2.0 * i / d_h)
+
+
+def rope(x, positions, theta: float) -> np.ndarray:
+    """Rotate rows of x [..., P, d_h] by their positions [P], [W] Step 4.3.
+
+    rotate_half pairing: the first half and the second half of a head vector
+    form the pairs, x' = x*cos + rotate_half(x)*sin with rotate_half(x) =
+    [-x_hi, x_lo] and cos/sin repeated over both halves."""
+    x = f64(x)
+    d_h = x.shape[-1]
+    half = d_h // 2
+    ang = f64(positions)[:, None] * rope_inv_freq(d_h, theta)[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    lo, hi = x[..., :half], x[..., half:]
+    return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
+
+
+# --------------------------------------------------------------------------
+# the layer
+# --------------------------------------------------------------------------
+
+@dataclass
+class LayerParams:
+    """One KV-injection attention layer.  w_qkv rows are W_Q | W_K | W_V, each
+    block stored output x input; w_o is [d, n_h*d_h]."""
+    w_qkv: np.ndarray
+    w_o: np.ndarray
+    gamma_q: np.ndarray
+    gamma_k: np.ndarray
+    n_h: int
+    n_kv: int
+    d_h: int
+    eps: float = 1e-6
+    theta: float = 1e6
+    window: int = 0
+
+    def split(self):
+        qd, kvd = self.n_h * self.d_h, self.n_kv * self.d_h
+        w = f64(self.w_qkv)
+        return w[:qd], w[qd:qd + kvd], w[qd + kvd:qd + 2 * kvd]
+
+
+def project_q(p: LayerParams, H) -> np.ndarray:
+    """Q = QNorm(H W_Q), viewed per head: [n_h, B, d_h] (not yet rotated).
+    [W] Step 4.1: queries come from the block stream only."""
+    wq, _, _ = p.split()
+    B = H.shape[0]
+    q = (f64(H) @ wq.T).reshape(B, p.n_h, p.d_h)
+    q = rms_norm(q, p.gamma_q, p.eps)
+    return q.transpose(1, 0, 2)
+
+
+def project_kv(p: LayerParams, C, H):
+    """Dual-stream K/V, [W] Step 4.2 and [S] section 2: the same k_proj and
+    v_proj act on the context rows C and on the block rows H; the results are
+    concatenated along the sequence, context first.  K gets the per-head norm,
+    V does not.  Returns k [n_kv, n+B, d_h] (normed, not rotated), v alike."""
+    _, wk, wv = p.split()
+    S = np.concatenate([f64(C), f64(H)], axis=0)
+    rows = S.shape[0]
+    k = rms_norm((S @ wk.T).reshape(rows, p.n_kv, p.d_h), p.gamma_k, p.eps)
+    v = (S @ wv.T).reshape(rows, p.n_kv, p.d_h)
+    return k.transpose(1, 0, 2), v.transpose(1, 0, 2)
+
+
+def visible(qpos, kpos, window: int) -> np.ndarray:
+    """[B, L_tot] bool: which keys each query may attend to.  Full layers see
+    every key ([W] Step 4.4: no causal mask; [S] key design: is_causal False and
+    no attention mask).  Sliding layers (reading R12) see keys with
+    pos_q - pos_k < window."""
+    qpos, kpos = np.asarray(qpos), np.asarray(kpos)
+    if window <= 0:
+        return np.ones((qpos.size, kpos.size), dtype=bool)
+    return (qpos[:, None] - kpos[None, :]) < window
+
+
+def gqa_attention(q, K, V, qpos, kpos, window: int = 0):
+    """Softmax attention of rotated queries q [n_h, B, d_h] over the cache
+    K, V [n_kv, L_tot, d_h], [W] Step 4.4: A = softmax(q'.k'^T / sqrt(d_h)),
+    out = A V, scale d_h^-0.5.  Query head h reads K/V head h // (n_h/n_kv)
+    ([S] section 1, [T] 6.3 repeat_interleave).
+    Returns o [n_h, B, d_h] and the weights A [n_h, B, L_tot]."""
+    q, K, V = f64(q), f64(K), f64(V)
+    n_h, B, d_h = q.shape
+    n_kv, L_tot, _ = K.shape
+    group = n_h // n_kv
+    scale = d_h ** -0.5
+    vis = visible(qpos, kpos, window)
+    o = np.empty((n_h, B, d_h))
+    A = np.empty((n_h, B, L_tot))
+    for h in range(n_h):
+        g = h // group
+        s = (q[h] @ K[g].T) * scale
+        s = np.where(vis, s, -np.inf)
+        s = s - s.max(axis=1, keepdims=True)
+        e = np.exp(s)
+        a = e / e.sum(axis=1, keepdims=True)
+        A[h] = a
+        o[h] = a @ V[g]
+    return o, A
+
+
+def o_proj(o, w_o) -> np.ndarray:
+    """[W] Step 4.5: heads concatenated per row (head h at columns h*d_h ..),
+    then one projection back to d.  Only block rows produce output."""
+    o = f64(o)
+    n_h, B, d_h = o.shape
+    return o.transpose(1, 0, 2).reshape(B, n_h * d_h) @ f64(w_o).T
+
+
+@dataclass
+class LayerResult:
+    out: np.ndarray        # [B, d]
+    K: np.ndarray          # cache after the append, [n_kv, L + n + B, d_h]
+    V: np.ndarray
+    q: np.ndarray          # rotated queries [n_h, B, d_h]
+    weights: np.ndarray    # attention weights [n_h, B, L + n + B]
+    qpos: np.ndarray
+    kpos: np.ndarray
+
+
+def kv_inject_layer(p: LayerParams, K_cache, V_cache, C, H) -> LayerResult:
+    """One request through one layer, [W] Step 4 with the cache of [S] section 4.
+
+    K_cache, V_cache [n_kv, L, d_h] hold rotated keys and raw values of
+    positions 0..L-1.  C [n, d] are this round's new context rows and H [B, d]
+    the block rows.  The RoPE window covers positions L .. L+n+B-1 (reading R6,
+    [S] section 3): keys take all of it (context rows then block rows), queries
+    the last B positions ([W] Step 4.3).  The rotated keys and raw values of
+    all n + B rows are appended (reading R7) before attention, which runs over
+    every cached key."""
+    K_cache, V_cache = f64(K_cache), f64(V_cache)
+    L = K_cache.shape[1]
+    n, B = C.shape[0], H.shape[0]
+    pos = L + np.arange(n + B, dtype=np.int64)
+    qpos = pos[n:]
+    q = rope(project_q(p, H), qpos, p.theta)
+    k, v = project_kv(p, C, H)
+    k = rope(k, pos, p.theta)
+    K = np.concatenate([K_cache, k], axis=1)
+    V = np.concatenate([V_cache, v], axis=1)
+    kpos = np.arange(L + n + B, dtype=np.int64)
+    o, A = gqa_attention(q, K, V, qpos, kpos, p.window)
+    return LayerResult(o_proj(o, p.w_o), K, V, q, A, qpos, kpos)
+
+
+def crop(K, V, new_len: int):
+    """Keep the accepted prefix, [S] section 4 and [W] Step 7: the draft cache
+    is cut back to the block start, dropping block rows and rejected rows."""
+    if not 0 <= new_len <= K.shape[1]:
+        raise ValueError("crop beyond the current length")
+    return K[:, :new_len], V[:, :new_len]
+
+
+# --------------------------------------------------------------------------
+# round bookkeeping, [W] Step 6 and Step 7
+# --------------------------------------------------------------------------
+
+def acceptance_length(draft_tail, posterior_head) -> int:
+    """Number of leading draft tokens the target agrees with: the cumulative
+    product of per-position matches, summed."""
+    m = np.asarray([a == b for a, b in zip(draft_tail, posterior_head)], dtype=np.int64)
+    return int(np.cumprod(m).sum())
+
+
+def next_start(start: int, acc: int) -> int:
+    """The accepted tokens plus the target's own correction advance the start."""
+    return start + acc + 1
+
+
+def new_context_rows(acc: int) -> int:
+    """Rows of new context injected next round: the accepted positions plus the
+    corrected one."""
+    return acc + 1
+
+
+# --------------------------------------------------------------------------
+# multi-request rounds and layer stacks
+# --------------------------------------------------------------------------
+
+class OracleStack:
+    """Per-layer, per-request caches for a batch of R requests through a stack
+    of layers.  One round: C = ctx_project(new raw rows) once, shared by every
+    layer ([W] Step 2: one context for all draft layers); then each layer runs
+    kv_inject_layer per request, chaining H_{l+1} = H_l + out_l (reading R14);
+    then every layer's cache is cropped to L + n."""
+
+    def __init__(self, layers, w_fc, gamma_h, eps, K0, V0):
+        """K0[l][r], V0[l][r]: [n_kv, L_r, d_h] cache content before round 0."""
+        self.layers = list(layers)
+        self.w_fc, self.gamma_h, self.eps = w_fc, gamma_h, eps
+        self.K = [[f64(k) for k in row] for row in K0]
+        self.V = [[f64(v) for v in row] for row in V0]
+
+    def lengths(self, layer: int = 0):
+        return [k.shape[1] for k in self.K[layer]]
+
+    def round(self, x_raw, cu, H, B: int):
+        """x_raw [T, k*d] with request r at rows cu[r]..cu[r+1]-1; H [R*B, d].
+        Returns outputs [n_layers][R*B, d] (each layer's o_proj output) and the
+        last layer's LayerResult per request."""
+        R = len(cu) - 1
+        C = ctx_project(x_raw, self.w_fc, self.gamma_h, self.eps)
+        h = f64(H).copy()
+        outs, last = [], []
+        for li, p in enumerate(self.layers):
+            out_l = np.empty_like(h)
+            res_l = []
+            for r in range(R):
+                L = self.K[li][r].shape[1]
+                res = kv_inject_layer(p, self.K[li][r], self.V[li][r],
+                                      C[cu[r]:cu[r + 1]], h[r * B:(r + 1) * B])
+                out_l[r * B:(r + 1) * B] = res.out
+                n = cu[r + 1] - cu[r]
+                self.K[li][r], self.V[li][r] = crop(res.K, res.V, L + n)
+                res_l.append(res)
+            outs.append(out_l)
+            last = res_l
+            h = h + out_l
+        return outs, last

@@ -1,0 +1,387 @@
+"""Pins for the fp64 oracle, checked against what the pages and the mathematics
+fix rather than against the oracle itself.
+
+Sources: "DFlash KV Injection Walkthrough" (shapes of Steps 1-4, the scaling
+0.125, RoPE relative-position identity of Step 4.3, non-causal 4 x 7 attention
+of Step 4.4, acceptance example of Step 6, cache growth of Step 7);
+"DFlash源码导读二 Qwen3DFlashAttention注意力实现全解析" (same k_proj/v_proj on both
+streams, GQA groups); "KV Cache + Speculative Decoding 面试 Cheat Sheet" 6.3
+(grouped attention equals attention with repeat_interleave'd K/V heads).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dflash_oracle as O
+from workloads import configs, generate as G
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "walkthrough.json")))
+
+
+def _params(wl, layer=0):
+    lw = G.layer_weights(wl, layer)
+    return O.LayerParams(lw["w_qkv"], lw["w_o"], lw["gamma_q"], lw["gamma_k"],
+                         wl.n_h, wl.n_kv, wl.d_h, wl.eps, wl.rope_theta, wl.layer_window(layer))
+
+
+def _tiny_params(rng, d=8, n_h=4, n_kv=2, d_h=4, window=0, theta=1e4):
+    qd, kvd = n_h * d_h, n_kv * d_h
+    return O.LayerParams(rng.standard_normal((qd + 2 * kvd, d)) / math.sqrt(d),
+                         rng.standard_normal((d, qd)) / math.sqrt(qd),
+                         1 + 0.1 * rng.standard_normal(d_h), 1 + 0.1 * rng.standard_normal(d_h),
+                         n_h, n_kv, d_h, 1e-6, theta, window)
+
+
+# ---------------------------------------------------------------- walkthrough
+
+def test_walkthrough_shapes_and_positions():
+    wl = configs.WALKTHROUGH
+    s, sh = GOLDEN["setup"], GOLDEN["shapes"]
+    assert (wl.d, wl.n_h, wl.d_h, wl.k_layers, wl.B) == (s["d"], s["n_h"], s["d_h"], s["k"], s["block_size"])
+    assert wl.d_h == wl.d // wl.n_h
+    fc = G.fc_weights(wl)
+    x, cu, H = G.round_inputs(wl, 0, [wl.n_fixed])
+    assert list(x.shape) == sh["target_hidden_raw"]
+    assert list(fc["w_fc"].T.shape) == sh["w_fc_math"]
+    C = O.ctx_project(x, fc["w_fc"], fc["gamma_h"], wl.eps)
+    assert list(C.shape) == sh["C"] and list(H.shape) == sh["H"]
+    p = _params(wl)
+    K0 = np.zeros((wl.n_kv, 0, wl.d_h))
+    res = O.kv_inject_layer(p, K0, K0, C, H)
+    assert list(res.q.shape) == sh["Q"]
+    assert list(res.K.shape) == sh["K"] and list(res.V.shape) == sh["V"]
+    assert list(res.weights.shape[1:]) == sh["A"]
+    assert list(res.out.shape) == sh["attn_out"]
+    pos = GOLDEN["positions"]
+    assert list(res.qpos) == pos["q"] and list(res.kpos) == pos["k"]
+    # the cos/sin table covers the whole window, one row per position, width d_h
+    assert [len(pos["window"]), wl.d_h] == sh["cos_sin"]
+
+
+def test_scaling_is_printed_value():
+    """Two keys with score gap g: the first weight is 1/(1+exp(-g*scale)), the
+    scale printed for d_h = 64 being 0.125."""
+    d_h = GOLDEN["scaling"]["d_h"]
+    scale = GOLDEN["scaling"]["value"]
+    q = np.zeros((1, 1, d_h)); q[0, 0, 0] = 3.0
+    K = np.zeros((1, 2, d_h)); K[0, 0, 0] = 2.0; K[0, 1, 0] = -1.0
+    V = np.zeros((1, 2, d_h)); V[0, 0, 1] = 1.0
+    _, A = O.gqa_attention(q, K, V, [0], [0, 0])
+    gap = 3.0 * 2.0 - 3.0 * (-1.0)
+    assert abs(A[0, 0, 0] - 1.0 / (1.0 + math.exp(-gap * scale))) < 1e-15
+
+
+def test_softmax_rows_sum_to_one_and_no_causal_mask():
+    wl = configs.WALKTHROUGH
+    fc = G.fc_weights(wl)
+    x, _, H = G.round_inputs(wl, 0, [wl.n_fixed])
+    C = O.ctx_project(x, fc["w_fc"], fc["gamma_h"], wl.eps)
+    K0 = np.zeros((wl.n_kv, 0, wl.d_h))
+    res = O.kv_inject_layer(_params(wl), K0, K0, C, H)
+    assert np.max(np.abs(res.weights.sum(axis=-1) - 1.0)) < 1e-12
+    # every query sees every key, including later block positions
+    assert np.all(res.weights > 0)
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+def test_rmsnorm_closed_forms():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((7, 33)) * rng.uniform(0.01, 10, size=(7, 1))
+    eps = 1e-3
+    y = O.rms_norm(x, np.ones(33), eps)
+    ms = np.mean(x * x, axis=-1)
+    assert np.allclose(np.mean(y * y, axis=-1), ms / (ms + eps), rtol=1e-12)
+    # scale invariance as eps -> 0, and the gain multiplies elementwise
+    g = rng.uniform(0.5, 1.5, 33)
+    assert np.allclose(O.rms_norm(5.0 * x, g, 0.0), O.rms_norm(x, g, 0.0), rtol=1e-12)
+    assert np.allclose(O.rms_norm(x, g, 0.0), O.rms_norm(x, np.ones(33), 0.0) * g, rtol=1e-12)
+
+
+def test_ctx_project_brute_force():
+    rng = np.random.default_rng(6)
+    T, kd, d = 3, 6, 4
+    x, w, g = rng.standard_normal((T, kd)), rng.standard_normal((d, kd)), rng.standard_normal(d)
+    C = O.ctx_project(x, w, g, 1e-6)
+    for t in range(T):
+        u = [sum(x[t, i] * w[o, i] for i in range(kd)) for o in range(d)]
+        r = math.sqrt(sum(v * v for v in u) / d + 1e-6)
+        for o in range(d):
+            assert abs(C[t, o] - u[o] / r * g[o]) < 1e-12
+
+
+# ---------------------------------------------------------------- RoPE
+
+def test_rope_equals_complex_rotation():
+    """rotate_half pairs (x_i, x_{i+d/2}) rotate like the complex number
+    x_i + j x_{i+d/2} multiplied by exp(j p w_i)."""
+    rng = np.random.default_rng(7)
+    d_h, theta = 16, 1e6
+    x = rng.standard_normal((5, d_h))
+    pos = np.array([0, 1, 7, 8191, 33000])
+    y = O.rope(x, pos, theta)
+    half = d_h // 2
+    for r in range(5):
+        for i in range(half):
+            w = theta ** (-2.0 * i / d_h)
+            z = complex(x[r, i], x[r, i + half]) * complex(math.cos(pos[r] * w), math.sin(pos[r] * w))
+            assert abs(y[r, i] - z.real) < 1e-12 and abs(y[r, i + half] - z.imag) < 1e-12
+
+
+def test_rope_group_properties():
+    rng = np.random.default_rng(8)
+    d_h = 128
+    x = rng.standard_normal((4, d_h))
+    p = np.array([0, 3, 100, 9000]); q = np.array([5, 2, 77, 24000])
+    assert np.allclose(O.rope(x, np.zeros(4), 1e6), x, atol=0)
+    assert np.allclose(np.linalg.norm(O.rope(x, p, 1e6), axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+    assert np.allclose(O.rope(O.rope(x, p, 1e6), q, 1e6), O.rope(x, p + q, 1e6), atol=1e-10)
+
+
+@pytest.mark.parametrize("delta", [1, 37, 8192, 100000])
+def test_rope_relative_position_invariance(delta):
+    """q'_i . k'_j depends on j - i only: shifting every position by delta
+    leaves all scores unchanged (Step 4.3)."""
+    rng = np.random.default_rng(9)
+    d_h = 64
+    q, k = rng.standard_normal((4, d_h)), rng.standard_normal((7, d_h))
+    qpos, kpos = np.arange(3, 7), np.arange(7)
+    s0 = O.rope(q, qpos, 1e6) @ O.rope(k, kpos, 1e6).T
+    s1 = O.rope(q, qpos + delta, 1e6) @ O.rope(k, kpos + delta, 1e6).T
+    assert np.max(np.abs(s1 - s0)) <= 1e-9 * np.max(np.abs(s0))
+
+
+def test_rope_example_pair_and_wrong_offset():
+    """The walkthrough's example: the query at position 5 against the key at
+    position 2 sees a relative rotation of -3; the wrong window (queries at
+    0..3) would put that query at position 2, relative rotation 0."""
+    ex = GOLDEN["positions"]["example_pair"]
+    rng = np.random.default_rng(10)
+    d_h = 64
+    q, k = rng.standard_normal(d_h), rng.standard_normal(d_h)
+    s = O.rope(q[None], np.array([ex["q_pos"]]), 1e6) @ O.rope(k[None], np.array([ex["k_pos"]]), 1e6).T
+    rel = O.rope(k[None], np.array([ex["relative"]]), 1e6)
+    assert abs(s[0, 0] - (q @ rel[0])) < 1e-12
+    wrong = O.rope(q[None], np.array([ex["wrong_q_pos"]]), 1e6) @ O.rope(k[None], np.array([ex["k_pos"]]), 1e6).T
+    assert abs(wrong[0, 0] - q @ O.rope(k[None], np.array([ex["wrong_relative"]]), 1e6)[0]) < 1e-12
+    assert abs(wrong[0, 0] - s[0, 0]) > 1e-3
+
+
+def test_layer_tail_offset_matters():
+    """Queries on the last B window positions (correct) versus on the first B
+    (the wrong reading): outputs must differ by far more than any tolerance."""
+    wl = configs.WALKTHROUGH
+    p = _params(wl)
+    fc = G.fc_weights(wl)
+    x, _, H = G.round_inputs(wl, 0, [wl.n_fixed])
+    C = O.ctx_project(x, fc["w_fc"], fc["gamma_h"], wl.eps)
+    K0 = np.zeros((wl.n_kv, 0, wl.d_h))
+    good = O.kv_inject_layer(p, K0, K0, C, H)
+    q_wrong = O.rope(O.project_q(p, H), np.arange(wl.B), p.theta)
+    o, _ = O.gqa_attention(q_wrong, good.K, good.V, np.arange(wl.B), good.kpos)
+    bad = O.o_proj(o, p.w_o)
+    rel = np.linalg.norm(bad - good.out) / np.linalg.norm(good.out)
+    assert rel > 1e-2
+
+
+# ---------------------------------------------------------------- attention
+
+def test_gqa_equals_repeated_kv_mha():
+    rng = np.random.default_rng(11)
+    n_h, n_kv, B, L, d_h = 8, 2, 3, 11, 16
+    q = rng.standard_normal((n_h, B, d_h))
+    K, V = rng.standard_normal((n_kv, L, d_h)), rng.standard_normal((n_kv, L, d_h))
+    o_g, _ = O.gqa_attention(q, K, V, np.arange(B), np.arange(L))
+    Kr, Vr = np.repeat(K, n_h // n_kv, axis=0), np.repeat(V, n_h // n_kv, axis=0)
+    o_m, _ = O.gqa_attention(q, Kr, Vr, np.arange(B), np.arange(L))
+    assert np.max(np.abs(o_g - o_m)) < 1e-12
+
+
+def test_position_zero_reduces_to_library_sdpa():
+    """All positions 0: RoPE is the identity and attention is textbook SDPA,
+    here torch's CPU scaled_dot_product_attention in float64."""
+    rng = np.random.default_rng(12)
+    n_h, n_kv, B, L, d_h = 8, 2, 5, 9, 32
+    q = rng.standard_normal((n_h, B, d_h))
+    K, V = rng.standard_normal((n_kv, L, d_h)), rng.standard_normal((n_kv, L, d_h))
+    qr = O.rope(q, np.zeros(B), 1e6)
+    Kr = O.rope(K, np.zeros(L), 1e6)
+    o, _ = O.gqa_attention(qr, Kr, V, np.zeros(B, int), np.zeros(L, int))
+    tq = torch.from_numpy(q)[None]
+    tk = torch.from_numpy(K).repeat_interleave(n_h // n_kv, dim=0)[None]
+    tv = torch.from_numpy(V).repeat_interleave(n_h // n_kv, dim=0)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=False)[0].numpy()
+    assert np.max(np.abs(o - ref)) < 1e-12
+
+
+def test_single_key_closed_form():
+    """No cache, no context, one block row: attention over the row's own key
+    returns its own value, so out = v_own . W_O^T with v_own repeated per group."""
+    rng = np.random.default_rng(13)
+    p = _tiny_params(rng)
+    d = p.w_qkv.shape[1]
+    H = rng.standard_normal((1, d))
+    res = O.kv_inject_layer(p, np.zeros((p.n_kv, 0, p.d_h)), np.zeros((p.n_kv, 0, p.d_h)),
+                            np.zeros((0, d)), H)
+    wv = p.w_qkv[(p.n_h + p.n_kv) * p.d_h:]
+    v = (H @ wv.T).reshape(p.n_kv, p.d_h)
+    attn = np.concatenate([v[h // (p.n_h // p.n_kv)] for h in range(p.n_h)])
+    assert np.allclose(res.out[0], attn @ p.w_o.T, atol=1e-12)
+
+
+def test_dual_stream_rows_are_independent():
+    """The same k_proj/v_proj act on the context and the block rows: the
+    context rows of the cache do not depend on the block, and after the crop
+    the cache equals what the context alone produces."""
+    rng = np.random.default_rng(14)
+    p = _tiny_params(rng)
+    d = p.w_qkv.shape[1]
+    L, n, B = 3, 2, 3
+    K0, V0 = rng.standard_normal((p.n_kv, L, p.d_h)), rng.standard_normal((p.n_kv, L, p.d_h))
+    C = rng.standard_normal((n, d))
+    r1 = O.kv_inject_layer(p, K0, V0, C, rng.standard_normal((B, d)))
+    r2 = O.kv_inject_layer(p, K0, V0, C, rng.standard_normal((B, d)))
+    k1, v1 = O.crop(r1.K, r1.V, L + n)
+    k2, v2 = O.crop(r2.K, r2.V, L + n)
+    assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+    k_ctx, v_ctx = O.project_kv(p, C, np.zeros((0, d)))
+    assert np.allclose(k1[:, L:], O.rope(k_ctx, L + np.arange(n), p.theta), atol=1e-13)
+    assert np.allclose(v1[:, L:], v_ctx, atol=1e-13)
+
+
+# ---------------------------------------------------------------- window
+
+def test_window_closed_forms():
+    rng = np.random.default_rng(15)
+    L, n, B = 5, 2, 3
+    p_full = _tiny_params(rng)
+    K0, V0 = rng.standard_normal((p_full.n_kv, L, p_full.d_h)), rng.standard_normal((p_full.n_kv, L, p_full.d_h))
+    d = p_full.w_qkv.shape[1]
+    C, H = rng.standard_normal((n, d)), rng.standard_normal((B, d))
+    full = O.kv_inject_layer(p_full, K0, V0, C, H)
+    for W in (L + n + B, L + n + B + 100):
+        p_w = O.LayerParams(**{**p_full.__dict__, "window": W})
+        assert np.array_equal(O.kv_inject_layer(p_w, K0, V0, C, H).out, full.out)
+    p1 = O.LayerParams(**{**p_full.__dict__, "window": 1})
+    r1 = O.kv_inject_layer(p1, K0, V0, C, H)
+    for b in range(B):
+        qp = L + n + b
+        seen = set(np.nonzero(r1.weights[0, b] > 0)[0].tolist())
+        assert seen == set(range(qp, L + n + B))   # itself and the later block rows
+
+
+# ---------------------------------------------------------------- brute force
+
+def _brute_layer(p, K0, V0, C, H):
+    """Scalar-loop formulation: explicit 2x2 rotations, explicit exp and sums,
+    K/V heads repeated explicitly for every query head."""
+    d_h, n_h, n_kv = p.d_h, p.n_h, p.n_kv
+    half = d_h // 2
+    W = p.w_qkv
+    rows = [list(r) for r in C] + [list(r) for r in H]
+    n, B, L = len(C), len(H), K0.shape[1]
+
+    def lin(x, first_row, count):
+        return [sum(x[i] * W[first_row + o][i] for i in range(len(x))) for o in range(count)]
+
+    def norm(v, g):
+        ms = sum(t * t for t in v) / len(v)
+        return [v[i] / math.sqrt(ms + p.eps) * g[i] for i in range(len(v))]
+
+    def rot(v, pos):
+        out = [0.0] * d_h
+        for i in range(half):
+            a = pos * p.theta ** (-2.0 * i / d_h)
+            m = [[math.cos(a), -math.sin(a)], [math.sin(a), math.cos(a)]]
+            out[i] = m[0][0] * v[i] + m[0][1] * v[i + half]
+            out[i + half] = m[1][0] * v[i] + m[1][1] * v[i + half]
+        return out
+
+    Kc = [[list(K0[g, j]) for j in range(L)] for g in range(n_kv)]
+    Vc = [[list(V0[g, j]) for j in range(L)] for g in range(n_kv)]
+    for t, x in enumerate(rows):
+        kx = lin(x, n_h * d_h, n_kv * d_h)
+        vx = lin(x, (n_h + n_kv) * d_h, n_kv * d_h)
+        for g in range(n_kv):
+            Kc[g].append(rot(norm(kx[g * d_h:(g + 1) * d_h], p.gamma_k), L + t))
+            Vc[g].append(vx[g * d_h:(g + 1) * d_h])
+    Kh = [Kc[h * n_kv // n_h] for h in range(n_h)]     # explicit repetition per query head
+    Vh = [Vc[h * n_kv // n_h] for h in range(n_h)]
+    out = []
+    for b in range(B):
+        qx = lin(list(H[b]), 0, n_h * d_h)
+        qpos = L + n + b
+        concat = []
+        for h in range(n_h):
+            qh = rot(norm(qx[h * d_h:(h + 1) * d_h], p.gamma_q), qpos)
+            keys = [j for j in range(L + n + B) if p.window <= 0 or qpos - j < p.window]
+            sc = [sum(qh[i] * Kh[h][j][i] for i in range(d_h)) / math.sqrt(d_h) for j in keys]
+            mx = max(sc)
+            ex = [math.exp(s - mx) for s in sc]
+            tot = sum(ex)
+            concat += [sum(ex[a] / tot * Vh[h][j][i] for a, j in enumerate(keys)) for i in range(d_h)]
+        out.append([sum(concat[i] * p.w_o[o][i] for i in range(len(concat))) for o in range(len(p.w_o))])
+    return np.array(out), Kc, Vc
+
+
+@pytest.mark.parametrize("L,n,B,window", [(0, 0, 1, 0), (0, 3, 2, 0), (5, 1, 3, 0), (2, 2, 2, 0),
+                                          (4, 3, 3, 3), (5, 2, 1, 1), (3, 0, 3, 2)])
+def test_brute_force_tiny(L, n, B, window):
+    rng = np.random.default_rng(100 + 7 * L + 3 * n + B)
+    p = _tiny_params(rng, window=window)
+    d = p.w_qkv.shape[1]
+    K0, V0 = rng.standard_normal((p.n_kv, L, p.d_h)), rng.standard_normal((p.n_kv, L, p.d_h))
+    C, H = rng.standard_normal((n, d)), rng.standard_normal((B, d))
+    res = O.kv_inject_layer(p, K0, V0, C, H)
+    out, Kc, Vc = _brute_layer(p, K0, V0, C, H)
+    assert np.max(np.abs(res.out - out)) < 1e-12
+    assert np.max(np.abs(res.K - np.array(Kc))) < 1e-12
+    assert np.max(np.abs(res.V - np.array(Vc))) < 1e-12
+
+
+# ---------------------------------------------------------------- bookkeeping
+
+def test_acceptance_example_and_state_update():
+    a, s = GOLDEN["acceptance"], GOLDEN["state_update"]
+    acc = O.acceptance_length(a["block"][1:], a["posterior_head"])
+    assert acc == a["acceptance_length"]
+    assert O.next_start(s["start_before"], acc) == s["start_after"]
+    assert O.new_context_rows(acc) == s["new_context_rows"] == len(s["new_context_positions"])
+    # identical and fully-mismatched blocks
+    assert O.acceptance_length([1, 2, 3], [1, 2, 3]) == 3
+    assert O.acceptance_length([9, 2, 3], [1, 2, 3]) == 0
+
+
+def test_cache_growth_over_two_rounds():
+    """Round 1 injects the 3 prompt positions; after the crop the draft cache
+    holds positions 0-2; round 2 injects 3 accepted positions: 0-5."""
+    rng = np.random.default_rng(16)
+    p = _tiny_params(rng)
+    d = p.w_qkv.shape[1]
+    kd = 3 * d
+    w_fc, g_h = rng.standard_normal((d, kd)) / math.sqrt(kd), np.ones(d)
+    st = O.OracleStack([p], w_fc, g_h, 1e-6, [[np.zeros((p.n_kv, 0, p.d_h))]], [[np.zeros((p.n_kv, 0, p.d_h))]])
+    s = GOLDEN["state_update"]
+    B = 4
+    st.round(rng.standard_normal((3, kd)), [0, 3], rng.standard_normal((B, d)), B)
+    assert st.lengths() == [len(s["draft_cache_positions_round1"])]
+    st.round(rng.standard_normal((s["new_context_rows"], kd)), [0, 3], rng.standard_normal((B, d)), B)
+    assert st.lengths() == [len(s["draft_cache_positions_round2"])]
+
+
+def test_stack_single_layer_matches_layer():
+    """A one-layer stack round is exactly ctx_project followed by the layer."""
+    rng = np.random.default_rng(17)
+    p = _tiny_params(rng)
+    d = p.w_qkv.shape[1]
+    w_fc = rng.standard_normal((d, 2 * d))
+    K0, V0 = rng.standard_normal((p.n_kv, 4, p.d_h)), rng.standard_normal((p.n_kv, 4, p.d_h))
+    x, H = rng.standard_normal((2, 2 * d)), rng.standard_normal((3, d))
+    st = O.OracleStack([p], w_fc, np.ones(d), 1e-6, [[K0]], [[V0]])
+    outs, _ = st.round(x, [0, 2], H, 3)
+    res = O.kv_inject_layer(p, K0, V0, O.ctx_project(x, w_fc, np.ones(d), 1e-6), H)
+    assert np.array_equal(outs[0], res.out)

@@ -1,0 +1,165 @@
+"""Plant plausible mistakes in the oracle (on the CPU, by monkeypatching) and
+check that the pins catch every one: a dropped term, a wrong sign or index, a
+transposed operand, a wrong scale, a causal mask, a wrong RoPE offset."""
+import numpy as np
+import pytest
+
+from oracle import dflash_oracle as O
+import tests.test_oracle as T
+
+PINS = [
+    T.test_walkthrough_shapes_and_positions,
+    T.test_scaling_is_printed_value,
+    T.test_softmax_rows_sum_to_one_and_no_causal_mask,
+    T.test_rmsnorm_closed_forms,
+    T.test_ctx_project_brute_force,
+    T.test_rope_equals_complex_rotation,
+    T.test_rope_group_properties,
+    lambda: T.test_rope_relative_position_invariance(8192),
+    T.test_rope_example_pair_and_wrong_offset,
+    T.test_layer_tail_offset_matters,
+    T.test_gqa_equals_repeated_kv_mha,
+    T.test_position_zero_reduces_to_library_sdpa,
+    T.test_single_key_closed_form,
+    T.test_dual_stream_rows_are_independent,
+    T.test_window_closed_forms,
+    lambda: T.test_brute_force_tiny(5, 1, 3, 0),
+    lambda: T.test_brute_force_tiny(4, 3, 3, 3),
+    lambda: T.test_brute_force_tiny(5, 2, 1, 1),
+    T.test_cache_growth_over_two_rounds,
+]
+
+
+def _rope_sign(x, positions, theta):
+    x = O.f64(x); half = x.shape[-1] // 2
+    ang = O.f64(positions)[:, None] * O.rope_inv_freq(x.shape[-1], theta)[None, :]
+    lo, hi = x[..., :half], x[..., half:]
+    return np.concatenate([lo * np.cos(ang) + hi * np.sin(ang), hi * np.cos(ang) - lo * np.sin(ang)], -1)
+
+
+def _rope_interleaved(x, positions, theta):
+    x = O.f64(x)
+    ang = O.f64(positions)[:, None] * O.rope_inv_freq(x.shape[-1], theta)[None, :]
+    ev, od = x[..., 0::2], x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2] = ev * np.cos(ang) - od * np.sin(ang)
+    y[..., 1::2] = od * np.cos(ang) + ev * np.sin(ang)
+    return y
+
+
+def _attn_factory(head_map=None, scale_pow=-0.5, causal=False):
+    def attn(q, K, V, qpos, kpos, window=0):
+        q, K, V = O.f64(q), O.f64(K), O.f64(V)
+        n_h, B, d_h = q.shape
+        n_kv, L_tot, _ = K.shape
+        vis = O.visible(qpos, kpos, window)
+        if causal:
+            vis = vis & (np.asarray(kpos)[None, :] <= np.asarray(qpos)[:, None])
+        o = np.empty((n_h, B, d_h)); A = np.empty((n_h, B, L_tot))
+        for h in range(n_h):
+            g = head_map(h, n_h, n_kv) if head_map else h // (n_h // n_kv)
+            s = np.where(vis, (q[h] @ K[g].T) * d_h ** scale_pow, -np.inf)
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            A[h] = e / e.sum(axis=1, keepdims=True)
+            o[h] = A[h] @ V[g]
+        return o, A
+    return attn
+
+
+def _kv_no_knorm(p, C, H):
+    _, wk, wv = p.split()
+    S = np.concatenate([O.f64(C), O.f64(H)], axis=0)
+    k = (S @ wk.T).reshape(S.shape[0], p.n_kv, p.d_h)
+    v = (S @ wv.T).reshape(S.shape[0], p.n_kv, p.d_h)
+    return k.transpose(1, 0, 2), v.transpose(1, 0, 2)
+
+
+def _kv_block_first(p, C, H):
+    return _ORIG["project_kv"](p, H, C)
+
+
+def _rms_no_gamma(x, gamma, eps):
+    x = O.f64(x)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def _rms_no_eps(x, gamma, eps):
+    x = O.f64(x)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) * O.f64(gamma)
+
+
+def _rms_sum(x, gamma, eps):
+    x = O.f64(x)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps) * O.f64(gamma)
+
+
+def _ctx_transposed(x_raw, w_fc, gamma_h, eps):
+    w = O.f64(w_fc)
+    return O.rms_norm(O.f64(x_raw) @ w.reshape(w.shape[1], w.shape[0]), gamma_h, eps)
+
+
+def _oproj_head_minor(o, w_o):
+    o = O.f64(o); n_h, B, d_h = o.shape
+    return o.transpose(1, 2, 0).reshape(B, n_h * d_h) @ O.f64(w_o).T
+
+
+def _crop_keep_block(K, V, new_len):
+    return K, V
+
+
+def _window_inclusive(qpos, kpos, window):
+    qpos, kpos = np.asarray(qpos), np.asarray(kpos)
+    if window <= 0:
+        return np.ones((qpos.size, kpos.size), dtype=bool)
+    return (qpos[:, None] - kpos[None, :]) <= window
+
+
+def _inv_freq_wrong(d_h, theta):
+    i = np.arange(d_h // 2, dtype=np.float64)
+    return np.power(float(theta), -i / d_h)
+
+
+def _layer_q_front(p, K_cache, V_cache, C, H):
+    res = _ORIG["kv_inject_layer"](p, K_cache, V_cache, C, H)
+    L = np.asarray(K_cache).shape[1]
+    qpos = L + np.arange(H.shape[0])
+    q = O.rope(O.project_q(p, H), qpos, p.theta)
+    o, A = O.gqa_attention(q, res.K, res.V, qpos, res.kpos, p.window)
+    return O.LayerResult(O.o_proj(o, p.w_o), res.K, res.V, q, A, qpos, res.kpos)
+
+
+_ORIG = {name: getattr(O, name) for name in
+         ("rope", "gqa_attention", "project_kv", "rms_norm", "ctx_project", "o_proj",
+          "crop", "visible", "rope_inv_freq", "kv_inject_layer")}
+
+MUTANTS = {
+    "rope_sign_flipped": ("rope", _rope_sign),
+    "rope_interleaved_pairs": ("rope", _rope_interleaved),
+    "rope_freq_exponent": ("rope_inv_freq", _inv_freq_wrong),
+    "gqa_head_modulo": ("gqa_attention", _attn_factory(head_map=lambda h, n_h, n_kv: h % n_kv)),
+    "scale_one_over_d": ("gqa_attention", _attn_factory(scale_pow=-1.0)),
+    "causal_mask": ("gqa_attention", _attn_factory(causal=True)),
+    "no_k_norm": ("project_kv", _kv_no_knorm),
+    "block_rows_first": ("project_kv", _kv_block_first),
+    "rmsnorm_no_gamma": ("rms_norm", _rms_no_gamma),
+    "rmsnorm_no_eps": ("rms_norm", _rms_no_eps),
+    "rmsnorm_sum_not_mean": ("rms_norm", _rms_sum),
+    "fc_weight_transposed": ("ctx_project", _ctx_transposed),
+    "oproj_head_minor": ("o_proj", _oproj_head_minor),
+    "crop_does_nothing": ("crop", _crop_keep_block),
+    "window_inclusive": ("visible", _window_inclusive),
+    "queries_on_window_front": ("kv_inject_layer", _layer_q_front),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(O, attr, fn)
+    caught = []
+    for pin in PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            caught.append(getattr(pin, "__name__", "pin"))
+    assert caught, f"mutant {name} survived every pin"
