@@ -1,0 +1,201 @@
+"""ctypes binding of libdflash.so (include/dflash.h).
+
+Argument marshalling only: torch tensors become device pointers, the current
+HIP stream becomes the stream argument, and negative status codes become
+DFlashError.  Every step of the layer runs in the library's HIP kernels.  If
+the library has not been built, importing the binding raises: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdflash.so")
+
+DFLASH_OK = 0
+ERR_ARG, ERR_SHAPE, ERR_DTYPE, ERR_RANGE, ERR_CAPACITY, ERR_HIP, ERR_WORKSPACE = -1, -2, -3, -4, -5, -6, -7
+DFLASH_F32, DFLASH_BF16 = 0, 1
+
+
+class DFlashError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {strerror(code)} ({code})")
+        self.code = code
+
+
+class LayerDesc(C.Structure):
+    _fields_ = [("d", C.c_int32), ("n_h", C.c_int32), ("n_kv", C.c_int32), ("d_h", C.c_int32),
+                ("eps", C.c_float), ("rope_theta", C.c_double), ("window", C.c_int32),
+                ("dtype", C.c_int32), ("w_qkv", C.c_void_p), ("w_o", C.c_void_p),
+                ("gamma_q", C.c_void_p), ("gamma_k", C.c_void_p)]
+
+
+class CacheDesc(C.Structure):
+    _fields_ = [("n_seqs", C.c_int32), ("n_kv", C.c_int32), ("d_h", C.c_int32), ("dtype", C.c_int32),
+                ("page_size", C.c_int32), ("max_pages_per_seq", C.c_int32), ("capacity", C.c_int64),
+                ("k_pool", C.c_void_p), ("v_pool", C.c_void_p), ("block_table", C.c_void_p)]
+
+
+def _load() -> C.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m block_diffusion_draft_fc_amd.build` (there is no CPU fallback)")
+    lib = C.CDLL(LIB_PATH)
+    vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+    p32 = C.POINTER(C.c_int32)
+    sig = {
+        "dflash_strerror": (C.c_char_p, [C.c_int]),
+        "dflash_cache_init": (C.c_int, [C.POINTER(vp), C.POINTER(CacheDesc)]),
+        "dflash_cache_destroy": (C.c_int, [vp]),
+        "dflash_cache_lengths": (C.c_int, [vp, p32]),
+        "dflash_cache_block_table": (C.c_int, [vp, p32]),
+        "dflash_cache_free_pages": (i64, [vp]),
+        "dflash_ctx_project_ws_bytes": (sz, [i64, i64, i64, i32]),
+        "dflash_ctx_project": (C.c_int, [vp, i64, i64, vp, vp, i64, C.c_float, i32, vp, vp, sz, vp]),
+        "dflash_cache_append": (C.c_int, [vp, p32, vp, vp, vp]),
+        "dflash_cache_crop": (C.c_int, [vp, p32, vp]),
+        "dflash_kv_inject_attn_ws_bytes": (sz, [C.POINTER(LayerDesc), vp, i64, i32]),
+        "dflash_kv_inject_attn": (C.c_int, [C.POINTER(LayerDesc), vp, vp, p32, vp, i32, vp, vp, sz, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+LIB = _load()
+
+
+def strerror(code: int) -> str:
+    return LIB.dflash_strerror(code).decode()
+
+
+def _check(code: int, where: str) -> None:
+    if code != DFLASH_OK:
+        raise DFlashError(code, where)
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return DFLASH_F32
+    if dt == torch.bfloat16:
+        return DFLASH_BF16
+    raise DFlashError(ERR_DTYPE, f"dtype {dt}")
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not (t.is_cuda and t.is_contiguous()):
+        raise DFlashError(ERR_ARG, "tensors must be contiguous device tensors")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _i32(values):
+    arr = (C.c_int32 * len(values))(*[int(v) for v in values])
+    return arr
+
+
+# --------------------------------------------------------------------- cache
+
+class Cache:
+    """dflash_cache handle plus the caller-owned device pools it describes."""
+
+    def __init__(self, n_seqs, n_kv, d_h, dtype, capacity, page_size=0, max_pages_per_seq=0,
+                 device="cuda", pools=None):
+        self.n_seqs, self.n_kv, self.d_h = n_seqs, n_kv, d_h
+        self.page_size, self.capacity, self.max_pages = page_size, capacity, max_pages_per_seq
+        self.dtype = dtype
+        if pools is not None:
+            self.k_pool, self.v_pool, self.table = pools
+        elif page_size == 0:
+            self.k_pool = torch.zeros((n_seqs, n_kv, capacity, d_h), dtype=dtype, device=device)
+            self.v_pool = torch.zeros((n_seqs, n_kv, d_h, capacity), dtype=dtype, device=device)
+            self.table = None
+        else:
+            self.k_pool = torch.zeros((capacity, n_kv, page_size, d_h), dtype=dtype, device=device)
+            self.v_pool = torch.zeros((capacity, n_kv, d_h, page_size), dtype=dtype, device=device)
+            self.table = torch.full((n_seqs, max_pages_per_seq), -1, dtype=torch.int32, device=device)
+        desc = CacheDesc(n_seqs, n_kv, d_h, dtype_code(dtype), page_size, max_pages_per_seq, capacity,
+                         self.k_pool.data_ptr(), self.v_pool.data_ptr(),
+                         self.table.data_ptr() if self.table is not None else None)
+        h = C.c_void_p()
+        _check(LIB.dflash_cache_init(C.byref(h), C.byref(desc)), "dflash_cache_init")
+        self.handle = h
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            LIB.dflash_cache_destroy(h)
+            self.handle = None
+
+    def lengths(self):
+        out = (C.c_int32 * self.n_seqs)()
+        _check(LIB.dflash_cache_lengths(self.handle, out), "dflash_cache_lengths")
+        return list(out)
+
+    def block_table(self):
+        mp = self.max_pages if self.page_size > 0 else 1
+        out = (C.c_int32 * (self.n_seqs * mp))()
+        _check(LIB.dflash_cache_block_table(self.handle, out), "dflash_cache_block_table")
+        return [list(out[s * mp:(s + 1) * mp]) for s in range(self.n_seqs)]
+
+    def free_pages(self) -> int:
+        return int(LIB.dflash_cache_free_pages(self.handle))
+
+
+def dflash_cache_append(cache: Cache, cu_rows, k_rows, v_rows, stream=None) -> None:
+    _check(LIB.dflash_cache_append(cache.handle, _i32(cu_rows), _ptr(k_rows), _ptr(v_rows), _stream(stream)),
+           "dflash_cache_append")
+
+
+def dflash_cache_crop(cache: Cache, new_len, stream=None) -> None:
+    _check(LIB.dflash_cache_crop(cache.handle, _i32(new_len), _stream(stream)), "dflash_cache_crop")
+
+
+# --------------------------------------------------------------------- context projection
+
+def dflash_ctx_project_ws_bytes(T, kd, d, dtype: torch.dtype) -> int:
+    return int(LIB.dflash_ctx_project_ws_bytes(T, kd, d, dtype_code(dtype)))
+
+
+def dflash_ctx_project(x_raw, w_fc, gamma_h, eps, c_out, ws, stream=None) -> None:
+    T, kd = x_raw.shape
+    d = w_fc.shape[0]
+    _check(LIB.dflash_ctx_project(_ptr(x_raw), T, kd, _ptr(w_fc), _ptr(gamma_h), d, float(eps),
+                                  dtype_code(x_raw.dtype), _ptr(c_out), _ptr(ws), ws.numel() if ws is not None else 0,
+                                  _stream(stream)),
+           "dflash_ctx_project")
+
+
+# --------------------------------------------------------------------- layer
+
+class Layer:
+    """Device weights of one KV-injection attention layer and its descriptor."""
+
+    def __init__(self, w_qkv, w_o, gamma_q, gamma_k, n_h, n_kv, d_h, eps=1e-6, rope_theta=1e6, window=0):
+        self.w_qkv, self.w_o, self.gamma_q, self.gamma_k = w_qkv, w_o, gamma_q, gamma_k
+        self.d = w_qkv.shape[1]
+        self.desc = LayerDesc(self.d, n_h, n_kv, d_h, float(eps), float(rope_theta), int(window),
+                              dtype_code(w_qkv.dtype), w_qkv.data_ptr(), w_o.data_ptr(),
+                              gamma_q.data_ptr(), gamma_k.data_ptr())
+
+
+def dflash_kv_inject_attn_ws_bytes(layer: Layer, cache: Cache, T: int, B: int) -> int:
+    return int(LIB.dflash_kv_inject_attn_ws_bytes(C.byref(layer.desc), cache.handle, T, B))
+
+
+def dflash_kv_inject_attn(layer: Layer, cache: Cache, C_rows, cu_ctx, H, B, out, ws, stream=None) -> None:
+    _check(LIB.dflash_kv_inject_attn(C.byref(layer.desc), cache.handle, _ptr(C_rows) if C_rows is not None and C_rows.numel() else None,
+                                     _i32(cu_ctx), _ptr(H), int(B), _ptr(out), _ptr(ws),
+                                     ws.numel() if ws is not None else 0, _stream(stream)),
+           "dflash_kv_inject_attn")

@@ -1,0 +1,546 @@
+// C ABI of the DFlash KV-injection attention library: argument validation,
+// host-side cache metadata, work planning and the launch sequence of each call.
+// Every check runs before the first enqueue, so a call that fails validation
+// changes no state.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <set>
+#include <vector>
+
+#include "dflash.h"
+#include "kernels.hpp"
+
+using namespace dflash;
+
+struct dflash_cache {
+  dflash_cache_desc desc;
+  std::vector<int32_t> len;
+  std::vector<std::vector<int32_t>> pages;   // paged: physical page per logical page
+  std::set<int32_t> free_pages;             // paged: lowest first
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+// Upper bound on attention work items per call beyond one per (sequence, head).
+constexpr int kAttnMaxTarget = 1024;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool dtype_ok(int32_t dt) { return dt == DFLASH_F32 || dt == DFLASH_BF16; }
+size_t elem_bytes(int32_t dt) { return dt == DFLASH_BF16 ? 2 : 4; }
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int attn_target_items() {
+  static int v = [] {
+    const char* e = std::getenv("DFLASH_ATTN_TARGET_ITEMS");
+    int t = e ? std::atoi(e) : 256;
+    return std::min(std::max(t, 1), kAttnMaxTarget);
+  }();
+  return v;
+}
+
+// ---------------------------------------------------------------- GEMM planning
+
+struct SkinnyPlan {
+  int32_t k_chunk, splits, mt, n_tiles;
+};
+
+// Weight-streaming GEMM of M <= 64 rows: choose the K split so that (a) the
+// activation slice fits the LDS budget and (b) there are enough workgroups to
+// keep every CU streaming.
+SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, size_t eb) {
+  SkinnyPlan p;
+  p.mt = (int32_t)std::max<int64_t>(1, cdiv(M, 16));
+  p.n_tiles = (int32_t)cdiv(N, 64);
+  int64_t kmax = ((int64_t)kSkinnyLdsBytes / (int64_t)(p.mt * 16 * eb) - 8) / 256 * 256;
+  kmax = std::max<int64_t>(kmax, 256);
+  int64_t splits = std::max<int64_t>(cdiv(K, kmax), cdiv(512, p.n_tiles));
+  splits = std::min<int64_t>(splits, std::max<int64_t>(1, cdiv(K, 256)));
+  int64_t kc = cdiv(cdiv(K, splits), 256) * 256;
+  p.k_chunk = (int32_t)kc;
+  p.splits = (int32_t)cdiv(K, kc);
+  return p;
+}
+
+size_t skinny_lds(const SkinnyPlan& p, size_t eb) {
+  return (size_t)p.mt * 16 * (size_t)(p.k_chunk + 8) * eb;
+}
+
+// A product of the (virtual) row concatenation [x0 (m0 rows); x1 (m1 rows)] with
+// W^T, written as fp32 split-K partials [splits][M][N].  Rows are processed in
+// problems of at most 64.
+struct GemmJob {
+  const void* x0;
+  const void* x1;
+  int64_t m0, m1;
+  const void* w;
+  int64_t N, K;
+  SkinnyPlan plan;
+  float* part;
+};
+
+GemmJob make_job(const void* x0, int64_t m0, const void* x1, int64_t m1, const void* w, int64_t N,
+                 int64_t K, size_t eb) {
+  GemmJob j;
+  j.x0 = x0; j.m0 = m0; j.x1 = x1; j.m1 = m1; j.w = w; j.N = N; j.K = K;
+  j.plan = plan_skinny(std::min<int64_t>(m0 + m1, kSkinnyMaxM), N, K, eb);
+  j.part = nullptr;
+  return j;
+}
+
+size_t job_part_bytes(const GemmJob& j) {
+  return (size_t)j.plan.splits * (size_t)(j.m0 + j.m1) * (size_t)j.N * sizeof(float);
+}
+
+void job_problems(const GemmJob& j, size_t eb, std::vector<GemmProb>* out) {
+  const int64_t M = j.m0 + j.m1;
+  for (int64_t a = 0; a < M; a += kSkinnyMaxM) {
+    const int64_t e = std::min<int64_t>(a + kSkinnyMaxM, M);
+    GemmProb p{};
+    const int64_t a0 = std::min(a, j.m0), e0 = std::min(e, j.m0);
+    p.m0 = (int32_t)(e0 - a0);
+    p.x0 = static_cast<const char*>(j.x0) + (size_t)a0 * j.K * eb;
+    const int64_t a1 = std::max(a, j.m0) - j.m0, e1 = std::max(e, j.m0) - j.m0;
+    p.m1 = (int32_t)(e1 - a1);
+    p.x1 = j.x1 ? static_cast<const char*>(j.x1) + (size_t)a1 * j.K * eb : nullptr;
+    p.w = j.w;
+    p.part = j.part;
+    p.row_off = (int32_t)a;
+    p.m_out = (int32_t)M;
+    p.N = (int32_t)j.N;
+    p.K = (int32_t)j.K;
+    p.k_chunk = j.plan.k_chunk;
+    p.splits = j.plan.splits;
+    p.mt = (int32_t)cdiv(e - a, 16);
+    p.n_tiles = j.plan.n_tiles;
+    p.blocks = p.n_tiles * p.splits;
+    out->push_back(p);
+  }
+}
+
+hipError_t run_gemms(int32_t dt, const std::vector<GemmJob>& jobs, hipStream_t s) {
+  const size_t eb = elem_bytes(dt);
+  std::vector<GemmProb> probs;
+  for (const auto& j : jobs)
+    if (j.m0 + j.m1 > 0) job_problems(j, eb, &probs);
+  for (size_t i = 0; i < probs.size(); i += 2) {
+    GemmArgs a{};
+    a.p[0] = probs[i];
+    a.nprob = 1;
+    int max_mt = probs[i].mt;
+    size_t lds = (size_t)probs[i].mt * 16 * (probs[i].k_chunk + 8) * eb;
+    if (i + 1 < probs.size()) {
+      a.p[1] = probs[i + 1];
+      a.nprob = 2;
+      max_mt = std::max(max_mt, probs[i + 1].mt);
+      lds = std::max(lds, (size_t)probs[i + 1].mt * 16 * (probs[i + 1].k_chunk + 8) * eb);
+    }
+    hipError_t e = launch_gemm_skinny(dt, a, max_mt, lds, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------- cache helpers
+
+CacheView view_of(const dflash_cache* c) {
+  CacheView v{};
+  v.k_pool = c->desc.k_pool;
+  v.v_pool = c->desc.v_pool;
+  v.block_table = c->desc.page_size > 0 ? c->desc.block_table : nullptr;
+  v.page_rows = c->desc.page_size > 0 ? c->desc.page_size : (int32_t)c->desc.capacity;
+  v.max_pages = c->desc.page_size > 0 ? c->desc.max_pages_per_seq : 1;
+  v.n_kv = c->desc.n_kv;
+  v.d_h = c->desc.d_h;
+  return v;
+}
+
+// New pages an append of n[s] rows per sequence needs; checks every limit.
+struct AppendPlan {
+  std::vector<std::vector<int32_t>> new_pages;   // per sequence, in logical order
+};
+
+int plan_append(const dflash_cache* c, const std::vector<int64_t>& n, AppendPlan* plan) {
+  const auto& d = c->desc;
+  plan->new_pages.assign(d.n_seqs, {});
+  if (d.page_size == 0) {
+    for (int s = 0; s < d.n_seqs; ++s)
+      if (c->len[s] + n[s] > d.capacity) return DFLASH_ERR_CAPACITY;
+    return DFLASH_OK;
+  }
+  int64_t need = 0;
+  for (int s = 0; s < d.n_seqs; ++s) {
+    const int64_t want = cdiv(c->len[s] + n[s], d.page_size);
+    if (want > d.max_pages_per_seq) return DFLASH_ERR_CAPACITY;
+    need += std::max<int64_t>(0, want - (int64_t)c->pages[s].size());
+  }
+  if (need > (int64_t)c->free_pages.size()) return DFLASH_ERR_CAPACITY;
+  auto it = c->free_pages.begin();
+  for (int s = 0; s < d.n_seqs; ++s) {
+    const int64_t want = cdiv(c->len[s] + n[s], d.page_size);
+    for (int64_t j = (int64_t)c->pages[s].size(); j < want; ++j) plan->new_pages[s].push_back(*it++);
+  }
+  return DFLASH_OK;
+}
+
+hipError_t enqueue_page_table(const dflash_cache* c, const AppendPlan& plan, hipStream_t st) {
+  const auto& d = c->desc;
+  if (d.page_size == 0) return hipSuccess;
+  BtUpdateArgs a{};
+  a.table = d.block_table;
+  for (int s = 0; s < d.n_seqs; ++s) {
+    const int32_t first = (int32_t)c->pages[s].size();
+    for (size_t j = 0; j < plan.new_pages[s].size(); ++j) {
+      a.index[a.count] = s * d.max_pages_per_seq + first + (int32_t)j;
+      a.value[a.count] = plan.new_pages[s][j];
+      if (++a.count == kBtBatch) {
+        hipError_t e = launch_bt_update(a, st);
+        if (e != hipSuccess) return e;
+        a.count = 0;
+      }
+    }
+  }
+  return launch_bt_update(a, st);
+}
+
+void commit_append(dflash_cache* c, const std::vector<int64_t>& n, const AppendPlan& plan) {
+  for (int s = 0; s < c->desc.n_seqs; ++s) {
+    c->len[s] += (int32_t)n[s];
+    for (int32_t pg : plan.new_pages[s]) {
+      c->free_pages.erase(pg);
+      c->pages[s].push_back(pg);
+    }
+  }
+}
+
+int check_cu(const int32_t* cu, int n_seqs, std::vector<int64_t>* n) {
+  if (!cu || cu[0] != 0) return DFLASH_ERR_ARG;
+  n->resize(n_seqs);
+  for (int s = 0; s < n_seqs; ++s) {
+    if (cu[s + 1] < cu[s]) return DFLASH_ERR_ARG;
+    (*n)[s] = cu[s + 1] - cu[s];
+  }
+  return DFLASH_OK;
+}
+
+// ---------------------------------------------------------------- layer planning
+
+int check_layer(const dflash_layer_desc* L) {
+  if (!L) return DFLASH_ERR_ARG;
+  if (!dtype_ok(L->dtype)) return DFLASH_ERR_DTYPE;
+  if (L->d <= 0 || L->n_h <= 0 || L->n_kv <= 0 || L->n_h % L->n_kv != 0) return DFLASH_ERR_SHAPE;
+  if (L->d_h != 64 && L->d_h != 128) return DFLASH_ERR_SHAPE;
+  if (L->d % 8 != 0 || L->window < 0 || !(L->eps >= 0.f) || !(L->rope_theta > 0.0)) return DFLASH_ERR_SHAPE;
+  if (!L->w_qkv || !L->w_o || !L->gamma_q || !L->gamma_k) return DFLASH_ERR_ARG;
+  if (!aligned16(L->w_qkv) || !aligned16(L->w_o)) return DFLASH_ERR_ARG;
+  return DFLASH_OK;
+}
+
+struct KvPlan {
+  int64_t R, B, T, RB, qd, kvd, group, qrows;
+  GemmJob gq, gkv, go;
+  size_t off_q, off_pq, off_pkv, off_po, off_pml, off_attn, off_pout, total;
+  int64_t max_items;
+};
+
+KvPlan plan_kv(const dflash_layer_desc* L, const dflash_cache* c, int64_t T, int32_t B) {
+  KvPlan p{};
+  const size_t eb = elem_bytes(L->dtype);
+  p.R = c->desc.n_seqs; p.B = B; p.T = T; p.RB = p.R * B;
+  p.qd = (int64_t)L->n_h * L->d_h;
+  p.kvd = (int64_t)L->n_kv * L->d_h;
+  p.group = L->n_h / L->n_kv;
+  p.qrows = cdiv(p.group * B, 16) * 16;
+  p.gq = make_job(nullptr, 0, nullptr, p.RB, L->w_qkv, p.qd, L->d, eb);
+  p.gkv = make_job(nullptr, T, nullptr, p.RB, nullptr, 2 * p.kvd, L->d, eb);
+  p.go = make_job(nullptr, p.RB, nullptr, 0, L->w_o, L->d, p.qd, eb);
+  p.max_items = kAttnMaxTarget + p.R * L->n_kv;
+  size_t o = 0;
+  p.off_q = o;   o = align_up(o + (size_t)p.R * L->n_kv * p.qrows * L->d_h * eb);
+  p.off_pq = o;  o = align_up(o + job_part_bytes(p.gq));
+  p.off_pkv = o; o = align_up(o + job_part_bytes(p.gkv));
+  p.off_po = o;  o = align_up(o + (size_t)p.max_items * p.qrows * L->d_h * sizeof(float));
+  p.off_pml = o; o = align_up(o + (size_t)p.max_items * 2 * p.qrows * sizeof(float));
+  p.off_attn = o; o = align_up(o + (size_t)p.RB * p.qd * eb);
+  p.off_pout = o; o = align_up(o + job_part_bytes(p.go));
+  p.total = o;
+  return p;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP; }
+
+}  // namespace
+
+// ======================================================================== ABI
+
+extern "C" {
+
+const char* dflash_strerror(int status) {
+  switch (status) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_ERR_ARG: return "invalid argument (null/misaligned pointer, bad handle or offsets)";
+    case DFLASH_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case DFLASH_ERR_DTYPE: return "unsupported dtype or dtype mismatch";
+    case DFLASH_ERR_RANGE: return "crop length outside [0, current length]";
+    case DFLASH_ERR_CAPACITY: return "cache capacity, page table or page pool exhausted";
+    case DFLASH_ERR_HIP: return "HIP runtime error";
+    case DFLASH_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+int dflash_cache_init(dflash_cache** out, const dflash_cache_desc* desc) {
+  if (!out || !desc) return DFLASH_ERR_ARG;
+  const auto& d = *desc;
+  if (!dtype_ok(d.dtype)) return DFLASH_ERR_DTYPE;
+  if (d.n_seqs < 1 || d.n_seqs > DFLASH_MAX_SEQS || d.n_kv < 1 || d.d_h < 8 || d.d_h % 8 != 0)
+    return DFLASH_ERR_SHAPE;
+  if (d.page_size < 0 || d.page_size % DFLASH_KEY_ALIGN != 0 || d.capacity <= 0) return DFLASH_ERR_SHAPE;
+  if (d.page_size == 0 && (d.capacity % DFLASH_KEY_ALIGN != 0 || d.capacity > (int64_t)1 << 30))
+    return DFLASH_ERR_SHAPE;
+  if (d.page_size > 0 && (d.max_pages_per_seq < 1 || d.capacity > (int64_t)1 << 30)) return DFLASH_ERR_SHAPE;
+  if (!d.k_pool || !d.v_pool || !aligned16(d.k_pool) || !aligned16(d.v_pool)) return DFLASH_ERR_ARG;
+  if (d.page_size > 0 && (!d.block_table || (reinterpret_cast<uintptr_t>(d.block_table) & 3)))
+    return DFLASH_ERR_ARG;
+  auto* c = new dflash_cache;
+  c->desc = d;
+  c->len.assign(d.n_seqs, 0);
+  c->pages.assign(d.n_seqs, {});
+  if (d.page_size > 0)
+    for (int64_t i = 0; i < d.capacity; ++i) c->free_pages.insert(c->free_pages.end(), (int32_t)i);
+  *out = c;
+  return DFLASH_OK;
+}
+
+int dflash_cache_destroy(dflash_cache* c) {
+  if (!c) return DFLASH_ERR_ARG;
+  delete c;
+  return DFLASH_OK;
+}
+
+int dflash_cache_lengths(const dflash_cache* c, int32_t* host_len) {
+  if (!c || !host_len) return DFLASH_ERR_ARG;
+  std::copy(c->len.begin(), c->len.end(), host_len);
+  return DFLASH_OK;
+}
+
+int dflash_cache_block_table(const dflash_cache* c, int32_t* t) {
+  if (!c || !t) return DFLASH_ERR_ARG;
+  const int mp = c->desc.page_size > 0 ? c->desc.max_pages_per_seq : 1;
+  for (int s = 0; s < c->desc.n_seqs; ++s)
+    for (int j = 0; j < mp; ++j) {
+      int32_t v = -1;
+      if (c->desc.page_size == 0) v = j == 0 ? s : -1;
+      else if (j < (int)c->pages[s].size()) v = c->pages[s][j];
+      t[s * mp + j] = v;
+    }
+  return DFLASH_OK;
+}
+
+int64_t dflash_cache_free_pages(const dflash_cache* c) {
+  if (!c) return DFLASH_ERR_ARG;
+  return (int64_t)c->free_pages.size();
+}
+
+int dflash_cache_append(dflash_cache* c, const int32_t* cu_rows, const void* k_rows, const void* v_rows,
+                        void* stream) {
+  if (!c) return DFLASH_ERR_ARG;
+  std::vector<int64_t> n;
+  int st = check_cu(cu_rows, c->desc.n_seqs, &n);
+  if (st) return st;
+  const int64_t n_rows = cu_rows[c->desc.n_seqs];
+  if (n_rows > 0 && (!k_rows || !v_rows || !aligned16(k_rows) || !aligned16(v_rows))) return DFLASH_ERR_ARG;
+  AppendPlan plan;
+  st = plan_append(c, n, &plan);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = enqueue_page_table(c, plan, s);
+  if (e == hipSuccess && n_rows > 0) {
+    AppendArgs a{};
+    a.k_rows = k_rows;
+    a.v_rows = v_rows;
+    a.cache = view_of(c);
+    // the kernel sees the page table including this call's new pages
+    a.n_seqs = c->desc.n_seqs;
+    for (int i = 0; i < c->desc.n_seqs; ++i) a.L[i] = c->len[i];
+    for (int i = 0; i <= c->desc.n_seqs; ++i) a.cu[i] = cu_rows[i];
+    e = launch_cache_append(c->desc.dtype, a, n_rows, s);
+  }
+  if (e != hipSuccess) return DFLASH_ERR_HIP;
+  commit_append(c, n, plan);
+  return DFLASH_OK;
+}
+
+int dflash_cache_crop(dflash_cache* c, const int32_t* new_len, void* /*stream*/) {
+  if (!c || !new_len) return DFLASH_ERR_ARG;
+  for (int s = 0; s < c->desc.n_seqs; ++s)
+    if (new_len[s] < 0 || new_len[s] > c->len[s]) return DFLASH_ERR_RANGE;
+  for (int s = 0; s < c->desc.n_seqs; ++s) {
+    c->len[s] = new_len[s];
+    if (c->desc.page_size > 0) {
+      const size_t keep = (size_t)cdiv(new_len[s], c->desc.page_size);
+      for (size_t j = keep; j < c->pages[s].size(); ++j) c->free_pages.insert(c->pages[s][j]);
+      c->pages[s].resize(std::min(keep, c->pages[s].size()));
+    }
+  }
+  return DFLASH_OK;
+}
+
+size_t dflash_ctx_project_ws_bytes(int64_t T, int64_t kd, int64_t d, int32_t dtype) {
+  if (T <= 0 || kd <= 0 || d <= 0 || !dtype_ok(dtype)) return 0;
+  GemmJob j = make_job(nullptr, T, nullptr, 0, nullptr, d, kd, elem_bytes(dtype));
+  return align_up(job_part_bytes(j)) + align_up((size_t)T * d * sizeof(float));
+}
+
+int dflash_ctx_project(const void* x_raw, int64_t T, int64_t kd, const void* w_fc, const void* gamma_h,
+                       int64_t d, float eps, int32_t dtype, void* c_out, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (!dtype_ok(dtype)) return DFLASH_ERR_DTYPE;
+  if (T < 0 || kd <= 0 || d <= 0 || kd % 8 != 0 || d % 8 != 0 || kd > INT32_MAX / 2 || d > INT32_MAX / 2 ||
+      T > INT32_MAX / 2 || !(eps >= 0.f))
+    return DFLASH_ERR_SHAPE;
+  if (T == 0) return DFLASH_OK;
+  if (!x_raw || !w_fc || !gamma_h || !c_out || !ws) return DFLASH_ERR_ARG;
+  if (!aligned16(x_raw) || !aligned16(w_fc) || !aligned16(c_out) || !aligned16(ws)) return DFLASH_ERR_ARG;
+  if (ws_bytes < dflash_ctx_project_ws_bytes(T, kd, d, dtype)) return DFLASH_ERR_WORKSPACE;
+  const size_t eb = elem_bytes(dtype);
+  GemmJob j = make_job(x_raw, T, nullptr, 0, w_fc, d, kd, eb);
+  j.part = static_cast<float*>(ws);
+  float* u = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(job_part_bytes(j)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = run_gemms(dtype, {j}, s);
+  const float* src = j.part;
+  if (e == hipSuccess && j.plan.splits > 1) {
+    e = launch_splitk_reduce(DFLASH_F32, j.part, j.plan.splits, T, d, u, s);
+    src = u;
+  }
+  if (e == hipSuccess) e = launch_rmsnorm_rows(dtype, src, T, d, gamma_h, eps, c_out, s);
+  return hip_status(e);
+}
+
+size_t dflash_kv_inject_attn_ws_bytes(const dflash_layer_desc* L, const dflash_cache* c, int64_t T, int32_t B) {
+  if (check_layer(L) != DFLASH_OK || !c || T < 0 || B < 1) return 0;
+  return plan_kv(L, c, T, B).total;
+}
+
+int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const void* C, const int32_t* cu_ctx,
+                          const void* H, int32_t B, void* out, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_layer(L);
+  if (st) return st;
+  if (!c) return DFLASH_ERR_ARG;
+  const auto& cd = c->desc;
+  if (cd.dtype != L->dtype) return DFLASH_ERR_DTYPE;
+  if (cd.n_kv != L->n_kv || cd.d_h != L->d_h) return DFLASH_ERR_SHAPE;
+  if (B < 1 || (int64_t)(L->n_h / L->n_kv) * B > DFLASH_MAX_GROUP_ROWS) return DFLASH_ERR_SHAPE;
+  std::vector<int64_t> n;
+  st = check_cu(cu_ctx, cd.n_seqs, &n);
+  if (st) return st;
+  const int64_t T = cu_ctx[cd.n_seqs];
+  if (T > 0 && (!C || !aligned16(C))) return DFLASH_ERR_ARG;
+  if (!H || !out || !ws || !aligned16(H) || !aligned16(out) || !aligned16(ws)) return DFLASH_ERR_ARG;
+  const KvPlan p = plan_kv(L, c, T, B);
+  if (ws_bytes < p.total) return DFLASH_ERR_WORKSPACE;
+  std::vector<int64_t> rows(cd.n_seqs);
+  for (int s = 0; s < cd.n_seqs; ++s) rows[s] = n[s] + B;
+  AppendPlan ap;
+  st = plan_append(c, rows, &ap);
+  if (st) return st;
+
+  const int32_t dt = L->dtype;
+  const int R = cd.n_seqs;
+  char* w = static_cast<char*>(ws);
+  void* q_ws = w + p.off_q;
+  float* part_q = reinterpret_cast<float*>(w + p.off_pq);
+  float* part_kv = reinterpret_cast<float*>(w + p.off_pkv);
+  float* part_o = reinterpret_cast<float*>(w + p.off_po);
+  float* part_ml = reinterpret_cast<float*>(w + p.off_pml);
+  void* attn = w + p.off_attn;
+  float* part_out = reinterpret_cast<float*>(w + p.off_pout);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t eb = elem_bytes(dt);
+
+  // 1. page table entries for the rows this call appends
+  hipError_t e = enqueue_page_table(c, ap, s);
+
+  // 2. q/k/v projection: Q from the block rows, K/V from [C; H] with one weight
+  GemmJob gq = p.gq, gkv = p.gkv;
+  gq.x1 = H; gq.part = part_q;
+  gkv.x0 = C; gkv.x1 = H; gkv.part = part_kv;
+  gkv.w = static_cast<const char*>(L->w_qkv) + (size_t)p.qd * L->d * eb;
+  if (e == hipSuccess) e = run_gemms(dt, {gq, gkv}, s);
+
+  // 3. norms, RoPE, Q to the workspace, K/V into the cache
+  CacheView cv = view_of(c);
+  if (e == hipSuccess) {
+    QkvEpiArgs a{};
+    a.part_q = part_q; a.part_kv = part_kv;
+    a.sq = gq.plan.splits; a.skv = gkv.plan.splits;
+    a.gamma_q = L->gamma_q; a.gamma_k = L->gamma_k;
+    a.q_ws = q_ws;
+    a.cache = cv;
+    a.R = R; a.B = B; a.T = (int32_t)T; a.n_h = L->n_h; a.n_kv = L->n_kv; a.d_h = L->d_h;
+    a.qrows = (int32_t)p.qrows;
+    a.eps = L->eps;
+    for (int i = 0; i < L->d_h / 2; ++i) a.inv_freq[i] = std::pow(L->rope_theta, -2.0 * i / L->d_h);
+    for (int r = 0; r < R; ++r) { a.seq.L[r] = c->len[r]; a.seq.n[r] = (int32_t)n[r]; }
+    for (int r = 0; r <= R; ++r) a.seq.cu[r] = cu_ctx[r];
+    e = launch_qkv_epilogue(dt, a, s);
+  }
+
+  // 4. attention over every cached key, split into chunks
+  AttnArgs aa{};
+  if (e == hipSuccess) {
+    aa.q_ws = q_ws; aa.cache = cv; aa.part_o = part_o; aa.part_ml = part_ml;
+    aa.R = R; aa.B = B; aa.n_kv = L->n_kv; aa.group = (int32_t)p.group; aa.qrows = (int32_t)p.qrows;
+    aa.d_h = L->d_h; aa.window = L->window;
+    aa.scale_log2 = (float)(1.0 / std::sqrt((double)L->d_h) * 1.4426950408889634);
+    int64_t total = 0;
+    std::vector<int64_t> keys(R);
+    for (int r = 0; r < R; ++r) {
+      const int64_t hi = c->len[r] + n[r] + B;
+      const int64_t lo = L->window > 0 ? std::max<int64_t>(0, c->len[r] + n[r] - L->window + 1) : 0;
+      aa.key_hi[r] = (int32_t)hi;
+      aa.key_lo[r] = (int32_t)lo;
+      aa.qpos0[r] = (int32_t)(c->len[r] + n[r]);
+      keys[r] = hi - (lo & ~int64_t(31));
+      total += keys[r] * L->n_kv;
+    }
+    int64_t chunk = cdiv(cdiv(total, attn_target_items()), 128) * 128;
+    chunk = std::max<int64_t>(chunk, 128);
+    aa.chunk_keys = (int32_t)chunk;
+    int64_t items = 0;
+    for (int r = 0; r < R; ++r) {
+      aa.item_base[r] = (int32_t)items;
+      aa.chunks[r] = (int32_t)std::max<int64_t>(1, cdiv(keys[r], chunk));
+      items += (int64_t)aa.chunks[r] * L->n_kv;
+    }
+    aa.item_base[R] = (int32_t)items;
+    if (items > p.max_items) e = hipErrorInvalidValue;  // cannot happen: bounded by construction
+    if (e == hipSuccess) e = launch_attn_split(dt, aa, (int)items, s);
+    if (e == hipSuccess) {
+      CombineArgs ca{};
+      ca.part_o = part_o; ca.part_ml = part_ml; ca.attn = attn;
+      ca.R = R; ca.B = B; ca.n_kv = L->n_kv; ca.group = (int32_t)p.group; ca.qrows = (int32_t)p.qrows;
+      ca.d_h = L->d_h;
+      for (int r = 0; r <= R; ++r) ca.item_base[r] = aa.item_base[r];
+      for (int r = 0; r < R; ++r) ca.chunks[r] = aa.chunks[r];
+      e = launch_attn_combine(dt, ca, s);
+    }
+  }
+
+  // 5. o_proj
+  GemmJob go = p.go;
+  go.x0 = attn; go.part = part_out;
+  if (e == hipSuccess) e = run_gemms(dt, {go}, s);
+  if (e == hipSuccess) e = launch_splitk_reduce(dt, part_out, go.plan.splits, p.RB, L->d, out, s);
+  if (e != hipSuccess) return DFLASH_ERR_HIP;
+  commit_append(c, rows, ap);
+  return DFLASH_OK;
+}
+
+}  // extern "C"

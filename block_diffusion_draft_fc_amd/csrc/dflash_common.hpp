@@ -1,0 +1,97 @@
+// Shared device-side definitions for the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(8 * sizeof(float)))) float f32x8;
+
+namespace dflash {
+
+constexpr int kWave = 64;
+
+// Eight consecutive elements of the storage type, the per-lane operand of one
+// K=32 matrix step (16 bytes for bf16, 32 bytes for fp32).
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16> { using type = bf16x8; };
+template <> struct Vec8<float> { using type = f32x8; };
+template <typename T> using vec8_t = typename Vec8<T>::type;
+
+__device__ __forceinline__ bf16x8 load8(const bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ f32x8 load8(const float* p) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ void store8(bf16* p, bf16x8 v) { *reinterpret_cast<bf16x8*>(p) = v; }
+__device__ __forceinline__ void store8(float* p, f32x8 v) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+template <typename T> __device__ __forceinline__ vec8_t<T> zero8() { return vec8_t<T>{}; }
+
+template <typename T> __device__ __forceinline__ float to_f32(T x) { return static_cast<float>(x); }
+template <typename T> __device__ __forceinline__ T from_f32(float x) { return static_cast<T>(x); }
+
+__device__ __forceinline__ bf16x8 cvt8_bf16(f32x8 v) { return __builtin_convertvector(v, bf16x8); }
+template <typename T> __device__ __forceinline__ vec8_t<T> cvt8(f32x8 v);
+template <> __device__ __forceinline__ bf16x8 cvt8<bf16>(f32x8 v) { return cvt8_bf16(v); }
+template <> __device__ __forceinline__ f32x8 cvt8<float>(f32x8 v) { return v; }
+
+// One K=32 step of a 16x16 fp32-accumulating matrix product.
+// Operand order (both A and B): lane l holds row/column l % 16 and the eight
+// k-values 8*(l/16) .. 8*(l/16)+7 of the step.  Result: lane l holds column
+// l % 16, rows 4*(l/16) .. 4*(l/16)+3.
+__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// fp32 inputs: eight 16x16x4 steps.  Step e takes element e of every lane, i.e.
+// k-value 8*(l/16)+e for the lane group l/16 - the same k on both operands, so
+// the eight steps together cover the 32 k-values exactly once.
+__device__ __forceinline__ f32x4 mma32(f32x8 a, f32x8 b, f32x4 c) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
+  return c;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Cache addressing shared by the append paths and the attention kernel.
+// Contiguous caches are the special case of one "page" of `rows` slots per
+// sequence whose physical index is the sequence index.
+struct CacheView {
+  void* k_pool;
+  void* v_pool;
+  const int32_t* block_table;  // nullptr for contiguous
+  int32_t page_rows;           // page_size, or the capacity of a contiguous cache
+  int32_t max_pages;           // page-table row length
+  int32_t n_kv, d_h;
+};
+
+__device__ __forceinline__ int64_t cache_page(const CacheView& c, int seq, int pos) {
+  if (c.block_table == nullptr) return seq;
+  return c.block_table[(int64_t)seq * c.max_pages + pos / c.page_rows];
+}
+// Element offset of K[seq][g][pos][0].
+__device__ __forceinline__ int64_t k_offset(const CacheView& c, int64_t page, int g, int slot) {
+  return ((page * c.n_kv + g) * (int64_t)c.page_rows + slot) * c.d_h;
+}
+// Element offset of V^T[seq][g][0][pos] (V rows stored key-minor).
+__device__ __forceinline__ int64_t v_offset(const CacheView& c, int64_t page, int g, int slot) {
+  return (page * c.n_kv + g) * (int64_t)c.d_h * c.page_rows + slot;
+}
+
+}  // namespace dflash

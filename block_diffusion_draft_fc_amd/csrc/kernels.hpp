@@ -1,0 +1,120 @@
+// Launch interface between the C-ABI host layer and the gfx950 kernels.
+// Every struct here is passed by value as a kernel argument.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dflash_common.hpp"
+
+namespace dflash {
+
+constexpr int kMaxSeqs = 64;
+
+// ---------------------------------------------------------------- GEMM
+// part[s][row_off + m][n] = sum over k in split s of A[m][k] * W[n][k], for the
+// rows m of a virtual concatenation: m < m0 from x0, m0 <= m < m0 + m1 from x1
+// (row stride K for both).  The partial buffer holds m_out rows per split.
+struct GemmProb {
+  const void* x0;
+  const void* x1;
+  const void* w;
+  float* part;
+  int32_t m0, m1;
+  int32_t row_off, m_out;
+  int32_t N, K;
+  int32_t k_chunk;   // K per split, multiple of 256
+  int32_t splits;
+  int32_t mt;        // 16-row tiles: ceil((m0 + m1) / 16)
+  int32_t n_tiles;   // ceil(N / 64)
+  int32_t blocks;    // n_tiles * splits
+};
+struct GemmArgs {
+  GemmProb p[2];
+  int32_t nprob;
+};
+// Rows handled by one weight-streaming problem.
+constexpr int kSkinnyMaxM = 64;
+// LDS budget for the staged activation slice of one workgroup.
+constexpr int kSkinnyLdsBytes = 64 * 1024;
+
+hipError_t launch_gemm_skinny(int dtype, const GemmArgs& a, int max_mt, size_t lds_bytes,
+                              hipStream_t s);
+
+// out[m][n] = sum_s part[s][m][n], written as fp32 (out_dtype 0) or bf16 (1).
+hipError_t launch_splitk_reduce(int out_dtype, const float* part, int splits, int64_t M,
+                                int64_t N, void* out, hipStream_t s);
+
+// C[t] = u[t] / sqrt(mean(u[t]^2) + eps) * gamma, one row of d per workgroup.
+hipError_t launch_rmsnorm_rows(int dtype, const float* u, int64_t T, int64_t d,
+                               const void* gamma, float eps, void* out, hipStream_t s);
+
+// ---------------------------------------------------------------- QKV epilogue
+struct SeqTable {
+  int32_t L[kMaxSeqs];       // cache length before the call
+  int32_t n[kMaxSeqs];       // new context rows
+  int32_t cu[kMaxSeqs + 1];  // context row offsets
+};
+struct QkvEpiArgs {
+  const float* part_q;   // [sq][R*B][n_h*d_h]
+  const float* part_kv;  // [skv][T + R*B][2*n_kv*d_h]
+  int32_t sq, skv;
+  const void* gamma_q;
+  const void* gamma_k;
+  void* q_ws;            // [R][n_kv][qrows][d_h]
+  CacheView cache;
+  int32_t R, B, T, n_h, n_kv, d_h, qrows;
+  float eps;
+  double inv_freq[64];   // RoPE w_i, i < d_h/2, computed in fp64 on the host
+  SeqTable seq;
+};
+hipError_t launch_qkv_epilogue(int dtype, const QkvEpiArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+  const void* q_ws;      // [R][n_kv][qrows][d_h]
+  CacheView cache;
+  float* part_o;         // [items][qrows][d_h]
+  float* part_ml;        // [items][2][qrows]
+  int32_t R, B, n_kv, group, qrows, d_h;
+  int32_t chunk_keys;    // keys per work item (multiple of 32)
+  int32_t window;
+  float scale_log2;      // d_h^-0.5 * log2(e)
+  int32_t item_base[kMaxSeqs + 1];  // items of sequence r: [item_base[r], item_base[r+1])
+  int32_t chunks[kMaxSeqs];         // items per (sequence, K/V head)
+  int32_t key_lo[kMaxSeqs];         // first key any query may see
+  int32_t key_hi[kMaxSeqs];         // keys in the cache after the append
+  int32_t qpos0[kMaxSeqs];          // position of block row 0
+};
+hipError_t launch_attn_split(int dtype, const AttnArgs& a, int items, hipStream_t s);
+
+struct CombineArgs {
+  const float* part_o;
+  const float* part_ml;
+  void* attn;            // [R*B][n_h*d_h]
+  int32_t R, B, n_kv, group, qrows, d_h;
+  int32_t item_base[kMaxSeqs + 1];
+  int32_t chunks[kMaxSeqs];
+};
+hipError_t launch_attn_combine(int dtype, const CombineArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- cache
+struct AppendArgs {
+  const void* k_rows;    // [n_rows][n_kv][d_h]
+  const void* v_rows;
+  CacheView cache;
+  int32_t n_seqs;
+  int32_t L[kMaxSeqs];
+  int32_t cu[kMaxSeqs + 1];
+};
+hipError_t launch_cache_append(int dtype, const AppendArgs& a, int64_t n_rows, hipStream_t s);
+
+constexpr int kBtBatch = 240;
+struct BtUpdateArgs {
+  int32_t* table;
+  int32_t count;
+  int32_t index[kBtBatch];
+  int32_t value[kBtBatch];
+};
+hipError_t launch_bt_update(const BtUpdateArgs& a, hipStream_t s);
+
+}  // namespace dflash

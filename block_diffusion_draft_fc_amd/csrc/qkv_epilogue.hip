@@ -1,0 +1,123 @@
+// Epilogue of the fused q/k/v projection: split-K reduction, per-head RMSNorm
+// on Q and K, rotary embedding, and the stores (Q to the workspace in GQA
+// order, K and V straight into the draft cache).
+//
+//   per-head norms: "DFlash源码导读二 Qwen3DFlashAttention注意力实现全解析" section 1
+//     (q_norm / k_norm over head_dim); V is not normed ("DFlash KV Injection
+//     Walkthrough" Step 4.2).
+//   rotary window: Step 4.3 of the walkthrough and section 3 of the article: the
+//     n + B new K rows take positions L .. L+n+B-1 (context rows first), the B
+//     queries the last B of them; pairs are (i, i + d_h/2) as in rotate_half.
+//   cache write: section 4 of the article, the rows enter the cache after the
+//     norm and the rotation.
+//
+// One wavefront per (row, head); lane l < d_h/2 owns the rotation pair
+// (l, l + d_h/2).  Angles p * w_i are formed and reduced in fp64 (positions go
+// past 3e4, where an fp32 angle is off by ~1e-3 rad), then rounded to fp32.
+#include "kernels.hpp"
+
+namespace dflash {
+
+template <typename T>
+__global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvEpiArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int RB = a.R * a.B;
+  const int Mkv = a.T + RB;
+  const int half = a.d_h >> 1;
+  const int qd = a.n_h * a.d_h, kvd = a.n_kv * a.d_h;
+  const int64_t n_q_items = (int64_t)RB * a.n_h;
+  const int64_t n_kv_items = (int64_t)Mkv * a.n_kv;
+  if (item >= n_q_items + 2 * n_kv_items) return;
+
+  int kind;   // 0 = Q, 1 = K, 2 = V
+  int m, head;
+  if (item < n_q_items) {
+    kind = 0; m = (int)(item / a.n_h); head = (int)(item % a.n_h);
+  } else {
+    const int64_t k = item - n_q_items;
+    kind = k < n_kv_items ? 1 : 2;
+    const int64_t kk = kind == 1 ? k : k - n_kv_items;
+    m = (int)(kk / a.n_kv); head = (int)(kk % a.n_kv);
+  }
+
+  // split-K reduction of the two elements of this lane's rotation pair
+  const float* part;
+  int splits, width, col;
+  int64_t stride;
+  if (kind == 0) { part = a.part_q; splits = a.sq; width = qd; col = head * a.d_h; stride = (int64_t)RB * qd; }
+  else { part = a.part_kv; splits = a.skv; width = 2 * kvd; col = (kind == 2 ? kvd : 0) + head * a.d_h;
+         stride = (int64_t)Mkv * 2 * kvd; }
+  const bool act = lane < half;
+  float x0 = 0.f, x1 = 0.f;
+  if (act) {
+    const float* src = part + (int64_t)m * width + col + lane;
+    for (int s = 0; s < splits; ++s) { x0 += src[s * stride]; x1 += src[s * stride + half]; }
+  }
+
+  // sequence and position of this row
+  int r, pos;
+  if (kind == 0) {
+    r = m / a.B;
+    pos = a.seq.L[r] + a.seq.n[r] + (m - r * a.B);
+  } else if (m < a.T) {
+    r = 0;
+    while (r + 1 < a.R && m >= a.seq.cu[r + 1]) ++r;
+    pos = a.seq.L[r] + (m - a.seq.cu[r]);
+  } else {
+    const int bm = m - a.T;
+    r = bm / a.B;
+    pos = a.seq.L[r] + a.seq.n[r] + (bm - r * a.B);
+  }
+
+  if (kind != 2) {
+    const T* gam = static_cast<const T*>(kind == 0 ? a.gamma_q : a.gamma_k);
+    const float ss = wave_sum(x0 * x0 + x1 * x1);
+    const float rr = 1.0f / sqrtf(ss / (float)a.d_h + a.eps);
+    if (act) {
+      x0 = x0 * rr * to_f32(gam[lane]);
+      x1 = x1 * rr * to_f32(gam[lane + half]);
+      double sn, cs;
+      sincos((double)pos * a.inv_freq[lane], &sn, &cs);
+      const float c = (float)cs, sv = (float)sn;
+      const float y0 = x0 * c - x1 * sv;
+      const float y1 = x1 * c + x0 * sv;
+      x0 = y0; x1 = y1;
+    }
+  }
+  if (!act) return;
+
+  if (kind == 0) {
+    const int b = m - r * a.B;
+    const int group = a.n_h / a.n_kv;
+    const int g = head / group, hl = head - g * group;
+    T* dst = static_cast<T*>(a.q_ws) + (((int64_t)r * a.n_kv + g) * a.qrows + hl * a.B + b) * a.d_h;
+    dst[lane] = from_f32<T>(x0);
+    dst[lane + half] = from_f32<T>(x1);
+  } else {
+    const int64_t page = cache_page(a.cache, r, pos);
+    const int slot = pos % a.cache.page_rows;
+    if (kind == 1) {
+      T* dst = static_cast<T*>(a.cache.k_pool) + k_offset(a.cache, page, head, slot);
+      dst[lane] = from_f32<T>(x0);
+      dst[lane + half] = from_f32<T>(x1);
+    } else {
+      T* dst = static_cast<T*>(a.cache.v_pool) + v_offset(a.cache, page, head, slot);
+      dst[(int64_t)lane * a.cache.page_rows] = from_f32<T>(x0);
+      dst[(int64_t)(lane + half) * a.cache.page_rows] = from_f32<T>(x1);
+    }
+  }
+}
+
+hipError_t launch_qkv_epilogue(int dtype, const QkvEpiArgs& a, hipStream_t s) {
+  const int64_t items = (int64_t)a.R * a.B * a.n_h + 2 * (int64_t)(a.T + a.R * a.B) * a.n_kv;
+  if (items == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((items + 3) / 4);
+  if (dtype == 1)
+    hipLaunchKernelGGL(qkv_epilogue_kernel<bf16>, dim3(blocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(qkv_epilogue_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace dflash

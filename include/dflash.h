@@ -1,0 +1,188 @@
+/*
+ * dflash.h - C ABI of the DFlash KV-injection attention library (gfx950).
+ *
+ * The layer (sources cited by page title and section):
+ *   "DFlash KV Injection Walkthrough", Step 2: the k concatenated target-layer
+ *     hidden states of each position go through fc (no bias) and an RMSNorm,
+ *     giving the context C shared by every draft layer.
+ *   Same page, Step 4.1-4.5, and "DFlash源码导读二 Qwen3DFlashAttention注意力实现全解析"
+ *     sections 1-5: Q from the block rows H only; K = k_proj([C; H]),
+ *     V = v_proj([C; H]) with one weight for both streams; per-head RMSNorm on
+ *     Q and K; RoPE over one window of positions with the queries on its last
+ *     B positions; non-causal GQA attention with scale d_h^-0.5 over the draft
+ *     KV cache; o_proj.
+ *   Same article, section 4: the round's rows are written into the draft cache,
+ *     which is later cut back to the accepted prefix.
+ *   "KV Cache + Speculative Decoding 面试 Cheat Sheet", sections 5.2-5.3, 6.2:
+ *     fixed-size pages, per-request page tables, a free list.
+ *
+ * Conventions for every entry point:
+ *   - Returns DFLASH_OK (0) or a negative dflash_status; never throws.
+ *   - Device pointers are caller-owned device memory; host pointers are read
+ *     during the call only.  The library allocates no device memory and never
+ *     frees caller memory.  Device pointers must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     asynchronously on it; no call synchronises the device.
+ *   - All arguments are validated on the host before anything is enqueued, so
+ *     a call that returns an error has changed no state.
+ *   - Storage dtype is DFLASH_F32 or DFLASH_BF16 for every tensor of a call;
+ *     accumulation is always fp32.  Matrices are row-major, innermost
+ *     dimension contiguous.
+ *   - A cache handle is used from one stream at a time.  Calls that overlap on
+ *     one workspace race.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DFLASH_OK = 0,
+  DFLASH_ERR_ARG = -1,       /* null / misaligned pointer, bad handle, bad cu array */
+  DFLASH_ERR_SHAPE = -2,     /* unsupported or inconsistent sizes */
+  DFLASH_ERR_DTYPE = -3,     /* dtype not F32/BF16 or not matching the cache */
+  DFLASH_ERR_RANGE = -4,     /* crop to a length outside [0, current length] */
+  DFLASH_ERR_CAPACITY = -5,  /* sequence capacity, page table or page pool exhausted */
+  DFLASH_ERR_HIP = -6,       /* a HIP runtime call or kernel launch failed */
+  DFLASH_ERR_WORKSPACE = -7  /* workspace smaller than the *_ws_bytes figure */
+} dflash_status;
+
+typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
+
+/* Limits of this build. */
+#define DFLASH_MAX_SEQS 64        /* requests per cache handle */
+#define DFLASH_MAX_GROUP_ROWS 64  /* (n_h / n_kv) * B query rows per K/V head */
+#define DFLASH_KEY_ALIGN 64       /* contiguous capacity and page size are multiples of this */
+
+/* ------------------------------------------------------------------------
+ * One KV-injection attention layer.  All weight pointers are device memory in
+ * the layer dtype.
+ *   w_qkv   [(n_h + 2*n_kv) * d_h, d]: rows W_Q (n_h*d_h) | W_K | W_V, each
+ *           stored output x input; row h*d_h + i is output i of head h.
+ *   w_o     [d, n_h * d_h], output x input (input column h*d_h + i = head h).
+ *   gamma_q, gamma_k [d_h]: per-head RMSNorm gains shared by all heads.
+ * Shapes: n_h % n_kv == 0, d_h in {64, 128}, (n_h/n_kv)*B <= 64, d % 8 == 0.
+ * window 0 = full attention; window > 0 = sliding layer where query position
+ * p sees key position j iff p - j < window (no upper bound).
+ * ---------------------------------------------------------------------- */
+typedef struct dflash_layer_desc {
+  int32_t d, n_h, n_kv, d_h;
+  float eps;            /* RMSNorm epsilon (Q/K norms) */
+  double rope_theta;    /* RoPE base; w_i = theta^(-2i/d_h) */
+  int32_t window;
+  int32_t dtype;        /* dflash_dtype */
+  const void *w_qkv;
+  const void *w_o;
+  const void *gamma_q;
+  const void *gamma_k;
+} dflash_layer_desc;
+
+/* ------------------------------------------------------------------------
+ * Draft KV cache.  Pools and the page table are caller-owned device buffers;
+ * the handle owns host metadata only (lengths, page lists, free list).
+ *
+ * contiguous (page_size == 0): capacity = rows per sequence (multiple of 64)
+ *     K pool [n_seqs][n_kv][capacity][d_h]
+ *     V pool [n_seqs][n_kv][d_h][capacity]     (V stored key-minor)
+ * paged (page_size > 0, multiple of 64): capacity = pages in the pool
+ *     K pool [capacity][n_kv][page_size][d_h]
+ *     V pool [capacity][n_kv][d_h][page_size]
+ *     block_table [n_seqs][max_pages_per_seq] int32, device; entry (s, j) is the
+ *     physical page of logical page j of sequence s, valid for
+ *     j < ceil(len_s / page_size) (other entries are left as they were).
+ * Row `pos` of sequence s sits in logical page pos / page_size, slot
+ * pos % page_size.  K rows hold post-norm post-RoPE keys; V rows raw values.
+ * Allocation takes the lowest-numbered free page, sequences in index order,
+ * each sequence's logical pages in order.  Crop returns every page at or
+ * beyond ceil(new_len / page_size) to the free list.
+ * ---------------------------------------------------------------------- */
+typedef struct dflash_cache_desc {
+  int32_t n_seqs, n_kv, d_h;
+  int32_t dtype;
+  int32_t page_size;
+  int32_t max_pages_per_seq;   /* paged only */
+  int64_t capacity;
+  void *k_pool;
+  void *v_pool;
+  int32_t *block_table;        /* paged only, device */
+} dflash_cache_desc;
+
+typedef struct dflash_cache dflash_cache;
+
+/* Create a handle with every sequence empty.  The pools are not touched. */
+int dflash_cache_init(dflash_cache **out, const dflash_cache_desc *desc);
+int dflash_cache_destroy(dflash_cache *c);
+/* Host copies of the metadata (no device access, no synchronisation). */
+int dflash_cache_lengths(const dflash_cache *c, int32_t *host_len /* [n_seqs] */);
+/* [n_seqs][max_pages_per_seq], -1 where no page is mapped; contiguous caches
+ * report entry (s, 0) = s. */
+int dflash_cache_block_table(const dflash_cache *c, int32_t *host_table);
+int64_t dflash_cache_free_pages(const dflash_cache *c);
+
+/* ------------------------------------------------------------------------
+ * Context projection ("DFlash KV Injection Walkthrough", Step 2):
+ *   C[t] = RMSNorm(X_raw[t] . W_fc^T) * gamma_h,  RMSNorm over d.
+ *   x_raw   [T, kd] device (each row = k layer vectors in layer order)
+ *   w_fc    [d, kd] device (output x input; no bias)
+ *   gamma_h [d] device
+ *   c_out   [T, d] device, written in `dtype`
+ *   ws      device workspace of at least dflash_ctx_project_ws_bytes(...)
+ * T == 0 is a no-op.  kd % 8 == 0, d % 8 == 0.
+ * ---------------------------------------------------------------------- */
+size_t dflash_ctx_project_ws_bytes(int64_t T, int64_t kd, int64_t d, int32_t dtype);
+int dflash_ctx_project(const void *x_raw, int64_t T, int64_t kd, const void *w_fc,
+                       const void *gamma_h, int64_t d, float eps, int32_t dtype,
+                       void *c_out, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Raw append ("DFlash源码导读二 ..." section 4, the cache update): rows
+ * [cu_rows[s], cu_rows[s+1]) of k_rows / v_rows [n_rows, n_kv, d_h] (device,
+ * cache dtype) land at positions len_s .. len_s + n_s - 1 of sequence s, then
+ * len_s += n_s.  cu_rows is a host array [n_seqs + 1], non-decreasing from 0.
+ * Bytes are copied unchanged.  Capacity, page-table or pool overflow ->
+ * DFLASH_ERR_CAPACITY with nothing written.
+ * ---------------------------------------------------------------------- */
+int dflash_cache_append(dflash_cache *c, const int32_t *cu_rows, const void *k_rows,
+                        const void *v_rows, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Crop to the accepted prefix ("DFlash KV Injection Walkthrough", Step 7;
+ * "DFlash源码导读二 ..." section 4): len_s = new_len[s] (host [n_seqs]).
+ * Requires 0 <= new_len[s] <= len_s for every s, else DFLASH_ERR_RANGE and
+ * no change.  Retained rows are untouched.  Host metadata only: nothing is
+ * enqueued on `stream`.
+ * ---------------------------------------------------------------------- */
+int dflash_cache_crop(dflash_cache *c, const int32_t *new_len, void *stream);
+
+/* ------------------------------------------------------------------------
+ * One KV-injection attention layer for every sequence of the cache
+ * ("DFlash KV Injection Walkthrough", Step 4; "DFlash源码导读二 ..." 1-5).
+ *   C      [T, d] device: new context rows, sequence r owns rows
+ *          [cu_ctx[r], cu_ctx[r+1]) (cu_ctx: host [n_seqs + 1]); n_r >= 0.
+ *   H      [n_seqs * B, d] device: block rows, sequence r owns rows r*B .. r*B+B-1.
+ *   out    [n_seqs * B, d] device: o_proj output of the block rows.
+ * For each sequence r with cache length L_r: the n_r + B new K/V rows get RoPE
+ * positions L_r .. L_r+n_r+B-1 (context rows first), the queries the last B of
+ * them; all n_r + B rows are appended (len_r = L_r + n_r + B), then the
+ * queries attend over all len_r keys.  The caller crops afterwards (to
+ * L_r + n_r to keep the accepted context).  Needs ws of at least
+ * dflash_kv_inject_attn_ws_bytes(L, cache, T, B) bytes; the figure depends on
+ * T, B and the handle's sizes, not on the current lengths.
+ * ---------------------------------------------------------------------- */
+size_t dflash_kv_inject_attn_ws_bytes(const dflash_layer_desc *L, const dflash_cache *c,
+                                      int64_t T, int32_t B);
+int dflash_kv_inject_attn(const dflash_layer_desc *L, dflash_cache *c, const void *C,
+                          const int32_t *cu_ctx, const void *H, int32_t B, void *out,
+                          void *ws, size_t ws_bytes, void *stream);
+
+const char *dflash_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_H */

@@ -1,0 +1,164 @@
+"""C-ABI contract checks that need no GPU: the library loads and exports every
+symbol of include/dflash.h, the ctypes structs match the C layout, and every
+validation path returns its documented status before anything is enqueued
+(fake, never-dereferenced device pointers)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash.h")
+
+L = pytest.importorskip("block_diffusion_draft_fc_amd._lib")
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation or touches host state only
+
+
+def test_exports_every_declared_symbol():
+    names = set(re.findall(r"\b(dflash_\w+)\s*\(", open(HEADER).read()))
+    assert {"dflash_ctx_project", "dflash_kv_inject_attn", "dflash_cache_append", "dflash_cache_crop"} <= names
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (dflash_\w+)", out))
+    assert names <= exported, names - exported
+
+
+def test_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text("""
+#include <stdio.h>
+#include <stddef.h>
+#include "dflash.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu\\n", sizeof(dflash_layer_desc), offsetof(dflash_layer_desc, eps),
+         offsetof(dflash_layer_desc, rope_theta), offsetof(dflash_layer_desc, window),
+         offsetof(dflash_layer_desc, gamma_k));
+  printf("%zu %zu %zu %zu\\n", sizeof(dflash_cache_desc), offsetof(dflash_cache_desc, capacity),
+         offsetof(dflash_cache_desc, k_pool), offsetof(dflash_cache_desc, block_table));
+  return 0;
+}""")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    lines = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    ld, cd = L.LayerDesc, L.CacheDesc
+    assert [int(x) for x in lines[0].split()] == [C.sizeof(ld), ld.eps.offset, ld.rope_theta.offset,
+                                                  ld.window.offset, ld.gamma_k.offset]
+    assert [int(x) for x in lines[1].split()] == [C.sizeof(cd), cd.capacity.offset, cd.k_pool.offset,
+                                                  cd.block_table.offset]
+
+
+def _cache(n_seqs=2, page_size=0, capacity=128, max_pages=0, dtype=L.DFLASH_BF16):
+    desc = L.CacheDesc(n_seqs, 2, 64, dtype, page_size, max_pages, capacity, FAKE, FAKE,
+                       FAKE if page_size else None)
+    h = C.c_void_p()
+    rc = L.LIB.dflash_cache_init(C.byref(h), C.byref(desc))
+    return rc, h
+
+
+def test_strerror_table():
+    for code in range(0, -8, -1):
+        assert L.strerror(code) and L.strerror(code) != "unknown status"
+    assert L.strerror(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(capacity=100), L.ERR_SHAPE),                 # contiguous capacity not a multiple of 64
+    (dict(page_size=100, capacity=4, max_pages=4), L.ERR_SHAPE),
+    (dict(page_size=64, capacity=4, max_pages=0), L.ERR_SHAPE),
+    (dict(n_seqs=0), L.ERR_SHAPE),
+    (dict(n_seqs=65), L.ERR_SHAPE),
+    (dict(dtype=7), L.ERR_DTYPE),
+])
+def test_cache_init_rejects(kw, code):
+    rc, _ = _cache(**kw)
+    assert rc == code
+
+
+def test_cache_host_metadata_and_errors():
+    rc, h = _cache(n_seqs=2, page_size=64, capacity=3, max_pages=2)
+    assert rc == L.DFLASH_OK
+    try:
+        lens = (C.c_int32 * 2)()
+        assert L.LIB.dflash_cache_lengths(h, lens) == 0 and list(lens) == [0, 0]
+        assert L.LIB.dflash_cache_free_pages(h) == 3
+        # crop beyond the current length
+        assert L.LIB.dflash_cache_crop(h, L._i32([1, 0]), None) == L.ERR_RANGE
+        assert L.LIB.dflash_cache_crop(h, L._i32([0, 0]), None) == L.DFLASH_OK
+        # malformed offsets
+        assert L.LIB.dflash_cache_append(h, L._i32([1, 2, 3]), FAKE, FAKE, None) == L.ERR_ARG
+        assert L.LIB.dflash_cache_append(h, L._i32([0, 5, 3]), FAKE, FAKE, None) == L.ERR_ARG
+        # 129 rows need 3 pages > max_pages_per_seq = 2
+        assert L.LIB.dflash_cache_append(h, L._i32([0, 129, 129]), FAKE, FAKE, None) == L.ERR_CAPACITY
+        # 2 + 2 pages > pool of 3
+        assert L.LIB.dflash_cache_append(h, L._i32([0, 128, 256]), FAKE, FAKE, None) == L.ERR_CAPACITY
+        # misaligned rows
+        assert L.LIB.dflash_cache_append(h, L._i32([0, 1, 1]), FAKE + 2, FAKE, None) == L.ERR_ARG
+        # a zero-row append is a no-op that succeeds without touching the device
+        assert L.LIB.dflash_cache_append(h, L._i32([0, 0, 0]), None, None, None) == L.DFLASH_OK
+        assert L.LIB.dflash_cache_lengths(h, lens) == 0 and list(lens) == [0, 0]
+        assert L.LIB.dflash_cache_free_pages(h) == 3
+        tab = (C.c_int32 * 4)()
+        assert L.LIB.dflash_cache_block_table(h, tab) == 0 and list(tab) == [-1] * 4
+    finally:
+        L.LIB.dflash_cache_destroy(h)
+
+
+def test_contiguous_capacity_error():
+    rc, h = _cache(n_seqs=1, capacity=64)
+    assert rc == 0
+    try:
+        assert L.LIB.dflash_cache_append(h, L._i32([0, 65]), FAKE, FAKE, None) == L.ERR_CAPACITY
+        tab = (C.c_int32 * 1)()
+        assert L.LIB.dflash_cache_block_table(h, tab) == 0 and list(tab) == [0]
+    finally:
+        L.LIB.dflash_cache_destroy(h)
+
+
+def test_ctx_project_validation():
+    f = L.LIB.dflash_ctx_project
+    ws = L.LIB.dflash_ctx_project_ws_bytes(16, 20480, 4096, L.DFLASH_BF16)
+    assert ws >= 16 * 4096 * 4
+    assert L.LIB.dflash_ctx_project_ws_bytes(0, 20480, 4096, L.DFLASH_BF16) == 0
+    # T = 0 is a no-op
+    assert f(None, 0, 1536, None, None, 512, 1e-6, L.DFLASH_F32, None, None, 0, None) == 0
+    assert f(FAKE, 3, 1536, FAKE, FAKE, 512, 1e-6, 5, FAKE, FAKE, 1 << 30, None) == L.ERR_DTYPE
+    assert f(FAKE, 3, 1535, FAKE, FAKE, 512, 1e-6, 0, FAKE, FAKE, 1 << 30, None) == L.ERR_SHAPE
+    assert f(None, 3, 1536, FAKE, FAKE, 512, 1e-6, 0, FAKE, FAKE, 1 << 30, None) == L.ERR_ARG
+    assert f(FAKE + 4, 3, 1536, FAKE, FAKE, 512, 1e-6, 0, FAKE, FAKE, 1 << 30, None) == L.ERR_ARG
+    assert f(FAKE, 3, 1536, FAKE, FAKE, 512, 1e-6, 0, FAKE, FAKE, 16, None) == L.ERR_WORKSPACE
+
+
+def _layer(**kw):
+    base = dict(d=512, n_h=8, n_kv=2, d_h=64, eps=1e-6, rope_theta=1e6, window=0, dtype=L.DFLASH_BF16)
+    base.update(kw)
+    return L.LayerDesc(base["d"], base["n_h"], base["n_kv"], base["d_h"], base["eps"], base["rope_theta"],
+                       base["window"], base["dtype"], FAKE, FAKE, FAKE, FAKE)
+
+
+def test_kv_inject_validation():
+    rc, h = _cache(n_seqs=2, capacity=128)
+    assert rc == 0
+    try:
+        f = L.LIB.dflash_kv_inject_attn
+        good = _layer()
+        wsb = L.LIB.dflash_kv_inject_attn_ws_bytes(C.byref(good), h, 8, 4)
+        assert wsb > 0
+        cu = L._i32([0, 4, 8])
+        args = lambda lay, B=4, cu=cu, ws=wsb: (C.byref(lay), h, FAKE, cu, FAKE, B, FAKE, FAKE, ws, None)  # noqa: E731
+        assert f(*args(_layer(dtype=L.DFLASH_F32))) == L.ERR_DTYPE          # cache is bf16
+        assert f(*args(_layer(n_kv=4, n_h=8))) == L.ERR_SHAPE                # cache has 2 K/V heads
+        assert f(*args(_layer(n_h=7))) == L.ERR_SHAPE                        # n_h % n_kv
+        assert f(*args(_layer(d_h=96))) == L.ERR_SHAPE
+        assert f(*args(good, B=17)) == L.ERR_SHAPE                           # group 4 * 17 > 64 rows
+        assert f(*args(good, cu=L._i32([0, 9, 8]))) == L.ERR_ARG
+        assert f(*args(good, ws=wsb - 1)) == L.ERR_WORKSPACE
+        # 64 + 64 + 4 rows exceed the 128-row capacity
+        ws_big = L.LIB.dflash_kv_inject_attn_ws_bytes(C.byref(good), h, 126, 4)
+        assert f(*args(good, cu=L._i32([0, 125, 126]), ws=ws_big)) == L.ERR_CAPACITY
+        lens = (C.c_int32 * 2)()
+        L.LIB.dflash_cache_lengths(h, lens)
+        assert list(lens) == [0, 0]
+    finally:
+        L.LIB.dflash_cache_destroy(h)
