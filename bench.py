@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Draft-round throughput of the DFlash KV-injection attention layer on one MI355X.
+
+Workload: one Qwen3-8B-shaped draft attention layer in steady-state decode
+(d 4096, 32 query / 8 K/V heads of 128, k = 5 target layers -> 20480-wide raw
+context, block of 16, bf16 storage with fp32 accumulation, batch 1).  The draft
+KV cache starts at 8192 rows; each round appends 1..16 newly accepted context
+rows (seeded schedule of 64 rounds) plus the block, attends, and is cropped back
+to the accepted prefix.  Step i runs round i mod 64; every 64 steps the cache is
+cropped back to 8192 rows, so every step sees an 8.2K-8.7K-key cache.
+
+One step = dflash_ctx_project (fc + hidden_norm) + dflash_kv_inject_attn
+(q/k/v projections, QK-norm, RoPE, cache append, attention, o_proj) +
+dflash_cache_crop.  All inputs are resident in HBM before timing starts.
+
+Prints one JSON line: draft blocks/s (value), the attention kernel's HBM
+throughput against the 8 TB/s peak (roofline), per-stage times from HIP events
+recorded on the launch stream, and the fp64 CPU oracle timed on a bounded
+sample of the same rounds (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+METRIC = "draft blocks/sec + attn HBM GB/s (% peak), ctx 8K, block 16, GQA 32/8"
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--mode", choices=("graph", "eager"), default="graph",
+                    help="graph: each round's launches replayed from a captured HIP graph")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------- algorithmic work
+
+def round_work(wl, L, n):
+    """Algorithmic bytes / FLOPs of one round at cache length L with n new rows:
+    every tensor the method must touch, moved once."""
+    eb = 2
+    B, d, kd = wl.B, wl.d, wl.kd
+    qd, kvd = wl.n_h * wl.d_h, wl.n_kv * wl.d_h
+    L_tot = L + n + B
+    w = {}
+    w["ctx_gemm"] = dict(bytes=(d * kd + n * kd + n * d) * eb, flops=2 * n * kd * d)
+    w["qkv_gemm"] = dict(bytes=((qd + 2 * kvd) * d + (n + B) * d) * eb, flops=2 * (B * qd + (n + B) * 2 * kvd) * d)
+    # attention: every cached K and V row once, the queries once
+    w["attn"] = dict(bytes=(L_tot * 2 * kvd + B * qd) * eb, flops=4 * wl.n_h * B * L_tot * wl.d_h)
+    w["o_gemm"] = dict(bytes=(d * qd + B * qd + B * d) * eb, flops=2 * B * qd * d)
+    w["round"] = dict(bytes=sum(v["bytes"] for v in w.values()), flops=sum(v["flops"] for v in w.values()))
+    return w
+
+
+# ---------------------------------------------------------------------------- CPU oracle leg
+
+def cpu_baseline(wl, budget_s):
+    """The fp64 oracle on the host cores, over the first rounds of the same
+    schedule until `budget_s` seconds of round work have run."""
+    from oracle import dflash_oracle as O
+    from workloads import generate as G
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    fc, lw = G.fc_weights(wl), G.layer_weights(wl, 0)
+    p = O.LayerParams(lw["w_qkv"].astype(np.float64), lw["w_o"].astype(np.float64), lw["gamma_q"],
+                      lw["gamma_k"], wl.n_h, wl.n_kv, wl.d_h, wl.eps, wl.rope_theta, 0)
+    K0, V0 = G.prefill_kv(wl, 0, 0, wl.prefill_len)
+    stack = O.OracleStack([p], fc["w_fc"].astype(np.float64), fc["gamma_h"], wl.eps, [[K0]], [[V0]])
+    sched = G.schedule(wl)
+    done, spent = 0, 0.0
+    while spent < budget_s and done < wl.rounds:
+        x, cu, H = G.round_inputs(wl, done, sched[done])
+        t0 = time.perf_counter()
+        stack.round(x, cu, H, wl.B)
+        spent += time.perf_counter() - t0
+        done += 1
+    return {"value": done / spent, "unit": "draft blocks/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {done} of the {wl.rounds} seeded rounds (8192-row cache, 1-16 new rows, block 16), "
+                      f"fp64 NumPy, {spent:.1f} s of round work; weight set-up excluded"}
+
+
+# ---------------------------------------------------------------------------- GPU leg
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the layer runs on a single MI355X here; "
+              "multi-GPU sharding is not part of this build (see the design notes).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from block_diffusion_draft_fc_amd import _lib as L
+    from workloads import configs, generate as G
+    from workloads.device import to_device
+
+    wl = configs.DECODE_8K
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    log(f"bench: {wl.name}: generating weights and inputs")
+    fc, lw = G.fc_weights(wl), G.layer_weights(wl, 0)
+    w_fc, gamma_h = to_device(fc["w_fc"], wl, dev), to_device(fc["gamma_h"], wl, dev)
+    layer = L.Layer(*(to_device(lw[k], wl, dev) for k in ("w_qkv", "w_o", "gamma_q", "gamma_k")),
+                    n_h=wl.n_h, n_kv=wl.n_kv, d_h=wl.d_h, eps=wl.eps, rope_theta=wl.rope_theta)
+    sched = G.schedule(wl)[:, 0]
+    L0 = wl.prefill_len
+    cap = (L0 + int(sched.sum()) + wl.B + 63) // 64 * 64
+    cache = L.Cache(1, wl.n_kv, wl.d_h, torch.bfloat16, cap, device=dev)
+    K0, V0 = G.prefill_kv(wl, 0, 0, L0)
+    L.dflash_cache_append(cache, [0, L0], to_device(np.ascontiguousarray(K0.transpose(1, 0, 2)), wl, dev),
+                          to_device(np.ascontiguousarray(V0.transpose(1, 0, 2)), wl, dev))
+    xs, Hs = [], []
+    for rnd in range(wl.rounds):
+        x, _, H = G.round_inputs(wl, rnd, [int(sched[rnd])])
+        xs.append(to_device(x, wl, dev))
+        Hs.append(to_device(H, wl, dev))
+    max_n = int(sched.max())
+    C = torch.empty((max_n, wl.d), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((wl.B, wl.d), dtype=torch.bfloat16, device=dev)
+    ctx_ws = torch.empty(L.dflash_ctx_project_ws_bytes(max_n, wl.kd, wl.d, torch.bfloat16), dtype=torch.uint8,
+                         device=dev)
+    layer_ws = torch.empty(L.dflash_kv_inject_attn_ws_bytes(layer, cache, max_n, wl.B), dtype=torch.uint8,
+                           device=dev)
+    torch.cuda.synchronize()
+
+    # cache length at the start of round r of a 64-round cycle
+    starts = L0 + np.concatenate([[0], np.cumsum(sched)[:-1]])
+
+    def step(i):
+        r = i % wl.rounds
+        if cache.lengths()[0] != starts[r]:
+            L.dflash_cache_crop(cache, [int(starts[r])])
+        n = int(sched[r])
+        Cn = C[:n]
+        L.dflash_ctx_project(xs[r], w_fc, gamma_h, wl.eps, Cn, ctx_ws)
+        L.dflash_kv_inject_attn(layer, cache, Cn, [0, n], Hs[r], wl.B, out, layer_ws)
+        L.dflash_cache_crop(cache, [int(starts[r]) + n])
+
+    graphs = None
+    if args.mode == "graph":
+        # One HIP graph per round of the cycle.  Capture runs the library's host
+        # side (validation, planning, cache metadata) and records the kernels with
+        # their arguments; replaying graph r re-runs round r's kernels on the
+        # cache rows it wrote at capture, so the cache is cropped back first.
+        log("bench: capturing one graph per round")
+        s = torch.cuda.Stream()
+        graphs = []
+        torch.cuda.synchronize()
+        for r in range(wl.rounds):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                step(r)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+        # The crops of a round are host metadata only (nothing is enqueued), so a
+        # replay carries the whole GPU side of the round; replays run the cycle
+        # in order, so every cache row is written before a later round reads it.
+        def run(i):
+            graphs[i % wl.rounds].replay()
+    else:
+        run = step
+
+    # ---------------- timed region
+    log(f"bench: warmup {args.warmup}, timed {args.steps} steps ({args.mode})")
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        run(args.warmup + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
+    log(f"bench: {ms_per_step * 1e3:.1f} us/step (events {gpu_ms / args.steps * 1e3:.1f}, "
+        f"wall {wall / args.steps * 1e6:.1f})")
+
+    # ---------------- the same steps issued eagerly (host launch path included)
+    eager_ms = None
+    if args.mode == "graph":
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ev0.record()
+        for i in range(args.steps):
+            step(args.warmup + i)
+        ev1.record()
+        torch.cuda.synchronize()
+        eager_ms = max(ev0.elapsed_time(ev1), (time.perf_counter() - t1) * 1e3) / args.steps
+        log(f"bench: eager {eager_ms * 1e3:.1f} us/step")
+    else:
+        eager_ms = ms_per_step
+
+    # ---------------- per-stage times: the same steps, eagerly, with the library's
+    # HIP events recorded on the launch stream around every stage
+    L.timing_reset()
+    L.timing_enable(True)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    stages = L.timing_read()
+    L.timing_enable(False)
+
+    # algorithmic work of the timed steps
+    work = {}
+    for i in range(args.steps):
+        r = (args.warmup + i) % wl.rounds
+        for k, v in round_work(wl, int(starts[r]), int(sched[r])).items():
+            a = work.setdefault(k, {"bytes": 0, "flops": 0})
+            a["bytes"] += v["bytes"]
+            a["flops"] += v["flops"]
+
+    def stage_entry(name, stage_names, bound):
+        n = stages[stage_names[0]][0]
+        ms = sum(stages[s][1] for s in stage_names)
+        us = ms / max(n, 1) * 1e3
+        b, f = work[name]["bytes"] / max(n, 1), work[name]["flops"] / max(n, 1)
+        gbps = b / (us * 1e-6) / 1e9 if us > 0 else 0.0
+        tflops = f / (us * 1e-6) / 1e12 if us > 0 else 0.0
+        e = {"stages": list(stage_names), "launches": n, "us_per_launch": round(us, 3),
+             "alg_bytes_per_launch": int(b), "alg_flops_per_launch": int(f),
+             "gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+             "tflops": round(tflops, 2), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 5), "bound": bound}
+        return e
+
+    kernels = {
+        "attn": stage_entry("attn", ["attn"], "hbm"),
+        "attn+combine": stage_entry("attn", ["attn", "attn_combine"], "hbm"),
+        "ctx_project": stage_entry("ctx_gemm", ["ctx_gemm", "ctx_reduce", "ctx_norm"], "hbm"),
+        "qkv": stage_entry("qkv_gemm", ["qkv_gemm", "qkv_epilogue"], "hbm"),
+        "o_proj": stage_entry("o_gemm", ["o_gemm", "o_reduce"], "hbm"),
+    }
+    kernels["ctx_gemm_only"] = stage_entry("ctx_gemm", ["ctx_gemm"], "hbm")
+    stage_us = {k: round(v[1] / max(v[0], 1) * 1e3, 3) for k, v in stages.items() if v[0]}
+
+    att = kernels["attn"]
+    round_bytes = work["round"]["bytes"] / args.steps
+    blocks_per_s = 1e3 / ms_per_step
+    res = {
+        "metric": METRIC,
+        "value": round(blocks_per_s, 1),
+        "unit": "draft blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "eager_ms_per_step": round(eager_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs, N(0,1/fan_in) weights)",
+        "config": {"workload": wl.name, "ctx": L0, "block": wl.B, "heads": f"{wl.n_h}/{wl.n_kv}", "d": wl.d,
+                   "d_h": wl.d_h, "k_layers": wl.k_layers, "rounds_per_cycle": wl.rounds, "batch": wl.R,
+                   "mode": args.mode},
+        "attn_hbm_gbps": att["gbps"],
+        "attn_hbm_frac_peak": att["hbm_frac"],
+        "roofline": {"bound": "hbm", "achieved": att["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": att["hbm_frac"], "traffic": None, "kernel": "attn_split_kernel",
+                     "us_per_launch": att["us_per_launch"], "alg_bytes_per_launch": att["alg_bytes_per_launch"]},
+        "round_alg_bytes": int(round_bytes),
+        "round_hbm_gbps": round(round_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "kernels": kernels,
+        "stage_us": stage_us,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the fp64 oracle on the host")
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -59,6 +59,9 @@ def _load() -> C.CDLL:
         "dflash_cache_crop": (C.c_int, [vp, p32, vp]),
         "dflash_kv_inject_attn_ws_bytes": (sz, [C.POINTER(LayerDesc), vp, i64, i32]),
         "dflash_kv_inject_attn": (C.c_int, [C.POINTER(LayerDesc), vp, vp, p32, vp, i32, vp, vp, sz, vp]),
+        "dflash_timing_enable": (C.c_int, [C.c_int]),
+        "dflash_timing_read": (C.c_int, [i32, C.POINTER(i64), C.POINTER(C.c_double)]),
+        "dflash_timing_reset": (C.c_int, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -199,3 +202,27 @@ def dflash_kv_inject_attn(layer: Layer, cache: Cache, C_rows, cu_ctx, H, B, out,
                                      _i32(cu_ctx), _ptr(H), int(B), _ptr(out), _ptr(ws),
                                      ws.numel() if ws is not None else 0, _stream(stream)),
            "dflash_kv_inject_attn")
+
+
+# --------------------------------------------------------------------- stage timing
+
+STAGES = ("ctx_gemm", "ctx_reduce", "ctx_norm", "qkv_gemm", "qkv_epilogue", "attn", "attn_combine",
+          "o_gemm", "o_reduce", "cache_append", "page_table")
+
+
+def timing_enable(on: bool = True) -> None:
+    _check(LIB.dflash_timing_enable(1 if on else 0), "dflash_timing_enable")
+
+
+def timing_reset() -> None:
+    _check(LIB.dflash_timing_reset(), "dflash_timing_reset")
+
+
+def timing_read() -> dict:
+    """{stage name: (launches, total ms)} since the last reset."""
+    out = {}
+    for i, name in enumerate(STAGES):
+        n, ms = C.c_int64(), C.c_double()
+        _check(LIB.dflash_timing_read(i, C.byref(n), C.byref(ms)), "dflash_timing_read")
+        out[name] = (int(n.value), float(ms.value))
+    return out

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <set>
 #include <vector>
 
@@ -34,6 +35,67 @@ bool dtype_ok(int32_t dt) { return dt == DFLASH_F32 || dt == DFLASH_BF16; }
 size_t elem_bytes(int32_t dt) { return dt == DFLASH_BF16 ? 2 : 4; }
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- stage timing
+// While enabled, each stage of a call is bracketed by two HIP events recorded
+// on the caller's stream; the elapsed times are collected when read.
+struct TimingRec {
+  int stage;
+  hipEvent_t a, b;
+};
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  std::vector<TimingRec> pending;
+  int64_t launches[DFLASH_STAGE_COUNT] = {};
+  double ms[DFLASH_STAGE_COUNT] = {};
+};
+Timing& timing() {
+  static Timing t;
+  return t;
+}
+
+hipEvent_t take_event(Timing& t) {
+  if (!t.pool.empty()) {
+    hipEvent_t e = t.pool.back();
+    t.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `f` (which enqueues the stage's kernels on `s`), bracketed by events when
+// timing is on and the stage does launch something.
+template <class F>
+hipError_t staged(int stage, hipStream_t s, bool launches, F&& f) {
+  Timing& t = timing();
+  if (!launches) return f();
+  bool on;
+  hipEvent_t a = nullptr, b = nullptr;
+  {
+    std::lock_guard<std::mutex> g(t.mu);
+    on = t.on;
+    if (on) {
+      a = take_event(t);
+      b = take_event(t);
+    }
+  }
+  if (!on || !a || !b) return f();
+  hipError_t e = hipEventRecord(a, s);
+  if (e == hipSuccess) e = f();
+  if (e == hipSuccess) e = hipEventRecord(b, s);
+  std::lock_guard<std::mutex> g(t.mu);
+  if (e == hipSuccess) {
+    t.pending.push_back({stage, a, b});
+  } else {
+    t.pool.push_back(a);
+    t.pool.push_back(b);
+  }
+  return e;
+}
 
 int attn_target_items() {
   static int v = [] {
@@ -67,9 +129,10 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, size_t eb) {
   return p;
 }
 
-size_t skinny_lds(const SkinnyPlan& p, size_t eb) {
-  return (size_t)p.mt * 16 * (size_t)(p.k_chunk + 8) * eb;
-}
+// Rows per weight-streaming problem: 64 for bf16; 32 for fp32, whose staged
+// activation rows take twice the LDS (this keeps every plan within the 64 KB
+// dynamic LDS budget).
+int64_t rows_per_problem(size_t eb) { return eb == 2 ? kSkinnyMaxM : kSkinnyMaxM / 2; }
 
 // A product of the (virtual) row concatenation [x0 (m0 rows); x1 (m1 rows)] with
 // W^T, written as fp32 split-K partials [splits][M][N].  Rows are processed in
@@ -88,7 +151,7 @@ GemmJob make_job(const void* x0, int64_t m0, const void* x1, int64_t m1, const v
                  int64_t K, size_t eb) {
   GemmJob j;
   j.x0 = x0; j.m0 = m0; j.x1 = x1; j.m1 = m1; j.w = w; j.N = N; j.K = K;
-  j.plan = plan_skinny(std::min<int64_t>(m0 + m1, kSkinnyMaxM), N, K, eb);
+  j.plan = plan_skinny(std::min<int64_t>(m0 + m1, rows_per_problem(eb)), N, K, eb);
   j.part = nullptr;
   return j;
 }
@@ -99,8 +162,9 @@ size_t job_part_bytes(const GemmJob& j) {
 
 void job_problems(const GemmJob& j, size_t eb, std::vector<GemmProb>* out) {
   const int64_t M = j.m0 + j.m1;
-  for (int64_t a = 0; a < M; a += kSkinnyMaxM) {
-    const int64_t e = std::min<int64_t>(a + kSkinnyMaxM, M);
+  const int64_t step = rows_per_problem(eb);
+  for (int64_t a = 0; a < M; a += step) {
+    const int64_t e = std::min<int64_t>(a + step, M);
     GemmProb p{};
     const int64_t a0 = std::min(a, j.m0), e0 = std::min(e, j.m0);
     p.m0 = (int32_t)(e0 - a0);
@@ -188,9 +252,19 @@ int plan_append(const dflash_cache* c, const std::vector<int64_t>& n, AppendPlan
   return DFLASH_OK;
 }
 
+hipError_t enqueue_page_table_now(const dflash_cache* c, const AppendPlan& plan, hipStream_t st);
+
 hipError_t enqueue_page_table(const dflash_cache* c, const AppendPlan& plan, hipStream_t st) {
   const auto& d = c->desc;
   if (d.page_size == 0) return hipSuccess;
+  size_t total = 0;
+  for (const auto& v : plan.new_pages) total += v.size();
+  if (total == 0) return hipSuccess;
+  return staged(DFLASH_STAGE_PAGE_TABLE, st, true, [&] { return enqueue_page_table_now(c, plan, st); });
+}
+
+hipError_t enqueue_page_table_now(const dflash_cache* c, const AppendPlan& plan, hipStream_t st) {
+  const auto& d = c->desc;
   BtUpdateArgs a{};
   a.table = d.block_table;
   for (int s = 0; s < d.n_seqs; ++s) {
@@ -369,7 +443,8 @@ int dflash_cache_append(dflash_cache* c, const int32_t* cu_rows, const void* k_r
     a.n_seqs = c->desc.n_seqs;
     for (int i = 0; i < c->desc.n_seqs; ++i) a.L[i] = c->len[i];
     for (int i = 0; i <= c->desc.n_seqs; ++i) a.cu[i] = cu_rows[i];
-    e = launch_cache_append(c->desc.dtype, a, n_rows, s);
+    e = staged(DFLASH_STAGE_CACHE_APPEND, s, true,
+               [&] { return launch_cache_append(c->desc.dtype, a, n_rows, s); });
   }
   if (e != hipSuccess) return DFLASH_ERR_HIP;
   commit_append(c, n, plan);
@@ -413,13 +488,16 @@ int dflash_ctx_project(const void* x_raw, int64_t T, int64_t kd, const void* w_f
   j.part = static_cast<float*>(ws);
   float* u = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(job_part_bytes(j)));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = run_gemms(dtype, {j}, s);
+  hipError_t e = staged(DFLASH_STAGE_CTX_GEMM, s, true, [&] { return run_gemms(dtype, {j}, s); });
   const float* src = j.part;
   if (e == hipSuccess && j.plan.splits > 1) {
-    e = launch_splitk_reduce(DFLASH_F32, j.part, j.plan.splits, T, d, u, s);
+    e = staged(DFLASH_STAGE_CTX_REDUCE, s, true,
+               [&] { return launch_splitk_reduce(DFLASH_F32, j.part, j.plan.splits, T, d, u, s); });
     src = u;
   }
-  if (e == hipSuccess) e = launch_rmsnorm_rows(dtype, src, T, d, gamma_h, eps, c_out, s);
+  if (e == hipSuccess)
+    e = staged(DFLASH_STAGE_CTX_NORM, s, true,
+               [&] { return launch_rmsnorm_rows(dtype, src, T, d, gamma_h, eps, c_out, s); });
   return hip_status(e);
 }
 
@@ -472,7 +550,7 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
   gq.x1 = H; gq.part = part_q;
   gkv.x0 = C; gkv.x1 = H; gkv.part = part_kv;
   gkv.w = static_cast<const char*>(L->w_qkv) + (size_t)p.qd * L->d * eb;
-  if (e == hipSuccess) e = run_gemms(dt, {gq, gkv}, s);
+  if (e == hipSuccess) e = staged(DFLASH_STAGE_QKV_GEMM, s, true, [&] { return run_gemms(dt, {gq, gkv}, s); });
 
   // 3. norms, RoPE, Q to the workspace, K/V into the cache
   CacheView cv = view_of(c);
@@ -489,7 +567,7 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
     for (int i = 0; i < L->d_h / 2; ++i) a.inv_freq[i] = std::pow(L->rope_theta, -2.0 * i / L->d_h);
     for (int r = 0; r < R; ++r) { a.seq.L[r] = c->len[r]; a.seq.n[r] = (int32_t)n[r]; }
     for (int r = 0; r <= R; ++r) a.seq.cu[r] = cu_ctx[r];
-    e = launch_qkv_epilogue(dt, a, s);
+    e = staged(DFLASH_STAGE_QKV_EPILOGUE, s, true, [&] { return launch_qkv_epilogue(dt, a, s); });
   }
 
   // 4. attention over every cached key, split into chunks
@@ -521,7 +599,8 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
     }
     aa.item_base[R] = (int32_t)items;
     if (items > p.max_items) e = hipErrorInvalidValue;  // cannot happen: bounded by construction
-    if (e == hipSuccess) e = launch_attn_split(dt, aa, (int)items, s);
+    if (e == hipSuccess)
+      e = staged(DFLASH_STAGE_ATTN, s, items > 0, [&] { return launch_attn_split(dt, aa, (int)items, s); });
     if (e == hipSuccess) {
       CombineArgs ca{};
       ca.part_o = part_o; ca.part_ml = part_ml; ca.attn = attn;
@@ -529,17 +608,65 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
       ca.d_h = L->d_h;
       for (int r = 0; r <= R; ++r) ca.item_base[r] = aa.item_base[r];
       for (int r = 0; r < R; ++r) ca.chunks[r] = aa.chunks[r];
-      e = launch_attn_combine(dt, ca, s);
+      e = staged(DFLASH_STAGE_ATTN_COMBINE, s, true, [&] { return launch_attn_combine(dt, ca, s); });
     }
   }
 
   // 5. o_proj
   GemmJob go = p.go;
   go.x0 = attn; go.part = part_out;
-  if (e == hipSuccess) e = run_gemms(dt, {go}, s);
-  if (e == hipSuccess) e = launch_splitk_reduce(dt, part_out, go.plan.splits, p.RB, L->d, out, s);
+  if (e == hipSuccess) e = staged(DFLASH_STAGE_O_GEMM, s, true, [&] { return run_gemms(dt, {go}, s); });
+  if (e == hipSuccess)
+    e = staged(DFLASH_STAGE_O_REDUCE, s, true,
+               [&] { return launch_splitk_reduce(dt, part_out, go.plan.splits, p.RB, L->d, out, s); });
   if (e != hipSuccess) return DFLASH_ERR_HIP;
   commit_append(c, rows, ap);
+  return DFLASH_OK;
+}
+
+int dflash_timing_enable(int on) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  t.on = on != 0;
+  return DFLASH_OK;
+}
+
+// Collects every pending pair (waiting for its end event), then reports.
+int dflash_timing_read(int32_t stage, int64_t* launches, double* total_ms) {
+  if (stage < 0 || stage >= DFLASH_STAGE_COUNT || !launches || !total_ms) return DFLASH_ERR_ARG;
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  int st = DFLASH_OK;
+  for (const auto& r : t.pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+      st = DFLASH_ERR_HIP;
+    } else {
+      t.launches[r.stage] += 1;
+      t.ms[r.stage] += ms;
+    }
+    t.pool.push_back(r.a);
+    t.pool.push_back(r.b);
+  }
+  t.pending.clear();
+  *launches = t.launches[stage];
+  *total_ms = t.ms[stage];
+  return st;
+}
+
+int dflash_timing_reset(void) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  for (const auto& r : t.pending) {
+    hipEventSynchronize(r.b);
+    t.pool.push_back(r.a);
+    t.pool.push_back(r.b);
+  }
+  t.pending.clear();
+  for (int i = 0; i < DFLASH_STAGE_COUNT; ++i) {
+    t.launches[i] = 0;
+    t.ms[i] = 0.0;
+  }
   return DFLASH_OK;
 }
 

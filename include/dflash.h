@@ -182,6 +182,35 @@ int dflash_kv_inject_attn(const dflash_layer_desc *L, dflash_cache *c, const voi
 
 const char *dflash_strerror(int status);
 
+/* ------------------------------------------------------------------------
+ * Stage timing (a measurement aid, off by default).  While enabled, every
+ * stage a call enqueues is bracketed by two HIP events recorded on that call's
+ * stream, so a stage's time is the GPU time between its first kernel's start
+ * and its last kernel's end on that stream.  dflash_timing_read waits for the
+ * recorded events (it synchronises with them, never with the whole device),
+ * folds them into per-stage totals and reports the launches and summed
+ * milliseconds of one stage since the last reset.  Process-wide; thread-safe.
+ * Stages that launch nothing (e.g. T == 0) are not recorded.
+ * ---------------------------------------------------------------------- */
+typedef enum {
+  DFLASH_STAGE_CTX_GEMM = 0,     /* fc: X_raw . W_fc^T, split-K partials */
+  DFLASH_STAGE_CTX_REDUCE = 1,   /* fc split-K reduction */
+  DFLASH_STAGE_CTX_NORM = 2,     /* hidden_norm */
+  DFLASH_STAGE_QKV_GEMM = 3,     /* q_proj of H, k_proj/v_proj of [C; H] */
+  DFLASH_STAGE_QKV_EPILOGUE = 4, /* QK-norm, RoPE, Q to workspace, K/V to cache */
+  DFLASH_STAGE_ATTN = 5,         /* split-context block attention */
+  DFLASH_STAGE_ATTN_COMBINE = 6, /* merge of the split partials */
+  DFLASH_STAGE_O_GEMM = 7,       /* o_proj split-K partials */
+  DFLASH_STAGE_O_REDUCE = 8,     /* o_proj reduction and store */
+  DFLASH_STAGE_CACHE_APPEND = 9, /* dflash_cache_append copy */
+  DFLASH_STAGE_PAGE_TABLE = 10,  /* device page-table update */
+  DFLASH_STAGE_COUNT = 11
+} dflash_stage;
+
+int dflash_timing_enable(int on);
+int dflash_timing_read(int32_t stage, int64_t *launches, double *total_ms);
+int dflash_timing_reset(void);
+
 #ifdef __cplusplus
 }
 #endif

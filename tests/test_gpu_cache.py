@@ -1,0 +1,96 @@
+"""GPU cache append / crop against the integer cache model, bit for bit.
+
+Random sequences of appends and crops (contiguous and paged caches, 16- and
+32-bit words, payloads that include NaN and infinity bit patterns) go through
+dflash_cache_append / dflash_cache_crop and through oracle.cache_model; after
+every operation the whole K and V pools, the lengths, the page tables (host
+and device) and the free-page count must be identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU containers
+    pytest.skip("no GPU visible", allow_module_level=True)
+
+from block_diffusion_draft_fc_amd import _lib as L  # noqa: E402
+from oracle.cache_model import CacheError, CacheModel  # noqa: E402
+
+from gpu_harness import say  # noqa: E402
+
+CASES = [
+    # (name, n_seqs, n_kv, d_h, page_size, capacity, max_pages, word)
+    ("contig_bf16", 3, 2, 64, 0, 320, 0, np.uint16),
+    ("contig_f32", 2, 1, 128, 0, 192, 0, np.uint32),
+    ("paged64_bf16", 4, 2, 64, 64, 14, 6, np.uint16),
+    ("paged128_bf16_dh128", 3, 8, 128, 128, 9, 5, np.uint16),
+    ("paged64_f32", 2, 2, 128, 64, 7, 5, np.uint32),
+]
+
+
+def _device_bits(t, word):
+    it = torch.int16 if word == np.uint16 else torch.int32
+    return t.view(it).cpu().numpy().view(word)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_random_append_crop_sequences(case, seed):
+    name, n_seqs, n_kv, d_h, ps, cap, maxp, word = case
+    say(f"case cache {name} seed={seed}")
+    rng = np.random.default_rng(1000 + seed)
+    tdt = torch.bfloat16 if word == np.uint16 else torch.float32
+    cache = L.Cache(n_seqs, n_kv, d_h, tdt, cap, ps, maxp, "cuda")
+    model = CacheModel(n_seqs, n_kv, d_h, ps, cap, maxp, word=word)
+    special = np.array([0x7FC0, 0xFF80, 0x7F80, 0x0001, 0x8000] if word == np.uint16 else
+                       [0x7FC00001, 0xFF800000, 0x7F800000, 0x00000001, 0x80000000], dtype=word)
+    for step in range(40):
+        if rng.random() < 0.6:
+            n = rng.integers(0, 90, size=n_seqs)
+            cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
+            rows = int(cu[-1])
+            k = rng.integers(0, np.iinfo(word).max, size=(rows, n_kv, d_h), dtype=word, endpoint=True)
+            v = rng.integers(0, np.iinfo(word).max, size=(rows, n_kv, d_h), dtype=word, endpoint=True)
+            if rows:
+                k.reshape(-1)[: special.size] = special
+                v.reshape(-1)[-special.size:] = special
+            kd = torch.from_numpy(k.view(np.int16 if word == np.uint16 else np.int32)).to("cuda").view(tdt)
+            vd = torch.from_numpy(v.view(np.int16 if word == np.uint16 else np.int32)).to("cuda").view(tdt)
+            try:
+                model.append(cu, k, v)
+                expect = 0
+            except CacheError as e:
+                expect = e.code
+            try:
+                L.dflash_cache_append(cache, cu, kd, vd)
+                got = 0
+            except L.DFlashError as e:
+                got = e.code
+            assert got == expect, f"step {step}: append status {got} != {expect}"
+        else:
+            new = [int(rng.integers(0, x + 1)) if rng.random() < 0.8 else x + 1 for x in model.len]
+            try:
+                model.crop(new)
+                expect = 0
+            except CacheError as e:
+                expect = e.code
+            try:
+                L.dflash_cache_crop(cache, new)
+                got = 0
+            except L.DFlashError as e:
+                got = e.code
+            assert got == expect, f"step {step}: crop status {got} != {expect}"
+        torch.cuda.synchronize()
+        assert cache.lengths() == model.len
+        assert np.array_equal(_device_bits(cache.k_pool, word), model.K), f"step {step}: K pool"
+        assert np.array_equal(_device_bits(cache.v_pool, word), model.V), f"step {step}: V pool"
+        if ps:
+            assert cache.free_pages() == len(model.free)
+            host = cache.block_table()
+            dev = cache.table.cpu().numpy()
+            for s in range(n_seqs):
+                pages = model.pages[s]
+                assert host[s][: len(pages)] == pages and all(x == -1 for x in host[s][len(pages):])
+                assert list(dev[s, : len(pages)]) == pages
