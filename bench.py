@@ -49,7 +49,24 @@ def parse():
                     help="graph: each round's launches replayed from a captured HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy 8 times (scales HBM counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain copy kernel of known size: 256 MiB read and 256 MiB written per
+    launch, so per-dispatch FETCH_SIZE / WRITE_SIZE should read 262144 KiB."""
+    import torch
+
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(8):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 8}), flush=True)
+    return 0
 
 
 # ---------------------------------------------------------------------------- algorithmic work
@@ -111,6 +128,9 @@ def main():
         print("bench.py measures one GPU only: the layer runs on a single MI355X here; "
               "multi-GPU sharding is not part of this build (see the design notes).", file=sys.stderr)
         return 2
+
+    if args.copy_calibration:
+        return copy_calibration()
 
     import torch
 

@@ -40,6 +40,12 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   constexpr int NS = 4 / QS;       // block streams: waves that share query rows
   constexpr int LDO = DH + 4;      // LDS row stride of the merge buffer
 
+  constexpr int QROWS = QS * QW;   // query rows staged for the workgroup
+  constexpr int LDQ = DH + 8;      // LDS row stride of the queries: 16 rows of a
+                                   // 16-byte read land on distinct banks
+
+  __shared__ __align__(16) T s_q[QROWS * LDQ];
+  __shared__ int32_t s_page[kAttnMaxChunkPages];
   __shared__ float s_o[4][QW][LDO];
   __shared__ float s_m[4][QW];
   __shared__ float s_l[4][QW];
@@ -55,31 +61,54 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   const int kend = min(kbeg + a.chunk_keys, key_hi);
   const int nblk = kend > kbeg ? (kend - kbeg + 31) >> 5 : 0;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index is uniform across the wave; saying so keeps the block loop
+  // scalar (a loop the compiler thinks divergent gets exec masking and a
+  // full wait for every load at its header)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qg = wave % QS;        // which QW query rows this wave holds
   const int stream = wave / QS;    // which blocks it walks: stream, stream + NS, ...
   const int j16 = lane & 15, q4 = lane >> 4;
   const int valid_q = a.group * a.B;
 
-  // queries: B operand of S^T; lane (j16, q4) holds row qg*QW + 16t + j16,
-  // head dims 32s + 8q4 .. +7
-  V8 qv[NQW][DS];
+  // The workgroup's query rows go to LDS (rows past g*B as zeros); every wave
+  // reads its B operands of S^T from there, lane (j16, q4) taking row
+  // qg*QW + 16t + j16, head dims 32s + 8q4 .. +7.  Their global loads are
+  // issued before any K/V load, so waiting for them never waits for K/V.
+  constexpr int QV8 = QROWS * DH / 8;
+  constexpr int QPT = (QV8 + 255) / 256;
   const T* qbase = static_cast<const T*>(a.q_ws) + (int64_t)(r * a.n_kv + g) * a.qrows * DH;
-  int qpos[NQW];
+  V8 qstage[QPT];
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int idx = tid + 256 * i;
+    const int row = idx / (DH / 8);
+    qstage[i] = (idx < QV8 && row < valid_q) ? load8(qbase + (int64_t)idx * 8) : zero8<T>();
+  }
+  // keys visible to query row q are [vlo_q, key_hi): vlo_q = pos_q - window + 1
+  // on sliding layers, no lower bound on full ones
+  int vlo[NQW];
   float m_run[NQW], l_run[NQW];
   f32x4 o[NQW][DT];
 #pragma unroll
   for (int t = 0; t < NQW; ++t) {
     const int qrow = qg * QW + t * 16 + j16;
-#pragma unroll
-    for (int s = 0; s < DS; ++s)
-      qv[t][s] = qrow < valid_q ? load8(qbase + (int64_t)qrow * DH + 32 * s + 8 * q4) : zero8<T>();
-    qpos[t] = a.qpos0[r] + qrow % a.B;
+    vlo[t] = a.window > 0 ? a.qpos0[r] + qrow % a.B - a.window + 1 : INT_MIN;
     m_run[t] = -INFINITY;
     l_run[t] = 0.f;
 #pragma unroll
     for (int d = 0; d < DT; ++d) o[t][d] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const T* qlds = s_q + (qg * QW + j16) * LDQ + 8 * q4;
+  // the largest lower bound among the rows (the last block row's)
+  const int vis_lo_max = a.qpos0[r] + a.B - 1 - a.window + 1;
+
+  // physical pages of the chunk, read once: fetches then take their page from
+  // LDS and never wait on a global load (vector loads complete in order, so a
+  // dependent page-table load would also wait for every K/V load in flight)
+  const int pg0 = kbeg / a.cache.page_rows;
+  const int npg = nblk > 0 ? (kend - 1) / a.cache.page_rows - pg0 + 1 : 0;
+  for (int i = tid; i < npg; i += 256) s_page[i] = (int32_t)cache_page(a.cache, r, (pg0 + i) * a.cache.page_rows);
 
   const T* kpool = static_cast<const T*>(a.cache.k_pool);
   const T* vpool = static_cast<const T*>(a.cache.v_pool);
@@ -87,109 +116,135 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
 
   // One 32-key block: K rows into the A operand of S^T (tile kt, row i holds
   // key 8*(i/4) + 4*kt + i%4), V^T into the A operand of O^T (16 head dims x
-  // 8 consecutive keys per lane).  Keys at or beyond key_hi read as zero.
+  // 8 consecutive keys per lane).  The loads are unconditional: a block starts
+  // at a multiple of 32 below key_hi and never crosses a page (pages and
+  // contiguous capacities are multiples of 64 rows), so rows at or beyond
+  // key_hi are stale cache rows inside the allocation.  Their scores are
+  // masked and their V entries zeroed in `process`, so no load result is
+  // touched here and the next block's loads stay in flight.
   auto fetch = [&](V8 (&kv)[2][DS], V8 (&vv)[DT], int blk) {
-    const int64_t page = cache_page(a.cache, r, blk);
+    const int64_t page = s_page[blk / a.cache.page_rows - pg0];
     const int slot = blk % a.cache.page_rows;
     const T* kb = kpool + k_offset(a.cache, page, g, slot);
     const T* vb = vpool + v_offset(a.cache, page, g, slot);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int kr = krow_in_tile + 4 * kt;
-      const bool ok = blk + kr < key_hi;
 #pragma unroll
-      for (int s = 0; s < DS; ++s)
-        kv[kt][s] = ok ? load8(kb + (int64_t)kr * DH + 32 * s + 8 * q4) : zero8<T>();
+      for (int s = 0; s < DS; ++s) kv[kt][s] = load8(kb + (int64_t)kr * DH + 32 * s + 8 * q4);
     }
-    const int kk0 = blk + 8 * q4;
 #pragma unroll
-    for (int d = 0; d < DT; ++d) {
-      V8 v = kk0 < key_hi ? load8(vb + (int64_t)(16 * d + j16) * a.cache.page_rows + 8 * q4) : zero8<T>();
-      if (kk0 + 8 > key_hi) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (kk0 + e >= key_hi) v[e] = static_cast<T>(0.f);
-      }
-      vv[d] = v;
-    }
+    for (int d = 0; d < DT; ++d) vv[d] = load8(vb + (int64_t)(16 * d + j16) * a.cache.page_rows + 8 * q4);
+    // keep the loads here: without the barrier the compiler sinks them to
+    // their first use, which leaves no block in flight while another computes
+    asm volatile("" ::: "memory");
   };
 
-  auto process = [&](const V8 (&kv)[2][DS], const V8 (&vv)[DT], int blk) {
-    f32x4 sacc[2][NQW];
+  auto process = [&](const V8 (&kv)[2][DS], V8 (&vv)[DT], int blk) {
+    // stale rows past the end of the cache may hold any bits: zero their V
+    // entries so that p = 0 cannot meet an Inf or NaN (wave-uniform branch,
+    // taken on the last block of a sequence only)
+    if (blk + 32 > key_hi) {
+      const int kk0 = blk + 8 * q4;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int d = 0; d < DT; ++d)
 #pragma unroll
-      for (int t = 0; t < NQW; ++t) {
-        f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < DS; ++s) c = mma32(kv[kt][s], qv[t][s], c);
-        sacc[kt][t] = c;
-      }
+        for (int e = 0; e < 8; ++e)
+          if (kk0 + e >= key_hi) vv[d][e] = static_cast<T>(0.f);
+    }
+    // the queries are re-read from LDS for every block: the empty asm with a
+    // memory clobber keeps the compiler from hoisting them into registers
+    asm volatile("" ::: "memory");
     const int key0 = blk + 8 * q4;   // this lane's 8 consecutive keys
-    V8 pv[NQW];
-    float alpha[NQW];
-    bool any_need = false;
+    // every key of the block is visible to every query row of the workgroup
+    // (the usual case): no per-element masking
+    const bool all_vis = blk + 32 <= key_hi && (a.window <= 0 || blk >= vis_lo_max);
+    // one 16-row query tile at a time: scores, softmax update, then P V
 #pragma unroll
     for (int t = 0; t < NQW; ++t) {
+      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        const V8 q = *reinterpret_cast<const V8*>(qlds + t * 16 * LDQ + 32 * s);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) sacc[kt] = mma32(kv[kt][s], q, sacc[kt]);
+      }
       f32x8 sv;
-      float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = key0 + 4 * kt + e;
-          bool vis = key < key_hi;
-          if (a.window > 0) vis = vis && (qpos[t] - key < a.window);
-          const float x = vis ? sacc[kt][t][e] * a.scale_log2 : -INFINITY;
-          sv[4 * kt + e] = x;
-          mx = fmaxf(mx, x);
+        for (int e = 0; e < 4; ++e) sv[4 * kt + e] = sacc[kt][e] * a.scale_log2;
+      if (!all_vis) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = key0 + e;
+          const bool vis = (key >= vlo[t]) & (key < key_hi);
+          sv[e] = vis ? sv[e] : -INFINITY;
         }
+      }
+      float mx = sv[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
       // Lazy rescale: the reference max only moves when the block max exceeds
       // it by more than 8 (log2 units), so every p <= 256, and O is rescaled
-      // only on those rare blocks (wave-uniform branch below), which keeps the
+      // only on those rare blocks (wave-uniform branch), which keeps the
       // accumulators out of the VALU path.
       const bool need = mx > m_run[t] + 8.f;
       const float m_new = need ? mx : m_run[t];
-      alpha[t] = need ? exp2f(m_run[t] - m_new) : 1.f;
-      any_need |= need;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run[t] - m_new) : 1.f;
       m_run[t] = m_new;
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       f32x8 p;
       float ps = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        p[e] = exp2f(sv[e] - m_use);
+        // raw v_exp_f32: results below the normal range flush to zero, which
+        // only drops weights under 2^-126 of the row maximum
+        p[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
         ps += p[e];
       }
-      l_run[t] = l_run[t] * alpha[t] + ps;
-      pv[t] = cvt8<T>(p);
+      l_run[t] = l_run[t] * alpha + ps;
+      const V8 pv = cvt8<T>(p);
+      if (__any(need)) {
+#pragma unroll
+        for (int d = 0; d < DT; ++d) o[t][d] *= alpha;
+      }
+#pragma unroll
+      for (int d = 0; d < DT; ++d) o[t][d] = mma32(vv[d], pv, o[t][d]);
     }
-    if (__any(any_need)) {
-#pragma unroll
-      for (int t = 0; t < NQW; ++t)
-#pragma unroll
-        for (int d = 0; d < DT; ++d) o[t][d] *= alpha[t];
-    }
-#pragma unroll
-    for (int d = 0; d < DT; ++d)
-#pragma unroll
-      for (int t = 0; t < NQW; ++t) o[t][d] = mma32(vv[d], pv[t], o[t][d]);
   };
 
-  // this wave's blocks: stream, stream + NS, ... (double-buffered)
+  // this wave's blocks: stream, stream + NS, ... (double-buffered).  Every
+  // prefetch in the loop is unconditional (a prefetch past the wave's last
+  // block re-reads that block, an L2 hit): with a conditional prefetch the
+  // wait-count pass would have to assume it missing and wait for it too.
   const int my_n = nblk > stream ? (nblk - stream + NS - 1) / NS : 0;
   constexpr int STEP = 32 * NS;
   V8 kA[2][DS], vA[DT], kB[2][DS], vB[DT];
-  if (my_n > 0) fetch(kA, vA, kbeg + 32 * stream);
-  for (int i = 0; i < my_n; i += 2) {
-    const int blk = kbeg + 32 * stream + STEP * i;
-    if (i + 1 < my_n) fetch(kB, vB, blk + STEP);
-    process(kA, vA, blk);
-    if (i + 1 >= my_n) break;
-    if (i + 2 < my_n) fetch(kA, vA, blk + 2 * STEP);
-    process(kB, vB, blk + STEP);
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int idx = tid + 256 * i;
+    if (idx < QV8) {
+      const int row = idx / (DH / 8), c = idx - row * (DH / 8);
+      *reinterpret_cast<V8*>(s_q + row * LDQ + 8 * c) = qstage[i];
+    }
+  }
+  __syncthreads();
+  if (my_n > 0) {
+    const int first = kbeg + 32 * stream;
+    const int last = first + STEP * (my_n - 1);
+    fetch(kA, vA, first);
+    for (int i = 0;; i += 2) {
+      const int blk = first + STEP * i;
+      fetch(kB, vB, min(blk + STEP, last));
+      process(kA, vA, blk);
+      if (i + 1 >= my_n) break;
+      fetch(kA, vA, min(blk + 2 * STEP, last));
+      process(kB, vB, blk + STEP);
+      if (i + 2 >= my_n) break;
+    }
   }
 
   // merge the waves that hold the same query rows, through LDS
@@ -240,6 +295,383 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- bf16: LDS-streamed keys
+// The bf16 path streams K/V through LDS instead of registers.  Each wave owns
+// two 32-key stages of a ring in LDS and fills them with direct-to-LDS loads
+// (global_load_lds_dwordx4, 16 bytes per lane), so the block in flight costs
+// no registers; the wave's queries (all g*B rows of its K/V head) stay in
+// VGPRs and its output accumulators in AGPRs.
+//
+// A stage holds the block in MFMA operand order: for K, one 1 KB slab per
+// (key tile kt, head-dim step s) whose lane l entry is the 16 bytes that lane l
+// feeds to the S^T product; for V^T, one slab per 16-dim tile d.  Reading an
+// operand is one ds_read_b128 at slab + 16 * lane (consecutive lanes,
+// consecutive 16-byte words: no bank conflicts), and each K/V operand is read
+// once per block and reused by every query tile.
+//
+// The compiler does not order LDS reads after direct-to-LDS loads, so the
+// waits are explicit: vector memory operations of a wave complete in order
+// and the loop issues nothing else, so "all but the newest block's loads
+// done" is s_waitcnt vmcnt(loads per block).  A wave reads only the stages it
+// filled itself, so no barrier is needed inside the loop.
+
+template <int DH, int NQT>
+__global__ __launch_bounds__(256, 1) void attn_lds_kernel(AttnArgs a) {
+  using V8 = bf16x8;
+  constexpr int DS = DH / 32;                 // K=32 steps over the head dim
+  constexpr int DT = DH / 16;                 // 16-dim tiles of the head dim
+  constexpr int QROWS = NQT * 16;
+  constexpr int KSLABS = 2 * DS, VSLABS = DT;
+  constexpr int LOADS = KSLABS + VSLABS;      // direct-to-LDS loads per block and wave
+  constexpr int STAGE = LOADS * 1024;
+  constexpr int RING_HALF = 4 * STAGE;        // one stage of each of the four waves
+  constexpr int LDO = DH + 4;                 // merge buffer row stride (floats)
+  constexpr int MERGE_HALF = 2 * QROWS * LDO * 4;   // two waves' accumulators
+  constexpr int HALF = RING_HALF > MERGE_HALF ? RING_HALF : MERGE_HALF;
+
+  // the two ring stages are separate arrays, so that alias analysis can tell a
+  // read of one stage from a load in flight into the other
+  __shared__ __align__(16) unsigned char lds0[HALF];
+  __shared__ __align__(16) unsigned char lds1[HALF];
+  // queries in operand order: slab (t, s) holds, at 16 * lane, the 16 bytes lane
+  // (j16, q4) feeds to the S^T product: row 16t + j16, head dims 32s + 8q4 ..
+  __shared__ __align__(16) unsigned char s_q[NQT * DS * 1024];
+  __shared__ float s_ml[2][4][QROWS];
+  __shared__ int32_t s_page[kAttnMaxChunkPages];
+
+  const int item = blockIdx.x;
+  int r = 0;
+  while (r + 1 < a.R && item >= a.item_base[r + 1]) ++r;
+  const int local = item - a.item_base[r];
+  const int g = local / a.chunks[r];
+  const int chunk = local - g * a.chunks[r];
+  const int key_hi = a.key_hi[r];
+  const int kbeg = (a.key_lo[r] & ~31) + chunk * a.chunk_keys;
+  const int kend = min(kbeg + a.chunk_keys, key_hi);
+  const int nblk = kend > kbeg ? (kend - kbeg + 31) >> 5 : 0;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  // uniform across the wave; saying so keeps the block loop scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j16 = lane & 15, q4 = lane >> 4;
+  const int valid_q = a.group * a.B;
+
+  // queries of the K/V head (rows past g*B as zeros), staged to s_q below
+  const bf16* qbase = static_cast<const bf16*>(a.q_ws) + (int64_t)(r * a.n_kv + g) * a.qrows * DH;
+  constexpr int QSLOTS = NQT * DS * 64;       // 16-byte slots of s_q
+  constexpr int QPT = (QSLOTS + 255) / 256;   // per thread
+  V8 qstage[QPT];
+  int vlo[NQT];
+  float m_run[NQT], l_run[NQT];
+  f32x4 o[NQT][DT];
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    const int qrow = t * 16 + j16;
+    // keys visible to the row: [vlo, key_hi), vlo = pos - window + 1 on sliding layers
+    vlo[t] = a.window > 0 ? a.qpos0[r] + qrow % a.B - a.window + 1 : INT_MIN;
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.f;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) o[t][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int vis_lo_max = a.qpos0[r] + a.B - a.window;   // largest row bound (sliding layers)
+
+  // physical pages of the chunk, read once so that no load of the block loop
+  // depends on another global load
+  const int pg0 = kbeg / a.cache.page_rows;
+  const int npg = nblk > 0 ? (kend - 1) / a.cache.page_rows - pg0 + 1 : 0;
+  for (int i = tid; i < npg; i += 256) s_page[i] = (int32_t)cache_page(a.cache, r, (pg0 + i) * a.cache.page_rows);
+  __syncthreads();
+
+  const bf16* kpool = static_cast<const bf16*>(a.cache.k_pool);
+  const bf16* vpool = static_cast<const bf16*>(a.cache.v_pool);
+  const int krow = 8 * (j16 >> 2) + (j16 & 3);   // + 4*kt: key of A-operand row j16
+  unsigned char* ring0 = lds0 + wave * STAGE;
+  unsigned char* ring1 = lds1 + wave * STAGE;
+
+  // direct-to-LDS loads of one 32-key block into stage st.  Blocks start at a
+  // multiple of 32 below key_hi and never cross a page (pages and contiguous
+  // capacities are multiples of 64 rows): rows past key_hi are stale rows
+  // inside the allocation, masked below.
+  auto issue = [&](int blk, int st) {
+    const int64_t page = s_page[blk / a.cache.page_rows - pg0];
+    const int slot = blk % a.cache.page_rows;
+    const bf16* kb = kpool + k_offset(a.cache, page, g, slot);
+    const bf16* vb = vpool + v_offset(a.cache, page, g, slot);
+    unsigned char* sb = st ? ring1 : ring0;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int s = 0; s < DS; ++s)
+        __builtin_amdgcn_global_load_lds(kb + (int64_t)(krow + 4 * kt) * DH + 32 * s + 8 * q4,
+                                         sb + (kt * DS + s) * 1024, 16, 0, 0);
+#pragma unroll
+    for (int d = 0; d < DT; ++d)
+      __builtin_amdgcn_global_load_lds(vb + (int64_t)(16 * d + j16) * a.cache.page_rows + 8 * q4,
+                                       sb + (KSLABS + d) * 1024, 16, 0, 0);
+  };
+
+  // Fast path for one block: every row's reference maximum m_run stays where
+  // it was set (by the row's first visible key), weights exp2(s - m_run) may
+  // exceed 1, and no VALU instruction touches the accumulators - which lets
+  // them live in AGPRs through the loop.  Returns false, having accumulated
+  // nothing, if some score exceeds its row's reference by more than 64
+  // (weights up to 2^64 keep every sum far from the fp32 range); the block is
+  // then redone by `process`, which rescales.
+  auto process_fast = [&](int blk, int st) -> bool {
+    asm volatile("" ::: "memory");
+    const unsigned char* sb = (st ? ring1 : ring0) + 16 * lane;
+    const unsigned char* qb = s_q + 16 * lane;
+    V8 kv[2][DS], vv[DT];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int s = 0; s < DS; ++s) kv[kt][s] = *reinterpret_cast<const V8*>(sb + (kt * DS + s) * 1024);
+#pragma unroll
+    for (int d = 0; d < DT; ++d) vv[d] = *reinterpret_cast<const V8*>(sb + (KSLABS + d) * 1024);
+    const int key0 = blk + 8 * q4;
+    if (blk + 32 > key_hi) {
+#pragma unroll
+      for (int d = 0; d < DT; ++d)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (key0 + e >= key_hi) vv[d][e] = static_cast<bf16>(0.f);
+    }
+    const bool all_vis = blk + 32 <= key_hi && (a.window <= 0 || blk >= vis_lo_max);
+    f32x8 sv[NQT];
+    bool over = false;
+#pragma unroll
+    for (int t = 0; t < NQT; ++t) {
+      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        const V8 q = *reinterpret_cast<const V8*>(qb + (t * DS + s) * 1024);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) sacc[kt] = mma32(kv[kt][s], q, sacc[kt]);
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[t][4 * kt + e] = sacc[kt][e] * a.scale_log2;
+      if (!all_vis) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = key0 + e;
+          sv[t][e] = ((key >= vlo[t]) & (key < key_hi)) ? sv[t][e] : -INFINITY;
+        }
+      }
+      float mx = sv[t][0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[t][e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      // a row's first visible key sets its reference (its sums are still zero)
+      if (m_run[t] == -INFINITY) m_run[t] = mx;
+      over |= mx > m_run[t] + 64.f;
+    }
+    if (__any(over)) return false;
+#pragma unroll
+    for (int t = 0; t < NQT; ++t) {
+      const float m_use = m_run[t] == -INFINITY ? 0.f : m_run[t];
+      f32x8 p;
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(sv[t][e] - m_use);
+        ps += p[e];
+      }
+      l_run[t] += ps;
+      const V8 pv = cvt8<bf16>(p);
+#pragma unroll
+      for (int d = 0; d < DT; ++d) o[t][d] = mma32(vv[d], pv, o[t][d]);
+    }
+    return true;
+  };
+
+  // General path for one block: online softmax with a lazily moved maximum.
+  auto process = [&](int blk, int st) {
+    asm volatile("" ::: "memory");
+    const unsigned char* sb = (st ? ring1 : ring0) + 16 * lane;
+    const unsigned char* qb = s_q + 16 * lane;
+    V8 kv[2][DS], vv[DT];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int s = 0; s < DS; ++s) kv[kt][s] = *reinterpret_cast<const V8*>(sb + (kt * DS + s) * 1024);
+#pragma unroll
+    for (int d = 0; d < DT; ++d) vv[d] = *reinterpret_cast<const V8*>(sb + (KSLABS + d) * 1024);
+    const int key0 = blk + 8 * q4;   // this lane's 8 consecutive keys
+    // stale rows past the end of the cache may hold any bits: zero their V
+    // entries so that p = 0 cannot meet an Inf or NaN (last block only)
+    if (blk + 32 > key_hi) {
+#pragma unroll
+      for (int d = 0; d < DT; ++d)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (key0 + e >= key_hi) vv[d][e] = static_cast<bf16>(0.f);
+    }
+    // every key of the block visible to every row of the workgroup (the usual
+    // case): no per-element masking
+    const bool all_vis = blk + 32 <= key_hi && (a.window <= 0 || blk >= vis_lo_max);
+#pragma unroll
+    for (int t = 0; t < NQT; ++t) {
+      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        const V8 q = *reinterpret_cast<const V8*>(qb + (t * DS + s) * 1024);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) sacc[kt] = mma32(kv[kt][s], q, sacc[kt]);
+      }
+      // lane holds the scores of keys key0 .. key0+7 for row 16t + j16
+      f32x8 sv;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[4 * kt + e] = sacc[kt][e] * a.scale_log2;
+      if (!all_vis) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = key0 + e;
+          sv[e] = ((key >= vlo[t]) & (key < key_hi)) ? sv[e] : -INFINITY;
+        }
+      }
+      float mx = sv[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      // Lazy rescale: the reference max only moves when the block max exceeds
+      // it by more than 8 (log2 units), so every p <= 256 and O is rescaled on
+      // those rare blocks only (wave-uniform branch).
+      const bool need = mx > m_run[t] + 8.f;
+      const float m_new = need ? mx : m_run[t];
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run[t] - m_new) : 1.f;
+      m_run[t] = m_new;
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      f32x8 p;
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // raw v_exp_f32: results below the normal range flush to zero, which
+        // only drops weights under 2^-126 of the row maximum
+        p[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
+        ps += p[e];
+      }
+      l_run[t] = l_run[t] * alpha + ps;
+      const V8 pv = cvt8<bf16>(p);
+      if (__any(need)) {
+#pragma unroll
+        for (int d = 0; d < DT; ++d) o[t][d] *= alpha;
+      }
+#pragma unroll
+      for (int d = 0; d < DT; ++d) o[t][d] = mma32(vv[d], pv, o[t][d]);
+    }
+  };
+
+  // this wave's blocks: wave, wave + 4, ...; block i lives in stage i % 2.
+  // The query loads go out first and the first two blocks' loads right after,
+  // so that their latencies overlap.
+  const int my_n = nblk > wave ? (nblk - wave + 3) / 4 : 0;
+  const int first = kbeg + 32 * wave;
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int idx = tid + 256 * i;                 // slot: slab idx / 64, lane idx % 64
+    const int slab = idx >> 6, L = idx & 63;
+    const int row = 16 * (slab / DS) + (L & 15);
+    const int col = 32 * (slab % DS) + 8 * (L >> 4);
+    qstage[i] = (idx < QSLOTS && row < valid_q) ? load8(qbase + (int64_t)row * DH + col) : zero8<bf16>();
+  }
+  if (my_n > 0) issue(first, 0);
+  if (my_n > 1) issue(first + 128, 1);
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int idx = tid + 256 * i;
+    if (idx < QSLOTS) *reinterpret_cast<V8*>(s_q + 16 * idx) = qstage[i];
+  }
+  __syncthreads();
+  int i = 0;
+  for (; i < my_n; ++i) {
+    // outstanding loads: block i and, if it exists, block i+1, issued after it
+    if (i + 1 < my_n)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (!process_fast(first + 128 * i, i & 1)) break;
+    if (i + 2 < my_n) {
+      // every LDS read of this stage has returned before it is refilled
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(first + 128 * (i + 2), i & 1);
+    }
+  }
+  // a score far above its row's reference: the rest goes through the
+  // rescaling path, starting with the block the fast path gave back
+  for (; i < my_n; ++i) {
+    if (i + 1 < my_n)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    process(first + 128 * i, i & 1);
+    if (i + 2 < my_n) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(first + 128 * (i + 2), i & 1);
+    }
+  }
+
+  // merge the four waves' (m, l, O) through LDS, which the ring gives up now:
+  // every wave rescales its rows to the workgroup maximum (one exponential per
+  // row), then the scaled accumulators are summed with 16-byte LDS reads
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  // accumulators of waves 0-1 in the first array, 2-3 in the second:
+  // wave w's row q at s_ow(w) + q * LDO
+  auto s_ow = [&](int w) {
+    return reinterpret_cast<float*>(w < 2 ? lds0 : lds1) + (w & 1) * QROWS * LDO;
+  };
+  float* s_m = &s_ml[0][0][0];                                // [4][QROWS]
+  float* s_l = &s_ml[1][0][0];                                // [4][QROWS]
+  if (q4 == 0) {
+#pragma unroll
+    for (int t = 0; t < NQT; ++t) s_m[wave * QROWS + t * 16 + j16] = m_run[t];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < NQT; ++t) {
+    const int row = t * 16 + j16;
+    float mm = s_m[row];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) mm = fmaxf(mm, s_m[w * QROWS + row]);
+    const float f = m_run[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[t] - mm);
+    float l = l_run[t];
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    if (q4 == 0) s_l[wave * QROWS + row] = l * f;
+#pragma unroll
+    for (int d = 0; d < DT; ++d)
+      *reinterpret_cast<f32x4*>(s_ow(wave) + row * LDO + 16 * d + 4 * q4) = o[t][d] * f;
+  }
+  __syncthreads();
+
+  float* po = a.part_o + (int64_t)item * a.qrows * DH;
+  const int rows_out = min(a.qrows, QROWS);
+  constexpr int C4 = DH / 4;
+  for (int idx = tid; idx < rows_out * C4; idx += 256) {
+    const int row = idx / C4, c = idx - row * C4;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(s_ow(0) + row * LDO + 4 * c);
+#pragma unroll
+    for (int w = 1; w < 4; ++w) acc += *reinterpret_cast<const f32x4*>(s_ow(w) + row * LDO + 4 * c);
+    *reinterpret_cast<f32x4*>(po + (int64_t)row * DH + 4 * c) = acc;
+  }
+  if (tid < rows_out) {
+    const int row = tid;
+    float mm = s_m[row];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) mm = fmaxf(mm, s_m[w * QROWS + row]);
+    float* pml = a.part_ml + (int64_t)item * 2 * a.qrows;
+    pml[row] = mm;
+    pml[a.qrows + row] = s_l[row] + s_l[QROWS + row] + s_l[2 * QROWS + row] + s_l[3 * QROWS + row];
+  }
+}
+
 template <typename T>
 static hipError_t launch_attn_t(const AttnArgs& a, int items, hipStream_t s) {
   const int nqt = (a.qrows + 15) / 16;
@@ -248,12 +680,19 @@ static hipError_t launch_attn_t(const AttnArgs& a, int items, hipStream_t s) {
     hipLaunchKernelGGL((attn_split_kernel<T, DH_, NQW_, QS_>), dim3(items), dim3(256), 0, s, a);    \
     return hipGetLastError();                                                                      \
   }
-  DFLASH_ATTN_CASE(64, 1, 1, 1) DFLASH_ATTN_CASE(64, 2, 2, 1) DFLASH_ATTN_CASE(64, 3, 3, 1)
-  DFLASH_ATTN_CASE(64, 4, 2, 2)
   if constexpr (sizeof(T) == 2) {
-    DFLASH_ATTN_CASE(128, 1, 1, 1) DFLASH_ATTN_CASE(128, 2, 2, 1) DFLASH_ATTN_CASE(128, 3, 3, 1)
-    DFLASH_ATTN_CASE(128, 4, 2, 2)
+#define DFLASH_ATTN_LDS_CASE(DH_, NQT_)                                                          \
+  if (a.d_h == DH_ && nqt == NQT_) {                                                             \
+    hipLaunchKernelGGL((attn_lds_kernel<DH_, NQT_>), dim3(items), dim3(256), 0, s, a);           \
+    return hipGetLastError();                                                                    \
+  }
+    DFLASH_ATTN_LDS_CASE(64, 1) DFLASH_ATTN_LDS_CASE(64, 2) DFLASH_ATTN_LDS_CASE(64, 3) DFLASH_ATTN_LDS_CASE(64, 4)
+    DFLASH_ATTN_LDS_CASE(128, 1) DFLASH_ATTN_LDS_CASE(128, 2) DFLASH_ATTN_LDS_CASE(128, 3)
+    DFLASH_ATTN_LDS_CASE(128, 4)
+#undef DFLASH_ATTN_LDS_CASE
   } else {
+    DFLASH_ATTN_CASE(64, 1, 1, 1) DFLASH_ATTN_CASE(64, 2, 2, 1) DFLASH_ATTN_CASE(64, 3, 3, 1)
+    DFLASH_ATTN_CASE(64, 4, 2, 2)
     // fp32 operands take twice the registers: one 16-row tile per wave
     DFLASH_ATTN_CASE(128, 1, 1, 1) DFLASH_ATTN_CASE(128, 2, 1, 2) DFLASH_ATTN_CASE(128, 3, 1, 4)
     DFLASH_ATTN_CASE(128, 4, 1, 4)
@@ -271,12 +710,20 @@ hipError_t launch_attn_split(int dtype, const AttnArgs& a, int items, hipStream_
 // Merges the chunk partials of one query row: m = max_c m_c,
 // l = sum_c 2^(m_c - m) l_c, O = sum_c 2^(m_c - m) O_c / l, and stores O in the
 // row-major [R*B][n_h*d_h] order of the attention output (head h at columns
-// h*d_h .., "DFlash KV Injection Walkthrough" Step 4.5).  One wave per row.
+// h*d_h .., "DFlash KV Injection Walkthrough" Step 4.5).
+// One wave per query row, lane l owning head dims 2l, 2l+1 (d_h <= 128).
+// Chunks go in groups of 32: every O load of the group and the group's (m, l)
+// loads (lane c % 32 loads chunk c's) are issued before any is used, so a row
+// costs one memory latency per 32 chunks; the group maximum and weights come
+// from wave reductions and readlane.  A group maximum above the running one
+// rescales the accumulators.
 
 template <typename T>
 __global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
+  constexpr int G = 32;
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // uniform per wave (so the per-sequence tables are read with scalar loads)
+  const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int per_seq = a.n_kv * a.group * a.B;
   if (row >= (int64_t)a.R * per_seq) return;
   const int r = (int)(row / per_seq);
@@ -286,28 +733,45 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
   const int hl = qrow / a.B, b = qrow - hl * a.B;
   const int n = a.chunks[r];
   const int64_t it0 = a.item_base[r] + (int64_t)g * n;
+  const float* ml = a.part_ml + it0 * 2 * a.qrows + qrow;   // m_c at ml[c * mstride], l_c at + qrows
+  const int64_t mstride = 2 * (int64_t)a.qrows;
+  const bool act = 2 * lane < a.d_h;
+  const float* po = a.part_o + (it0 * a.qrows + qrow) * a.d_h + 2 * (act ? lane : 0);
+  const int64_t ostride = (int64_t)a.qrows * a.d_h;
 
-  float mm = -INFINITY;
-  for (int c = lane; c < n; c += 64) mm = fmaxf(mm, a.part_ml[(it0 + c) * 2 * a.qrows + qrow]);
-  mm = wave_max(mm);
-  const float mu = mm == -INFINITY ? 0.f : mm;
-  float lsum = 0.f;
-  for (int c = lane; c < n; c += 64) {
-    const float* pml = a.part_ml + (it0 + c) * 2 * a.qrows;
-    lsum += exp2f(pml[qrow] - mu) * pml[a.qrows + qrow];
-  }
-  lsum = wave_sum(lsum);
-  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-
-  const int h = g * a.group + hl;
-  T* dst = static_cast<T*>(a.attn) + ((int64_t)r * a.B + b) * (a.n_kv * a.group * a.d_h) + h * a.d_h;
-  for (int d = lane; d < a.d_h; d += 64) {
-    float acc = 0.f;
-    for (int c = 0; c < n; ++c) {
-      const float w = exp2f(a.part_ml[(it0 + c) * 2 * a.qrows + qrow] - mu);
-      acc += w * a.part_o[((it0 + c) * a.qrows + qrow) * a.d_h + d];
+  float mrun = -INFINITY, lrun = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int cb = 0; cb < n; cb += G) {
+    float2 oc[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k)
+      oc[k] = cb + k < n ? *reinterpret_cast<const float2*>(po + (int64_t)(cb + k) * ostride) : float2{0.f, 0.f};
+    // issue the O loads before the (m, l) loads and their reductions
+    asm volatile("" ::: "memory");
+    const int c = cb + (lane & (G - 1));
+    const float mc = c < n ? ml[c * mstride] : -INFINITY;
+    const float lc = c < n ? ml[c * mstride + a.qrows] : 0.f;
+    const float mg = fmaxf(wave_max(mc), mrun);
+    const float mu = mg == -INFINITY ? 0.f : mg;
+    const float wc = exp2f(mc - mu);            // weight of chunk cb + lane % 32
+    const float sa = exp2f(mrun - mu);          // rescale of the groups before
+    // lanes 32..63 repeat lanes 0..31: half the wave sum is the group's
+    lrun = lrun * sa + 0.5f * wave_sum(wc * lc);
+    o0 *= sa;
+    o1 *= sa;
+    mrun = mg;
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wc), k));
+      o0 += w * oc[k].x;
+      o1 += w * oc[k].y;
     }
-    dst[d] = from_f32<T>(acc * inv);
+  }
+  const float inv = lrun > 0.f ? 1.0f / lrun : 0.f;
+  if (act) {
+    const int h = g * a.group + hl;
+    T* dst = static_cast<T*>(a.attn) + ((int64_t)r * a.B + b) * (a.n_kv * a.group * a.d_h) + h * a.d_h + 2 * lane;
+    dst[0] = from_f32<T>(o0 * inv);
+    dst[1] = from_f32<T>(o1 * inv);
   }
 }
 

@@ -110,24 +110,47 @@ int attn_target_items() {
 
 struct SkinnyPlan {
   int32_t k_chunk, splits, mt, n_tiles;
+  bool wide;   // gemm_wide_kernel (256-column tiles) instead of gemm_lds_kernel
 };
 
-// Weight-streaming GEMM of M <= 64 rows: choose the K split so that (a) the
-// activation slice fits the LDS budget and (b) there are enough workgroups to
-// keep every CU streaming.
+int env_int(const char* name, int dflt, int lo, int hi) {
+  const char* e = std::getenv(name);
+  const int v = e ? std::atoi(e) : dflt;
+  return std::min(std::max(v, lo), hi);
+}
+
+// Plans for at most 64 rows (32 for fp32), tuned on the decode-round shapes:
+//  * long inputs (K >= 8192, bf16, <= 32 rows): gemm_wide_kernel, 256-column
+//    tiles, about 256 workgroups with chunks of whole 128-wide stages;
+//  * otherwise gemm_lds_kernel, 64-column tiles, about 1024 workgroups with
+//    256-wide chunks, the staged activation slice within the LDS budget.
 SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, size_t eb) {
+  static const int wide_target = env_int("DFLASH_GEMM_WIDE_BLOCKS", 256, 1, 1 << 16);
+  static const int lds_target = env_int("DFLASH_GEMM_LDS_BLOCKS", 1024, 1, 1 << 16);
   SkinnyPlan p;
   p.mt = (int32_t)std::max<int64_t>(1, cdiv(M, 16));
+  p.wide = eb == 2 && p.mt <= 2 && K >= 8192;
+  if (p.wide) {
+    p.n_tiles = (int32_t)cdiv(N, 256);
+    int64_t splits = std::max<int64_t>(1, cdiv(wide_target, p.n_tiles));
+    splits = std::min<int64_t>(splits, std::max<int64_t>(1, cdiv(K, 128)));
+    const int64_t kc = cdiv(cdiv(K, splits), 128) * 128;
+    p.k_chunk = (int32_t)kc;
+    p.splits = (int32_t)cdiv(K, kc);
+    return p;
+  }
   p.n_tiles = (int32_t)cdiv(N, 64);
-  int64_t kmax = ((int64_t)kSkinnyLdsBytes / (int64_t)(p.mt * 16 * eb) - 8) / 256 * 256;
+  int64_t kmax = ((int64_t)kLdsGemmBytes / (int64_t)(p.mt * 16 * eb) - 8) / 256 * 256;
   kmax = std::max<int64_t>(kmax, 256);
-  int64_t splits = std::max<int64_t>(cdiv(K, kmax), cdiv(512, p.n_tiles));
+  int64_t splits = std::max<int64_t>(cdiv(K, kmax), cdiv(lds_target, p.n_tiles));
   splits = std::min<int64_t>(splits, std::max<int64_t>(1, cdiv(K, 256)));
-  int64_t kc = cdiv(cdiv(K, splits), 256) * 256;
+  const int64_t kc = cdiv(cdiv(K, splits), 256) * 256;
   p.k_chunk = (int32_t)kc;
   p.splits = (int32_t)cdiv(K, kc);
   return p;
 }
+
+size_t lds_bytes(const GemmProb& p, size_t eb) { return (size_t)p.mt * 16 * (size_t)(p.k_chunk + 8) * eb; }
 
 // Rows per weight-streaming problem: 64 for bf16; 32 for fp32, whose staged
 // activation rows take twice the LDS (this keeps every plan within the 64 KB
@@ -190,21 +213,33 @@ void job_problems(const GemmJob& j, size_t eb, std::vector<GemmProb>* out) {
 hipError_t run_gemms(int32_t dt, const std::vector<GemmJob>& jobs, hipStream_t s) {
   const size_t eb = elem_bytes(dt);
   std::vector<GemmProb> probs;
-  for (const auto& j : jobs)
-    if (j.m0 + j.m1 > 0) job_problems(j, eb, &probs);
+  for (const auto& j : jobs) {
+    if (j.m0 + j.m1 == 0) continue;
+    if (j.plan.wide) {
+      std::vector<GemmProb> w;
+      job_problems(j, eb, &w);
+      for (const auto& p : w) {
+        hipError_t e = launch_gemm_wide(p, s);
+        if (e != hipSuccess) return e;
+      }
+    } else {
+      job_problems(j, eb, &probs);
+    }
+  }
+  // gemm_lds_kernel problems, two per launch
   for (size_t i = 0; i < probs.size(); i += 2) {
     GemmArgs a{};
     a.p[0] = probs[i];
     a.nprob = 1;
     int max_mt = probs[i].mt;
-    size_t lds = (size_t)probs[i].mt * 16 * (probs[i].k_chunk + 8) * eb;
+    size_t lds = lds_bytes(probs[i], eb);
     if (i + 1 < probs.size()) {
       a.p[1] = probs[i + 1];
       a.nprob = 2;
       max_mt = std::max(max_mt, probs[i + 1].mt);
-      lds = std::max(lds, (size_t)probs[i + 1].mt * 16 * (probs[i + 1].k_chunk + 8) * eb);
+      lds = std::max(lds, lds_bytes(probs[i + 1], eb));
     }
-    hipError_t e = launch_gemm_skinny(dt, a, max_mt, lds, s);
+    hipError_t e = launch_gemm_lds(dt, a, max_mt, lds, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -333,7 +368,12 @@ KvPlan plan_kv(const dflash_layer_desc* L, const dflash_cache* c, int64_t T, int
   p.gq = make_job(nullptr, 0, nullptr, p.RB, L->w_qkv, p.qd, L->d, eb);
   p.gkv = make_job(nullptr, T, nullptr, p.RB, nullptr, 2 * p.kvd, L->d, eb);
   p.go = make_job(nullptr, p.RB, nullptr, 0, L->w_o, L->d, p.qd, eb);
-  p.max_items = kAttnMaxTarget + p.R * L->n_kv;
+  // work items of one attention launch: at most the target count plus one
+  // partial chunk per (sequence, head); on a paged cache the chunk may be capped
+  // at (kAttnMaxChunkPages - 2) pages, and the keys of all sequences fit in the
+  // pool, which bounds the extra items
+  p.max_items = kAttnMaxTarget + 2 * p.R * L->n_kv;
+  if (c->desc.page_size > 0) p.max_items += cdiv(c->desc.capacity * L->n_kv, kAttnMaxChunkPages - 2);
   size_t o = 0;
   p.off_q = o;   o = align_up(o + (size_t)p.R * L->n_kv * p.qrows * L->d_h * eb);
   p.off_pq = o;  o = align_up(o + job_part_bytes(p.gq));
@@ -469,14 +509,14 @@ int dflash_cache_crop(dflash_cache* c, const int32_t* new_len, void* /*stream*/)
 size_t dflash_ctx_project_ws_bytes(int64_t T, int64_t kd, int64_t d, int32_t dtype) {
   if (T <= 0 || kd <= 0 || d <= 0 || !dtype_ok(dtype)) return 0;
   GemmJob j = make_job(nullptr, T, nullptr, 0, nullptr, d, kd, elem_bytes(dtype));
-  return align_up(job_part_bytes(j)) + align_up((size_t)T * d * sizeof(float));
+  return align_up(job_part_bytes(j));
 }
 
 int dflash_ctx_project(const void* x_raw, int64_t T, int64_t kd, const void* w_fc, const void* gamma_h,
                        int64_t d, float eps, int32_t dtype, void* c_out, void* ws, size_t ws_bytes,
                        void* stream) {
   if (!dtype_ok(dtype)) return DFLASH_ERR_DTYPE;
-  if (T < 0 || kd <= 0 || d <= 0 || kd % 8 != 0 || d % 8 != 0 || kd > INT32_MAX / 2 || d > INT32_MAX / 2 ||
+  if (T < 0 || kd <= 0 || d <= 0 || kd % 8 != 0 || d % 8 != 0 || kd > INT32_MAX / 2 || d > 16384 ||
       T > INT32_MAX / 2 || !(eps >= 0.f))
     return DFLASH_ERR_SHAPE;
   if (T == 0) return DFLASH_OK;
@@ -486,18 +526,12 @@ int dflash_ctx_project(const void* x_raw, int64_t T, int64_t kd, const void* w_f
   const size_t eb = elem_bytes(dtype);
   GemmJob j = make_job(x_raw, T, nullptr, 0, w_fc, d, kd, eb);
   j.part = static_cast<float*>(ws);
-  float* u = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(job_part_bytes(j)));
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = staged(DFLASH_STAGE_CTX_GEMM, s, true, [&] { return run_gemms(dtype, {j}, s); });
-  const float* src = j.part;
-  if (e == hipSuccess && j.plan.splits > 1) {
-    e = staged(DFLASH_STAGE_CTX_REDUCE, s, true,
-               [&] { return launch_splitk_reduce(DFLASH_F32, j.part, j.plan.splits, T, d, u, s); });
-    src = u;
-  }
   if (e == hipSuccess)
-    e = staged(DFLASH_STAGE_CTX_NORM, s, true,
-               [&] { return launch_rmsnorm_rows(dtype, src, T, d, gamma_h, eps, c_out, s); });
+    e = staged(DFLASH_STAGE_CTX_NORM, s, true, [&] {
+      return launch_reduce_rmsnorm(dtype, j.part, j.plan.splits, T, d, gamma_h, eps, c_out, s);
+    });
   return hip_status(e);
 }
 
@@ -588,8 +622,14 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
       keys[r] = hi - (lo & ~int64_t(31));
       total += keys[r] * L->n_kv;
     }
-    int64_t chunk = cdiv(cdiv(total, attn_target_items()), 128) * 128;
+    // keys per work item: a multiple of the 32-key block, at least one block
+    // per wave, sized so that the items cover the target count
+    int64_t chunk = cdiv(cdiv(total, attn_target_items()), 32) * 32;
     chunk = std::max<int64_t>(chunk, 128);
+    // an item's keys may span at most kAttnMaxChunkPages pages (its page list
+    // is staged in LDS); two pages go to a chunk that does not start on a page
+    if (cd.page_size > 0)
+      chunk = std::min<int64_t>(chunk, (int64_t)(kAttnMaxChunkPages - 2) * cd.page_size);
     aa.chunk_keys = (int32_t)chunk;
     int64_t items = 0;
     for (int r = 0; r < R; ++r) {
@@ -658,7 +698,7 @@ int dflash_timing_reset(void) {
   Timing& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
   for (const auto& r : t.pending) {
-    hipEventSynchronize(r.b);
+    (void)hipEventSynchronize(r.b);
     t.pool.push_back(r.a);
     t.pool.push_back(r.b);
   }

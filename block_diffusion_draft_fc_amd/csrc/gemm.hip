@@ -1,20 +1,29 @@
-// Weight-streaming GEMM for the few-row projections of a draft round, plus the
-// split-K reduction and the row RMSNorm epilogue.
+// Weight-streaming GEMMs for the few-row projections of a draft round, plus
+// the split-K reduction and the row RMSNorm epilogue.
 //
 // The projections of a decode round multiply at most a few dozen activation
 // rows by weight matrices of tens to hundreds of MB (fc: the context rows
 // against W_fc, "DFlash KV Injection Walkthrough" Step 2; q/k/v and o: Step 4.1,
-// 4.2, 4.5).  They are bound by streaming the weight from HBM once.  Each
-// workgroup owns 64 weight rows (output columns) and one K-split; the
-// workgroup's activation slice sits in LDS, every wave streams 16 weight rows
-// straight into the B operand of 16x16x32 MFMAs with 16-byte loads, and fp32
-// partial sums go to a [split][M][N] buffer.
+// 4.2, 4.5).  They are bound by streaming the weight from HBM once, with fp32
+// split-K partial sums going to a [split][M][N] buffer.  Two kernels:
+//
+//  * gemm_lds_kernel - a workgroup owns 64 weight rows (output columns) and one
+//    K-chunk; the chunk's activation slice is staged in LDS once, then each wave
+//    streams 16 weight rows straight into the B operand of 16x16x32 MFMAs
+//    (16-byte loads, double-buffered).  Short chunks and many workgroups: the
+//    right shape for 4096-wide inputs, where the time is mostly latency.
+//  * gemm_wide_kernel - for long inputs (the 20480-wide fc): each wave streams
+//    64 weight rows and reads the activation rows straight from L2 into the A
+//    operand, one activation load feeding four weight tiles; no LDS, no
+//    barrier, and long per-wave streams.
+#include <algorithm>
+
 #include "kernels.hpp"
 
 namespace dflash {
 
 template <typename T, int MTMAX>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs args) {
+__global__ __launch_bounds__(256) void gemm_lds_kernel(GemmArgs args) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* xs = reinterpret_cast<T*>(smem_raw);
   using V8 = vec8_t<T>;
@@ -109,24 +118,148 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs args) {
 }
 
 template <typename T>
-static hipError_t launch_skinny_t(const GemmArgs& a, int max_mt, size_t lds, hipStream_t s) {
+static hipError_t launch_lds_t(const GemmArgs& a, int max_mt, size_t lds, hipStream_t s) {
   const int blocks = a.p[0].blocks + (a.nprob > 1 ? a.p[1].blocks : 0);
   if (blocks == 0) return hipSuccess;
   switch (max_mt) {
-    case 1: hipLaunchKernelGGL((gemm_skinny_kernel<T, 1>), dim3(blocks), dim3(256), lds, s, a); break;
-    case 2: hipLaunchKernelGGL((gemm_skinny_kernel<T, 2>), dim3(blocks), dim3(256), lds, s, a); break;
-    case 3: hipLaunchKernelGGL((gemm_skinny_kernel<T, 3>), dim3(blocks), dim3(256), lds, s, a); break;
-    case 4: hipLaunchKernelGGL((gemm_skinny_kernel<T, 4>), dim3(blocks), dim3(256), lds, s, a); break;
+    case 1: hipLaunchKernelGGL((gemm_lds_kernel<T, 1>), dim3(blocks), dim3(256), lds, s, a); break;
+    case 2: hipLaunchKernelGGL((gemm_lds_kernel<T, 2>), dim3(blocks), dim3(256), lds, s, a); break;
+    case 3: hipLaunchKernelGGL((gemm_lds_kernel<T, 3>), dim3(blocks), dim3(256), lds, s, a); break;
+    case 4: hipLaunchKernelGGL((gemm_lds_kernel<T, 4>), dim3(blocks), dim3(256), lds, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_skinny(int dtype, const GemmArgs& a, int max_mt, size_t lds, hipStream_t s) {
-  return dtype == 1 ? launch_skinny_t<bf16>(a, max_mt, lds, s) : launch_skinny_t<float>(a, max_mt, lds, s);
+hipError_t launch_gemm_lds(int dtype, const GemmArgs& a, int max_mt, size_t lds, hipStream_t s) {
+  return dtype == 1 ? launch_lds_t<bf16>(a, max_mt, lds, s) : launch_lds_t<float>(a, max_mt, lds, s);
+}
+
+// ---------------------------------------------------------------- wide (bf16)
+// Workgroup tile: 256 output columns (wave w: columns 64w .. 64w+63 of the tile,
+// as four 16-column MFMA tiles) x one K-chunk.  A stage is 4 K-steps of 32;
+// loads go out one stage ahead of the MFMAs that use them.
+
+template <int MT>
+__global__ __launch_bounds__(256) void gemm_wide_kernel(GemmProb p) {
+  constexpr int C = 4;   // 16-column tiles per wave
+  constexpr int U = 4;   // K-steps per stage
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l16 = lane & 15, q8 = (lane >> 4) * 8;
+  const int n_tile = blockIdx.x % p.n_tiles, split = blockIdx.x / p.n_tiles;
+  const int k_begin = split * p.k_chunk;
+  const int k_end = min(p.K, k_begin + p.k_chunk);
+  const int M = p.m0 + p.m1;
+  const int nbase = n_tile * 256 + wave * 64;
+
+  const bf16* wp[C];
+  bool nvalid[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int n = nbase + 16 * c + l16;
+    nvalid[c] = n < p.N;
+    wp[c] = static_cast<const bf16*>(p.w) + (int64_t)(nvalid[c] ? n : 0) * p.K + k_begin + q8;
+  }
+  // activation rows; rows past M read row 0 and are never stored
+  const bf16* xp[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    int m = t * 16 + l16;
+    m = m < M ? m : 0;
+    const bf16* base = m < p.m0 ? static_cast<const bf16*>(p.x0) + (int64_t)m * p.K
+                                : static_cast<const bf16*>(p.x1) + (int64_t)(m - p.m0) * p.K;
+    xp[t] = base + k_begin + q8;
+  }
+
+  f32x4 acc[C][MT];
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nsteps = (k_end - k_begin + 31) >> 5;
+  const int nfull = nsteps / U;
+
+  auto fetch = [&](bf16x8 (&w)[U][C], bf16x8 (&x)[U][MT], int stage) {
+    const int k = stage * U * 32;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int c = 0; c < C; ++c) w[u][c] = load8(wp[c] + k + 32 * u);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) x[u][t] = load8(xp[t] + k + 32 * u);
+    // keep the loads here: otherwise the compiler sinks them to their use
+    asm volatile("" ::: "memory");
+  };
+  auto compute = [&](const bf16x8 (&w)[U][C], const bf16x8 (&x)[U][MT]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[c][t] = mma32(x[u][t], w[u][c], acc[c][t]);
+  };
+
+  if (nfull > 0) {
+    // double-buffered; every prefetch is unconditional (past the last stage it
+    // re-reads that stage, an L2 hit) so that the wait counts stay exact
+    bf16x8 wa[U][C], xa[U][MT], wb[U][C], xb[U][MT];
+    fetch(wa, xa, 0);
+    for (int st = 0;; st += 2) {
+      fetch(wb, xb, min(st + 1, nfull - 1));
+      compute(wa, xa);
+      if (st + 1 >= nfull) break;
+      fetch(wa, xa, min(st + 2, nfull - 1));
+      compute(wb, xb);
+      if (st + 2 >= nfull) break;
+    }
+  }
+  // K-steps past the last whole stage: guarded loads
+  for (int step = nfull * U; step < nsteps; ++step) {
+    const int k = step * 32;
+    const bool kin = k_begin + k + q8 < k_end;
+    bf16x8 x[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) x[t] = kin ? load8(xp[t] + k) : zero8<bf16>();
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const bf16x8 w = kin ? load8(wp[c] + k) : zero8<bf16>();
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[c][t] = mma32(x[t], w, acc[c][t]);
+    }
+  }
+
+  const int m_lane = (lane >> 4) * 4;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    if (!nvalid[c]) continue;
+    float* out = p.part + ((int64_t)split * p.m_out + p.row_off) * p.N + nbase + 16 * c + l16;
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = t * 16 + m_lane + e;
+        if (m < M) out[(int64_t)m * p.N] = acc[c][t][e];
+      }
+  }
+}
+
+hipError_t launch_gemm_wide(const GemmProb& p, hipStream_t s) {
+  if (p.blocks == 0) return hipSuccess;
+  switch (p.mt) {
+    case 1: hipLaunchKernelGGL((gemm_wide_kernel<1>), dim3(p.blocks), dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((gemm_wide_kernel<2>), dim3(p.blocks), dim3(256), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- split-K reduction
+// out[m][n] = sum_s part[s][m][n]; one thread per 4 outputs, the split loop
+// unrolled so that its loads are in flight together.
 
 template <typename Tout>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits,
@@ -134,6 +267,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= MN) return;
   f32x4 s = *reinterpret_cast<const f32x4*>(part + i);
+#pragma unroll 8
   for (int sp = 1; sp < splits; ++sp) s += *reinterpret_cast<const f32x4*>(part + (int64_t)sp * MN + i);
 #pragma unroll
   for (int e = 0; e < 4; ++e) out[i + e] = from_f32<Tout>(s[e]);
@@ -153,35 +287,62 @@ hipError_t launch_splitk_reduce(int out_dtype, const float* part, int splits, in
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- RMSNorm over rows
-// hidden_norm of "DFlash KV Injection Walkthrough" Step 2: each context row is
-// divided by the root of its mean square (plus eps) and scaled by the gain.
+// ---------------------------------------------------------------- split-K reduction + RMSNorm
+// hidden_norm of "DFlash KV Injection Walkthrough" Step 2 fused with the fc
+// split-K sum: one workgroup per context row; each thread sums the partials of
+// four columns (all splits' loads in flight together), the row's sum of
+// squares is reduced through LDS, then C[t] = u / sqrt(mean(u^2) + eps) * gamma.
 
 template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* __restrict__ u, int64_t d,
-                                                           const T* __restrict__ gamma, float eps,
-                                                           T* __restrict__ out) {
-  __shared__ float red[4];
-  const float* ur = u + (int64_t)blockIdx.x * d;
+__global__ __launch_bounds__(1024) void reduce_rmsnorm_kernel(const float* __restrict__ part, int splits,
+                                                              int64_t T_rows, int64_t d,
+                                                              const T* __restrict__ gamma, float eps,
+                                                              T* __restrict__ out) {
+  constexpr int MAXC = 4;   // column quads per thread: d <= 4 * 1024 * MAXC
+  __shared__ float red[16];
+  const int64_t t = blockIdx.x;
+  const int64_t stride = T_rows * d;
+  f32x4 u[MAXC];
   float ss = 0.f;
-  for (int64_t i = threadIdx.x; i < d; i += 256) ss += ur[i] * ur[i];
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int64_t col = ((int64_t)c * blockDim.x + threadIdx.x) * 4;
+    u[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (col < d) {
+      const float* src = part + t * d + col;
+#pragma unroll 8
+      for (int sp = 0; sp < splits; ++sp) u[c] += *reinterpret_cast<const f32x4*>(src + sp * stride);
+      ss += u[c][0] * u[c][0] + u[c][1] * u[c][1] + u[c][2] * u[c][2] + u[c][3] * u[c][3];
+    }
+  }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float tot = red[0] + red[1] + red[2] + red[3];
+  float tot = 0.f;
+  const int nw = blockDim.x >> 6;
+  for (int w = 0; w < nw; ++w) tot += red[w];
   const float r = 1.0f / sqrtf(tot / (float)d + eps);
-  T* orow = out + (int64_t)blockIdx.x * d;
-  for (int64_t i = threadIdx.x; i < d; i += 256) orow[i] = from_f32<T>(ur[i] * r * to_f32(gamma[i]));
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int64_t col = ((int64_t)c * blockDim.x + threadIdx.x) * 4;
+    if (col < d) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[t * d + col + e] = from_f32<T>(u[c][e] * r * to_f32(gamma[col + e]));
+    }
+  }
 }
 
-hipError_t launch_rmsnorm_rows(int dtype, const float* u, int64_t T, int64_t d, const void* gamma,
-                               float eps, void* out, hipStream_t s) {
+hipError_t launch_reduce_rmsnorm(int dtype, const float* part, int splits, int64_t T, int64_t d,
+                                 const void* gamma, float eps, void* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  // d % 4 == 0 and d <= 16384 (checked by the caller); threads: one per column quad, at most 1024
+  const int64_t quads = d / 4;
+  const unsigned threads = (unsigned)std::min<int64_t>(1024, ((quads + 63) / 64) * 64);
   if (dtype == 1)
-    hipLaunchKernelGGL(rmsnorm_rows_kernel<bf16>, dim3((unsigned)T), dim3(256), 0, s, u, d,
+    hipLaunchKernelGGL(reduce_rmsnorm_kernel<bf16>, dim3((unsigned)T), dim3(threads), 0, s, part, splits, T, d,
                        static_cast<const bf16*>(gamma), eps, static_cast<bf16*>(out));
   else
-    hipLaunchKernelGGL(rmsnorm_rows_kernel<float>, dim3((unsigned)T), dim3(256), 0, s, u, d,
+    hipLaunchKernelGGL(reduce_rmsnorm_kernel<float>, dim3((unsigned)T), dim3(threads), 0, s, part, splits, T, d,
                        static_cast<const float*>(gamma), eps, static_cast<float*>(out));
   return hipGetLastError();
 }

@@ -22,7 +22,7 @@ struct GemmProb {
   int32_t m0, m1;
   int32_t row_off, m_out;
   int32_t N, K;
-  int32_t k_chunk;   // K per split, multiple of 256
+  int32_t k_chunk;   // K per split, a multiple of 256 (one stage of 8 K-steps)
   int32_t splits;
   int32_t mt;        // 16-row tiles: ceil((m0 + m1) / 16)
   int32_t n_tiles;   // ceil(N / 64)
@@ -34,19 +34,21 @@ struct GemmArgs {
 };
 // Rows handled by one weight-streaming problem.
 constexpr int kSkinnyMaxM = 64;
-// LDS budget for the staged activation slice of one workgroup.
-constexpr int kSkinnyLdsBytes = 64 * 1024;
 
-hipError_t launch_gemm_skinny(int dtype, const GemmArgs& a, int max_mt, size_t lds_bytes,
-                              hipStream_t s);
+// LDS budget for the staged activation slice of one gemm_lds_kernel workgroup.
+constexpr int kLdsGemmBytes = 64 * 1024;
+hipError_t launch_gemm_lds(int dtype, const GemmArgs& a, int max_mt, size_t lds_bytes, hipStream_t s);
+// bf16 only, at most 32 rows (mt <= 2); 256-column tiles (n_tiles = ceil(N/256)).
+hipError_t launch_gemm_wide(const GemmProb& p, hipStream_t s);
 
 // out[m][n] = sum_s part[s][m][n], written as fp32 (out_dtype 0) or bf16 (1).
 hipError_t launch_splitk_reduce(int out_dtype, const float* part, int splits, int64_t M,
                                 int64_t N, void* out, hipStream_t s);
 
-// C[t] = u[t] / sqrt(mean(u[t]^2) + eps) * gamma, one row of d per workgroup.
-hipError_t launch_rmsnorm_rows(int dtype, const float* u, int64_t T, int64_t d,
-                               const void* gamma, float eps, void* out, hipStream_t s);
+// C[t] = u[t] / sqrt(mean(u[t]^2) + eps) * gamma with u[t] = sum_s part[s][t],
+// one row of d per workgroup; d % 4 == 0 and d <= 16384.
+hipError_t launch_reduce_rmsnorm(int dtype, const float* part, int splits, int64_t T, int64_t d,
+                                 const void* gamma, float eps, void* out, hipStream_t s);
 
 // ---------------------------------------------------------------- QKV epilogue
 struct SeqTable {
@@ -70,6 +72,10 @@ struct QkvEpiArgs {
 hipError_t launch_qkv_epilogue(int dtype, const QkvEpiArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
+// Pages one attention work item may span (its chunk is limited to
+// (kAttnMaxChunkPages - 2) pages of keys by the host planner).
+constexpr int kAttnMaxChunkPages = 64;
+
 struct AttnArgs {
   const void* q_ws;      // [R][n_kv][qrows][d_h]
   CacheView cache;

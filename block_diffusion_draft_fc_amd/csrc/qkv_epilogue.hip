@@ -52,6 +52,7 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvEpiArgs a) {
   float x0 = 0.f, x1 = 0.f;
   if (act) {
     const float* src = part + (int64_t)m * width + col + lane;
+#pragma unroll 8
     for (int s = 0; s < splits; ++s) { x0 += src[s * stride]; x1 += src[s * stride + half]; }
   }
 

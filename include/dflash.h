@@ -132,7 +132,7 @@ int64_t dflash_cache_free_pages(const dflash_cache *c);
  *   gamma_h [d] device
  *   c_out   [T, d] device, written in `dtype`
  *   ws      device workspace of at least dflash_ctx_project_ws_bytes(...)
- * T == 0 is a no-op.  kd % 8 == 0, d % 8 == 0.
+ * T == 0 is a no-op.  kd % 8 == 0, d % 8 == 0, d <= 16384.
  * ---------------------------------------------------------------------- */
 size_t dflash_ctx_project_ws_bytes(int64_t T, int64_t kd, int64_t d, int32_t dtype);
 int dflash_ctx_project(const void *x_raw, int64_t T, int64_t kd, const void *w_fc,
@@ -194,8 +194,8 @@ const char *dflash_strerror(int status);
  * ---------------------------------------------------------------------- */
 typedef enum {
   DFLASH_STAGE_CTX_GEMM = 0,     /* fc: X_raw . W_fc^T, split-K partials */
-  DFLASH_STAGE_CTX_REDUCE = 1,   /* fc split-K reduction */
-  DFLASH_STAGE_CTX_NORM = 2,     /* hidden_norm */
+  DFLASH_STAGE_CTX_REDUCE = 1,   /* reserved: the fc split-K sum is fused into CTX_NORM */
+  DFLASH_STAGE_CTX_NORM = 2,     /* fc split-K sum fused with hidden_norm */
   DFLASH_STAGE_QKV_GEMM = 3,     /* q_proj of H, k_proj/v_proj of [C; H] */
   DFLASH_STAGE_QKV_EPILOGUE = 4, /* QK-norm, RoPE, Q to workspace, K/V to cache */
   DFLASH_STAGE_ATTN = 5,         /* split-context block attention */
