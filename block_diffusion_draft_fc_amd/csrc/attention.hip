@@ -677,13 +677,13 @@ static hipError_t launch_attn_t(const AttnArgs& a, int items, hipStream_t s) {
   const int nqt = (a.qrows + 15) / 16;
 #define DFLASH_ATTN_CASE(DH_, NQT_, NQW_, QS_)                                                     \
   if (a.d_h == DH_ && nqt == NQT_) {                                                               \
-    hipLaunchKernelGGL((attn_split_kernel<T, DH_, NQW_, QS_>), dim3(items), dim3(256), 0, s, a);    \
+    launch((attn_split_kernel<T, DH_, NQW_, QS_>), dim3(items), dim3(256), 0, s, a);    \
     return hipGetLastError();                                                                      \
   }
   if constexpr (sizeof(T) == 2) {
 #define DFLASH_ATTN_LDS_CASE(DH_, NQT_)                                                          \
   if (a.d_h == DH_ && nqt == NQT_) {                                                             \
-    hipLaunchKernelGGL((attn_lds_kernel<DH_, NQT_>), dim3(items), dim3(256), 0, s, a);           \
+    launch((attn_lds_kernel<DH_, NQT_>), dim3(items), dim3(256), 0, s, a);           \
     return hipGetLastError();                                                                    \
   }
     DFLASH_ATTN_LDS_CASE(64, 1) DFLASH_ATTN_LDS_CASE(64, 2) DFLASH_ATTN_LDS_CASE(64, 3) DFLASH_ATTN_LDS_CASE(64, 4)
@@ -780,9 +780,9 @@ hipError_t launch_attn_combine(int dtype, const CombineArgs& a, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((rows + 3) / 4);
   if (dtype == 1)
-    hipLaunchKernelGGL(attn_combine_kernel<bf16>, dim3(blocks), dim3(256), 0, s, a);
+    launch(attn_combine_kernel<bf16>, dim3(blocks), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(attn_combine_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
+    launch(attn_combine_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

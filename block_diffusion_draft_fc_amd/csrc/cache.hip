@@ -44,9 +44,9 @@ hipError_t launch_cache_append(int dtype, const AppendArgs& a, int64_t n_rows, h
   if (total == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((total + 255) / 256);
   if (dtype == 1)
-    hipLaunchKernelGGL(cache_append_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, a, n_rows);
+    launch(cache_append_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, a, n_rows);
   else
-    hipLaunchKernelGGL(cache_append_kernel<uint32_t>, dim3(blocks), dim3(256), 0, s, a, n_rows);
+    launch(cache_append_kernel<uint32_t>, dim3(blocks), dim3(256), 0, s, a, n_rows);
   return hipGetLastError();
 }
 
@@ -57,7 +57,7 @@ __global__ void bt_update_kernel(BtUpdateArgs a) {
 
 hipError_t launch_bt_update(const BtUpdateArgs& a, hipStream_t s) {
   if (a.count == 0) return hipSuccess;
-  hipLaunchKernelGGL(bt_update_kernel, dim3(1), dim3(256), 0, s, a);
+  launch(bt_update_kernel, dim3(1), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

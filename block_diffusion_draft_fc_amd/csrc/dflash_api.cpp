@@ -36,6 +36,12 @@ size_t elem_bytes(int32_t dt) { return dt == DFLASH_BF16 ? 2 : 4; }
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+int env_int(const char* name, int dflt, int lo, int hi) {
+  const char* e = std::getenv(name);
+  const int v = e ? std::atoi(e) : dflt;
+  return std::min(std::max(v, lo), hi);
+}
+
 // ---------------------------------------------------------------- stage timing
 // While enabled, each stage of a call is bracketed by two HIP events recorded
 // on the caller's stream; the elapsed times are collected when read.
@@ -67,10 +73,24 @@ hipEvent_t take_event(Timing& t) {
   return e;
 }
 
-// Runs `f` (which enqueues the stage's kernels on `s`), bracketed by events when
-// timing is on and the stage does launch something.
+}  // namespace
+
+namespace dflash {
+LaunchEvents& launch_events() {
+  static thread_local LaunchEvents ev;
+  return ev;
+}
+}  // namespace dflash
+
+namespace {
+
+// Runs `f` (which enqueues the stage's kernels on `s`).  With timing on, the
+// stage's kernels carry an event pair (hipExtLaunchKernel start/stop events,
+// stamped when the kernels themselves start and end on the GPU); a stage that
+// launched nothing records nothing.
 template <class F>
 hipError_t staged(int stage, hipStream_t s, bool launches, F&& f) {
+  (void)s;
   Timing& t = timing();
   if (!launches) return f();
   bool on;
@@ -84,11 +104,15 @@ hipError_t staged(int stage, hipStream_t s, bool launches, F&& f) {
     }
   }
   if (!on || !a || !b) return f();
-  hipError_t e = hipEventRecord(a, s);
-  if (e == hipSuccess) e = f();
-  if (e == hipSuccess) e = hipEventRecord(b, s);
+  LaunchEvents& ev = launch_events();
+  ev.start = a;
+  ev.stop = b;
+  const hipError_t e = f();
+  const bool launched = ev.start == nullptr;
+  ev.start = nullptr;
+  ev.stop = nullptr;
   std::lock_guard<std::mutex> g(t.mu);
-  if (e == hipSuccess) {
+  if (e == hipSuccess && launched) {
     t.pending.push_back({stage, a, b});
   } else {
     t.pool.push_back(a);
@@ -113,11 +137,6 @@ struct SkinnyPlan {
   bool wide;   // gemm_wide_kernel (256-column tiles) instead of gemm_lds_kernel
 };
 
-int env_int(const char* name, int dflt, int lo, int hi) {
-  const char* e = std::getenv(name);
-  const int v = e ? std::atoi(e) : dflt;
-  return std::min(std::max(v, lo), hi);
-}
 
 // Plans for at most 64 rows (32 for fp32), tuned on the decode-round shapes:
 //  * long inputs (K >= 8192, bf16, <= 32 rows): gemm_wide_kernel, 256-column

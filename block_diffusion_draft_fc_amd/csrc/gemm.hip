@@ -122,10 +122,10 @@ static hipError_t launch_lds_t(const GemmArgs& a, int max_mt, size_t lds, hipStr
   const int blocks = a.p[0].blocks + (a.nprob > 1 ? a.p[1].blocks : 0);
   if (blocks == 0) return hipSuccess;
   switch (max_mt) {
-    case 1: hipLaunchKernelGGL((gemm_lds_kernel<T, 1>), dim3(blocks), dim3(256), lds, s, a); break;
-    case 2: hipLaunchKernelGGL((gemm_lds_kernel<T, 2>), dim3(blocks), dim3(256), lds, s, a); break;
-    case 3: hipLaunchKernelGGL((gemm_lds_kernel<T, 3>), dim3(blocks), dim3(256), lds, s, a); break;
-    case 4: hipLaunchKernelGGL((gemm_lds_kernel<T, 4>), dim3(blocks), dim3(256), lds, s, a); break;
+    case 1: launch((gemm_lds_kernel<T, 1>), dim3(blocks), dim3(256), lds, s, a); break;
+    case 2: launch((gemm_lds_kernel<T, 2>), dim3(blocks), dim3(256), lds, s, a); break;
+    case 3: launch((gemm_lds_kernel<T, 3>), dim3(blocks), dim3(256), lds, s, a); break;
+    case 4: launch((gemm_lds_kernel<T, 4>), dim3(blocks), dim3(256), lds, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -250,8 +250,8 @@ __global__ __launch_bounds__(256) void gemm_wide_kernel(GemmProb p) {
 hipError_t launch_gemm_wide(const GemmProb& p, hipStream_t s) {
   if (p.blocks == 0) return hipSuccess;
   switch (p.mt) {
-    case 1: hipLaunchKernelGGL((gemm_wide_kernel<1>), dim3(p.blocks), dim3(256), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((gemm_wide_kernel<2>), dim3(p.blocks), dim3(256), 0, s, p); break;
+    case 1: launch((gemm_wide_kernel<1>), dim3(p.blocks), dim3(256), 0, s, p); break;
+    case 2: launch((gemm_wide_kernel<2>), dim3(p.blocks), dim3(256), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -279,10 +279,10 @@ hipError_t launch_splitk_reduce(int out_dtype, const float* part, int splits, in
   if (MN == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((MN / 4 + 255) / 256);
   if (out_dtype == 1)
-    hipLaunchKernelGGL(splitk_reduce_kernel<bf16>, dim3(blocks), dim3(256), 0, s, part, splits, MN,
+    launch(splitk_reduce_kernel<bf16>, dim3(blocks), dim3(256), 0, s, part, splits, MN,
                        static_cast<bf16*>(out));
   else
-    hipLaunchKernelGGL(splitk_reduce_kernel<float>, dim3(blocks), dim3(256), 0, s, part, splits, MN,
+    launch(splitk_reduce_kernel<float>, dim3(blocks), dim3(256), 0, s, part, splits, MN,
                        static_cast<float*>(out));
   return hipGetLastError();
 }
@@ -339,10 +339,10 @@ hipError_t launch_reduce_rmsnorm(int dtype, const float* part, int splits, int64
   const int64_t quads = d / 4;
   const unsigned threads = (unsigned)std::min<int64_t>(1024, ((quads + 63) / 64) * 64);
   if (dtype == 1)
-    hipLaunchKernelGGL(reduce_rmsnorm_kernel<bf16>, dim3((unsigned)T), dim3(threads), 0, s, part, splits, T, d,
+    launch(reduce_rmsnorm_kernel<bf16>, dim3((unsigned)T), dim3(threads), 0, s, part, splits, T, d,
                        static_cast<const bf16*>(gamma), eps, static_cast<bf16*>(out));
   else
-    hipLaunchKernelGGL(reduce_rmsnorm_kernel<float>, dim3((unsigned)T), dim3(threads), 0, s, part, splits, T, d,
+    launch(reduce_rmsnorm_kernel<float>, dim3((unsigned)T), dim3(threads), 0, s, part, splits, T, d,
                        static_cast<const float*>(gamma), eps, static_cast<float*>(out));
   return hipGetLastError();
 }

@@ -1,12 +1,34 @@
 // Launch interface between the C-ABI host layer and the gfx950 kernels.
 // Every struct here is passed by value as a kernel argument.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "dflash_common.hpp"
 
 namespace dflash {
+
+// Events that the kernel launches of the stage being enqueued attach to (set
+// by the host timing layer, null when timing is off): the first launch takes
+// `start`, every launch `stop`, so the pair spans the stage's kernels from the
+// first one's start to the last one's end as the GPU executes them.
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+LaunchEvents& launch_events();   // per host thread
+
+template <typename F, typename... Args>
+inline void launch(F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t s, Args... args) {
+  LaunchEvents& ev = launch_events();
+  if (ev.stop != nullptr) {
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, ev.start, ev.stop, 0u, args...);
+    ev.start = nullptr;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+  }
+}
 
 constexpr int kMaxSeqs = 64;
 

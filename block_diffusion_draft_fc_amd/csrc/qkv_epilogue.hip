@@ -115,9 +115,9 @@ hipError_t launch_qkv_epilogue(int dtype, const QkvEpiArgs& a, hipStream_t s) {
   if (items == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((items + 3) / 4);
   if (dtype == 1)
-    hipLaunchKernelGGL(qkv_epilogue_kernel<bf16>, dim3(blocks), dim3(256), 0, s, a);
+    launch(qkv_epilogue_kernel<bf16>, dim3(blocks), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(qkv_epilogue_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
+    launch(qkv_epilogue_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -183,14 +183,15 @@ int dflash_kv_inject_attn(const dflash_layer_desc *L, dflash_cache *c, const voi
 const char *dflash_strerror(int status);
 
 /* ------------------------------------------------------------------------
- * Stage timing (a measurement aid, off by default).  While enabled, every
- * stage a call enqueues is bracketed by two HIP events recorded on that call's
- * stream, so a stage's time is the GPU time between its first kernel's start
- * and its last kernel's end on that stream.  dflash_timing_read waits for the
- * recorded events (it synchronises with them, never with the whole device),
- * folds them into per-stage totals and reports the launches and summed
- * milliseconds of one stage since the last reset.  Process-wide; thread-safe.
- * Stages that launch nothing (e.g. T == 0) are not recorded.
+ * Stage timing (a measurement aid, off by default).  While enabled, the
+ * kernels of every stage a call enqueues carry a pair of HIP events
+ * (hipExtLaunchKernel start/stop events): the first kernel's start and the
+ * last kernel's end as the GPU executes them, so a stage's time excludes the
+ * dispatch gaps before it.  dflash_timing_read waits for the recorded events
+ * (it synchronises with them, never with the whole device), folds them into
+ * per-stage totals and reports the launches and summed milliseconds of one
+ * stage since the last reset.  Process-wide; thread-safe.  Stages that launch
+ * nothing (e.g. T == 0) are not recorded.
  * ---------------------------------------------------------------------- */
 typedef enum {
   DFLASH_STAGE_CTX_GEMM = 0,     /* fc: X_raw . W_fc^T, split-K partials */
