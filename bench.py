@@ -88,6 +88,25 @@ def round_work(wl, L, n):
     return w
 
 
+# ---------------------------------------------------------------------------- HBM traffic record
+
+def traffic_record():
+    """Measured HBM bytes per attention launch (rocprofv3 FETCH_SIZE + WRITE_SIZE,
+    scaled by a plain copy's reading), from the record kept with the profiles -
+    or None when the attention kernel's source has changed since it was taken."""
+    import hashlib
+    rec_path = os.path.join(ROOT, "profiles", "attn_decode_ctx8k_traffic.json")
+    src_path = os.path.join(ROOT, "block_diffusion_draft_fc_amd", "csrc", "attention.hip")
+    try:
+        rec = json.load(open(rec_path))
+        sha = hashlib.sha256(open(src_path, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("attention_source_sha256") != sha:
+        return None
+    return int(rec["fetch_bytes_per_launch"]) + int(rec["write_bytes_per_launch"])
+
+
 # ---------------------------------------------------------------------------- CPU oracle leg
 
 def cpu_baseline(wl, budget_s):
@@ -305,7 +324,7 @@ def main():
         "attn_hbm_gbps": att["gbps"],
         "attn_hbm_frac_peak": att["hbm_frac"],
         "roofline": {"bound": "hbm", "achieved": att["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": att["hbm_frac"], "traffic": None, "kernel": "attn_lds_kernel<128,4> (split-context attention)",
+                     "frac": att["hbm_frac"], "traffic": traffic_record(), "kernel": "attn_lds_kernel<128,4> (split-context attention)",
                      "us_per_launch": att["us_per_launch"], "alg_bytes_per_launch": att["alg_bytes_per_launch"]},
         "round_alg_bytes": int(round_bytes),
         "round_hbm_gbps": round(round_bytes / (ms_per_step * 1e-3) / 1e9, 1),
