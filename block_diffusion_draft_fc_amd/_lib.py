@@ -29,7 +29,7 @@ class DFlashError(RuntimeError):
 class LayerDesc(C.Structure):
     _fields_ = [("d", C.c_int32), ("n_h", C.c_int32), ("n_kv", C.c_int32), ("d_h", C.c_int32),
                 ("eps", C.c_float), ("rope_theta", C.c_double), ("window", C.c_int32),
-                ("dtype", C.c_int32), ("w_qkv", C.c_void_p), ("w_o", C.c_void_p),
+                ("dtype", C.c_int32), ("residual", C.c_int32), ("w_qkv", C.c_void_p), ("w_o", C.c_void_p),
                 ("gamma_q", C.c_void_p), ("gamma_k", C.c_void_p)]
 
 
@@ -185,11 +185,12 @@ def dflash_ctx_project(x_raw, w_fc, gamma_h, eps, c_out, ws, stream=None) -> Non
 class Layer:
     """Device weights of one KV-injection attention layer and its descriptor."""
 
-    def __init__(self, w_qkv, w_o, gamma_q, gamma_k, n_h, n_kv, d_h, eps=1e-6, rope_theta=1e6, window=0):
+    def __init__(self, w_qkv, w_o, gamma_q, gamma_k, n_h, n_kv, d_h, eps=1e-6, rope_theta=1e6, window=0,
+                 residual=False):
         self.w_qkv, self.w_o, self.gamma_q, self.gamma_k = w_qkv, w_o, gamma_q, gamma_k
         self.d = w_qkv.shape[1]
         self.desc = LayerDesc(self.d, n_h, n_kv, d_h, float(eps), float(rope_theta), int(window),
-                              dtype_code(w_qkv.dtype), w_qkv.data_ptr(), w_o.data_ptr(),
+                              dtype_code(w_qkv.dtype), 1 if residual else 0, w_qkv.data_ptr(), w_o.data_ptr(),
                               gamma_q.data_ptr(), gamma_k.data_ptr())
 
 

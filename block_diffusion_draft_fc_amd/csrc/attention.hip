@@ -569,10 +569,12 @@ __global__ __launch_bounds__(256, 1) void attn_lds_kernel(AttnArgs a) {
   };
 
   // this wave's blocks: wave, wave + 4, ...; block i lives in stage i % 2.
-  // The query loads go out first and the first two blocks' loads right after,
-  // so that their latencies overlap.
+  // Block 0's loads go out first, then the query loads, then block 1's: the
+  // wait before the queries are stored covers block 0 as well and leaves
+  // block 1 in flight.
   const int my_n = nblk > wave ? (nblk - wave + 3) / 4 : 0;
   const int first = kbeg + 32 * wave;
+  if (my_n > 0) issue(first, 0);
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {
     const int idx = tid + 256 * i;                 // slot: slab idx / 64, lane idx % 64
@@ -581,7 +583,6 @@ __global__ __launch_bounds__(256, 1) void attn_lds_kernel(AttnArgs a) {
     const int col = 32 * (slab % DS) + 8 * (L >> 4);
     qstage[i] = (idx < QSLOTS && row < valid_q) ? load8(qbase + (int64_t)row * DH + col) : zero8<bf16>();
   }
-  if (my_n > 0) issue(first, 0);
   if (my_n > 1) issue(first + 128, 1);
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {

@@ -364,6 +364,7 @@ int check_layer(const dflash_layer_desc* L) {
   if (L->d <= 0 || L->n_h <= 0 || L->n_kv <= 0 || L->n_h % L->n_kv != 0) return DFLASH_ERR_SHAPE;
   if (L->d_h != 64 && L->d_h != 128) return DFLASH_ERR_SHAPE;
   if (L->d % 8 != 0 || L->window < 0 || !(L->eps >= 0.f) || !(L->rope_theta > 0.0)) return DFLASH_ERR_SHAPE;
+  if (L->residual != 0 && L->residual != 1) return DFLASH_ERR_ARG;
   if (!L->w_qkv || !L->w_o || !L->gamma_q || !L->gamma_k) return DFLASH_ERR_ARG;
   if (!aligned16(L->w_qkv) || !aligned16(L->w_o)) return DFLASH_ERR_ARG;
   return DFLASH_OK;
@@ -677,7 +678,10 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
   if (e == hipSuccess) e = staged(DFLASH_STAGE_O_GEMM, s, true, [&] { return run_gemms(dt, {go}, s); });
   if (e == hipSuccess)
     e = staged(DFLASH_STAGE_O_REDUCE, s, true,
-               [&] { return launch_splitk_reduce(dt, part_out, go.plan.splits, p.RB, L->d, out, s); });
+               [&] {
+                 return launch_splitk_reduce(dt, part_out, go.plan.splits, p.RB, L->d, L->residual ? H : nullptr,
+                                             out, s);
+               });
   if (e != hipSuccess) return DFLASH_ERR_HIP;
   commit_append(c, rows, ap);
   return DFLASH_OK;

@@ -258,32 +258,38 @@ hipError_t launch_gemm_wide(const GemmProb& p, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- split-K reduction
-// out[m][n] = sum_s part[s][m][n]; one thread per 4 outputs, the split loop
-// unrolled so that its loads are in flight together.
+// out[m][n] = sum_s part[s][m][n] (+ add[m][n] when add is given); one thread
+// per 4 outputs, the split loop unrolled so that its loads are in flight
+// together.
 
 template <typename Tout>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits,
-                                                            int64_t MN, Tout* __restrict__ out) {
+                                                            int64_t MN, const Tout* __restrict__ add,
+                                                            Tout* __restrict__ out) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= MN) return;
   f32x4 s = *reinterpret_cast<const f32x4*>(part + i);
 #pragma unroll 8
   for (int sp = 1; sp < splits; ++sp) s += *reinterpret_cast<const f32x4*>(part + (int64_t)sp * MN + i);
+  if (add != nullptr) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] += to_f32(add[i + e]);
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) out[i + e] = from_f32<Tout>(s[e]);
 }
 
 hipError_t launch_splitk_reduce(int out_dtype, const float* part, int splits, int64_t M, int64_t N,
-                                void* out, hipStream_t s) {
+                                const void* add, void* out, hipStream_t s) {
   const int64_t MN = M * N;
   if (MN == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((MN / 4 + 255) / 256);
   if (out_dtype == 1)
     launch(splitk_reduce_kernel<bf16>, dim3(blocks), dim3(256), 0, s, part, splits, MN,
-                       static_cast<bf16*>(out));
+           static_cast<const bf16*>(add), static_cast<bf16*>(out));
   else
     launch(splitk_reduce_kernel<float>, dim3(blocks), dim3(256), 0, s, part, splits, MN,
-                       static_cast<float*>(out));
+           static_cast<const float*>(add), static_cast<float*>(out));
   return hipGetLastError();
 }
 

@@ -63,9 +63,10 @@ hipError_t launch_gemm_lds(int dtype, const GemmArgs& a, int max_mt, size_t lds_
 // bf16 only, at most 32 rows (mt <= 2); 256-column tiles (n_tiles = ceil(N/256)).
 hipError_t launch_gemm_wide(const GemmProb& p, hipStream_t s);
 
-// out[m][n] = sum_s part[s][m][n], written as fp32 (out_dtype 0) or bf16 (1).
+// out[m][n] = sum_s part[s][m][n] (+ add[m][n] when add is not null), written
+// as fp32 (out_dtype 0) or bf16 (1); add has the output dtype.
 hipError_t launch_splitk_reduce(int out_dtype, const float* part, int splits, int64_t M,
-                                int64_t N, void* out, hipStream_t s);
+                                int64_t N, const void* add, void* out, hipStream_t s);
 
 // C[t] = u[t] / sqrt(mean(u[t]^2) + eps) * gamma with u[t] = sum_s part[s][t],
 // one row of d per workgroup; d % 4 == 0 and d <= 16384.

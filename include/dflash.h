@@ -69,6 +69,10 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
  * Shapes: n_h % n_kv == 0, d_h in {64, 128}, (n_h/n_kv)*B <= 64, d % 8 == 0.
  * window 0 = full attention; window > 0 = sliding layer where query position
  * p sees key position j iff p - j < window (no upper bound).
+ * residual 1 adds the block rows H to the output, so that in a stack of layers
+ * sharing one context C the output of layer l is the block input of layer l+1
+ * (H_{l+1} = H_l + o_proj_l; the decoder internals between layers are not part
+ * of this library).
  * ---------------------------------------------------------------------- */
 typedef struct dflash_layer_desc {
   int32_t d, n_h, n_kv, d_h;
@@ -76,6 +80,8 @@ typedef struct dflash_layer_desc {
   double rope_theta;    /* RoPE base; w_i = theta^(-2i/d_h) */
   int32_t window;
   int32_t dtype;        /* dflash_dtype */
+  int32_t residual;     /* 0: out = o_proj(attn); 1: out = H + o_proj(attn), the
+                           chaining of a layer stack (the next layer's block rows) */
   const void *w_qkv;
   const void *w_o;
   const void *gamma_q;
@@ -165,7 +171,8 @@ int dflash_cache_crop(dflash_cache *c, const int32_t *new_len, void *stream);
  *   C      [T, d] device: new context rows, sequence r owns rows
  *          [cu_ctx[r], cu_ctx[r+1]) (cu_ctx: host [n_seqs + 1]); n_r >= 0.
  *   H      [n_seqs * B, d] device: block rows, sequence r owns rows r*B .. r*B+B-1.
- *   out    [n_seqs * B, d] device: o_proj output of the block rows.
+ *   out    [n_seqs * B, d] device: o_proj output of the block rows (plus H when
+ *          the layer has residual set; out may then be the same buffer as H).
  * For each sequence r with cache length L_r: the n_r + B new K/V rows get RoPE
  * positions L_r .. L_r+n_r+B-1 (context rows first), the queries the last B of
  * them; all n_r + B rows are appended (len_r = L_r + n_r + B), then the

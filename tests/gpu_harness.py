@@ -50,7 +50,8 @@ class GpuModel:
             lw = G.layer_weights(wl, li)
             self.layers.append(L.Layer(*(to_device(lw[k], wl, device) for k in ("w_qkv", "w_o", "gamma_q", "gamma_k")),
                                        n_h=wl.n_h, n_kv=wl.n_kv, d_h=wl.d_h, eps=wl.eps,
-                                       rope_theta=wl.rope_theta, window=wl.layer_window(li)))
+                                       rope_theta=wl.rope_theta, window=wl.layer_window(li),
+                                       residual=wl.n_layers > 1))
             need = [int(self.L0[r] + grow[r] + wl.B) for r in range(wl.R)]
             if wl.page_size:
                 ps = wl.page_size

@@ -32,9 +32,9 @@ def test_struct_layout_matches_c(tmp_path):
 #include <stddef.h>
 #include "dflash.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu\\n", sizeof(dflash_layer_desc), offsetof(dflash_layer_desc, eps),
+  printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(dflash_layer_desc), offsetof(dflash_layer_desc, eps),
          offsetof(dflash_layer_desc, rope_theta), offsetof(dflash_layer_desc, window),
-         offsetof(dflash_layer_desc, gamma_k));
+         offsetof(dflash_layer_desc, residual), offsetof(dflash_layer_desc, gamma_k));
   printf("%zu %zu %zu %zu\\n", sizeof(dflash_cache_desc), offsetof(dflash_cache_desc, capacity),
          offsetof(dflash_cache_desc, k_pool), offsetof(dflash_cache_desc, block_table));
   return 0;
@@ -44,7 +44,7 @@ int main(void) {
     lines = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
     ld, cd = L.LayerDesc, L.CacheDesc
     assert [int(x) for x in lines[0].split()] == [C.sizeof(ld), ld.eps.offset, ld.rope_theta.offset,
-                                                  ld.window.offset, ld.gamma_k.offset]
+                                                  ld.window.offset, ld.residual.offset, ld.gamma_k.offset]
     assert [int(x) for x in lines[1].split()] == [C.sizeof(cd), cd.capacity.offset, cd.k_pool.offset,
                                                   cd.block_table.offset]
 
@@ -134,7 +134,7 @@ def _layer(**kw):
     base = dict(d=512, n_h=8, n_kv=2, d_h=64, eps=1e-6, rope_theta=1e6, window=0, dtype=L.DFLASH_BF16)
     base.update(kw)
     return L.LayerDesc(base["d"], base["n_h"], base["n_kv"], base["d_h"], base["eps"], base["rope_theta"],
-                       base["window"], base["dtype"], FAKE, FAKE, FAKE, FAKE)
+                       base["window"], base["dtype"], base.get("residual", 0), FAKE, FAKE, FAKE, FAKE)
 
 
 def test_kv_inject_validation():

@@ -10,9 +10,13 @@ Cases: the walkthrough layer (d 512, 8 heads of 64, k = 3, 3 context rows and a
 block of 4, fp32); the fresh 1024-row context of a Qwen3-4B-shaped layer; all
 64 rounds of the Qwen3-8B-shaped decode workload on an 8192-row cache (the
 configuration the benchmark times); the first rounds of the 16-request ragged
-paged workload; and small cases that reach every kernel variant and edge
-(d_h 64 / 128, 1 to 4 query tiles per K/V head, B = 1, rounds without new
-context, empty caches, sliding windows, paged ragged batches).
+paged workload; the 5-layer hybrid sliding/full stack at its layer shapes; and
+small cases that reach every kernel variant and edge (d_h 64 / 128, 1 to 4
+query tiles per K/V head, B = 1, rounds without new context, empty caches,
+sliding windows, paged ragged batches, residual stacks).  In a stack the
+oracle chains H_{l+1} = H_l + out_l in fp64 while the GPU stores each layer's
+H_{l+1} in bf16, so later layers see inputs one bf16 rounding apart; the bar
+is unchanged.
 """
 import numpy as np
 import pytest
@@ -45,9 +49,21 @@ def run_rounds(wl, rounds, check_cache=True):
         got = gm.round(x, cu, H)
         ref, _ = orc.round(x, cu, H, wl.B)
         for li in range(wl.n_layers):
-            e = rel_l2(got[li], ref[li])
-            worst = max(worst, e)
-            assert e <= TOL[wl.dtype], f"round {rnd} layer {li}: rel-L2 {e:.3e}"
+            if wl.n_layers == 1:
+                e = rel_l2(got[li], ref[li])
+                worst = max(worst, e)
+                assert e <= TOL[wl.dtype], f"round {rnd} layer {li}: rel-L2 {e:.3e}"
+                continue
+            # a stack layer stores H_in + o_proj in one bf16 rounding: its error
+            # against H_in + the oracle's o_proj may be the o_proj bar plus that
+            # rounding (at most 2^-9 of the stored sum's norm)
+            h_in = H if li == 0 else got[li - 1]
+            want = h_in + ref[li]
+            err = float(np.linalg.norm(got[li] - want))
+            o_norm = float(np.linalg.norm(ref[li]))
+            allow = TOL[wl.dtype] * o_norm + 2.0 ** -9 * float(np.linalg.norm(want))
+            worst = max(worst, err / o_norm)
+            assert err <= allow, f"round {rnd} layer {li}: |err| {err:.3e} > {allow:.3e} (|o| {o_norm:.3e})"
         for li, cache in enumerate(gm.caches):
             assert cache.lengths() == orc.lengths(li), f"round {rnd}: cache lengths"
     if check_cache:
@@ -120,6 +136,15 @@ def test_ragged_paged_16_requests():
     run_rounds(wl, 4)
 
 
+def test_stack5_hybrid_window_full_shapes():
+    """The 5-layer hybrid stack (sliding window 4096 on layers 0/2/4, full on
+    1/3, one shared context, residual chaining, per-layer crop) at its full
+    layer shapes, with 2 requests on 8192-row caches so the windows bite."""
+    wl = configs.STACK5_HYBRID.scaled(name="stack5_hybrid_swa4096_ctx8k_batch2", R=2, prefill_len=8192,
+                                      rounds=2)
+    run_rounds(wl, wl.rounds)
+
+
 # ------------------------------------------------------------------ small cases: kernel variants and edges
 
 def _small(name, **kw):
@@ -155,6 +180,8 @@ SMALL = [
            page_size=64, rounds=4),
     _small("ragged_paged_r4_window", R=4, d_h=128, B=16, prefill="uniform", prefill_range=(100, 900),
            page_size=128, window=300, sliding_layers=(0,), rounds=3),
+    _small("stack3_window_residual", n_layers=3, d_h=128, B=16, R=2, prefill_len=600, window=256,
+           sliding_layers=(0, 2), rounds=3),
 ]
 
 
