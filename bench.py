@@ -50,6 +50,8 @@ def parse():
                          "by the library calls; best: time both, report the faster")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fresh-ctx", action="store_true",
+                    help="skip the MFMA-utilisation pass over the fresh 1024-row context projections")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 8 times (scales HBM counters)")
     return ap.parse_args()
@@ -137,6 +139,71 @@ def cpu_baseline(wl, budget_s):
     return {"value": done / spent, "unit": "draft blocks/s", "cores": cores, "kind": "oracle",
             "sample": f"first {done} of the {wl.rounds} seeded rounds (8192-row cache, 1-16 new rows, block 16), "
                       f"fp64 NumPy, {spent:.1f} s of round work; weight set-up excluded"}
+
+
+# ---------------------------------------------------------------------------- fresh-context projections
+
+def fresh_ctx_projections(iters):
+    """MFMA utilisation of the projections on the fresh-context workload (one
+    Qwen3-4B-shaped layer: d 2560, 32/8 heads of 128, k = 5 -> 12800-wide raw
+    context, 1024 new context rows plus a block of 16, bf16): the layer call on
+    an empty cache, timed per stage with the library's kernel-attached events.
+    The fc GEMM (1024 x 12800 -> 2560) and the K/V GEMM of [C; H] (1040 x 2560 ->
+    2048) run on the MFMA tile kernel; Q (16 rows) and o_proj (16 rows) stream
+    their weights and are HBM-bound."""
+    import torch
+
+    from block_diffusion_draft_fc_amd import _lib as L
+    from workloads import configs, generate as G
+    from workloads.device import to_device
+
+    wl = configs.FRESH_CTX
+    dev = "cuda:0"
+    n = wl.n_fixed
+    fc, lw = G.fc_weights(wl), G.layer_weights(wl, 0)
+    w_fc, gamma_h = to_device(fc["w_fc"], wl, dev), to_device(fc["gamma_h"], wl, dev)
+    layer = L.Layer(*(to_device(lw[k], wl, dev) for k in ("w_qkv", "w_o", "gamma_q", "gamma_k")),
+                    n_h=wl.n_h, n_kv=wl.n_kv, d_h=wl.d_h, eps=wl.eps, rope_theta=wl.rope_theta)
+    cache = L.Cache(1, wl.n_kv, wl.d_h, torch.bfloat16, (n + wl.B + 63) // 64 * 64, device=dev)
+    x, _, H = G.round_inputs(wl, 0, [n])
+    xd, Hd = to_device(x, wl, dev), to_device(H, wl, dev)
+    C = torch.empty((n, wl.d), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((wl.B, wl.d), dtype=torch.bfloat16, device=dev)
+    ctx_ws = torch.empty(L.dflash_ctx_project_ws_bytes(n, wl.kd, wl.d, torch.bfloat16), dtype=torch.uint8,
+                         device=dev)
+    layer_ws = torch.empty(L.dflash_kv_inject_attn_ws_bytes(layer, cache, n, wl.B), dtype=torch.uint8, device=dev)
+
+    def call():
+        L.dflash_ctx_project(xd, w_fc, gamma_h, wl.eps, C, ctx_ws)
+        L.dflash_kv_inject_attn(layer, cache, C, [0, n], Hd, wl.B, out, layer_ws)
+        L.dflash_cache_crop(cache, [0])
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    L.timing_reset()
+    L.timing_enable(True)
+    for _ in range(iters):
+        call()
+    torch.cuda.synchronize()
+    st = L.timing_read()
+    L.timing_enable(False)
+    us = {k: v[1] / max(v[0], 1) * 1e3 for k, v in st.items()}
+    qd, kvd, d, kd, B = wl.n_h * wl.d_h, wl.n_kv * wl.d_h, wl.d, wl.kd, wl.B
+    flops = {"ctx_gemm": 2 * n * kd * d, "qkv_gemm": 2 * (B * qd + (n + B) * 2 * kvd) * d, "o_gemm": 2 * B * qd * d}
+    res = {"workload": wl.name, "iters": iters, "peak_tflops": BF16_PEAK_TFLOPS}
+    for k, f in flops.items():
+        t = us[k]
+        res[k] = {"us": round(t, 2), "tflops": round(f / t / 1e6, 1), "mfma_frac": round(f / t / 1e6 / BF16_PEAK_TFLOPS, 4)}
+    gemm_us = sum(us[k] for k in flops)
+    all_us = gemm_us + us["ctx_norm"] + us["qkv_epilogue"] + us["o_reduce"]
+    tot = sum(flops.values())
+    res["gemms"] = {"us": round(gemm_us, 2), "tflops": round(tot / gemm_us / 1e6, 1),
+                    "mfma_frac": round(tot / gemm_us / 1e6 / BF16_PEAK_TFLOPS, 4)}
+    res["gemms+reductions"] = {"us": round(all_us, 2), "tflops": round(tot / all_us / 1e6, 1),
+                               "mfma_frac": round(tot / all_us / 1e6 / BF16_PEAK_TFLOPS, 4)}
+    res["stage_us"] = {k: round(v, 2) for k, v in us.items() if st[k][0]}
+    return res
 
 
 # ---------------------------------------------------------------------------- GPU leg
@@ -324,6 +391,9 @@ def main():
         "kernels": kernels,
         "stage_us": stage_us,
     }
+    if not args.no_fresh_ctx:
+        log("bench: fresh-context projections")
+        res["fresh_ctx_projections"] = fresh_ctx_projections(20)
     if not args.no_cpu_baseline:
         log("bench: timing the fp64 oracle on the host")
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -134,7 +134,9 @@ int attn_target_items() {
 
 struct SkinnyPlan {
   int32_t k_chunk, splits, mt, n_tiles;
-  bool wide;   // gemm_wide_kernel (256-column tiles) instead of gemm_lds_kernel
+  bool wide;         // gemm_wide_kernel (256-column tiles) instead of gemm_lds_kernel
+  bool tile;         // gemm_tile_kernel (256x256 MFMA tiles) for many rows
+  int32_t m_tiles;   // tile plans only
 };
 
 
@@ -146,7 +148,7 @@ struct SkinnyPlan {
 SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, size_t eb) {
   static const int wide_target = env_int("DFLASH_GEMM_WIDE_BLOCKS", 256, 1, 1 << 16);
   static const int lds_target = env_int("DFLASH_GEMM_LDS_BLOCKS", 1024, 1, 1 << 16);
-  SkinnyPlan p;
+  SkinnyPlan p{};
   p.mt = (int32_t)std::max<int64_t>(1, cdiv(M, 16));
   p.wide = eb == 2 && p.mt <= 2 && K >= 8192;
   if (p.wide) {
@@ -167,6 +169,49 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, size_t eb) {
   p.k_chunk = (int32_t)kc;
   p.splits = (int32_t)cdiv(K, kc);
   return p;
+}
+
+// Many rows (bf16): gemm_tile_kernel, 256x256 tiles, one workgroup per CU.
+// Splitting K fills more CUs but writes (and makes the consumer read) one fp32
+// partial product per split, so the split count minimises a two-term estimate:
+// MFMA time (tiles x splits workgroups in rounds of 256, each at a per-CU rate
+// of 60% of the bf16 peak) plus the partial traffic (8 bytes per output and
+// split at 5 TB/s).  Chunks are whole 64-wide K-steps.
+SkinnyPlan plan_tile(int64_t M, int64_t N, int64_t K) {
+  static const int forced = env_int("DFLASH_GEMM_TILE_SPLITS", 0, 0, 1 << 16);
+  SkinnyPlan p{};
+  p.tile = true;
+  p.m_tiles = (int32_t)cdiv(M, 256);
+  p.n_tiles = (int32_t)cdiv(N, 256);
+  const int64_t tiles = (int64_t)p.m_tiles * p.n_tiles;
+  const int64_t max_splits = std::max<int64_t>(1, std::min<int64_t>(K / 64, 32));
+  int64_t best = 1;
+  if (forced > 0) {
+    best = std::min<int64_t>(forced, max_splits);
+  } else {
+    const double cu_flops = 2.5e15 / 256 * 0.6, bw = 5e12;
+    const double tile_flops = 2.0 * 256 * 256 * (double)K;
+    double best_t = 0;
+    for (int64_t sp = 1; sp <= max_splits; ++sp) {
+      const double rounds = (double)cdiv(tiles * sp, 256);
+      const double t = rounds * tile_flops / sp / cu_flops + (double)sp * M * N * 8 / bw;
+      if (sp == 1 || t < best_t) { best = sp; best_t = t; }
+    }
+  }
+  const int64_t kc = cdiv(cdiv(K, best), 64) * 64;
+  p.k_chunk = (int32_t)kc;
+  p.splits = (int32_t)cdiv(K, kc);
+  return p;
+}
+
+// Whether a bf16 product of M rows takes gemm_tile_kernel: enough rows to fill
+// 256-row tiles reasonably, K a multiple of the 64-wide step and N of 4 (row
+// alignment follows from the 16-byte alignment every device pointer of the
+// interface must have).  Depends on shapes only, so that a workspace sized
+// from the plan fits the plan the call makes.
+bool tile_eligible(int64_t M, int64_t N, int64_t K, size_t eb) {
+  static const int min_rows = env_int("DFLASH_GEMM_TILE_MIN_ROWS", 256, 1, 1 << 30);
+  return eb == 2 && M >= min_rows && K % 64 == 0 && N % 4 == 0;
 }
 
 size_t lds_bytes(const GemmProb& p, size_t eb) { return (size_t)p.mt * 16 * (size_t)(p.k_chunk + 8) * eb; }
@@ -193,7 +238,10 @@ GemmJob make_job(const void* x0, int64_t m0, const void* x1, int64_t m1, const v
                  int64_t K, size_t eb) {
   GemmJob j;
   j.x0 = x0; j.m0 = m0; j.x1 = x1; j.m1 = m1; j.w = w; j.N = N; j.K = K;
-  j.plan = plan_skinny(std::min<int64_t>(m0 + m1, rows_per_problem(eb)), N, K, eb);
+  if (tile_eligible(m0 + m1, N, K, eb))
+    j.plan = plan_tile(m0 + m1, N, K);
+  else
+    j.plan = plan_skinny(std::min<int64_t>(m0 + m1, rows_per_problem(eb)), N, K, eb);
   j.part = nullptr;
   return j;
 }
@@ -234,6 +282,24 @@ hipError_t run_gemms(int32_t dt, const std::vector<GemmJob>& jobs, hipStream_t s
   std::vector<GemmProb> probs;
   for (const auto& j : jobs) {
     if (j.m0 + j.m1 == 0) continue;
+    if (j.plan.tile) {
+      TileProb t{};
+      t.x0 = static_cast<const bf16*>(j.x0);
+      t.x1 = static_cast<const bf16*>(j.x1);
+      t.m0 = (int32_t)j.m0;
+      t.m1 = (int32_t)j.m1;
+      t.w = static_cast<const bf16*>(j.w);
+      t.part = j.part;
+      t.N = (int32_t)j.N;
+      t.K = (int32_t)j.K;
+      t.k_chunk = j.plan.k_chunk;
+      t.splits = j.plan.splits;
+      t.m_tiles = j.plan.m_tiles;
+      t.n_tiles = j.plan.n_tiles;
+      hipError_t e = launch_gemm_tile(t, s);
+      if (e != hipSuccess) return e;
+      continue;
+    }
     if (j.plan.wide) {
       std::vector<GemmProb> w;
       job_problems(j, eb, &w);

@@ -18,6 +18,8 @@
 //    barrier, and long per-wave streams.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace dflash {
@@ -254,6 +256,190 @@ hipError_t launch_gemm_wide(const GemmProb& p, hipStream_t s) {
     case 2: launch((gemm_wide_kernel<2>), dim3(p.blocks), dim3(256), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- tiled (bf16, many rows)
+// For the fresh-context projections (hundreds to thousands of rows), where the
+// product is MFMA-bound: a workgroup computes a 256x256 output tile over one
+// K-chunk with eight waves, each owning a 128x64 block, i.e. 8x4 tiles of
+// 16x16x32 MFMAs, 128 fp32 accumulators per lane (two waves per SIMD).
+//
+// The K loop steps by 64 through two LDS stages of 64 KB; the copies of step
+// s + 1 are issued right after the barrier of step s and land while step s
+// computes.  Operands reach LDS by direct-to-LDS copies that each move 8 rows
+// x 128 bytes (whole cache lines: copies of half lines run at well under half
+// the rate), so a stage holds each tile row's 64 K-values contiguously, in
+// 1 KB blocks of 8 rows.  An MFMA fragment read (16 rows, one 16-byte chunk of
+// each) would then hit the same banks from many rows, so chunk c of tile row R
+// is stored at position c ^ (R % 8) ^ ((R / 8) % 2) of its row - the copy
+// picks, for each lane, the chunk its LDS slot must hold - which makes every
+// 16-lane group of a ds_read_b128 cover all 64 banks once.  An A fragment
+// feeds 4 MFMAs, a B fragment 8.  One barrier per step: after it, every
+// wave's copies of the step have landed and every wave is done with the
+// previous step, whose stage is the one refilled.
+//
+// Workgroups are ordered for the L2 of each XCD: consecutive block indices go
+// to different XCDs, so the block index is remapped so that each XCD's share
+// is a contiguous run of tiles of one split, in groups of kTileGroupM row
+// tiles - the XCD's workgroups then read the same activation and weight rows.
+// Requirements (checked by the planner): bf16, K and the K-chunk multiples of
+// 64, N a multiple of 4, 16-byte aligned rows.
+
+namespace {
+constexpr int kTileBM = 256, kTileBN = 256, kTileBK = 64;
+constexpr int kTileWaves = 8;
+constexpr int kTileBlocks = kTileBM / 8;   // 1 KB blocks (8 rows x 128 B) of A (and of B) per stage
+constexpr int kTileGroupM = 4;
+constexpr int kXcds = 8;
+}
+
+// One direct-to-LDS copy of 16 bytes per lane (lane l's bytes land at
+// lds + 16 * l), written in asm so that the compiler does not track it: its
+// own tracking of these copies cannot follow the LDS stages across the K loop
+// and waits for every copy in flight before reading a stage.  The kernel
+// orders these copies with explicit s_waitcnt vmcnt instead; other
+// vector-memory waits the compiler emits stay correct, since copies it does
+// not count only make a vmcnt wait stricter.  M0 (the LDS base of the copy) is
+// a reserved register, so the asm saves and restores it rather than declaring
+// it clobbered.
+__device__ __forceinline__ void lds_copy16(const void* src, const unsigned char* lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(base)
+      : "memory");
+}
+
+__global__ __launch_bounds__(512, 1) void gemm_tile_kernel(TileProb p) {
+  // one array per stage and operand, so that each stage is named statically
+  __shared__ __align__(16) unsigned char sa0[kTileBlocks * 1024], sb0[kTileBlocks * 1024];
+  __shared__ __align__(16) unsigned char sa1[kTileBlocks * 1024], sb1[kTileBlocks * 1024];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // XCD-aware order: block b runs on XCD b % 8; give XCD x the run
+  // [x * per, (x + 1) * per) of virtual indices (the remainder keeps its own)
+  int v = blockIdx.x;
+  const int per = gridDim.x / kXcds;
+  if (v < per * kXcds) v = (v % kXcds) * per + v / kXcds;
+  const int tiles = p.m_tiles * p.n_tiles;
+  const int split = v / tiles;
+  const int t = v - split * tiles;
+  const int band = kTileGroupM * p.n_tiles;
+  const int first_m = (t / band) * kTileGroupM;
+  const int gsz = min(p.m_tiles - first_m, kTileGroupM);
+  const int mt = first_m + (t % band) % gsz, nt = (t % band) / gsz;
+  const int m_base = mt * kTileBM, n_base = nt * kTileBN;
+  const int k_begin = split * p.k_chunk;
+  const int k_end = min(p.K, k_begin + p.k_chunk);
+  const int nsteps = (k_end - k_begin) / kTileBK;   // >= 1: K and chunks are multiples of 64
+  const int M = p.m0 + p.m1;
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+
+  // Copies of one K-step: block b of a stage holds tile rows 8 b .. 8 b + 7;
+  // wave w copies blocks w, w + 8, w + 16, w + 24 of A and of B.  Lane l
+  // fills row 8 b + l / 8, slot l % 8, with the chunk that the swizzle puts
+  // there.  Rows past M (columns past N) read row 0 and are never stored.
+  constexpr int PER_WAVE = kTileBlocks / kTileWaves;
+  const int crow = lane >> 3;
+  const int cchunk = (lane & 7) ^ crow ^ (wave & 1);   // blocks w + 8 i all have parity w & 1
+  auto issue = [&](int step, auto st) {
+    unsigned char* da = st.value ? sa1 : sa0;
+    unsigned char* db = st.value ? sb1 : sb0;
+    const int k = k_begin + step * kTileBK + 8 * cchunk;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int b = wave + kTileWaves * i;
+      int m = m_base + 8 * b + crow;
+      m = m < M ? m : 0;
+      const bf16* xa = m < p.m0 ? p.x0 + (int64_t)m * p.K : p.x1 + (int64_t)(m - p.m0) * p.K;
+      lds_copy16(xa + k, da + b * 1024);
+      int n = n_base + 8 * b + crow;
+      n = n < p.N ? n : 0;
+      lds_copy16(p.w + (int64_t)n * p.K + k, db + b * 1024);
+    }
+  };
+
+  // wave (wm, wn) owns rows 128 wm .. +127 and columns 64 wn .. +63 of the tile
+  const int wm = wave >> 2, wn = wave & 3;
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Fragment reads: lane l takes row R = l % 16 of a 16-row group (2 blocks)
+  // and chunk 4 kk + l / 16 of the step's 64 K-values, found at its swizzled
+  // position.
+  const int fr = lane & 15;
+  const int fkey = (fr & 7) ^ (fr >> 3);
+  const int frow_off = (fr >> 3) * 1024 + (fr & 7) * 128;
+  const int foff0 = frow_off + (((lane >> 4)) ^ fkey) * 16;
+  const int foff1 = frow_off + ((4 + (lane >> 4)) ^ fkey) * 16;
+
+  // The products are taken as W x^T (B fragments in the MFMA's first operand)
+  // so that each lane ends up with four consecutive output columns of a row.
+  auto compute = [&](auto st) {
+    const unsigned char* ga = (st.value ? sa1 : sa0) + (8 * wm) * 2048;
+    const unsigned char* gb = (st.value ? sb1 : sb0) + (4 * wn) * 2048;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int off = kk ? foff1 : foff0;
+      bf16x8 af[8], bfr[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(gb + j * 2048 + off);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) af[i] = *reinterpret_cast<const bf16x8*>(ga + i * 2048 + off);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mma32(bfr[j], af[i], acc[i][j]);
+    }
+  };
+
+  // Step s: wait for this wave's copies of step s (the only ones in flight),
+  // barrier, refill the stage of step s - 1 with step s + 1, compute.  The
+  // barrier is s_barrier in asm, a compiler memory barrier as well;
+  // __syncthreads() would add a release fence that waits for every copy.
+  auto step = [&](int s, auto st, auto st_next) {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (s + 1 < nsteps) issue(s + 1, st_next);
+    compute(st);
+  };
+  issue(0, S0{});
+  for (int s = 0; s < nsteps; s += 2) {
+    step(s, S0{}, S1{});
+    if (s + 1 < nsteps) step(s + 1, S1{}, S0{});
+  }
+
+  // lane l holds, for row m = 16 i + l % 16 of the wave's block, the four
+  // consecutive columns 16 j + 4 (l / 16) .. +3: one 16-byte store each
+  float* out = p.part + (int64_t)split * M * p.N;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int m = m_base + 128 * wm + 16 * i + (lane & 15);
+    if (m >= M) continue;
+    float* row = out + (int64_t)m * p.N;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n_base + 64 * wn + 16 * j + 4 * (lane >> 4);
+      if (n < p.N) *reinterpret_cast<f32x4*>(row + n) = acc[i][j];
+    }
+  }
+}
+
+hipError_t launch_gemm_tile(const TileProb& p, hipStream_t s) {
+  const int blocks = p.m_tiles * p.n_tiles * p.splits;
+  if (blocks == 0) return hipSuccess;
+  launch(gemm_tile_kernel, dim3(blocks), dim3(64 * kTileWaves), 0, s, p);
   return hipGetLastError();
 }
 

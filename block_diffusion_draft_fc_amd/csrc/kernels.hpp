@@ -57,6 +57,20 @@ struct GemmArgs {
 // Rows handled by one weight-streaming problem.
 constexpr int kSkinnyMaxM = 64;
 
+// Tiled bf16 product for many rows: part[s][m][n] over the virtual rows
+// [x0 (m0 rows); x1 (m1 rows)] (row stride K), 256x256 tiles, K and k_chunk
+// multiples of 64.
+struct TileProb {
+  const bf16* x0;
+  const bf16* x1;
+  int32_t m0, m1;
+  const bf16* w;     // [N][K]
+  float* part;       // [splits][m0 + m1][N]
+  int32_t N, K;
+  int32_t k_chunk, splits, m_tiles, n_tiles;
+};
+hipError_t launch_gemm_tile(const TileProb& p, hipStream_t s);
+
 // LDS budget for the staged activation slice of one gemm_lds_kernel workgroup.
 constexpr int kLdsGemmBytes = 64 * 1024;
 hipError_t launch_gemm_lds(int dtype, const GemmArgs& a, int max_mt, size_t lds_bytes, hipStream_t s);

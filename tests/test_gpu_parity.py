@@ -114,6 +114,27 @@ def test_ctx_project_bf16(T):
     assert rel_l2(from_device(C), ref) <= TOL["bf16"]
 
 
+# Shapes that take the 256x256 MFMA tile GEMM (bf16, at least 256 rows, K a
+# multiple of 64): a last row tile holding one row, last column tiles of 64 and
+# 8 columns, a K of 2080 (a multiple of 32 only) and (last case) 3000, which
+# take the weight-streaming kernels instead.
+@pytest.mark.parametrize("T,d,k_layers", [(257, 1088, 2), (600, 520, 8), (512, 1024, 3), (400, 1040, 2),
+                                          (300, 1000, 3)])
+def test_ctx_project_bf16_many_rows(T, d, k_layers):
+    wl = configs.FRESH_CTX.scaled(name=f"ctx_project_T{T}_d{d}_k{k_layers}", d=d, k_layers=k_layers, n_h=8,
+                                  n_kv=2, d_h=64)
+    say(f"case ctx_project {wl.name}")
+    fc = G.fc_weights(wl)
+    x, _, _ = G.round_inputs(wl, 0, [T])
+    ref = O.ctx_project(x, fc["w_fc"], fc["gamma_h"], wl.eps)
+    C = torch.empty((T, wl.d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(L.dflash_ctx_project_ws_bytes(T, wl.kd, wl.d, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    L.dflash_ctx_project(to_device(x, wl), to_device(fc["w_fc"], wl), to_device(fc["gamma_h"], wl), wl.eps, C, ws)
+    torch.cuda.synchronize()
+    assert rel_l2(from_device(C), ref) <= TOL["bf16"]
+
+
 # ------------------------------------------------------------------ the named workloads
 
 def test_walkthrough_layer_f32():
@@ -182,6 +203,12 @@ SMALL = [
            page_size=128, window=300, sliding_layers=(0,), rounds=3),
     _small("stack3_window_residual", n_layers=3, d_h=128, B=16, R=2, prefill_len=600, window=256,
            sliding_layers=(0, 2), rounds=3),
+    # many new context rows: the context projection and the K/V projection of
+    # [C; H] take the MFMA tile GEMM, with the C/H boundary inside a row tile
+    _small("fresh_ctx300_tile_gemm", d=512, k_layers=2, B=16, prefill="none", n_new="fixed", n_fixed=300,
+           rounds=1),
+    _small("fresh_ctx2x200_tile_gemm_r2", d=512, k_layers=2, d_h=128, B=16, R=2, prefill="none",
+           n_new="fixed", n_fixed=200, rounds=1),
 ]
 
 
