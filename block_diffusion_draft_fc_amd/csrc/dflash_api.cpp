@@ -148,9 +148,10 @@ struct SkinnyPlan {
 SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, size_t eb) {
   static const int wide_target = env_int("DFLASH_GEMM_WIDE_BLOCKS", 256, 1, 1 << 16);
   static const int lds_target = env_int("DFLASH_GEMM_LDS_BLOCKS", 1024, 1, 1 << 16);
+  static const int wide_min_k = env_int("DFLASH_GEMM_WIDE_MIN_K", 8192, 0, 1 << 30);
   SkinnyPlan p{};
   p.mt = (int32_t)std::max<int64_t>(1, cdiv(M, 16));
-  p.wide = eb == 2 && p.mt <= 2 && K >= 8192;
+  p.wide = eb == 2 && p.mt <= 2 && K >= wide_min_k;
   if (p.wide) {
     p.n_tiles = (int32_t)cdiv(N, 256);
     int64_t splits = std::max<int64_t>(1, cdiv(wide_target, p.n_tiles));
@@ -438,6 +439,11 @@ int check_layer(const dflash_layer_desc* L) {
 
 struct KvPlan {
   int64_t R, B, T, RB, qd, kvd, group, qrows;
+  // fused_qkv: one product of [C; H] with all of W_qkv (Q columns of the C
+  // rows are computed and ignored) when every row fits one weight-streaming
+  // problem - the weights are then streamed once, in one launch; otherwise Q
+  // of H and K/V of [C; H] as two products (gq, gkv).
+  bool fused_qkv;
   GemmJob gq, gkv, go;
   size_t off_q, off_pq, off_pkv, off_po, off_pml, off_attn, off_pout, total;
   int64_t max_items;
@@ -451,8 +457,15 @@ KvPlan plan_kv(const dflash_layer_desc* L, const dflash_cache* c, int64_t T, int
   p.kvd = (int64_t)L->n_kv * L->d_h;
   p.group = L->n_h / L->n_kv;
   p.qrows = cdiv(p.group * B, 16) * 16;
-  p.gq = make_job(nullptr, 0, nullptr, p.RB, L->w_qkv, p.qd, L->d, eb);
-  p.gkv = make_job(nullptr, T, nullptr, p.RB, nullptr, 2 * p.kvd, L->d, eb);
+  p.fused_qkv = T + p.RB <= rows_per_problem(eb);
+  if (p.fused_qkv) {
+    p.gkv = make_job(nullptr, T, nullptr, p.RB, L->w_qkv, p.qd + 2 * p.kvd, L->d, eb);
+    p.gq = p.gkv;
+    p.gq.plan.splits = 0;   // no separate partials
+  } else {
+    p.gq = make_job(nullptr, 0, nullptr, p.RB, L->w_qkv, p.qd, L->d, eb);
+    p.gkv = make_job(nullptr, T, nullptr, p.RB, nullptr, 2 * p.kvd, L->d, eb);
+  }
   p.go = make_job(nullptr, p.RB, nullptr, 0, L->w_o, L->d, p.qd, eb);
   // work items of one attention launch: at most the target count plus one
   // partial chunk per (sequence, head); on a paged cache the chunk may be capped
@@ -462,7 +475,7 @@ KvPlan plan_kv(const dflash_layer_desc* L, const dflash_cache* c, int64_t T, int
   if (c->desc.page_size > 0) p.max_items += cdiv(c->desc.capacity * L->n_kv, kAttnMaxChunkPages - 2);
   size_t o = 0;
   p.off_q = o;   o = align_up(o + (size_t)p.R * L->n_kv * p.qrows * L->d_h * eb);
-  p.off_pq = o;  o = align_up(o + job_part_bytes(p.gq));
+  p.off_pq = o;  o = align_up(o + (p.fused_qkv ? 0 : job_part_bytes(p.gq)));
   p.off_pkv = o; o = align_up(o + job_part_bytes(p.gkv));
   p.off_po = o;  o = align_up(o + (size_t)p.max_items * p.qrows * L->d_h * sizeof(float));
   p.off_pml = o; o = align_up(o + (size_t)p.max_items * 2 * p.qrows * sizeof(float));
@@ -667,17 +680,34 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
 
   // 2. q/k/v projection: Q from the block rows, K/V from [C; H] with one weight
   GemmJob gq = p.gq, gkv = p.gkv;
-  gq.x1 = H; gq.part = part_q;
   gkv.x0 = C; gkv.x1 = H; gkv.part = part_kv;
-  gkv.w = static_cast<const char*>(L->w_qkv) + (size_t)p.qd * L->d * eb;
-  if (e == hipSuccess) e = staged(DFLASH_STAGE_QKV_GEMM, s, true, [&] { return run_gemms(dt, {gq, gkv}, s); });
+  if (p.fused_qkv) {
+    if (e == hipSuccess) e = staged(DFLASH_STAGE_QKV_GEMM, s, true, [&] { return run_gemms(dt, {gkv}, s); });
+  } else {
+    gq.x1 = H; gq.part = part_q;
+    gkv.w = static_cast<const char*>(L->w_qkv) + (size_t)p.qd * L->d * eb;
+    if (e == hipSuccess) e = staged(DFLASH_STAGE_QKV_GEMM, s, true, [&] { return run_gemms(dt, {gq, gkv}, s); });
+  }
 
   // 3. norms, RoPE, Q to the workspace, K/V into the cache
   CacheView cv = view_of(c);
   if (e == hipSuccess) {
     QkvEpiArgs a{};
-    a.part_q = part_q; a.part_kv = part_kv;
-    a.sq = gq.plan.splits; a.skv = gkv.plan.splits;
+    if (p.fused_qkv) {
+      // [splits][T + RB][qd + 2 kvd]: Q of the block rows at rows T.., K/V after column qd
+      const int64_t w = p.qd + 2 * p.kvd, split = (T + p.RB) * w;
+      a.part_q = part_kv + T * w;
+      a.q_row = w; a.q_split = split;
+      a.part_kv = part_kv + p.qd;
+      a.kv_row = w; a.kv_split = split;
+      a.sq = a.skv = gkv.plan.splits;
+    } else {
+      a.part_q = part_q;
+      a.q_row = p.qd; a.q_split = p.RB * p.qd;
+      a.part_kv = part_kv;
+      a.kv_row = 2 * p.kvd; a.kv_split = (T + p.RB) * 2 * p.kvd;
+      a.sq = gq.plan.splits; a.skv = gkv.plan.splits;
+    }
     a.gamma_q = L->gamma_q; a.gamma_k = L->gamma_k;
     a.q_ws = q_ws;
     a.cache = cv;

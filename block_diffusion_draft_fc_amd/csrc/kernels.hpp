@@ -94,8 +94,12 @@ struct SeqTable {
   int32_t cu[kMaxSeqs + 1];  // context row offsets
 };
 struct QkvEpiArgs {
-  const float* part_q;   // [sq][R*B][n_h*d_h]
-  const float* part_kv;  // [skv][T + R*B][2*n_kv*d_h]
+  // Split-K partials: Q of block row b (0 <= b < R*B), split s, column c at
+  // part_q[s * q_split + b * q_row + c]; K/V of row m of [C; H] (K columns
+  // first, then V) at part_kv[s * kv_split + m * kv_row + c].
+  const float* part_q;
+  const float* part_kv;
+  int64_t q_row, q_split, kv_row, kv_split;
   int32_t sq, skv;
   const void* gamma_q;
   const void* gamma_k;

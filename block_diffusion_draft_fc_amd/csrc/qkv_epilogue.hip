@@ -25,7 +25,7 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvEpiArgs a) {
   const int RB = a.R * a.B;
   const int Mkv = a.T + RB;
   const int half = a.d_h >> 1;
-  const int qd = a.n_h * a.d_h, kvd = a.n_kv * a.d_h;
+  const int kvd = a.n_kv * a.d_h;
   const int64_t n_q_items = (int64_t)RB * a.n_h;
   const int64_t n_kv_items = (int64_t)Mkv * a.n_kv;
   if (item >= n_q_items + 2 * n_kv_items) return;
@@ -43,15 +43,15 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvEpiArgs a) {
 
   // split-K reduction of the two elements of this lane's rotation pair
   const float* part;
-  int splits, width, col;
-  int64_t stride;
-  if (kind == 0) { part = a.part_q; splits = a.sq; width = qd; col = head * a.d_h; stride = (int64_t)RB * qd; }
-  else { part = a.part_kv; splits = a.skv; width = 2 * kvd; col = (kind == 2 ? kvd : 0) + head * a.d_h;
-         stride = (int64_t)Mkv * 2 * kvd; }
+  int splits, col;
+  int64_t row_stride, stride;
+  if (kind == 0) { part = a.part_q; splits = a.sq; row_stride = a.q_row; stride = a.q_split; col = head * a.d_h; }
+  else { part = a.part_kv; splits = a.skv; row_stride = a.kv_row; stride = a.kv_split;
+         col = (kind == 2 ? kvd : 0) + head * a.d_h; }
   const bool act = lane < half;
   float x0 = 0.f, x1 = 0.f;
   if (act) {
-    const float* src = part + (int64_t)m * width + col + lane;
+    const float* src = part + (int64_t)m * row_stride + col + lane;
 #pragma unroll 8
     for (int s = 0; s < splits; ++s) { x0 += src[s * stride]; x1 += src[s * stride + half]; }
   }
