@@ -69,6 +69,28 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// One direct-to-LDS copy of 16 bytes per lane (lane l's bytes land at
+// lds + 16 * l), written in asm so that the compiler does not track it: its
+// own tracking of these copies cannot follow LDS stages chosen at run time or
+// carried around a loop, and waits for every copy in flight before reading a
+// stage.  The kernels order these copies with explicit s_waitcnt vmcnt instead
+// (vector memory operations of a wave complete in order); other
+// vector-memory waits the compiler emits stay correct, since copies it does
+// not count only make a vmcnt wait stricter.  M0 (the LDS base of the copy) is
+// a reserved register, so the asm saves and restores it rather than declaring
+// it clobbered.
+__device__ __forceinline__ void lds_copy16(const void* src, const unsigned char* lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(base)
+      : "memory");
+}
+
 // Cache addressing shared by the append paths and the attention kernel.
 // Contiguous caches are the special case of one "page" of `rows` slots per
 // sequence whose physical index is the sequence index.

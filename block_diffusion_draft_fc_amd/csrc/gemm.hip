@@ -294,27 +294,6 @@ constexpr int kTileGroupM = 4;
 constexpr int kXcds = 8;
 }
 
-// One direct-to-LDS copy of 16 bytes per lane (lane l's bytes land at
-// lds + 16 * l), written in asm so that the compiler does not track it: its
-// own tracking of these copies cannot follow the LDS stages across the K loop
-// and waits for every copy in flight before reading a stage.  The kernel
-// orders these copies with explicit s_waitcnt vmcnt instead; other
-// vector-memory waits the compiler emits stay correct, since copies it does
-// not count only make a vmcnt wait stricter.  M0 (the LDS base of the copy) is
-// a reserved register, so the asm saves and restores it rather than declaring
-// it clobbered.
-__device__ __forceinline__ void lds_copy16(const void* src, const unsigned char* lds) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)lds);
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(base)
-      : "memory");
-}
-
 __global__ __launch_bounds__(512, 1) void gemm_tile_kernel(TileProb p) {
   // one array per stage and operand, so that each stage is named statically
   __shared__ __align__(16) unsigned char sa0[kTileBlocks * 1024], sb0[kTileBlocks * 1024];
