@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   const int g = local / a.chunks[r];
   const int chunk = local - g * a.chunks[r];
   const int key_hi = a.key_hi[r];
-  const int kbeg = (a.key_lo[r] & ~31) + chunk * a.chunk_keys;
+  const int kbeg = (a.key_lo[r] & ~63) + chunk * a.chunk_keys;
   const int kend = min(kbeg + a.chunk_keys, key_hi);
   const int nblk = kend > kbeg ? (kend - kbeg + 31) >> 5 : 0;
 
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(256, 1) void attn_lds_kernel(AttnArgs a) {
   const int g = local / a.chunks[r];
   const int chunk = local - g * a.chunks[r];
   const int key_hi = a.key_hi[r];
-  const int kbeg = (a.key_lo[r] & ~31) + chunk * a.chunk_keys;
+  const int kbeg = (a.key_lo[r] & ~63) + chunk * a.chunk_keys;
   const int kend = min(kbeg + a.chunk_keys, key_hi);
   const int nblk = kend > kbeg ? (kend - kbeg + 31) >> 5 : 0;
 
@@ -720,7 +720,7 @@ __global__ __launch_bounds__(256, 1) void attn_ring_kernel(AttnArgs a) {
   const int g = local / a.chunks[r];
   const int chunk = local - g * a.chunks[r];
   const int key_hi = a.key_hi[r];
-  const int kbeg = (a.key_lo[r] & ~31) + chunk * a.chunk_keys;
+  const int kbeg = (a.key_lo[r] & ~63) + chunk * a.chunk_keys;
   const int kend = min(kbeg + a.chunk_keys, key_hi);
   const int nblk = kend > kbeg ? (kend - kbeg + 31) >> 5 : 0;
 
@@ -880,6 +880,208 @@ __global__ __launch_bounds__(256, 1) void attn_ring_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- bf16: shared ring of 64-key blocks
+// attn_ring_kernel with 64-key blocks: twice the keys per barrier and per
+// dependency chain (K reads -> S -> softmax -> PV) of each wave, and V^T copied
+// in whole 128-byte lines (64 keys of one head dim).  A stage holds
+//   K: operand-order slabs (half hh, key tile kt, head-dim step s), lane l's
+//      16 bytes at 16 l: key 32 hh + krow(l % 16) + 4 kt, dims 32 s + 8 (l / 16);
+//   V^T: one 128-byte row per head dim R (the block's 64 keys), in 16-byte
+//      chunks of 8 keys, chunk c at position c ^ (R % 8) ^ ((R / 8) % 2) - each
+//      copy moves 8 whole rows and picks, per lane, the chunk its slot holds;
+//      a fragment read (16 consecutive rows, one chunk) then covers all banks.
+// Block starts are multiples of 64, so a block never crosses a page.
+template <int DH, int NST>
+__global__ __launch_bounds__(256, 1) void attn_ring64_kernel(AttnArgs a) {
+  using V8 = bf16x8;
+  static_assert(NST >= 2 && NST <= 8, "blocks in flight are counted by wait_vm_blocks (up to 6 after the current)");
+  constexpr int DS = DH / 32;                 // K=32 steps over the head dim
+  constexpr int DT = DH / 16;                 // 16-dim tiles of the head dim
+  constexpr int KSLABS = 4 * DS;              // (hh, kt, s)
+  constexpr int VROWS = DH / 8;               // 1 KB copies of 8 V^T rows
+  constexpr int COPIES = KSLABS + VROWS;
+  constexpr int PER_WAVE = COPIES / 4;
+  constexpr int STAGE = COPIES * 1024;
+  __shared__ __align__(16) unsigned char ring[NST * STAGE];
+  __shared__ int32_t s_page[kAttnMaxChunkPages];
+
+  const int item = blockIdx.x;
+  int r = 0;
+  while (r + 1 < a.R && item >= a.item_base[r + 1]) ++r;
+  const int local = item - a.item_base[r];
+  const int g = local / a.chunks[r];
+  const int chunk = local - g * a.chunks[r];
+  const int key_hi = a.key_hi[r];
+  const int kbeg = (a.key_lo[r] & ~63) + chunk * a.chunk_keys;
+  const int kend = min(kbeg + a.chunk_keys, key_hi);
+  const int nblk = kend > kbeg ? (kend - kbeg + 63) >> 6 : 0;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j16 = lane & 15, q4 = lane >> 4;
+  const int valid_q = a.group * a.B;
+
+  const int row = 16 * wave + j16;
+  const bf16* qbase = static_cast<const bf16*>(a.q_ws) + (int64_t)(r * a.n_kv + g) * a.qrows * DH;
+  V8 qv[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) qv[s] = row < valid_q ? load8(qbase + (int64_t)row * DH + 32 * s + 8 * q4) : zero8<bf16>();
+  const int vlo = a.window > 0 ? a.qpos0[r] + row % a.B - a.window + 1 : INT_MIN;
+  const int vis_lo_max = a.qpos0[r] + a.B - a.window;   // largest row bound (sliding layers)
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[DT];
+#pragma unroll
+  for (int d = 0; d < DT; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int pg0 = kbeg / a.cache.page_rows;
+  const int npg = nblk > 0 ? (kend - 1) / a.cache.page_rows - pg0 + 1 : 0;
+  for (int i = tid; i < npg; i += 256) s_page[i] = (int32_t)cache_page(a.cache, r, (pg0 + i) * a.cache.page_rows);
+#pragma unroll
+  for (int s = 0; s < DS; ++s) asm volatile("" ::"v"(qv[s]));   // queries waited for before any copy
+  __syncthreads();
+
+  const bf16* kpool = static_cast<const bf16*>(a.cache.k_pool);
+  const bf16* vpool = static_cast<const bf16*>(a.cache.v_pool);
+  const int krow = 8 * (j16 >> 2) + (j16 & 3);   // + 4 kt + 32 hh: key of A-operand row j16
+  // V^T copies: lane l fills row 8 i + l / 8, slot l % 8, with the chunk the swizzle puts there
+  const int vrow_in = lane >> 3;
+  // V^T fragment reads: row 16 d + j16, chunk 4 kk + q4 at its swizzled position
+  const int vkey = (j16 & 7) ^ (j16 >> 3);
+  const int voff0 = j16 * 128 + ((q4) ^ vkey) * 16;
+  const int voff1 = j16 * 128 + ((4 + q4) ^ vkey) * 16;
+
+  auto issue = [&](int b) {
+    const int blk = kbeg + 64 * b;
+    const int64_t page = s_page[blk / a.cache.page_rows - pg0];
+    const int slot = blk % a.cache.page_rows;
+    const bf16* kb = kpool + k_offset(a.cache, page, g, slot);
+    const bf16* vb = vpool + v_offset(a.cache, page, g, slot);
+    unsigned char* sb = ring + (b % NST) * STAGE;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int idx = wave * PER_WAVE + i;
+      const bf16* src;
+      if (idx < KSLABS) {
+        const int hk = idx / DS, s = idx - hk * DS;
+        const int hh = hk >> 1, kt = hk & 1;
+        src = kb + (int64_t)(32 * hh + krow + 4 * kt) * DH + 32 * s + 8 * q4;
+      } else {
+        const int R = 8 * (idx - KSLABS) + vrow_in;
+        const int c = (lane & 7) ^ (R & 7) ^ ((R >> 3) & 1);
+        src = vb + (int64_t)R * a.cache.page_rows + 8 * c;
+      }
+      lds_copy16(src, sb + idx * 1024);
+    }
+  };
+
+  auto process = [&](int b) {
+    const unsigned char* sb = ring + (b % NST) * STAGE;
+    const unsigned char* kbs = sb + 16 * lane;
+    const unsigned char* vbs = sb + KSLABS * 1024;
+    const int blk = kbeg + 64 * b;
+    // scores: lane (j16, q4) holds row j16's keys blk + 32 hh + 8 q4 .. +7 in sv[hh]
+    f32x8 sv[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      V8 kv[2][DS];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int s = 0; s < DS; ++s)
+          kv[kt][s] = *reinterpret_cast<const V8*>(kbs + (((2 * hh + kt) * DS + s) * 1024));
+      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int s = 0; s < DS; ++s)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) sacc[kt] = mma32(kv[kt][s], qv[s], sacc[kt]);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[hh][4 * kt + e] = sacc[kt][e] * a.scale_log2;
+    }
+    const bool all_vis = blk + 64 <= key_hi && (a.window <= 0 || blk >= vis_lo_max);
+    if (!all_vis) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = blk + 32 * hh + 8 * q4 + e;
+          sv[hh][e] = ((key >= vlo) & (key < key_hi)) ? sv[hh][e] : -INFINITY;
+        }
+    }
+    float mx = sv[0][0];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sv[hh][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    // the reference maximum moves only when the block maximum exceeds it by
+    // more than 8 (log2 units): every p <= 256, O rescaled on those blocks only
+    const bool need = mx > m_run + 8.f;
+    const float m_new = need ? mx : m_run;
+    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+    m_run = m_new;
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    V8 pv[2];
+    float ps = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      f32x8 p;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(sv[hh][e] - m_use);
+        ps += p[e];
+      }
+      pv[hh] = cvt8<bf16>(p);
+    }
+    l_run = l_run * alpha + ps;
+    if (__any(need)) {
+#pragma unroll
+      for (int d = 0; d < DT; ++d) o[d] *= alpha;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      V8 vv[DT];
+#pragma unroll
+      for (int d = 0; d < DT; ++d) vv[d] = *reinterpret_cast<const V8*>(vbs + d * 2048 + (kk ? voff1 : voff0));
+      // stale rows past the end of the cache may hold any bits: zero their V
+      // entries so that p = 0 cannot meet an Inf or NaN (last block only)
+      const int key0 = blk + 32 * kk + 8 * q4;
+      if (key0 + 8 > key_hi) {
+#pragma unroll
+        for (int d = 0; d < DT; ++d)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (key0 + e >= key_hi) vv[d][e] = static_cast<bf16>(0.f);
+      }
+#pragma unroll
+      for (int d = 0; d < DT; ++d) o[d] = mma32(vv[d], pv[kk], o[d]);
+    }
+  };
+
+  constexpr int AHEAD = NST - 1;   // blocks in flight
+  for (int b = 0; b < min(AHEAD, nblk); ++b) issue(b);
+  for (int b = 0; b < nblk; ++b) {
+    wait_vm_blocks<PER_WAVE>(min(nblk - 1 - b, AHEAD - 1));
+    asm volatile("s_barrier" ::: "memory");
+    if (b + AHEAD < nblk) issue(b + AHEAD);   // into the stage of block b - 1
+    process(b);
+  }
+
+  float* po = a.part_o + (int64_t)item * a.qrows * DH;
+#pragma unroll
+  for (int d = 0; d < DT; ++d) *reinterpret_cast<f32x4*>(po + (int64_t)row * DH + 16 * d + 4 * q4) = o[d];
+  float l = l_run;
+  l += __shfl_xor(l, 16, kWave);
+  l += __shfl_xor(l, 32, kWave);
+  if (q4 == 0) {
+    float* pml = a.part_ml + (int64_t)item * 2 * a.qrows;
+    pml[row] = m_run;
+    pml[a.qrows + row] = l;
+  }
+}
+
 template <typename T>
 static hipError_t launch_attn_t(const AttnArgs& a, int items, hipStream_t s) {
   const int nqt = (a.qrows + 15) / 16;
@@ -889,14 +1091,25 @@ static hipError_t launch_attn_t(const AttnArgs& a, int items, hipStream_t s) {
     return hipGetLastError();                                                                      \
   }
   if constexpr (sizeof(T) == 2) {
-    // four query tiles: the shared-ring kernel (four 16 KB stages for d_h 128:
-    // deeper rings measured slower, and 64 KB leaves room for two workgroups
-    // per CU); DFLASH_ATTN_RING=0 selects attn_lds_kernel instead
+    // four query tiles: the shared ring of 64-key blocks, two stages (64 KB,
+    // so two workgroups share a CU and cover each other's load latency: deeper
+    // rings, one workgroup per CU, measured slower); DFLASH_ATTN_RING=32 takes
+    // the ring of 32-key blocks, 0 attn_lds_kernel
     static const int ring = [] {
       const char* e = std::getenv("DFLASH_ATTN_RING");
-      return e ? std::atoi(e) : 1;
+      return e ? std::atoi(e) : 64;
     }();
-    if (ring && nqt == 4) {
+    if (ring == 64 && nqt == 4) {
+      if (a.d_h == 128) {
+        launch((attn_ring64_kernel<128, 2>), dim3(items), dim3(256), 0, s, a);
+        return hipGetLastError();
+      }
+      if (a.d_h == 64) {
+        launch((attn_ring64_kernel<64, 4>), dim3(items), dim3(256), 0, s, a);
+        return hipGetLastError();
+      }
+    }
+    if (ring == 32 && nqt == 4) {
       if (a.d_h == 128) {
         launch((attn_ring_kernel<128, 4>), dim3(items), dim3(256), 0, s, a);
         return hipGetLastError();

@@ -735,12 +735,13 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
       aa.key_hi[r] = (int32_t)hi;
       aa.key_lo[r] = (int32_t)lo;
       aa.qpos0[r] = (int32_t)(c->len[r] + n[r]);
-      keys[r] = hi - (lo & ~int64_t(31));
+      keys[r] = hi - (lo & ~int64_t(63));
       total += keys[r] * L->n_kv;
     }
-    // keys per work item: a multiple of the 32-key block, at least one block
-    // per wave, sized so that the items cover the target count
-    int64_t chunk = cdiv(cdiv(total, attn_target_items()), 32) * 32;
+    // keys per work item: a multiple of 64 (the largest key block of the
+    // kernels; chunks start at multiples of 64), at least 128, sized so that
+    // the items cover the target count
+    int64_t chunk = cdiv(cdiv(total, attn_target_items()), 64) * 64;
     chunk = std::max<int64_t>(chunk, 128);
     // an item's keys may span at most kAttnMaxChunkPages pages (its page list
     // is staged in LDS); two pages go to a chunk that does not start on a page
