@@ -686,19 +686,6 @@ __global__ __launch_bounds__(256, 1) void attn_lds_kernel(AttnArgs a) {
 // barrier per block, after which the block has landed for every wave and the
 // previous block's stage is free to refill.  The K/V operand slabs and the
 // score layout are those of attn_lds_kernel.
-template <int N>
-__device__ __forceinline__ void wait_vm_blocks(int blocks) {
-  // s_waitcnt vmcnt(blocks * N) for blocks in 0..6 (the count is an immediate)
-  switch (blocks) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * N) : "memory"); break;
-    case 3: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * N) : "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * N) : "memory"); break;
-    case 5: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(5 * N) : "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(6 * N) : "memory"); break;
-  }
-}
 
 template <int DH, int NST>
 __global__ __launch_bounds__(256, 1) void attn_ring_kernel(AttnArgs a) {

@@ -136,6 +136,7 @@ struct SkinnyPlan {
   int32_t k_chunk, splits, mt, n_tiles;
   bool wide;         // gemm_wide_kernel (256-column tiles) instead of gemm_lds_kernel
   bool tile;         // gemm_tile_kernel (256x256 MFMA tiles) for many rows
+  bool stream;       // gemm_stream_kernel (per-wave weight streams) for at most 32 rows
   int32_t m_tiles;   // tile plans only
 };
 
@@ -149,8 +150,18 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, size_t eb) {
   static const int wide_target = env_int("DFLASH_GEMM_WIDE_BLOCKS", 256, 1, 1 << 16);
   static const int lds_target = env_int("DFLASH_GEMM_LDS_BLOCKS", 1024, 1, 1 << 16);
   static const int wide_min_k = env_int("DFLASH_GEMM_WIDE_MIN_K", 8192, 0, 1 << 30);
+  static const int use_stream = env_int("DFLASH_GEMM_STREAM", 1, 0, 1);
   SkinnyPlan p{};
   p.mt = (int32_t)std::max<int64_t>(1, cdiv(M, 16));
+  // at most 32 rows, K below the wide kernel's range: per-wave weight streams
+  // in 512-wide K-chunks
+  if (use_stream && eb == 2 && p.mt <= 2 && K < wide_min_k && K % 64 == 0 && N % 4 == 0) {
+    p.stream = true;
+    p.n_tiles = (int32_t)cdiv(N, 16 * gemm_stream_waves(p.mt));
+    p.k_chunk = 512;
+    p.splits = (int32_t)cdiv(K, 512);
+    return p;
+  }
   p.wide = eb == 2 && p.mt <= 2 && K >= wide_min_k;
   if (p.wide) {
     p.n_tiles = (int32_t)cdiv(N, 256);
@@ -298,6 +309,23 @@ hipError_t run_gemms(int32_t dt, const std::vector<GemmJob>& jobs, hipStream_t s
       t.m_tiles = j.plan.m_tiles;
       t.n_tiles = j.plan.n_tiles;
       hipError_t e = launch_gemm_tile(t, s);
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    if (j.plan.stream) {
+      TileProb t{};
+      t.x0 = static_cast<const bf16*>(j.x0);
+      t.x1 = static_cast<const bf16*>(j.x1);
+      t.m0 = (int32_t)j.m0;
+      t.m1 = (int32_t)j.m1;
+      t.w = static_cast<const bf16*>(j.w);
+      t.part = j.part;
+      t.N = (int32_t)j.N;
+      t.K = (int32_t)j.K;
+      t.k_chunk = j.plan.k_chunk;
+      t.splits = j.plan.splits;
+      t.n_tiles = j.plan.n_tiles;
+      hipError_t e = launch_gemm_stream(t, j.plan.mt, s);
       if (e != hipSuccess) return e;
       continue;
     }

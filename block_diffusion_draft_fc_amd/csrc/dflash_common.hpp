@@ -91,6 +91,21 @@ __device__ __forceinline__ void lds_copy16(const void* src, const unsigned char*
       : "memory");
 }
 
+// s_waitcnt vmcnt(blocks * N) for blocks in 0..6 (the count must be an
+// immediate): "at most the copies of the `blocks` later steps remain".
+template <int N>
+__device__ __forceinline__ void wait_vm_blocks(int blocks) {
+  switch (blocks) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * N) : "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * N) : "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * N) : "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(5 * N) : "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(6 * N) : "memory"); break;
+  }
+}
+
 // Cache addressing shared by the append paths and the attention kernel.
 // Contiguous caches are the special case of one "page" of `rows` slots per
 // sequence whose physical index is the sequence index.

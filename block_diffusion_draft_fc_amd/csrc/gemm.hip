@@ -422,6 +422,120 @@ hipError_t launch_gemm_tile(const TileProb& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- weight streaming (bf16, at most 32 rows)
+// part[split][m][n] = sum over the split's K-chunk of x[m][k] w[n][k], for the
+// q/k/v and o projections of a draft round (16..32 rows): the product is the
+// weight stream, so each wave owns 16 weight rows and streams them through its
+// own direct-to-LDS ring of 64-wide K-steps - 16 rows x 128 bytes per step,
+// two copies of 8 whole rows (whole cache lines), chunks XOR-swizzled so that
+// the MFMA fragment reads are conflict free - with no barrier in the loop.  The
+// workgroup's activation chunk (at most 32 rows x 512) is staged once in LDS in
+// MFMA operand order.  Products are taken as W x^T, so each lane ends with four
+// consecutive columns of one row (16-byte partial stores).
+// Requirements (checked by the planner): bf16, K a multiple of 64, N of 4.
+constexpr int kStreamKC = 512;   // K-chunk per workgroup
+
+template <int MT, int WAVES, int NST>
+__global__ __launch_bounds__(64 * WAVES) void gemm_stream_kernel(TileProb p) {
+  constexpr int XS = kStreamKC / 32;                         // activation slabs per 16-row tile
+  __shared__ __align__(16) unsigned char sx[MT * XS * 1024];
+  __shared__ __align__(16) unsigned char ring[WAVES][NST * 2048];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nt = blockIdx.x % p.n_tiles, split = blockIdx.x / p.n_tiles;
+  const int k0 = split * p.k_chunk;
+  const int kc = min(p.k_chunk, p.K - k0);                   // a multiple of 64
+  const int nsteps = kc / 64;
+  const int n0 = nt * (16 * WAVES) + 16 * wave;               // this wave's 16 weight rows
+  const int M = p.m0 + p.m1;
+
+  // activation chunk in operand order: slab (mt, s), lane l: row 16 mt + l % 16,
+  // k 32 s + 8 (l / 16) .. +7 (rows past M as zeros)
+  const int slabs = MT * (kc / 32);
+  for (int i = threadIdx.x; i < slabs * 64; i += 64 * WAVES) {
+    const int slab = i >> 6, l = i & 63;
+    const int mt = slab / (kc / 32), s = slab - mt * (kc / 32);
+    const int m = 16 * mt + (l & 15);
+    bf16x8 v = {};
+    if (m < M) {
+      const bf16* row = m < p.m0 ? p.x0 + (int64_t)m * p.K : p.x1 + (int64_t)(m - p.m0) * p.K;
+      v = *reinterpret_cast<const bf16x8*>(row + k0 + 32 * s + 8 * (l >> 4));
+    }
+    *reinterpret_cast<bf16x8*>(sx + (mt * XS + s) * 1024 + 16 * l) = v;
+  }
+  __syncthreads();
+
+  // copies of step t into stage t % NST: copy j (0, 1) moves rows 8 j .. 8 j + 7
+  // of the wave's 16; lane l fills row 8 j + l / 8, slot l % 8, with chunk
+  // (l % 8) ^ key(row), key(R) = (R % 8) ^ (R / 8).  Rows past N read row 0 and
+  // are never stored.
+  const int crow = lane >> 3;
+  unsigned char* my = ring[wave];
+  auto issue = [&](int t) {
+    unsigned char* st = my + (t % NST) * 2048;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int R = 8 * j + crow;
+      const int c = (lane & 7) ^ (R & 7) ^ j;
+      int n = n0 + R;
+      n = n < p.N ? n : 0;
+      lds_copy16(p.w + (int64_t)n * p.K + k0 + 64 * t + 8 * c, st + j * 1024);
+    }
+  };
+  // fragment reads: lane (j16, q4) takes row j16, chunk 4 kk + q4 at its slot
+  const int fr = lane & 15, fkey = (fr & 7) ^ (fr >> 3);
+  const int foff0 = fr * 128 + ((lane >> 4) ^ fkey) * 16;
+  const int foff1 = fr * 128 + ((4 + (lane >> 4)) ^ fkey) * 16;
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int AHEAD = NST - 1;   // steps in flight
+  for (int t = 0; t < min(AHEAD, nsteps); ++t) issue(t);
+  for (int t = 0; t < nsteps; ++t) {
+    // this wave's copies of step t have landed when at most those of the
+    // later steps already issued remain (two copies per step)
+    wait_vm_blocks<2>(min(nsteps - 1 - t, AHEAD - 1));
+    const unsigned char* st = my + (t % NST) * 2048;
+    const bf16x8 w0 = *reinterpret_cast<const bf16x8*>(st + foff0);
+    const bf16x8 w1 = *reinterpret_cast<const bf16x8*>(st + foff1);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const bf16x8 x0 = *reinterpret_cast<const bf16x8*>(sx + (mt * XS + 2 * t) * 1024 + 16 * lane);
+      const bf16x8 x1 = *reinterpret_cast<const bf16x8*>(sx + (mt * XS + 2 * t + 1) * 1024 + 16 * lane);
+      acc[mt] = mma32(w0, x0, acc[mt]);
+      acc[mt] = mma32(w1, x1, acc[mt]);
+    }
+    // every LDS read of this stage has returned before it is refilled
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (t + AHEAD < nsteps) issue(t + AHEAD);
+  }
+
+  // lane (j16, q4): row m = 16 mt + j16, columns n0 + 4 q4 .. +3
+  float* out = p.part + (int64_t)split * M * p.N;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = 16 * mt + (lane & 15);
+    const int n = n0 + 4 * (lane >> 4);
+    if (m < M && n < p.N) *reinterpret_cast<f32x4*>(out + (int64_t)m * p.N + n) = acc[mt];
+  }
+}
+
+// Configurations (measured): one 16-row tile: 8 waves, 4 stages; two tiles:
+// 16 waves, 3 stages.  p.n_tiles must be ceil(N / (16 * waves)).
+int gemm_stream_waves(int mt) { return mt <= 1 ? 8 : 16; }
+
+hipError_t launch_gemm_stream(const TileProb& p, int mt, hipStream_t s) {
+  const int blocks = p.n_tiles * p.splits;
+  if (blocks == 0) return hipSuccess;
+  if (p.k_chunk != kStreamKC || mt < 1 || mt > 2) return hipErrorInvalidValue;
+  if (mt == 1)
+    launch((gemm_stream_kernel<1, 8, 4>), dim3(blocks), dim3(64 * 8), 0, s, p);
+  else
+    launch((gemm_stream_kernel<2, 16, 3>), dim3(blocks), dim3(64 * 16), 0, s, p);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- split-K reduction
 // out[m][n] = sum_s part[s][m][n] (+ add[m][n] when add is given); one thread
 // per 4 outputs, the split loop unrolled so that its loads are in flight

@@ -70,6 +70,11 @@ struct TileProb {
   int32_t k_chunk, splits, m_tiles, n_tiles;
 };
 hipError_t launch_gemm_tile(const TileProb& p, hipStream_t s);
+// Weight-streaming product for at most 32 rows (mt = ceil(M / 16) of 1 or 2):
+// bf16, K a multiple of 64, N of 4, k_chunk == 512; the TileProb's n_tiles is
+// ceil(N / (16 * gemm_stream_waves(mt))) and m_tiles is unused.
+int gemm_stream_waves(int mt);
+hipError_t launch_gemm_stream(const TileProb& p, int mt, hipStream_t s);
 
 // LDS budget for the staged activation slice of one gemm_lds_kernel workgroup.
 constexpr int kLdsGemmBytes = 64 * 1024;
