@@ -137,6 +137,7 @@ struct SkinnyPlan {
   bool wide;         // gemm_wide_kernel (256-column tiles) instead of gemm_lds_kernel
   bool tile;         // gemm_tile_kernel (256x256 MFMA tiles) for many rows
   bool stream;       // gemm_stream_kernel (per-wave weight streams) for at most 32 rows
+  bool fullk;        // gemm_fullk_kernel (no split-K partials) for at most 16 rows
   int32_t m_tiles;   // tile plans only
 };
 
@@ -151,8 +152,17 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, size_t eb) {
   static const int lds_target = env_int("DFLASH_GEMM_LDS_BLOCKS", 1024, 1, 1 << 16);
   static const int wide_min_k = env_int("DFLASH_GEMM_WIDE_MIN_K", 8192, 0, 1 << 30);
   static const int use_stream = env_int("DFLASH_GEMM_STREAM", 1, 0, 1);
+  static const int use_fullk = env_int("DFLASH_GEMM_FULLK", 1, 0, 1);
   SkinnyPlan p{};
   p.mt = (int32_t)std::max<int64_t>(1, cdiv(M, 16));
+  // at most 16 rows: the whole K in one workgroup per 16 columns, one result
+  if (use_fullk && eb == 2 && p.mt == 1 && K % 512 == 0 && N % 4 == 0) {
+    p.fullk = true;
+    p.n_tiles = (int32_t)cdiv(N, 16);
+    p.k_chunk = (int32_t)K;
+    p.splits = 1;
+    return p;
+  }
   // at most 32 rows, K below the wide kernel's range: per-wave weight streams
   // in 512-wide K-chunks
   if (use_stream && eb == 2 && p.mt <= 2 && K < wide_min_k && K % 64 == 0 && N % 4 == 0) {
@@ -244,6 +254,10 @@ struct GemmJob {
   int64_t N, K;
   SkinnyPlan plan;
   float* part;
+  // full-K plans only: write the result in the storage type to out_final (plus
+  // add, when set) instead of fp32 to part
+  void* out_final = nullptr;
+  const void* add = nullptr;
 };
 
 GemmJob make_job(const void* x0, int64_t m0, const void* x1, int64_t m1, const void* w, int64_t N,
@@ -309,6 +323,25 @@ hipError_t run_gemms(int32_t dt, const std::vector<GemmJob>& jobs, hipStream_t s
       t.m_tiles = j.plan.m_tiles;
       t.n_tiles = j.plan.n_tiles;
       hipError_t e = launch_gemm_tile(t, s);
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    if (j.plan.fullk) {
+      FullkArgs f{};
+      f.x0 = static_cast<const bf16*>(j.x0);
+      f.x1 = static_cast<const bf16*>(j.x1);
+      f.m0 = (int32_t)j.m0;
+      f.m1 = (int32_t)j.m1;
+      f.w = static_cast<const bf16*>(j.w);
+      f.N = (int32_t)j.N;
+      f.K = (int32_t)j.K;
+      if (j.out_final != nullptr) {
+        f.out = j.out_final;
+        f.add = j.add;
+      } else {
+        f.part = j.part;
+      }
+      hipError_t e = launch_gemm_fullk(f, s);
       if (e != hipSuccess) return e;
       continue;
     }
@@ -800,8 +833,13 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
   // 5. o_proj
   GemmJob go = p.go;
   go.x0 = attn; go.part = part_out;
+  if (go.plan.fullk) {
+    // one result per output: o_proj (plus the residual) straight into out
+    go.out_final = out;
+    go.add = L->residual ? H : nullptr;
+  }
   if (e == hipSuccess) e = staged(DFLASH_STAGE_O_GEMM, s, true, [&] { return run_gemms(dt, {go}, s); });
-  if (e == hipSuccess)
+  if (e == hipSuccess && !go.plan.fullk)
     e = staged(DFLASH_STAGE_O_REDUCE, s, true,
                [&] {
                  return launch_splitk_reduce(dt, part_out, go.plan.splits, p.RB, L->d, L->residual ? H : nullptr,

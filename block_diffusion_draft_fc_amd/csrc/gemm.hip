@@ -536,6 +536,102 @@ hipError_t launch_gemm_stream(const TileProb& p, int mt, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- full-K weight streaming (bf16, at most 16 rows)
+// One workgroup per 16 output columns; its eight waves split K (wave w takes
+// K/8 .. ) and stream, per 64-wide step, their 16 weight rows and the 16
+// activation rows (whole 128-byte lines, XOR-swizzled chunks) into their own
+// direct-to-LDS rings; the waves' accumulators are summed in LDS at the end.
+// No split-K partials: the result is written once, either as fp32 [M][N] (a
+// single "split" for the reductions that follow) or, for the o projection, as
+// the storage type with the residual added (out may alias add: each element
+// is read and written by the same lane).
+// Requirements (checked by the planner): bf16, K a multiple of 512, N of 4.
+constexpr int kFullkWaves = 8, kFullkStages = 4;
+
+__global__ __launch_bounds__(64 * kFullkWaves) void gemm_fullk_kernel(FullkArgs p) {
+  constexpr int STAGE = 4 * 1024;   // 16 weight rows + 16 activation rows, 128 bytes each
+  __shared__ __align__(16) unsigned char ring[kFullkWaves][kFullkStages * STAGE];
+  __shared__ f32x4 red[kFullkWaves][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * 16;
+  const int M = p.m0 + p.m1;
+  const int kw = p.K / kFullkWaves;   // a multiple of 64
+  const int k0 = wave * kw;
+  const int nsteps = kw / 64;
+
+  // copies of step t into stage t % kFullkStages: copies 0-1 move weight rows
+  // 8 j .. 8 j + 7, copies 2-3 activation rows; lane l fills row 8 j + l / 8,
+  // slot l % 8, with chunk (l % 8) ^ key(row), key(R) = (R % 8) ^ (R / 8).
+  // Rows past N (past M) read row 0; they are never stored.
+  const int crow = lane >> 3;
+  unsigned char* my = ring[wave];
+  auto issue = [&](int t) {
+    unsigned char* st = my + (t % kFullkStages) * STAGE;
+    const int k = k0 + 64 * t;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int R = 8 * j + crow;
+      const int c = (lane & 7) ^ (R & 7) ^ j;
+      int n = n0 + R;
+      n = n < p.N ? n : 0;
+      lds_copy16(p.w + (int64_t)n * p.K + k + 8 * c, st + j * 1024);
+      int m = R < M ? R : 0;
+      const bf16* xr = m < p.m0 ? p.x0 + (int64_t)m * p.K : p.x1 + (int64_t)(m - p.m0) * p.K;
+      lds_copy16(xr + k + 8 * c, st + (2 + j) * 1024);
+    }
+  };
+  const int fr = lane & 15, fkey = (fr & 7) ^ (fr >> 3);
+  const int foff0 = fr * 128 + ((lane >> 4) ^ fkey) * 16;
+  const int foff1 = fr * 128 + ((4 + (lane >> 4)) ^ fkey) * 16;
+
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int AHEAD = kFullkStages - 1;
+  for (int t = 0; t < min(AHEAD, nsteps); ++t) issue(t);
+  for (int t = 0; t < nsteps; ++t) {
+    wait_vm_blocks<4>(min(nsteps - 1 - t, AHEAD - 1));   // four copies per step
+    const unsigned char* st = my + (t % kFullkStages) * STAGE;
+    const bf16x8 w0 = *reinterpret_cast<const bf16x8*>(st + foff0);
+    const bf16x8 w1 = *reinterpret_cast<const bf16x8*>(st + foff1);
+    const bf16x8 x0 = *reinterpret_cast<const bf16x8*>(st + 2048 + foff0);
+    const bf16x8 x1 = *reinterpret_cast<const bf16x8*>(st + 2048 + foff1);
+    acc = mma32(w0, x0, acc);
+    acc = mma32(w1, x1, acc);
+    // every LDS read of this stage has returned before it is refilled
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (t + AHEAD < nsteps) issue(t + AHEAD);
+  }
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  // lane (j16, q4): row m = j16, columns n0 + 4 q4 .. +3
+  f32x4 sum = red[0][lane];
+#pragma unroll
+  for (int w = 1; w < kFullkWaves; ++w) sum += red[w][lane];
+  const int m = lane & 15, n = n0 + 4 * (lane >> 4);
+  if (m >= M || n >= p.N) return;
+  const int64_t o = (int64_t)m * p.N + n;
+  if (p.part != nullptr) {
+    *reinterpret_cast<f32x4*>(p.part + o) = sum;
+  } else {
+    const bf16* add = static_cast<const bf16*>(p.add);
+    bf16* out = static_cast<bf16*>(p.out);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = add != nullptr ? to_f32(add[o + e]) : 0.f;
+      out[o + e] = from_f32<bf16>(sum[e] + a);
+    }
+  }
+}
+
+hipError_t launch_gemm_fullk(const FullkArgs& p, hipStream_t s) {
+  if (p.m0 + p.m1 <= 0 || p.N <= 0) return hipSuccess;
+  if (p.m0 + p.m1 > 16 || p.K % (64 * kFullkWaves) != 0 || p.N % 4 != 0) return hipErrorInvalidValue;
+  if ((p.part == nullptr) == (p.out == nullptr)) return hipErrorInvalidValue;
+  launch(gemm_fullk_kernel, dim3((p.N + 15) / 16), dim3(64 * kFullkWaves), 0, s, p);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- split-K reduction
 // out[m][n] = sum_s part[s][m][n] (+ add[m][n] when add is given); one thread
 // per 4 outputs, the split loop unrolled so that its loads are in flight

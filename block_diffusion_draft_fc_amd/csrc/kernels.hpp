@@ -76,6 +76,21 @@ hipError_t launch_gemm_tile(const TileProb& p, hipStream_t s);
 int gemm_stream_waves(int mt);
 hipError_t launch_gemm_stream(const TileProb& p, int mt, hipStream_t s);
 
+// Full-K product for at most 16 rows of the virtual concatenation [x0; x1]
+// (bf16, K a multiple of 512, N of 4): exactly one of part (fp32 [M][N]) and
+// out (bf16 [M][N], plus add when add is not null; out may alias add) is set.
+struct FullkArgs {
+  const bf16* x0;
+  const bf16* x1;
+  int32_t m0, m1;
+  const bf16* w;     // [N][K]
+  int32_t N, K;
+  float* part;
+  void* out;
+  const void* add;
+};
+hipError_t launch_gemm_fullk(const FullkArgs& p, hipStream_t s);
+
 // LDS budget for the staged activation slice of one gemm_lds_kernel workgroup.
 constexpr int kLdsGemmBytes = 64 * 1024;
 hipError_t launch_gemm_lds(int dtype, const GemmArgs& a, int max_mt, size_t lds_bytes, hipStream_t s);
