@@ -28,6 +28,7 @@
 //    four waves merge through LDS at the end and the workgroup writes one
 //    partial (m, l, unnormalised O) per query row.
 #include <cstdlib>
+#include <string>
 
 #include "kernels.hpp"
 
@@ -878,6 +879,10 @@ __global__ __launch_bounds__(256, 1) void attn_ring_kernel(AttnArgs a) {
 //      copy moves 8 whole rows and picks, per lane, the chunk its slot holds;
 //      a fragment read (16 consecutive rows, one chunk) then covers all banks.
 // Block starts are multiples of 64, so a block never crosses a page.
+// NST stages keep NST - 1 blocks in flight while the waves compute on one.
+// The queries travel as direct copies too, ahead of the first blocks', into
+// the last stage (free until the loop's first refill of it): their latency
+// overlaps the blocks' instead of preceding it.
 template <int DH, int NST>
 __global__ __launch_bounds__(256, 1) void attn_ring64_kernel(AttnArgs a) {
   using V8 = bf16x8;
@@ -910,9 +915,6 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_kernel(AttnArgs a) {
 
   const int row = 16 * wave + j16;
   const bf16* qbase = static_cast<const bf16*>(a.q_ws) + (int64_t)(r * a.n_kv + g) * a.qrows * DH;
-  V8 qv[DS];
-#pragma unroll
-  for (int s = 0; s < DS; ++s) qv[s] = row < valid_q ? load8(qbase + (int64_t)row * DH + 32 * s + 8 * q4) : zero8<bf16>();
   const int vlo = a.window > 0 ? a.qpos0[r] + row % a.B - a.window + 1 : INT_MIN;
   const int vis_lo_max = a.qpos0[r] + a.B - a.window;   // largest row bound (sliding layers)
   float m_run = -INFINITY, l_run = 0.f;
@@ -923,9 +925,21 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_kernel(AttnArgs a) {
   const int pg0 = kbeg / a.cache.page_rows;
   const int npg = nblk > 0 ? (kend - 1) / a.cache.page_rows - pg0 + 1 : 0;
   for (int i = tid; i < npg; i += 256) s_page[i] = (int32_t)cache_page(a.cache, r, (pg0 + i) * a.cache.page_rows);
-#pragma unroll
-  for (int s = 0; s < DS; ++s) asm volatile("" ::"v"(qv[s]));   // queries waited for before any copy
   __syncthreads();
+  // The queries go to LDS by direct copies issued before the first blocks',
+  // so the wait for block 0 covers them too and their latency overlaps the
+  // blocks' (a register load would be waited for on its own: the compiler
+  // cannot see the block copies, so it would wait for everything in flight
+  // at the first use, or on every block if that use sits in the loop).  The
+  // workspace holds qrows >= 16 * 4 rows, so every copy is in bounds.  They
+  // land in the last stage, which the first copies into it (issued after the
+  // first barrier of the loop) find read: wave w's operand-order slabs
+  // (wave w, s) hold, at 16 * lane, row 16 w + j16, head dims 32 s + 8 q4 ..
+  static_assert(4 * DS * 1024 <= STAGE, "the queries fit one stage");
+  unsigned char* my_q = ring + (NST - 1) * STAGE + wave * DS * 1024;
+#pragma unroll
+  for (int s = 0; s < DS; ++s) lds_copy16(qbase + (int64_t)row * DH + 32 * s + 8 * q4, my_q + s * 1024);
+  V8 qv[DS];
 
   const bf16* kpool = static_cast<const bf16*>(a.cache.k_pool);
   const bf16* vpool = static_cast<const bf16*>(a.cache.v_pool);
@@ -1049,6 +1063,15 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_kernel(AttnArgs a) {
 
   constexpr int AHEAD = NST - 1;   // blocks in flight
   for (int b = 0; b < min(AHEAD, nblk); ++b) issue(b);
+  // this wave's queries (rows past g*B as zeros), once its first copies have
+  // landed: they went out first
+  wait_vm_blocks<PER_WAVE>(max(0, min(nblk - 1, AHEAD - 1)));
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    qv[s] = *reinterpret_cast<const V8*>(my_q + s * 1024 + 16 * lane);
+    if (row >= valid_q) qv[s] = zero8<bf16>();
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read before the stage is refilled
   for (int b = 0; b < nblk; ++b) {
     wait_vm_blocks<PER_WAVE>(min(nblk - 1 - b, AHEAD - 1));
     asm volatile("s_barrier" ::: "memory");
@@ -1078,17 +1101,30 @@ static hipError_t launch_attn_t(const AttnArgs& a, int items, hipStream_t s) {
     return hipGetLastError();                                                                      \
   }
   if constexpr (sizeof(T) == 2) {
-    // four query tiles: the shared ring of 64-key blocks, two stages (64 KB,
-    // so two workgroups share a CU and cover each other's load latency: deeper
-    // rings, one workgroup per CU, measured slower); DFLASH_ATTN_RING=32 takes
-    // the ring of 32-key blocks, 0 attn_lds_kernel
-    static const int ring = [] {
-      const char* e = std::getenv("DFLASH_ATTN_RING");
-      return e ? std::atoi(e) : 64;
+    // bf16, four query tiles: the shared ring of 64-key blocks.  For
+    // comparison, DFLASH_ATTN_KERNEL=ring32 takes the ring of 32-key blocks
+    // and =lds the per-wave LDS rings; DFLASH_ATTN_NST sets the depth of the
+    // 64-key ring.
+    static const int kind = [] {
+      const char* e = std::getenv("DFLASH_ATTN_KERNEL");
+      if (e == nullptr) return 0;
+      const std::string v(e);
+      return v == "ring32" ? 2 : v == "lds" ? 3 : 0;
     }();
-    if (ring == 64 && nqt == 4) {
+    // Ring depth: with at most one work item per CU, three stages (96 KB, one
+    // workgroup per CU: two blocks in flight while it computes on a third);
+    // with more, two stages (64 KB), so that two workgroups share a CU and
+    // cover each other's load latency.
+    static const int forced_nst = [] {
+      const char* e = std::getenv("DFLASH_ATTN_NST");
+      return e ? std::atoi(e) : 0;
+    }();
+    const int nst = forced_nst > 0 ? forced_nst : items <= 256 ? 3 : 2;
+    if (kind == 0 && nqt == 4) {
       if (a.d_h == 128) {
-        launch((attn_ring64_kernel<128, 2>), dim3(items), dim3(256), 0, s, a);
+        if (nst == 2) launch((attn_ring64_kernel<128, 2>), dim3(items), dim3(256), 0, s, a);
+        else if (nst == 4) launch((attn_ring64_kernel<128, 4>), dim3(items), dim3(256), 0, s, a);
+        else launch((attn_ring64_kernel<128, 3>), dim3(items), dim3(256), 0, s, a);
         return hipGetLastError();
       }
       if (a.d_h == 64) {
@@ -1096,7 +1132,7 @@ static hipError_t launch_attn_t(const AttnArgs& a, int items, hipStream_t s) {
         return hipGetLastError();
       }
     }
-    if (ring == 32 && nqt == 4) {
+    if (kind == 2 && nqt == 4) {
       if (a.d_h == 128) {
         launch((attn_ring_kernel<128, 4>), dim3(items), dim3(256), 0, s, a);
         return hipGetLastError();

@@ -121,13 +121,18 @@ hipError_t staged(int stage, hipStream_t s, bool launches, F&& f) {
   return e;
 }
 
-int attn_target_items() {
-  static int v = [] {
+// Attention work items to aim for, given the keys of all (sequence, K/V head)
+// pairs: about one per CU for up to 256K keys, where each CU's ring then
+// runs three blocks deep; four per CU beyond, where two workgroups share a CU
+// and cover each other's latency (measured on the 8K decode and the 16-request
+// ragged workloads).  DFLASH_ATTN_TARGET_ITEMS overrides.
+int attn_target_items(int64_t total_keys) {
+  static const int forced = [] {
     const char* e = std::getenv("DFLASH_ATTN_TARGET_ITEMS");
-    int t = e ? std::atoi(e) : 256;
-    return std::min(std::max(t, 1), kAttnMaxTarget);
+    return e ? std::min(std::max(std::atoi(e), 1), kAttnMaxTarget) : 0;
   }();
-  return v;
+  if (forced > 0) return forced;
+  return total_keys > ((int64_t)256 << 10) ? 1024 : 256;
 }
 
 // ---------------------------------------------------------------- GEMM planning
@@ -802,7 +807,7 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
     // keys per work item: a multiple of 64 (the largest key block of the
     // kernels; chunks start at multiples of 64), at least 128, sized so that
     // the items cover the target count
-    int64_t chunk = cdiv(cdiv(total, attn_target_items()), 64) * 64;
+    int64_t chunk = cdiv(cdiv(total, attn_target_items(total)), 64) * 64;
     chunk = std::max<int64_t>(chunk, 128);
     // an item's keys may span at most kAttnMaxChunkPages pages (its page list
     // is staged in LDS); two pages go to a chunk that does not start on a page
