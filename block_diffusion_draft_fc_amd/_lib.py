@@ -35,7 +35,8 @@ class LayerDesc(C.Structure):
 
 class CacheDesc(C.Structure):
     _fields_ = [("n_seqs", C.c_int32), ("n_kv", C.c_int32), ("d_h", C.c_int32), ("dtype", C.c_int32),
-                ("page_size", C.c_int32), ("max_pages_per_seq", C.c_int32), ("capacity", C.c_int64),
+                ("page_size", C.c_int32), ("max_pages_per_seq", C.c_int32), ("ring", C.c_int32),
+                ("capacity", C.c_int64),
                 ("k_pool", C.c_void_p), ("v_pool", C.c_void_p), ("block_table", C.c_void_p)]
 
 
@@ -114,9 +115,10 @@ class Cache:
     """dflash_cache handle plus the caller-owned device pools it describes."""
 
     def __init__(self, n_seqs, n_kv, d_h, dtype, capacity, page_size=0, max_pages_per_seq=0,
-                 device="cuda", pools=None):
+                 device="cuda", pools=None, ring=False):
         self.n_seqs, self.n_kv, self.d_h = n_seqs, n_kv, d_h
         self.page_size, self.capacity, self.max_pages = page_size, capacity, max_pages_per_seq
+        self.ring = bool(ring)
         self.dtype = dtype
         if pools is not None:
             self.k_pool, self.v_pool, self.table = pools
@@ -128,7 +130,8 @@ class Cache:
             self.k_pool = torch.zeros((capacity, n_kv, page_size, d_h), dtype=dtype, device=device)
             self.v_pool = torch.zeros((capacity, n_kv, d_h, page_size), dtype=dtype, device=device)
             self.table = torch.full((n_seqs, max_pages_per_seq), -1, dtype=torch.int32, device=device)
-        desc = CacheDesc(n_seqs, n_kv, d_h, dtype_code(dtype), page_size, max_pages_per_seq, capacity,
+        desc = CacheDesc(n_seqs, n_kv, d_h, dtype_code(dtype), page_size, max_pages_per_seq, 1 if ring else 0,
+                         capacity,
                          self.k_pool.data_ptr(), self.v_pool.data_ptr(),
                          self.table.data_ptr() if self.table is not None else None)
         h = C.c_void_p()

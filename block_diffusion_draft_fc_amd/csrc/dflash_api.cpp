@@ -20,6 +20,7 @@ using namespace dflash;
 struct dflash_cache {
   dflash_cache_desc desc;
   std::vector<int32_t> len;
+  std::vector<int64_t> written_hi;          // ring: highest position ever written + 1
   std::vector<std::vector<int32_t>> pages;   // paged: physical page per logical page
   std::set<int32_t> free_pages;             // paged: lowest first
 };
@@ -420,8 +421,10 @@ int plan_append(const dflash_cache* c, const std::vector<int64_t>& n, AppendPlan
   const auto& d = c->desc;
   plan->new_pages.assign(d.n_seqs, {});
   if (d.page_size == 0) {
+    // a ring takes any length, at most `capacity` new rows per call (more
+    // would land twice in one slot)
     for (int s = 0; s < d.n_seqs; ++s)
-      if (c->len[s] + n[s] > d.capacity) return DFLASH_ERR_CAPACITY;
+      if (d.ring ? n[s] > d.capacity : c->len[s] + n[s] > d.capacity) return DFLASH_ERR_CAPACITY;
     return DFLASH_OK;
   }
   int64_t need = 0;
@@ -472,6 +475,7 @@ hipError_t enqueue_page_table_now(const dflash_cache* c, const AppendPlan& plan,
 void commit_append(dflash_cache* c, const std::vector<int64_t>& n, const AppendPlan& plan) {
   for (int s = 0; s < c->desc.n_seqs; ++s) {
     c->len[s] += (int32_t)n[s];
+    c->written_hi[s] = std::max<int64_t>(c->written_hi[s], c->len[s]);
     for (int32_t pg : plan.new_pages[s]) {
       c->free_pages.erase(pg);
       c->pages[s].push_back(pg);
@@ -553,6 +557,16 @@ KvPlan plan_kv(const dflash_layer_desc* L, const dflash_cache* c, int64_t T, int
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP; }
 
+// max of f(t) over t = 0 .. T: plans are evaluated for every row count up to
+// 65536 (host arithmetic only) and for T itself beyond that, where every
+// product takes the tile GEMM and its partials grow with the rows.
+template <class F>
+size_t max_over_rows(int64_t T, F&& f) {
+  size_t m = f(T);
+  for (int64_t t = 0; t < std::min<int64_t>(T, 65536); ++t) m = std::max(m, f(t));
+  return m;
+}
+
 }  // namespace
 
 // ======================================================================== ABI
@@ -583,12 +597,14 @@ int dflash_cache_init(dflash_cache** out, const dflash_cache_desc* desc) {
   if (d.page_size == 0 && (d.capacity % DFLASH_KEY_ALIGN != 0 || d.capacity > (int64_t)1 << 30))
     return DFLASH_ERR_SHAPE;
   if (d.page_size > 0 && (d.max_pages_per_seq < 1 || d.capacity > (int64_t)1 << 30)) return DFLASH_ERR_SHAPE;
+  if (d.ring != 0 && (d.ring != 1 || d.page_size != 0)) return DFLASH_ERR_SHAPE;
   if (!d.k_pool || !d.v_pool || !aligned16(d.k_pool) || !aligned16(d.v_pool)) return DFLASH_ERR_ARG;
   if (d.page_size > 0 && (!d.block_table || (reinterpret_cast<uintptr_t>(d.block_table) & 3)))
     return DFLASH_ERR_ARG;
   auto* c = new dflash_cache;
   c->desc = d;
   c->len.assign(d.n_seqs, 0);
+  c->written_hi.assign(d.n_seqs, 0);
   c->pages.assign(d.n_seqs, {});
   if (d.page_size > 0)
     for (int64_t i = 0; i < d.capacity; ++i) c->free_pages.insert(c->free_pages.end(), (int32_t)i);
@@ -673,8 +689,12 @@ int dflash_cache_crop(dflash_cache* c, const int32_t* new_len, void* /*stream*/)
 
 size_t dflash_ctx_project_ws_bytes(int64_t T, int64_t kd, int64_t d, int32_t dtype) {
   if (T <= 0 || kd <= 0 || d <= 0 || !dtype_ok(dtype)) return 0;
-  GemmJob j = make_job(nullptr, T, nullptr, 0, nullptr, d, kd, elem_bytes(dtype));
-  return align_up(job_part_bytes(j));
+  // enough for every row count up to T: the GEMM plan (and its split count)
+  // changes with the rows, so fewer rows may need more partials
+  return max_over_rows(T, [&](int64_t t) {
+    GemmJob j = make_job(nullptr, t, nullptr, 0, nullptr, d, kd, elem_bytes(dtype));
+    return align_up(job_part_bytes(j));
+  });
 }
 
 int dflash_ctx_project(const void* x_raw, int64_t T, int64_t kd, const void* w_fc, const void* gamma_h,
@@ -702,7 +722,8 @@ int dflash_ctx_project(const void* x_raw, int64_t T, int64_t kd, const void* w_f
 
 size_t dflash_kv_inject_attn_ws_bytes(const dflash_layer_desc* L, const dflash_cache* c, int64_t T, int32_t B) {
   if (check_layer(L) != DFLASH_OK || !c || T < 0 || B < 1) return 0;
-  return plan_kv(L, c, T, B).total;
+  // enough for every context row count up to T (see dflash_ctx_project_ws_bytes)
+  return max_over_rows(T, [&](int64_t t) { return plan_kv(L, c, t, B).total; });
 }
 
 int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const void* C, const int32_t* cu_ctx,
@@ -724,6 +745,16 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
   if (ws_bytes < p.total) return DFLASH_ERR_WORKSPACE;
   std::vector<int64_t> rows(cd.n_seqs);
   for (int s = 0; s < cd.n_seqs; ++s) rows[s] = n[s] + B;
+  if (cd.ring) {
+    // a ring holds the last `capacity` positions: the window and the new rows
+    // must fit, and every key the window reaches must still be held
+    if (L->window <= 0) return DFLASH_ERR_SHAPE;
+    if (cd.capacity < (int64_t)L->window + B - 1) return DFLASH_ERR_CAPACITY;
+    for (int s = 0; s < cd.n_seqs; ++s) {
+      const int64_t lo = std::max<int64_t>(0, c->len[s] + n[s] - L->window + 1);
+      if (lo < c->written_hi[s] - cd.capacity) return DFLASH_ERR_RANGE;
+    }
+  }
   AppendPlan ap;
   st = plan_append(c, rows, &ap);
   if (st) return st;
@@ -813,6 +844,9 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
     // is staged in LDS); two pages go to a chunk that does not start on a page
     if (cd.page_size > 0)
       chunk = std::min<int64_t>(chunk, (int64_t)(kAttnMaxChunkPages - 2) * cd.page_size);
+    // a ring's positions wrap every `capacity` rows: each wrap an item spans
+    // takes one more entry of its page list
+    if (cd.ring) chunk = std::min<int64_t>(chunk, (int64_t)(kAttnMaxChunkPages - 2) * cd.capacity);
     aa.chunk_keys = (int32_t)chunk;
     int64_t items = 0;
     for (int r = 0; r < R; ++r) {

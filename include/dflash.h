@@ -46,7 +46,7 @@ typedef enum {
   DFLASH_ERR_ARG = -1,       /* null / misaligned pointer, bad handle, bad cu array */
   DFLASH_ERR_SHAPE = -2,     /* unsupported or inconsistent sizes */
   DFLASH_ERR_DTYPE = -3,     /* dtype not F32/BF16 or not matching the cache */
-  DFLASH_ERR_RANGE = -4,     /* crop to a length outside [0, current length] */
+  DFLASH_ERR_RANGE = -4,     /* crop outside [0, current length]; window beyond a ring's rows */
   DFLASH_ERR_CAPACITY = -5,  /* sequence capacity, page table or page pool exhausted */
   DFLASH_ERR_HIP = -6,       /* a HIP runtime call or kernel launch failed */
   DFLASH_ERR_WORKSPACE = -7  /* workspace smaller than the *_ws_bytes figure */
@@ -106,12 +106,26 @@ typedef struct dflash_layer_desc {
  * Allocation takes the lowest-numbered free page, sequences in index order,
  * each sequence's logical pages in order.  Crop returns every page at or
  * beyond ceil(new_len / page_size) to the free list.
+ *
+ * ring (contiguous only, for sliding-window layers): the cache keeps the last
+ * `capacity` positions of each sequence, row pos in slot pos % capacity, so
+ * lengths may exceed the capacity and memory stays O(window) however long
+ * the context grows (the bounded cache of a sliding layer, "DFlash源码导读二
+ * Qwen3DFlashAttention注意力实现全解析", the MLX comparison: a rotating cache
+ * trimmed like the full one is cropped).  Let hw_s be the highest position
+ * ever written to sequence s, plus one; positions below hw_s - capacity are
+ * gone.  Each append call may bring at most `capacity` rows per sequence.  A
+ * layer call on a ring needs window > 0, capacity >= window + B - 1,
+ * n_s + B <= capacity, and every key the window reaches still held
+ * (max(0, L_s + n_s - window + 1) >= hw_s - capacity; else DFLASH_ERR_RANGE).
+ * Crop is unchanged: it sets the length, and later appends overwrite slots.
  * ---------------------------------------------------------------------- */
 typedef struct dflash_cache_desc {
   int32_t n_seqs, n_kv, d_h;
   int32_t dtype;
   int32_t page_size;
   int32_t max_pages_per_seq;   /* paged only */
+  int32_t ring;                /* 0 or 1 (contiguous only): keep the last `capacity` positions */
   int64_t capacity;
   void *k_pool;
   void *v_pool;
@@ -137,7 +151,8 @@ int64_t dflash_cache_free_pages(const dflash_cache *c);
  *   w_fc    [d, kd] device (output x input; no bias)
  *   gamma_h [d] device
  *   c_out   [T, d] device, written in `dtype`
- *   ws      device workspace of at least dflash_ctx_project_ws_bytes(...)
+ *   ws      device workspace of at least dflash_ctx_project_ws_bytes(...),
+ *           a figure that holds for every call with at most T rows
  * T == 0 is a no-op.  kd % 8 == 0, d % 8 == 0, d <= 16384.
  * ---------------------------------------------------------------------- */
 size_t dflash_ctx_project_ws_bytes(int64_t T, int64_t kd, int64_t d, int32_t dtype);
@@ -150,8 +165,9 @@ int dflash_ctx_project(const void *x_raw, int64_t T, int64_t kd, const void *w_f
  * [cu_rows[s], cu_rows[s+1]) of k_rows / v_rows [n_rows, n_kv, d_h] (device,
  * cache dtype) land at positions len_s .. len_s + n_s - 1 of sequence s, then
  * len_s += n_s.  cu_rows is a host array [n_seqs + 1], non-decreasing from 0.
- * Bytes are copied unchanged.  Capacity, page-table or pool overflow ->
- * DFLASH_ERR_CAPACITY with nothing written.
+ * Bytes are copied unchanged.  Capacity, page-table or pool overflow (for a
+ * ring: more than `capacity` rows for one sequence) -> DFLASH_ERR_CAPACITY
+ * with nothing written.
  * ---------------------------------------------------------------------- */
 int dflash_cache_append(dflash_cache *c, const int32_t *cu_rows, const void *k_rows,
                         const void *v_rows, void *stream);
@@ -179,7 +195,8 @@ int dflash_cache_crop(dflash_cache *c, const int32_t *new_len, void *stream);
  * queries attend over all len_r keys.  The caller crops afterwards (to
  * L_r + n_r to keep the accepted context).  Needs ws of at least
  * dflash_kv_inject_attn_ws_bytes(L, cache, T, B) bytes; the figure depends on
- * T, B and the handle's sizes, not on the current lengths.
+ * T, B and the handle's sizes, not on the current lengths, and holds for
+ * every call with at most T context rows.
  * ---------------------------------------------------------------------- */
 size_t dflash_kv_inject_attn_ws_bytes(const dflash_layer_desc *L, const dflash_cache *c,
                                       int64_t T, int32_t B);

@@ -25,6 +25,16 @@ Pool layout (as declared in the library header):
   pos % page_size.  Allocation takes the lowest-numbered free page; sequences
   are served in index order and each sequence's new logical pages in order.
   Crop returns every page at or beyond ceil(new_len / page_size).
+
+Ring (contiguous only): the bounded cache of a sliding-window layer, the
+rotating cache that "DFlash源码导读二 Qwen3DFlashAttention注意力实现全解析"
+(the MLX comparison table) pairs with the trim of the full cache.  Row `pos`
+lives in slot pos % capacity and lengths may exceed the capacity; with hw the
+highest position ever written plus one, the rows at positions
+[max(0, hw - capacity), len) are held.  One append brings at most `capacity`
+rows per sequence.  A layer call with window W, n new context rows and B
+block rows reads keys from max(0, len + n - W + 1) on; it needs W > 0,
+W + B - 1 <= capacity, n + B <= capacity, and that first key still held.
 """
 from __future__ import annotations
 
@@ -41,12 +51,16 @@ class CacheError(Exception):
 
 class CacheModel:
     def __init__(self, n_seqs, n_kv, d_h, page_size, capacity, max_pages_per_seq=0,
-                 word=np.uint16):
+                 word=np.uint16, ring=False):
         self.n_seqs, self.n_kv, self.d_h = int(n_seqs), int(n_kv), int(d_h)
         self.page_size, self.capacity = int(page_size), int(capacity)
         self.max_pages = int(max_pages_per_seq)
         self.word = word
+        self.ring = bool(ring)
+        if self.ring and self.page_size:
+            raise CacheError(ERR_SHAPE, "a ring is a contiguous cache")
         self.len = [0] * self.n_seqs
+        self.hw = [0] * self.n_seqs
         if self.paged:
             self.K = np.zeros((capacity, n_kv, page_size, d_h), dtype=word)
             self.V = np.zeros((capacity, n_kv, d_h, page_size), dtype=word)
@@ -87,7 +101,9 @@ class CacheModel:
                     self.pages[s].append(pg)
         else:
             for s in range(self.n_seqs):
-                if self.len[s] + n[s] > self.capacity:
+                if self.ring and n[s] > self.capacity:
+                    raise CacheError(ERR_CAPACITY, "more rows than ring slots in one call")
+                if not self.ring and self.len[s] + n[s] > self.capacity:
                     raise CacheError(ERR_CAPACITY, "sequence exceeds capacity")
         for s in range(self.n_seqs):
             for j in range(n[s]):
@@ -98,9 +114,11 @@ class CacheModel:
                     self.K[pg, :, slot, :] = krow
                     self.V[pg, :, :, slot] = vrow
                 else:
-                    self.K[s, :, pos, :] = krow
-                    self.V[s, :, :, pos] = vrow
+                    slot = pos % self.capacity
+                    self.K[s, :, slot, :] = krow
+                    self.V[s, :, :, slot] = vrow
             self.len[s] += n[s]
+            self.hw[s] = max(self.hw[s], self.len[s])
 
     def crop(self, new_len):
         new_len = [int(x) for x in new_len]
@@ -117,6 +135,34 @@ class CacheModel:
                     self.free.add(pg)
                 del self.pages[s][keep:]
 
+    def layer_call_status(self, n, B: int, window: int) -> int:
+        """Status of a layer call on a ring with n[s] new context rows, B block
+        rows and the given window (checked before anything changes)."""
+        if window <= 0:
+            return ERR_SHAPE
+        if window + B - 1 > self.capacity:
+            return ERR_CAPACITY
+        for s in range(self.n_seqs):
+            if max(0, self.len[s] + int(n[s]) - window + 1) < self.hw[s] - self.capacity:
+                return ERR_RANGE
+        for s in range(self.n_seqs):
+            if int(n[s]) + B > self.capacity:
+                return ERR_CAPACITY
+        return OK
+
+    def held(self, s: int):
+        """Ring: (lo, K, V) with K, V [n_kv, len - lo, d_h] the rows of positions
+        lo .. len - 1 that the ring still holds, lo = max(0, hw - capacity)."""
+        lo = max(0, self.hw[s] - self.capacity)
+        L = self.len[s]
+        K = np.empty((self.n_kv, max(0, L - lo), self.d_h), dtype=self.word)
+        V = np.empty((self.n_kv, max(0, L - lo), self.d_h), dtype=self.word)
+        for pos in range(lo, L):
+            slot = pos % self.capacity
+            K[:, pos - lo, :] = self.K[s, :, slot, :]
+            V[:, pos - lo, :] = self.V[s, :, :, slot]
+        return lo, K, V
+
     def block_table(self):
         return [list(p) for p in self.pages] if self.paged else None
 
@@ -124,7 +170,10 @@ class CacheModel:
         return sum(len(p) for p in self.pages) if self.paged else 0
 
     def rows(self, s: int):
-        """Logical view of sequence s: K, V as [n_kv, len, d_h] words."""
+        """Logical view of sequence s: K, V as [n_kv, len, d_h] words (not for
+        rings, which hold only the last rows: see `held`)."""
+        if self.ring:
+            raise ValueError("a ring holds only its last rows")
         L = self.len[s]
         K = np.empty((self.n_kv, L, self.d_h), dtype=self.word)
         V = np.empty((self.n_kv, L, self.d_h), dtype=self.word)

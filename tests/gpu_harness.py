@@ -53,7 +53,10 @@ class GpuModel:
                                        rope_theta=wl.rope_theta, window=wl.layer_window(li),
                                        residual=wl.n_layers > 1))
             need = [int(self.L0[r] + grow[r] + wl.B) for r in range(wl.R)]
-            if wl.page_size:
+            if wl.ring_capacity(li):
+                self.caches.append(L.Cache(wl.R, wl.n_kv, wl.d_h, self.dtype, wl.ring_capacity(li), 0, 0, device,
+                                           ring=True))
+            elif wl.page_size:
                 ps = wl.page_size
                 pages = sum(-(-x // ps) for x in need) + wl.R
                 maxp = max(-(-x // ps) for x in need) + 1
@@ -67,19 +70,23 @@ class GpuModel:
 
     def prefill(self, kv_host):
         """kv_host[l][r] = (K, V) [n_kv, L_r, d_h] float32 storage values; appended
-        through dflash_cache_append (one call per layer, all requests)."""
+        through dflash_cache_append (one call per layer and all requests; a ring
+        takes them in calls of at most its capacity rows per request)."""
         for li, cache in enumerate(self.caches):
-            ks, vs, cu = [], [], [0]
-            for r in range(self.wl.R):
-                k, v = kv_host[li][r]
-                ks.append(np.ascontiguousarray(k.transpose(1, 0, 2)))
-                vs.append(np.ascontiguousarray(v.transpose(1, 0, 2)))
-                cu.append(cu[-1] + k.shape[1])
-            if cu[-1] == 0:
-                continue
-            kd = to_device(np.concatenate(ks, axis=0), self.wl)
-            vd = to_device(np.concatenate(vs, axis=0), self.wl)
-            L.dflash_cache_append(cache, cu, kd, vd)
+            step = cache.capacity if cache.ring else max([kv_host[li][r][0].shape[1] for r in range(self.wl.R)] + [1])
+            longest = max(kv_host[li][r][0].shape[1] for r in range(self.wl.R))
+            for a in range(0, longest, step):
+                ks, vs, cu = [], [], [0]
+                for r in range(self.wl.R):
+                    k, v = kv_host[li][r]
+                    ks.append(np.ascontiguousarray(k[:, a:a + step].transpose(1, 0, 2)))
+                    vs.append(np.ascontiguousarray(v[:, a:a + step].transpose(1, 0, 2)))
+                    cu.append(cu[-1] + ks[-1].shape[0])
+                if cu[-1] == 0:
+                    continue
+                kd = to_device(np.concatenate(ks, axis=0), self.wl)
+                vd = to_device(np.concatenate(vs, axis=0), self.wl)
+                L.dflash_cache_append(cache, cu, kd, vd)
         torch.cuda.synchronize()
 
     def round(self, x_raw, cu, H):
@@ -109,9 +116,21 @@ def oracle_stack(wl, kv_host):
     return O.OracleStack(layers, fc["w_fc"].astype(np.float64), fc["gamma_h"], wl.eps, K0, V0)
 
 
+def ring_rows(cache: L.Cache, s: int, lo: int):
+    """Rows of positions lo .. len-1 of sequence s of a ring cache (slot
+    pos % capacity) read back as float64: K, V [n_kv, len - lo, d_h]."""
+    n = cache.lengths()[s]
+    slots = torch.tensor([p % cache.capacity for p in range(lo, n)], dtype=torch.long,
+                         device=cache.k_pool.device)
+    K = cache.k_pool[s][:, slots, :]
+    V = cache.v_pool[s][:, :, slots].transpose(1, 2)
+    return from_device(K.contiguous()), from_device(V.contiguous())
+
+
 def cache_rows(cache: L.Cache, s: int):
     """Logical rows of sequence s read back from the device pools as float64:
     K, V [n_kv, len, d_h]."""
+    assert not cache.ring, "a ring holds only its last rows: use ring_rows"
     n = cache.lengths()[s]
     if cache.page_size == 0:
         K = cache.k_pool[s, :, :n, :]

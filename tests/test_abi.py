@@ -35,8 +35,9 @@ int main(void) {
   printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(dflash_layer_desc), offsetof(dflash_layer_desc, eps),
          offsetof(dflash_layer_desc, rope_theta), offsetof(dflash_layer_desc, window),
          offsetof(dflash_layer_desc, residual), offsetof(dflash_layer_desc, gamma_k));
-  printf("%zu %zu %zu %zu\\n", sizeof(dflash_cache_desc), offsetof(dflash_cache_desc, capacity),
-         offsetof(dflash_cache_desc, k_pool), offsetof(dflash_cache_desc, block_table));
+  printf("%zu %zu %zu %zu %zu\\n", sizeof(dflash_cache_desc), offsetof(dflash_cache_desc, capacity),
+         offsetof(dflash_cache_desc, k_pool), offsetof(dflash_cache_desc, block_table),
+         offsetof(dflash_cache_desc, ring));
   return 0;
 }""")
     exe = tmp_path / "layout"
@@ -46,11 +47,11 @@ int main(void) {
     assert [int(x) for x in lines[0].split()] == [C.sizeof(ld), ld.eps.offset, ld.rope_theta.offset,
                                                   ld.window.offset, ld.residual.offset, ld.gamma_k.offset]
     assert [int(x) for x in lines[1].split()] == [C.sizeof(cd), cd.capacity.offset, cd.k_pool.offset,
-                                                  cd.block_table.offset]
+                                                  cd.block_table.offset, cd.ring.offset]
 
 
-def _cache(n_seqs=2, page_size=0, capacity=128, max_pages=0, dtype=L.DFLASH_BF16):
-    desc = L.CacheDesc(n_seqs, 2, 64, dtype, page_size, max_pages, capacity, FAKE, FAKE,
+def _cache(n_seqs=2, page_size=0, capacity=128, max_pages=0, dtype=L.DFLASH_BF16, ring=0):
+    desc = L.CacheDesc(n_seqs, 2, 64, dtype, page_size, max_pages, ring, capacity, FAKE, FAKE,
                        FAKE if page_size else None)
     h = C.c_void_p()
     rc = L.LIB.dflash_cache_init(C.byref(h), C.byref(desc))
@@ -70,6 +71,8 @@ def test_strerror_table():
     (dict(n_seqs=0), L.ERR_SHAPE),
     (dict(n_seqs=65), L.ERR_SHAPE),
     (dict(dtype=7), L.ERR_DTYPE),
+    (dict(page_size=64, capacity=4, max_pages=4, ring=1), L.ERR_SHAPE),   # rings are contiguous only
+    (dict(ring=2), L.ERR_SHAPE),
 ])
 def test_cache_init_rejects(kw, code):
     rc, _ = _cache(**kw)
@@ -160,5 +163,48 @@ def test_kv_inject_validation():
         lens = (C.c_int32 * 2)()
         L.LIB.dflash_cache_lengths(h, lens)
         assert list(lens) == [0, 0]
+    finally:
+        L.LIB.dflash_cache_destroy(h)
+
+
+def test_ring_validation():
+    """Ring caches: lengths beyond the capacity are allowed, one call brings at
+    most `capacity` rows per sequence, and a layer call needs a sliding window
+    with window + B - 1 <= capacity and n + B <= capacity."""
+    rc, h = _cache(n_seqs=2, capacity=128, ring=1)
+    assert rc == 0
+    try:
+        # 129 rows in one call would land twice in one slot
+        assert L.LIB.dflash_cache_append(h, L._i32([0, 129, 129]), FAKE, FAKE, None) == L.ERR_CAPACITY
+        f = L.LIB.dflash_kv_inject_attn
+
+        def call(lay, cu, B=4):
+            ws = L.LIB.dflash_kv_inject_attn_ws_bytes(C.byref(lay), h, cu[-1], B)
+            return f(C.byref(lay), h, FAKE, L._i32(cu), FAKE, B, FAKE, FAKE, ws, None)
+
+        assert call(_layer(window=0), [0, 4, 8]) == L.ERR_SHAPE            # full attention on a ring
+        assert call(_layer(window=126), [0, 4, 8]) == L.ERR_CAPACITY       # 126 + 4 - 1 > 128
+        assert call(_layer(window=100), [0, 125, 126]) == L.ERR_CAPACITY   # 125 + 4 new rows > 128
+        lens = (C.c_int32 * 2)()
+        L.LIB.dflash_cache_lengths(h, lens)
+        assert list(lens) == [0, 0]
+    finally:
+        L.LIB.dflash_cache_destroy(h)
+
+
+def test_workspace_figures_cover_every_smaller_call():
+    """A workspace sized for T rows serves every call with fewer rows, although
+    the projection plans (one fused q/k/v product up to 64 rows, split counts)
+    change with the rows."""
+    rc, h = _cache(n_seqs=3, capacity=512)
+    assert rc == 0
+    try:
+        lay = _layer(d=256, n_h=8, n_kv=2, d_h=128)
+        f = lambda T: L.LIB.dflash_kv_inject_attn_ws_bytes(C.byref(lay), h, T, 16)  # noqa: E731
+        figs = [f(T) for T in range(0, 80)]
+        assert all(b >= a for a, b in zip(figs, figs[1:])), figs
+        g = lambda T: L.LIB.dflash_ctx_project_ws_bytes(T, 20480, 4096, L.DFLASH_BF16)  # noqa: E731
+        figs = [g(T) for T in range(1, 80)]
+        assert all(b >= a for a, b in zip(figs, figs[1:])), figs
     finally:
         L.LIB.dflash_cache_destroy(h)

@@ -115,3 +115,77 @@ def test_walkthrough_growth():
         assert m.len == [keep]
     k, _ = m.rows(0)
     assert list(k[0, :, 0]) == [1, 1, 1, 2, 2, 2]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_ring_holds_the_last_rows(seed):
+    """A ring keeps the rows of positions [max(0, hw - capacity), len): they
+    must equal the plain per-sequence list of appended rows there (the list
+    has no slots, so a wrong slot or a stale overwrite shows up)."""
+    n_seqs, n_kv, d_h, cap = 2, 2, 3, 16
+    ring = CacheModel(n_seqs, n_kv, d_h, 0, capacity=cap, ring=True)
+    lists = [[] for _ in range(n_seqs)]
+    rng = np.random.default_rng(2000 + seed)
+    for kind, arg in _random_ops(seed, n_seqs, 60, 9):
+        if kind == "append":
+            n = [int(a) for a in arg]
+            cu = np.concatenate([[0], np.cumsum(n)])
+            k = rng.integers(0, 2 ** 16, size=(cu[-1], n_kv, d_h), dtype=np.uint16)
+            v = rng.integers(0, 2 ** 16, size=(cu[-1], n_kv, d_h), dtype=np.uint16)
+            ring.append(cu, k, v)
+            for s in range(n_seqs):
+                lists[s] += [(k[j], v[j]) for j in range(cu[s], cu[s + 1])]
+        else:
+            new = [int(f * len(lists[s])) for s, f in enumerate(arg)]
+            ring.crop(new)
+            for s in range(n_seqs):
+                del lists[s][new[s]:]
+        for s in range(n_seqs):
+            assert ring.len[s] == len(lists[s])
+            lo, kr, vr = ring.held(s)
+            assert lo == max(0, ring.hw[s] - cap)
+            for pos in range(lo, ring.len[s]):
+                assert np.array_equal(kr[:, pos - lo], lists[s][pos][0])
+                assert np.array_equal(vr[:, pos - lo], lists[s][pos][1])
+
+
+def test_ring_wider_than_every_length_is_the_contiguous_cache():
+    rng = np.random.default_rng(7)
+    ring = CacheModel(2, 1, 4, 0, capacity=64, ring=True)
+    flat = CacheModel(2, 1, 4, 0, capacity=64)
+    for _ in range(30):
+        n = rng.integers(0, 6, size=2)
+        if all(flat.len[s] + n[s] <= 64 for s in range(2)):
+            cu = np.concatenate([[0], np.cumsum(n)])
+            k = rng.integers(0, 2 ** 16, size=(cu[-1], 1, 4), dtype=np.uint16)
+            for m in (ring, flat):
+                m.append(cu, k, k)
+        else:
+            new = [x // 2 for x in flat.len]
+            for m in (ring, flat):
+                m.crop(new)
+        assert np.array_equal(ring.K, flat.K) and np.array_equal(ring.V, flat.V)
+
+
+def test_ring_round_cycle_and_errors():
+    """Rounds that append n + B rows and crop the B block rows run forever on
+    a ring of window + B - 1 slots; a crop far back makes the next window reach
+    rows the ring no longer holds; the call-level limits."""
+    W, B, cap = 12, 4, 16                      # cap >= W + B - 1 = 15
+    m = CacheModel(1, 1, 2, 0, capacity=cap, ring=True)
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        n = int(rng.integers(0, 6))
+        assert m.layer_call_status([n], B, W) == 0
+        z = np.zeros((n + B, 1, 2), dtype=np.uint16)
+        m.append([0, n + B], z, z)
+        m.crop([m.len[0] - B])
+    assert m.len[0] > 4 * cap
+    assert m.layer_call_status([0], B, 0) == -2          # full attention on a ring
+    assert m.layer_call_status([0], B, cap) == ERR_CAPACITY
+    assert m.layer_call_status([cap - B + 1], B, W) == ERR_CAPACITY
+    m.crop([m.len[0] - 8])                                # the window now starts below hw - cap
+    assert m.layer_call_status([0], B, W) == ERR_RANGE
+    with pytest.raises(CacheError) as e:
+        m.append([0, cap + 1], np.zeros((cap + 1, 1, 2), np.uint16), np.zeros((cap + 1, 1, 2), np.uint16))
+    assert e.value.code == ERR_CAPACITY

@@ -21,12 +21,16 @@ from oracle.cache_model import CacheError, CacheModel  # noqa: E402
 from gpu_harness import say  # noqa: E402
 
 CASES = [
-    # (name, n_seqs, n_kv, d_h, page_size, capacity, max_pages, word)
-    ("contig_bf16", 3, 2, 64, 0, 320, 0, np.uint16),
-    ("contig_f32", 2, 1, 128, 0, 192, 0, np.uint32),
-    ("paged64_bf16", 4, 2, 64, 64, 14, 6, np.uint16),
-    ("paged128_bf16_dh128", 3, 8, 128, 128, 9, 5, np.uint16),
-    ("paged64_f32", 2, 2, 128, 64, 7, 5, np.uint32),
+    # (name, n_seqs, n_kv, d_h, page_size, capacity, max_pages, word, ring)
+    ("contig_bf16", 3, 2, 64, 0, 320, 0, np.uint16, False),
+    ("contig_f32", 2, 1, 128, 0, 192, 0, np.uint32, False),
+    ("paged64_bf16", 4, 2, 64, 64, 14, 6, np.uint16, False),
+    ("paged128_bf16_dh128", 3, 8, 128, 128, 9, 5, np.uint16, False),
+    ("paged64_f32", 2, 2, 128, 64, 7, 5, np.uint32, False),
+    # rings: lengths run past the capacity; the f32 ring is narrower than the
+    # largest appends, which must fail on both sides
+    ("ring_bf16", 3, 2, 64, 0, 128, 0, np.uint16, True),
+    ("ring_f32_dh128", 2, 1, 128, 0, 64, 0, np.uint32, True),
 ]
 
 
@@ -38,12 +42,12 @@ def _device_bits(t, word):
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 @pytest.mark.parametrize("seed", [0, 1])
 def test_random_append_crop_sequences(case, seed):
-    name, n_seqs, n_kv, d_h, ps, cap, maxp, word = case
+    name, n_seqs, n_kv, d_h, ps, cap, maxp, word, ring = case
     say(f"case cache {name} seed={seed}")
     rng = np.random.default_rng(1000 + seed)
     tdt = torch.bfloat16 if word == np.uint16 else torch.float32
-    cache = L.Cache(n_seqs, n_kv, d_h, tdt, cap, ps, maxp, "cuda")
-    model = CacheModel(n_seqs, n_kv, d_h, ps, cap, maxp, word=word)
+    cache = L.Cache(n_seqs, n_kv, d_h, tdt, cap, ps, maxp, "cuda", ring=ring)
+    model = CacheModel(n_seqs, n_kv, d_h, ps, cap, maxp, word=word, ring=ring)
     special = np.array([0x7FC0, 0xFF80, 0x7F80, 0x0001, 0x8000] if word == np.uint16 else
                        [0x7FC00001, 0xFF800000, 0x7F800000, 0x00000001, 0x80000000], dtype=word)
     for step in range(40):
@@ -94,3 +98,50 @@ def test_random_append_crop_sequences(case, seed):
                 pages = model.pages[s]
                 assert host[s][: len(pages)] == pages and all(x == -1 for x in host[s][len(pages):])
                 assert list(dev[s, : len(pages)]) == pages
+
+
+def test_ring_layer_call_status():
+    """A layer call on a ring fails with DFLASH_ERR_RANGE, changing nothing,
+    when its window reaches rows the ring no longer holds, and runs when they
+    are all held; the statuses follow the integer model."""
+    from workloads import configs, generate as G
+    from workloads.device import to_device
+
+    say("case ring layer-call status")
+    wl = configs.WALKTHROUGH.scaled(name="ring_status", d=256, n_h=8, n_kv=2, d_h=64, k_layers=2, B=4,
+                                    dtype="bf16", window=60, sliding_layers=(0,))
+    lw = G.layer_weights(wl, 0)
+    layer = L.Layer(*(to_device(lw[k], wl) for k in ("w_qkv", "w_o", "gamma_q", "gamma_k")), n_h=wl.n_h,
+                    n_kv=wl.n_kv, d_h=wl.d_h, window=wl.window)
+    cap = 64
+    cache = L.Cache(1, wl.n_kv, wl.d_h, torch.bfloat16, cap, 0, 0, "cuda", ring=True)
+    model = CacheModel(1, wl.n_kv, wl.d_h, 0, cap, word=np.uint16, ring=True)
+    rng = np.random.default_rng(5)
+    for rows in (64, 36):                                   # hw = 100
+        k = rng.integers(0, 2 ** 14, size=(rows, wl.n_kv, wl.d_h), dtype=np.uint16)
+        kd = torch.from_numpy(k.view(np.int16)).to("cuda").view(torch.bfloat16)
+        model.append([0, rows], k, k)
+        L.dflash_cache_append(cache, [0, rows], kd, kd)
+    model.crop([90])
+    L.dflash_cache_crop(cache, [90])
+    H = torch.randn((wl.B, wl.d), device="cuda").to(torch.bfloat16)
+    Cm = torch.randn((8, wl.d), device="cuda").to(torch.bfloat16)
+    out = torch.empty_like(H)
+    ws = torch.empty(L.dflash_kv_inject_attn_ws_bytes(layer, cache, 8, wl.B), dtype=torch.uint8, device="cuda")
+    for n in (0, 4, 5, 8):
+        want = model.layer_call_status([n], wl.B, wl.window)
+        try:
+            L.dflash_kv_inject_attn(layer, cache, Cm[:n], [0, n], H, wl.B, out, ws)
+            got = 0
+        except L.DFlashError as e:
+            got = e.code
+        assert got == want, f"n={n}: status {got} != {want}"
+        if got == 0:
+            torch.cuda.synchronize()
+            assert torch.isfinite(out.float()).all()
+            model.append([0, n + wl.B], np.zeros((n + wl.B, wl.n_kv, wl.d_h), np.uint16),
+                         np.zeros((n + wl.B, wl.n_kv, wl.d_h), np.uint16))
+            model.crop([90])
+            L.dflash_cache_crop(cache, [90])
+        assert cache.lengths() == model.len
+    assert model.layer_call_status([0], wl.B, wl.window) == L.ERR_RANGE

@@ -32,7 +32,7 @@ from oracle import dflash_oracle as O  # noqa: E402
 from workloads import configs, generate as G  # noqa: E402
 from workloads.device import from_device, to_device  # noqa: E402
 
-from gpu_harness import TOL, GpuModel, cache_rows, oracle_stack, prefill_host, rel_l2, say  # noqa: E402
+from gpu_harness import TOL, GpuModel, cache_rows, oracle_stack, prefill_host, rel_l2, ring_rows, say  # noqa: E402
 
 
 def run_rounds(wl, rounds, check_cache=True):
@@ -44,8 +44,13 @@ def run_rounds(wl, rounds, check_cache=True):
     orc = oracle_stack(wl, kv)
     sched = G.schedule(wl)
     worst = 0.0
+    # highest position written + 1 per (layer, request): the rows a ring holds
+    hw = [[int(n) for n in G.prefill_lengths(wl)] for _ in range(wl.n_layers)]
     for rnd in range(rounds):
         x, cu, H = G.round_inputs(wl, rnd, sched[rnd])
+        for li, cache in enumerate(gm.caches):
+            for r, length in enumerate(cache.lengths()):
+                hw[li][r] = max(hw[li][r], length + int(cu[r + 1] - cu[r]) + wl.B)
         got = gm.round(x, cu, H)
         ref, _ = orc.round(x, cu, H, wl.B)
         for li in range(wl.n_layers):
@@ -70,15 +75,18 @@ def run_rounds(wl, rounds, check_cache=True):
         L0 = G.prefill_lengths(wl)
         for li, cache in enumerate(gm.caches):
             for r in range(wl.R):
-                K, V = cache_rows(cache, r)
+                # a ring holds positions [hw - capacity, len) only
+                lo = max(0, hw[li][r] - cache.capacity) if cache.ring else 0
+                K, V = ring_rows(cache, r, lo) if cache.ring else cache_rows(cache, r)
                 Kp, Vp = kv[li][r]
                 n0 = int(L0[r])
                 # prefilled rows were moved, not computed: identical values
-                assert np.array_equal(K[:, :n0], Kp.astype(np.float64))
-                assert np.array_equal(V[:, :n0], Vp.astype(np.float64))
-                if K.shape[1] > n0:
-                    assert rel_l2(K[:, n0:], orc.K[li][r][:, n0:]) <= TOL[wl.dtype]
-                    assert rel_l2(V[:, n0:], orc.V[li][r][:, n0:]) <= TOL[wl.dtype]
+                assert np.array_equal(K[:, :max(0, n0 - lo)], Kp[:, lo:n0].astype(np.float64))
+                assert np.array_equal(V[:, :max(0, n0 - lo)], Vp[:, lo:n0].astype(np.float64))
+                a = max(n0, lo)
+                if K.shape[1] + lo > a:
+                    assert rel_l2(K[:, a - lo:], orc.K[li][r][:, a:]) <= TOL[wl.dtype]
+                    assert rel_l2(V[:, a - lo:], orc.V[li][r][:, a:]) <= TOL[wl.dtype]
     say(f"  worst rel-L2 {worst:.3e}")
     return worst
 
@@ -157,6 +165,15 @@ def test_ragged_paged_16_requests():
     run_rounds(wl, 4)
 
 
+def test_stack5_hybrid_ring_full_shapes():
+    """The same stack with bounded ring caches on the sliding layers (4160
+    rows instead of the whole context): 2 requests on 8192-row contexts, so
+    the rings have wrapped before the first round."""
+    wl = configs.STACK5_HYBRID.scaled(name="stack5_hybrid_swa4096_ring_ctx8k_batch2", R=2, prefill_len=8192,
+                                      rounds=2, ring=True)
+    run_rounds(wl, wl.rounds)
+
+
 def test_stack5_hybrid_window_full_shapes():
     """The 5-layer hybrid stack (sliding window 4096 on layers 0/2/4, full on
     1/3, one shared context, residual chaining, per-layer crop) at its full
@@ -203,6 +220,17 @@ SMALL = [
            page_size=128, window=300, sliding_layers=(0,), rounds=3),
     _small("stack3_window_residual", n_layers=3, d_h=128, B=16, R=2, prefill_len=600, window=256,
            sliding_layers=(0, 2), rounds=3),
+    # bounded ring caches on the sliding layers, prefills several times the
+    # ring, rounds that wrap it again
+    _small("ring_window_100", d_h=128, B=16, prefill_len=500, window=100, sliding_layers=(0,), ring=True,
+           rounds=6),
+    _small("ring_window_1", d_h=128, B=16, prefill_len=200, window=1, sliding_layers=(0,), ring=True, rounds=4),
+    _small("ring_window_60_dh64_b4", B=4, prefill_len=333, window=60, sliding_layers=(0,), ring=True, rounds=8,
+           n_range=(0, 8)),
+    _small("ring_ragged_r3_window_70", R=3, d_h=128, B=16, prefill="uniform", prefill_range=(0, 400), window=70,
+           sliding_layers=(0,), ring=True, n_range=(0, 9), rounds=5),
+    _small("ring_stack3_residual", n_layers=3, d_h=128, B=16, R=2, prefill_len=600, window=256,
+           sliding_layers=(0, 2), ring=True, rounds=3),
     # many new context rows: the context projection and the K/V projection of
     # [C; H] take the MFMA tile GEMM, with the C/H boundary inside a row tile
     _small("fresh_ctx300_tile_gemm", d=512, k_layers=2, B=16, prefill="none", n_new="fixed", n_fixed=300,

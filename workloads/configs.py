@@ -43,6 +43,9 @@ class Workload:
     n_layers: int = 1
     window: int = 0                # sliding window of the sliding layers (0 = none)
     sliding_layers: Tuple[int, ...] = ()
+    # sliding layers keep a bounded ring cache (window + B - 1 rows, rounded up
+    # to 64, at least the rows of one round) instead of the whole context
+    ring: bool = False
     eps: float = 1e-6
     rope_theta: float = 1e6
 
@@ -56,6 +59,14 @@ class Workload:
 
     def layer_window(self, layer: int) -> int:
         return self.window if layer in self.sliding_layers else 0
+
+    def ring_capacity(self, layer: int) -> int:
+        """Rows of the layer's ring cache, 0 for an unbounded cache."""
+        if not (self.ring and layer in self.sliding_layers):
+            return 0
+        n_max = self.n_fixed if self.n_new == "fixed" else self.n_range[1]
+        need = max(self.window + self.B - 1, n_max + self.B)
+        return (need + 63) // 64 * 64
 
     def scaled(self, **kw) -> "Workload":
         """A copy with some fields replaced (smaller parity cases)."""
