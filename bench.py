@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fresh-ctx", action="store_true",
                     help="skip the MFMA-utilisation pass over the fresh 1024-row context projections")
+    ap.add_argument("--no-batched", action="store_true",
+                    help="skip the ragged 16-request and 5-layer hybrid stack rounds")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 8 times (scales HBM counters)")
     return ap.parse_args()
@@ -203,6 +205,118 @@ def fresh_ctx_projections(iters):
     res["gemms+reductions"] = {"us": round(all_us, 2), "tflops": round(tot / all_us / 1e6, 1),
                                "mfma_frac": round(tot / all_us / 1e6 / BF16_PEAK_TFLOPS, 4)}
     res["stage_us"] = {k: round(v, 2) for k, v in us.items() if st[k][0]}
+    return res
+
+
+# ---------------------------------------------------------------------------- batched workloads
+
+def batched_rounds(wl, rounds, ring=False):
+    """Rounds of a batched workload (the 16-request ragged paged batch, or the
+    5-layer hybrid stack): the seeded schedule of new context rows and the
+    seeded cache lengths, with cache rows, raw context rows and block rows drawn
+    on the device (values N(0,1): their statistics, not their bits, matter for
+    timing).  Each round = dflash_ctx_project once + every layer's
+    dflash_kv_inject_attn and crop, issued eagerly.  Three passes over the
+    `rounds` scheduled rounds, the caches growing throughout: a warm-up pass,
+    a timed pass and a pass with stage timing.  Reports the round time, draft
+    blocks/s (one block per request per round), the attention stage's time and
+    algorithmic HBM rate, and the caches' device bytes; with ring=True the
+    sliding layers keep bounded ring caches."""
+    import torch
+
+    from block_diffusion_draft_fc_amd import _lib as L
+    from block_diffusion_draft_fc_amd.draft_round import DraftRound
+    from workloads import generate as G
+    from workloads.device import to_device
+
+    dev = "cuda:0"
+    passes = 3
+    g = torch.Generator(device=dev).manual_seed(wl.seed)
+    L0 = G.prefill_lengths(wl)
+    sched = G.schedule(wl)[:rounds]
+    grow = passes * sched.sum(axis=0)
+    fc = G.fc_weights(wl)
+    w_fc, gamma_h = to_device(fc["w_fc"], wl, dev), to_device(fc["gamma_h"], wl, dev)
+    layers, caches = [], []
+    for li in range(wl.n_layers):
+        lw = G.layer_weights(wl, li)
+        layers.append(L.Layer(*(to_device(lw[k], wl, dev) for k in ("w_qkv", "w_o", "gamma_q", "gamma_k")),
+                              n_h=wl.n_h, n_kv=wl.n_kv, d_h=wl.d_h, eps=wl.eps, rope_theta=wl.rope_theta,
+                              window=wl.layer_window(li), residual=wl.n_layers > 1))
+        need = [int(L0[r] + grow[r] + wl.B) for r in range(wl.R)]
+        cap_ring = wl.scaled(ring=ring).ring_capacity(li)
+        if cap_ring:
+            caches.append(L.Cache(wl.R, wl.n_kv, wl.d_h, torch.bfloat16, cap_ring, 0, 0, dev, ring=True))
+        elif wl.page_size:
+            ps = wl.page_size
+            caches.append(L.Cache(wl.R, wl.n_kv, wl.d_h, torch.bfloat16, sum(-(-x // ps) for x in need) + wl.R,
+                                  ps, max(-(-x // ps) for x in need) + 1, dev))
+        else:
+            caches.append(L.Cache(wl.R, wl.n_kv, wl.d_h, torch.bfloat16, (max(need) + 63) // 64 * 64, 0, 0, dev))
+    for cache in caches:
+        step = cache.capacity if cache.ring else int(L0.max())
+        for a in range(0, int(L0.max()), step):
+            cu = [0]
+            for r in range(wl.R):
+                cu.append(cu[-1] + max(0, min(int(L0[r]), a + step) - a))
+            k = torch.randn((cu[-1], wl.n_kv, wl.d_h), device=dev, generator=g).to(torch.bfloat16)
+            v = torch.randn((cu[-1], wl.n_kv, wl.d_h), device=dev, generator=g).to(torch.bfloat16)
+            L.dflash_cache_append(cache, cu, k, v)
+            del k, v
+    T_max = int(sched.sum(axis=1).max())
+    drv = DraftRound(w_fc, gamma_h, wl.eps, layers, caches, wl.B, T_max, dev)
+    xs = [torch.randn((int(sched[i].sum()), wl.kd), device=dev, generator=g).to(torch.bfloat16)
+          for i in range(rounds)]
+    Hs = [torch.randn((wl.R * wl.B, wl.d), device=dev, generator=g).to(torch.bfloat16) for i in range(rounds)]
+    cus = [[0] + np.cumsum(sched[i]).astype(int).tolist() for i in range(rounds)]
+    # algorithmic attention bytes per pass: every key a query may see, once
+    att_bytes = []
+    lens = [list(map(int, L0)) for _ in caches]
+    for _ in range(passes):
+        tot = 0
+        for i in range(rounds):
+            for li in range(wl.n_layers):
+                W = wl.layer_window(li)
+                for r in range(wl.R):
+                    Lr, n = lens[li][r], int(sched[i][r])
+                    lo = max(0, Lr + n - W + 1) if W else 0
+                    tot += (Lr + n + wl.B - lo) * 2 * wl.n_kv * wl.d_h * 2 + wl.B * wl.n_h * wl.d_h * 2
+                    lens[li][r] = Lr + n
+        att_bytes.append(tot)
+    torch.cuda.synchronize()
+
+    def cycle():
+        for i in range(rounds):
+            drv.run(xs[i], cus[i], Hs[i])
+
+    cycle()                      # warm-up pass
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    cycle()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = max(ev0.elapsed_time(ev1), (time.perf_counter() - t0) * 1e3) / rounds
+    L.timing_reset()
+    L.timing_enable(True)
+    cycle()
+    torch.cuda.synchronize()
+    st = L.timing_read()
+    L.timing_enable(False)
+    att_us = st["attn"][1] * 1e3 / rounds
+    ab = att_bytes[2] / rounds
+    cache_bytes = sum(c.k_pool.numel() * 2 * 2 for c in caches)
+    res = {"workload": wl.name, "rounds": rounds, "requests": wl.R, "layers": wl.n_layers,
+           "ring_sliding_layers": bool(ring), "ms_per_round": round(ms, 4),
+           "draft_blocks_per_s": round(wl.R * 1e3 / ms, 1),
+           "attn_us_per_round": round(att_us, 2), "attn_alg_bytes_per_round": int(ab),
+           "attn_hbm_gbps": round(ab / (att_us * 1e-6) / 1e9, 1),
+           "attn_hbm_frac": round(ab / (att_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+           "stage_us_per_round": {k: round(v[1] * 1e3 / rounds, 2) for k, v in st.items() if v[0]},
+           "cache_bytes": int(cache_bytes)}
+    del drv, caches, layers, xs, Hs
+    torch.cuda.empty_cache()
     return res
 
 
@@ -394,6 +508,13 @@ def main():
     if not args.no_fresh_ctx:
         log("bench: fresh-context projections")
         res["fresh_ctx_projections"] = fresh_ctx_projections(20)
+    if not args.no_batched:
+        log("bench: ragged 16-request paged batch")
+        res["ragged_paged"] = batched_rounds(configs.RAGGED_PAGED, 16)
+        log("bench: 5-layer hybrid stack, ring caches on the sliding layers")
+        res["stack5_hybrid_ring"] = batched_rounds(configs.STACK5_HYBRID, 8, ring=True)
+        log("bench: 5-layer hybrid stack, unbounded caches")
+        res["stack5_hybrid_full_caches"] = batched_rounds(configs.STACK5_HYBRID, 8, ring=False)
     if not args.no_cpu_baseline:
         log("bench: timing the fp64 oracle on the host")
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -232,13 +232,14 @@ SkinnyPlan plan_tile(int64_t M, int64_t N, int64_t K) {
   return p;
 }
 
-// Whether a bf16 product of M rows takes gemm_tile_kernel: enough rows to fill
-// 256-row tiles reasonably, K a multiple of the 64-wide step and N of 4 (row
-// alignment follows from the 16-byte alignment every device pointer of the
-// interface must have).  Depends on shapes only, so that a workspace sized
-// from the plan fits the plan the call makes.
+// Whether a bf16 product of M rows takes gemm_tile_kernel: more rows than one
+// weight-streaming problem holds (which would stream the weights once per 64
+// rows), K a multiple of the 64-wide step and N of 4 (row alignment follows
+// from the 16-byte alignment every device pointer of the interface must have).
+// Depends on shapes only, so that a workspace sized from the plan fits the
+// plan the call makes.
 bool tile_eligible(int64_t M, int64_t N, int64_t K, size_t eb) {
-  static const int min_rows = env_int("DFLASH_GEMM_TILE_MIN_ROWS", 256, 1, 1 << 30);
+  static const int min_rows = env_int("DFLASH_GEMM_TILE_MIN_ROWS", kSkinnyMaxM + 1, 1, 1 << 30);
   return eb == 2 && M >= min_rows && K % 64 == 0 && N % 4 == 0;
 }
 
