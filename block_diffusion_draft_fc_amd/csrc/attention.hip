@@ -1061,11 +1061,17 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_kernel(AttnArgs a) {
     }
   };
 
-  constexpr int AHEAD = NST - 1;   // blocks in flight
-  for (int b = 0; b < min(AHEAD, nblk); ++b) issue(b);
+  // Up to AHEAD = NST - 1 blocks in flight beyond the one being processed.
+  // Only INIT of them go out before the first block is waited for: when every
+  // CU asks for all of its first AHEAD blocks at once, each one's first block
+  // lands later; the ring deepens to AHEAD once computing has begun.
+  constexpr int AHEAD = NST - 1;
+  constexpr int INIT = AHEAD < 2 ? AHEAD : 2;
+  int issued = 0;
+  for (; issued < min(INIT, nblk); ++issued) issue(issued);
   // this wave's queries (rows past g*B as zeros), once its first copies have
   // landed: they went out first
-  wait_vm_blocks<PER_WAVE>(max(0, min(nblk - 1, AHEAD - 1)));
+  wait_vm_blocks<PER_WAVE>(max(0, issued - 1));
 #pragma unroll
   for (int s = 0; s < DS; ++s) {
     qv[s] = *reinterpret_cast<const V8*>(my_q + s * 1024 + 16 * lane);
@@ -1073,9 +1079,13 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_kernel(AttnArgs a) {
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read before the stage is refilled
   for (int b = 0; b < nblk; ++b) {
-    wait_vm_blocks<PER_WAVE>(min(nblk - 1 - b, AHEAD - 1));
+    // this wave's copies of block b have landed when at most those of the
+    // blocks issued after it remain; after the barrier every wave's have, and
+    // every wave is done with block b - 1, whose stage (and those before it)
+    // may be refilled with the blocks up to b + AHEAD
+    wait_vm_blocks<PER_WAVE>(issued - 1 - b);
     asm volatile("s_barrier" ::: "memory");
-    if (b + AHEAD < nblk) issue(b + AHEAD);   // into the stage of block b - 1
+    for (; issued < min(nblk, b + AHEAD + 1); ++issued) issue(issued);
     process(b);
   }
 
@@ -1112,9 +1122,10 @@ static hipError_t launch_attn_t(const AttnArgs& a, int items, hipStream_t s) {
       return v == "ring32" ? 2 : v == "lds" ? 3 : 0;
     }();
     // Ring depth: with at most one work item per CU, three stages (96 KB, one
-    // workgroup per CU: two blocks in flight while it computes on a third);
-    // with more, two stages (64 KB), so that two workgroups share a CU and
-    // cover each other's load latency.
+    // workgroup per CU: two blocks in flight while it computes on a third;
+    // four stages measured slower on the 8K decode workload); with more, two
+    // stages (64 KB), so that two workgroups share a CU and cover each other's
+    // load latency.
     static const int forced_nst = [] {
       const char* e = std::getenv("DFLASH_ATTN_NST");
       return e ? std::atoi(e) : 0;
