@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--no-fresh-ctx", action="store_true",
                     help="skip the MFMA-utilisation pass over the fresh 1024-row context projections")
     ap.add_argument("--no-batched", action="store_true",
-                    help="skip the ragged 16-request and 5-layer hybrid stack rounds")
+                    help="skip the draft head, the ragged 16-request and the 5-layer hybrid stack rounds")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 8 times (scales HBM counters)")
     return ap.parse_args()
@@ -320,6 +320,55 @@ def batched_rounds(wl, rounds, ring=False):
     return res
 
 
+# ---------------------------------------------------------------------------- draft head
+
+def draft_head_pass(iters):
+    """The draft head after the stack ("DFlash KV Injection Walkthrough" Step
+    5) for one request of the 8K decode workload: final RMSNorm of the block's
+    15 tail rows, lm_head over the Qwen3 vocabulary (151936 x 4096 bf16 =
+    1.24 GB, drawn on the device), argmax.  HBM-bound on the lm_head stream."""
+    import torch
+
+    from block_diffusion_draft_fc_amd import _lib as L
+    from workloads import configs
+
+    wl = configs.DECODE_8K
+    vocab, d, B = configs.QWEN3_VOCAB, wl.d, wl.B
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(7)
+    w = (torch.randn((vocab, d), device=dev, generator=g) / d ** 0.5).to(torch.bfloat16)
+    gam = (1 + 0.1 * torch.randn((d,), device=dev, generator=g)).to(torch.bfloat16)
+    h = torch.randn((B, d), device=dev, generator=g).to(torch.bfloat16)
+    ids = torch.empty((B - 1,), dtype=torch.int32, device=dev)
+    ws = torch.empty(L.dflash_draft_head_ws_bytes(1, B, d, vocab, torch.bfloat16), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        L.dflash_draft_head(h, B, gam, wl.eps, w, ids, ws)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(iters):
+        L.dflash_draft_head(h, B, gam, wl.eps, w, ids, ws)
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / iters
+    L.timing_reset()
+    L.timing_enable(True)
+    for _ in range(iters):
+        L.dflash_draft_head(h, B, gam, wl.eps, w, ids, ws)
+    torch.cuda.synchronize()
+    st = L.timing_read()
+    L.timing_enable(False)
+    gemm_us = st["head_gemm"][1] * 1e3 / iters
+    alg = (vocab * d + (B - 1) * d) * 2
+    res = {"workload": f"draft_head_vocab{vocab}_d{d}_rows{B - 1}_bf16", "us_per_call": round(us, 2),
+           "stage_us": {k: round(v[1] * 1e3 / iters, 2) for k, v in st.items() if v[0]},
+           "lm_head_alg_bytes": alg, "lm_head_gbps": round(alg / (gemm_us * 1e-6) / 1e9, 1),
+           "lm_head_hbm_frac": round(alg / (gemm_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+    del w
+    torch.cuda.empty_cache()
+    return res
+
+
 # ---------------------------------------------------------------------------- GPU leg
 
 def main():
@@ -509,6 +558,8 @@ def main():
         log("bench: fresh-context projections")
         res["fresh_ctx_projections"] = fresh_ctx_projections(20)
     if not args.no_batched:
+        log("bench: draft head (lm_head over the Qwen3 vocabulary)")
+        res["draft_head"] = draft_head_pass(20)
         log("bench: ragged 16-request paged batch")
         res["ragged_paged"] = batched_rounds(configs.RAGGED_PAGED, 16)
         log("bench: 5-layer hybrid stack, ring caches on the sliding layers")

@@ -60,6 +60,8 @@ def _load() -> C.CDLL:
         "dflash_cache_crop": (C.c_int, [vp, p32, vp]),
         "dflash_kv_inject_attn_ws_bytes": (sz, [C.POINTER(LayerDesc), vp, i64, i32]),
         "dflash_kv_inject_attn": (C.c_int, [C.POINTER(LayerDesc), vp, vp, p32, vp, i32, vp, vp, sz, vp]),
+        "dflash_draft_head_ws_bytes": (sz, [i64, i32, i64, i64, i32]),
+        "dflash_draft_head": (C.c_int, [vp, i64, i32, i64, vp, C.c_float, vp, i64, i32, vp, vp, vp, sz, vp]),
         "dflash_timing_enable": (C.c_int, [C.c_int]),
         "dflash_timing_read": (C.c_int, [i32, C.POINTER(i64), C.POINTER(C.c_double)]),
         "dflash_timing_reset": (C.c_int, []),
@@ -208,10 +210,26 @@ def dflash_kv_inject_attn(layer: Layer, cache: Cache, C_rows, cu_ctx, H, B, out,
            "dflash_kv_inject_attn")
 
 
+# --------------------------------------------------------------------- draft head
+
+def dflash_draft_head_ws_bytes(R, B, d, vocab, dtype: torch.dtype) -> int:
+    return int(LIB.dflash_draft_head_ws_bytes(R, B, d, vocab, dtype_code(dtype)))
+
+
+def dflash_draft_head(h, B, gamma_f, eps, w_lm, token_ids, ws, max_logit=None, stream=None) -> None:
+    """h [R*B, d]; token_ids [R*(B-1)] int32 (and max_logit float32) device tensors."""
+    RB, d = h.shape
+    vocab = w_lm.shape[0]
+    _check(LIB.dflash_draft_head(_ptr(h), RB // B, int(B), d, _ptr(gamma_f), float(eps), _ptr(w_lm), vocab,
+                                 dtype_code(h.dtype), _ptr(token_ids), _ptr(max_logit), _ptr(ws),
+                                 ws.numel() if ws is not None else 0, _stream(stream)),
+           "dflash_draft_head")
+
+
 # --------------------------------------------------------------------- stage timing
 
 STAGES = ("ctx_gemm", "ctx_reduce", "ctx_norm", "qkv_gemm", "qkv_epilogue", "attn", "attn_combine",
-          "o_gemm", "o_reduce", "cache_append", "page_table")
+          "o_gemm", "o_reduce", "cache_append", "page_table", "head_norm", "head_gemm", "head_argmax")
 
 
 def timing_enable(on: bool = True) -> None:

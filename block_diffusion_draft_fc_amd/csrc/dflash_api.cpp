@@ -890,6 +890,76 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
   return DFLASH_OK;
 }
 
+// ---------------------------------------------------------------- draft head
+
+namespace {
+struct HeadPlan {
+  int64_t M;
+  GemmJob j;
+  int nseg;
+  size_t off_x, off_part, off_val, off_idx, total;
+};
+
+HeadPlan plan_head(int64_t R, int32_t B, int64_t d, int64_t vocab, size_t eb) {
+  HeadPlan p{};
+  p.M = R * (B - 1);
+  p.j = make_job(nullptr, p.M, nullptr, 0, nullptr, vocab, d, eb);
+  p.nseg = (int)cdiv(vocab, kHeadSeg);
+  size_t o = 0;
+  p.off_x = o;    o = align_up(o + (size_t)p.M * d * eb);
+  p.off_part = o; o = align_up(o + job_part_bytes(p.j));
+  p.off_val = o;  o = align_up(o + (size_t)p.M * p.nseg * sizeof(float));
+  p.off_idx = o;  o = align_up(o + (size_t)p.M * p.nseg * sizeof(int32_t));
+  p.total = o;
+  return p;
+}
+
+int check_head(int64_t R, int32_t B, int64_t d, int64_t vocab, int32_t dtype) {
+  if (!dtype_ok(dtype)) return DFLASH_ERR_DTYPE;
+  if (R < 1 || B < 1 || d <= 0 || d % 8 != 0 || d > 16384 || vocab <= 0 || vocab % 4 != 0 ||
+      vocab >= ((int64_t)1 << 30) || R * (B - 1) > INT32_MAX / 2)
+    return DFLASH_ERR_SHAPE;
+  return DFLASH_OK;
+}
+}  // namespace
+
+size_t dflash_draft_head_ws_bytes(int64_t R, int32_t B, int64_t d, int64_t vocab, int32_t dtype) {
+  if (check_head(R, B, d, vocab, dtype) != DFLASH_OK || B == 1) return 0;
+  return plan_head(R, B, d, vocab, elem_bytes(dtype)).total;
+}
+
+int dflash_draft_head(const void* h, int64_t R, int32_t B, int64_t d, const void* gamma_f, float eps,
+                      const void* w_lm, int64_t vocab, int32_t dtype, int32_t* token_ids, float* max_logit,
+                      void* ws, size_t ws_bytes, void* stream) {
+  int st = check_head(R, B, d, vocab, dtype);
+  if (st) return st;
+  if (!(eps >= 0.f)) return DFLASH_ERR_SHAPE;
+  if (B == 1) return DFLASH_OK;
+  if (!h || !gamma_f || !w_lm || !token_ids || !ws) return DFLASH_ERR_ARG;
+  if (!aligned16(h) || !aligned16(gamma_f) || !aligned16(w_lm) || !aligned16(ws) ||
+      (reinterpret_cast<uintptr_t>(token_ids) & 3) || (reinterpret_cast<uintptr_t>(max_logit) & 3))
+    return DFLASH_ERR_ARG;
+  const size_t eb = elem_bytes(dtype);
+  HeadPlan p = plan_head(R, B, d, vocab, eb);
+  if (ws_bytes < p.total) return DFLASH_ERR_WORKSPACE;
+  char* w = static_cast<char*>(ws);
+  void* x = w + p.off_x;
+  GemmJob j = p.j;
+  j.x0 = x;
+  j.w = w_lm;
+  j.part = reinterpret_cast<float*>(w + p.off_part);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = staged(DFLASH_STAGE_HEAD_NORM, s, true,
+                        [&] { return launch_head_norm(dtype, h, p.M, B, d, gamma_f, eps, x, s); });
+  if (e == hipSuccess) e = staged(DFLASH_STAGE_HEAD_GEMM, s, true, [&] { return run_gemms(dtype, {j}, s); });
+  if (e == hipSuccess)
+    e = staged(DFLASH_STAGE_HEAD_ARGMAX, s, true, [&] {
+      return launch_head_argmax(j.part, j.plan.splits, p.M, vocab, reinterpret_cast<float*>(w + p.off_val),
+                                reinterpret_cast<int32_t*>(w + p.off_idx), token_ids, max_logit, s);
+    });
+  return hip_status(e);
+}
+
 int dflash_timing_enable(int on) {
   Timing& t = timing();
   std::lock_guard<std::mutex> g(t.mu);

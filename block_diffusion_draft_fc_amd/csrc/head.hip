@@ -1,0 +1,132 @@
+// Draft head ("DFlash KV Injection Walkthrough" Step 5): the stack's block
+// outputs go through a final RMSNorm over d, the last B-1 rows of every
+// request's block (row 0 is the known token, whose prediction is dropped) go
+// through lm_head, and greedy sampling keeps the argmax of each row's logits.
+// The lm_head product itself is one of the weight-streaming / tile GEMMs
+// (fp32 split-K partials [split][M][vocab]); this file holds the norm in front
+// of it and the argmax behind it.
+#include "kernels.hpp"
+
+namespace dflash {
+
+// x[m] = h[r*B + 1 + j] / sqrt(mean(h^2) + eps) * gamma for m = r*(B-1) + j:
+// one workgroup per output row, four columns per thread and pass.
+template <typename T>
+__global__ __launch_bounds__(256) void head_norm_kernel(const T* __restrict__ h, int B, int64_t d,
+                                                        const T* __restrict__ gamma, float eps,
+                                                        T* __restrict__ x) {
+  __shared__ float red[4];
+  const int64_t m = blockIdx.x;
+  const int64_t src_row = (m / (B - 1)) * B + 1 + m % (B - 1);
+  const T* row = h + src_row * d;
+  float ss = 0.f;
+  for (int64_t c = threadIdx.x; c < d; c += 256) {
+    const float v = to_f32(row[c]);
+    ss += v * v;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float r = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + eps);
+  for (int64_t c = threadIdx.x; c < d; c += 256) x[m * d + c] = from_f32<T>(to_f32(row[c]) * r * to_f32(gamma[c]));
+}
+
+hipError_t launch_head_norm(int dtype, const void* h, int64_t rows, int B, int64_t d, const void* gamma,
+                            float eps, void* x, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (dtype == 1)
+    launch(head_norm_kernel<bf16>, dim3((unsigned)rows), dim3(256), 0, s, static_cast<const bf16*>(h), B, d,
+           static_cast<const bf16*>(gamma), eps, static_cast<bf16*>(x));
+  else
+    launch(head_norm_kernel<float>, dim3((unsigned)rows), dim3(256), 0, s, static_cast<const float*>(h), B, d,
+           static_cast<const float*>(gamma), eps, static_cast<float*>(x));
+  return hipGetLastError();
+}
+
+// (value, index) pairs: the larger value wins, the lower index on a tie - the
+// first maximum, as an argmax over the row reports it.
+__device__ __forceinline__ void arg_better(float& v, int& i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) {
+    v = v2;
+    i = i2;
+  }
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float v2 = __shfl_xor(v, o, kWave);
+    const int i2 = __shfl_xor(i, o, kWave);
+    arg_better(v, i, v2, i2);
+  }
+}
+
+// Stage 1: workgroup (segment, row) sums the split-K partials of its
+// kHeadSeg-wide slice of the row's logits and keeps the slice's first maximum.
+template <int SPLITS_UNROLL>
+__global__ __launch_bounds__(256) void head_argmax_seg_kernel(const float* __restrict__ part, int splits,
+                                                              int64_t M, int64_t vocab,
+                                                              float* __restrict__ seg_val,
+                                                              int32_t* __restrict__ seg_idx) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int seg = blockIdx.x, nseg = gridDim.x;
+  const int64_t m = blockIdx.y;
+  const int64_t c0 = (int64_t)seg * kHeadSeg, c1 = min<int64_t>(vocab, c0 + kHeadSeg);
+  const int64_t stride = M * vocab;
+  float best = -INFINITY;
+  int bi = INT32_MAX;
+  for (int64_t c = c0 + 4 * threadIdx.x; c < c1; c += 4 * 256) {
+    // vocab % 4 == 0: four whole columns per thread and pass
+    const float* src = part + m * vocab + c;
+    f32x4 u = *reinterpret_cast<const f32x4*>(src);
+#pragma unroll SPLITS_UNROLL
+    for (int sp = 1; sp < splits; ++sp) u += *reinterpret_cast<const f32x4*>(src + sp * stride);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) arg_better(best, bi, u[e], (int)(c + e));
+  }
+  wave_argmax(best, bi);
+  if ((threadIdx.x & 63) == 0) {
+    sv[threadIdx.x >> 6] = best;
+    si[threadIdx.x >> 6] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) arg_better(best, bi, sv[w], si[w]);
+    seg_val[m * nseg + seg] = best;
+    seg_idx[m * nseg + seg] = bi;
+  }
+}
+
+// Stage 2: one wave per row reduces the segments' maxima.
+__global__ __launch_bounds__(256) void head_argmax_final_kernel(const float* __restrict__ seg_val,
+                                                                const int32_t* __restrict__ seg_idx, int nseg,
+                                                                int64_t M, int32_t* __restrict__ ids,
+                                                                float* __restrict__ max_logit) {
+  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (m >= M) return;
+  float best = -INFINITY;
+  int bi = INT32_MAX;
+  for (int s = lane; s < nseg; s += 64) arg_better(best, bi, seg_val[m * nseg + s], seg_idx[m * nseg + s]);
+  wave_argmax(best, bi);
+  if (lane == 0) {
+    ids[m] = bi;
+    if (max_logit != nullptr) max_logit[m] = best;
+  }
+}
+
+hipError_t launch_head_argmax(const float* part, int splits, int64_t M, int64_t vocab, float* seg_val,
+                              int32_t* seg_idx, int32_t* ids, float* max_logit, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const int nseg = (int)((vocab + kHeadSeg - 1) / kHeadSeg);
+  launch(head_argmax_seg_kernel<8>, dim3(nseg, (unsigned)M), dim3(256), 0, s, part, splits, M, vocab, seg_val,
+         seg_idx);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  launch(head_argmax_final_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s, seg_val, seg_idx, nseg, M, ids,
+         max_logit);
+  return hipGetLastError();
+}
+
+}  // namespace dflash

@@ -164,6 +164,19 @@ struct CombineArgs {
 };
 hipError_t launch_attn_combine(int dtype, const CombineArgs& a, hipStream_t s);
 
+// ---------------------------------------------------------------- draft head
+// x[m] = RMSNorm(h[r*B + 1 + j]) * gamma for m = r*(B-1) + j (the last B-1
+// rows of every request's block), in the storage type.
+hipError_t launch_head_norm(int dtype, const void* h, int64_t rows, int B, int64_t d, const void* gamma,
+                            float eps, void* x, hipStream_t s);
+// Columns per argmax segment (one workgroup per segment and row).
+constexpr int kHeadSeg = 8192;
+// ids[m] = the first argmax over n of sum_s part[s][m][n] (vocab % 4 == 0);
+// max_logit[m] its value (when not null).  seg_val / seg_idx: [M][ceil(vocab /
+// kHeadSeg)] scratch.
+hipError_t launch_head_argmax(const float* part, int splits, int64_t M, int64_t vocab, float* seg_val,
+                              int32_t* seg_idx, int32_t* ids, float* max_logit, hipStream_t s);
+
 // ---------------------------------------------------------------- cache
 struct AppendArgs {
   const void* k_rows;    // [n_rows][n_kv][d_h]

@@ -204,6 +204,29 @@ int dflash_kv_inject_attn(const dflash_layer_desc *L, dflash_cache *c, const voi
                           const int32_t *cu_ctx, const void *H, int32_t B, void *out,
                           void *ws, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Draft head ("DFlash KV Injection Walkthrough", Step 5): after the last draft
+ * layer, every request's block rows go through a final RMSNorm over d (gain
+ * gamma_f, the formula of hidden_norm), the last B-1 of them (row 0 holds the
+ * already-known token, whose prediction is dropped) through lm_head, and
+ * greedy sampling keeps the argmax over the vocabulary.
+ *   h         [R*B, d] device: the stack's output rows of the blocks
+ *   gamma_f   [d] device
+ *   w_lm      [vocab, d] device (output x input, no bias)
+ *   token_ids [R*(B-1)] int32 device: entry r*(B-1)+j = the draft token of
+ *             block position j+1 of request r, the first maximal logit
+ *   max_logit [R*(B-1)] float device, or NULL: that logit
+ *   ws        device workspace of at least dflash_draft_head_ws_bytes(R, B, d,
+ *             vocab, dtype) bytes
+ * Logits accumulate in fp32 from operands in the storage dtype (the normed
+ * rows are stored in it).  B == 1 (nothing to predict) is a no-op.
+ * d % 8 == 0, d <= 16384, vocab % 4 == 0, vocab < 2^30.
+ * ---------------------------------------------------------------------- */
+size_t dflash_draft_head_ws_bytes(int64_t R, int32_t B, int64_t d, int64_t vocab, int32_t dtype);
+int dflash_draft_head(const void *h, int64_t R, int32_t B, int64_t d, const void *gamma_f, float eps,
+                      const void *w_lm, int64_t vocab, int32_t dtype, int32_t *token_ids, float *max_logit,
+                      void *ws, size_t ws_bytes, void *stream);
+
 const char *dflash_strerror(int status);
 
 /* ------------------------------------------------------------------------
@@ -229,7 +252,10 @@ typedef enum {
   DFLASH_STAGE_O_REDUCE = 8,     /* o_proj reduction and store */
   DFLASH_STAGE_CACHE_APPEND = 9, /* dflash_cache_append copy */
   DFLASH_STAGE_PAGE_TABLE = 10,  /* device page-table update */
-  DFLASH_STAGE_COUNT = 11
+  DFLASH_STAGE_HEAD_NORM = 11,   /* draft head: final RMSNorm of the block tails */
+  DFLASH_STAGE_HEAD_GEMM = 12,   /* draft head: lm_head product */
+  DFLASH_STAGE_HEAD_ARGMAX = 13, /* draft head: argmax over the vocabulary */
+  DFLASH_STAGE_COUNT = 14
 } dflash_stage;
 
 int dflash_timing_enable(int on);

@@ -34,6 +34,9 @@ of readings kept with the design notes):
       (no upper bound: still non-causal inside the block).
   R14 layer stacks chain H_{l+1} = H_l + out_l (the decoder MLP is not on the
       pages).  parity unpinned: this chaining is a builder choice.
+  R21 the draft head samples greedily: the token of a row is the first index of
+      its maximal logit (temperature sampling would need random draws the
+      pages do not fix).
 """
 from __future__ import annotations
 
@@ -229,6 +232,47 @@ def crop(K, V, new_len: int):
     if not 0 <= new_len <= K.shape[1]:
         raise ValueError("crop beyond the current length")
     return K[:, :new_len], V[:, :new_len]
+
+
+# --------------------------------------------------------------------------
+# draft head, [W] Step 5
+# --------------------------------------------------------------------------
+
+def draft_head(h, gamma_f, eps: float, w_lm, B: int):
+    """[W] Step 5: after the last draft layer and a final RMSNorm over d, the
+    last B-1 rows of every request's block (the first row holds the known
+    token, whose prediction is dropped) go through lm_head (w_lm [vocab, d],
+    output x input, no bias), and greedy sampling (reading R21) keeps each
+    row's argmax.  h [R*B, d].  Returns logits [R*(B-1), vocab] and token ids
+    [R*(B-1)]; row r*(B-1)+j is block position j+1 of request r."""
+    h = f64(h)
+    R = h.shape[0] // B
+    x = rms_norm(h, gamma_f, eps).reshape(R, B, -1)[:, 1:, :].reshape(R * (B - 1), -1)
+    logits = x @ f64(w_lm).T
+    return logits, np.argmax(logits, axis=-1)
+
+
+def round_to_bf16(x) -> np.ndarray:
+    """Nearest bfloat16 value (ties to even) of each element, as float64: the
+    upper 16 bits of the float32 encoding after adding half an ulp of the
+    16-bit result (plus one when the kept part is odd).  Finite inputs."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (b >> np.uint64(16)) & np.uint64(1)
+    r = ((b + np.uint64(0x7FFF) + lsb) & np.uint64(0xFFFF0000)).astype(np.uint32)
+    return r.view(np.float32).astype(np.float64)
+
+
+def draft_head_decision(h, gamma_f, eps: float, w_lm, B: int, bf16_rows: bool):
+    """The argmax of draft_head taken in the kernel's precision (an integer
+    decided by floating point): the normed rows stored in the layer's storage
+    type (bfloat16 when bf16_rows), the logits accumulated in float32.
+    Returns (logits32 [R*(B-1), vocab] float32, ids)."""
+    h = f64(h)
+    R = h.shape[0] // B
+    x = rms_norm(h, gamma_f, eps).reshape(R, B, -1)[:, 1:, :].reshape(R * (B - 1), -1)
+    x = round_to_bf16(x) if bf16_rows else x
+    logits = x.astype(np.float32) @ np.asarray(w_lm, dtype=np.float32).T
+    return logits, np.argmax(logits, axis=-1)
 
 
 # --------------------------------------------------------------------------

@@ -208,3 +208,20 @@ def test_workspace_figures_cover_every_smaller_call():
         assert all(b >= a for a, b in zip(figs, figs[1:])), figs
     finally:
         L.LIB.dflash_cache_destroy(h)
+
+
+def test_draft_head_validation():
+    f = L.LIB.dflash_draft_head
+    ws = L.LIB.dflash_draft_head_ws_bytes(1, 16, 4096, 151936, L.DFLASH_BF16)
+    assert ws >= 15 * 151936 * 4
+    assert L.LIB.dflash_draft_head_ws_bytes(1, 1, 4096, 151936, L.DFLASH_BF16) == 0
+    args = lambda R=1, B=16, d=512, vocab=1000, dt=L.DFLASH_BF16, ids=FAKE, w=1 << 30: (  # noqa: E731
+        FAKE, R, B, d, FAKE, 1e-6, FAKE, vocab, dt, ids, None, FAKE, w, None)
+    assert f(*args(dt=9)) == L.ERR_DTYPE
+    assert f(*args(vocab=1002)) == L.ERR_SHAPE          # vocab % 4
+    assert f(*args(d=500)) == L.ERR_SHAPE               # d % 8
+    assert f(*args(R=0)) == L.ERR_SHAPE
+    assert f(*args(ids=None)) == L.ERR_ARG
+    assert f(*args(ids=FAKE + 2)) == L.ERR_ARG
+    assert f(*args(w=16)) == L.ERR_WORKSPACE
+    assert f(*args(B=1, ids=None)) == L.DFLASH_OK       # nothing to predict

@@ -1,0 +1,97 @@
+"""GPU parity of the draft head ("DFlash KV Injection Walkthrough" Step 5):
+final RMSNorm of the block rows, lm_head over the vocabulary, greedy argmax.
+
+The token ids are integers decided by floating point, so the oracle takes
+that decision in the kernel's precision (normed rows stored as bf16 for bf16
+layers, logits summed in fp32; oracle.draft_head_decision).  Ids must be equal
+wherever the decision is clear; where the oracle's top two fp32 logits lie
+within DELTA of each other (summation order alone can swap them) the GPU's id
+must be one whose fp32 logit is within DELTA of the maximum.  The maximal
+logit the GPU reports is compared with the fp64 oracle's logit of that id by
+rel-L2 (the layer bars: 1e-5 fp32, 1e-2 bf16).
+
+DELTA = 1e-3 (absolute): fp32 sums of 4096 products of magnitude <= 0.1 differ
+by order-of-summation errors below 1e-5; a normed row element may round to a
+neighbouring bf16 value on the two sides when its fp32 values straddle a
+rounding boundary (one ulp, 2^-8 relative, of a few elements times |w| ~ 1/64),
+which stays below 1e-4."""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU containers
+    pytest.skip("no GPU visible", allow_module_level=True)
+
+from block_diffusion_draft_fc_amd import _lib as L  # noqa: E402
+from oracle import dflash_oracle as O  # noqa: E402
+from workloads import configs, generate as G  # noqa: E402
+from workloads.device import to_device  # noqa: E402
+
+from gpu_harness import TOL, rel_l2, say  # noqa: E402
+
+DELTA = 1e-3
+
+
+def _run(wl, vocab):
+    say(f"case draft_head {wl.name} R={wl.R} B={wl.B} d={wl.d} vocab={vocab}")
+    hw = G.head_weights(wl, vocab)
+    h = G.head_input(wl)
+    dev = "cuda"
+    hd, gd, wd = to_device(h, wl, dev), to_device(hw["gamma_f"], wl, dev), to_device(hw["w_lm"], wl, dev)
+    M = wl.R * (wl.B - 1)
+    ids = torch.full((max(M, 1),), -1, dtype=torch.int32, device=dev)
+    mx = torch.full((max(M, 1),), float("nan"), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(L.dflash_draft_head_ws_bytes(wl.R, wl.B, wl.d, vocab, hd.dtype), 256), dtype=torch.uint8,
+                     device=dev)
+    L.dflash_draft_head(hd, wl.B, gd, wl.eps, wd, ids, ws, max_logit=mx)
+    torch.cuda.synchronize()
+    return h, hw, ids.cpu().numpy()[:M], mx.cpu().numpy().astype(np.float64)[:M]
+
+
+def _check(wl, vocab):
+    h, hw, ids, mx = _run(wl, vocab)
+    l64, _ = O.draft_head(h, hw["gamma_f"], wl.eps, hw["w_lm"], wl.B)
+    l32, ids32 = O.draft_head_decision(h, hw["gamma_f"], wl.eps, hw["w_lm"], wl.B, bf16_rows=wl.dtype == "bf16")
+    M = l64.shape[0]
+    assert ids.shape == (M,) and ids.min() >= 0 and ids.max() < vocab
+    top2 = np.sort(l32, axis=1)[:, -2:]
+    clear = (top2[:, 1] - top2[:, 0]) > DELTA
+    assert np.array_equal(ids[clear], ids32[clear]), f"ids differ on clear rows: {np.nonzero(ids != ids32)[0]}"
+    rows = np.arange(M)
+    assert np.all(l32[rows, ids] >= top2[:, 1] - DELTA)
+    e = rel_l2(mx, l64[rows, ids])
+    assert e <= TOL[wl.dtype], f"max logits rel-L2 {e:.3e}"
+    say(f"  rows {M}, clear {int(clear.sum())}, max-logit rel-L2 {e:.2e}")
+
+
+def test_walkthrough_head_f32():
+    """Walkthrough layer sizes (d 512, block of 4 -> 3 rows), fp32, a small vocabulary."""
+    _check(configs.WALKTHROUGH, 1000)
+
+
+def test_qwen3_vocab_bf16():
+    """The Qwen3-8B-shaped head: d 4096, block of 16 -> 15 rows, the 151936-entry
+    vocabulary (1.24 GB of lm_head, the full-K streaming GEMM)."""
+    _check(configs.DECODE_8K, configs.QWEN3_VOCAB)
+
+
+@pytest.mark.parametrize("R,B,d,vocab", [(4, 16, 512, 32000), (16, 16, 512, 12000), (2, 16, 4096, 20000),
+                                         (3, 2, 256, 4096), (1, 16, 1024, 8196)])
+def test_batched_heads_bf16(R, B, d, vocab):
+    """Several requests (60, 240, 30, 3 and 15 rows: the LDS, tile, stream and
+    full-K products), a vocabulary that is not a multiple of the argmax
+    segment, B = 2."""
+    wl = configs.DECODE_8K.scaled(name=f"head_R{R}_B{B}_d{d}", R=R, B=B, d=d)
+    _check(wl, vocab)
+
+
+def test_block_of_one_is_a_no_op():
+    wl = configs.WALKTHROUGH.scaled(name="head_B1", B=1)
+    hd = torch.zeros((1, wl.d), dtype=torch.float32, device="cuda")
+    w = torch.zeros((8, wl.d), dtype=torch.float32, device="cuda")
+    ids = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    L.dflash_draft_head(hd, 1, hd[0], wl.eps, w, ids, None)
+    torch.cuda.synchronize()
+    assert int(ids[0]) == -7

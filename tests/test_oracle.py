@@ -385,3 +385,87 @@ def test_stack_single_layer_matches_layer():
     outs, _ = st.round(x, [0, 2], H, 3)
     res = O.kv_inject_layer(p, K0, V0, O.ctx_project(x, w_fc, np.ones(d), 1e-6), H)
     assert np.array_equal(outs[0], res.out)
+
+
+# ---------------------------------------------------------------- draft head (Step 5)
+
+def _head_inputs(rng, B, d, vocab):
+    h = rng.standard_normal((B, d))
+    gamma = 1 + 0.1 * rng.standard_normal(d)
+    w = rng.standard_normal((vocab, d)) / math.sqrt(d)
+    return h, gamma, w
+
+
+def test_draft_head_keeps_the_last_rows():
+    """Step 5: the block's 4 output rows [4, 512] give 3 rows of logits, those
+    of positions 4-6; row 0 (the known token at position 3) does not enter.
+    Negating block row j negates logits row j - 1 and nothing else (the norm
+    and the product are odd in each row)."""
+    wl = configs.WALKTHROUGH
+    gh = GOLDEN["draft_head"]
+    rng = np.random.default_rng(0)
+    vocab = 50
+    h, gamma, w = _head_inputs(rng, wl.B, wl.d, vocab)
+    logits, ids = O.draft_head(h, gamma, wl.eps, w, wl.B)
+    assert logits.shape == (gh["rows_kept"], vocab) and ids.shape == (gh["rows_kept"],)
+    block_pos = GOLDEN["positions"]["q"]
+    assert block_pos[1:] == gh["positions"]
+    h0 = h.copy()
+    h0[0] = 7.0 * rng.standard_normal(wl.d)
+    assert np.array_equal(O.draft_head(h0, gamma, wl.eps, w, wl.B)[0], logits)
+    for j in range(1, wl.B):
+        hj = h.copy()
+        hj[j] = -hj[j]
+        lj, _ = O.draft_head(hj, gamma, wl.eps, w, wl.B)
+        for i in range(wl.B - 1):
+            assert np.allclose(lj[i], -logits[i] if i == j - 1 else logits[i], rtol=0, atol=1e-12)
+
+
+def test_draft_head_closed_forms():
+    """lm_head rows that are permuted unit vectors read single normed entries:
+    with every |h| entry equal to a, RMSNorm divides by a, so logit j of a row
+    is sign(h[pi(j)]) * gamma[pi(j)] (pi the permutation); requests are
+    independent blocks of B rows; the argmax is the first maximal logit."""
+    rng = np.random.default_rng(1)
+    d, B, R = 16, 3, 2
+    a = 2.5
+    signs = rng.choice([-1.0, 1.0], size=(R * B, d))
+    h = a * signs
+    gamma = 1.0 + np.arange(d) / 8.0
+    pi = rng.permutation(d)
+    w = np.eye(d)[pi]                       # row j = e_{pi(j)}
+    logits, ids = O.draft_head(h, gamma, 0.0, w, B)
+    rows = [r * B + 1 + j for r in range(R) for j in range(B - 1)]
+    want = signs[rows][:, pi] * gamma[pi][None, :]
+    assert np.allclose(logits, want, rtol=1e-15, atol=0)
+    assert list(ids) == [int(np.argmax(want[i])) for i in range(len(rows))]
+    # ties: two lm_head rows equal to the row holding the maximum -> the lower index
+    top = int(ids[0])
+    w2 = np.vstack([w, w[top:top + 1]])
+    _, ids2 = O.draft_head(h, gamma, 0.0, w2, B)
+    assert ids2[0] == top and top < d
+
+
+def test_round_to_bf16_matches_library_and_ties_to_even():
+    x = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -3.14159, 6.1e-5, 65504.0, 1e30, -2 ** -130])
+    got = O.round_to_bf16(x)
+    lib = torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(got, lib)
+    assert got[1] == 1.0 and got[2] == 1 + 2 ** -6     # halfway cases go to the even mantissa
+    r = np.random.default_rng(2).standard_normal(10000) * 10.0 ** np.random.default_rng(3).integers(-30, 30, 10000)
+    assert np.array_equal(O.round_to_bf16(r), torch.tensor(r, dtype=torch.float32).to(torch.bfloat16).double().numpy())
+
+
+def test_draft_head_decision_agrees_away_from_ties():
+    """The decision in the kernel's precision picks the fp64 argmax whenever
+    the fp64 top-2 gap exceeds the error of bf16 rows and fp32 sums."""
+    rng = np.random.default_rng(4)
+    B, d, vocab = 8, 256, 3000
+    h, gamma, w = _head_inputs(rng, B, d, vocab)
+    w = O.round_to_bf16(w)
+    l64, ids64 = O.draft_head(h, gamma, 1e-6, w, B)
+    l32, ids32 = O.draft_head_decision(h, gamma, 1e-6, w, B, bf16_rows=True)
+    assert np.max(np.abs(l32 - l64)) < 0.05
+    top2 = np.sort(l64, axis=1)[:, -2:]
+    clear = (top2[:, 1] - top2[:, 0]) > 0.05
+    assert clear.sum() >= 3 and np.array_equal(ids32[clear], ids64[clear])

@@ -27,6 +27,8 @@ PINS = [
     lambda: T.test_brute_force_tiny(4, 3, 3, 3),
     lambda: T.test_brute_force_tiny(5, 2, 1, 1),
     T.test_cache_growth_over_two_rounds,
+    T.test_draft_head_keeps_the_last_rows,
+    T.test_draft_head_closed_forms,
 ]
 
 
@@ -128,9 +130,36 @@ def _layer_q_front(p, K_cache, V_cache, C, H):
     return O.LayerResult(O.o_proj(o, p.w_o), res.K, res.V, q, A, qpos, res.kpos)
 
 
+def _head_first_rows(h, gamma_f, eps, w_lm, B):
+    h = O.f64(h); R = h.shape[0] // B
+    x = O.rms_norm(h, gamma_f, eps).reshape(R, B, -1)[:, :-1, :].reshape(R * (B - 1), -1)
+    logits = x @ O.f64(w_lm).T
+    return logits, np.argmax(logits, axis=-1)
+
+
+def _head_no_norm(h, gamma_f, eps, w_lm, B):
+    h = O.f64(h); R = h.shape[0] // B
+    x = (h * O.f64(gamma_f)).reshape(R, B, -1)[:, 1:, :].reshape(R * (B - 1), -1)
+    logits = x @ O.f64(w_lm).T
+    return logits, np.argmax(logits, axis=-1)
+
+
+def _head_weight_columns(h, gamma_f, eps, w_lm, B):
+    h = O.f64(h); R = h.shape[0] // B
+    x = O.rms_norm(h, gamma_f, eps).reshape(R, B, -1)[:, 1:, :].reshape(R * (B - 1), -1)
+    w = O.f64(w_lm)
+    logits = x @ w.reshape(w.shape[1], w.shape[0])
+    return logits, np.argmax(logits, axis=-1)
+
+
+def _head_last_max(h, gamma_f, eps, w_lm, B):
+    logits, _ = _ORIG["draft_head"](h, gamma_f, eps, w_lm, B)
+    return logits, logits.shape[1] - 1 - np.argmax(logits[:, ::-1], axis=-1)
+
+
 _ORIG = {name: getattr(O, name) for name in
          ("rope", "gqa_attention", "project_kv", "rms_norm", "ctx_project", "o_proj",
-          "crop", "visible", "rope_inv_freq", "kv_inject_layer")}
+          "crop", "visible", "rope_inv_freq", "kv_inject_layer", "draft_head")}
 
 MUTANTS = {
     "rope_sign_flipped": ("rope", _rope_sign),
@@ -149,6 +178,10 @@ MUTANTS = {
     "crop_does_nothing": ("crop", _crop_keep_block),
     "window_inclusive": ("visible", _window_inclusive),
     "queries_on_window_front": ("kv_inject_layer", _layer_q_front),
+    "head_first_rows": ("draft_head", _head_first_rows),
+    "head_no_norm": ("draft_head", _head_no_norm),
+    "head_weight_columns": ("draft_head", _head_weight_columns),
+    "head_last_maximum": ("draft_head", _head_last_max),
 }
 
 

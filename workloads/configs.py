@@ -109,4 +109,8 @@ STACK5_HYBRID = Workload(
     n_layers=5, window=4096, sliding_layers=(0, 2, 4))
 
 ALL = (WALKTHROUGH, FRESH_CTX, DECODE_8K, RAGGED_PAGED, STACK5_HYBRID)
+
+# Vocabulary of the Qwen3 family's lm_head (the draft head of a Qwen3-8B-shaped
+# draft model reads the target's lm_head: [151936, 4096]).
+QWEN3_VOCAB = 151936
 BY_NAME = {w.name: w for w in ALL}

@@ -25,7 +25,7 @@ import numpy as np
 from .configs import Workload
 
 # stream tags
-_FC, _LAYER, _PREFILL_KV, _PREFILL_LEN, _SCHED, _RAW, _ANCHOR, _MASK, _H_IID = range(1, 10)
+_FC, _LAYER, _PREFILL_KV, _PREFILL_LEN, _SCHED, _RAW, _ANCHOR, _MASK, _H_IID, _HEAD, _HEAD_IN = range(1, 12)
 
 
 def _rng(seed: int, *tags: int) -> np.random.Generator:
@@ -144,3 +144,18 @@ def round_inputs(wl: Workload, rnd: int, n_per_req):
         x[cu[r]:cu[r + 1]] = raw_rows(wl, rnd, r, n_per_req[r])
         h[r * wl.B:(r + 1) * wl.B] = block_rows(wl, rnd, r)
     return x, cu, h
+
+
+def head_weights(wl: Workload, vocab: int):
+    """Draft head: the final-norm gain [d] and lm_head [vocab, d] (output x
+    input), drawn like every other weight (N(0, 1/d), gain 1 + N(0, 0.1^2))."""
+    g = _rng(wl.seed, _HEAD, vocab)
+    gamma_f = 1.0 + _normal(g, (wl.d,), 0.1)
+    w_lm = _normal(g, (vocab, wl.d), 1.0 / np.sqrt(wl.d))
+    return {"gamma_f": _store(gamma_f, wl), "w_lm": _store(w_lm, wl)}
+
+
+def head_input(wl: Workload, rnd: int = 0) -> np.ndarray:
+    """Rows [R*B, d] that the draft head reads (the stack's output for the
+    blocks), N(0, 1)."""
+    return _store(_normal(_rng(wl.seed, _HEAD_IN, rnd), (wl.R * wl.B, wl.d)), wl)
