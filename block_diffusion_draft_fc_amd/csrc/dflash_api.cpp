@@ -144,6 +144,7 @@ struct SkinnyPlan {
   bool tile;         // gemm_tile_kernel (256x256 MFMA tiles) for many rows
   bool stream;       // gemm_stream_kernel (per-wave weight streams) for at most 32 rows
   bool fullk;        // gemm_fullk_kernel (no split-K partials) for at most 16 rows
+  bool resident;     // gemm_resident_kernel: at most 16 rows kept in LDS, very many columns
   int32_t m_tiles;   // tile plans only
 };
 
@@ -161,6 +162,16 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, size_t eb) {
   static const int use_fullk = env_int("DFLASH_GEMM_FULLK", 1, 0, 1);
   SkinnyPlan p{};
   p.mt = (int32_t)std::max<int64_t>(1, cdiv(M, 16));
+  static const int use_resident = env_int("DFLASH_GEMM_RESIDENT", 1, 0, 1);
+  // at most 16 rows and very many columns (a vocabulary): the rows stay in
+  // LDS and each wave streams whole weight tiles, one result
+  if (use_resident && eb == 2 && p.mt == 1 && K % 64 == 0 && K <= kResMaxK && N % 4 == 0 && N >= 65536) {
+    p.resident = true;
+    p.n_tiles = (int32_t)cdiv(N, 16);
+    p.k_chunk = (int32_t)K;
+    p.splits = 1;
+    return p;
+  }
   // at most 16 rows: the whole K in one workgroup per 16 columns, one result
   if (use_fullk && eb == 2 && p.mt == 1 && K % 512 == 0 && N % 4 == 0) {
     p.fullk = true;
@@ -330,6 +341,20 @@ hipError_t run_gemms(int32_t dt, const std::vector<GemmJob>& jobs, hipStream_t s
       t.m_tiles = j.plan.m_tiles;
       t.n_tiles = j.plan.n_tiles;
       hipError_t e = launch_gemm_tile(t, s);
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    if (j.plan.resident) {
+      FullkArgs f{};
+      f.x0 = static_cast<const bf16*>(j.x0);
+      f.x1 = static_cast<const bf16*>(j.x1);
+      f.m0 = (int32_t)j.m0;
+      f.m1 = (int32_t)j.m1;
+      f.w = static_cast<const bf16*>(j.w);
+      f.N = (int32_t)j.N;
+      f.K = (int32_t)j.K;
+      f.part = j.part;
+      hipError_t e = launch_gemm_resident(f, s);
       if (e != hipSuccess) return e;
       continue;
     }

@@ -17,6 +17,7 @@
 //    operand, one activation load feeding four weight tiles; no LDS, no
 //    barrier, and long per-wave streams.
 #include <algorithm>
+#include <cstdlib>
 
 #include <type_traits>
 
@@ -629,6 +630,110 @@ hipError_t launch_gemm_fullk(const FullkArgs& p, hipStream_t s) {
   if (p.m0 + p.m1 > 16 || p.K % (64 * kFullkWaves) != 0 || p.N % 4 != 0) return hipErrorInvalidValue;
   if ((p.part == nullptr) == (p.out == nullptr)) return hipErrorInvalidValue;
   launch(gemm_fullk_kernel, dim3((p.N + 15) / 16), dim3(64 * kFullkWaves), 0, s, p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- resident activations (bf16, at most 16 rows, many columns)
+// For products with tens of thousands of output columns and at most 16 rows
+// (the draft head's lm_head: 15 rows x 4096 -> 151936 columns): each
+// workgroup copies the activation rows into LDS once, then every wave streams
+// whole 16-column weight tiles over the full K straight into MFMA A operands
+// (16-byte loads, kResPf K-steps in flight per wave), reading the activation
+// operand from LDS.  Where the full-K kernel re-reads the activation rows for
+// every 16 columns (as many bytes as the weights), here each workgroup reads
+// them once; there are no split-K partials.  Result: fp32 [M][N].
+// LDS layout of the rows: 16-byte granule (row, chunk) at granule index
+// row * K/8 + (chunk ^ (row % 8)) - the xor spreads the 16 rows of an operand
+// read over the banks.
+// Requirements (checked by the planner): bf16, M <= 16, K a multiple of 64 and
+// at most kResMaxK, N a multiple of 4.
+// kResPf: 8 measured best on the lm_head shape (12 and 16 slower).
+constexpr int kResWaves = 8, kResPf = 8;
+
+__global__ __launch_bounds__(64 * kResWaves, 1) void gemm_resident_kernel(FullkArgs p) {
+  __shared__ __align__(16) unsigned char xs[16 * kResMaxK * 2];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int M = p.m0 + p.m1;
+  const int K = p.K;
+  const int gpr = K / 8;   // 16-byte granules per row (a multiple of 8)
+
+  // stage the 16 activation rows (rows past M read row 0; never stored):
+  // copy i fills granules 64 i .. 64 i + 63, lane l granule 64 i + l
+  for (int i = wave; i < 2 * K / 64; i += kResWaves) {
+    const int gi = 64 * i + lane;
+    const int row = gi / gpr, slot = gi - row * gpr;
+    const int chunk = slot ^ (row & 7);
+    const int m = row < M ? row : 0;
+    const bf16* xr = m < p.m0 ? p.x0 + (int64_t)m * K : p.x1 + (int64_t)(m - p.m0) * K;
+    lds_copy16(xr + 8 * chunk, xs + i * 1024);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // this wave's tiles: first, first + G, ... (G = waves in the grid); its
+  // work is the sequence of (tile, K-step) pairs, q = i * S + t
+  const int S = K / 64;
+  const int n_tiles = (p.N + 15) / 16;
+  const int G = gridDim.x * kResWaves;
+  const int first = blockIdx.x + gridDim.x * wave;
+  const int my_tiles = first < n_tiles ? (n_tiles - first + G - 1) / G : 0;
+  const int total = my_tiles * S;
+  if (total == 0) return;
+  const int j16 = lane & 15, q4 = lane >> 4;
+  // weight operand of step q: row tile * 16 + j16 (past N: row 0), K-values
+  // 64 t + 8 q4 .. (+ 32 for the second half); the prefetch past the last
+  // step re-reads that step (an L2 hit) so that every load is unconditional
+  auto wsrc = [&](int q) {
+    q = min(q, total - 1);
+    const int tile = first + G * (q / S);
+    int n = tile * 16 + j16;
+    n = n < p.N ? n : 0;
+    return p.w + (int64_t)n * K + 64 * (q % S) + 8 * q4;
+  };
+  const unsigned char* xrow = xs + j16 * gpr * 16;
+  const int xkey = j16 & 7;
+
+  bf16x8 ra[kResPf], rb[kResPf];
+#pragma unroll
+  for (int u = 0; u < kResPf; ++u) {
+    const bf16* src = wsrc(u);
+    ra[u] = load8(src);
+    rb[u] = load8(src + 32);
+  }
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int base = 0; base < total; base += kResPf) {
+#pragma unroll
+    for (int u = 0; u < kResPf; ++u) {
+      const int q = base + u;
+      if (q < total) {
+        const int t = q % S;
+        const bf16x8 x0 = *reinterpret_cast<const bf16x8*>(xrow + (8 * t + (q4 ^ xkey)) * 16);
+        const bf16x8 x1 = *reinterpret_cast<const bf16x8*>(xrow + (8 * t + ((4 + q4) ^ xkey)) * 16);
+        acc = mma32(ra[u], x0, acc);
+        acc = mma32(rb[u], x1, acc);
+        if (t == S - 1) {
+          // lane (j16, q4): row m = j16, columns tile * 16 + 4 q4 .. +3
+          const int n = (first + G * (q / S)) * 16 + 4 * q4;
+          if (j16 < M && n < p.N) *reinterpret_cast<f32x4*>(p.part + (int64_t)j16 * p.N + n) = acc;
+          acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      const bf16* src = wsrc(base + u + kResPf);
+      ra[u] = load8(src);
+      rb[u] = load8(src + 32);
+    }
+  }
+}
+
+hipError_t launch_gemm_resident(const FullkArgs& p, hipStream_t s) {
+  if (p.m0 + p.m1 <= 0 || p.N <= 0) return hipSuccess;
+  if (p.m0 + p.m1 > 16 || p.K % 64 != 0 || p.K > kResMaxK || p.N % 4 != 0 || p.part == nullptr)
+    return hipErrorInvalidValue;
+  // one workgroup per CU (the rows take most of the LDS), capped by the tiles
+  const int tiles = (p.N + 15) / 16;
+  const int blocks = std::min(256, (tiles + kResWaves - 1) / kResWaves);
+  launch(gemm_resident_kernel, dim3(blocks), dim3(64 * kResWaves), 0, s, p);
   return hipGetLastError();
 }
 

@@ -10,35 +10,56 @@
 namespace dflash {
 
 // x[m] = h[r*B + 1 + j] / sqrt(mean(h^2) + eps) * gamma for m = r*(B-1) + j:
-// one workgroup per output row, four columns per thread and pass.
+// one workgroup per output row; each thread holds eight consecutive columns
+// per pass (d <= 16384: at most four passes), loaded once for both the sum of
+// squares and the output.
 template <typename T>
-__global__ __launch_bounds__(256) void head_norm_kernel(const T* __restrict__ h, int B, int64_t d,
+__global__ __launch_bounds__(512) void head_norm_kernel(const T* __restrict__ h, int B, int64_t d,
                                                         const T* __restrict__ gamma, float eps,
                                                         T* __restrict__ x) {
-  __shared__ float red[4];
+  constexpr int PASSES = 4;
+  __shared__ float red[8];
   const int64_t m = blockIdx.x;
   const int64_t src_row = (m / (B - 1)) * B + 1 + m % (B - 1);
   const T* row = h + src_row * d;
+  vec8_t<T> v[PASSES];
   float ss = 0.f;
-  for (int64_t c = threadIdx.x; c < d; c += 256) {
-    const float v = to_f32(row[c]);
-    ss += v * v;
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int64_t c = ((int64_t)p * 512 + threadIdx.x) * 8;
+    v[p] = c < d ? load8(row + c) : zero8<T>();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += to_f32(v[p][e]) * to_f32(v[p][e]);
   }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float r = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + eps);
-  for (int64_t c = threadIdx.x; c < d; c += 256) x[m * d + c] = from_f32<T>(to_f32(row[c]) * r * to_f32(gamma[c]));
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) tot += red[w];
+  const float r = 1.0f / sqrtf(tot / (float)d + eps);
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int64_t c = ((int64_t)p * 512 + threadIdx.x) * 8;
+    if (c < d) {
+      const vec8_t<T> g = load8(gamma + c);
+      f32x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = to_f32(v[p][e]) * r * to_f32(g[e]);
+      store8(x + m * d + c, cvt8<T>(o));
+    }
+  }
 }
 
 hipError_t launch_head_norm(int dtype, const void* h, int64_t rows, int B, int64_t d, const void* gamma,
                             float eps, void* x, hipStream_t s) {
   if (rows == 0) return hipSuccess;
+  // d % 8 == 0 and d <= 16384 (checked by the caller)
   if (dtype == 1)
-    launch(head_norm_kernel<bf16>, dim3((unsigned)rows), dim3(256), 0, s, static_cast<const bf16*>(h), B, d,
+    launch(head_norm_kernel<bf16>, dim3((unsigned)rows), dim3(512), 0, s, static_cast<const bf16*>(h), B, d,
            static_cast<const bf16*>(gamma), eps, static_cast<bf16*>(x));
   else
-    launch(head_norm_kernel<float>, dim3((unsigned)rows), dim3(256), 0, s, static_cast<const float*>(h), B, d,
+    launch(head_norm_kernel<float>, dim3((unsigned)rows), dim3(512), 0, s, static_cast<const float*>(h), B, d,
            static_cast<const float*>(gamma), eps, static_cast<float*>(x));
   return hipGetLastError();
 }
@@ -63,7 +84,6 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
 
 // Stage 1: workgroup (segment, row) sums the split-K partials of its
 // kHeadSeg-wide slice of the row's logits and keeps the slice's first maximum.
-template <int SPLITS_UNROLL>
 __global__ __launch_bounds__(256) void head_argmax_seg_kernel(const float* __restrict__ part, int splits,
                                                               int64_t M, int64_t vocab,
                                                               float* __restrict__ seg_val,
@@ -76,14 +96,30 @@ __global__ __launch_bounds__(256) void head_argmax_seg_kernel(const float* __res
   const int64_t stride = M * vocab;
   float best = -INFINITY;
   int bi = INT32_MAX;
-  for (int64_t c = c0 + 4 * threadIdx.x; c < c1; c += 4 * 256) {
-    // vocab % 4 == 0: four whole columns per thread and pass
-    const float* src = part + m * vocab + c;
-    f32x4 u = *reinterpret_cast<const f32x4*>(src);
-#pragma unroll SPLITS_UNROLL
-    for (int sp = 1; sp < splits; ++sp) u += *reinterpret_cast<const f32x4*>(src + sp * stride);
+  // vocab % 4 == 0: four whole columns per thread and pass; the segment's
+  // kHeadSeg / 1024 passes are unrolled so that their loads are in flight
+  // together (columns past the vocabulary are skipped)
+  constexpr int PASSES = kHeadSeg / 1024;
+  f32x4 u[PASSES];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) arg_better(best, bi, u[e], (int)(c + e));
+  for (int i = 0; i < PASSES; ++i) {
+    const int64_t c = c0 + 4 * threadIdx.x + 1024 * i;
+    u[i] = c < c1 ? *reinterpret_cast<const f32x4*>(part + m * vocab + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int sp = 1; sp < splits; ++sp) {
+#pragma unroll
+    for (int i = 0; i < PASSES; ++i) {
+      const int64_t c = c0 + 4 * threadIdx.x + 1024 * i;
+      if (c < c1) u[i] += *reinterpret_cast<const f32x4*>(part + sp * stride + m * vocab + c);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PASSES; ++i) {
+    const int64_t c = c0 + 4 * threadIdx.x + 1024 * i;
+    if (c < c1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) arg_better(best, bi, u[i][e], (int)(c + e));
+    }
   }
   wave_argmax(best, bi);
   if ((threadIdx.x & 63) == 0) {
@@ -120,7 +156,7 @@ hipError_t launch_head_argmax(const float* part, int splits, int64_t M, int64_t 
                               int32_t* seg_idx, int32_t* ids, float* max_logit, hipStream_t s) {
   if (M == 0) return hipSuccess;
   const int nseg = (int)((vocab + kHeadSeg - 1) / kHeadSeg);
-  launch(head_argmax_seg_kernel<8>, dim3(nseg, (unsigned)M), dim3(256), 0, s, part, splits, M, vocab, seg_val,
+  launch(head_argmax_seg_kernel, dim3(nseg, (unsigned)M), dim3(256), 0, s, part, splits, M, vocab, seg_val,
          seg_idx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

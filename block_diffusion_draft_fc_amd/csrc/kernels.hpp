@@ -90,6 +90,12 @@ struct FullkArgs {
   const void* add;
 };
 hipError_t launch_gemm_fullk(const FullkArgs& p, hipStream_t s);
+// The same product with the (at most 16) activation rows resident in LDS and
+// whole-K 16-column weight tiles streamed per wave, for very many columns:
+// bf16, K a multiple of 64 and at most kResMaxK, N of 4; writes part (fp32
+// [M][N]) only.
+constexpr int kResMaxK = 4096;
+hipError_t launch_gemm_resident(const FullkArgs& p, hipStream_t s);
 
 // LDS budget for the staged activation slice of one gemm_lds_kernel workgroup.
 constexpr int kLdsGemmBytes = 64 * 1024;
