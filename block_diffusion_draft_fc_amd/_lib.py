@@ -126,11 +126,12 @@ class Cache:
             self.k_pool, self.v_pool, self.table = pools
         elif page_size == 0:
             self.k_pool = torch.zeros((n_seqs, n_kv, capacity, d_h), dtype=dtype, device=device)
-            self.v_pool = torch.zeros((n_seqs, n_kv, d_h, capacity), dtype=dtype, device=device)
+            # V transposed in tiles of 64 slots: [.., tile, head dim, slot % 64]
+            self.v_pool = torch.zeros((n_seqs, n_kv, -(-capacity // 64), d_h, 64), dtype=dtype, device=device)
             self.table = None
         else:
             self.k_pool = torch.zeros((capacity, n_kv, page_size, d_h), dtype=dtype, device=device)
-            self.v_pool = torch.zeros((capacity, n_kv, d_h, page_size), dtype=dtype, device=device)
+            self.v_pool = torch.zeros((capacity, n_kv, -(-page_size // 64), d_h, 64), dtype=dtype, device=device)
             self.table = torch.full((n_seqs, max_pages_per_seq), -1, dtype=torch.int32, device=device)
         desc = CacheDesc(n_seqs, n_kv, d_h, dtype_code(dtype), page_size, max_pages_per_seq, 1 if ring else 0,
                          capacity,

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
       for (int s = 0; s < DS; ++s) kv[kt][s] = load8(kb + (int64_t)kr * DH + 32 * s + 8 * q4);
     }
 #pragma unroll
-    for (int d = 0; d < DT; ++d) vv[d] = load8(vb + (int64_t)(16 * d + j16) * a.cache.page_rows + 8 * q4);
+    for (int d = 0; d < DT; ++d) vv[d] = load8(vb + (16 * d + j16) * kVTile + 8 * q4);
     // keep the loads here: without the barrier the compiler sinks them to
     // their first use, which leaves no block in flight while another computes
     asm volatile("" ::: "memory");
@@ -410,7 +410,7 @@ __global__ __launch_bounds__(256, 1) void attn_lds_kernel(AttnArgs a) {
                                          sb + (kt * DS + s) * 1024, 16, 0, 0);
 #pragma unroll
     for (int d = 0; d < DT; ++d)
-      __builtin_amdgcn_global_load_lds(vb + (int64_t)(16 * d + j16) * a.cache.page_rows + 8 * q4,
+      __builtin_amdgcn_global_load_lds(vb + (16 * d + j16) * kVTile + 8 * q4,
                                        sb + (KSLABS + d) * 1024, 16, 0, 0);
   };
 
@@ -768,7 +768,7 @@ __global__ __launch_bounds__(256, 1) void attn_ring_kernel(AttnArgs a) {
         src = kb + (int64_t)(krow + 4 * kt) * DH + 32 * s + 8 * q4;
       } else {
         const int d = slab - KSLABS;
-        src = vb + (int64_t)(16 * d + j16) * a.cache.page_rows + 8 * q4;
+        src = vb + (16 * d + j16) * kVTile + 8 * q4;
       }
       lds_copy16(src, sb + slab * 1024);
     }
@@ -872,8 +872,11 @@ __global__ __launch_bounds__(256, 1) void attn_ring_kernel(AttnArgs a) {
 // attn_ring_kernel with 64-key blocks: twice the keys per barrier and per
 // dependency chain (K reads -> S -> softmax -> PV) of each wave, and V^T copied
 // in whole 128-byte lines (64 keys of one head dim).  A stage holds
-//   K: operand-order slabs (half hh, key tile kt, head-dim step s), lane l's
-//      16 bytes at 16 l: key 32 hh + krow(l % 16) + 4 kt, dims 32 s + 8 (l / 16);
+//   K: the block's 64 key rows in key order (2 DH bytes each), the 16-byte
+//      chunk c of key j at position c ^ kswz(j) within its row - each copy
+//      moves whole rows (1 KB of consecutive keys, contiguous in the cache),
+//      picking per lane the chunk its slot holds; an operand read (16 keys,
+//      one chunk) then covers all banks;
 //   V^T: one 128-byte row per head dim R (the block's 64 keys), in 16-byte
 //      chunks of 8 keys, chunk c at position c ^ (R % 8) ^ ((R / 8) % 2) - each
 //      copy moves 8 whole rows and picks, per lane, the chunk its slot holds;
@@ -889,7 +892,9 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_kernel(AttnArgs a) {
   static_assert(NST >= 2 && NST <= 8, "blocks in flight are counted by wait_vm_blocks (up to 6 after the current)");
   constexpr int DS = DH / 32;                 // K=32 steps over the head dim
   constexpr int DT = DH / 16;                 // 16-dim tiles of the head dim
-  constexpr int KSLABS = 4 * DS;              // (hh, kt, s)
+  constexpr int KSLABS = DH / 8;              // 1 KB copies of 1024 / (2 DH) key rows
+  constexpr int CK = DH / 8;                  // 16-byte chunks per key row
+  static_assert(DH == 64 || DH == 128, "key-row swizzle defined for d_h 64 and 128");
   constexpr int VROWS = DH / 8;               // 1 KB copies of 8 V^T rows
   constexpr int COPIES = KSLABS + VROWS;
   constexpr int PER_WAVE = COPIES / 4;
@@ -944,6 +949,16 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_kernel(AttnArgs a) {
   const bf16* kpool = static_cast<const bf16*>(a.cache.k_pool);
   const bf16* vpool = static_cast<const bf16*>(a.cache.v_pool);
   const int krow = 8 * (j16 >> 2) + (j16 & 3);   // + 4 kt + 32 hh: key of A-operand row j16
+  // chunk swizzle of key row j: a function of the key bits that krow varies
+  // (0, 1, 3, 4), distinct over an operand read's 16 keys in every 256 bytes
+  auto kswz = [](int j) { return DH == 128 ? (j & 3) | ((j >> 1) & 12) : ((j >> 1) & 1) | ((j >> 2) & 6); };
+  // K copies: lane l fills key kcopy_key + l / CK, slot l % CK
+  const int kkey_in = lane / CK, kslot = lane % CK;
+  // K operand reads: key 32 hh + 4 kt + krow (whose swizzle is kswz(krow)),
+  // chunk 4 s + q4
+  int koff[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) koff[s] = krow * (2 * DH) + (((4 * s + q4) ^ kswz(krow)) * 16);
   // V^T copies: lane l fills row 8 i + l / 8, slot l % 8, with the chunk the swizzle puts there
   const int vrow_in = lane >> 3;
   // V^T fragment reads: row 16 d + j16, chunk 4 kk + q4 at its swizzled position
@@ -951,8 +966,13 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_kernel(AttnArgs a) {
   const int voff0 = j16 * 128 + ((q4) ^ vkey) * 16;
   const int voff1 = j16 * 128 + ((4 + q4) ^ vkey) * 16;
 
+  // blocks in a rotated order (the online softmax does not depend on it): the
+  // items that run at once then do not all stream the same offsets of their
+  // chunks at the same time
+  const int rot0 = a.rot > 0 && nblk > 0 ? (int)(((unsigned)item * (unsigned)a.rot) % (unsigned)nblk) : 0;
+  auto rot_blk = [&](int b) { const int x = b + rot0; return x >= nblk ? x - nblk : x; };
   auto issue = [&](int b) {
-    const int blk = kbeg + 64 * b;
+    const int blk = kbeg + 64 * rot_blk(b);
     const int64_t page = s_page[blk / a.cache.page_rows - pg0];
     const int slot = blk % a.cache.page_rows;
     const bf16* kb = kpool + k_offset(a.cache, page, g, slot);
@@ -963,13 +983,12 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_kernel(AttnArgs a) {
       const int idx = wave * PER_WAVE + i;
       const bf16* src;
       if (idx < KSLABS) {
-        const int hk = idx / DS, s = idx - hk * DS;
-        const int hh = hk >> 1, kt = hk & 1;
-        src = kb + (int64_t)(32 * hh + krow + 4 * kt) * DH + 32 * s + 8 * q4;
+        const int key = idx * (64 / CK) + kkey_in;
+        src = kb + (int64_t)key * DH + 8 * (kslot ^ kswz(key));
       } else {
         const int R = 8 * (idx - KSLABS) + vrow_in;
         const int c = (lane & 7) ^ (R & 7) ^ ((R >> 3) & 1);
-        src = vb + (int64_t)R * a.cache.page_rows + 8 * c;
+        src = vb + R * kVTile + 8 * c;
       }
       lds_copy16(src, sb + idx * 1024);
     }
@@ -977,9 +996,9 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_kernel(AttnArgs a) {
 
   auto process = [&](int b) {
     const unsigned char* sb = ring + (b % NST) * STAGE;
-    const unsigned char* kbs = sb + 16 * lane;
+    const unsigned char* kbs = sb;
     const unsigned char* vbs = sb + KSLABS * 1024;
-    const int blk = kbeg + 64 * b;
+    const int blk = kbeg + 64 * rot_blk(b);
     // scores: lane (j16, q4) holds row j16's keys blk + 32 hh + 8 q4 .. +7 in sv[hh]
     f32x8 sv[2];
 #pragma unroll
@@ -989,7 +1008,7 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_kernel(AttnArgs a) {
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int s = 0; s < DS; ++s)
-          kv[kt][s] = *reinterpret_cast<const V8*>(kbs + (((2 * hh + kt) * DS + s) * 1024));
+          kv[kt][s] = *reinterpret_cast<const V8*>(kbs + (32 * hh + 4 * kt) * (2 * DH) + koff[s]);
       f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int s = 0; s < DS; ++s)
@@ -1089,16 +1108,19 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_kernel(AttnArgs a) {
     process(b);
   }
 
+  // partials as non-temporal stores: the combine reads them once, after
+  // this kernel, and the stores at the end of every item cost the stream less
   float* po = a.part_o + (int64_t)item * a.qrows * DH;
 #pragma unroll
-  for (int d = 0; d < DT; ++d) *reinterpret_cast<f32x4*>(po + (int64_t)row * DH + 16 * d + 4 * q4) = o[d];
+  for (int d = 0; d < DT; ++d)
+    __builtin_nontemporal_store(o[d], reinterpret_cast<f32x4*>(po + (int64_t)row * DH + 16 * d + 4 * q4));
   float l = l_run;
   l += __shfl_xor(l, 16, kWave);
   l += __shfl_xor(l, 32, kWave);
   if (q4 == 0) {
     float* pml = a.part_ml + (int64_t)item * 2 * a.qrows;
-    pml[row] = m_run;
-    pml[a.qrows + row] = l;
+    __builtin_nontemporal_store(m_run, pml + row);
+    __builtin_nontemporal_store(l, pml + a.qrows + row);
   }
 }
 
@@ -1113,24 +1135,16 @@ static hipError_t launch_attn_t(const AttnArgs& a, int items, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
     // bf16, four query tiles: the shared ring of 64-key blocks.  For
     // comparison, DFLASH_ATTN_KERNEL=ring32 takes the ring of 32-key blocks
-    // and =lds the per-wave LDS rings; DFLASH_ATTN_NST sets the depth of the
-    // 64-key ring.
+    // and =lds the per-wave LDS rings.
     static const int kind = [] {
       const char* e = std::getenv("DFLASH_ATTN_KERNEL");
       if (e == nullptr) return 0;
       const std::string v(e);
       return v == "ring32" ? 2 : v == "lds" ? 3 : 0;
     }();
-    // Ring depth: with at most one work item per CU, three stages (96 KB, one
-    // workgroup per CU: two blocks in flight while it computes on a third;
-    // four stages measured slower on the 8K decode workload); with more, two
-    // stages (64 KB), so that two workgroups share a CU and cover each other's
-    // load latency.
-    static const int forced_nst = [] {
-      const char* e = std::getenv("DFLASH_ATTN_NST");
-      return e ? std::atoi(e) : 0;
-    }();
-    const int nst = forced_nst > 0 ? forced_nst : items <= 256 ? 3 : 2;
+    // Ring depth from the host's plan (three stages, 96 KB: one workgroup per
+    // CU; two, 64 KB: two per CU; four: one per CU, three blocks ahead)
+    const int nst = a.nst > 0 ? a.nst : items <= 256 ? 3 : 2;
     if (kind == 0 && nqt == 4) {
       if (a.d_h == 128) {
         if (nst == 2) launch((attn_ring64_kernel<128, 2>), dim3(items), dim3(256), 0, s, a);

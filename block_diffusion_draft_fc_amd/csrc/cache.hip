@@ -30,12 +30,11 @@ __global__ __launch_bounds__(256) void cache_append_kernel(AppendArgs a, int64_t
   const W* ks = static_cast<const W*>(a.k_rows) + src;
   const W* vs = static_cast<const W*>(a.v_rows) + src;
   W* kd = static_cast<W*>(a.cache.k_pool) + k_offset(a.cache, page, g, slot) + c8 * 8;
-  W* vd = static_cast<W*>(a.cache.v_pool) + v_offset(a.cache, page, g, slot) +
-          (int64_t)c8 * 8 * a.cache.page_rows;
+  W* vd = static_cast<W*>(a.cache.v_pool) + v_offset(a.cache, page, g, slot) + c8 * 8 * kVTile;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     kd[e] = ks[e];
-    vd[(int64_t)e * a.cache.page_rows] = vs[e];
+    vd[e * kVTile] = vs[e];
   }
 }
 

@@ -122,18 +122,61 @@ hipError_t staged(int stage, hipStream_t s, bool launches, F&& f) {
   return e;
 }
 
-// Attention work items to aim for, given the keys of all (sequence, K/V head)
-// pairs: about one per CU for up to 256K keys, where each CU's ring then
-// runs three blocks deep; four per CU beyond, where two workgroups share a CU
-// and cover each other's latency (measured on the 8K decode and the 16-request
-// ragged workloads).  DFLASH_ATTN_TARGET_ITEMS overrides.
-int attn_target_items(int64_t total_keys) {
-  static const int forced = [] {
-    const char* e = std::getenv("DFLASH_ATTN_TARGET_ITEMS");
-    return e ? std::min(std::max(std::atoi(e), 1), kAttnMaxTarget) : 0;
-  }();
-  if (forced > 0) return forced;
-  return total_keys > ((int64_t)256 << 10) ? 1024 : 256;
+// How one attention launch splits the keys into work items (sequence, K/V
+// head, chunk of `chunk` keys) and which ring depth runs them.
+//  * Ring depth: up to 256K keys over all (sequence, K/V head) pairs, three
+//    stages and one workgroup per CU (the 8K decode round: each CU's ring
+//    runs two blocks ahead of its compute); beyond, two stages and two
+//    workgroups per CU, which cover each other's load latency.
+//  * Item count: the CUs hold `slots` workgroups at once (256 or 512).  Items
+//    past a whole number of rounds of slots would run by themselves at the end
+//    (a few items over 512 cost a third of the time on the 16-request ragged
+//    batch), so the chunk is the smallest multiple of 64 keys (at least 128)
+//    whose items fit `rounds` rounds.  One round measured best on the ragged
+//    batch and the 5-layer stack, where two rounds balance the unequal last
+//    chunks of the requests no better than they cost in partials.
+// DFLASH_ATTN_NST forces the depth, DFLASH_ATTN_ROUNDS the rounds, and
+// DFLASH_ATTN_TARGET_ITEMS a plain target count instead of the fit.
+struct AttnSplit {
+  int64_t chunk;
+  int64_t items;
+  int nst;
+};
+
+AttnSplit plan_attn_split(const std::vector<int64_t>& keys, int n_kv, int64_t chunk_cap) {
+  static const int forced_nst = env_int("DFLASH_ATTN_NST", 0, 0, 4);
+  static const int rounds_env = env_int("DFLASH_ATTN_ROUNDS", 1, 1, 4);
+  static const int target_env = env_int("DFLASH_ATTN_TARGET_ITEMS", 0, 0, kAttnMaxTarget);
+  int64_t total = 0;
+  for (int64_t k : keys) total += k * n_kv;
+  AttnSplit sp{};
+  sp.nst = forced_nst > 0 ? forced_nst : total > ((int64_t)256 << 10) ? 2 : 3;
+  auto items_of = [&](int64_t chunk) {
+    int64_t it = 0;
+    for (int64_t k : keys) it += std::max<int64_t>(1, cdiv(k, chunk)) * n_kv;
+    return it;
+  };
+  const int64_t cap = std::max<int64_t>(128, chunk_cap / 64 * 64);
+  if (target_env > 0) {
+    sp.chunk = std::min(cap, std::max<int64_t>(128, cdiv(cdiv(total, target_env), 64) * 64));
+  } else {
+    const int64_t slots = sp.nst == 2 ? 512 : 256;
+    const int64_t limit = std::min<int64_t>(kAttnMaxTarget, rounds_env * slots);
+    // items_of is non-increasing in the chunk: the smallest chunk (in units of
+    // 64 keys) in [2, cap / 64] with items_of <= limit, else the cap
+    int64_t lo = 2, hi = cap / 64;
+    if (items_of(hi * 64) > limit) {
+      lo = hi;
+    } else {
+      while (lo < hi) {
+        const int64_t mid = (lo + hi) / 2;
+        if (items_of(mid * 64) <= limit) hi = mid; else lo = mid + 1;
+      }
+    }
+    sp.chunk = lo * 64;
+  }
+  sp.items = items_of(sp.chunk);
+  return sp;
 }
 
 // ---------------------------------------------------------------- GEMM planning
@@ -850,7 +893,6 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
     aa.R = R; aa.B = B; aa.n_kv = L->n_kv; aa.group = (int32_t)p.group; aa.qrows = (int32_t)p.qrows;
     aa.d_h = L->d_h; aa.window = L->window;
     aa.scale_log2 = (float)(1.0 / std::sqrt((double)L->d_h) * 1.4426950408889634);
-    int64_t total = 0;
     std::vector<int64_t> keys(R);
     for (int r = 0; r < R; ++r) {
       const int64_t hi = c->len[r] + n[r] + B;
@@ -859,20 +901,23 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
       aa.key_lo[r] = (int32_t)lo;
       aa.qpos0[r] = (int32_t)(c->len[r] + n[r]);
       keys[r] = hi - (lo & ~int64_t(63));
-      total += keys[r] * L->n_kv;
     }
-    // keys per work item: a multiple of 64 (the largest key block of the
-    // kernels; chunks start at multiples of 64), at least 128, sized so that
-    // the items cover the target count
-    int64_t chunk = cdiv(cdiv(total, attn_target_items(total)), 64) * 64;
-    chunk = std::max<int64_t>(chunk, 128);
     // an item's keys may span at most kAttnMaxChunkPages pages (its page list
-    // is staged in LDS); two pages go to a chunk that does not start on a page
-    if (cd.page_size > 0)
-      chunk = std::min<int64_t>(chunk, (int64_t)(kAttnMaxChunkPages - 2) * cd.page_size);
-    // a ring's positions wrap every `capacity` rows: each wrap an item spans
-    // takes one more entry of its page list
-    if (cd.ring) chunk = std::min<int64_t>(chunk, (int64_t)(kAttnMaxChunkPages - 2) * cd.capacity);
+    // is staged in LDS); two pages go to a chunk that does not start on a page.
+    // A ring's positions wrap every `capacity` rows: each wrap an item spans
+    // takes one more entry of its page list.
+    int64_t cap = (int64_t)1 << 30;
+    if (cd.page_size > 0) cap = std::min<int64_t>(cap, (int64_t)(kAttnMaxChunkPages - 2) * cd.page_size);
+    if (cd.ring) cap = std::min<int64_t>(cap, (int64_t)(kAttnMaxChunkPages - 2) * cd.capacity);
+    const AttnSplit sp = plan_attn_split(keys, L->n_kv, cap);
+    const int64_t chunk = sp.chunk;
+    aa.nst = sp.nst;
+    // each item starts its blocks at (item * rot) mod its block count: with
+    // every item starting at block 0, the items running at once stream
+    // regularly spaced addresses in step (a 4 x 33K batch: 125 -> 110 us).
+    // DFLASH_ATTN_ROT=0 keeps the plain order.
+    static const int rot = env_int("DFLASH_ATTN_ROT", 37, 0, 1 << 20);
+    aa.rot = rot;
     aa.chunk_keys = (int32_t)chunk;
     int64_t items = 0;
     for (int r = 0; r < R; ++r) {

@@ -126,9 +126,19 @@ __device__ __forceinline__ int64_t cache_page(const CacheView& c, int seq, int p
 __device__ __forceinline__ int64_t k_offset(const CacheView& c, int64_t page, int g, int slot) {
   return ((page * c.n_kv + g) * (int64_t)c.page_rows + slot) * c.d_h;
 }
-// Element offset of V^T[seq][g][0][pos] (V rows stored key-minor).
+// V is stored transposed in tiles of kVTile slots: tile t of a (page, head)
+// holds d_h rows of kVTile elements, row i = head dim i of slots
+// t * kVTile .. t * kVTile + kVTile - 1.  A 64-key block (blocks start at
+// multiples of 64) is then one contiguous run of d_h * 64 elements, whatever
+// the capacity or page size: the rows of a whole-page transposed layout sit a
+// page apart, and at some page strides (capacity 129 * 64, say) the 128 rows
+// of every block meet in the same memory channels.
+constexpr int kVTile = 64;
+// Element offset of V^T head dim 0 of slot `slot`; head dim i is kVTile * i
+// further.
 __device__ __forceinline__ int64_t v_offset(const CacheView& c, int64_t page, int g, int slot) {
-  return (page * c.n_kv + g) * (int64_t)c.d_h * c.page_rows + slot;
+  return (page * c.n_kv + g) * (int64_t)c.d_h * c.page_rows + (int64_t)(slot / kVTile) * c.d_h * kVTile +
+         slot % kVTile;
 }
 
 }  // namespace dflash

@@ -149,7 +149,9 @@ struct AttnArgs {
   float* part_o;         // [items][qrows][d_h]
   float* part_ml;        // [items][2][qrows]
   int32_t R, B, n_kv, group, qrows, d_h;
-  int32_t chunk_keys;    // keys per work item (multiple of 32)
+  int32_t chunk_keys;    // keys per work item (multiple of 64)
+  int32_t rot;           // block order rotation multiplier (0: in order)
+  int32_t nst;           // ring stages of the bf16 64-key-block kernel (2..4; 0: by item count)
   int32_t window;
   float scale_log2;      // d_h^-0.5 * log2(e)
   int32_t item_base[kMaxSeqs + 1];  // items of sequence r: [item_base[r], item_base[r+1])

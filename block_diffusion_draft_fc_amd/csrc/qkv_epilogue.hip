@@ -104,8 +104,8 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvEpiArgs a) {
       dst[lane + half] = from_f32<T>(x1);
     } else {
       T* dst = static_cast<T*>(a.cache.v_pool) + v_offset(a.cache, page, head, slot);
-      dst[(int64_t)lane * a.cache.page_rows] = from_f32<T>(x0);
-      dst[(int64_t)(lane + half) * a.cache.page_rows] = from_f32<T>(x1);
+      dst[lane * kVTile] = from_f32<T>(x0);
+      dst[(lane + half) * kVTile] = from_f32<T>(x1);
     }
   }
 }

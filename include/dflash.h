@@ -94,10 +94,13 @@ typedef struct dflash_layer_desc {
  *
  * contiguous (page_size == 0): capacity = rows per sequence (multiple of 64)
  *     K pool [n_seqs][n_kv][capacity][d_h]
- *     V pool [n_seqs][n_kv][d_h][capacity]     (V stored key-minor)
+ *     V pool [n_seqs][n_kv][capacity / 64][d_h][64]
  * paged (page_size > 0, multiple of 64): capacity = pages in the pool
  *     K pool [capacity][n_kv][page_size][d_h]
- *     V pool [capacity][n_kv][d_h][page_size]
+ *     V pool [capacity][n_kv][page_size / 64][d_h][64]
+ * V is stored transposed in tiles of 64 slots: head dim i of slot j sits in
+ * tile j / 64, row i, column j % 64, so the 64 keys of an attention block are
+ * one contiguous run whatever the capacity or page size.
  *     block_table [n_seqs][max_pages_per_seq] int32, device; entry (s, j) is the
  *     physical page of logical page j of sequence s, valid for
  *     j < ceil(len_s / page_size) (other entries are left as they were).

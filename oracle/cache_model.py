@@ -17,10 +17,14 @@ and copy-on-write are not modelled (no request shares pages here).
 Pool layout (as declared in the library header):
   contiguous (page_size == 0), capacity = rows per sequence:
       K pool [n_seqs][n_kv][capacity][d_h]
-      V pool [n_seqs][n_kv][d_h][capacity]          (V stored key-minor)
+      V pool [n_seqs][n_kv][capacity / 64][d_h][64]
   paged (page_size > 0), capacity = pages in the pool:
       K pool [capacity][n_kv][page_size][d_h]
-      V pool [capacity][n_kv][d_h][page_size]
+      V pool [capacity][n_kv][page_size / 64][d_h][64]
+  V is stored transposed in tiles of 64 slots: slot j's head dim i sits in
+  tile j // 64, row i, column j % 64.  (The library takes capacities and page
+  sizes in multiples of 64; for the small sizes of the logic tests the model
+  pads its last tile.)
   Row `pos` of sequence s lives in logical page pos // page_size, slot
   pos % page_size.  Allocation takes the lowest-numbered free page; sequences
   are served in index order and each sequence's new logical pages in order.
@@ -41,6 +45,7 @@ from __future__ import annotations
 import numpy as np
 
 OK, ERR_ARG, ERR_SHAPE, ERR_DTYPE, ERR_RANGE, ERR_CAPACITY = 0, -1, -2, -3, -4, -5
+V_TILE = 64   # slots per transposed V tile
 
 
 class CacheError(Exception):
@@ -63,12 +68,12 @@ class CacheModel:
         self.hw = [0] * self.n_seqs
         if self.paged:
             self.K = np.zeros((capacity, n_kv, page_size, d_h), dtype=word)
-            self.V = np.zeros((capacity, n_kv, d_h, page_size), dtype=word)
+            self.V = np.zeros((capacity, n_kv, -(-page_size // V_TILE), d_h, V_TILE), dtype=word)
             self.pages = [[] for _ in range(self.n_seqs)]
             self.free = set(range(self.capacity))
         else:
             self.K = np.zeros((n_seqs, n_kv, capacity, d_h), dtype=word)
-            self.V = np.zeros((n_seqs, n_kv, d_h, capacity), dtype=word)
+            self.V = np.zeros((n_seqs, n_kv, -(-capacity // V_TILE), d_h, V_TILE), dtype=word)
 
     @property
     def paged(self) -> bool:
@@ -112,11 +117,11 @@ class CacheModel:
                 if self.paged:
                     pg, slot = self.pages[s][pos // self.page_size], pos % self.page_size
                     self.K[pg, :, slot, :] = krow
-                    self.V[pg, :, :, slot] = vrow
+                    self.V[pg, :, slot // V_TILE, :, slot % V_TILE] = vrow
                 else:
                     slot = pos % self.capacity
                     self.K[s, :, slot, :] = krow
-                    self.V[s, :, :, slot] = vrow
+                    self.V[s, :, slot // V_TILE, :, slot % V_TILE] = vrow
             self.len[s] += n[s]
             self.hw[s] = max(self.hw[s], self.len[s])
 
@@ -160,7 +165,7 @@ class CacheModel:
         for pos in range(lo, L):
             slot = pos % self.capacity
             K[:, pos - lo, :] = self.K[s, :, slot, :]
-            V[:, pos - lo, :] = self.V[s, :, :, slot]
+            V[:, pos - lo, :] = self.V[s, :, slot // V_TILE, :, slot % V_TILE]
         return lo, K, V
 
     def block_table(self):
@@ -181,8 +186,8 @@ class CacheModel:
             if self.paged:
                 pg, slot = self.pages[s][pos // self.page_size], pos % self.page_size
                 K[:, pos, :] = self.K[pg, :, slot, :]
-                V[:, pos, :] = self.V[pg, :, :, slot]
+                V[:, pos, :] = self.V[pg, :, slot // V_TILE, :, slot % V_TILE]
             else:
                 K[:, pos, :] = self.K[s, :, pos, :]
-                V[:, pos, :] = self.V[s, :, :, pos]
+                V[:, pos, :] = self.V[s, :, pos // V_TILE, :, pos % V_TILE]
         return K, V

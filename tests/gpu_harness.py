@@ -116,6 +116,17 @@ def oracle_stack(wl, kv_host):
     return O.OracleStack(layers, fc["w_fc"].astype(np.float64), fc["gamma_h"], wl.eps, K0, V0)
 
 
+def v_rows_view(vp):
+    """V pool tiles [..., n_kv, tiles, d_h, 64] (slot j's head dim i in tile
+    j // 64, row i, column j % 64) as rows [n_kv, tiles * 64, d_h] (any leading
+    dims are folded into the row axis after n_kv)."""
+    if vp.dim() == 4:
+        g, t, d, w = vp.shape
+        return vp.permute(0, 1, 3, 2).reshape(g, t * w, d)
+    g, p, t, d, w = vp.shape
+    return vp.permute(0, 1, 2, 4, 3).reshape(g, p * t * w, d)
+
+
 def ring_rows(cache: L.Cache, s: int, lo: int):
     """Rows of positions lo .. len-1 of sequence s of a ring cache (slot
     pos % capacity) read back as float64: K, V [n_kv, len - lo, d_h]."""
@@ -123,7 +134,7 @@ def ring_rows(cache: L.Cache, s: int, lo: int):
     slots = torch.tensor([p % cache.capacity for p in range(lo, n)], dtype=torch.long,
                          device=cache.k_pool.device)
     K = cache.k_pool[s][:, slots, :]
-    V = cache.v_pool[s][:, :, slots].transpose(1, 2)
+    V = v_rows_view(cache.v_pool[s])[:, slots, :]
     return from_device(K.contiguous()), from_device(V.contiguous())
 
 
@@ -134,11 +145,11 @@ def cache_rows(cache: L.Cache, s: int):
     n = cache.lengths()[s]
     if cache.page_size == 0:
         K = cache.k_pool[s, :, :n, :]
-        V = cache.v_pool[s, :, :, :n].transpose(1, 2)
+        V = v_rows_view(cache.v_pool[s])[:, :n, :]
     else:
         ps = cache.page_size
         pages = cache.block_table()[s][: -(-n // ps)]
         idx = torch.tensor(pages, dtype=torch.long, device=cache.k_pool.device)
         K = cache.k_pool[idx].permute(1, 0, 2, 3).reshape(cache.n_kv, -1, cache.d_h)[:, :n]
-        V = cache.v_pool[idx].permute(1, 0, 3, 2).reshape(cache.n_kv, -1, cache.d_h)[:, :n]
+        V = v_rows_view(cache.v_pool[idx].transpose(0, 1))[:, :n]
     return from_device(K.contiguous()), from_device(V.contiguous())
