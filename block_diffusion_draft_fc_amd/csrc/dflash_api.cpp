@@ -188,11 +188,30 @@ struct SkinnyPlan {
   bool stream;       // gemm_stream_kernel (per-wave weight streams) for at most 32 rows
   bool fullk;        // gemm_fullk_kernel (no split-K partials) for at most 16 rows
   bool resident;     // gemm_resident_kernel: at most 16 rows kept in LDS, very many columns
+  bool slab;         // gemm_slab_kernel: bf16, up to 128 rows, slice staged in up to 160 KB of LDS
   int32_t m_tiles;   // tile plans only
 };
 
 
-// Plans for at most 64 rows (32 for fp32), tuned on the decode-round shapes:
+// Whether a product may take gemm_slab_kernel: bf16 and K a multiple of 512
+// (DFLASH_GEMM_SLAB=0 turns it off).
+bool slab_eligible(int64_t K, size_t eb) {
+  static const int use_slab = env_int("DFLASH_GEMM_SLAB", 1, 0, 1);
+  return use_slab && eb == 2 && K % 512 == 0;
+}
+
+// Rows per weight-streaming problem: 128 for slab-eligible products (the
+// kernel's row limit; DFLASH_GEMM_SLAB_ROWS lowers it), else 64 for bf16 and
+// 32 for fp32, whose staged activation rows take twice the LDS (this keeps
+// every gemm_lds_kernel plan within its 64 KB dynamic LDS budget).
+int64_t rows_per_problem(int64_t K, size_t eb) {
+  static const int slab_rows = env_int("DFLASH_GEMM_SLAB_ROWS", 128, 64, 128) / 16 * 16;
+  if (slab_eligible(K, eb)) return slab_rows;
+  return eb == 2 ? kSkinnyMaxM : kSkinnyMaxM / 2;
+}
+
+// Plans for at most 128 rows (64 or 32 without the slab kernel), tuned on the
+// decode-round shapes:
 //  * long inputs (K >= 8192, bf16, <= 32 rows): gemm_wide_kernel, 256-column
 //    tiles, about 256 workgroups with chunks of whole 128-wide stages;
 //  * otherwise gemm_lds_kernel, 64-column tiles, about 1024 workgroups with
@@ -230,6 +249,21 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, size_t eb) {
     p.n_tiles = (int32_t)cdiv(N, 16 * gemm_stream_waves(p.mt));
     p.k_chunk = 512;
     p.splits = (int32_t)cdiv(K, 512);
+    return p;
+  }
+  // 33..128 rows (bf16, K a multiple of 512): the slice staged by direct
+  // copies in up to 160 KB of LDS, which allows 1024-wide chunks at 64 rows
+  // and 512-wide at 128; splits to about one workgroup per CU
+  if (slab_eligible(K, eb) && p.mt > 2 && p.mt <= 8) {
+    static const int slab_target = env_int("DFLASH_GEMM_SLAB_BLOCKS", 256, 1, 1 << 16);
+    p.slab = true;
+    p.n_tiles = (int32_t)cdiv(N, 64);
+    const int64_t kmax = std::max<int64_t>(512, ((int64_t)kSlabLdsBytes / (p.mt * 16 * 2) - 8) / 512 * 512);
+    int64_t splits = std::max<int64_t>(cdiv(K, kmax), cdiv(slab_target, p.n_tiles));
+    splits = std::min<int64_t>(splits, K / 512);
+    const int64_t kc = cdiv(cdiv(K, splits), 512) * 512;
+    p.k_chunk = (int32_t)kc;
+    p.splits = (int32_t)cdiv(K, kc);
     return p;
   }
   p.wide = eb == 2 && p.mt <= 2 && K >= wide_min_k;
@@ -293,16 +327,13 @@ SkinnyPlan plan_tile(int64_t M, int64_t N, int64_t K) {
 // Depends on shapes only, so that a workspace sized from the plan fits the
 // plan the call makes.
 bool tile_eligible(int64_t M, int64_t N, int64_t K, size_t eb) {
-  static const int min_rows = env_int("DFLASH_GEMM_TILE_MIN_ROWS", kSkinnyMaxM + 1, 1, 1 << 30);
-  return eb == 2 && M >= min_rows && K % 64 == 0 && N % 4 == 0;
+  static const int min_rows = env_int("DFLASH_GEMM_TILE_MIN_ROWS", 0, 0, 1 << 30);
+  const int64_t lo = min_rows > 0 ? min_rows : rows_per_problem(K, eb) + 1;
+  return eb == 2 && M >= lo && K % 64 == 0 && N % 4 == 0;
 }
 
 size_t lds_bytes(const GemmProb& p, size_t eb) { return (size_t)p.mt * 16 * (size_t)(p.k_chunk + 8) * eb; }
 
-// Rows per weight-streaming problem: 64 for bf16; 32 for fp32, whose staged
-// activation rows take twice the LDS (this keeps every plan within the 64 KB
-// dynamic LDS budget).
-int64_t rows_per_problem(size_t eb) { return eb == 2 ? kSkinnyMaxM : kSkinnyMaxM / 2; }
 
 // A product of the (virtual) row concatenation [x0 (m0 rows); x1 (m1 rows)] with
 // W^T, written as fp32 split-K partials [splits][M][N].  Rows are processed in
@@ -328,7 +359,7 @@ GemmJob make_job(const void* x0, int64_t m0, const void* x1, int64_t m1, const v
   if (tile_eligible(m0 + m1, N, K, eb))
     j.plan = plan_tile(m0 + m1, N, K);
   else
-    j.plan = plan_skinny(std::min<int64_t>(m0 + m1, rows_per_problem(eb)), N, K, eb);
+    j.plan = plan_skinny(std::min<int64_t>(m0 + m1, rows_per_problem(K, eb)), N, K, eb);
   j.part = nullptr;
   return j;
 }
@@ -339,7 +370,7 @@ size_t job_part_bytes(const GemmJob& j) {
 
 void job_problems(const GemmJob& j, size_t eb, std::vector<GemmProb>* out) {
   const int64_t M = j.m0 + j.m1;
-  const int64_t step = rows_per_problem(eb);
+  const int64_t step = rows_per_problem(j.K, eb);
   for (int64_t a = 0; a < M; a += step) {
     const int64_t e = std::min<int64_t>(a + step, M);
     GemmProb p{};
@@ -366,7 +397,7 @@ void job_problems(const GemmJob& j, size_t eb, std::vector<GemmProb>* out) {
 
 hipError_t run_gemms(int32_t dt, const std::vector<GemmJob>& jobs, hipStream_t s) {
   const size_t eb = elem_bytes(dt);
-  std::vector<GemmProb> probs;
+  std::vector<GemmProb> probs, slab_probs;
   for (const auto& j : jobs) {
     if (j.m0 + j.m1 == 0) continue;
     if (j.plan.tile) {
@@ -444,9 +475,26 @@ hipError_t run_gemms(int32_t dt, const std::vector<GemmJob>& jobs, hipStream_t s
         hipError_t e = launch_gemm_wide(p, s);
         if (e != hipSuccess) return e;
       }
+    } else if (j.plan.slab) {
+      job_problems(j, eb, &slab_probs);
     } else {
       job_problems(j, eb, &probs);
     }
+  }
+  // gemm_slab_kernel problems, two per launch when their row tiles agree
+  for (size_t i = 0; i < slab_probs.size();) {
+    GemmArgs a{};
+    a.p[0] = slab_probs[i];
+    a.nprob = 1;
+    size_t lds = lds_bytes(slab_probs[i], eb);
+    if (i + 1 < slab_probs.size() && slab_probs[i + 1].mt == slab_probs[i].mt) {
+      a.p[1] = slab_probs[i + 1];
+      a.nprob = 2;
+      lds = std::max(lds, lds_bytes(slab_probs[i + 1], eb));
+    }
+    i += a.nprob;
+    hipError_t e = launch_gemm_slab(a, lds, s);
+    if (e != hipSuccess) return e;
   }
   // gemm_lds_kernel problems, two per launch
   for (size_t i = 0; i < probs.size(); i += 2) {
@@ -596,7 +644,11 @@ KvPlan plan_kv(const dflash_layer_desc* L, const dflash_cache* c, int64_t T, int
   p.kvd = (int64_t)L->n_kv * L->d_h;
   p.group = L->n_h / L->n_kv;
   p.qrows = cdiv(p.group * B, 16) * 16;
-  p.fused_qkv = T + p.RB <= rows_per_problem(eb);
+  // one [C; H] product with all of w_qkv up to 64 rows (the Q columns of the
+  // context rows cost nothing next to streaming the weights once); beyond,
+  // Q of the block rows and K/V of all rows separately (the fused product's
+  // split-K partials would be 1.5x the two separate ones')
+  p.fused_qkv = T + p.RB <= std::min<int64_t>(kSkinnyMaxM, rows_per_problem(L->d, eb));
   if (p.fused_qkv) {
     p.gkv = make_job(nullptr, T, nullptr, p.RB, L->w_qkv, p.qd + 2 * p.kvd, L->d, eb);
     p.gq = p.gkv;

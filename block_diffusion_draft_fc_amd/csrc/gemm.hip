@@ -138,6 +138,135 @@ hipError_t launch_gemm_lds(int dtype, const GemmArgs& a, int max_mt, size_t lds,
   return dtype == 1 ? launch_lds_t<bf16>(a, max_mt, lds, s) : launch_lds_t<float>(a, max_mt, lds, s);
 }
 
+// ---------------------------------------------------------------- slab (bf16, up to 128 rows)
+// gemm_lds_kernel's scheme with the activation slice [rows][k_chunk] staged
+// by direct-to-LDS copies (1 KB of one row each, all issued before the first
+// weight loads and waited for once) into up to 160 KB of LDS: a 64-row
+// problem over a 4096-wide input takes four 1024-wide splits instead of
+// sixteen 256-wide ones, a 128-row problem eight 512-wide ones, which cuts the
+// fp32 partial traffic written here and read by the consumer 2-4 times.
+// LDS row stride k_chunk + 8 elements: the 16-byte pad moves the 16 rows of an
+// operand read onto different banks.
+// Requirements (checked by the planner): bf16, K and k_chunk multiples of 512,
+// exactly MT 16-row tiles (the problems of one launch share MT), and
+// MT * 16 * (k_chunk + 8) * 2 bytes within kSlabLdsBytes.
+template <int MT>
+__global__ __launch_bounds__(256) void gemm_slab_kernel(GemmArgs args) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  const bf16* xs = reinterpret_cast<const bf16*>(smem_raw);
+
+  int b = blockIdx.x;
+  int pi = 0;
+  if (args.nprob > 1 && b >= args.p[0].blocks) {
+    b -= args.p[0].blocks;
+    pi = 1;
+  }
+  const GemmProb p = args.p[pi];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_tile = b % p.n_tiles, split = b / p.n_tiles;
+  const int k_begin = split * p.k_chunk;
+  const int klen = min(p.K, k_begin + p.k_chunk) - k_begin;   // a multiple of 512
+  const int M = p.m0 + p.m1;
+  const int ld = klen + 8;
+  const bf16* x0 = static_cast<const bf16*>(p.x0);
+  const bf16* x1 = static_cast<const bf16*>(p.x1);
+
+  // copy i: row i / segs, elements 512 (i % segs) .. + 511 of the chunk; rows
+  // past M read row 0 (their results are never stored)
+  const int segs = klen >> 9;
+  const int ncopies = MT * 16 * segs;
+  for (int i = wave; i < ncopies; i += 4) {
+    const int r = i / segs, seg = i - r * segs;
+    const int m = r < M ? r : 0;
+    const bf16* src = (m < p.m0 ? x0 + (int64_t)m * p.K : x1 + (int64_t)(m - p.m0) * p.K) + k_begin + 512 * seg + 8 * lane;
+    lds_copy16(src, smem_raw + 2 * (r * ld + 512 * seg));
+  }
+
+  // columns past N stream row 0 (finite values, never stored)
+  const int n = n_tile * 64 + wave * 16 + (lane & 15);
+  const int q8 = (lane >> 4) * 8;
+  const bool nvalid = n < p.N;
+  const bf16* wrow = static_cast<const bf16*>(p.w) + (int64_t)(nvalid ? n : 0) * p.K + k_begin + q8;
+  const bf16* xrow = xs + (lane & 15) * ld + q8;
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 wa[8], wb[8];
+  auto fetch = [&](bf16x8* dst, int kk) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dst[j] = load8(wrow + kk + 32 * j);
+    // keep the loads here: otherwise the compiler sinks them below the
+    // MFMAs of the other buffer, and only one buffer is ever in flight
+    asm volatile("" ::: "memory");
+  };
+  auto compute = [&](const bf16x8* wv, int kk) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[t] = mma32(load8(xrow + t * 16 * ld + kk + 32 * j), wv[j], acc[t]);
+  };
+
+  fetch(wa, 0);
+  // the copies went out before these eight weight loads: this wave's have
+  // landed when at most eight loads remain; after the barrier, every wave's
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  asm volatile("s_barrier" ::: "memory");
+  for (int kk = 0; kk < klen; kk += 512) {
+    fetch(wb, kk + 256);
+    compute(wa, kk);
+    // unconditional (the last step re-reads its own K-values, an L2 hit): a
+    // branch here makes the compiler wait for these loads inside compute(wb)
+    fetch(wa, kk + 512 < klen ? kk + 512 : kk);
+    compute(wb, kk + 256);
+  }
+
+  if (nvalid) {
+    float* out = p.part + ((int64_t)split * p.m_out + p.row_off) * p.N + n;
+    const int m_lane = (lane >> 4) * 4;
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = t * 16 + m_lane + e;
+        if (m < M) out[(int64_t)m * p.N] = acc[t][e];
+      }
+  }
+}
+
+template <int MT>
+static hipError_t launch_slab_t(const GemmArgs& a, int blocks, size_t lds, hipStream_t s) {
+  // dynamic LDS above the default limit, allowed once per kernel
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_slab_kernel<MT>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kSlabLdsBytes);
+  if (attr != hipSuccess) return attr;
+  launch((gemm_slab_kernel<MT>), dim3(blocks), dim3(256), (uint32_t)lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_slab(const GemmArgs& a, size_t lds, hipStream_t s) {
+  const int blocks = a.p[0].blocks + (a.nprob > 1 ? a.p[1].blocks : 0);
+  if (blocks == 0) return hipSuccess;
+  const int mt = a.p[0].mt;
+  if (lds > (size_t)kSlabLdsBytes) return hipErrorInvalidValue;
+  for (int i = 0; i < a.nprob; ++i) {
+    const GemmProb& p = a.p[i];
+    if (p.mt != mt || p.K % 512 != 0 || p.k_chunk % 512 != 0 || p.m0 + p.m1 > 16 * mt ||
+        (size_t)mt * 16 * (p.k_chunk + 8) * 2 > lds)
+      return hipErrorInvalidValue;
+  }
+  switch (mt) {
+    case 3: return launch_slab_t<3>(a, blocks, lds, s);
+    case 4: return launch_slab_t<4>(a, blocks, lds, s);
+    case 5: return launch_slab_t<5>(a, blocks, lds, s);
+    case 6: return launch_slab_t<6>(a, blocks, lds, s);
+    case 7: return launch_slab_t<7>(a, blocks, lds, s);
+    case 8: return launch_slab_t<8>(a, blocks, lds, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 // ---------------------------------------------------------------- wide (bf16)
 // Workgroup tile: 256 output columns (wave w: columns 64w .. 64w+63 of the tile,
 // as four 16-column MFMA tiles) x one K-chunk.  A stage is 4 K-steps of 32;

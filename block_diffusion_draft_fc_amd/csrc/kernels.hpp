@@ -100,6 +100,11 @@ hipError_t launch_gemm_resident(const FullkArgs& p, hipStream_t s);
 // LDS budget for the staged activation slice of one gemm_lds_kernel workgroup.
 constexpr int kLdsGemmBytes = 64 * 1024;
 hipError_t launch_gemm_lds(int dtype, const GemmArgs& a, int max_mt, size_t lds_bytes, hipStream_t s);
+// bf16, 33..128 rows (mt of 3 to 8, the same for both problems), K and
+// k_chunk multiples of 512: the activation slice staged by direct copies in
+// lds_bytes (at most kSlabLdsBytes) of LDS.
+constexpr int kSlabLdsBytes = 160 * 1024;
+hipError_t launch_gemm_slab(const GemmArgs& a, size_t lds_bytes, hipStream_t s);
 // bf16 only, at most 32 rows (mt <= 2); 256-column tiles (n_tiles = ceil(N/256)).
 hipError_t launch_gemm_wide(const GemmProb& p, hipStream_t s);
 

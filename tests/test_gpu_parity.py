@@ -125,9 +125,11 @@ def test_ctx_project_bf16(T):
 # Shapes that take the 256x256 MFMA tile GEMM (bf16, at least 256 rows, K a
 # multiple of 64): a last row tile holding one row, last column tiles of 64 and
 # 8 columns, a K of 2080 (a multiple of 32 only) and (last case) 3000, which
-# take the weight-streaming kernels instead.
+# take the weight-streaming kernels instead.  Then 33..128 rows with K a
+# multiple of 512 (the LDS-slab GEMM): three and seven row tiles, last column
+# tiles of 40 and 8 columns, 1536- and 512-wide chunks.
 @pytest.mark.parametrize("T,d,k_layers", [(257, 1088, 2), (600, 520, 8), (512, 1024, 3), (400, 1040, 2),
-                                          (300, 1000, 3)])
+                                          (300, 1000, 3), (40, 1000, 64), (100, 520, 64), (128, 512, 3)])
 def test_ctx_project_bf16_many_rows(T, d, k_layers):
     wl = configs.FRESH_CTX.scaled(name=f"ctx_project_T{T}_d{d}_k{k_layers}", d=d, k_layers=k_layers, n_h=8,
                                   n_kv=2, d_h=64)
@@ -231,6 +233,13 @@ SMALL = [
            sliding_layers=(0,), ring=True, n_range=(0, 9), rounds=5),
     _small("ring_stack3_residual", n_layers=3, d_h=128, B=16, R=2, prefill_len=600, window=256,
            sliding_layers=(0, 2), ring=True, rounds=3),
+    # 33..128-row products with K a multiple of 512 (the LDS-slab GEMM): block
+    # rows of 4 and 6 requests, [C; H] rows up to 128, C/H boundaries inside a
+    # problem, one to three 512-wide segments per chunk
+    _small("slab_gemm_r4_d512", d=512, n_h=8, n_kv=2, d_h=64, B=16, R=4, n_range=(1, 16), rounds=2),
+    _small("slab_gemm_r6_d1024_b8", d=1024, n_h=8, n_kv=2, d_h=128, B=8, R=6, n_range=(4, 16), rounds=2),
+    _small("slab_gemm_r3_d1536_b16", d=1536, n_h=12, n_kv=4, d_h=128, B=16, R=3, n_range=(8, 16), rounds=2,
+           k_layers=1),
     # many new context rows: the context projection and the K/V projection of
     # [C; H] take the MFMA tile GEMM, with the C/H boundary inside a row tile
     _small("fresh_ctx300_tile_gemm", d=512, k_layers=2, B=16, prefill="none", n_new="fixed", n_fixed=300,
