@@ -53,7 +53,8 @@ def parse():
     ap.add_argument("--no-fresh-ctx", action="store_true",
                     help="skip the MFMA-utilisation pass over the fresh 1024-row context projections")
     ap.add_argument("--no-batched", action="store_true",
-                    help="skip the draft head, the ragged 16-request and the 5-layer hybrid stack rounds")
+                    help="skip the attention-at-scale pass, the draft head, the ragged 16-request and the 5-layer "
+                         "hybrid stack rounds")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 8 times (scales HBM counters)")
     return ap.parse_args()
@@ -320,6 +321,69 @@ def batched_rounds(wl, rounds, ring=False):
     return res
 
 
+# ---------------------------------------------------------------------------- attention at scale
+
+def attn_at_scale(iters):
+    """The attention kernel on the full-attention layer shape of the 5-layer
+    stack: 4 requests x 32768 cached keys, 8 new context rows and a block of 16
+    each, Qwen3-8B heads (32/8, d_h 128), contiguous bf16 cache.  Every call
+    appends its rows, attends and is cropped back, so each reads the same
+    4 x 32792 keys per K/V head (537 MB).  The attention stage's time comes
+    from the library's HIP events on the launch stream; K/V rows are N(0,1)
+    drawn on the device."""
+    import torch
+
+    from block_diffusion_draft_fc_amd import _lib as L
+    from workloads import configs, generate as G
+    from workloads.device import to_device
+
+    wl = configs.STACK5_HYBRID
+    dev = "cuda:0"
+    R, ctx, n, B = wl.R, wl.prefill_len, 8, wl.B
+    li = next(i for i in range(wl.n_layers) if not wl.layer_window(i))
+    lw = G.layer_weights(wl, li)
+    layer = L.Layer(*(to_device(lw[k], wl, dev) for k in ("w_qkv", "w_o", "gamma_q", "gamma_k")),
+                    n_h=wl.n_h, n_kv=wl.n_kv, d_h=wl.d_h, eps=wl.eps, rope_theta=wl.rope_theta)
+    cap = (ctx + 1024 + 63) // 64 * 64
+    cache = L.Cache(R, wl.n_kv, wl.d_h, torch.bfloat16, cap, 0, 0, dev)
+    g = torch.Generator(device=dev).manual_seed(wl.seed)
+    k = torch.randn((R * ctx, wl.n_kv, wl.d_h), device=dev, generator=g).to(torch.bfloat16)
+    v = torch.randn((R * ctx, wl.n_kv, wl.d_h), device=dev, generator=g).to(torch.bfloat16)
+    L.dflash_cache_append(cache, [r * ctx for r in range(R + 1)], k, v)
+    del k, v
+    C = torch.randn((R * n, wl.d), device=dev, generator=g).to(torch.bfloat16)
+    H = torch.randn((R * B, wl.d), device=dev, generator=g).to(torch.bfloat16)
+    out = torch.empty((R * B, wl.d), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(L.dflash_kv_inject_attn_ws_bytes(layer, cache, R * n, B), dtype=torch.uint8, device=dev)
+    cu = [r * n for r in range(R + 1)]
+
+    def call():
+        L.dflash_kv_inject_attn(layer, cache, C, cu, H, B, out, ws)
+        L.dflash_cache_crop(cache, [ctx] * R)
+
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    L.timing_reset()
+    L.timing_enable(True)
+    for _ in range(iters):
+        call()
+    torch.cuda.synchronize()
+    st = L.timing_read()
+    L.timing_enable(False)
+    keys = ctx + n + B
+    alg = R * keys * wl.n_kv * wl.d_h * 2 * 2 + R * B * wl.n_h * wl.d_h * 2
+    us = st["attn"][1] * 1e3 / st["attn"][0]
+    gbps = alg / (us * 1e-6) / 1e9
+    res = {"shape": f"{R} requests x {keys} keys, GQA {wl.n_h}/{wl.n_kv}, d_h {wl.d_h}, block {B}, bf16",
+           "launches": st["attn"][0], "us_per_launch": round(us, 2), "alg_bytes_per_launch": int(alg),
+           "gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+           "combine_us": round(st["attn_combine"][1] * 1e3 / st["attn_combine"][0], 2)}
+    del cache, layer, C, H, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 # ---------------------------------------------------------------------------- draft head
 
 def draft_head_pass(iters):
@@ -558,6 +622,8 @@ def main():
         log("bench: fresh-context projections")
         res["fresh_ctx_projections"] = fresh_ctx_projections(20)
     if not args.no_batched:
+        log("bench: attention kernel on the stack's full-attention layer shape")
+        res["attn_at_scale"] = attn_at_scale(30)
         log("bench: draft head (lm_head over the Qwen3 vocabulary)")
         res["draft_head"] = draft_head_pass(20)
         log("bench: ragged 16-request paged batch")

@@ -1108,19 +1108,16 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_kernel(AttnArgs a) {
     process(b);
   }
 
-  // partials as non-temporal stores: the combine reads them once, after
-  // this kernel, and the stores at the end of every item cost the stream less
   float* po = a.part_o + (int64_t)item * a.qrows * DH;
 #pragma unroll
-  for (int d = 0; d < DT; ++d)
-    __builtin_nontemporal_store(o[d], reinterpret_cast<f32x4*>(po + (int64_t)row * DH + 16 * d + 4 * q4));
+  for (int d = 0; d < DT; ++d) *reinterpret_cast<f32x4*>(po + (int64_t)row * DH + 16 * d + 4 * q4) = o[d];
   float l = l_run;
   l += __shfl_xor(l, 16, kWave);
   l += __shfl_xor(l, 32, kWave);
   if (q4 == 0) {
     float* pml = a.part_ml + (int64_t)item * 2 * a.qrows;
-    __builtin_nontemporal_store(m_run, pml + row);
-    __builtin_nontemporal_store(l, pml + a.qrows + row);
+    pml[row] = m_run;
+    pml[a.qrows + row] = l;
   }
 }
 

@@ -200,13 +200,17 @@ bool slab_eligible(int64_t K, size_t eb) {
   return use_slab && eb == 2 && K % 512 == 0;
 }
 
-// Rows per weight-streaming problem: 128 for slab-eligible products (the
-// kernel's row limit; DFLASH_GEMM_SLAB_ROWS lowers it), else 64 for bf16 and
-// 32 for fp32, whose staged activation rows take twice the LDS (this keeps
-// every gemm_lds_kernel plan within its 64 KB dynamic LDS budget).
+// Rows per weight-streaming problem: 128 for slab-eligible products with K
+// up to 8192 (the kernel's row limit; DFLASH_GEMM_SLAB_ROWS lowers it), else
+// 64 for bf16 and 32 for fp32, whose staged activation rows take twice the
+// LDS (this keeps every gemm_lds_kernel plan within its 64 KB dynamic LDS
+// budget).  Above 64 rows the slab kernel's chunk is 512 wide, so its fp32
+// partials weigh half the weights: fine for a 4096-wide input (the 5-layer
+// stack's K/V product beats the tile kernel), not for the 20480-wide fc,
+// where the tile kernel takes 65+ rows (ragged batch fc: 64 -> 47 us).
 int64_t rows_per_problem(int64_t K, size_t eb) {
   static const int slab_rows = env_int("DFLASH_GEMM_SLAB_ROWS", 128, 64, 128) / 16 * 16;
-  if (slab_eligible(K, eb)) return slab_rows;
+  if (slab_eligible(K, eb)) return K <= 8192 ? slab_rows : kSkinnyMaxM;
   return eb == 2 ? kSkinnyMaxM : kSkinnyMaxM / 2;
 }
 
@@ -254,7 +258,8 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, size_t eb) {
   // 33..128 rows (bf16, K a multiple of 512): the slice staged by direct
   // copies in up to 160 KB of LDS, which allows 1024-wide chunks at 64 rows
   // and 512-wide at 128; splits to about one workgroup per CU
-  if (slab_eligible(K, eb) && p.mt > 2 && p.mt <= 8) {
+  static const int slab_min_mt = env_int("DFLASH_GEMM_SLAB_MIN_MT", 3, 1, 8);
+  if (slab_eligible(K, eb) && p.mt >= slab_min_mt && p.mt <= 8) {
     static const int slab_target = env_int("DFLASH_GEMM_SLAB_BLOCKS", 256, 1, 1 << 16);
     p.slab = true;
     p.n_tiles = (int32_t)cdiv(N, 64);

@@ -257,6 +257,8 @@ hipError_t launch_gemm_slab(const GemmArgs& a, size_t lds, hipStream_t s) {
       return hipErrorInvalidValue;
   }
   switch (mt) {
+    case 1: return launch_slab_t<1>(a, blocks, lds, s);
+    case 2: return launch_slab_t<2>(a, blocks, lds, s);
     case 3: return launch_slab_t<3>(a, blocks, lds, s);
     case 4: return launch_slab_t<4>(a, blocks, lds, s);
     case 5: return launch_slab_t<5>(a, blocks, lds, s);

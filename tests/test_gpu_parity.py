@@ -125,9 +125,10 @@ def test_ctx_project_bf16(T):
 # Shapes that take the 256x256 MFMA tile GEMM (bf16, at least 256 rows, K a
 # multiple of 64): a last row tile holding one row, last column tiles of 64 and
 # 8 columns, a K of 2080 (a multiple of 32 only) and (last case) 3000, which
-# take the weight-streaming kernels instead.  Then 33..128 rows with K a
-# multiple of 512 (the LDS-slab GEMM): three and seven row tiles, last column
-# tiles of 40 and 8 columns, 1536- and 512-wide chunks.
+# take the weight-streaming kernels instead.  Then K a multiple of 512: 40 and
+# 128 rows take the LDS-slab GEMM (three and eight row tiles, a last column
+# tile of 40 columns, 1536- and 512-wide chunks); 100 rows over a 33280-wide
+# input take the tile kernel (above K = 8192 the slab kernel keeps to 64 rows).
 @pytest.mark.parametrize("T,d,k_layers", [(257, 1088, 2), (600, 520, 8), (512, 1024, 3), (400, 1040, 2),
                                           (300, 1000, 3), (40, 1000, 64), (100, 520, 64), (128, 512, 3)])
 def test_ctx_project_bf16_many_rows(T, d, k_layers):
