@@ -562,8 +562,9 @@ hipError_t launch_gemm_tile(const TileProb& p, hipStream_t s) {
 // two copies of 8 whole rows (whole cache lines), chunks XOR-swizzled so that
 // the MFMA fragment reads are conflict free - with no barrier in the loop.  The
 // workgroup's activation chunk (at most 32 rows x 512) is staged once in LDS in
-// MFMA operand order.  Products are taken as W x^T, so each lane ends with four
-// consecutive columns of one row (16-byte partial stores).
+// MFMA operand order by direct copies issued together with the first weight
+// steps, so its latency overlaps theirs.  Products are taken as W x^T, so each
+// lane ends with four consecutive columns of one row (16-byte partial stores).
 // Requirements (checked by the planner): bf16, K a multiple of 64, N of 4.
 constexpr int kStreamKC = 512;   // K-chunk per workgroup
 
@@ -581,21 +582,17 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_stream_kernel(TileProb p) {
   const int n0 = nt * (16 * WAVES) + 16 * wave;               // this wave's 16 weight rows
   const int M = p.m0 + p.m1;
 
-  // activation chunk in operand order: slab (mt, s), lane l: row 16 mt + l % 16,
-  // k 32 s + 8 (l / 16) .. +7 (rows past M as zeros)
+  // activation chunk in operand order, one direct copy per slab (mt, s): lane
+  // l brings row 16 mt + l % 16, k 32 s + 8 (l / 16) .. +7.  Rows past M read
+  // row 0: their products are never stored.
   const int slabs = MT * (kc / 32);
-  for (int i = threadIdx.x; i < slabs * 64; i += 64 * WAVES) {
-    const int slab = i >> 6, l = i & 63;
+  for (int slab = wave; slab < slabs; slab += WAVES) {
     const int mt = slab / (kc / 32), s = slab - mt * (kc / 32);
-    const int m = 16 * mt + (l & 15);
-    bf16x8 v = {};
-    if (m < M) {
-      const bf16* row = m < p.m0 ? p.x0 + (int64_t)m * p.K : p.x1 + (int64_t)(m - p.m0) * p.K;
-      v = *reinterpret_cast<const bf16x8*>(row + k0 + 32 * s + 8 * (l >> 4));
-    }
-    *reinterpret_cast<bf16x8*>(sx + (mt * XS + s) * 1024 + 16 * l) = v;
+    int m = 16 * mt + (lane & 15);
+    m = m < M ? m : 0;
+    const bf16* row = m < p.m0 ? p.x0 + (int64_t)m * p.K : p.x1 + (int64_t)(m - p.m0) * p.K;
+    lds_copy16(row + k0 + 32 * s + 8 * (lane >> 4), sx + (mt * XS + s) * 1024);
   }
-  __syncthreads();
 
   // copies of step t into stage t % NST: copy j (0, 1) moves rows 8 j .. 8 j + 7
   // of the wave's 16; lane l fills row 8 j + l / 8, slot l % 8, with chunk
@@ -624,6 +621,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_stream_kernel(TileProb p) {
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   constexpr int AHEAD = NST - 1;   // steps in flight
   for (int t = 0; t < min(AHEAD, nsteps); ++t) issue(t);
+  // the activation copies went out before the weight steps: once step 0 has
+  // landed, so have this wave's; after the barrier, every wave's
+  wait_vm_blocks<2>(min(nsteps - 1, AHEAD - 1));
+  asm volatile("s_barrier" ::: "memory");
   for (int t = 0; t < nsteps; ++t) {
     // this wave's copies of step t have landed when at most those of the
     // later steps already issued remain (two copies per step)
@@ -654,8 +655,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_stream_kernel(TileProb p) {
 }
 
 // Configurations (measured): one 16-row tile: 8 waves, 4 stages; two tiles:
-// 16 waves, 3 stages.  p.n_tiles must be ceil(N / (16 * waves)).
-int gemm_stream_waves(int mt) { return mt <= 1 ? 8 : 16; }
+// 16 waves, 3 stages (DFLASH_GEMM_STREAM_WAVES=12 takes 12).  p.n_tiles must
+// be ceil(N / (16 * waves)).
+int gemm_stream_waves(int mt) {
+  static const int w2 = [] {
+    const char* e = std::getenv("DFLASH_GEMM_STREAM_WAVES");
+    const int v = e ? std::atoi(e) : 16;
+    return v == 12 || v == 8 ? v : 16;
+  }();
+  return mt <= 1 ? 8 : w2;
+}
 
 hipError_t launch_gemm_stream(const TileProb& p, int mt, hipStream_t s) {
   const int blocks = p.n_tiles * p.splits;
@@ -663,6 +672,10 @@ hipError_t launch_gemm_stream(const TileProb& p, int mt, hipStream_t s) {
   if (p.k_chunk != kStreamKC || mt < 1 || mt > 2) return hipErrorInvalidValue;
   if (mt == 1)
     launch((gemm_stream_kernel<1, 8, 4>), dim3(blocks), dim3(64 * 8), 0, s, p);
+  else if (gemm_stream_waves(2) == 12)
+    launch((gemm_stream_kernel<2, 12, 3>), dim3(blocks), dim3(64 * 12), 0, s, p);
+  else if (gemm_stream_waves(2) == 8)
+    launch((gemm_stream_kernel<2, 8, 4>), dim3(blocks), dim3(64 * 8), 0, s, p);
   else
     launch((gemm_stream_kernel<2, 16, 3>), dim3(blocks), dim3(64 * 16), 0, s, p);
   return hipGetLastError();
