@@ -190,6 +190,7 @@ struct SkinnyPlan {
   bool resident;     // gemm_resident_kernel: at most 16 rows kept in LDS, very many columns
   bool slab;         // gemm_slab_kernel: bf16, up to 128 rows, slice staged in up to 160 KB of LDS
   int32_t m_tiles;   // tile plans only
+  int32_t tile_bn;   // tile plans only: output columns per tile
 };
 
 
@@ -292,34 +293,45 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, size_t eb) {
   return p;
 }
 
-// Many rows (bf16): gemm_tile_kernel, 256x256 tiles, one workgroup per CU.
+// Many rows (bf16): gemm_tile_kernel, 256 x bn tiles, one workgroup per CU.
 // Splitting K fills more CUs but writes (and makes the consumer read) one fp32
-// partial product per split, so the split count minimises a two-term estimate:
-// MFMA time (tiles x splits workgroups in rounds of 256, each at a per-CU rate
-// of 60% of the bf16 peak) plus the partial traffic (8 bytes per output and
-// split at 5 TB/s).  Chunks are whole 64-wide K-steps.
+// partial product per split; narrower tiles fill more CUs without splits but
+// re-read the activation rows once per column tile and reuse each fragment
+// less.  The (bn, splits) pair minimises a three-term estimate: MFMA time
+// (workgroups in rounds of 256, each at a per-CU rate of 60% of the bf16 peak
+// for 256-wide tiles, 55% for 128, 45% for 64), the partial traffic (8 bytes
+// per output and split at 5 TB/s) and the activation re-reads (2 bytes per
+// row, K-value and column tile at 20 TB/s from L2).  Chunks are whole 64-wide
+// K-steps.  DFLASH_GEMM_TILE_BN and DFLASH_GEMM_TILE_SPLITS force either.
 SkinnyPlan plan_tile(int64_t M, int64_t N, int64_t K) {
   static const int forced = env_int("DFLASH_GEMM_TILE_SPLITS", 0, 0, 1 << 16);
+  static const int forced_bn = env_int("DFLASH_GEMM_TILE_BN", 0, 0, 256);
   SkinnyPlan p{};
   p.tile = true;
   p.m_tiles = (int32_t)cdiv(M, 256);
-  p.n_tiles = (int32_t)cdiv(N, 256);
-  const int64_t tiles = (int64_t)p.m_tiles * p.n_tiles;
   const int64_t max_splits = std::max<int64_t>(1, std::min<int64_t>(K / 64, 32));
-  int64_t best = 1;
-  if (forced > 0) {
-    best = std::min<int64_t>(forced, max_splits);
-  } else {
-    const double cu_flops = 2.5e15 / 256 * 0.6, bw = 5e12;
-    const double tile_flops = 2.0 * 256 * 256 * (double)K;
-    double best_t = 0;
+  const double peak_cu = 2.5e15 / 256, bw = 5e12, l2 = 20e12;
+  int best_bn = 256;
+  int64_t best_sp = 1;
+  double best_t = 0;
+  bool first = true;
+  for (int bn : {256, 128, 64}) {
+    if (forced_bn > 0 && bn != forced_bn) continue;
+    const double eff = bn == 256 ? 0.6 : bn == 128 ? 0.55 : 0.45;
+    const int64_t n_tiles = cdiv(N, bn);
+    const int64_t tiles = (int64_t)p.m_tiles * n_tiles;
+    const double tile_flops = 2.0 * 256 * bn * (double)K;
+    const double reread = (double)n_tiles * p.m_tiles * 256 * K * 2 / l2;
     for (int64_t sp = 1; sp <= max_splits; ++sp) {
+      if (forced > 0 && sp != std::min<int64_t>(forced, max_splits)) continue;
       const double rounds = (double)cdiv(tiles * sp, 256);
-      const double t = rounds * tile_flops / sp / cu_flops + (double)sp * M * N * 8 / bw;
-      if (sp == 1 || t < best_t) { best = sp; best_t = t; }
+      const double t = rounds * tile_flops / sp / (peak_cu * eff) + (double)sp * M * N * 8 / bw + reread;
+      if (first || t < best_t) { best_bn = bn; best_sp = sp; best_t = t; first = false; }
     }
   }
-  const int64_t kc = cdiv(cdiv(K, best), 64) * 64;
+  p.tile_bn = best_bn;
+  p.n_tiles = (int32_t)cdiv(N, best_bn);
+  const int64_t kc = cdiv(cdiv(K, best_sp), 64) * 64;
   p.k_chunk = (int32_t)kc;
   p.splits = (int32_t)cdiv(K, kc);
   return p;
@@ -419,7 +431,7 @@ hipError_t run_gemms(int32_t dt, const std::vector<GemmJob>& jobs, hipStream_t s
       t.splits = j.plan.splits;
       t.m_tiles = j.plan.m_tiles;
       t.n_tiles = j.plan.n_tiles;
-      hipError_t e = launch_gemm_tile(t, s);
+      hipError_t e = launch_gemm_tile(t, j.plan.tile_bn, s);
       if (e != hipSuccess) return e;
       continue;
     }

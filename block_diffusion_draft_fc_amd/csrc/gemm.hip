@@ -393,9 +393,12 @@ hipError_t launch_gemm_wide(const GemmProb& p, hipStream_t s) {
 
 // ---------------------------------------------------------------- tiled (bf16, many rows)
 // For the fresh-context projections (hundreds to thousands of rows), where the
-// product is MFMA-bound: a workgroup computes a 256x256 output tile over one
-// K-chunk with eight waves, each owning a 128x64 block, i.e. 8x4 tiles of
-// 16x16x32 MFMAs, 128 fp32 accumulators per lane (two waves per SIMD).
+// product is MFMA-bound: a workgroup computes a 256xBN output tile over one
+// K-chunk with eight waves.  BN = 256: each wave owns a 128x64 block, i.e. 8x4
+// tiles of 16x16x32 MFMAs, 128 fp32 accumulators per lane (two waves per
+// SIMD).  BN = 128 / 64 (a few hundred rows, where 256-wide tiles would need
+// many K-splits to fill the CUs, and their partials cost more than the
+// product): 64x64 / 32x64 blocks per wave.
 //
 // The K loop steps by 64 through two LDS stages of 64 KB; the copies of step
 // s + 1 are issued right after the barrier of step s and land while step s
@@ -419,17 +422,23 @@ hipError_t launch_gemm_wide(const GemmProb& p, hipStream_t s) {
 // 64, N a multiple of 4, 16-byte aligned rows.
 
 namespace {
-constexpr int kTileBM = 256, kTileBN = 256, kTileBK = 64;
+constexpr int kTileBM = 256, kTileBK = 64;
 constexpr int kTileWaves = 8;
-constexpr int kTileBlocks = kTileBM / 8;   // 1 KB blocks (8 rows x 128 B) of A (and of B) per stage
+constexpr int kTileBlocks = kTileBM / 8;   // 1 KB blocks (8 rows x 128 B) of A per stage
 constexpr int kTileGroupM = 4;
 constexpr int kXcds = 8;
 }
 
+template <int BN>
 __global__ __launch_bounds__(512, 1) void gemm_tile_kernel(TileProb p) {
+  constexpr int BBLOCKS = BN / 8;          // 1 KB blocks of B per stage
+  constexpr int WN = BN / 64;              // waves along N
+  constexpr int WM = kTileWaves / WN;      // waves along M
+  constexpr int RM = kTileBM / WM;         // rows per wave
+  constexpr int FM = RM / 16;              // 16-row fragments per wave
   // one array per stage and operand, so that each stage is named statically
-  __shared__ __align__(16) unsigned char sa0[kTileBlocks * 1024], sb0[kTileBlocks * 1024];
-  __shared__ __align__(16) unsigned char sa1[kTileBlocks * 1024], sb1[kTileBlocks * 1024];
+  __shared__ __align__(16) unsigned char sa0[kTileBlocks * 1024], sb0[BBLOCKS * 1024];
+  __shared__ __align__(16) unsigned char sa1[kTileBlocks * 1024], sb1[BBLOCKS * 1024];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -446,7 +455,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tile_kernel(TileProb p) {
   const int first_m = (t / band) * kTileGroupM;
   const int gsz = min(p.m_tiles - first_m, kTileGroupM);
   const int mt = first_m + (t % band) % gsz, nt = (t % band) / gsz;
-  const int m_base = mt * kTileBM, n_base = nt * kTileBN;
+  const int m_base = mt * kTileBM, n_base = nt * BN;
   const int k_begin = split * p.k_chunk;
   const int k_end = min(p.K, k_begin + p.k_chunk);
   const int nsteps = (k_end - k_begin) / kTileBK;   // >= 1: K and chunks are multiples of 64
@@ -456,10 +465,11 @@ __global__ __launch_bounds__(512, 1) void gemm_tile_kernel(TileProb p) {
   using S1 = std::integral_constant<int, 1>;
 
   // Copies of one K-step: block b of a stage holds tile rows 8 b .. 8 b + 7;
-  // wave w copies blocks w, w + 8, w + 16, w + 24 of A and of B.  Lane l
-  // fills row 8 b + l / 8, slot l % 8, with the chunk that the swizzle puts
-  // there.  Rows past M (columns past N) read row 0 and are never stored.
+  // wave w copies blocks w, w + 8, w + 16, w + 24 of A and w, w + 8, .. of B.
+  // Lane l fills row 8 b + l / 8, slot l % 8, with the chunk that the swizzle
+  // puts there.  Rows past M (columns past N) read row 0 and are never stored.
   constexpr int PER_WAVE = kTileBlocks / kTileWaves;
+  constexpr int PER_WAVE_B = BBLOCKS / kTileWaves;
   const int crow = lane >> 3;
   const int cchunk = (lane & 7) ^ crow ^ (wave & 1);   // blocks w + 8 i all have parity w & 1
   auto issue = [&](int step, auto st) {
@@ -473,17 +483,19 @@ __global__ __launch_bounds__(512, 1) void gemm_tile_kernel(TileProb p) {
       m = m < M ? m : 0;
       const bf16* xa = m < p.m0 ? p.x0 + (int64_t)m * p.K : p.x1 + (int64_t)(m - p.m0) * p.K;
       lds_copy16(xa + k, da + b * 1024);
-      int n = n_base + 8 * b + crow;
-      n = n < p.N ? n : 0;
-      lds_copy16(p.w + (int64_t)n * p.K + k, db + b * 1024);
+      if (i < PER_WAVE_B) {
+        int n = n_base + 8 * b + crow;
+        n = n < p.N ? n : 0;
+        lds_copy16(p.w + (int64_t)n * p.K + k, db + b * 1024);
+      }
     }
   };
 
-  // wave (wm, wn) owns rows 128 wm .. +127 and columns 64 wn .. +63 of the tile
-  const int wm = wave >> 2, wn = wave & 3;
-  f32x4 acc[8][4];
+  // wave (wm, wn) owns rows RM wm .. +RM-1 and columns 64 wn .. +63 of the tile
+  const int wm = wave / WN, wn = wave % WN;
+  f32x4 acc[FM][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -499,18 +511,18 @@ __global__ __launch_bounds__(512, 1) void gemm_tile_kernel(TileProb p) {
   // The products are taken as W x^T (B fragments in the MFMA's first operand)
   // so that each lane ends up with four consecutive output columns of a row.
   auto compute = [&](auto st) {
-    const unsigned char* ga = (st.value ? sa1 : sa0) + (8 * wm) * 2048;
+    const unsigned char* ga = (st.value ? sa1 : sa0) + (FM * wm) * 2048;
     const unsigned char* gb = (st.value ? sb1 : sb0) + (4 * wn) * 2048;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int off = kk ? foff1 : foff0;
-      bf16x8 af[8], bfr[4];
+      bf16x8 af[FM], bfr[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(gb + j * 2048 + off);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) af[i] = *reinterpret_cast<const bf16x8*>(ga + i * 2048 + off);
+      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(ga + i * 2048 + off);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mma32(bfr[j], af[i], acc[i][j]);
     }
@@ -535,8 +547,8 @@ __global__ __launch_bounds__(512, 1) void gemm_tile_kernel(TileProb p) {
   // consecutive columns 16 j + 4 (l / 16) .. +3: one 16-byte store each
   float* out = p.part + (int64_t)split * M * p.N;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int m = m_base + 128 * wm + 16 * i + (lane & 15);
+  for (int i = 0; i < FM; ++i) {
+    const int m = m_base + RM * wm + 16 * i + (lane & 15);
     if (m >= M) continue;
     float* row = out + (int64_t)m * p.N;
 #pragma unroll
@@ -547,10 +559,16 @@ __global__ __launch_bounds__(512, 1) void gemm_tile_kernel(TileProb p) {
   }
 }
 
-hipError_t launch_gemm_tile(const TileProb& p, hipStream_t s) {
+hipError_t launch_gemm_tile(const TileProb& p, int bn, hipStream_t s) {
   const int blocks = p.m_tiles * p.n_tiles * p.splits;
   if (blocks == 0) return hipSuccess;
-  launch(gemm_tile_kernel, dim3(blocks), dim3(64 * kTileWaves), 0, s, p);
+  if (p.n_tiles != (p.N + bn - 1) / bn) return hipErrorInvalidValue;
+  switch (bn) {
+    case 256: launch(gemm_tile_kernel<256>, dim3(blocks), dim3(64 * kTileWaves), 0, s, p); break;
+    case 128: launch(gemm_tile_kernel<128>, dim3(blocks), dim3(64 * kTileWaves), 0, s, p); break;
+    case 64: launch(gemm_tile_kernel<64>, dim3(blocks), dim3(64 * kTileWaves), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
