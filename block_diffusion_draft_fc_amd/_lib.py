@@ -65,6 +65,7 @@ def _load() -> C.CDLL:
         "dflash_timing_enable": (C.c_int, [C.c_int]),
         "dflash_timing_read": (C.c_int, [i32, C.POINTER(i64), C.POINTER(C.c_double)]),
         "dflash_timing_reset": (C.c_int, []),
+        "dflash_gemm_plan": (C.c_int, [C.c_int64, C.c_int64, C.c_int64, C.c_int32, C.POINTER(C.c_int32)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -239,6 +240,18 @@ def timing_enable(on: bool = True) -> None:
 
 def timing_reset() -> None:
     _check(LIB.dflash_timing_reset(), "dflash_timing_reset")
+
+
+GEMM_KERNELS = ("lds", "wide", "stream", "fullk", "resident", "slab", "tile")
+
+
+def dflash_gemm_plan(M: int, N: int, K: int, dtype) -> dict:
+    """The kernel and decomposition the library picks for a product of M rows
+    with an [N][K] weight (host-side planning only)."""
+    out = (C.c_int32 * 6)()
+    _check(LIB.dflash_gemm_plan(int(M), int(N), int(K), dtype_code(dtype), out), "dflash_gemm_plan")
+    return {"kernel": GEMM_KERNELS[out[0]], "splits": out[1], "k_chunk": out[2], "n_tiles": out[3],
+            "tile_bn": out[4], "rows_per_problem": out[5]}
 
 
 def timing_read() -> dict:

@@ -21,9 +21,10 @@
 //    tile kt, row i -> key 8*(i/4) + 4*kt + i%4, so after the S^T products each
 //    lane holds the scores of 8 consecutive keys for one query row: exactly the
 //    B operand of O^T = V^T P^T.
-//  * V is stored key-minor in the cache, so the A operand of that product (16
-//    head dims x 32 keys) is 16 contiguous bytes per lane as well.  No LDS and
-//    no lane shuffles sit in the key loop; the row max needs two xor shuffles.
+//  * V is stored transposed in the cache (tiles of 64 slots, head dim-major
+//    within a tile), so the A operand of that product (16 head dims x 32 keys)
+//    is 16 contiguous bytes per lane as well.  No LDS and no lane shuffles sit
+//    in the key loop; the row max needs two xor shuffles.
 //  * The running max, sum and output stay per lane in the log2 domain; the
 //    four waves merge through LDS at the end and the workgroup writes one
 //    partial (m, l, unnormalised O) per query row.

@@ -1129,6 +1129,30 @@ int dflash_timing_read(int32_t stage, int64_t* launches, double* total_ms) {
   return st;
 }
 
+int dflash_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t* out) {
+  if (!out) return DFLASH_ERR_ARG;
+  if (!dtype_ok(dtype)) return DFLASH_ERR_DTYPE;
+  if (M < 1 || N < 1 || K < 1 || M > ((int64_t)1 << 30) || N > ((int64_t)1 << 30) || K > ((int64_t)1 << 30))
+    return DFLASH_ERR_SHAPE;
+  const size_t eb = elem_bytes(dtype);
+  const GemmJob j = make_job(nullptr, M, nullptr, 0, nullptr, N, K, eb);
+  const SkinnyPlan& p = j.plan;
+  int32_t kind = DFLASH_GEMM_LDS;
+  if (p.tile) kind = DFLASH_GEMM_TILE;
+  else if (p.resident) kind = DFLASH_GEMM_RESIDENT;
+  else if (p.fullk) kind = DFLASH_GEMM_FULLK;
+  else if (p.stream) kind = DFLASH_GEMM_STREAM;
+  else if (p.slab) kind = DFLASH_GEMM_SLAB;
+  else if (p.wide) kind = DFLASH_GEMM_WIDE;
+  out[0] = kind;
+  out[1] = p.splits;
+  out[2] = p.k_chunk;
+  out[3] = p.n_tiles;
+  out[4] = p.tile ? p.tile_bn : 0;
+  out[5] = p.tile ? 0 : (int32_t)rows_per_problem(K, eb);
+  return DFLASH_OK;
+}
+
 int dflash_timing_reset(void) {
   Timing& t = timing();
   std::lock_guard<std::mutex> g(t.mu);

@@ -265,6 +265,33 @@ int dflash_timing_enable(int on);
 int dflash_timing_read(int32_t stage, int64_t *launches, double *total_ms);
 int dflash_timing_reset(void);
 
+/* ------------------------------------------------------------------------
+ * GEMM plan inspection (a diagnostic, host only: nothing is enqueued).  The
+ * projections of every entry point above (fc, q/k/v, o_proj, lm_head) are
+ * products of M activation rows with a [N][K] weight; this reports the
+ * kernel and the decomposition the library picks for one such product:
+ *   out[0] kernel: DFLASH_GEMM_* below
+ *   out[1] K-splits (fp32 partial products written for the consumer; 1 for
+ *          the kernels that write the result directly)
+ *   out[2] K-chunk per split
+ *   out[3] output-column tiles (per 16-row problem set)
+ *   out[4] columns per tile (256/128/64 for the tile kernel, else 0)
+ *   out[5] rows per weight-streaming problem (products of more rows are done
+ *          as several problems; 0 for the tile kernel)
+ * dtype as for the layer calls.  Returns DFLASH_ERR_ARG for a null out,
+ * DFLASH_ERR_SHAPE unless M, N, K >= 1, DFLASH_ERR_DTYPE for other dtypes.
+ * ---------------------------------------------------------------------- */
+typedef enum {
+  DFLASH_GEMM_LDS = 0,       /* activation slice in up to 64 KB of LDS, fp32 or other K */
+  DFLASH_GEMM_WIDE = 1,      /* <= 32 rows, K >= 8192: activation from L2 */
+  DFLASH_GEMM_STREAM = 2,    /* <= 32 rows: per-wave weight rings */
+  DFLASH_GEMM_FULLK = 3,     /* <= 16 rows: whole K per workgroup, no partials */
+  DFLASH_GEMM_RESIDENT = 4,  /* <= 16 rows, >= 65536 columns: rows kept in LDS */
+  DFLASH_GEMM_SLAB = 5,      /* 33..128 rows: slice staged in up to 160 KB of LDS */
+  DFLASH_GEMM_TILE = 6       /* many rows: 256 x 256/128/64 MFMA tiles */
+} dflash_gemm_kernel;
+int dflash_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t *out /* [6] */);
+
 #ifdef __cplusplus
 }
 #endif

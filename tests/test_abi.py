@@ -225,3 +225,74 @@ def test_draft_head_validation():
     assert f(*args(ids=FAKE + 2)) == L.ERR_ARG
     assert f(*args(w=16)) == L.ERR_WORKSPACE
     assert f(*args(B=1, ids=None)) == L.DFLASH_OK       # nothing to predict
+
+
+# ------------------------------------------------------------------ GEMM plans (host-side planning)
+
+def _plan(M, N, K, dt):
+    out = (C.c_int32 * 6)()
+    rc = L.LIB.dflash_gemm_plan(M, N, K, dt, out)
+    return rc, {"kernel": L.GEMM_KERNELS[out[0]] if rc == 0 else None, "splits": out[1], "k_chunk": out[2],
+                "n_tiles": out[3], "tile_bn": out[4], "rows_per_problem": out[5]}
+
+
+# the projections of the named workloads and the kernel each takes: decode
+# rounds (<= 16 and <= 32 rows), the 4-request stack (64 block rows, up to 128
+# [C; H] rows), the 16-request ragged batch (256 block rows, ~400 [C; H] rows),
+# the fresh 1024-row context and the draft head over the Qwen3 vocabulary
+ROUTES = [
+    ((16, 4096, 20480), "fullk"), ((16, 4096, 4096), "fullk"), ((32, 6144, 4096), "stream"),
+    ((24, 6144, 4096), "stream"), ((64, 4096, 4096), "slab"), ((128, 2048, 4096), "slab"),
+    ((48, 4096, 20480), "slab"), ((100, 4096, 20480), "tile"), ((256, 4096, 4096), "tile"),
+    ((392, 2048, 4096), "tile"), ((1024, 2560, 12800), "tile"), ((15, 151936, 4096), "resident"),
+    ((20, 4096, 20480), "wide"),
+]
+
+
+@pytest.mark.parametrize("shape,kernel", ROUTES, ids=[f"{m}x{n}x{k}" for (m, n, k), _ in ROUTES])
+def test_gemm_plan_routes(shape, kernel):
+    rc, p = _plan(*shape, L.DFLASH_BF16)
+    assert rc == 0 and p["kernel"] == kernel, p
+
+
+def test_gemm_plan_invariants():
+    """Over a grid of shapes: the splits cover K exactly once in whole chunks,
+    every kernel's own limits hold (rows, K alignment, LDS budget, tile width),
+    and the fp32 path stays on the kernel that handles it."""
+    for dt in (L.DFLASH_BF16, L.DFLASH_F32):
+        for M in (1, 3, 16, 17, 31, 32, 33, 48, 63, 64, 65, 100, 128, 129, 200, 256, 300, 1040):
+            for N in (64, 520, 2048, 4096, 6144, 70000):
+                for K in (256, 512, 1536, 2080, 4096, 12800, 20480):
+                    rc, p = _plan(M, N, K, dt)
+                    assert rc == 0, (M, N, K, dt)
+                    kind, sp, kc = p["kernel"], p["splits"], p["k_chunk"]
+                    where = (M, N, K, dt, p)
+                    assert sp >= 1 and kc >= 1 and (sp - 1) * kc < K <= sp * kc, where
+                    if dt == L.DFLASH_F32:
+                        assert kind == "lds" and p["rows_per_problem"] == 32, where
+                        continue
+                    rows = min(M, p["rows_per_problem"]) if kind != "tile" else M
+                    if kind in ("fullk", "resident"):
+                        assert rows <= 16 and sp == 1 and kc == K, where
+                    if kind in ("stream", "wide"):
+                        assert rows <= 32, where
+                    if kind == "slab":
+                        mt = -(-rows // 16)
+                        assert 3 <= mt <= 8 and K % 512 == 0 and kc % 512 == 0, where
+                        assert mt * 16 * (kc + 8) * 2 <= 160 * 1024, where
+                        assert p["n_tiles"] == -(-N // 64), where
+                    if kind == "tile":
+                        assert p["tile_bn"] in (64, 128, 256) and kc % 64 == 0, where
+                        assert p["n_tiles"] == -(-N // p["tile_bn"]), where
+                        assert M > p["rows_per_problem"] or p["rows_per_problem"] == 0, where
+                    if kind == "lds":
+                        assert kc % 256 == 0 and -(-rows // 16) * 16 * (kc + 8) * 2 <= 64 * 1024, where
+
+
+def test_gemm_plan_validation():
+    out = (C.c_int32 * 6)()
+    assert L.LIB.dflash_gemm_plan(16, 64, 64, L.DFLASH_BF16, None) == L.ERR_ARG
+    assert L.LIB.dflash_gemm_plan(0, 64, 64, L.DFLASH_BF16, out) == L.ERR_SHAPE
+    assert L.LIB.dflash_gemm_plan(16, 0, 64, L.DFLASH_BF16, out) == L.ERR_SHAPE
+    assert L.LIB.dflash_gemm_plan(16, 64, -1, L.DFLASH_BF16, out) == L.ERR_SHAPE
+    assert L.LIB.dflash_gemm_plan(16, 64, 64, 7, out) == L.ERR_DTYPE

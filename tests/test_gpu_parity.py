@@ -146,6 +146,28 @@ def test_ctx_project_bf16_many_rows(T, d, k_layers):
     assert rel_l2(from_device(C), ref) <= TOL["bf16"]
 
 
+# The three widths of the tile kernel's column tiles, each checked to be the
+# one the planner picks for the shape: 256 x 64 tiles (the ragged batch's
+# 256-row products), 256 x 128 (~400 rows over 2048 columns) and 256 x 256
+# (the fresh 1024-row context).
+@pytest.mark.parametrize("T,d,k_layers,bn", [(256, 4096, 1, 64), (392, 2048, 2, 128), (1024, 2560, 5, 256)])
+def test_ctx_project_tile_widths(T, d, k_layers, bn):
+    wl = configs.FRESH_CTX.scaled(name=f"ctx_project_T{T}_d{d}_k{k_layers}", d=d, k_layers=k_layers, n_h=8,
+                                  n_kv=2, d_h=64)
+    plan = L.dflash_gemm_plan(T, wl.d, wl.kd, torch.bfloat16)
+    assert plan["kernel"] == "tile" and plan["tile_bn"] == bn, plan
+    say(f"case ctx_project {wl.name} tile {bn} splits {plan['splits']}")
+    fc = G.fc_weights(wl)
+    x, _, _ = G.round_inputs(wl, 0, [T])
+    ref = O.ctx_project(x, fc["w_fc"], fc["gamma_h"], wl.eps)
+    C = torch.empty((T, wl.d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(L.dflash_ctx_project_ws_bytes(T, wl.kd, wl.d, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    L.dflash_ctx_project(to_device(x, wl), to_device(fc["w_fc"], wl), to_device(fc["gamma_h"], wl), wl.eps, C, ws)
+    torch.cuda.synchronize()
+    assert rel_l2(from_device(C), ref) <= TOL["bf16"]
+
+
 # ------------------------------------------------------------------ the named workloads
 
 def test_walkthrough_layer_f32():
