@@ -53,8 +53,8 @@ def parse():
     ap.add_argument("--no-fresh-ctx", action="store_true",
                     help="skip the MFMA-utilisation pass over the fresh 1024-row context projections")
     ap.add_argument("--no-batched", action="store_true",
-                    help="skip the attention-at-scale pass, the draft head, the ragged 16-request and the 5-layer "
-                         "hybrid stack rounds")
+                    help="skip the attention-at-scale pass, the draft head, the acceptance, the ragged 16-request "
+                         "and the 5-layer hybrid stack rounds")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 8 times (scales HBM counters)")
     return ap.parse_args()
@@ -384,6 +384,36 @@ def attn_at_scale(iters):
     return res
 
 
+# ---------------------------------------------------------------------------- acceptance
+
+def accept_pass(iters):
+    """dflash_accept on the 16-request batch (B = 16, Qwen3 vocabulary ids with
+    planted match prefixes): the acceptance lengths, next-round context rows
+    and anchors of a round written to device memory.  Kernel time from the
+    library's stage events."""
+    import torch
+
+    from block_diffusion_draft_fc_amd import _lib as L
+    from workloads import configs, generate as G
+
+    R, B = configs.RAGGED_PAGED.R, configs.RAGGED_PAGED.B
+    draft, post, _ = G.accept_tokens(configs.RAGGED_PAGED.seed, R, B, configs.QWEN3_VOCAB)
+    d_draft = torch.from_numpy(draft.reshape(-1).copy()).cuda()
+    d_post = torch.from_numpy(post).cuda()
+    acc, rows, anchor = (torch.empty((R,), dtype=torch.int32, device="cuda") for _ in range(3))
+    for _ in range(3):
+        L.dflash_accept(d_draft, d_post, acc, rows, anchor)
+    torch.cuda.synchronize()
+    L.timing_reset()
+    L.timing_enable(True)
+    for _ in range(iters):
+        L.dflash_accept(d_draft, d_post, acc, rows, anchor)
+    torch.cuda.synchronize()
+    st = L.timing_read()
+    L.timing_enable(False)
+    return {"requests": R, "block": B, "us_per_call": round(st["accept"][1] * 1e3 / st["accept"][0], 2)}
+
+
 # ---------------------------------------------------------------------------- draft head
 
 def draft_head_pass(iters):
@@ -626,6 +656,8 @@ def main():
         res["attn_at_scale"] = attn_at_scale(30)
         log("bench: draft head (lm_head over the Qwen3 vocabulary)")
         res["draft_head"] = draft_head_pass(20)
+        log("bench: acceptance of a 16-request round")
+        res["accept"] = accept_pass(100)
         log("bench: ragged 16-request paged batch")
         res["ragged_paged"] = batched_rounds(configs.RAGGED_PAGED, 16)
         log("bench: 5-layer hybrid stack, ring caches on the sliding layers")

@@ -66,6 +66,7 @@ def _load() -> C.CDLL:
         "dflash_timing_read": (C.c_int, [i32, C.POINTER(i64), C.POINTER(C.c_double)]),
         "dflash_timing_reset": (C.c_int, []),
         "dflash_gemm_plan": (C.c_int, [C.c_int64, C.c_int64, C.c_int64, C.c_int32, C.POINTER(C.c_int32)]),
+        "dflash_accept": (C.c_int, [vp, vp, i64, i32, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -228,10 +229,19 @@ def dflash_draft_head(h, B, gamma_f, eps, w_lm, token_ids, ws, max_logit=None, s
            "dflash_draft_head")
 
 
+def dflash_accept(draft_ids, posterior, acc, next_rows=None, next_anchor=None, stream=None) -> None:
+    """posterior [R, B] int32; draft_ids [R*(B-1)] (or [R, B-1]) int32; acc,
+    next_rows, next_anchor [R] int32 device tensors (the last two optional)."""
+    R, B = posterior.shape
+    _check(LIB.dflash_accept(_ptr(draft_ids), _ptr(posterior), int(R), int(B), _ptr(acc), _ptr(next_rows),
+                             _ptr(next_anchor), _stream(stream)), "dflash_accept")
+
+
 # --------------------------------------------------------------------- stage timing
 
 STAGES = ("ctx_gemm", "ctx_reduce", "ctx_norm", "qkv_gemm", "qkv_epilogue", "attn", "attn_combine",
-          "o_gemm", "o_reduce", "cache_append", "page_table", "head_norm", "head_gemm", "head_argmax")
+          "o_gemm", "o_reduce", "cache_append", "page_table", "head_norm", "head_gemm", "head_argmax",
+          "accept")
 
 
 def timing_enable(on: bool = True) -> None:

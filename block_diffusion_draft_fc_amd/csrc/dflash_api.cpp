@@ -1099,6 +1099,21 @@ int dflash_draft_head(const void* h, int64_t R, int32_t B, int64_t d, const void
   return hip_status(e);
 }
 
+int dflash_accept(const int32_t* draft_ids, const int32_t* posterior, int64_t R, int32_t B, int32_t* acc,
+                  int32_t* next_rows, int32_t* next_anchor, void* stream) {
+  if (R < 0 || R >= ((int64_t)1 << 31) || B < 1) return DFLASH_ERR_SHAPE;
+  auto misaligned = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 3) != 0; };
+  if (misaligned(draft_ids) || misaligned(posterior) || misaligned(acc) || misaligned(next_rows) ||
+      misaligned(next_anchor))
+    return DFLASH_ERR_ARG;
+  if (R == 0) return DFLASH_OK;
+  if (!posterior || !acc || (B > 1 && !draft_ids)) return DFLASH_ERR_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(staged(DFLASH_STAGE_ACCEPT, s, true, [&] {
+    return launch_accept(draft_ids, posterior, R, B, acc, next_rows, next_anchor, s);
+  }));
+}
+
 int dflash_timing_enable(int on) {
   Timing& t = timing();
   std::lock_guard<std::mutex> g(t.mu);

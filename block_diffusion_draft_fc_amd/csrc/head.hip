@@ -165,4 +165,48 @@ hipError_t launch_head_argmax(const float* part, int splits, int64_t M, int64_t 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- acceptance
+// "DFlash KV Injection Walkthrough" Step 6 and Step 7, per request r: the
+// draft token of block position j+1 is checked against the target's
+// prediction from position j; acc = the number of leading matches (the
+// cumulative product of the matches, summed), the next round injects acc + 1
+// context rows and opens its block with the target's token at the first
+// position not accepted, posterior[acc].
+// One wave per request: lanes compare 64 positions at a time and a ballot
+// of the mismatches gives the first one.
+__global__ __launch_bounds__(256) void accept_kernel(const int32_t* __restrict__ draft,
+                                                     const int32_t* __restrict__ post, int64_t R, int B,
+                                                     int32_t* __restrict__ acc, int32_t* __restrict__ next_rows,
+                                                     int32_t* __restrict__ next_anchor) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= R) return;
+  const int nd = B - 1;
+  const int32_t* dr = draft + r * nd;
+  const int32_t* pr = post + r * B;
+  int a = nd;
+  for (int j0 = 0; j0 < nd; j0 += 64) {
+    const int j = j0 + lane;
+    const bool miss = j < nd && dr[j] != pr[j];
+    const unsigned long long bal = __ballot(miss);
+    if (bal != 0ull) {
+      a = j0 + __ffsll(bal) - 1;
+      break;
+    }
+  }
+  if (lane == 0) {
+    acc[r] = a;
+    if (next_rows != nullptr) next_rows[r] = a + 1;
+    if (next_anchor != nullptr) next_anchor[r] = pr[a];
+  }
+}
+
+hipError_t launch_accept(const int32_t* draft, const int32_t* post, int64_t R, int B, int32_t* acc,
+                         int32_t* next_rows, int32_t* next_anchor, hipStream_t s) {
+  if (R == 0) return hipSuccess;
+  launch(accept_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, s, draft, post, R, B, acc, next_rows,
+         next_anchor);
+  return hipGetLastError();
+}
+
 }  // namespace dflash

@@ -188,6 +188,11 @@ constexpr int kHeadSeg = 8192;
 // ids[m] = the first argmax over n of sum_s part[s][m][n] (vocab % 4 == 0);
 // max_logit[m] its value (when not null).  seg_val / seg_idx: [M][ceil(vocab /
 // kHeadSeg)] scratch.
+// acc[r] = leading matches of draft [R][B-1] against post [R][B] (position j+1
+// against the prediction from j); next_rows = acc + 1 and next_anchor =
+// post[r][acc] when not null.
+hipError_t launch_accept(const int32_t* draft, const int32_t* post, int64_t R, int B, int32_t* acc,
+                         int32_t* next_rows, int32_t* next_anchor, hipStream_t s);
 hipError_t launch_head_argmax(const float* part, int splits, int64_t M, int64_t vocab, float* seg_val,
                               int32_t* seg_idx, int32_t* ids, float* max_logit, hipStream_t s);
 

@@ -230,6 +230,28 @@ int dflash_draft_head(const void *h, int64_t R, int32_t B, int64_t d, const void
                       const void *w_lm, int64_t vocab, int32_t dtype, int32_t *token_ids, float *max_logit,
                       void *ws, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Acceptance of a speculative round ("DFlash KV Injection Walkthrough", Step 6
+ * and Step 7), computed on the device so that the round's results stay there:
+ *   draft_ids   [R*(B-1)] int32 device: entry r*(B-1)+j = the draft token of
+ *               block position j+1 of request r (the token_ids layout of
+ *               dflash_draft_head)
+ *   posterior   [R*B] int32 device: entry r*B+j = the target's prediction of
+ *               the token after block position j of request r
+ *   acc         [R] int32 device: the number of leading draft tokens equal to
+ *               the target's prediction from the position before (the
+ *               cumulative product of the matches, summed; 0..B-1)
+ *   next_rows   [R] int32 device, or NULL: acc + 1, the context rows the next
+ *               round injects (the accepted positions and the corrected one)
+ *   next_anchor [R] int32 device, or NULL: the target's token at the first
+ *               position not accepted (posterior[r*B + acc]), which opens the
+ *               next round's block
+ * R == 0 is a no-op; B >= 1 (B == 1: nothing was drafted, acc = 0); R < 2^31.
+ * Pointers 4-byte aligned (else DFLASH_ERR_ARG).  Asynchronous on `stream`.
+ * ---------------------------------------------------------------------- */
+int dflash_accept(const int32_t *draft_ids, const int32_t *posterior, int64_t R, int32_t B, int32_t *acc,
+                  int32_t *next_rows, int32_t *next_anchor, void *stream);
+
 const char *dflash_strerror(int status);
 
 /* ------------------------------------------------------------------------
@@ -258,7 +280,8 @@ typedef enum {
   DFLASH_STAGE_HEAD_NORM = 11,   /* draft head: final RMSNorm of the block tails */
   DFLASH_STAGE_HEAD_GEMM = 12,   /* draft head: lm_head product */
   DFLASH_STAGE_HEAD_ARGMAX = 13, /* draft head: argmax over the vocabulary */
-  DFLASH_STAGE_COUNT = 14
+  DFLASH_STAGE_ACCEPT = 14,      /* acceptance of a round */
+  DFLASH_STAGE_COUNT = 15
 } dflash_stage;
 
 int dflash_timing_enable(int on);

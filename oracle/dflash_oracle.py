@@ -297,6 +297,30 @@ def new_context_rows(acc: int) -> int:
     return acc + 1
 
 
+def accept_round(draft_ids, posterior):
+    """[W] Step 6 and Step 7 for a batch of R requests.  draft_ids [R, B-1]:
+    the draft tokens of block positions 1..B-1; posterior [R, B]: the target's
+    prediction of the token after each block position 0..B-1.  Per request the
+    draft token of position j+1 is checked against the target's prediction
+    from position j (block_output_ids[:, 1:] against posterior[:, :-1]);
+    acc counts the leading matches.  The next round injects new_context_rows
+    (acc) context rows, and its block opens with the target's own token at
+    the first position not accepted, posterior[acc] (the correction that
+    replaces the rejected draft token).  Returns (acc, next_rows, anchor),
+    int64 arrays of length R."""
+    draft_ids = np.asarray(draft_ids).reshape(len(posterior), -1)
+    posterior = np.asarray(posterior)
+    R = posterior.shape[0]
+    acc = np.zeros(R, dtype=np.int64)
+    rows = np.zeros(R, dtype=np.int64)
+    anchor = np.zeros(R, dtype=np.int64)
+    for r in range(R):
+        acc[r] = acceptance_length(list(draft_ids[r]), list(posterior[r][:-1]))
+        rows[r] = new_context_rows(int(acc[r]))
+        anchor[r] = posterior[r][acc[r]]
+    return acc, rows, anchor
+
+
 # --------------------------------------------------------------------------
 # multi-request rounds and layer stacks
 # --------------------------------------------------------------------------

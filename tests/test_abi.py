@@ -296,3 +296,16 @@ def test_gemm_plan_validation():
     assert L.LIB.dflash_gemm_plan(16, 0, 64, L.DFLASH_BF16, out) == L.ERR_SHAPE
     assert L.LIB.dflash_gemm_plan(16, 64, -1, L.DFLASH_BF16, out) == L.ERR_SHAPE
     assert L.LIB.dflash_gemm_plan(16, 64, 64, 7, out) == L.ERR_DTYPE
+
+
+def test_accept_validation():
+    f = L.LIB.dflash_accept
+    assert f(FAKE, FAKE, 4, 0, FAKE, None, None, None) == L.ERR_SHAPE        # B < 1
+    assert f(FAKE, FAKE, -1, 16, FAKE, None, None, None) == L.ERR_SHAPE      # R < 0
+    assert f(FAKE, FAKE, 1 << 31, 16, FAKE, None, None, None) == L.ERR_SHAPE
+    assert f(FAKE, FAKE, 4, 16, None, None, None, None) == L.ERR_ARG         # acc missing
+    assert f(FAKE, None, 4, 16, FAKE, None, None, None) == L.ERR_ARG         # posterior missing
+    assert f(None, FAKE, 4, 16, FAKE, None, None, None) == L.ERR_ARG         # draft missing, B > 1
+    assert f(FAKE + 2, FAKE, 4, 16, FAKE, None, None, None) == L.ERR_ARG     # misaligned
+    assert f(FAKE, FAKE, 4, 16, FAKE, FAKE, FAKE + 1, None) == L.ERR_ARG
+    assert f(None, None, 0, 16, None, None, None, None) == L.DFLASH_OK       # no requests: no-op

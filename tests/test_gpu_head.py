@@ -97,3 +97,56 @@ def test_block_of_one_is_a_no_op():
     L.dflash_draft_head(hd, 1, hd[0], wl.eps, w, ids, None)
     torch.cuda.synchronize()
     assert int(ids[0]) == -7
+
+
+# ------------------------------------------------------------------ acceptance ([W] Step 6, Step 7)
+
+@pytest.mark.parametrize("R,B", [(1, 16), (16, 16), (37, 16), (5, 1), (7, 2), (9, 65), (3, 130), (256, 16)])
+def test_accept_parity(R, B):
+    """Acceptance lengths, next-round context rows and anchors equal the
+    oracle's exactly, on Qwen3-vocabulary ids with planted match prefixes
+    (every length 0..B-1 among them for the larger batches, B past one
+    64-lane group, B = 1 with nothing drafted)."""
+    say(f"case accept R={R} B={B}")
+    draft, post, k = G.accept_tokens(7, R, B, configs.QWEN3_VOCAB)
+    acc_o, rows_o, anchor_o = O.accept_round(draft, post)
+    assert list(acc_o) == list(k)   # the planted prefix is the acceptance length
+    d_draft = torch.from_numpy(draft.reshape(-1).copy()).cuda() if B > 1 else None
+    d_post = torch.from_numpy(post).cuda()
+    acc = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    rows = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    anchor = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    L.dflash_accept(d_draft, d_post, acc, rows, anchor)
+    torch.cuda.synchronize()
+    assert acc.cpu().numpy().tolist() == acc_o.tolist()
+    assert rows.cpu().numpy().tolist() == rows_o.tolist()
+    assert anchor.cpu().numpy().tolist() == anchor_o.tolist()
+    # the optional outputs may be left out
+    acc2 = torch.zeros((R,), dtype=torch.int32, device="cuda")
+    L.dflash_accept(d_draft, d_post, acc2)
+    torch.cuda.synchronize()
+    assert acc2.cpu().numpy().tolist() == acc_o.tolist()
+
+
+def test_accept_after_draft_head():
+    """The draft head's token ids feed the acceptance directly (its token_ids
+    layout): a posterior equal to the drafted tokens accepts the whole block
+    and anchors on the posterior's last token."""
+    wl = configs.DECODE_8K.scaled(name="accept_head_chain", R=3)
+    vocab = 4096
+    say(f"case accept after draft_head R={wl.R} B={wl.B} vocab={vocab}")
+    hw = G.head_weights(wl, vocab)
+    h = torch.from_numpy(G.head_input(wl)).cuda().to(torch.bfloat16)
+    ids = torch.empty((wl.R * (wl.B - 1),), dtype=torch.int32, device="cuda")
+    ws = torch.empty(L.dflash_draft_head_ws_bytes(wl.R, wl.B, wl.d, vocab, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    L.dflash_draft_head(h, wl.B, to_device(hw["gamma_f"], wl), wl.eps, to_device(hw["w_lm"], wl), ids, ws)
+    post = torch.empty((wl.R, wl.B), dtype=torch.int32, device="cuda")
+    post[:, :-1] = ids.view(wl.R, wl.B - 1)
+    post[:, -1] = torch.arange(wl.R, dtype=torch.int32, device="cuda") + 11
+    acc = torch.empty((wl.R,), dtype=torch.int32, device="cuda")
+    anchor = torch.empty((wl.R,), dtype=torch.int32, device="cuda")
+    L.dflash_accept(ids, post, acc, None, anchor)
+    torch.cuda.synchronize()
+    assert acc.cpu().tolist() == [wl.B - 1] * wl.R
+    assert anchor.cpu().tolist() == [11 + r for r in range(wl.R)]

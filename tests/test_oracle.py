@@ -356,6 +356,25 @@ def test_acceptance_example_and_state_update():
     assert O.acceptance_length([9, 2, 3], [1, 2, 3]) == 0
 
 
+def test_accept_round_batch():
+    """The batched acceptance on the walkthrough's block (tokens as ids), with
+    the posterior's last prediction (from position 6, never checked) an
+    arbitrary token; the identical, first-mismatch and later-match cases;
+    B = 1 (nothing drafted)."""
+    a = GOLDEN["acceptance"]
+    vocab = {w: i for i, w in enumerate(sorted(set(a["block"] + a["posterior_head"] + [a["correction"], "<x>"])))}
+    block = [vocab[w] for w in a["block"]]
+    post = [vocab[w] for w in a["posterior_head"]] + [vocab["<x>"]]
+    draft = [block[1:], [5, 6, 7], [9, 6, 7], [5, 9, 7]]
+    posterior = [post, [5, 6, 7, 8], [5, 6, 7, 8], [5, 6, 7, 8]]
+    acc, rows, anchor = O.accept_round(draft, posterior)
+    assert list(acc) == [a["acceptance_length"], 3, 0, 1]
+    assert list(rows) == [GOLDEN["state_update"]["new_context_rows"], 4, 1, 2]
+    assert list(anchor) == [vocab[a["correction"]], 8, 5, 6]
+    acc, rows, anchor = O.accept_round(np.zeros((2, 0), dtype=np.int64), [[3], [4]])
+    assert list(acc) == [0, 0] and list(rows) == [1, 1] and list(anchor) == [3, 4]
+
+
 def test_cache_growth_over_two_rounds():
     """Round 1 injects the 3 prompt positions; after the crop the draft cache
     holds positions 0-2; round 2 injects 3 accepted positions: 0-5."""

@@ -29,6 +29,8 @@ PINS = [
     T.test_cache_growth_over_two_rounds,
     T.test_draft_head_keeps_the_last_rows,
     T.test_draft_head_closed_forms,
+    T.test_acceptance_example_and_state_update,
+    T.test_accept_round_batch,
 ]
 
 
@@ -157,9 +159,27 @@ def _head_last_max(h, gamma_f, eps, w_lm, B):
     return logits, logits.shape[1] - 1 - np.argmax(logits[:, ::-1], axis=-1)
 
 
+def _accept_counts_every_match(draft_tail, posterior_head):
+    return int(sum(a == b for a, b in zip(draft_tail, posterior_head)))
+
+
+def _accept_round_shifted(draft_ids, posterior):
+    # the draft compared with the posterior of its own position, not the one before
+    posterior = np.asarray(posterior)
+    draft_ids = np.asarray(draft_ids).reshape(len(posterior), -1)
+    acc = np.array([O.acceptance_length(list(draft_ids[r]), list(posterior[r][1:])) for r in range(len(posterior))])
+    return acc, acc + 1, np.array([posterior[r][acc[r]] for r in range(len(posterior))])
+
+
+def _accept_round_anchor_after(draft_ids, posterior):
+    acc, rows, _ = _ORIG["accept_round"](draft_ids, posterior)
+    posterior = np.asarray(posterior)
+    return acc, rows, np.array([posterior[r][min(acc[r] + 1, posterior.shape[1] - 1)] for r in range(len(acc))])
+
+
 _ORIG = {name: getattr(O, name) for name in
          ("rope", "gqa_attention", "project_kv", "rms_norm", "ctx_project", "o_proj",
-          "crop", "visible", "rope_inv_freq", "kv_inject_layer", "draft_head")}
+          "crop", "visible", "rope_inv_freq", "kv_inject_layer", "draft_head", "accept_round")}
 
 MUTANTS = {
     "rope_sign_flipped": ("rope", _rope_sign),
@@ -182,6 +202,9 @@ MUTANTS = {
     "head_no_norm": ("draft_head", _head_no_norm),
     "head_weight_columns": ("draft_head", _head_weight_columns),
     "head_last_maximum": ("draft_head", _head_last_max),
+    "accept_counts_every_match": ("acceptance_length", _accept_counts_every_match),
+    "accept_posterior_shifted": ("accept_round", _accept_round_shifted),
+    "accept_anchor_one_late": ("accept_round", _accept_round_anchor_after),
 }
 
 

@@ -25,7 +25,8 @@ import numpy as np
 from .configs import Workload
 
 # stream tags
-_FC, _LAYER, _PREFILL_KV, _PREFILL_LEN, _SCHED, _RAW, _ANCHOR, _MASK, _H_IID, _HEAD, _HEAD_IN = range(1, 12)
+(_FC, _LAYER, _PREFILL_KV, _PREFILL_LEN, _SCHED, _RAW, _ANCHOR, _MASK, _H_IID, _HEAD, _HEAD_IN,
+ _ACCEPT) = range(1, 13)
 
 
 def _rng(seed: int, *tags: int) -> np.random.Generator:
@@ -159,3 +160,21 @@ def head_input(wl: Workload, rnd: int = 0) -> np.ndarray:
     """Rows [R*B, d] that the draft head reads (the stack's output for the
     blocks), N(0, 1)."""
     return _store(_normal(_rng(wl.seed, _HEAD_IN, rnd), (wl.R * wl.B, wl.d)), wl)
+
+
+def accept_tokens(seed: int, R: int, B: int, vocab: int, rnd: int = 0):
+    """Token ids for the acceptance of a round: posterior [R, B] uniform on
+    [0, vocab), and draft [R, B-1] that agrees with posterior[r][:-1] on a
+    planted prefix of k_r positions (k_r uniform on 0..B-1, the spread of
+    acceptance lengths 1..B of the decode workloads), differs at position k_r
+    and is uniform after it (later positions may agree again).
+    Returns (draft int32 [R, B-1], posterior int32 [R, B], k int64 [R])."""
+    g = _rng(seed, _ACCEPT, R, B, rnd)
+    post = g.integers(0, vocab, size=(R, B), dtype=np.int64)
+    k = g.integers(0, B, size=R, dtype=np.int64)
+    draft = g.integers(0, vocab, size=(R, max(B - 1, 0)), dtype=np.int64)
+    for r in range(R):
+        draft[r, :k[r]] = post[r, :k[r]]
+        if k[r] < B - 1:
+            draft[r, k[r]] = (post[r, k[r]] + 1 + g.integers(0, vocab - 1)) % vocab
+    return draft.astype(np.int32), post.astype(np.int32), k
