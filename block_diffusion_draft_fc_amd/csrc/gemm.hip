@@ -1,21 +1,29 @@
-// Weight-streaming GEMMs for the few-row projections of a draft round, plus
-// the split-K reduction and the row RMSNorm epilogue.
+// The GEMMs of a draft round's projections, plus the split-K reduction and
+// the row RMSNorm epilogue.
 //
-// The projections of a decode round multiply at most a few dozen activation
-// rows by weight matrices of tens to hundreds of MB (fc: the context rows
-// against W_fc, "DFlash KV Injection Walkthrough" Step 2; q/k/v and o: Step 4.1,
-// 4.2, 4.5).  They are bound by streaming the weight from HBM once, with fp32
-// split-K partial sums going to a [split][M][N] buffer.  Two kernels:
+// The projections multiply a few to a few thousand activation rows by weight
+// matrices of tens to hundreds of MB (fc: the context rows against W_fc,
+// "DFlash KV Injection Walkthrough" Step 2; q/k/v and o: Step 4.1, 4.2, 4.5;
+// lm_head: Step 5).  With few rows they are bound by streaming the weight
+// from HBM once; with many, by the MFMAs.  Results are fp32, either split-K
+// partial sums in a [split][M][N] buffer or the finished product.  Kernels,
+// by rows (the host planner picks one per product):
 //
-//  * gemm_lds_kernel - a workgroup owns 64 weight rows (output columns) and one
-//    K-chunk; the chunk's activation slice is staged in LDS once, then each wave
-//    streams 16 weight rows straight into the B operand of 16x16x32 MFMAs
-//    (16-byte loads, double-buffered).  Short chunks and many workgroups: the
-//    right shape for 4096-wide inputs, where the time is mostly latency.
-//  * gemm_wide_kernel - for long inputs (the 20480-wide fc): each wave streams
-//    64 weight rows and reads the activation rows straight from L2 into the A
-//    operand, one activation load feeding four weight tiles; no LDS, no
-//    barrier, and long per-wave streams.
+//  * gemm_fullk_kernel (<= 16 rows) - one workgroup per 16 output columns
+//    over the whole K, no partials;
+//  * gemm_resident_kernel (<= 16 rows, a vocabulary of columns) - the rows
+//    kept in LDS, whole-K weight tiles streamed per wave;
+//  * gemm_stream_kernel (<= 32 rows) - per-wave weight rings of 64-wide
+//    K-steps, 512-wide chunks;
+//  * gemm_wide_kernel (<= 32 rows, K >= 8192) - each wave streams 64 weight
+//    rows and reads the activation rows straight from L2;
+//  * gemm_slab_kernel (33..128 rows, K a multiple of 512) - the chunk's
+//    activation slice staged by direct copies in up to 160 KB of LDS, waves
+//    stream 16 weight rows each;
+//  * gemm_lds_kernel (fp32, and bf16 with other K) - the same scheme within
+//    64 KB of LDS, staged through registers;
+//  * gemm_tile_kernel (many rows) - 256 x 256/128/64 MFMA tiles through a
+//    two-stage LDS ring.
 #include <algorithm>
 #include <cstdlib>
 
