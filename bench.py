@@ -469,8 +469,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the layer runs on a single MI355X here; "
-              "multi-GPU sharding is not part of this build (see the design notes).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library runs the layer on a single MI355X and "
+              "implements no multi-GPU sharding.", file=sys.stderr)
         return 2
 
     if args.copy_calibration:

@@ -54,7 +54,7 @@ typedef enum {
 
 typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 
-/* Limits of this build. */
+/* Limits of the library. */
 #define DFLASH_MAX_SEQS 64        /* requests per cache handle */
 #define DFLASH_MAX_GROUP_ROWS 64  /* (n_h / n_kv) * B query rows per K/V head */
 #define DFLASH_KEY_ALIGN 64       /* contiguous capacity and page size are multiples of this */
