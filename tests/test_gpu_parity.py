@@ -208,6 +208,25 @@ def test_stack5_hybrid_window_full_shapes():
     run_rounds(wl, wl.rounds)
 
 
+def test_full_attention_layer_4x32k():
+    """One full-attention layer of the 5-layer stack at its full size: 4
+    requests on 32768-row caches (the shape the bench's attention-at-scale
+    pass times: one round of 512 work items, two-stage ring, rotated block
+    order; the slab GEMMs for the 64 block rows and the [C; H] rows)."""
+    wl = configs.STACK5_HYBRID.scaled(name="full_attention_layer_ctx32k_batch4", n_layers=1, sliding_layers=(),
+                                      rounds=1)
+    run_rounds(wl, wl.rounds)
+
+
+def test_sliding_ring_layer_4x32k():
+    """One sliding-window layer (window 4096) of the stack at its full size on
+    ring caches: 4 requests whose 32768-row prefill wrapped the 4160-slot ring
+    seven times before the round."""
+    wl = configs.STACK5_HYBRID.scaled(name="sliding_ring_layer_ctx32k_batch4", n_layers=1, sliding_layers=(0,),
+                                      rounds=1, ring=True)
+    run_rounds(wl, wl.rounds)
+
+
 # ------------------------------------------------------------------ small cases: kernel variants and edges
 
 def _small(name, **kw):
