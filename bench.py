@@ -46,8 +46,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=128)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--mode", choices=("best", "graph", "eager"), default="best",
-                    help="graph: each round's launches replayed from a captured HIP graph; eager: issued "
-                         "by the library calls; best: time both, report the faster")
+                    help="graph: the rounds' launches replayed from captured HIP graphs (one per 64-round "
+                         "cycle); eager: issued by the library calls; best: time both, report the faster")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fresh-ctx", action="store_true",
@@ -526,11 +526,17 @@ def main():
 
     graphs = None
     if args.mode in ("graph", "best"):
-        # One HIP graph per round of the cycle.  Capture runs the library's host
-        # side (validation, planning, cache metadata) and records the kernels with
-        # their arguments; replaying graph r re-runs round r's kernels on the
-        # cache rows it wrote at capture, so the cache is cropped back first.
-        log("bench: capturing one graph per round")
+        # HIP graphs of the cycle: one per round, and one holding all 64 rounds.
+        # Capture runs the library's host side (validation, planning, cache
+        # metadata) and records the kernels with their arguments; replaying
+        # round r's kernels re-writes the cache rows they wrote at capture, so
+        # the cache is cropped back first.  The crops of a round are host
+        # metadata only (nothing is enqueued), so a replay carries the whole
+        # GPU side of its rounds.  Steps replay in cycle order (every cache row
+        # is written before a later round reads it): single-round graphs up to
+        # a cycle boundary, the whole-cycle graph for each complete cycle, one
+        # launch per 64 rounds.
+        log("bench: capturing one graph per round and one per cycle")
         s = torch.cuda.Stream()
         graphs = []
         torch.cuda.synchronize()
@@ -539,35 +545,49 @@ def main():
             with torch.cuda.graph(g, stream=s):
                 step(r)
             graphs.append(g)
+        cycle = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cycle, stream=s):
+            for r in range(wl.rounds):
+                step(r)
         torch.cuda.synchronize()
 
-        # The crops of a round are host metadata only (nothing is enqueued), so a
-        # replay carries the whole GPU side of the round; replays run the cycle
-        # in order, so every cache row is written before a later round reads it.
-        def run(i):
-            graphs[i % wl.rounds].replay()
+        def run_steps(first, count):
+            i, end = first, first + count
+            while i < end:
+                if i % wl.rounds == 0 and end - i >= wl.rounds:
+                    cycle.replay()
+                    i += wl.rounds
+                else:
+                    graphs[i % wl.rounds].replay()
+                    i += 1
     else:
-        run = step
+        run_steps = None
+
+    def eager_steps(first, count):
+        for i in range(first, first + count):
+            step(i)
 
     # ---------------- timed regions: K steps after W warmup steps, bracketed by
     # synchronisation; a step's time is the slower of HIP events and wall clock
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
+    # the warmup steps end on a cycle boundary (the rounds still run in cycle
+    # order), so that graph replay times whole cycles
+    first = (-args.warmup) % wl.rounds
+
     def timed(fn):
-        for i in range(args.warmup):
-            fn(i)
+        fn(first, args.warmup)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         ev0.record()
-        for i in range(args.steps):
-            fn(args.warmup + i)
+        fn(first + args.warmup, args.steps)
         ev1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         return max(ev0.elapsed_time(ev1), wall * 1e3) / args.steps
 
-    graph_ms = timed(run) if graphs is not None else None
-    eager_ms = timed(step) if args.mode in ("eager", "best") else None
+    graph_ms = timed(run_steps) if graphs is not None else None
+    eager_ms = timed(eager_steps) if args.mode in ("eager", "best") else None
     if args.mode == "graph" or (args.mode == "best" and graph_ms <= eager_ms):
         ms_per_step, mode = graph_ms, "graph"
     else:
@@ -580,7 +600,7 @@ def main():
     L.timing_reset()
     L.timing_enable(True)
     for i in range(args.steps):
-        step(args.warmup + i)
+        step(first + args.warmup + i)
     torch.cuda.synchronize()
     stages = L.timing_read()
     L.timing_enable(False)
@@ -588,7 +608,7 @@ def main():
     # algorithmic work of the timed steps
     work = {}
     for i in range(args.steps):
-        r = (args.warmup + i) % wl.rounds
+        r = (first + args.warmup + i) % wl.rounds
         for k, v in round_work(wl, int(starts[r]), int(sched[r])).items():
             a = work.setdefault(k, {"bytes": 0, "flops": 0})
             a["bytes"] += v["bytes"]

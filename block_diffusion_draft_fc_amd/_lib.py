@@ -145,7 +145,9 @@ class Cache:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h is not None and h.value:
+        # at interpreter exit the module's globals may already be gone; the
+        # handle's host memory goes with the process then
+        if h is not None and h.value and LIB is not None:
             LIB.dflash_cache_destroy(h)
             self.handle = None
 
