@@ -25,6 +25,7 @@
 //  * gemm_tile_kernel (many rows) - 256 x 256/128/64 MFMA tiles through a
 //    two-stage LDS ring.
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
 
 #include <type_traits>
@@ -245,10 +246,19 @@ __global__ __launch_bounds__(256) void gemm_slab_kernel(GemmArgs args) {
 
 template <int MT>
 static hipError_t launch_slab_t(const GemmArgs& a, int blocks, size_t lds, hipStream_t s) {
-  // dynamic LDS above the default limit, allowed once per kernel
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_slab_kernel<MT>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kSlabLdsBytes);
-  if (attr != hipSuccess) return attr;
+  // dynamic LDS above the default limit, allowed once per kernel and device
+  constexpr int kMaxDevices = 64;
+  static std::atomic<bool> allowed[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (!allowed[dev].load(std::memory_order_acquire)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_slab_kernel<MT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kSlabLdsBytes);
+    if (e != hipSuccess) return e;
+    allowed[dev].store(true, std::memory_order_release);
+  }
   launch((gemm_slab_kernel<MT>), dim3(blocks), dim3(256), (uint32_t)lds, s, a);
   return hipGetLastError();
 }
