@@ -953,7 +953,7 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_kernel(AttnArgs a) {
   // chunk swizzle of key row j: a function of the key bits that krow varies
   // (0, 1, 3, 4), distinct over an operand read's 16 keys in every 256 bytes
   auto kswz = [](int j) { return DH == 128 ? (j & 3) | ((j >> 1) & 12) : ((j >> 1) & 1) | ((j >> 2) & 6); };
-  // K copies: lane l fills key kcopy_key + l / CK, slot l % CK
+  // K copy i: lane l fills key i * (64 / CK) + l / CK, slot l % CK
   const int kkey_in = lane / CK, kslot = lane % CK;
   // K operand reads: key 32 hh + 4 kt + krow (whose swizzle is kswz(krow)),
   // chunk 4 s + q4
