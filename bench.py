@@ -571,9 +571,12 @@ def main():
     # synchronisation; a step's time is the slower of HIP events and wall clock
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    # the warmup steps end on a cycle boundary (the rounds still run in cycle
-    # order), so that graph replay times whole cycles
-    first = (-args.warmup) % wl.rounds
+    # with graphs, the warmup steps end on a cycle boundary (the rounds still
+    # run in cycle order), so that graph replay times whole cycles; the
+    # captures have run every round's host side, so the cache's length is past
+    # every round's start and each step crops back to its own.  Eagerly alone,
+    # the cache starts at its prefill and the steps start at round 0.
+    first = (-args.warmup) % wl.rounds if graphs is not None else 0
 
     def timed(fn):
         fn(first, args.warmup)
