@@ -1031,6 +1031,8 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
 
 // ---------------------------------------------------------------- draft head
 
+}  // extern "C"
+
 namespace {
 struct HeadPlan {
   int64_t M;
@@ -1061,6 +1063,8 @@ int check_head(int64_t R, int32_t B, int64_t d, int64_t vocab, int32_t dtype) {
   return DFLASH_OK;
 }
 }  // namespace
+
+extern "C" {
 
 size_t dflash_draft_head_ws_bytes(int64_t R, int32_t B, int64_t d, int64_t vocab, int32_t dtype) {
   if (check_head(R, B, d, vocab, dtype) != DFLASH_OK || B == 1) return 0;
