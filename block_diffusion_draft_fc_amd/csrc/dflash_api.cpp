@@ -1172,6 +1172,19 @@ int dflash_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t* ou
   return DFLASH_OK;
 }
 
+int dflash_attn_plan(const int64_t* keys, int32_t R, int32_t n_kv, int64_t chunk_cap, int64_t* out) {
+  if (!keys || !out) return DFLASH_ERR_ARG;
+  if (R < 1 || R > DFLASH_MAX_SEQS || n_kv < 1 || chunk_cap < 64) return DFLASH_ERR_SHAPE;
+  std::vector<int64_t> k(keys, keys + R);
+  for (int64_t x : k)
+    if (x < 1 || x > ((int64_t)1 << 40)) return DFLASH_ERR_SHAPE;
+  const AttnSplit sp = plan_attn_split(k, n_kv, std::min<int64_t>(chunk_cap, (int64_t)1 << 30));
+  out[0] = sp.chunk;
+  out[1] = sp.items;
+  out[2] = sp.nst;
+  return DFLASH_OK;
+}
+
 int dflash_timing_reset(void) {
   Timing& t = timing();
   std::lock_guard<std::mutex> g(t.mu);

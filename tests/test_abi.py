@@ -309,3 +309,80 @@ def test_accept_validation():
     assert f(FAKE + 2, FAKE, 4, 16, FAKE, None, None, None) == L.ERR_ARG     # misaligned
     assert f(FAKE, FAKE, 4, 16, FAKE, FAKE, FAKE + 1, None) == L.ERR_ARG
     assert f(None, None, 0, 16, None, None, None, None) == L.DFLASH_OK       # no requests: no-op
+
+
+# ------------------------------------------------------------------ attention split (host-side planning)
+
+def _attn_plan(keys, n_kv, cap=1 << 30):
+    k = (C.c_int64 * len(keys))(*keys)
+    out = (C.c_int64 * 3)()
+    rc = L.LIB.dflash_attn_plan(k, len(keys), n_kv, cap, out)
+    return rc, int(out[0]), int(out[1]), int(out[2])
+
+
+def _items(keys, n_kv, chunk):
+    return sum(max(1, -(-k // chunk)) * n_kv for k in keys)
+
+
+_ATTN_KNOBS = ("DFLASH_ATTN_NST", "DFLASH_ATTN_ROUNDS", "DFLASH_ATTN_TARGET_ITEMS")
+
+
+# key counts of the named workloads: one 8K decode round (8192 cached + 16
+# block keys, plus the round's context rows), four 32K requests, a 4-request
+# stack, a 16-request ragged batch, a 4096-key sliding window on a ring of
+# 4096 + 64 rows, and a paged pool of 256-row pages
+ATTN_CASES = [
+    ([8216], 8, 1 << 30), ([8256], 8, 1 << 30), ([32792] * 4, 8, 1 << 30),
+    ([1040, 2112, 4160, 8256], 8, 1 << 30),
+    ([200 + 977 * i for i in range(16)], 8, 1 << 30), ([4160] * 4, 8, 62 * 4160),
+    ([33024] * 4, 8, 62 * 256), ([64], 1, 1 << 30), ([1], 8, 1 << 30), ([1 << 20], 8, 62 * 256),
+    ([100] * 64, 8, 1 << 30), ([300000] * 64, 8, 62 * 256), ([5000, 70, 130000], 2, 62 * 1024),
+]
+
+
+@pytest.mark.skipif(any(v in os.environ for v in _ATTN_KNOBS), reason="attention split overridden by env")
+@pytest.mark.parametrize("keys,n_kv,cap", ATTN_CASES, ids=[f"{len(k)}x{max(k)}-kv{g}-cap{c}" for k, g, c in ATTN_CASES])
+def test_attn_plan_invariants(keys, n_kv, cap):
+    """The chunk is a whole number of 64-key blocks, at least 128 and within
+    the cap; the item count is what the chunk gives; the ring depth follows the
+    total key count; and the chunk is the smallest that brings the items into
+    one round of launch slots (256 workgroups at depth 3, 512 at depth 2), or
+    the cap when no chunk within it does."""
+    rc, chunk, items, nst = _attn_plan(keys, n_kv, cap)
+    assert rc == 0
+    total = sum(keys) * n_kv
+    assert nst == (2 if total > 256 * 1024 else 3)
+    capc = max(128, cap // 64 * 64)
+    assert chunk % 64 == 0 and 128 <= chunk <= capc
+    assert items == _items(keys, n_kv, chunk)
+    limit = 512 if nst == 2 else 256
+    if _items(keys, n_kv, capc) <= limit:
+        assert items <= limit
+        assert chunk == 128 or _items(keys, n_kv, chunk - 64) > limit
+    else:
+        assert chunk == capc
+    # the workspace sizes partials for at most 1024 items plus two per
+    # (sequence, head), plus what a capped chunk adds
+    assert items <= 1024 + 2 * len(keys) * n_kv + -(-total // (capc - 128 if capc > 128 else 64))
+
+
+def test_attn_plan_headline_split():
+    """The 8K decode round: 8 heads x 26 chunks of 320 keys, one round of 256
+    slots at ring depth 3."""
+    if any(v in os.environ for v in _ATTN_KNOBS):
+        pytest.skip("attention split overridden by env")
+    assert _attn_plan([8216], 8) == (0, 320, 208, 3)
+
+
+def test_attn_plan_validation():
+    k = (C.c_int64 * 2)(100, 200)
+    out = (C.c_int64 * 3)()
+    f = L.LIB.dflash_attn_plan
+    assert f(None, 2, 8, 1 << 30, out) == L.ERR_ARG
+    assert f(k, 2, 8, 1 << 30, None) == L.ERR_ARG
+    assert f(k, 0, 8, 1 << 30, out) == L.ERR_SHAPE
+    assert f(k, 2, 0, 1 << 30, out) == L.ERR_SHAPE
+    assert f(k, 2, 8, 63, out) == L.ERR_SHAPE
+    z = (C.c_int64 * 2)(100, 0)
+    assert f(z, 2, 8, 1 << 30, out) == L.ERR_SHAPE
+    assert L.dflash_attn_plan([100, 200], 8) == {"chunk": 128, "items": 24, "nst": 3}
