@@ -13,7 +13,8 @@ Sources (cited by page title and section):
        3 (RoPE window), 4 (KV cache update and crop), 5 (sliding window), and the
        non-causal key design.
   [T]  "KV Cache + Speculative Decoding 面试 Cheat Sheet": section 4.2 and 6.3
-       (GQA: each K/V head serves a contiguous group of query heads).
+       (GQA: each K/V head serves a contiguous group of query heads), 2.1 and
+       4.5 (a cache element stored in one byte as fp8).
 
 Everything is float64.  Inputs arrive as float32 arrays holding exact bf16 or
 fp32 values and are upcast without any rounding afterwards.  Library routines
@@ -34,6 +35,10 @@ of readings kept with the design notes):
       (no upper bound: still non-causal inside the block).
   R14 layer stacks chain H_{l+1} = H_l + out_l (the decoder MLP is not on the
       pages).  parity unpinned: this chaining is a builder choice.
+  R23 an fp8 cache element is an OCP FP8 E4M3 byte: code = the nearest E4M3
+      value of x / scale (ties to the even mantissa, magnitudes from 448 up
+      saturated to 448), read back as value(code) * scale, with one fp32
+      scale for K and one for V per cache; nothing else changes precision.
   R21 the draft head samples greedily: the token of a row is the first index of
       its maximal logit (temperature sampling would need random draws the
       pages do not fix).
@@ -199,9 +204,11 @@ class LayerResult:
     weights: np.ndarray    # attention weights [n_h, B, L + n + B]
     qpos: np.ndarray
     kpos: np.ndarray
+    k_exact: np.ndarray = None   # appended rows before fp8 storage [n_kv, n + B, d_h]
+    v_exact: np.ndarray = None
 
 
-def kv_inject_layer(p: LayerParams, K_cache, V_cache, C, H) -> LayerResult:
+def kv_inject_layer(p: LayerParams, K_cache, V_cache, C, H, kv_scales=None) -> LayerResult:
     """One request through one layer, [W] Step 4 with the cache of [S] section 4.
 
     K_cache, V_cache [n_kv, L, d_h] hold rotated keys and raw values of
@@ -210,7 +217,12 @@ def kv_inject_layer(p: LayerParams, K_cache, V_cache, C, H) -> LayerResult:
     [S] section 3): keys take all of it (context rows then block rows), queries
     the last B positions ([W] Step 4.3).  The rotated keys and raw values of
     all n + B rows are appended (reading R7) before attention, which runs over
-    every cached key."""
+    every cached key.
+
+    kv_scales = (k_scale, v_scale) stores the cache in fp8 (reading R23): the
+    appended rows become e4m3_quantize(k, k_scale) and e4m3_quantize(v,
+    v_scale) before attention reads them, like every cached row (K_cache and
+    V_cache then hold such values already)."""
     K_cache, V_cache = f64(K_cache), f64(V_cache)
     L = K_cache.shape[1]
     n, B = C.shape[0], H.shape[0]
@@ -219,11 +231,15 @@ def kv_inject_layer(p: LayerParams, K_cache, V_cache, C, H) -> LayerResult:
     q = rope(project_q(p, H), qpos, p.theta)
     k, v = project_kv(p, C, H)
     k = rope(k, pos, p.theta)
+    k_exact, v_exact = k, v
+    if kv_scales is not None:
+        k = e4m3_quantize(k, kv_scales[0])
+        v = e4m3_quantize(v, kv_scales[1])
     K = np.concatenate([K_cache, k], axis=1)
     V = np.concatenate([V_cache, v], axis=1)
     kpos = np.arange(L + n + B, dtype=np.int64)
     o, A = gqa_attention(q, K, V, qpos, kpos, p.window)
-    return LayerResult(o_proj(o, p.w_o), K, V, q, A, qpos, kpos)
+    return LayerResult(o_proj(o, p.w_o), K, V, q, A, qpos, kpos, k_exact, v_exact)
 
 
 def crop(K, V, new_len: int):
@@ -322,6 +338,53 @@ def accept_round(draft_ids, posterior):
 
 
 # --------------------------------------------------------------------------
+# fp8 cache elements, [T] sections 2.1 and 4.5 (one byte per element), in the
+# OCP FP8 E4M3 format (reading R23)
+# --------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of each E4M3 byte: bit 7 the sign, bits 6..3 the exponent field e
+    (bias 7), bits 2..0 the mantissa m.  e = 0 holds the subnormals
+    (m / 8) * 2^-6; any other e holds (1 + m / 8) * 2^(e - 7), except that
+    e = 15 with m = 7 is NaN.  No infinities; the largest finite magnitude is
+    1.75 * 2^8 = 448."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    e, m = (c >> 3) & 15, c & 7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(c & 0x80, -mag, mag)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """The E4M3 byte nearest each value, ties to the even mantissa (reading
+    R23).  Magnitudes of 448 and more saturate to 448; NaN becomes 0x7F; the
+    sign of zero is kept.
+
+    A magnitude a in the binade [2^e, 2^(e+1)) (e >= -6; the subnormals share
+    the spacing of e = -6) lies on the grid of steps 2^(e-3): q = a * 2^(3-e),
+    rounded to an integer ties-to-even, is 8 + m for a normal value and m for
+    a subnormal one, so the magnitude bits are (e + 6) * 8 + q; q = 16 carries
+    into the next binade with m = 0, which the same formula gives."""
+    x = f64(x)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    _, k = np.frexp(a)
+    e = np.where(a < 2.0 ** -6, -6, k - 1)
+    q = np.rint(np.where(np.isnan(a), 0.0, a) * np.exp2(3.0 - e))
+    bits = (e + 6) * 8 + q.astype(np.int64)
+    bits = np.where(np.signbit(x), bits | 0x80, bits)
+    bits = np.where(np.isnan(x), 0x7F, bits)
+    return bits.astype(np.uint8)
+
+
+def e4m3_quantize(x, scale: float) -> np.ndarray:
+    """What an fp8 cache holds for x: value(code(x / scale)) * scale."""
+    return e4m3_decode(e4m3_encode(f64(x) / scale)) * scale
+
+
+# --------------------------------------------------------------------------
 # multi-request rounds and layer stacks
 # --------------------------------------------------------------------------
 
@@ -332,10 +395,13 @@ class OracleStack:
     kv_inject_layer per request, chaining H_{l+1} = H_l + out_l (reading R14);
     then every layer's cache is cropped to L + n."""
 
-    def __init__(self, layers, w_fc, gamma_h, eps, K0, V0):
-        """K0[l][r], V0[l][r]: [n_kv, L_r, d_h] cache content before round 0."""
+    def __init__(self, layers, w_fc, gamma_h, eps, K0, V0, kv_scales=None):
+        """K0[l][r], V0[l][r]: [n_kv, L_r, d_h] cache content before round 0.
+        kv_scales = (k_scale, v_scale): fp8 caches (reading R23), whose
+        content K0, V0 already holds fp8 values times the scales."""
         self.layers = list(layers)
         self.w_fc, self.gamma_h, self.eps = w_fc, gamma_h, eps
+        self.kv_scales = kv_scales
         self.K = [[f64(k) for k in row] for row in K0]
         self.V = [[f64(v) for v in row] for row in V0]
 
@@ -356,7 +422,7 @@ class OracleStack:
             for r in range(R):
                 L = self.K[li][r].shape[1]
                 res = kv_inject_layer(p, self.K[li][r], self.V[li][r],
-                                      C[cu[r]:cu[r + 1]], h[r * B:(r + 1) * B])
+                                      C[cu[r]:cu[r + 1]], h[r * B:(r + 1) * B], self.kv_scales)
                 out_l[r * B:(r + 1) * B] = res.out
                 n = cu[r + 1] - cu[r]
                 self.K[li][r], self.V[li][r] = crop(res.K, res.V, L + n)

@@ -276,9 +276,12 @@ def test_window_closed_forms():
 
 # ---------------------------------------------------------------- brute force
 
-def _brute_layer(p, K0, V0, C, H):
+def _brute_layer(p, K0, V0, C, H, quant_k=None, quant_v=None):
     """Scalar-loop formulation: explicit 2x2 rotations, explicit exp and sums,
-    K/V heads repeated explicitly for every query head."""
+    K/V heads repeated explicitly for every query head.  quant_k / quant_v map
+    an appended row to what the cache stores (identity when None)."""
+    quant_k = quant_k or (lambda r: r)
+    quant_v = quant_v or (lambda r: r)
     d_h, n_h, n_kv = p.d_h, p.n_h, p.n_kv
     half = d_h // 2
     W = p.w_qkv
@@ -307,8 +310,8 @@ def _brute_layer(p, K0, V0, C, H):
         kx = lin(x, n_h * d_h, n_kv * d_h)
         vx = lin(x, (n_h + n_kv) * d_h, n_kv * d_h)
         for g in range(n_kv):
-            Kc[g].append(rot(norm(kx[g * d_h:(g + 1) * d_h], p.gamma_k), L + t))
-            Vc[g].append(vx[g * d_h:(g + 1) * d_h])
+            Kc[g].append(quant_k(rot(norm(kx[g * d_h:(g + 1) * d_h], p.gamma_k), L + t)))
+            Vc[g].append(quant_v(vx[g * d_h:(g + 1) * d_h]))
     Kh = [Kc[h * n_kv // n_h] for h in range(n_h)]     # explicit repetition per query head
     Vh = [Vc[h * n_kv // n_h] for h in range(n_h)]
     out = []
@@ -341,6 +344,132 @@ def test_brute_force_tiny(L, n, B, window):
     assert np.max(np.abs(res.out - out)) < 1e-12
     assert np.max(np.abs(res.K - np.array(Kc))) < 1e-12
     assert np.max(np.abs(res.V - np.array(Vc))) < 1e-12
+
+
+# ---------------------------------------------------------------- fp8 cache elements
+# "KV Cache + Speculative Decoding 面试 Cheat Sheet" 2.1 and 4.5 give one byte
+# per fp8 element; the format is OCP FP8 E4M3 (sign, 4 exponent bits with bias
+# 7, 3 mantissa bits, no infinities, S.1111.111 = NaN, largest value 448).
+
+def _e4m3_grid():
+    """The 127 non-negative finite E4M3 magnitudes in code order, listed from
+    the format's definition: 8 subnormal steps of 2^-9, then 8 steps per binade
+    from 2^-6 up to 1.75 * 2^8."""
+    sub = [m * 2.0 ** -9 for m in range(8)]
+    norm = [(8 + m) * 2.0 ** (e - 10) for e in range(1, 16) for m in range(8)][:-1]
+    return np.array(sub + norm)
+
+
+def _brute_e4m3(x):
+    """Nearest grid magnitude by exhaustive search; a tie goes to the even code
+    (codes count up with the magnitude, so the even index); saturation at
+    448; the sign is re-applied.  Returns the code."""
+    grid = _e4m3_grid()
+    a = min(abs(x), 448.0)
+    dist = np.abs(grid - a)
+    best = np.flatnonzero(dist == dist.min())
+    code = int(best[0]) if len(best) == 1 else int([b for b in best if b % 2 == 0][0])
+    return code | (0x80 if math.copysign(1.0, x) < 0 else 0)
+
+
+def test_e4m3_format_values():
+    """Codes whose values the format fixes: zero, the smallest subnormal, the
+    largest subnormal, the smallest normal, one and its neighbours, the largest
+    value, NaN, and the negative codes mirroring the positive ones."""
+    table = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x37: 0.9375,
+             0x38: 1.0, 0x39: 1.125, 0x40: 2.0, 0x7E: 448.0, 0x7D: 416.0, 0x80: -0.0,
+             0xB8: -1.0, 0xFE: -448.0, 0x81: -(2.0 ** -9)}
+    for c, v in table.items():
+        assert O.e4m3_decode(np.uint8(c)) == v, hex(c)
+    assert math.copysign(1.0, O.e4m3_decode(np.uint8(0x80))) == -1.0
+    assert np.isnan(O.e4m3_decode(np.uint8(0x7F))) and np.isnan(O.e4m3_decode(np.uint8(0xFF)))
+    vals = O.e4m3_decode(np.arange(127, dtype=np.uint8))
+    assert np.array_equal(vals, _e4m3_grid())          # codes 0..126 in order of magnitude
+    assert np.array_equal(O.e4m3_decode(np.arange(128, 255, dtype=np.uint8)), -vals)
+
+
+def test_e4m3_matches_library_cast():
+    """Every code decodes as torch.float8_e4m3fn does, and in-range values
+    encode as its round-to-nearest-even cast does (the library saturates
+    nothing, so out-of-range values are pinned separately)."""
+    codes = np.arange(256, dtype=np.uint8)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    ours = O.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(ours), np.isnan(lib))
+    ok = ~np.isnan(lib)
+    assert np.array_equal(ours[ok], lib[ok]) and np.array_equal(np.signbit(ours[ok]), np.signbit(lib[ok]))
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal(200000) * np.exp2(rng.uniform(-13.0, 9.0, 200000))
+    x = x[np.abs(x) < 448.0]
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(x), want)
+
+
+def test_e4m3_encode_brute_force_and_ties():
+    """Exhaustive nearest search on random magnitudes, on every midpoint
+    between neighbouring codes (ties to the even code) and just beside each;
+    every finite code round-trips; saturation and NaN."""
+    grid = _e4m3_grid()
+    mids = (grid[:-1] + grid[1:]) / 2
+    rng = np.random.default_rng(5)
+    xs = list(mids) + list(np.nextafter(mids, 0)) + list(np.nextafter(mids, 1e9))
+    xs += list(rng.standard_normal(400) * np.exp2(rng.uniform(-12, 9, 400)))
+    xs += [-m for m in mids[::7]] + [0.0, -0.0, 2.0 ** -11, 2.0 ** -10, 3 * 2.0 ** -11]
+    got = O.e4m3_encode(np.array(xs))
+    for x, c in zip(xs, got):
+        assert int(c) == _brute_e4m3(x), (x, int(c))
+    fin = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    assert np.array_equal(O.e4m3_encode(O.e4m3_decode(fin)), fin)
+    sat = O.e4m3_encode(np.array([448.0, 449.0, 463.9, 464.0, 1e6, np.inf, -500.0, -np.inf, np.nan]))
+    assert list(sat) == [0x7E] * 6 + [0xFE, 0xFE, 0x7F]
+
+
+@pytest.mark.parametrize("L,n,B,window", [(5, 2, 3, 0), (4, 3, 2, 3)])
+def test_brute_force_tiny_fp8_cache(L, n, B, window):
+    """The layer over an fp8 cache: appended rows stored as the exhaustively
+    searched nearest E4M3 value of x / scale, times the scale, and attention
+    over those stored values, against the scalar-loop formulation."""
+    rng = np.random.default_rng(300 + L + n)
+    p = _tiny_params(rng, window=window)
+    d = p.w_qkv.shape[1]
+    ks, vs = 0.375, 0.0625
+    grid = np.concatenate([_e4m3_grid(), -_e4m3_grid()[1:]])
+    K0 = rng.choice(grid, (p.n_kv, L, p.d_h)) * ks          # a cache already in fp8
+    V0 = rng.choice(grid, (p.n_kv, L, p.d_h)) * vs
+    C, H = rng.standard_normal((n, d)), rng.standard_normal((B, d))
+
+    def q8(scale):
+        def f(row):
+            return [float(O.e4m3_decode(np.uint8(_brute_e4m3(t / scale)))) * scale for t in row]
+        return f
+
+    res = O.kv_inject_layer(p, K0, V0, C, H, kv_scales=(ks, vs))
+    out, Kc, Vc = _brute_layer(p, K0, V0, C, H, q8(ks), q8(vs))
+    assert np.max(np.abs(res.K - np.array(Kc))) == 0.0 and np.max(np.abs(res.V - np.array(Vc))) == 0.0
+    assert np.max(np.abs(res.out - out)) < 1e-12
+    exact = O.kv_inject_layer(p, K0, V0, C, H)
+    assert np.max(np.abs(exact.out - res.out)) > 1e-6   # fp8 storage does change the output
+
+
+def test_fp8_cache_error_is_bounded():
+    """Storing the new rows in fp8 moves every element by at most half a step
+    of its binade (relative 2^-4 for normal values), and the walkthrough
+    layer's output by a few percent, not more."""
+    wl = configs.WALKTHROUGH
+    p = _params(wl)
+    rng = np.random.default_rng(9)
+    d = p.w_qkv.shape[1]
+    K0, V0 = rng.standard_normal((p.n_kv, 40, p.d_h)), rng.standard_normal((p.n_kv, 40, p.d_h))
+    K0, V0 = O.e4m3_quantize(K0, 1.0), O.e4m3_quantize(V0, 1.0)
+    C, H = rng.standard_normal((3, d)), rng.standard_normal((4, d))
+    res = O.kv_inject_layer(p, K0, V0, C, H, kv_scales=(1.0, 1.0))
+    exact = O.kv_inject_layer(p, K0, V0, C, H)
+    for got, want in ((res.K[:, 40:], exact.K[:, 40:]), (res.V[:, 40:], exact.V[:, 40:])):
+        big = np.abs(want) >= 2.0 ** -6
+        assert np.all(np.abs(got - want)[big] <= 2.0 ** -4 * np.abs(want)[big])
+        assert np.all(np.abs(got - want)[~big] <= 2.0 ** -10)
+    e = np.linalg.norm(res.out - exact.out) / np.linalg.norm(exact.out)
+    assert 1e-4 < e < 0.05, e
 
 
 # ---------------------------------------------------------------- bookkeeping

@@ -31,7 +31,48 @@ PINS = [
     T.test_draft_head_closed_forms,
     T.test_acceptance_example_and_state_update,
     T.test_accept_round_batch,
+    T.test_e4m3_format_values,
+    T.test_e4m3_matches_library_cast,
+    T.test_e4m3_encode_brute_force_and_ties,
+    lambda: T.test_brute_force_tiny_fp8_cache(5, 2, 3, 0),
+    T.test_fp8_cache_error_is_bounded,
 ]
+
+_encode, _decode = O.e4m3_encode, O.e4m3_decode
+
+
+def _enc_rounding(rnd, saturate=True):
+    def enc(x):
+        x = O.f64(x)
+        a = np.abs(x)
+        if saturate:
+            a = np.minimum(a, 448.0)
+        _, k = np.frexp(a)
+        e = np.where(a < 2.0 ** -6, -6, k - 1)
+        q = rnd(np.where(np.isnan(a), 0.0, a) * np.exp2(3.0 - e))
+        bits = np.minimum((e + 6) * 8 + q.astype(np.int64), 0x7F)
+        bits = np.where(np.signbit(x), bits | 0x80, bits)
+        return np.where(np.isnan(x), 0x7F, bits).astype(np.uint8)
+    return enc
+
+
+def _dec_bias8(codes):
+    return _decode(codes) / 2.0
+
+
+def _dec_subnormal_hidden_one(codes):
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    v = _decode(codes)
+    sub = ((c >> 3) & 15) == 0
+    return np.where(sub, np.where(c & 0x80, -1.0, 1.0) * (1.0 + (c & 7) / 8.0) * 2.0 ** -6, v)
+
+
+def _quant_nothing(x, scale):
+    return O.f64(x)
+
+
+def _quant_scale_multiplied(x, scale):
+    return _decode(_encode(O.f64(x) * scale)) / scale
 
 
 def _rope_sign(x, positions, theta):
@@ -123,8 +164,8 @@ def _inv_freq_wrong(d_h, theta):
     return np.power(float(theta), -i / d_h)
 
 
-def _layer_q_front(p, K_cache, V_cache, C, H):
-    res = _ORIG["kv_inject_layer"](p, K_cache, V_cache, C, H)
+def _layer_q_front(p, K_cache, V_cache, C, H, kv_scales=None):
+    res = _ORIG["kv_inject_layer"](p, K_cache, V_cache, C, H, kv_scales)
     L = np.asarray(K_cache).shape[1]
     qpos = L + np.arange(H.shape[0])
     q = O.rope(O.project_q(p, H), qpos, p.theta)
@@ -205,6 +246,13 @@ MUTANTS = {
     "accept_counts_every_match": ("acceptance_length", _accept_counts_every_match),
     "accept_posterior_shifted": ("accept_round", _accept_round_shifted),
     "accept_anchor_one_late": ("accept_round", _accept_round_anchor_after),
+    "e4m3_ties_away": ("e4m3_encode", _enc_rounding(lambda q: np.floor(q + 0.5))),
+    "e4m3_truncates": ("e4m3_encode", _enc_rounding(np.floor)),
+    "e4m3_no_saturation": ("e4m3_encode", _enc_rounding(np.rint, saturate=False)),
+    "e4m3_bias_8": ("e4m3_decode", _dec_bias8),
+    "e4m3_subnormal_hidden_one": ("e4m3_decode", _dec_subnormal_hidden_one),
+    "fp8_cache_not_quantized": ("e4m3_quantize", _quant_nothing),
+    "fp8_scale_inverted": ("e4m3_quantize", _quant_scale_multiplied),
 }
 
 
