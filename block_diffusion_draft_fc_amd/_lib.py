@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdflash.s
 
 DFLASH_OK = 0
 ERR_ARG, ERR_SHAPE, ERR_DTYPE, ERR_RANGE, ERR_CAPACITY, ERR_HIP, ERR_WORKSPACE = -1, -2, -3, -4, -5, -6, -7
-DFLASH_F32, DFLASH_BF16 = 0, 1
+DFLASH_F32, DFLASH_BF16, DFLASH_FP8_E4M3 = 0, 1, 2
 
 
 class DFlashError(RuntimeError):
@@ -37,7 +37,8 @@ class CacheDesc(C.Structure):
     _fields_ = [("n_seqs", C.c_int32), ("n_kv", C.c_int32), ("d_h", C.c_int32), ("dtype", C.c_int32),
                 ("page_size", C.c_int32), ("max_pages_per_seq", C.c_int32), ("ring", C.c_int32),
                 ("capacity", C.c_int64),
-                ("k_pool", C.c_void_p), ("v_pool", C.c_void_p), ("block_table", C.c_void_p)]
+                ("k_pool", C.c_void_p), ("v_pool", C.c_void_p), ("block_table", C.c_void_p),
+                ("k_scale", C.c_float), ("v_scale", C.c_float)]
 
 
 def _load() -> C.CDLL:
@@ -92,6 +93,8 @@ def dtype_code(dt: torch.dtype) -> int:
         return DFLASH_F32
     if dt == torch.bfloat16:
         return DFLASH_BF16
+    if dt == torch.float8_e4m3fn:
+        return DFLASH_FP8_E4M3
     raise DFlashError(ERR_DTYPE, f"dtype {dt}")
 
 
@@ -120,26 +123,32 @@ class Cache:
     """dflash_cache handle plus the caller-owned device pools it describes."""
 
     def __init__(self, n_seqs, n_kv, d_h, dtype, capacity, page_size=0, max_pages_per_seq=0,
-                 device="cuda", pools=None, ring=False):
+                 device="cuda", pools=None, ring=False, k_scale=1.0, v_scale=1.0):
+        """dtype torch.float8_e4m3fn keeps K/V as E4M3 bytes (pools of
+        torch.uint8 holding the codes) read as code value * k_scale / v_scale."""
         self.n_seqs, self.n_kv, self.d_h = n_seqs, n_kv, d_h
         self.page_size, self.capacity, self.max_pages = page_size, capacity, max_pages_per_seq
         self.ring = bool(ring)
         self.dtype = dtype
+        self.fp8 = dtype == torch.float8_e4m3fn
+        self.k_scale, self.v_scale = float(k_scale), float(v_scale)
+        pool_dt = torch.uint8 if self.fp8 else dtype
         if pools is not None:
             self.k_pool, self.v_pool, self.table = pools
         elif page_size == 0:
-            self.k_pool = torch.zeros((n_seqs, n_kv, capacity, d_h), dtype=dtype, device=device)
+            self.k_pool = torch.zeros((n_seqs, n_kv, capacity, d_h), dtype=pool_dt, device=device)
             # V transposed in tiles of 64 slots: [.., tile, head dim, slot % 64]
-            self.v_pool = torch.zeros((n_seqs, n_kv, -(-capacity // 64), d_h, 64), dtype=dtype, device=device)
+            self.v_pool = torch.zeros((n_seqs, n_kv, -(-capacity // 64), d_h, 64), dtype=pool_dt, device=device)
             self.table = None
         else:
-            self.k_pool = torch.zeros((capacity, n_kv, page_size, d_h), dtype=dtype, device=device)
-            self.v_pool = torch.zeros((capacity, n_kv, -(-page_size // 64), d_h, 64), dtype=dtype, device=device)
+            self.k_pool = torch.zeros((capacity, n_kv, page_size, d_h), dtype=pool_dt, device=device)
+            self.v_pool = torch.zeros((capacity, n_kv, -(-page_size // 64), d_h, 64), dtype=pool_dt, device=device)
             self.table = torch.full((n_seqs, max_pages_per_seq), -1, dtype=torch.int32, device=device)
         desc = CacheDesc(n_seqs, n_kv, d_h, dtype_code(dtype), page_size, max_pages_per_seq, 1 if ring else 0,
                          capacity,
                          self.k_pool.data_ptr(), self.v_pool.data_ptr(),
-                         self.table.data_ptr() if self.table is not None else None)
+                         self.table.data_ptr() if self.table is not None else None,
+                         self.k_scale, self.v_scale)
         h = C.c_void_p()
         _check(LIB.dflash_cache_init(C.byref(h), C.byref(desc)), "dflash_cache_init")
         self.handle = h

@@ -1,0 +1,324 @@
+// Non-causal GQA block attention over an fp8 (OCP E4M3) draft KV cache: the
+// split-context attention of attention.hip with one byte per cached element
+// ("KV Cache + Speculative Decoding 面试 Cheat Sheet" 2.1 and 4.5), which halves
+// the bytes of the bandwidth-bound step.
+//
+// What it computes is unchanged ("DFlash KV Injection Walkthrough" Step 4.4;
+// "DFlash源码导读二 Qwen3DFlashAttention注意力实现全解析", the non-causal key
+// design and sections 1 and 5): every query row of the block attends to every
+// cached key with scale d_h^-0.5 (sliding layers hide pos_q - pos_k >= window),
+// with keys and values read as their E4M3 values times the cache's scales.
+// The key scale is folded into the softmax scale by the host, the value scale
+// multiplies the partial outputs here.  Queries stay bf16.
+//
+// Layout of the work on gfx950 (one workgroup of four waves per (sequence,
+// K/V head, key chunk), 64-key blocks through a ring of LDS stages filled by
+// direct copies, as in the bf16 ring kernel):
+//  * Every E4M3 value is a bf16 value, so the fp8 bytes are widened to bf16
+//    exactly (v_cvt_scalef32_pk_bf16_fp8 with scale 1) as they leave LDS and
+//    feed the same bf16 16x16x32 matrix steps; no precision is lost beyond
+//    the storage itself.
+//  * The head-dim order inside the QK contraction is free (any permutation
+//    applied to both operands): lane group q4 takes head dims
+//    q4 * d_h/4 .. q4 * d_h/4 + d_h/4 - 1 over the d_h/32 steps, so a lane's
+//    share of a key row is one or two 16-byte LDS reads.  The queries are
+//    loaded in that order too.
+//  * Likewise the key order: A-operand row i of 16-key tile (hh, kt) is key
+//    16 (i / 4) + 8 hh + 4 kt + i % 4.  After the S^T products lane group q4
+//    then holds keys 16 q4 .. 16 q4 + 15 of its query row, the B operand of
+//    both 32-key steps of O^T = V^T P^T, and the V^T operand of those two
+//    steps is one 16-byte read of a V^T row.
+//  * LDS stage: K as 64 key rows of d_h bytes, 16-byte chunk c of key j at
+//    c ^ hk(j); V^T as d_h rows of 64 bytes, chunk c of row R at
+//    c ^ ((R / 4) % 4).  Each operand read (16 lanes, 16 bytes each) then
+//    covers all 256 bytes of the banks.
+#include <cstdlib>
+
+#include "kernels.hpp"
+
+namespace dflash {
+
+namespace {
+
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+// Sixteen E4M3 bytes (byte e of the vector = element e) as two runs of eight
+// bf16 values, elements 0..7 and 8..15.
+__device__ __forceinline__ void widen16(u32x4 w, bf16x8& lo, bf16x8& hi) {
+  bf16x2 p[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false);
+    p[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true);
+  }
+  lo = bf16x8{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
+  hi = bf16x8{p[4][0], p[4][1], p[5][0], p[5][1], p[6][0], p[6][1], p[7][0], p[7][1]};
+}
+
+// the first `n` bytes of w kept, the rest cleared (0 <= n <= 16)
+__device__ __forceinline__ u32x4 keep_bytes(u32x4 w, int n) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = min(max(n - 4 * i, 0), 4);
+    w[i] &= k >= 4 ? 0xffffffffu : ((1u << (8 * k)) - 1u);
+  }
+  return w;
+}
+
+}  // namespace
+
+template <int DH, int NST>
+__global__ __launch_bounds__(256, 1) void attn_ring64_fp8_kernel(AttnArgs a) {
+  using V8 = bf16x8;
+  static_assert(DH == 64 || DH == 128, "layouts defined for d_h 64 and 128");
+  static_assert(NST >= 2 && NST <= 7, "blocks in flight are counted by wait_vm_blocks (up to 6 after the current)");
+  constexpr int DS = DH / 32;          // K=32 steps over the head dim
+  constexpr int DT = DH / 16;          // 16-dim tiles of the output
+  constexpr int KCH = DH / 16;         // 16-byte chunks per key row
+  constexpr int KSLABS = DH / 16;      // 1 KB copies of the block's K (64 rows of DH bytes)
+  constexpr int VSLABS = DH / 16;      // 1 KB copies of its V^T (DH rows of 64 bytes)
+  constexpr int COPIES = KSLABS + VSLABS;
+  constexpr int PER_WAVE = COPIES / 4;
+  constexpr int STAGE = COPIES * 1024;
+  constexpr int QSPAN = DH / 4;        // head dims of a lane group in the QK contraction
+  __shared__ __align__(16) unsigned char ring[NST * STAGE];
+  __shared__ int32_t s_page[kAttnMaxChunkPages];
+
+  const int item = blockIdx.x;
+  int r = 0;
+  while (r + 1 < a.R && item >= a.item_base[r + 1]) ++r;
+  const int local = item - a.item_base[r];
+  const int g = local / a.chunks[r];
+  const int chunk = local - g * a.chunks[r];
+  const int key_hi = a.key_hi[r];
+  const int kbeg = (a.key_lo[r] & ~63) + chunk * a.chunk_keys;
+  const int kend = min(kbeg + a.chunk_keys, key_hi);
+  const int nblk = kend > kbeg ? (kend - kbeg + 63) >> 6 : 0;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j16 = lane & 15, q4 = lane >> 4;
+  const int valid_q = a.group * a.B;
+  // query rows of this wave: 16 wave .. 16 wave + 15; the workspace holds
+  // qrows (a multiple of 16) rows per (sequence, K/V head), so a wave past
+  // them loads and stores nothing
+  const bool wave_rows = 16 * wave < a.qrows;
+
+  const int row = 16 * wave + j16;
+  const bf16* qbase = static_cast<const bf16*>(a.q_ws) + (int64_t)(r * a.n_kv + g) * a.qrows * DH;
+  const int vlo = a.window > 0 ? a.qpos0[r] + row % a.B - a.window + 1 : INT_MIN;
+  const int vis_lo_max = a.qpos0[r] + a.B - a.window;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[DT];
+#pragma unroll
+  for (int d = 0; d < DT; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int pg0 = kbeg / a.cache.page_rows;
+  const int npg = nblk > 0 ? (kend - 1) / a.cache.page_rows - pg0 + 1 : 0;
+  for (int i = tid; i < npg; i += 256) s_page[i] = (int32_t)cache_page(a.cache, r, (pg0 + i) * a.cache.page_rows);
+  __syncthreads();
+  // Queries: direct copies into the last stage ahead of the first blocks'
+  // (as in the bf16 ring kernel); step s of lane (j16, q4) holds head dims
+  // QSPAN q4 + 8 s .. + 7 of row 16 wave + j16, at 16 * lane of slab s.
+  static_assert(4 * DS * 1024 <= STAGE, "the queries fit one stage");
+  unsigned char* my_q = ring + (NST - 1) * STAGE + wave * DS * 1024;
+  if (wave_rows) {
+#pragma unroll
+    for (int s = 0; s < DS; ++s) lds_copy16(qbase + (int64_t)row * DH + QSPAN * q4 + 8 * s, my_q + s * 1024);
+  }
+  V8 qv[DS];
+
+  const unsigned char* kpool = static_cast<const unsigned char*>(a.cache.k_pool);
+  const unsigned char* vpool = static_cast<const unsigned char*>(a.cache.v_pool);
+  // chunk swizzle of key row j: distinct over the 16 keys of an operand read
+  // together with the key's offset in the 256 bytes of the banks (key bits
+  // 0, 1, 4, 5 vary in a read; 128-byte rows take bit 0 from the offset,
+  // 64-byte rows bits 0 and 1)
+  auto hk = [](int j) { return DH == 128 ? ((j >> 1) & 1) | ((j >> 3) & 6) : (j >> 4) & 3; };
+  const int krow = 16 * (j16 >> 2) + (j16 & 3);   // + 8 hh + 4 kt: key of A-operand row j16
+  int koff[DS / 2 > 0 ? DS / 2 : 1];
+  if constexpr (DH == 128) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) koff[t] = krow * DH + (((2 * q4 + t) ^ hk(krow)) * 16);
+  } else {
+    koff[0] = krow * DH + ((q4 ^ hk(krow)) * 16);
+  }
+  // V^T operand: row 16 d + j16, chunk q4 (keys 16 q4 .. 16 q4 + 15)
+  const int voff = j16 * 64 + ((q4 ^ ((j16 >> 2) & 3)) * 16);
+  // copies: K slab i, lane l -> key i * (64 / KCH) + l / KCH, slot l % KCH;
+  // V^T slab i, lane l -> row 16 i + l / 4, slot l % 4
+  const int kkey_in = lane / KCH, kslot = lane % KCH;
+  const int vrow_in = lane >> 2, vslot = lane & 3;
+
+  const int rot0 = a.rot > 0 && nblk > 0 ? (int)(((unsigned)item * (unsigned)a.rot) % (unsigned)nblk) : 0;
+  auto rot_blk = [&](int b) { const int x = b + rot0; return x >= nblk ? x - nblk : x; };
+  auto issue = [&](int b) {
+    const int blk = kbeg + 64 * rot_blk(b);
+    const int64_t page = s_page[blk / a.cache.page_rows - pg0];
+    const int slot = blk % a.cache.page_rows;
+    const unsigned char* kb = kpool + k_offset(a.cache, page, g, slot);
+    const unsigned char* vb = vpool + v_offset(a.cache, page, g, slot);
+    unsigned char* sb = ring + (b % NST) * STAGE;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int idx = wave * PER_WAVE + i;
+      const unsigned char* src;
+      if (idx < KSLABS) {
+        const int key = idx * (64 / KCH) + kkey_in;
+        src = kb + key * DH + 16 * (kslot ^ hk(key));
+      } else {
+        const int R = 16 * (idx - KSLABS) + vrow_in;
+        src = vb + R * kVTile + 16 * (vslot ^ ((R >> 2) & 3));
+      }
+      lds_copy16(src, sb + idx * 1024);
+    }
+  };
+
+  auto process = [&](int b) {
+    const unsigned char* sb = ring + (b % NST) * STAGE;
+    const unsigned char* kbs = sb;
+    const unsigned char* vbs = sb + KSLABS * 1024;
+    const int blk = kbeg + 64 * rot_blk(b);
+    // scores: lane (j16, q4) holds row j16's keys blk + 16 q4 + 8 hh .. + 7 in sv[hh]
+    f32x8 sv[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      V8 kv[2][DS];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const unsigned char* kr = kbs + (8 * hh + 4 * kt) * DH;
+        if constexpr (DH == 128) {
+          widen16(*reinterpret_cast<const u32x4*>(kr + koff[0]), kv[kt][0], kv[kt][1]);
+          widen16(*reinterpret_cast<const u32x4*>(kr + koff[1]), kv[kt][2], kv[kt][3]);
+        } else {
+          widen16(*reinterpret_cast<const u32x4*>(kr + koff[0]), kv[kt][0], kv[kt][1]);
+        }
+      }
+      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int s = 0; s < DS; ++s)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) sacc[kt] = mma32(kv[kt][s], qv[s], sacc[kt]);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[hh][4 * kt + e] = sacc[kt][e] * a.scale_log2;
+    }
+    const bool all_vis = blk + 64 <= key_hi && (a.window <= 0 || blk >= vis_lo_max);
+    if (!all_vis) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = blk + 16 * q4 + 8 * hh + e;
+          sv[hh][e] = ((key >= vlo) & (key < key_hi)) ? sv[hh][e] : -INFINITY;
+        }
+    }
+    float mx = sv[0][0];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sv[hh][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    // lazy maximum, as in the bf16 kernels: moved only when the block's
+    // exceeds it by more than 8 (log2 units), so every p <= 256
+    const bool need = mx > m_run + 8.f;
+    const float m_new = need ? mx : m_run;
+    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+    m_run = m_new;
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    V8 pv[2];
+    float ps = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      f32x8 p;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(sv[hh][e] - m_use);
+        ps += p[e];
+      }
+      pv[hh] = cvt8<bf16>(p);
+    }
+    l_run = l_run * alpha + ps;
+    if (__any(need)) {
+#pragma unroll
+      for (int d = 0; d < DT; ++d) o[d] *= alpha;
+    }
+    // stale rows past the end of the cache may hold any bytes (NaN codes
+    // included): clear them so that p = 0 cannot meet a NaN (last block only)
+    const int key0 = blk + 16 * q4;
+    const bool stale = key0 + 16 > key_hi;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) {
+      u32x4 w = *reinterpret_cast<const u32x4*>(vbs + d * 1024 + voff);
+      if (stale) w = keep_bytes(w, min(max(key_hi - key0, 0), 16));
+      V8 lo, hi;
+      widen16(w, lo, hi);
+      o[d] = mma32(lo, pv[0], o[d]);
+      o[d] = mma32(hi, pv[1], o[d]);
+    }
+  };
+
+  constexpr int AHEAD = NST - 1;
+  constexpr int INIT = AHEAD < 2 ? AHEAD : 2;
+  int issued = 0;
+  for (; issued < min(INIT, nblk); ++issued) issue(issued);
+  wait_vm_blocks<PER_WAVE>(max(0, issued - 1));
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    qv[s] = *reinterpret_cast<const V8*>(my_q + s * 1024 + 16 * lane);
+    if (row >= valid_q) qv[s] = zero8<bf16>();
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read before the stage is refilled
+  for (int b = 0; b < nblk; ++b) {
+    wait_vm_blocks<PER_WAVE>(issued - 1 - b);
+    asm volatile("s_barrier" ::: "memory");
+    for (; issued < min(nblk, b + AHEAD + 1); ++issued) issue(issued);
+    process(b);
+  }
+
+  if (!wave_rows) return;
+  float* po = a.part_o + (int64_t)item * a.qrows * DH;
+#pragma unroll
+  for (int d = 0; d < DT; ++d)
+    *reinterpret_cast<f32x4*>(po + (int64_t)row * DH + 16 * d + 4 * q4) = o[d] * a.v_scale;
+  float l = l_run;
+  l += __shfl_xor(l, 16, kWave);
+  l += __shfl_xor(l, 32, kWave);
+  if (q4 == 0) {
+    float* pml = a.part_ml + (int64_t)item * 2 * a.qrows;
+    pml[row] = m_run;
+    pml[a.qrows + row] = l;
+  }
+}
+
+// Ring depth: the host plans for the bf16 kernel's depths (3 stages of 32 KB:
+// one workgroup per CU; 2: two per CU).  fp8 stages are half as large, so the
+// same bytes stay in flight with twice the blocks ahead: 3 -> 5 stages (80 KB,
+// one workgroup per CU), 2 -> 3 (48 KB).  DFLASH_ATTN_FP8_NST overrides.
+hipError_t launch_attn_fp8(const AttnArgs& a, int items, hipStream_t s) {
+  if (items == 0) return hipSuccess;
+  if ((a.qrows + 15) / 16 > 4) return hipErrorInvalidValue;
+  static const int forced = [] {
+    const char* e = std::getenv("DFLASH_ATTN_FP8_NST");
+    const int v = e ? std::atoi(e) : 0;
+    return v >= 2 && v <= 7 ? v : 0;
+  }();
+  const int plan = a.nst > 0 ? a.nst : items <= 256 ? 3 : 2;
+  const int nst = forced ? forced : plan >= 3 ? 5 : 3;
+#define DFLASH_FP8_CASE(DH_, NST_)                                                 \
+  if (a.d_h == DH_ && nst == NST_) {                                               \
+    launch((attn_ring64_fp8_kernel<DH_, NST_>), dim3(items), dim3(256), 0, s, a); \
+    return hipGetLastError();                                                      \
+  }
+  DFLASH_FP8_CASE(128, 2) DFLASH_FP8_CASE(128, 3) DFLASH_FP8_CASE(128, 4) DFLASH_FP8_CASE(128, 5)
+  DFLASH_FP8_CASE(128, 6) DFLASH_FP8_CASE(128, 7)
+  DFLASH_FP8_CASE(64, 2) DFLASH_FP8_CASE(64, 3) DFLASH_FP8_CASE(64, 4) DFLASH_FP8_CASE(64, 5)
+  DFLASH_FP8_CASE(64, 6) DFLASH_FP8_CASE(64, 7)
+#undef DFLASH_FP8_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dflash

@@ -42,7 +42,9 @@ hipError_t launch_cache_append(int dtype, const AppendArgs& a, int64_t n_rows, h
   const int64_t total = n_rows * a.cache.n_kv * (a.cache.d_h >> 3);
   if (total == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((total + 255) / 256);
-  if (dtype == 1)
+  if (dtype == 2)
+    launch(cache_append_kernel<uint8_t>, dim3(blocks), dim3(256), 0, s, a, n_rows);
+  else if (dtype == 1)
     launch(cache_append_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, a, n_rows);
   else
     launch(cache_append_kernel<uint32_t>, dim3(blocks), dim3(256), 0, s, a, n_rows);

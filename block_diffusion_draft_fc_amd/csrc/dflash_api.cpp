@@ -33,6 +33,8 @@ constexpr int kAttnMaxTarget = 1024;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 bool dtype_ok(int32_t dt) { return dt == DFLASH_F32 || dt == DFLASH_BF16; }
+bool cache_dtype_ok(int32_t dt) { return dtype_ok(dt) || dt == DFLASH_FP8_E4M3; }
+bool scale_ok(float x) { return std::isfinite(x) && x > 0.f; }
 size_t elem_bytes(int32_t dt) { return dt == DFLASH_BF16 ? 2 : 4; }
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -728,7 +730,8 @@ const char* dflash_strerror(int status) {
 int dflash_cache_init(dflash_cache** out, const dflash_cache_desc* desc) {
   if (!out || !desc) return DFLASH_ERR_ARG;
   const auto& d = *desc;
-  if (!dtype_ok(d.dtype)) return DFLASH_ERR_DTYPE;
+  if (!cache_dtype_ok(d.dtype)) return DFLASH_ERR_DTYPE;
+  if (d.dtype == DFLASH_FP8_E4M3 && (!scale_ok(d.k_scale) || !scale_ok(d.v_scale))) return DFLASH_ERR_ARG;
   if (d.n_seqs < 1 || d.n_seqs > DFLASH_MAX_SEQS || d.n_kv < 1 || d.d_h < 8 || d.d_h % 8 != 0)
     return DFLASH_ERR_SHAPE;
   if (d.page_size < 0 || d.page_size % DFLASH_KEY_ALIGN != 0 || d.capacity <= 0) return DFLASH_ERR_SHAPE;
@@ -870,7 +873,8 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
   if (st) return st;
   if (!c) return DFLASH_ERR_ARG;
   const auto& cd = c->desc;
-  if (cd.dtype != L->dtype) return DFLASH_ERR_DTYPE;
+  const bool fp8 = cd.dtype == DFLASH_FP8_E4M3;
+  if (cd.dtype != L->dtype && !(fp8 && L->dtype == DFLASH_BF16)) return DFLASH_ERR_DTYPE;
   if (cd.n_kv != L->n_kv || cd.d_h != L->d_h) return DFLASH_ERR_SHAPE;
   if (B < 1 || (int64_t)(L->n_h / L->n_kv) * B > DFLASH_MAX_GROUP_ROWS) return DFLASH_ERR_SHAPE;
   std::vector<int64_t> n;
@@ -952,6 +956,9 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
     for (int i = 0; i < L->d_h / 2; ++i) a.inv_freq[i] = std::pow(L->rope_theta, -2.0 * i / L->d_h);
     for (int r = 0; r < R; ++r) { a.seq.L[r] = c->len[r]; a.seq.n[r] = (int32_t)n[r]; }
     for (int r = 0; r <= R; ++r) a.seq.cu[r] = cu_ctx[r];
+    a.cache_fp8 = fp8 ? 1 : 0;
+    a.k_scale = fp8 ? cd.k_scale : 1.f;
+    a.v_scale = fp8 ? cd.v_scale : 1.f;
     e = staged(DFLASH_STAGE_QKV_EPILOGUE, s, true, [&] { return launch_qkv_epilogue(dt, a, s); });
   }
 
@@ -961,7 +968,10 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
     aa.q_ws = q_ws; aa.cache = cv; aa.part_o = part_o; aa.part_ml = part_ml;
     aa.R = R; aa.B = B; aa.n_kv = L->n_kv; aa.group = (int32_t)p.group; aa.qrows = (int32_t)p.qrows;
     aa.d_h = L->d_h; aa.window = L->window;
-    aa.scale_log2 = (float)(1.0 / std::sqrt((double)L->d_h) * 1.4426950408889634);
+    // an fp8 cache's key scale multiplies every score: it joins the softmax
+    // scale; its value scale multiplies every output (applied to the partials)
+    aa.scale_log2 = (float)(1.0 / std::sqrt((double)L->d_h) * 1.4426950408889634 * (fp8 ? cd.k_scale : 1.0));
+    aa.v_scale = fp8 ? cd.v_scale : 1.f;
     std::vector<int64_t> keys(R);
     for (int r = 0; r < R; ++r) {
       const int64_t hi = c->len[r] + n[r] + B;
@@ -997,7 +1007,9 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
     aa.item_base[R] = (int32_t)items;
     if (items > p.max_items) e = hipErrorInvalidValue;  // cannot happen: bounded by construction
     if (e == hipSuccess)
-      e = staged(DFLASH_STAGE_ATTN, s, items > 0, [&] { return launch_attn_split(dt, aa, (int)items, s); });
+      e = staged(DFLASH_STAGE_ATTN, s, items > 0, [&] {
+        return fp8 ? launch_attn_fp8(aa, (int)items, s) : launch_attn_split(dt, aa, (int)items, s);
+      });
     if (e == hipSuccess) {
       CombineArgs ca{};
       ca.part_o = part_o; ca.part_ml = part_ml; ca.attn = attn;

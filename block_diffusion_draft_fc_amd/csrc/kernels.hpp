@@ -141,6 +141,8 @@ struct QkvEpiArgs {
   float eps;
   double inv_freq[64];   // RoPE w_i, i < d_h/2, computed in fp64 on the host
   SeqTable seq;
+  int32_t cache_fp8;     // 1: K/V go to the cache as E4M3 bytes of x / k_scale, x / v_scale
+  float k_scale, v_scale;
 };
 hipError_t launch_qkv_epilogue(int dtype, const QkvEpiArgs& a, hipStream_t s);
 
@@ -159,7 +161,8 @@ struct AttnArgs {
   int32_t rot;           // block order rotation multiplier (0: in order)
   int32_t nst;           // ring stages of the bf16 64-key-block kernel (2..4; 0: by item count)
   int32_t window;
-  float scale_log2;      // d_h^-0.5 * log2(e)
+  float scale_log2;      // d_h^-0.5 * log2(e) (times the key scale of an fp8 cache)
+  float v_scale;         // value scale of an fp8 cache (the fp8 kernel scales its partial O)
   int32_t item_base[kMaxSeqs + 1];  // items of sequence r: [item_base[r], item_base[r+1])
   int32_t chunks[kMaxSeqs];         // items per (sequence, K/V head)
   int32_t key_lo[kMaxSeqs];         // first key any query may see
@@ -167,6 +170,9 @@ struct AttnArgs {
   int32_t qpos0[kMaxSeqs];          // position of block row 0
 };
 hipError_t launch_attn_split(int dtype, const AttnArgs& a, int items, hipStream_t s);
+// bf16 queries over an fp8 (E4M3) cache, any d_h of 64 / 128 and up to four
+// 16-row query tiles; a.nst as for the bf16 64-key-block kernel.
+hipError_t launch_attn_fp8(const AttnArgs& a, int items, hipStream_t s);
 
 struct CombineArgs {
   const float* part_o;

@@ -9,7 +9,9 @@
 //     n + B new K rows take positions L .. L+n+B-1 (context rows first), the B
 //     queries the last B of them; pairs are (i, i + d_h/2) as in rotate_half.
 //   cache write: section 4 of the article, the rows enter the cache after the
-//     norm and the rotation.
+//     norm and the rotation.  An fp8 cache ("KV Cache + Speculative Decoding
+//     面试 Cheat Sheet" 2.1 and 4.5: one byte per element) takes the OCP E4M3
+//     byte nearest x / scale.
 //
 // One wavefront per (row, head); lane l < d_h/2 owns the rotation pair
 // (l, l + d_h/2).  Angles p * w_i are formed and reduced in fp64 (positions go
@@ -18,7 +20,15 @@
 
 namespace dflash {
 
-template <typename T>
+// The E4M3 byte nearest x (the conversion rounds to nearest even), magnitudes
+// beyond 448 clamped first so that they saturate whatever the conversion does
+// on overflow; NaN stays NaN.
+__device__ __forceinline__ uint8_t to_e4m3(float x) {
+  const float c = __builtin_isnan(x) ? x : fminf(fmaxf(x, -448.f), 448.f);
+  return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xff);
+}
+
+template <typename T, bool F8>
 __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvEpiArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -98,7 +108,19 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvEpiArgs a) {
   } else {
     const int64_t page = cache_page(a.cache, r, pos);
     const int slot = pos % a.cache.page_rows;
-    if (kind == 1) {
+    if constexpr (F8) {
+      const float sc = kind == 1 ? a.k_scale : a.v_scale;
+      const uint8_t c0 = to_e4m3(x0 / sc), c1 = to_e4m3(x1 / sc);
+      if (kind == 1) {
+        uint8_t* dst = static_cast<uint8_t*>(a.cache.k_pool) + k_offset(a.cache, page, head, slot);
+        dst[lane] = c0;
+        dst[lane + half] = c1;
+      } else {
+        uint8_t* dst = static_cast<uint8_t*>(a.cache.v_pool) + v_offset(a.cache, page, head, slot);
+        dst[lane * kVTile] = c0;
+        dst[(lane + half) * kVTile] = c1;
+      }
+    } else if (kind == 1) {
       T* dst = static_cast<T*>(a.cache.k_pool) + k_offset(a.cache, page, head, slot);
       dst[lane] = from_f32<T>(x0);
       dst[lane + half] = from_f32<T>(x1);
@@ -114,10 +136,12 @@ hipError_t launch_qkv_epilogue(int dtype, const QkvEpiArgs& a, hipStream_t s) {
   const int64_t items = (int64_t)a.R * a.B * a.n_h + 2 * (int64_t)(a.T + a.R * a.B) * a.n_kv;
   if (items == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((items + 3) / 4);
-  if (dtype == 1)
-    launch(qkv_epilogue_kernel<bf16>, dim3(blocks), dim3(256), 0, s, a);
+  if (dtype == 1 && a.cache_fp8)
+    launch(qkv_epilogue_kernel<bf16, true>, dim3(blocks), dim3(256), 0, s, a);
+  else if (dtype == 1)
+    launch(qkv_epilogue_kernel<bf16, false>, dim3(blocks), dim3(256), 0, s, a);
   else
-    launch(qkv_epilogue_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
+    launch(qkv_epilogue_kernel<float, false>, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

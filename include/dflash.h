@@ -25,9 +25,9 @@
  *     asynchronously on it; no call synchronises the device.
  *   - All arguments are validated on the host before anything is enqueued, so
  *     a call that returns an error has changed no state.
- *   - Storage dtype is DFLASH_F32 or DFLASH_BF16 for every tensor of a call;
- *     accumulation is always fp32.  Matrices are row-major, innermost
- *     dimension contiguous.
+ *   - Storage dtype is DFLASH_F32 or DFLASH_BF16 for every tensor of a call
+ *     (a BF16 layer may keep its cache in DFLASH_FP8_E4M3); accumulation is
+ *     always fp32.  Matrices are row-major, innermost dimension contiguous.
  *   - A cache handle is used from one stream at a time.  Calls that overlap on
  *     one workspace race.
  */
@@ -43,16 +43,18 @@ extern "C" {
 
 typedef enum {
   DFLASH_OK = 0,
-  DFLASH_ERR_ARG = -1,       /* null / misaligned pointer, bad handle, bad cu array */
+  DFLASH_ERR_ARG = -1,       /* null / misaligned pointer, bad handle, bad cu array, bad fp8 scale */
   DFLASH_ERR_SHAPE = -2,     /* unsupported or inconsistent sizes */
-  DFLASH_ERR_DTYPE = -3,     /* dtype not F32/BF16 or not matching the cache */
+  DFLASH_ERR_DTYPE = -3,     /* unsupported dtype, or a cache dtype the layer cannot use */
   DFLASH_ERR_RANGE = -4,     /* crop outside [0, current length]; window beyond a ring's rows */
   DFLASH_ERR_CAPACITY = -5,  /* sequence capacity, page table or page pool exhausted */
   DFLASH_ERR_HIP = -6,       /* a HIP runtime call or kernel launch failed */
   DFLASH_ERR_WORKSPACE = -7  /* workspace smaller than the *_ws_bytes figure */
 } dflash_status;
 
-typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
+/* DFLASH_FP8_E4M3 is a cache dtype only: one byte per K/V element, see the
+ * cache descriptor. */
+typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1, DFLASH_FP8_E4M3 = 2 } dflash_dtype;
 
 /* Limits of the library. */
 #define DFLASH_MAX_SEQS 64        /* requests per cache handle */
@@ -122,10 +124,21 @@ typedef struct dflash_layer_desc {
  * n_s + B <= capacity, and every key the window reaches still held
  * (max(0, L_s + n_s - window + 1) >= hw_s - capacity; else DFLASH_ERR_RANGE).
  * Crop is unchanged: it sets the length, and later appends overwrite slots.
+ *
+ * fp8 (dtype DFLASH_FP8_E4M3, for BF16 layers; "KV Cache + Speculative
+ * Decoding 面试 Cheat Sheet" 2.1 and 4.5: one byte per cached element instead
+ * of two): every pool element is an OCP FP8 E4M3 byte (sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits; no infinities, S.1111.111 is NaN, the largest
+ * value 448).  A key element x is stored as the E4M3 value nearest x / k_scale
+ * (ties to the even mantissa, magnitudes from 448 up saturated) and read as
+ * that value times k_scale; values use v_scale.  The pools take 1 byte per
+ * element in the same layouts; dflash_cache_append moves such bytes as they
+ * are.  Both scales must be finite and > 0 (else DFLASH_ERR_ARG); other
+ * dtypes ignore them.
  * ---------------------------------------------------------------------- */
 typedef struct dflash_cache_desc {
   int32_t n_seqs, n_kv, d_h;
-  int32_t dtype;
+  int32_t dtype;               /* DFLASH_F32, DFLASH_BF16 or DFLASH_FP8_E4M3 */
   int32_t page_size;
   int32_t max_pages_per_seq;   /* paged only */
   int32_t ring;                /* 0 or 1 (contiguous only): keep the last `capacity` positions */
@@ -133,6 +146,7 @@ typedef struct dflash_cache_desc {
   void *k_pool;
   void *v_pool;
   int32_t *block_table;        /* paged only, device */
+  float k_scale, v_scale;      /* DFLASH_FP8_E4M3 only */
 } dflash_cache_desc;
 
 typedef struct dflash_cache dflash_cache;
@@ -199,7 +213,10 @@ int dflash_cache_crop(dflash_cache *c, const int32_t *new_len, void *stream);
  * L_r + n_r to keep the accepted context).  Needs ws of at least
  * dflash_kv_inject_attn_ws_bytes(L, cache, T, B) bytes; the figure depends on
  * T, B and the handle's sizes, not on the current lengths, and holds for
- * every call with at most T context rows.
+ * every call with at most T context rows.  The cache dtype equals the layer
+ * dtype, or is DFLASH_FP8_E4M3 under a BF16 layer (else DFLASH_ERR_DTYPE):
+ * the new K/V rows are then stored as fp8 and attention reads every key and
+ * value as its fp8 value times the cache's scale.
  * ---------------------------------------------------------------------- */
 size_t dflash_kv_inject_attn_ws_bytes(const dflash_layer_desc *L, const dflash_cache *c,
                                       int64_t T, int32_t B);

@@ -404,6 +404,10 @@ class OracleStack:
         self.kv_scales = kv_scales
         self.K = [[f64(k) for k in row] for row in K0]
         self.V = [[f64(v) for v in row] for row in V0]
+        # fp8 caches: the values of the cached rows before storage (the given
+        # rows for K0, V0), to tell where a rounding decision was close
+        self.Kx = [[k.copy() for k in row] for row in self.K] if kv_scales else None
+        self.Vx = [[v.copy() for v in row] for row in self.V] if kv_scales else None
 
     def lengths(self, layer: int = 0):
         return [k.shape[1] for k in self.K[layer]]
@@ -426,6 +430,10 @@ class OracleStack:
                 out_l[r * B:(r + 1) * B] = res.out
                 n = cu[r + 1] - cu[r]
                 self.K[li][r], self.V[li][r] = crop(res.K, res.V, L + n)
+                if self.kv_scales:
+                    self.Kx[li][r], self.Vx[li][r] = crop(np.concatenate([self.Kx[li][r], res.k_exact], axis=1),
+                                                          np.concatenate([self.Vx[li][r], res.v_exact], axis=1),
+                                                          L + n)
                 res_l.append(res)
             outs.append(out_l)
             last = res_l

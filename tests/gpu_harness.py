@@ -53,23 +53,26 @@ class GpuModel:
                                        rope_theta=wl.rope_theta, window=wl.layer_window(li),
                                        residual=wl.n_layers > 1))
             need = [int(self.L0[r] + grow[r] + wl.B) for r in range(wl.R)]
+            cdt = torch.float8_e4m3fn if wl.kv_dtype == "fp8" else self.dtype
+            sc = dict(k_scale=wl.k_scale, v_scale=wl.v_scale)
             if wl.ring_capacity(li):
-                self.caches.append(L.Cache(wl.R, wl.n_kv, wl.d_h, self.dtype, wl.ring_capacity(li), 0, 0, device,
-                                           ring=True))
+                self.caches.append(L.Cache(wl.R, wl.n_kv, wl.d_h, cdt, wl.ring_capacity(li), 0, 0, device,
+                                           ring=True, **sc))
             elif wl.page_size:
                 ps = wl.page_size
                 pages = sum(-(-x // ps) for x in need) + wl.R
                 maxp = max(-(-x // ps) for x in need) + 1
-                self.caches.append(L.Cache(wl.R, wl.n_kv, wl.d_h, self.dtype, pages, ps, maxp, device))
+                self.caches.append(L.Cache(wl.R, wl.n_kv, wl.d_h, cdt, pages, ps, maxp, device, **sc))
             else:
                 cap = _round_up(max(need), 64)
-                self.caches.append(L.Cache(wl.R, wl.n_kv, wl.d_h, self.dtype, cap, 0, 0, device))
+                self.caches.append(L.Cache(wl.R, wl.n_kv, wl.d_h, cdt, cap, 0, 0, device, **sc))
         max_T = int(sched.sum(axis=1).max()) if rounds else 0
         self.driver = DraftRound(self.w_fc, self.gamma_h, wl.eps, self.layers, self.caches, wl.B,
                                  max(max_T, 1), device)
 
     def prefill(self, kv_host):
-        """kv_host[l][r] = (K, V) [n_kv, L_r, d_h] float32 storage values; appended
+        """kv_host[l][r] = (K, V) [n_kv, L_r, d_h] float32 storage values (uint8
+        E4M3 codes for fp8 caches); appended
         through dflash_cache_append (one call per layer and all requests; a ring
         takes them in calls of at most its capacity rows per request)."""
         for li, cache in enumerate(self.caches):
@@ -84,8 +87,12 @@ class GpuModel:
                     cu.append(cu[-1] + ks[-1].shape[0])
                 if cu[-1] == 0:
                     continue
-                kd = to_device(np.concatenate(ks, axis=0), self.wl)
-                vd = to_device(np.concatenate(vs, axis=0), self.wl)
+                if cache.fp8:
+                    kd = torch.from_numpy(np.concatenate(ks, axis=0)).to("cuda")
+                    vd = torch.from_numpy(np.concatenate(vs, axis=0)).to("cuda")
+                else:
+                    kd = to_device(np.concatenate(ks, axis=0), self.wl)
+                    vd = to_device(np.concatenate(vs, axis=0), self.wl)
                 L.dflash_cache_append(cache, cu, kd, vd)
         torch.cuda.synchronize()
 
@@ -98,9 +105,44 @@ class GpuModel:
 
 
 def prefill_host(wl):
-    """Seeded cache content before round 0, per layer and request."""
+    """Seeded cache content before round 0, per layer and request (E4M3 codes
+    for fp8 caches)."""
     L0 = G.prefill_lengths(wl)
-    return [[G.prefill_kv(wl, li, r, int(L0[r])) for r in range(wl.R)] for li in range(wl.n_layers)]
+    draw = G.prefill_kv_fp8 if wl.kv_dtype == "fp8" else G.prefill_kv
+    return [[draw(wl, li, r, int(L0[r])) for r in range(wl.R)] for li in range(wl.n_layers)]
+
+
+def kv_values(wl, k, v):
+    """The values a cache holds for stored rows (codes times the scales for
+    fp8 caches, else the stored values)."""
+    if wl.kv_dtype == "fp8":
+        return O.e4m3_decode(k) * wl.k_scale, O.e4m3_decode(v) * wl.v_scale
+    return k, v
+
+
+def check_fp8_codes(got, exact, scale, what):
+    """Codes an fp8 cache holds for layer-written rows against the oracle's
+    values before storage.  The GPU quantises values computed from its bf16
+    context rows C: each element of C is off by up to 2^-9 of itself, so a
+    projected element x_j = sum_i C_i W_ji is off by about 2^-9 / sqrt(3) of the
+    RMS of x (1.13e-3 RMS, one standard deviation; the per-head norm of K
+    keeps that ratio).  Let t = 8e-3 RMS (7 standard deviations).  A code that
+    is the nearest E4M3 code of some x' within t of x = exact / scale lies
+    within |nearest(x) - x| + 2 t of x, which is what every code must meet;
+    at most 10% of codes may differ from nearest(x) (about 4% expected for
+    N(0, 1) rows).  Returns the count of such codes."""
+    got = np.asarray(got).astype(np.uint8)
+    x = np.asarray(exact, dtype=np.float64) / scale
+    want = O.e4m3_encode(x)
+    a, b = O.e4m3_decode(got), O.e4m3_decode(want)
+    bad = a != b                       # +0 and -0 are the same value
+    if not bad.any():
+        return 0
+    t = 8e-3 * float(np.sqrt(np.mean(x * x)))
+    ok = np.abs(a[bad] - x[bad]) <= np.abs(b[bad] - x[bad]) + 2 * t
+    assert np.all(ok), f"{what}: {int((~ok).sum())} of {bad.size} codes off the nearest value"
+    assert bad.mean() <= 0.10, f"{what}: {int(bad.sum())} codes of {bad.size} not the nearest"
+    return int(bad.sum())
 
 
 def oracle_stack(wl, kv_host):
@@ -111,9 +153,10 @@ def oracle_stack(wl, kv_host):
         layers.append(O.LayerParams(lw["w_qkv"].astype(np.float64), lw["w_o"].astype(np.float64),
                                     lw["gamma_q"], lw["gamma_k"], wl.n_h, wl.n_kv, wl.d_h, wl.eps,
                                     wl.rope_theta, wl.layer_window(li)))
-    K0 = [[kv_host[li][r][0] for r in range(wl.R)] for li in range(wl.n_layers)]
-    V0 = [[kv_host[li][r][1] for r in range(wl.R)] for li in range(wl.n_layers)]
-    return O.OracleStack(layers, fc["w_fc"].astype(np.float64), fc["gamma_h"], wl.eps, K0, V0)
+    K0 = [[kv_values(wl, *kv_host[li][r])[0] for r in range(wl.R)] for li in range(wl.n_layers)]
+    V0 = [[kv_values(wl, *kv_host[li][r])[1] for r in range(wl.R)] for li in range(wl.n_layers)]
+    scales = (wl.k_scale, wl.v_scale) if wl.kv_dtype == "fp8" else None
+    return O.OracleStack(layers, fc["w_fc"].astype(np.float64), fc["gamma_h"], wl.eps, K0, V0, scales)
 
 
 def v_rows_view(vp):

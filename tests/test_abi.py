@@ -35,9 +35,10 @@ int main(void) {
   printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(dflash_layer_desc), offsetof(dflash_layer_desc, eps),
          offsetof(dflash_layer_desc, rope_theta), offsetof(dflash_layer_desc, window),
          offsetof(dflash_layer_desc, residual), offsetof(dflash_layer_desc, gamma_k));
-  printf("%zu %zu %zu %zu %zu\\n", sizeof(dflash_cache_desc), offsetof(dflash_cache_desc, capacity),
+  printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(dflash_cache_desc), offsetof(dflash_cache_desc, capacity),
          offsetof(dflash_cache_desc, k_pool), offsetof(dflash_cache_desc, block_table),
-         offsetof(dflash_cache_desc, ring));
+         offsetof(dflash_cache_desc, ring), offsetof(dflash_cache_desc, k_scale),
+         offsetof(dflash_cache_desc, v_scale));
   return 0;
 }""")
     exe = tmp_path / "layout"
@@ -47,12 +48,14 @@ int main(void) {
     assert [int(x) for x in lines[0].split()] == [C.sizeof(ld), ld.eps.offset, ld.rope_theta.offset,
                                                   ld.window.offset, ld.residual.offset, ld.gamma_k.offset]
     assert [int(x) for x in lines[1].split()] == [C.sizeof(cd), cd.capacity.offset, cd.k_pool.offset,
-                                                  cd.block_table.offset, cd.ring.offset]
+                                                  cd.block_table.offset, cd.ring.offset, cd.k_scale.offset,
+                                                  cd.v_scale.offset]
 
 
-def _cache(n_seqs=2, page_size=0, capacity=128, max_pages=0, dtype=L.DFLASH_BF16, ring=0):
+def _cache(n_seqs=2, page_size=0, capacity=128, max_pages=0, dtype=L.DFLASH_BF16, ring=0, k_scale=1.0,
+           v_scale=1.0):
     desc = L.CacheDesc(n_seqs, 2, 64, dtype, page_size, max_pages, ring, capacity, FAKE, FAKE,
-                       FAKE if page_size else None)
+                       FAKE if page_size else None, k_scale, v_scale)
     h = C.c_void_p()
     rc = L.LIB.dflash_cache_init(C.byref(h), C.byref(desc))
     return rc, h
@@ -73,10 +76,18 @@ def test_strerror_table():
     (dict(dtype=7), L.ERR_DTYPE),
     (dict(page_size=64, capacity=4, max_pages=4, ring=1), L.ERR_SHAPE),   # rings are contiguous only
     (dict(ring=2), L.ERR_SHAPE),
+    (dict(dtype=L.DFLASH_FP8_E4M3, k_scale=0.0), L.ERR_ARG),     # fp8 scales finite and > 0
+    (dict(dtype=L.DFLASH_FP8_E4M3, v_scale=-1.0), L.ERR_ARG),
+    (dict(dtype=L.DFLASH_FP8_E4M3, v_scale=float("nan")), L.ERR_ARG),
+    (dict(dtype=L.DFLASH_FP8_E4M3, k_scale=float("inf")), L.ERR_ARG),
+    (dict(dtype=L.DFLASH_BF16, k_scale=0.0), L.DFLASH_OK),       # other dtypes ignore the scales
+    (dict(dtype=L.DFLASH_FP8_E4M3, k_scale=0.5, v_scale=3.0), L.DFLASH_OK),
 ])
 def test_cache_init_rejects(kw, code):
-    rc, _ = _cache(**kw)
+    rc, h = _cache(**kw)
     assert rc == code
+    if rc == L.DFLASH_OK:
+        L.LIB.dflash_cache_destroy(h)
 
 
 def test_cache_host_metadata_and_errors():
@@ -163,6 +174,23 @@ def test_kv_inject_validation():
         lens = (C.c_int32 * 2)()
         L.LIB.dflash_cache_lengths(h, lens)
         assert list(lens) == [0, 0]
+    finally:
+        L.LIB.dflash_cache_destroy(h)
+
+
+def test_fp8_cache_needs_a_bf16_layer():
+    rc, h = _cache(n_seqs=2, capacity=128, dtype=L.DFLASH_FP8_E4M3, k_scale=0.25, v_scale=2.0)
+    assert rc == 0
+    try:
+        f = L.LIB.dflash_kv_inject_attn
+        good = _layer()
+        wsb = L.LIB.dflash_kv_inject_attn_ws_bytes(C.byref(good), h, 8, 4)
+        assert wsb > 0
+        cu = L._i32([0, 4, 8])
+        args = lambda lay, ws=wsb: (C.byref(lay), h, FAKE, cu, FAKE, 4, FAKE, FAKE, ws, None)  # noqa: E731
+        assert f(*args(_layer(dtype=L.DFLASH_F32))) == L.ERR_DTYPE
+        assert f(*args(_layer(dtype=L.DFLASH_FP8_E4M3))) == L.ERR_DTYPE     # not a layer dtype
+        assert f(*args(good, ws=wsb - 1)) == L.ERR_WORKSPACE                 # past the dtype checks
     finally:
         L.LIB.dflash_cache_destroy(h)
 

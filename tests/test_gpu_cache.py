@@ -1,7 +1,7 @@
 """GPU cache append / crop against the integer cache model, bit for bit.
 
-Random sequences of appends and crops (contiguous and paged caches, 16- and
-32-bit words, payloads that include NaN and infinity bit patterns) go through
+Random sequences of appends and crops (contiguous, paged and ring caches, 8-,
+16- and 32-bit words, payloads that include NaN and infinity bit patterns) go through
 dflash_cache_append / dflash_cache_crop and through oracle.cache_model; after
 every operation the whole K and V pools, the lengths, the page tables (host
 and device) and the free-page count must be identical.
@@ -31,12 +31,18 @@ CASES = [
     # largest appends, which must fail on both sides
     ("ring_bf16", 3, 2, 64, 0, 128, 0, np.uint16, True),
     ("ring_f32_dh128", 2, 1, 128, 0, 64, 0, np.uint32, True),
+    # fp8 (E4M3) caches move single bytes, NaN codes included
+    ("contig_fp8", 3, 2, 64, 0, 320, 0, np.uint8, False),
+    ("paged64_fp8_dh128", 3, 4, 128, 64, 10, 5, np.uint8, False),
+    ("ring_fp8", 2, 2, 64, 0, 128, 0, np.uint8, True),
 ]
+
+_TORCH = {np.uint8: (torch.float8_e4m3fn, torch.uint8, np.uint8), np.uint16: (torch.bfloat16, torch.int16, np.int16),
+          np.uint32: (torch.float32, torch.int32, np.int32)}
 
 
 def _device_bits(t, word):
-    it = torch.int16 if word == np.uint16 else torch.int32
-    return t.view(it).cpu().numpy().view(word)
+    return t.view(_TORCH[word][1]).cpu().numpy().view(word)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
@@ -45,11 +51,12 @@ def test_random_append_crop_sequences(case, seed):
     name, n_seqs, n_kv, d_h, ps, cap, maxp, word, ring = case
     say(f"case cache {name} seed={seed}")
     rng = np.random.default_rng(1000 + seed)
-    tdt = torch.bfloat16 if word == np.uint16 else torch.float32
+    tdt, bits_t, bits_np = _TORCH[word]
     cache = L.Cache(n_seqs, n_kv, d_h, tdt, cap, ps, maxp, "cuda", ring=ring)
     model = CacheModel(n_seqs, n_kv, d_h, ps, cap, maxp, word=word, ring=ring)
-    special = np.array([0x7FC0, 0xFF80, 0x7F80, 0x0001, 0x8000] if word == np.uint16 else
-                       [0x7FC00001, 0xFF800000, 0x7F800000, 0x00000001, 0x80000000], dtype=word)
+    special = np.array({np.uint8: [0x7F, 0xFF, 0x80, 0x01, 0x7E],
+                        np.uint16: [0x7FC0, 0xFF80, 0x7F80, 0x0001, 0x8000],
+                        np.uint32: [0x7FC00001, 0xFF800000, 0x7F800000, 0x00000001, 0x80000000]}[word], dtype=word)
     for step in range(40):
         if rng.random() < 0.6:
             n = rng.integers(0, 90, size=n_seqs)
@@ -60,8 +67,11 @@ def test_random_append_crop_sequences(case, seed):
             if rows:
                 k.reshape(-1)[: special.size] = special
                 v.reshape(-1)[-special.size:] = special
-            kd = torch.from_numpy(k.view(np.int16 if word == np.uint16 else np.int32)).to("cuda").view(tdt)
-            vd = torch.from_numpy(v.view(np.int16 if word == np.uint16 else np.int32)).to("cuda").view(tdt)
+            # fp8 caches take their codes as uint8 tensors
+            kd = torch.from_numpy(k.view(bits_np)).to("cuda")
+            vd = torch.from_numpy(v.view(bits_np)).to("cuda")
+            if word != np.uint8:
+                kd, vd = kd.view(tdt), vd.view(tdt)
             try:
                 model.append(cu, k, v)
                 expect = 0

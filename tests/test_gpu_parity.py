@@ -32,7 +32,8 @@ from oracle import dflash_oracle as O  # noqa: E402
 from workloads import configs, generate as G  # noqa: E402
 from workloads.device import from_device, to_device  # noqa: E402
 
-from gpu_harness import TOL, GpuModel, cache_rows, oracle_stack, prefill_host, rel_l2, ring_rows, say  # noqa: E402
+from gpu_harness import (TOL, GpuModel, cache_rows, check_fp8_codes, oracle_stack, prefill_host,  # noqa: E402
+                         rel_l2, ring_rows, say)
 
 
 def run_rounds(wl, rounds, check_cache=True):
@@ -84,7 +85,11 @@ def run_rounds(wl, rounds, check_cache=True):
                 assert np.array_equal(K[:, :max(0, n0 - lo)], Kp[:, lo:n0].astype(np.float64))
                 assert np.array_equal(V[:, :max(0, n0 - lo)], Vp[:, lo:n0].astype(np.float64))
                 a = max(n0, lo)
-                if K.shape[1] + lo > a:
+                if K.shape[1] + lo > a and wl.kv_dtype == "fp8":
+                    # codes: the nearest E4M3 value of the oracle's row / scale
+                    check_fp8_codes(K[:, a - lo:], orc.Kx[li][r][:, a:], wl.k_scale, f"layer {li} seq {r} K")
+                    check_fp8_codes(V[:, a - lo:], orc.Vx[li][r][:, a:], wl.v_scale, f"layer {li} seq {r} V")
+                elif K.shape[1] + lo > a:
                     assert rel_l2(K[:, a - lo:], orc.K[li][r][:, a:]) <= TOL[wl.dtype]
                     assert rel_l2(V[:, a - lo:], orc.V[li][r][:, a:]) <= TOL[wl.dtype]
     say(f"  worst rel-L2 {worst:.3e}")
@@ -293,6 +298,59 @@ SMALL = [
 
 @pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
 def test_small_case(wl):
+    run_rounds(wl, wl.rounds)
+
+
+# ------------------------------------------------------------------ fp8 (E4M3) caches
+
+def _fp8(name, **kw):
+    base = dict(kv_dtype="fp8", k_scale=1.5, v_scale=0.5)
+    base.update(kw)
+    return _small("fp8_" + name, **base)
+
+
+# every query-tile count and head dim of the fp8 kernel, ragged tails, empty
+# caches, windows, paged and ring caches, stacks, and scales that are and are
+# not powers of two
+SMALL_FP8 = [
+    _fp8("dh64_g4_b4_one_qtile"),
+    _fp8("dh64_g4_b5_two_qtiles", B=5),
+    _fp8("dh64_g8_b6_three_qtiles", n_h=16, n_kv=2, B=6),
+    _fp8("dh64_g16_b4_four_qtiles", n_h=16, n_kv=1, B=4),
+    _fp8("dh128_g4_b16", n_h=8, n_kv=2, d_h=128, B=16),
+    _fp8("dh128_g3_b16_three_qtiles", n_h=12, n_kv=4, d_h=128, B=16, prefill_len=1000),
+    _fp8("dh128_b1", n_h=8, n_kv=2, d_h=128, B=1),
+    _fp8("empty_cache_single_key", prefill="none", n_new="fixed", n_fixed=0, B=1, rounds=1),
+    _fp8("empty_cache_dh128", prefill="none", n_new="fixed", n_fixed=5, d_h=128, B=16, rounds=2),
+    _fp8("long_cache_ragged_tail", prefill_len=2999, d_h=128, n_h=8, n_kv=2, B=16, rounds=2),
+    _fp8("window_100", d_h=128, B=16, prefill_len=500, window=100, sliding_layers=(0,)),
+    _fp8("ragged_paged_r5", R=5, d_h=128, B=16, prefill="uniform", prefill_range=(0, 700), n_range=(0, 16),
+         page_size=64, rounds=4),
+    _fp8("ring_window_100", d_h=128, B=16, prefill_len=500, window=100, sliding_layers=(0,), ring=True, rounds=6),
+    _fp8("stack3_window_residual", n_layers=3, d_h=128, B=16, R=2, prefill_len=600, window=256,
+         sliding_layers=(0, 2), rounds=3),
+    _fp8("scales_pow2", d_h=128, B=16, prefill_len=800, k_scale=0.25, v_scale=4.0),
+    _fp8("scales_tiny_values", d_h=128, B=16, prefill_len=800, k_scale=8.0, v_scale=16.0),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL_FP8, ids=[w.name for w in SMALL_FP8])
+def test_fp8_cache_small_case(wl):
+    run_rounds(wl, wl.rounds)
+
+
+def test_fp8_cache_decode_8k():
+    """The decode workload with an fp8 cache: 16 rounds on the 8192-row cache
+    (one query tile group of 64 rows per K/V head, d_h 128)."""
+    wl = configs.DECODE_8K.scaled(name="decode_ctx8k_fp8_cache", kv_dtype="fp8", k_scale=1.0, v_scale=1.0)
+    run_rounds(wl, 16)
+
+
+def test_fp8_cache_full_attention_layer_4x32k():
+    """A full-attention layer of the stack at its full size over fp8 caches:
+    4 requests on 32768-row caches (one round of 512 items, two-deep plan)."""
+    wl = configs.STACK5_HYBRID.scaled(name="full_attention_layer_ctx32k_batch4_fp8", n_layers=1,
+                                      sliding_layers=(), rounds=1, kv_dtype="fp8", k_scale=1.5, v_scale=0.5)
     run_rounds(wl, wl.rounds)
 
 

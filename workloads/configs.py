@@ -48,6 +48,11 @@ class Workload:
     ring: bool = False
     eps: float = 1e-6
     rope_theta: float = 1e6
+    # cache element type: "same" as the layer, or "fp8" (E4M3 bytes read as
+    # value * k_scale / v_scale; bf16 layers only)
+    kv_dtype: str = "same"
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     @property
     def kd(self) -> int:

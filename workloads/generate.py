@@ -26,7 +26,7 @@ from .configs import Workload
 
 # stream tags
 (_FC, _LAYER, _PREFILL_KV, _PREFILL_LEN, _SCHED, _RAW, _ANCHOR, _MASK, _H_IID, _HEAD, _HEAD_IN,
- _ACCEPT) = range(1, 13)
+ _ACCEPT, _PREFILL_FP8) = range(1, 14)
 
 
 def _rng(seed: int, *tags: int) -> np.random.Generator:
@@ -103,6 +103,21 @@ def prefill_kv(wl: Workload, layer: int, r: int, L: int):
     k = _normal(g, (wl.n_kv, L, wl.d_h))
     v = _normal(g, (wl.n_kv, L, wl.d_h))
     return _store(k, wl), _store(v, wl)
+
+
+def prefill_kv_fp8(wl: Workload, layer: int, r: int, L: int):
+    """Cache rows of request r before round 0 for an fp8 cache, drawn directly
+    as E4M3 bytes (no arithmetic on them here): sign bit and 3 mantissa bits
+    uniform, exponent field uniform over 4..8, i.e. magnitudes 1/8 .. 3.75
+    before the cache's scale.  Returns uint8 K, V codes [n_kv, L, d_h]."""
+    g = _rng(wl.seed, _PREFILL_FP8, layer, r)
+
+    def codes():
+        sign = g.integers(0, 2, size=(wl.n_kv, L, wl.d_h)) << 7
+        expo = g.integers(4, 9, size=(wl.n_kv, L, wl.d_h)) << 3
+        mant = g.integers(0, 8, size=(wl.n_kv, L, wl.d_h))
+        return (sign | expo | mant).astype(np.uint8)
+    return codes(), codes()
 
 
 def schedule(wl: Workload) -> np.ndarray:
