@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--no-batched", action="store_true",
                     help="skip the attention-at-scale pass, the draft head, the acceptance, the ragged 16-request "
                          "and the 5-layer hybrid stack rounds")
+    ap.add_argument("--attn-pass", metavar="R,CTX,KV",
+                    help="only time the attention kernel for R requests of CTX cached keys with a KV "
+                         "(bf16 or fp8) cache, print its JSON and exit (for profiling one kernel)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 8 times (scales HBM counters)")
     return ap.parse_args()
@@ -323,14 +326,16 @@ def batched_rounds(wl, rounds, ring=False):
 
 # ---------------------------------------------------------------------------- attention at scale
 
-def attn_at_scale(iters):
-    """The attention kernel on the full-attention layer shape of the 5-layer
-    stack: 4 requests x 32768 cached keys, 8 new context rows and a block of 16
-    each, Qwen3-8B heads (32/8, d_h 128), contiguous bf16 cache.  Every call
-    appends its rows, attends and is cropped back, so each reads the same
-    4 x 32792 keys per K/V head (537 MB).  The attention stage's time comes
-    from the library's HIP events on the launch stream; K/V rows are N(0,1)
-    drawn on the device."""
+def attn_pass(iters, R=4, ctx=32768, kv="bf16"):
+    """The attention kernel on the Qwen3-8B head shape (32/8 heads of 128, d
+    4096) for R requests with `ctx` cached keys each, 8 new context rows and a
+    block of 16: every call appends its rows, attends and is cropped back, so
+    each reads the same R x (ctx + 24) keys per K/V head.  R = 4, ctx = 32768
+    is the full-attention layer of the 5-layer stack (537 MB in bf16); R = 1,
+    ctx = 8192 the decode workload's cache.  kv "fp8" keeps the cache as E4M3
+    bytes (scales 1), half the bytes.  The attention stage's time comes from
+    the library's HIP events on the launch stream; K/V rows are N(0,1) drawn
+    on the device (cast to E4M3 by torch for the fp8 cache)."""
     import torch
 
     from block_diffusion_draft_fc_amd import _lib as L
@@ -339,18 +344,22 @@ def attn_at_scale(iters):
 
     wl = configs.STACK5_HYBRID
     dev = "cuda:0"
-    R, ctx, n, B = wl.R, wl.prefill_len, 8, wl.B
+    n, B = 8, wl.B
     li = next(i for i in range(wl.n_layers) if not wl.layer_window(i))
     lw = G.layer_weights(wl, li)
     layer = L.Layer(*(to_device(lw[k], wl, dev) for k in ("w_qkv", "w_o", "gamma_q", "gamma_k")),
                     n_h=wl.n_h, n_kv=wl.n_kv, d_h=wl.d_h, eps=wl.eps, rope_theta=wl.rope_theta)
     cap = (ctx + 1024 + 63) // 64 * 64
-    cache = L.Cache(R, wl.n_kv, wl.d_h, torch.bfloat16, cap, 0, 0, dev)
+    fp8 = kv == "fp8"
+    cache = L.Cache(R, wl.n_kv, wl.d_h, torch.float8_e4m3fn if fp8 else torch.bfloat16, cap, 0, 0, dev)
     g = torch.Generator(device=dev).manual_seed(wl.seed)
-    k = torch.randn((R * ctx, wl.n_kv, wl.d_h), device=dev, generator=g).to(torch.bfloat16)
-    v = torch.randn((R * ctx, wl.n_kv, wl.d_h), device=dev, generator=g).to(torch.bfloat16)
-    L.dflash_cache_append(cache, [r * ctx for r in range(R + 1)], k, v)
-    del k, v
+    rows = []
+    for _ in range(2):
+        t = torch.randn((R * ctx, wl.n_kv, wl.d_h), device=dev, generator=g)
+        rows.append(t.to(torch.float8_e4m3fn).view(torch.uint8) if fp8 else t.to(torch.bfloat16))
+        del t
+    L.dflash_cache_append(cache, [r * ctx for r in range(R + 1)], rows[0], rows[1])
+    del rows
     C = torch.randn((R * n, wl.d), device=dev, generator=g).to(torch.bfloat16)
     H = torch.randn((R * B, wl.d), device=dev, generator=g).to(torch.bfloat16)
     out = torch.empty((R * B, wl.d), dtype=torch.bfloat16, device=dev)
@@ -372,12 +381,15 @@ def attn_at_scale(iters):
     st = L.timing_read()
     L.timing_enable(False)
     keys = ctx + n + B
-    alg = R * keys * wl.n_kv * wl.d_h * 2 * 2 + R * B * wl.n_h * wl.d_h * 2
+    eb = 1 if fp8 else 2
+    alg = R * keys * wl.n_kv * wl.d_h * eb * 2 + R * B * wl.n_h * wl.d_h * 2
     us = st["attn"][1] * 1e3 / st["attn"][0]
     gbps = alg / (us * 1e-6) / 1e9
-    res = {"shape": f"{R} requests x {keys} keys, GQA {wl.n_h}/{wl.n_kv}, d_h {wl.d_h}, block {B}, bf16",
+    res = {"shape": f"{R} requests x {keys} keys, GQA {wl.n_h}/{wl.n_kv}, d_h {wl.d_h}, block {B}, "
+                    f"{'fp8 E4M3' if fp8 else 'bf16'} cache",
            "launches": st["attn"][0], "us_per_launch": round(us, 2), "alg_bytes_per_launch": int(alg),
            "gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+           "keys_per_us": round(R * keys / us, 1),
            "combine_us": round(st["attn_combine"][1] * 1e3 / st["attn_combine"][0], 2)}
     del cache, layer, C, H, out, ws
     torch.cuda.empty_cache()
@@ -475,6 +487,13 @@ def main():
 
     if args.copy_calibration:
         return copy_calibration()
+    if args.attn_pass:
+        R, ctx, kv = args.attn_pass.split(",")
+        if kv not in ("bf16", "fp8"):
+            print("--attn-pass: KV is bf16 or fp8", file=sys.stderr)
+            return 2
+        print(json.dumps(attn_pass(60, int(R), int(ctx), kv)), flush=True)
+        return 0
 
     import torch
 
@@ -676,7 +695,11 @@ def main():
         res["fresh_ctx_projections"] = fresh_ctx_projections(20)
     if not args.no_batched:
         log("bench: attention kernel on the stack's full-attention layer shape")
-        res["attn_at_scale"] = attn_at_scale(30)
+        res["attn_at_scale"] = attn_pass(30, 4, 32768, "bf16")
+        log("bench: attention over fp8 caches")
+        res["fp8_kv_cache"] = {"ctx8k_batch1": attn_pass(60, 1, 8192, "fp8"),
+                               "ctx8k_batch1_bf16_same_harness": attn_pass(60, 1, 8192, "bf16"),
+                               "ctx32k_batch4": attn_pass(30, 4, 32768, "fp8")}
         log("bench: draft head (lm_head over the Qwen3 vocabulary)")
         res["draft_head"] = draft_head_pass(20)
         log("bench: acceptance of a 16-request round")

@@ -295,9 +295,11 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_fp8_kernel(AttnArgs a) {
 }
 
 // Ring depth: the host plans for the bf16 kernel's depths (3 stages of 32 KB:
-// one workgroup per CU; 2: two per CU).  fp8 stages are half as large, so the
-// same bytes stay in flight with twice the blocks ahead: 3 -> 5 stages (80 KB,
-// one workgroup per CU), 2 -> 3 (48 KB).  DFLASH_ATTN_FP8_NST overrides.
+// one workgroup per CU; 2: two per CU).  fp8 stages are half as large: plan 2
+// takes 3 stages (48 KB, two or three workgroups per CU), plan 3 takes 4
+// (64 KB).  Deeper rings measured no faster on the 8K decode cache (5 to 7
+// stages: 13.5-15 us against 13.0-13.5) and slower on four 32K caches (they
+// leave one workgroup per CU).  DFLASH_ATTN_FP8_NST overrides.
 hipError_t launch_attn_fp8(const AttnArgs& a, int items, hipStream_t s) {
   if (items == 0) return hipSuccess;
   if ((a.qrows + 15) / 16 > 4) return hipErrorInvalidValue;
@@ -307,7 +309,7 @@ hipError_t launch_attn_fp8(const AttnArgs& a, int items, hipStream_t s) {
     return v >= 2 && v <= 7 ? v : 0;
   }();
   const int plan = a.nst > 0 ? a.nst : items <= 256 ? 3 : 2;
-  const int nst = forced ? forced : plan >= 3 ? 5 : 3;
+  const int nst = forced ? forced : plan >= 3 ? 4 : 3;
 #define DFLASH_FP8_CASE(DH_, NST_)                                                 \
   if (a.d_h == DH_ && nst == NST_) {                                               \
     launch((attn_ring64_fp8_kernel<DH_, NST_>), dim3(items), dim3(256), 0, s, a); \
