@@ -683,7 +683,7 @@ def main():
         "attn_hbm_gbps": att["gbps"],
         "attn_hbm_frac_peak": att["hbm_frac"],
         "roofline": {"bound": "hbm", "achieved": att["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": att["hbm_frac"], "traffic": traffic_record(), "kernel": "attn_ring64_kernel<128,3> (split-context attention, 3-stage ring)",
+                     "frac": att["hbm_frac"], "traffic": traffic_record(), "kernel": "attn_ring64_kernel<128,4,2> (split-context attention, two wave groups, 4-stage ring)",
                      "us_per_launch": att["us_per_launch"], "alg_bytes_per_launch": att["alg_bytes_per_launch"]},
         "round_alg_bytes": int(round_bytes),
         "round_hbm_gbps": round(round_bytes / (ms_per_step * 1e-3) / 1e9, 1),

@@ -177,6 +177,17 @@ class Cache:
 
 
 def dflash_cache_append(cache: Cache, cu_rows, k_rows, v_rows, stream=None) -> None:
+    """k_rows, v_rows: [rows, n_kv, d_h] device tensors of the cache's element
+    size (E4M3 bytes as uint8 or float8_e4m3fn for fp8 caches).  The sizes are
+    checked here: the C call can only trust its pointers."""
+    rows = int(cu_rows[-1])
+    if rows:
+        esize = 1 if cache.fp8 else torch.empty((), dtype=cache.dtype).element_size()
+        need = rows * cache.n_kv * cache.d_h
+        for t in (k_rows, v_rows):
+            if t is None or t.element_size() != esize or t.numel() < need:
+                raise DFlashError(ERR_ARG, "dflash_cache_append: k_rows / v_rows must hold "
+                                           f"[{rows}, {cache.n_kv}, {cache.d_h}] elements of {esize} byte(s)")
     _check(LIB.dflash_cache_append(cache.handle, _i32(cu_rows), _ptr(k_rows), _ptr(v_rows), _stream(stream)),
            "dflash_cache_append")
 

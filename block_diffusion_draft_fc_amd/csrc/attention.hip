@@ -887,10 +887,16 @@ __global__ __launch_bounds__(256, 1) void attn_ring_kernel(AttnArgs a) {
 // The queries travel as direct copies too, ahead of the first blocks', into
 // the last stage (free until the loop's first refill of it): their latency
 // overlaps the blocks' instead of preceding it.
-template <int DH, int NST>
-__global__ __launch_bounds__(256, 1) void attn_ring64_kernel(AttnArgs a) {
+// NG = 2 doubles the workgroup to two groups of four waves, wave w taking
+// query tile w % 4 in group w / 4; group g processes blocks g, g + 2, ..., so
+// an item's chain of dependent blocks is half as long, and at the end group 1
+// hands its (m, l, O) to group 0 through LDS for an exact merge.  The ring
+// then holds the two blocks in work plus NST - 2 in flight.
+template <int DH, int NST, int NG = 1>
+__global__ __launch_bounds__(256 * NG, 1) void attn_ring64_kernel(AttnArgs a) {
   using V8 = bf16x8;
   static_assert(NST >= 2 && NST <= 8, "blocks in flight are counted by wait_vm_blocks (up to 6 after the current)");
+  static_assert((NG == 1 || NG == 2) && NST >= 2 * NG, "a step's blocks are issued by the end of the step before");
   constexpr int DS = DH / 32;                 // K=32 steps over the head dim
   constexpr int DT = DH / 16;                 // 16-dim tiles of the head dim
   constexpr int KSLABS = DH / 8;              // 1 KB copies of 1024 / (2 DH) key rows
@@ -898,7 +904,8 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_kernel(AttnArgs a) {
   static_assert(DH == 64 || DH == 128, "key-row swizzle defined for d_h 64 and 128");
   constexpr int VROWS = DH / 8;               // 1 KB copies of 8 V^T rows
   constexpr int COPIES = KSLABS + VROWS;
-  constexpr int PER_WAVE = COPIES / 4;
+  constexpr int PER_WAVE = COPIES / (4 * NG);
+  static_assert(PER_WAVE * 4 * NG == COPIES, "copies split evenly over the waves");
   constexpr int STAGE = COPIES * 1024;
   __shared__ __align__(16) unsigned char ring[NST * STAGE];
   __shared__ int32_t s_page[kAttnMaxChunkPages];
@@ -916,10 +923,11 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qt = wave & 3, grp = wave >> 2;   // query tile, wave group
   const int j16 = lane & 15, q4 = lane >> 4;
   const int valid_q = a.group * a.B;
 
-  const int row = 16 * wave + j16;
+  const int row = 16 * qt + j16;
   const bf16* qbase = static_cast<const bf16*>(a.q_ws) + (int64_t)(r * a.n_kv + g) * a.qrows * DH;
   const int vlo = a.window > 0 ? a.qpos0[r] + row % a.B - a.window + 1 : INT_MIN;
   const int vis_lo_max = a.qpos0[r] + a.B - a.window;   // largest row bound (sliding layers)
@@ -940,8 +948,8 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_kernel(AttnArgs a) {
   // workspace holds qrows >= 16 * 4 rows, so every copy is in bounds.  They
   // land in the last stage, which the first copies into it (issued after the
   // first barrier of the loop) find read: wave w's operand-order slabs
-  // (wave w, s) hold, at 16 * lane, row 16 w + j16, head dims 32 s + 8 q4 ..
-  static_assert(4 * DS * 1024 <= STAGE, "the queries fit one stage");
+  // (wave w, s) hold, at 16 * lane, row 16 (w % 4) + j16, head dims 32 s + 8 q4 ..
+  static_assert(4 * NG * DS * 1024 <= STAGE, "the queries fit one stage (one copy per wave)");
   unsigned char* my_q = ring + (NST - 1) * STAGE + wave * DS * 1024;
 #pragma unroll
   for (int s = 0; s < DS; ++s) lds_copy16(qbase + (int64_t)row * DH + 32 * s + 8 * q4, my_q + s * 1024);
@@ -1086,7 +1094,7 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_kernel(AttnArgs a) {
   // CU asks for all of its first AHEAD blocks at once, each one's first block
   // lands later; the ring deepens to AHEAD once computing has begun.
   constexpr int AHEAD = NST - 1;
-  constexpr int INIT = AHEAD < 2 ? AHEAD : 2;
+  constexpr int INIT = NG == 1 ? (AHEAD < 2 ? AHEAD : 2) : AHEAD;
   int issued = 0;
   for (; issued < min(INIT, nblk); ++issued) issue(issued);
   // this wave's queries (rows past g*B as zeros), once its first copies have
@@ -1098,15 +1106,44 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_kernel(AttnArgs a) {
     if (row >= valid_q) qv[s] = zero8<bf16>();
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read before the stage is refilled
-  for (int b = 0; b < nblk; ++b) {
-    // this wave's copies of block b have landed when at most those of the
-    // blocks issued after it remain; after the barrier every wave's have, and
-    // every wave is done with block b - 1, whose stage (and those before it)
-    // may be refilled with the blocks up to b + AHEAD
-    wait_vm_blocks<PER_WAVE>(issued - 1 - b);
+  // Step i works on blocks NG i .. NG i + NG - 1 (group g on block NG i + g).
+  // This wave's copies of them have landed when at most those of the blocks
+  // issued after them remain; after the barrier every wave's have, and every
+  // wave is done with the blocks of step i - 1, whose stages (and those
+  // before) may be refilled with the blocks up to NG i + NST - 1.
+  for (int i = 0; NG * i < nblk; ++i) {
+    wait_vm_blocks<PER_WAVE>(issued - min(NG * (i + 1), nblk));
     asm volatile("s_barrier" ::: "memory");
-    for (; issued < min(nblk, b + AHEAD + 1); ++issued) issue(issued);
-    process(b);
+    for (; issued < min(nblk, NG * i + NST); ++issued) issue(issued);
+    if (NG * i + grp < nblk) process(NG * i + grp);
+  }
+
+  if constexpr (NG == 2) {
+    // group 1's state through LDS (the ring is free once every wave is past
+    // its last block): lane l of tile t at [t][d][l] for O, then m and l
+    constexpr int XB = DT * 1024 + 512;
+    static_assert(4 * XB <= NST * STAGE, "the merge fits the ring");
+    unsigned char* xb = ring + qt * XB;
+    __syncthreads();
+    if (grp == 1) {
+#pragma unroll
+      for (int d = 0; d < DT; ++d) *reinterpret_cast<f32x4*>(xb + d * 1024 + 16 * lane) = o[d];
+      reinterpret_cast<float*>(xb + DT * 1024)[lane] = m_run;
+      reinterpret_cast<float*>(xb + DT * 1024 + 256)[lane] = l_run;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    // exact merge of two online-softmax states with reference maxima m0, m1
+    const float m1 = reinterpret_cast<const float*>(xb + DT * 1024)[lane];
+    const float l1 = reinterpret_cast<const float*>(xb + DT * 1024 + 256)[lane];
+    const float m = fmaxf(m_run, m1);
+    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+    for (int d = 0; d < DT; ++d)
+      o[d] = o[d] * a0 + *reinterpret_cast<const f32x4*>(xb + d * 1024 + 16 * lane) * a1;
+    l_run = l_run * a0 + l1 * a1;
+    m_run = m;
   }
 
   float* po = a.part_o + (int64_t)item * a.qrows * DH;
@@ -1143,7 +1180,18 @@ static hipError_t launch_attn_t(const AttnArgs& a, int items, hipStream_t s) {
     // Ring depth from the host's plan (three stages, 96 KB: one workgroup per
     // CU; two, 64 KB: two per CU; four: one per CU, three blocks ahead)
     const int nst = a.nst > 0 ? a.nst : items <= 256 ? 3 : 2;
+    // One-workgroup-per-CU plans (d_h 128) take two groups of four waves on
+    // alternate blocks with four stages (8K decode cache: 13.5 us against
+    // 14.2 us for one group of four); DFLASH_ATTN_GROUPS=1 keeps one group.
+    static const int groups = [] {
+      const char* e = std::getenv("DFLASH_ATTN_GROUPS");
+      return e != nullptr && std::string(e) == "1" ? 1 : 2;
+    }();
     if (kind == 0 && nqt == 4) {
+      if (a.d_h == 128 && groups == 2 && nst >= 3) {
+        launch((attn_ring64_kernel<128, 4, 2>), dim3(items), dim3(512), 0, s, a);
+        return hipGetLastError();
+      }
       if (a.d_h == 128) {
         if (nst == 2) launch((attn_ring64_kernel<128, 2>), dim3(items), dim3(256), 0, s, a);
         else if (nst == 4) launch((attn_ring64_kernel<128, 4>), dim3(items), dim3(256), 0, s, a);

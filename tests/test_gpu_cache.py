@@ -110,6 +110,18 @@ def test_random_append_crop_sequences(case, seed):
                 assert list(dev[s, : len(pages)]) == pages
 
 
+def test_append_checks_row_tensors():
+    """The binding refuses row tensors of the wrong element size or too few
+    elements before anything reaches the GPU."""
+    cache = L.Cache(2, 2, 64, torch.float8_e4m3fn, 128, device="cuda")
+    ok = torch.zeros((10, 2, 64), dtype=torch.uint8, device="cuda")
+    for k, v in ((ok.to(torch.bfloat16), ok), (ok, ok[:9]), (ok, None)):
+        with pytest.raises(L.DFlashError):
+            L.dflash_cache_append(cache, [0, 4, 10], k, v)
+    L.dflash_cache_append(cache, [0, 4, 10], ok, ok.view(torch.float8_e4m3fn))
+    assert cache.lengths() == [4, 6]
+
+
 def test_ring_layer_call_status():
     """A layer call on a ring fails with DFLASH_ERR_RANGE, changing nothing,
     when its window reaches rows the ring no longer holds, and runs when they
