@@ -293,6 +293,13 @@ SMALL = [
            rounds=1),
     _small("fresh_ctx2x200_tile_gemm_r2", d=512, k_layers=2, d_h=128, B=16, R=2, prefill="none",
            n_new="fixed", n_fixed=200, rounds=1),
+    # the library's limits: 64 requests per cache (ragged, some empty), and
+    # 64 query rows per K/V head from an MHA layer with B = 64
+    _small("max_seqs_r64", R=64, d_h=128, B=16, prefill="uniform", prefill_range=(0, 300), n_range=(0, 4),
+           rounds=2),
+    _small("max_seqs_r64_paged", R=64, d_h=64, B=4, prefill="uniform", prefill_range=(0, 200), n_range=(0, 6),
+           page_size=64, rounds=2),
+    _small("mha_b64_max_group_rows", n_h=4, n_kv=4, d_h=128, B=64, prefill_len=200, n_range=(1, 16), rounds=2),
 ]
 
 
@@ -331,6 +338,9 @@ SMALL_FP8 = [
          sliding_layers=(0, 2), rounds=3),
     _fp8("scales_pow2", d_h=128, B=16, prefill_len=800, k_scale=0.25, v_scale=4.0),
     _fp8("scales_tiny_values", d_h=128, B=16, prefill_len=800, k_scale=8.0, v_scale=16.0),
+    _fp8("max_seqs_r64", R=64, d_h=128, B=16, prefill="uniform", prefill_range=(0, 300), n_range=(0, 4),
+         rounds=2),
+    _fp8("mha_b64_max_group_rows", n_h=4, n_kv=4, d_h=128, B=64, prefill_len=200, n_range=(1, 16), rounds=2),
 ]
 
 
