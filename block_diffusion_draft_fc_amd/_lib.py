@@ -68,7 +68,7 @@ def _load() -> C.CDLL:
         "dflash_timing_reset": (C.c_int, []),
         "dflash_gemm_plan": (C.c_int, [C.c_int64, C.c_int64, C.c_int64, C.c_int32, C.POINTER(C.c_int32)]),
         "dflash_accept": (C.c_int, [vp, vp, i64, i32, vp, vp, vp, vp]),
-        "dflash_attn_plan": (C.c_int, [C.POINTER(C.c_int64), i32, i32, i64, C.POINTER(C.c_int64)]),
+        "dflash_attn_plan": (C.c_int, [C.POINTER(C.c_int64), i32, i32, i64, i32, C.POINTER(C.c_int64)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -287,12 +287,13 @@ def dflash_gemm_plan(M: int, N: int, K: int, dtype) -> dict:
             "tile_bn": out[4], "rows_per_problem": out[5]}
 
 
-def dflash_attn_plan(keys, n_kv: int, chunk_cap: int = 1 << 30) -> dict:
+def dflash_attn_plan(keys, n_kv: int, chunk_cap: int = 1 << 30, cache_dtype: int = DFLASH_BF16) -> dict:
     """The attention split a layer call would use for these per-sequence key
     counts (host-side planning only)."""
     k = (C.c_int64 * len(keys))(*[int(x) for x in keys])
     out = (C.c_int64 * 3)()
-    _check(LIB.dflash_attn_plan(k, len(keys), int(n_kv), int(chunk_cap), out), "dflash_attn_plan")
+    _check(LIB.dflash_attn_plan(k, len(keys), int(n_kv), int(chunk_cap), int(cache_dtype), out),
+           "dflash_attn_plan")
     return {"chunk": int(out[0]), "items": int(out[1]), "nst": int(out[2])}
 
 

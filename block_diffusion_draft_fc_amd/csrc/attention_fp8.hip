@@ -295,9 +295,9 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_fp8_kernel(AttnArgs a) {
 }
 
 // Ring depth: the host plans for the bf16 kernel's depths (3 stages of 32 KB:
-// one workgroup per CU; 2: two per CU).  fp8 stages are half as large: plan 2
-// takes 3 stages (48 KB, two or three workgroups per CU), plan 3 takes 4
-// (64 KB).  Deeper rings measured no faster on the 8K decode cache (5 to 7
+// one workgroup per CU; 2: several per CU).  fp8 stages are half as large:
+// plan 2 takes 3 stages (48 KB; the host fits three workgroups per CU to it),
+// plan 3 takes 4 (64 KB).  Deeper rings measured no faster on the 8K decode cache (5 to 7
 // stages: 13.5-15 us against 13.0-13.5) and slower on four 32K caches (they
 // leave one workgroup per CU).  DFLASH_ATTN_FP8_NST overrides.
 hipError_t launch_attn_fp8(const AttnArgs& a, int items, hipStream_t s) {

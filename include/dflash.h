@@ -340,14 +340,18 @@ int dflash_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t *ou
  *             key rounded down to a multiple of 64 (each >= 1)
  *   chunk_cap the largest chunk the cache allows (paged: 62 pages; ring:
  *             62 capacities; otherwise any value >= 2^30)
+ *   cache_dtype the cache's dtype, a dflash_dtype value: fp8 caches fit more items
+ *             per round
  *   out[0] chunk (keys per item, a multiple of 64, >= 128)
  *   out[1] items (sum over sequences of max(1, ceil(keys/chunk)) * n_kv)
- *   out[2] ring stages of the bf16 64-key-block kernel
- * Returns DFLASH_ERR_ARG for null pointers, DFLASH_ERR_SHAPE unless
- * 1 <= R <= DFLASH_MAX_SEQS, n_kv >= 1, every key count >= 1 and
- * chunk_cap >= 64.
+ *   out[2] ring depth planned for the 64-key-block kernels (3: one workgroup
+ *          per CU, 2: several)
+ * Returns DFLASH_ERR_ARG for null pointers, DFLASH_ERR_DTYPE for an unknown
+ * dtype, DFLASH_ERR_SHAPE unless 1 <= R <= DFLASH_MAX_SEQS, n_kv >= 1, every
+ * key count >= 1 and chunk_cap >= 64.
  * ---------------------------------------------------------------------- */
-int dflash_attn_plan(const int64_t *keys, int32_t R, int32_t n_kv, int64_t chunk_cap, int64_t *out /* [3] */);
+int dflash_attn_plan(const int64_t *keys, int32_t R, int32_t n_kv, int64_t chunk_cap, int32_t cache_dtype,
+                     int64_t *out /* [3] */);
 
 #ifdef __cplusplus
 }

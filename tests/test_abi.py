@@ -341,10 +341,10 @@ def test_accept_validation():
 
 # ------------------------------------------------------------------ attention split (host-side planning)
 
-def _attn_plan(keys, n_kv, cap=1 << 30):
+def _attn_plan(keys, n_kv, cap=1 << 30, dtype=L.DFLASH_BF16):
     k = (C.c_int64 * len(keys))(*keys)
     out = (C.c_int64 * 3)()
-    rc = L.LIB.dflash_attn_plan(k, len(keys), n_kv, cap, out)
+    rc = L.LIB.dflash_attn_plan(k, len(keys), n_kv, cap, dtype, out)
     return rc, int(out[0]), int(out[1]), int(out[2])
 
 
@@ -369,21 +369,22 @@ ATTN_CASES = [
 
 
 @pytest.mark.skipif(any(v in os.environ for v in _ATTN_KNOBS), reason="attention split overridden by env")
+@pytest.mark.parametrize("dtype", [L.DFLASH_BF16, L.DFLASH_FP8_E4M3], ids=["bf16", "fp8"])
 @pytest.mark.parametrize("keys,n_kv,cap", ATTN_CASES, ids=[f"{len(k)}x{max(k)}-kv{g}-cap{c}" for k, g, c in ATTN_CASES])
-def test_attn_plan_invariants(keys, n_kv, cap):
+def test_attn_plan_invariants(keys, n_kv, cap, dtype):
     """The chunk is a whole number of 64-key blocks, at least 128 and within
     the cap; the item count is what the chunk gives; the ring depth follows the
     total key count; and the chunk is the smallest that brings the items into
-    one round of launch slots (256 workgroups at depth 3, 512 at depth 2), or
-    the cap when no chunk within it does."""
-    rc, chunk, items, nst = _attn_plan(keys, n_kv, cap)
+    one round of launch slots (256 workgroups at depth 3, 512 at depth 2, 768
+    at depth 2 for fp8 caches), or the cap when no chunk within it does."""
+    rc, chunk, items, nst = _attn_plan(keys, n_kv, cap, dtype)
     assert rc == 0
     total = sum(keys) * n_kv
     assert nst == (2 if total > 256 * 1024 else 3)
     capc = max(128, cap // 64 * 64)
     assert chunk % 64 == 0 and 128 <= chunk <= capc
     assert items == _items(keys, n_kv, chunk)
-    limit = 512 if nst == 2 else 256
+    limit = (768 if dtype == L.DFLASH_FP8_E4M3 else 512) if nst == 2 else 256
     if _items(keys, n_kv, capc) <= limit:
         assert items <= limit
         assert chunk == 128 or _items(keys, n_kv, chunk - 64) > limit
@@ -400,17 +401,23 @@ def test_attn_plan_headline_split():
     if any(v in os.environ for v in _ATTN_KNOBS):
         pytest.skip("attention split overridden by env")
     assert _attn_plan([8216], 8) == (0, 320, 208, 3)
+    assert _attn_plan([8216], 8, dtype=L.DFLASH_FP8_E4M3) == (0, 320, 208, 3)
+    # four 32K requests: 512 items for bf16, 768 for fp8 caches
+    assert _attn_plan([32792] * 4, 8)[2] == 512
+    assert _attn_plan([32792] * 4, 8, dtype=L.DFLASH_FP8_E4M3)[2] == 768
 
 
 def test_attn_plan_validation():
     k = (C.c_int64 * 2)(100, 200)
     out = (C.c_int64 * 3)()
     f = L.LIB.dflash_attn_plan
-    assert f(None, 2, 8, 1 << 30, out) == L.ERR_ARG
-    assert f(k, 2, 8, 1 << 30, None) == L.ERR_ARG
-    assert f(k, 0, 8, 1 << 30, out) == L.ERR_SHAPE
-    assert f(k, 2, 0, 1 << 30, out) == L.ERR_SHAPE
-    assert f(k, 2, 8, 63, out) == L.ERR_SHAPE
+    bf = L.DFLASH_BF16
+    assert f(None, 2, 8, 1 << 30, bf, out) == L.ERR_ARG
+    assert f(k, 2, 8, 1 << 30, bf, None) == L.ERR_ARG
+    assert f(k, 2, 8, 1 << 30, 9, out) == L.ERR_DTYPE
+    assert f(k, 0, 8, 1 << 30, bf, out) == L.ERR_SHAPE
+    assert f(k, 2, 0, 1 << 30, bf, out) == L.ERR_SHAPE
+    assert f(k, 2, 8, 63, bf, out) == L.ERR_SHAPE
     z = (C.c_int64 * 2)(100, 0)
-    assert f(z, 2, 8, 1 << 30, out) == L.ERR_SHAPE
+    assert f(z, 2, 8, 1 << 30, bf, out) == L.ERR_SHAPE
     assert L.dflash_attn_plan([100, 200], 8) == {"chunk": 128, "items": 24, "nst": 3}
