@@ -68,18 +68,24 @@ __device__ __forceinline__ u32x4 keep_bytes(u32x4 w, int n) {
 
 }  // namespace
 
-template <int DH, int NST>
-__global__ __launch_bounds__(256, 1) void attn_ring64_fp8_kernel(AttnArgs a) {
+// NG = 2: two groups of four waves on alternate blocks with an exact merge of
+// their states at the end, as in the bf16 ring kernel; group 0 copies the
+// queries (the last stage holds one copy per tile) and group 1 reads them
+// after a barrier.
+template <int DH, int NST, int NG = 1>
+__global__ __launch_bounds__(256 * NG, 1) void attn_ring64_fp8_kernel(AttnArgs a) {
   using V8 = bf16x8;
   static_assert(DH == 64 || DH == 128, "layouts defined for d_h 64 and 128");
   static_assert(NST >= 2 && NST <= 7, "blocks in flight are counted by wait_vm_blocks (up to 6 after the current)");
+  static_assert((NG == 1 || NG == 2) && NST >= 2 * NG, "a step's blocks are issued by the end of the step before");
   constexpr int DS = DH / 32;          // K=32 steps over the head dim
   constexpr int DT = DH / 16;          // 16-dim tiles of the output
   constexpr int KCH = DH / 16;         // 16-byte chunks per key row
   constexpr int KSLABS = DH / 16;      // 1 KB copies of the block's K (64 rows of DH bytes)
   constexpr int VSLABS = DH / 16;      // 1 KB copies of its V^T (DH rows of 64 bytes)
   constexpr int COPIES = KSLABS + VSLABS;
-  constexpr int PER_WAVE = COPIES / 4;
+  constexpr int PER_WAVE = COPIES / (4 * NG);
+  static_assert(PER_WAVE * 4 * NG == COPIES, "copies split evenly over the waves");
   constexpr int STAGE = COPIES * 1024;
   constexpr int QSPAN = DH / 4;        // head dims of a lane group in the QK contraction
   __shared__ __align__(16) unsigned char ring[NST * STAGE];
@@ -98,14 +104,15 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_fp8_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qt = wave & 3, grp = wave >> 2;   // query tile, wave group
   const int j16 = lane & 15, q4 = lane >> 4;
   const int valid_q = a.group * a.B;
   // query rows of this wave: 16 wave .. 16 wave + 15; the workspace holds
   // qrows (a multiple of 16) rows per (sequence, K/V head), so a wave past
   // them loads and stores nothing
-  const bool wave_rows = 16 * wave < a.qrows;
+  const bool wave_rows = 16 * qt < a.qrows;
 
-  const int row = 16 * wave + j16;
+  const int row = 16 * qt + j16;
   const bf16* qbase = static_cast<const bf16*>(a.q_ws) + (int64_t)(r * a.n_kv + g) * a.qrows * DH;
   const int vlo = a.window > 0 ? a.qpos0[r] + row % a.B - a.window + 1 : INT_MIN;
   const int vis_lo_max = a.qpos0[r] + a.B - a.window;
@@ -122,8 +129,8 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_fp8_kernel(AttnArgs a) {
   // (as in the bf16 ring kernel); step s of lane (j16, q4) holds head dims
   // QSPAN q4 + 8 s .. + 7 of row 16 wave + j16, at 16 * lane of slab s.
   static_assert(4 * DS * 1024 <= STAGE, "the queries fit one stage");
-  unsigned char* my_q = ring + (NST - 1) * STAGE + wave * DS * 1024;
-  if (wave_rows) {
+  unsigned char* my_q = ring + (NST - 1) * STAGE + qt * DS * 1024;
+  if (wave_rows && grp == 0) {
 #pragma unroll
     for (int s = 0; s < DS; ++s) lds_copy16(qbase + (int64_t)row * DH + QSPAN * q4 + 8 * s, my_q + s * 1024);
   }
@@ -262,21 +269,52 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_fp8_kernel(AttnArgs a) {
   };
 
   constexpr int AHEAD = NST - 1;
-  constexpr int INIT = AHEAD < 2 ? AHEAD : 2;
+  constexpr int INIT = NG == 1 ? (AHEAD < 2 ? AHEAD : 2) : AHEAD;
   int issued = 0;
   for (; issued < min(INIT, nblk); ++issued) issue(issued);
+  // group 0's query copies have landed once its first block has (they went
+  // out first); with two groups a barrier shows that to group 1
   wait_vm_blocks<PER_WAVE>(max(0, issued - 1));
+  if constexpr (NG == 2) asm volatile("s_barrier" ::: "memory");
 #pragma unroll
   for (int s = 0; s < DS; ++s) {
     qv[s] = *reinterpret_cast<const V8*>(my_q + s * 1024 + 16 * lane);
     if (row >= valid_q) qv[s] = zero8<bf16>();
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read before the stage is refilled
-  for (int b = 0; b < nblk; ++b) {
-    wait_vm_blocks<PER_WAVE>(issued - 1 - b);
+  // step i: blocks NG i .. NG i + NG - 1 (group g on block NG i + g)
+  for (int i = 0; NG * i < nblk; ++i) {
+    wait_vm_blocks<PER_WAVE>(issued - min(NG * (i + 1), nblk));
     asm volatile("s_barrier" ::: "memory");
-    for (; issued < min(nblk, b + AHEAD + 1); ++issued) issue(issued);
-    process(b);
+    for (; issued < min(nblk, NG * i + NST); ++issued) issue(issued);
+    if (NG * i + grp < nblk) process(NG * i + grp);
+  }
+
+  if constexpr (NG == 2) {
+    // group 1's (m, l, O) to group 0 through LDS, lane l of tile t at
+    // [t][d][l] for O, then m and l; exact merge with reference maxima
+    constexpr int XB = DT * 1024 + 512;
+    static_assert(4 * XB <= NST * STAGE, "the merge fits the ring");
+    unsigned char* xb = ring + qt * XB;
+    __syncthreads();
+    if (grp == 1) {
+#pragma unroll
+      for (int d = 0; d < DT; ++d) *reinterpret_cast<f32x4*>(xb + d * 1024 + 16 * lane) = o[d];
+      reinterpret_cast<float*>(xb + DT * 1024)[lane] = m_run;
+      reinterpret_cast<float*>(xb + DT * 1024 + 256)[lane] = l_run;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = reinterpret_cast<const float*>(xb + DT * 1024)[lane];
+    const float l1 = reinterpret_cast<const float*>(xb + DT * 1024 + 256)[lane];
+    const float m = fmaxf(m_run, m1);
+    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+    for (int d = 0; d < DT; ++d)
+      o[d] = o[d] * a0 + *reinterpret_cast<const f32x4*>(xb + d * 1024 + 16 * lane) * a1;
+    l_run = l_run * a0 + l1 * a1;
+    m_run = m;
   }
 
   if (!wave_rows) return;
@@ -297,7 +335,8 @@ __global__ __launch_bounds__(256, 1) void attn_ring64_fp8_kernel(AttnArgs a) {
 // Ring depth: the host plans for the bf16 kernel's depths (3 stages of 32 KB:
 // one workgroup per CU; 2: several per CU).  fp8 stages are half as large:
 // plan 2 takes 3 stages (48 KB; the host fits three workgroups per CU to it),
-// plan 3 takes 4 (64 KB).  Deeper rings measured no faster on the 8K decode cache (5 to 7
+// plan 3 takes 4 (64 KB) for one wave group and 6 (96 KB) for two.  With one
+// group, deeper rings measured no faster on the 8K decode cache (5 to 7
 // stages: 13.5-15 us against 13.0-13.5) and slower on four 32K caches (they
 // leave one workgroup per CU).  DFLASH_ATTN_FP8_NST overrides.
 hipError_t launch_attn_fp8(const AttnArgs& a, int items, hipStream_t s) {
@@ -309,7 +348,19 @@ hipError_t launch_attn_fp8(const AttnArgs& a, int items, hipStream_t s) {
     return v >= 2 && v <= 7 ? v : 0;
   }();
   const int plan = a.nst > 0 ? a.nst : items <= 256 ? 3 : 2;
-  const int nst = forced ? forced : plan >= 3 ? 4 : 3;
+  // plans of one workgroup per CU at d_h 128: two wave groups with 6 stages
+  // (8K decode cache: 12.3-12.6 us; 12.6-13.0 with 4 stages; one group of
+  // four waves 13.6-14.4); DFLASH_ATTN_GROUPS=1 keeps one group
+  static const bool two = [] {
+    const char* e = std::getenv("DFLASH_ATTN_GROUPS");
+    return !(e != nullptr && e[0] == '1' && e[1] == 0);
+  }();
+  const int nst = forced ? forced : plan >= 3 ? (two && a.d_h == 128 ? 6 : 4) : 3;
+  if (two && plan >= 3 && a.d_h == 128 && (nst == 4 || nst == 6)) {
+    if (nst == 4) launch((attn_ring64_fp8_kernel<128, 4, 2>), dim3(items), dim3(512), 0, s, a);
+    else launch((attn_ring64_fp8_kernel<128, 6, 2>), dim3(items), dim3(512), 0, s, a);
+    return hipGetLastError();
+  }
 #define DFLASH_FP8_CASE(DH_, NST_)                                                 \
   if (a.d_h == DH_ && nst == NST_) {                                               \
     launch((attn_ring64_fp8_kernel<DH_, NST_>), dim3(items), dim3(256), 0, s, a); \
