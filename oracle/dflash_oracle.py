@@ -34,7 +34,8 @@ of readings kept with the design notes):
   R12 sliding layers: key j is visible to query i iff pos_i - pos_j < window
       (no upper bound: still non-causal inside the block).
   R14 layer stacks chain H_{l+1} = H_l + out_l (the decoder MLP is not on the
-      pages).  parity unpinned: this chaining is a builder choice.
+      pages, so the chaining is a builder choice); every layer reads the one
+      context C of the round and keeps its own cache, cropped after the round.
   R23 an fp8 cache element is an OCP FP8 E4M3 byte: code = the nearest E4M3
       value of x / scale (ties to the even mantissa, magnitudes from 448 up
       saturated to 448), read back as value(code) * scale, with one fp32
@@ -265,29 +266,6 @@ def draft_head(h, gamma_f, eps: float, w_lm, B: int):
     R = h.shape[0] // B
     x = rms_norm(h, gamma_f, eps).reshape(R, B, -1)[:, 1:, :].reshape(R * (B - 1), -1)
     logits = x @ f64(w_lm).T
-    return logits, np.argmax(logits, axis=-1)
-
-
-def round_to_bf16(x) -> np.ndarray:
-    """Nearest bfloat16 value (ties to even) of each element, as float64: the
-    upper 16 bits of the float32 encoding after adding half an ulp of the
-    16-bit result (plus one when the kept part is odd).  Finite inputs."""
-    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    lsb = (b >> np.uint64(16)) & np.uint64(1)
-    r = ((b + np.uint64(0x7FFF) + lsb) & np.uint64(0xFFFF0000)).astype(np.uint32)
-    return r.view(np.float32).astype(np.float64)
-
-
-def draft_head_decision(h, gamma_f, eps: float, w_lm, B: int, bf16_rows: bool):
-    """The argmax of draft_head taken in the kernel's precision (an integer
-    decided by floating point): the normed rows stored in the layer's storage
-    type (bfloat16 when bf16_rows), the logits accumulated in float32.
-    Returns (logits32 [R*(B-1), vocab] float32, ids)."""
-    h = f64(h)
-    R = h.shape[0] // B
-    x = rms_norm(h, gamma_f, eps).reshape(R, B, -1)[:, 1:, :].reshape(R * (B - 1), -1)
-    x = round_to_bf16(x) if bf16_rows else x
-    logits = x.astype(np.float32) @ np.asarray(w_lm, dtype=np.float32).T
     return logits, np.argmax(logits, axis=-1)
 
 

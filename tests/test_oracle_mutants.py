@@ -36,6 +36,8 @@ PINS = [
     T.test_e4m3_encode_brute_force_and_ties,
     lambda: T.test_brute_force_tiny_fp8_cache(5, 2, 3, 0),
     T.test_fp8_cache_error_is_bounded,
+    T.test_stack_single_layer_matches_layer,
+    T.test_stack_chaining_closed_form,
 ]
 
 _encode, _decode = O.e4m3_encode, O.e4m3_decode
@@ -218,6 +220,35 @@ def _accept_round_anchor_after(draft_ids, posterior):
     return acc, rows, np.array([posterior[r][min(acc[r] + 1, posterior.shape[1] - 1)] for r in range(len(acc))])
 
 
+def _stack_round_factory(no_residual=False, shared_cache=False, crop_last_only=False, ctx_first_layer_only=False):
+    # OracleStack.round with one chaining mistake (caches of bf16/f32 values only)
+    def round_(self, x_raw, cu, H, B):
+        R = len(cu) - 1
+        C = O.ctx_project(x_raw, self.w_fc, self.gamma_h, self.eps)
+        h = O.f64(H).copy()
+        outs, last = [], []
+        for li, p in enumerate(self.layers):
+            ci = 0 if shared_cache else li
+            out_l = np.empty_like(h)
+            res_l = []
+            for r in range(R):
+                L = self.K[ci][r].shape[1]
+                ctx = C[cu[r]:cu[r + 1]] if (li == 0 or not ctx_first_layer_only) else C[:0]
+                res = O.kv_inject_layer(p, self.K[ci][r], self.V[ci][r], ctx, h[r * B:(r + 1) * B])
+                out_l[r * B:(r + 1) * B] = res.out
+                n = cu[r + 1] - cu[r]
+                if crop_last_only and li != len(self.layers) - 1:
+                    self.K[ci][r], self.V[ci][r] = res.K, res.V
+                else:
+                    self.K[ci][r], self.V[ci][r] = O.crop(res.K, res.V, L + n)
+                res_l.append(res)
+            outs.append(out_l)
+            last = res_l
+            h = out_l if no_residual else h + out_l
+        return outs, last
+    return round_
+
+
 _ORIG = {name: getattr(O, name) for name in
          ("rope", "gqa_attention", "project_kv", "rms_norm", "ctx_project", "o_proj",
           "crop", "visible", "rope_inv_freq", "kv_inject_layer", "draft_head", "accept_round")}
@@ -253,13 +284,21 @@ MUTANTS = {
     "e4m3_subnormal_hidden_one": ("e4m3_decode", _dec_subnormal_hidden_one),
     "fp8_cache_not_quantized": ("e4m3_quantize", _quant_nothing),
     "fp8_scale_inverted": ("e4m3_quantize", _quant_scale_multiplied),
+    "stack_no_residual": ("OracleStack.round", _stack_round_factory(no_residual=True)),
+    "stack_layers_share_one_cache": ("OracleStack.round", _stack_round_factory(shared_cache=True)),
+    "stack_only_last_layer_cropped": ("OracleStack.round", _stack_round_factory(crop_last_only=True)),
+    "stack_context_into_first_layer_only": ("OracleStack.round", _stack_round_factory(ctx_first_layer_only=True)),
 }
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, monkeypatch):
     attr, fn = MUTANTS[name]
-    monkeypatch.setattr(O, attr, fn)
+    owner = O
+    if "." in attr:
+        cls, attr = attr.split(".")
+        owner = getattr(O, cls)
+    monkeypatch.setattr(owner, attr, fn)
     caught = []
     for pin in PINS:
         try:
