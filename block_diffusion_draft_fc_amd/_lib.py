@@ -69,6 +69,7 @@ def _load() -> C.CDLL:
         "dflash_gemm_plan": (C.c_int, [C.c_int64, C.c_int64, C.c_int64, C.c_int32, C.POINTER(C.c_int32)]),
         "dflash_accept": (C.c_int, [vp, vp, i64, i32, vp, vp, vp, vp]),
         "dflash_attn_plan": (C.c_int, [C.POINTER(C.c_int64), i32, i32, i64, i32, C.POINTER(C.c_int64)]),
+        "dflash_attn_force_chunk": (C.c_int, [i64]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -295,6 +296,12 @@ def dflash_attn_plan(keys, n_kv: int, chunk_cap: int = 1 << 30, cache_dtype: int
     _check(LIB.dflash_attn_plan(k, len(keys), int(n_kv), int(chunk_cap), int(cache_dtype), out),
            "dflash_attn_plan")
     return {"chunk": int(out[0]), "items": int(out[1]), "nst": int(out[2])}
+
+
+def dflash_attn_force_chunk(chunk: int) -> None:
+    """Force the attention split of later layer calls to `chunk` keys per
+    item (0: the planner's split); a diagnostic for split-invariance tests."""
+    _check(LIB.dflash_attn_force_chunk(int(chunk)), "dflash_attn_force_chunk")
 
 
 def timing_read() -> dict:

@@ -28,9 +28,6 @@
 //  * The running max, sum and output stay per lane in the log2 domain; the
 //    four waves merge through LDS at the end and the workgroup writes one
 //    partial (m, l, unnormalised O) per query row.
-#include <cstdlib>
-#include <string>
-
 #include "kernels.hpp"
 
 namespace dflash {
@@ -677,202 +674,17 @@ __global__ __launch_bounds__(256, 1) void attn_lds_kernel(AttnArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- bf16: shared ring, one query tile per wave
-// For work items with four 16-row query tiles (g*B of 49..64 rows): wave t
-// owns query tile t, with its queries in registers, and the four waves share
-// one ring of NST 32-key blocks in LDS.  Each block is brought in by all four
-// waves together (a quarter of its 1 KB operand slabs each, direct-to-LDS) and
-// read by each wave for its own tile, so every wave holds the online-softmax
-// state of 16 rows only and writes its rows' partials itself: there is no
-// merge across waves at the end.  Up to NST - 1 blocks are in flight; one
-// barrier per block, after which the block has landed for every wave and the
-// previous block's stage is free to refill.  The K/V operand slabs and the
-// score layout are those of attn_lds_kernel.
-
-template <int DH, int NST>
-__global__ __launch_bounds__(256, 1) void attn_ring_kernel(AttnArgs a) {
-  using V8 = bf16x8;
-  static_assert(NST >= 2 && NST <= 8, "blocks in flight are counted by wait_vm_blocks (up to 6 after the current)");
-  constexpr int DS = DH / 32;                 // K=32 steps over the head dim
-  constexpr int DT = DH / 16;                 // 16-dim tiles of the head dim
-  constexpr int KSLABS = 2 * DS, VSLABS = DT;
-  constexpr int SLABS = KSLABS + VSLABS;      // 1 KB operand slabs per block
-  constexpr int PER_WAVE = SLABS / 4;         // copies per wave and block
-  constexpr int STAGE = SLABS * 1024;
-  __shared__ __align__(16) unsigned char ring[NST * STAGE];
-  __shared__ int32_t s_page[kAttnMaxChunkPages];
-
-  const int item = blockIdx.x;
-  int r = 0;
-  while (r + 1 < a.R && item >= a.item_base[r + 1]) ++r;
-  const int local = item - a.item_base[r];
-  const int g = local / a.chunks[r];
-  const int chunk = local - g * a.chunks[r];
-  const int key_hi = a.key_hi[r];
-  const int kbeg = (a.key_lo[r] & ~63) + chunk * a.chunk_keys;
-  const int kend = min(kbeg + a.chunk_keys, key_hi);
-  const int nblk = kend > kbeg ? (kend - kbeg + 31) >> 5 : 0;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int j16 = lane & 15, q4 = lane >> 4;
-  const int valid_q = a.group * a.B;
-
-  // this wave's query tile: lane (j16, q4) holds row 16 wave + j16, head dims
-  // 32 s + 8 q4 .. +7 (rows past g*B are zeros)
-  const int row = 16 * wave + j16;
-  const bf16* qbase = static_cast<const bf16*>(a.q_ws) + (int64_t)(r * a.n_kv + g) * a.qrows * DH;
-  V8 qv[DS];
-#pragma unroll
-  for (int s = 0; s < DS; ++s) qv[s] = row < valid_q ? load8(qbase + (int64_t)row * DH + 32 * s + 8 * q4) : zero8<bf16>();
-  // keys visible to the row: [vlo, key_hi), vlo = pos - window + 1 on sliding layers
-  const int vlo = a.window > 0 ? a.qpos0[r] + row % a.B - a.window + 1 : INT_MIN;
-  const int vis_lo_max = a.qpos0[r] + a.B - a.window;   // largest row bound (sliding layers)
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 o[DT];
-#pragma unroll
-  for (int d = 0; d < DT; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // physical pages of the chunk, read once so that no copy of the block loop
-  // depends on another global load
-  const int pg0 = kbeg / a.cache.page_rows;
-  const int npg = nblk > 0 ? (kend - 1) / a.cache.page_rows - pg0 + 1 : 0;
-  for (int i = tid; i < npg; i += 256) s_page[i] = (int32_t)cache_page(a.cache, r, (pg0 + i) * a.cache.page_rows);
-  // the queries are consumed here, before any block copy is issued: the copies
-  // are invisible to the compiler, whose wait for the queries would otherwise
-  // also wait for every copy in flight
-#pragma unroll
-  for (int s = 0; s < DS; ++s) asm volatile("" ::"v"(qv[s]));
-  __syncthreads();
-
-  const bf16* kpool = static_cast<const bf16*>(a.cache.k_pool);
-  const bf16* vpool = static_cast<const bf16*>(a.cache.v_pool);
-  const int krow = 8 * (j16 >> 2) + (j16 & 3);   // + 4*kt: key of A-operand row j16
-
-  // copies of block b (keys kbeg + 32 b ..) into stage b % NST: this wave's
-  // slabs wave * PER_WAVE .. +PER_WAVE-1 (K slabs (kt, s) first, then V^T
-  // slabs d).  Blocks never cross a page; rows past key_hi are stale rows
-  // inside the allocation, masked below.
-  auto issue = [&](int b) {
-    const int blk = kbeg + 32 * b;
-    const int64_t page = s_page[blk / a.cache.page_rows - pg0];
-    const int slot = blk % a.cache.page_rows;
-    const bf16* kb = kpool + k_offset(a.cache, page, g, slot);
-    const bf16* vb = vpool + v_offset(a.cache, page, g, slot);
-    unsigned char* sb = ring + (b % NST) * STAGE;
-#pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const int slab = wave * PER_WAVE + i;
-      const bf16* src;
-      if (slab < KSLABS) {
-        const int kt = slab / DS, s = slab - kt * DS;
-        src = kb + (int64_t)(krow + 4 * kt) * DH + 32 * s + 8 * q4;
-      } else {
-        const int d = slab - KSLABS;
-        src = vb + (16 * d + j16) * kVTile + 8 * q4;
-      }
-      lds_copy16(src, sb + slab * 1024);
-    }
-  };
-
-  // one block for this wave's tile: online softmax with a lazily moved maximum
-  auto process = [&](int b) {
-    const unsigned char* sb = ring + (b % NST) * STAGE + 16 * lane;
-    V8 kv[2][DS], vv[DT];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int s = 0; s < DS; ++s) kv[kt][s] = *reinterpret_cast<const V8*>(sb + (kt * DS + s) * 1024);
-#pragma unroll
-    for (int d = 0; d < DT; ++d) vv[d] = *reinterpret_cast<const V8*>(sb + (KSLABS + d) * 1024);
-    const int blk = kbeg + 32 * b;
-    const int key0 = blk + 8 * q4;   // this lane's 8 consecutive keys
-    // stale rows past the end of the cache may hold any bits: zero their V
-    // entries so that p = 0 cannot meet an Inf or NaN (last block only)
-    if (blk + 32 > key_hi) {
-#pragma unroll
-      for (int d = 0; d < DT; ++d)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (key0 + e >= key_hi) vv[d][e] = static_cast<bf16>(0.f);
-    }
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int s = 0; s < DS; ++s)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) sacc[kt] = mma32(kv[kt][s], qv[s], sacc[kt]);
-    f32x8 sv;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sv[4 * kt + e] = sacc[kt][e] * a.scale_log2;
-    const bool all_vis = blk + 32 <= key_hi && (a.window <= 0 || blk >= vis_lo_max);
-    if (!all_vis) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = key0 + e;
-        sv[e] = ((key >= vlo) & (key < key_hi)) ? sv[e] : -INFINITY;
-      }
-    }
-    float mx = sv[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    // the reference maximum moves only when the block maximum exceeds it by
-    // more than 8 (log2 units): every p <= 256, O rescaled on those blocks only
-    const bool need = mx > m_run + 8.f;
-    const float m_new = need ? mx : m_run;
-    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-    m_run = m_new;
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    f32x8 p;
-    float ps = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(sv[e] - m_use);
-      ps += p[e];
-    }
-    l_run = l_run * alpha + ps;
-    const V8 pv = cvt8<bf16>(p);
-    if (__any(need)) {
-#pragma unroll
-      for (int d = 0; d < DT; ++d) o[d] *= alpha;
-    }
-#pragma unroll
-    for (int d = 0; d < DT; ++d) o[d] = mma32(vv[d], pv, o[d]);
-  };
-
-  constexpr int AHEAD = NST - 1;   // blocks in flight
-  for (int b = 0; b < min(AHEAD, nblk); ++b) issue(b);
-  for (int b = 0; b < nblk; ++b) {
-    // this wave's copies of block b have landed when at most those of the
-    // blocks issued after it (b + 1 .. b + AHEAD - 1) remain; after the
-    // barrier every wave's have, and every wave is done with block b - 1
-    wait_vm_blocks<PER_WAVE>(min(nblk - 1 - b, AHEAD - 1));
-    asm volatile("s_barrier" ::: "memory");
-    if (b + AHEAD < nblk) issue(b + AHEAD);   // into the stage of block b - 1
-    process(b);
-  }
-
-  // this wave's rows: O (relative to m_run), m, l
-  float* po = a.part_o + (int64_t)item * a.qrows * DH;
-#pragma unroll
-  for (int d = 0; d < DT; ++d) *reinterpret_cast<f32x4*>(po + (int64_t)row * DH + 16 * d + 4 * q4) = o[d];
-  float l = l_run;
-  l += __shfl_xor(l, 16, kWave);
-  l += __shfl_xor(l, 32, kWave);
-  if (q4 == 0) {
-    float* pml = a.part_ml + (int64_t)item * 2 * a.qrows;
-    pml[row] = m_run;
-    pml[a.qrows + row] = l;
-  }
-}
-
 // ---------------------------------------------------------------- bf16: shared ring of 64-key blocks
-// attn_ring_kernel with 64-key blocks: twice the keys per barrier and per
-// dependency chain (K reads -> S -> softmax -> PV) of each wave, and V^T copied
-// in whole 128-byte lines (64 keys of one head dim).  A stage holds
+// For work items with four 16-row query tiles (g*B of 49..64 rows): wave t
+// owns query tile t, and the four waves share one ring of NST 64-key blocks in
+// LDS.  Each block is brought in by all four waves together (a quarter of its
+// 1 KB copies each, direct-to-LDS) and read by each wave for its own tile, so
+// every wave holds the online-softmax state of 16 rows only and writes its
+// rows' partials itself.  One barrier per block, after which the block has
+// landed for every wave and the previous block's stage is free to refill.
+// 64-key blocks give each wave's dependency chain (K reads -> S -> softmax
+// -> PV) 64 keys per barrier, and V^T arrives in whole 128-byte lines (64
+// keys of one head dim).  A stage holds
 //   K: the block's 64 key rows in key order (2 DH bytes each), the 16-byte
 //      chunk c of key j at position c ^ kswz(j) within its row - each copy
 //      moves whole rows (1 KB of consecutive keys, contiguous in the cache),
@@ -1168,59 +980,28 @@ static hipError_t launch_attn_t(const AttnArgs& a, int items, hipStream_t s) {
     return hipGetLastError();                                                                      \
   }
   if constexpr (sizeof(T) == 2) {
-    // bf16, four query tiles: the shared ring of 64-key blocks.  For
-    // comparison, DFLASH_ATTN_KERNEL=ring32 takes the ring of 32-key blocks
-    // and =lds the per-wave LDS rings.
-    static const int kind = [] {
-      const char* e = std::getenv("DFLASH_ATTN_KERNEL");
-      if (e == nullptr) return 0;
-      const std::string v(e);
-      return v == "ring32" ? 2 : v == "lds" ? 3 : 0;
-    }();
-    // Ring depth from the host's plan (three stages, 96 KB: one workgroup per
-    // CU; two, 64 KB: two per CU; four: one per CU, three blocks ahead)
-    const int nst = a.nst > 0 ? a.nst : items <= 256 ? 3 : 2;
-    // One-workgroup-per-CU plans (d_h 128) take two groups of four waves on
-    // alternate blocks with four stages (8K decode cache: 13.5 us against
-    // 14.2 us for one group of four); DFLASH_ATTN_GROUPS=1 keeps one group.
-    static const int groups = [] {
-      const char* e = std::getenv("DFLASH_ATTN_GROUPS");
-      return e != nullptr && std::string(e) == "1" ? 1 : 2;
-    }();
-    if (kind == 0 && nqt == 4) {
-      if (a.d_h == 128 && groups == 2 && nst >= 3) {
+    // bf16, four query tiles: the shared ring of 64-key blocks.  Plans of one
+    // workgroup per CU (ring depth 3 and more) at d_h 128 take two groups of
+    // four waves on alternate blocks with four stages (8K decode cache: 13.5
+    // us against 14.2 us for one group of four); plans of several workgroups
+    // per CU two stages and one group.
+    if (nqt == 4) {
+      if (a.d_h == 128 && a.nst >= 3) {
         launch((attn_ring64_kernel<128, 4, 2>), dim3(items), dim3(512), 0, s, a);
-        return hipGetLastError();
-      }
-      if (a.d_h == 128) {
-        if (nst == 2) launch((attn_ring64_kernel<128, 2>), dim3(items), dim3(256), 0, s, a);
-        else if (nst == 4) launch((attn_ring64_kernel<128, 4>), dim3(items), dim3(256), 0, s, a);
-        else launch((attn_ring64_kernel<128, 3>), dim3(items), dim3(256), 0, s, a);
-        return hipGetLastError();
-      }
-      if (a.d_h == 64) {
+      } else if (a.d_h == 128) {
+        launch((attn_ring64_kernel<128, 2>), dim3(items), dim3(256), 0, s, a);
+      } else {
         launch((attn_ring64_kernel<64, 4>), dim3(items), dim3(256), 0, s, a);
-        return hipGetLastError();
       }
-    }
-    if (kind == 2 && nqt == 4) {
-      if (a.d_h == 128) {
-        launch((attn_ring_kernel<128, 4>), dim3(items), dim3(256), 0, s, a);
-        return hipGetLastError();
-      }
-      if (a.d_h == 64) {
-        launch((attn_ring_kernel<64, 8>), dim3(items), dim3(256), 0, s, a);
-        return hipGetLastError();
-      }
+      return hipGetLastError();
     }
 #define DFLASH_ATTN_LDS_CASE(DH_, NQT_)                                                          \
   if (a.d_h == DH_ && nqt == NQT_) {                                                             \
     launch((attn_lds_kernel<DH_, NQT_>), dim3(items), dim3(256), 0, s, a);           \
     return hipGetLastError();                                                                    \
   }
-    DFLASH_ATTN_LDS_CASE(64, 1) DFLASH_ATTN_LDS_CASE(64, 2) DFLASH_ATTN_LDS_CASE(64, 3) DFLASH_ATTN_LDS_CASE(64, 4)
+    DFLASH_ATTN_LDS_CASE(64, 1) DFLASH_ATTN_LDS_CASE(64, 2) DFLASH_ATTN_LDS_CASE(64, 3)
     DFLASH_ATTN_LDS_CASE(128, 1) DFLASH_ATTN_LDS_CASE(128, 2) DFLASH_ATTN_LDS_CASE(128, 3)
-    DFLASH_ATTN_LDS_CASE(128, 4)
 #undef DFLASH_ATTN_LDS_CASE
   } else {
     DFLASH_ATTN_CASE(64, 1, 1, 1) DFLASH_ATTN_CASE(64, 2, 2, 1) DFLASH_ATTN_CASE(64, 3, 3, 1)

@@ -32,7 +32,6 @@
 //    c ^ hk(j); V^T as d_h rows of 64 bytes, chunk c of row R at
 //    c ^ ((R / 4) % 4).  Each operand read (16 lanes, 16 bytes each) then
 //    covers all 256 bytes of the banks.
-#include <cstdlib>
 
 #include "kernels.hpp"
 
@@ -334,44 +333,24 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_fp8_kernel(AttnArgs a
 
 // Ring depth: the host plans for the bf16 kernel's depths (3 stages of 32 KB:
 // one workgroup per CU; 2: several per CU).  fp8 stages are half as large:
-// plan 2 takes 3 stages (48 KB; the host fits three workgroups per CU to it),
-// plan 3 takes 4 (64 KB) for one wave group and 6 (96 KB) for two.  With one
-// group, deeper rings measured no faster on the 8K decode cache (5 to 7
-// stages: 13.5-15 us against 13.0-13.5) and slower on four 32K caches (they
-// leave one workgroup per CU).  DFLASH_ATTN_FP8_NST overrides.
+// plan 2 takes 3 stages (48 KB; the host fits three workgroups per CU to it);
+// plan 3 takes two wave groups with 6 stages (96 KB) at d_h 128 (8K decode
+// cache: 12.3-12.6 us; 12.6-13.0 with 4 stages; one group of four waves
+// 13.6-14.4) and one group with 4 stages (64 KB) at d_h 64.  With one group,
+// deeper rings measured no faster on the 8K decode cache (5 to 7 stages:
+// 13.5-15 us against 13.0-13.5) and slower on four 32K caches (they leave one
+// workgroup per CU).
 hipError_t launch_attn_fp8(const AttnArgs& a, int items, hipStream_t s) {
   if (items == 0) return hipSuccess;
   if ((a.qrows + 15) / 16 > 4) return hipErrorInvalidValue;
-  static const int forced = [] {
-    const char* e = std::getenv("DFLASH_ATTN_FP8_NST");
-    const int v = e ? std::atoi(e) : 0;
-    return v >= 2 && v <= 7 ? v : 0;
-  }();
-  const int plan = a.nst > 0 ? a.nst : items <= 256 ? 3 : 2;
-  // plans of one workgroup per CU at d_h 128: two wave groups with 6 stages
-  // (8K decode cache: 12.3-12.6 us; 12.6-13.0 with 4 stages; one group of
-  // four waves 13.6-14.4); DFLASH_ATTN_GROUPS=1 keeps one group
-  static const bool two = [] {
-    const char* e = std::getenv("DFLASH_ATTN_GROUPS");
-    return !(e != nullptr && e[0] == '1' && e[1] == 0);
-  }();
-  const int nst = forced ? forced : plan >= 3 ? (two && a.d_h == 128 ? 6 : 4) : 3;
-  if (two && plan >= 3 && a.d_h == 128 && (nst == 4 || nst == 6)) {
-    if (nst == 4) launch((attn_ring64_fp8_kernel<128, 4, 2>), dim3(items), dim3(512), 0, s, a);
-    else launch((attn_ring64_fp8_kernel<128, 6, 2>), dim3(items), dim3(512), 0, s, a);
-    return hipGetLastError();
+  if (a.nst >= 3) {
+    if (a.d_h == 128) launch((attn_ring64_fp8_kernel<128, 6, 2>), dim3(items), dim3(512), 0, s, a);
+    else launch((attn_ring64_fp8_kernel<64, 4>), dim3(items), dim3(256), 0, s, a);
+  } else {
+    if (a.d_h == 128) launch((attn_ring64_fp8_kernel<128, 3>), dim3(items), dim3(256), 0, s, a);
+    else launch((attn_ring64_fp8_kernel<64, 3>), dim3(items), dim3(256), 0, s, a);
   }
-#define DFLASH_FP8_CASE(DH_, NST_)                                                 \
-  if (a.d_h == DH_ && nst == NST_) {                                               \
-    launch((attn_ring64_fp8_kernel<DH_, NST_>), dim3(items), dim3(256), 0, s, a); \
-    return hipGetLastError();                                                      \
-  }
-  DFLASH_FP8_CASE(128, 2) DFLASH_FP8_CASE(128, 3) DFLASH_FP8_CASE(128, 4) DFLASH_FP8_CASE(128, 5)
-  DFLASH_FP8_CASE(128, 6) DFLASH_FP8_CASE(128, 7)
-  DFLASH_FP8_CASE(64, 2) DFLASH_FP8_CASE(64, 3) DFLASH_FP8_CASE(64, 4) DFLASH_FP8_CASE(64, 5)
-  DFLASH_FP8_CASE(64, 6) DFLASH_FP8_CASE(64, 7)
-#undef DFLASH_FP8_CASE
-  return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace dflash

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -38,12 +39,6 @@ bool scale_ok(float x) { return std::isfinite(x) && x > 0.f; }
 size_t elem_bytes(int32_t dt) { return dt == DFLASH_BF16 ? 2 : 4; }
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-int env_int(const char* name, int dflt, int lo, int hi) {
-  const char* e = std::getenv(name);
-  const int v = e ? std::atoi(e) : dflt;
-  return std::min(std::max(v, lo), hi);
-}
 
 // ---------------------------------------------------------------- stage timing
 // While enabled, each stage of a call is bracketed by two HIP events recorded
@@ -131,42 +126,41 @@ hipError_t staged(int stage, hipStream_t s, bool launches, F&& f) {
 //    runs two blocks ahead of its compute); beyond, two stages and two
 //    workgroups per CU, which cover each other's load latency.
 //  * Item count: the CUs hold `slots` workgroups at once (256 or 512).  Items
-//    past a whole number of rounds of slots would run by themselves at the end
-//    (a few items over 512 cost a third of the time on the 16-request ragged
-//    batch), so the chunk is the smallest multiple of 64 keys (at least 128)
-//    whose items fit `rounds` rounds.  One round measured best on the ragged
-//    batch and the 5-layer stack, where two rounds balance the unequal last
-//    chunks of the requests no better than they cost in partials.
-// DFLASH_ATTN_NST forces the depth, DFLASH_ATTN_ROUNDS the rounds, and
-// DFLASH_ATTN_TARGET_ITEMS a plain target count instead of the fit.
+//    past a whole round of slots would run by themselves at the end (a few
+//    items over 512 cost a third of the time on the 16-request ragged batch),
+//    so the chunk is the smallest multiple of 64 keys (at least 128) whose
+//    items fit one round.  Two rounds balanced the unequal last chunks of the
+//    ragged batch and the 5-layer stack no better than they cost in partials.
+// dflash_attn_force_chunk replaces the chunk (a diagnostic: the result must
+// not depend on the split).
 struct AttnSplit {
   int64_t chunk;
   int64_t items;
   int nst;
 };
 
+std::atomic<int64_t> g_forced_chunk{0};
+
 AttnSplit plan_attn_split(const std::vector<int64_t>& keys, int n_kv, int64_t chunk_cap, bool fp8) {
-  static const int forced_nst = env_int("DFLASH_ATTN_NST", 0, 0, 4);
-  static const int rounds_env = env_int("DFLASH_ATTN_ROUNDS", 1, 1, 4);
-  static const int target_env = env_int("DFLASH_ATTN_TARGET_ITEMS", 0, 0, kAttnMaxTarget);
   int64_t total = 0;
   for (int64_t k : keys) total += k * n_kv;
   AttnSplit sp{};
-  sp.nst = forced_nst > 0 ? forced_nst : total > ((int64_t)256 << 10) ? 2 : 3;
+  sp.nst = total > ((int64_t)256 << 10) ? 2 : 3;
   auto items_of = [&](int64_t chunk) {
     int64_t it = 0;
     for (int64_t k : keys) it += std::max<int64_t>(1, cdiv(k, chunk)) * n_kv;
     return it;
   };
   const int64_t cap = std::max<int64_t>(128, chunk_cap / 64 * 64);
-  if (target_env > 0) {
-    sp.chunk = std::min(cap, std::max<int64_t>(128, cdiv(cdiv(total, target_env), 64) * 64));
+  const int64_t forced = g_forced_chunk.load();
+  if (forced > 0) {
+    sp.chunk = std::min(cap, forced);
   } else {
     // workgroup slots of one round: 256 at depth 3 (one per CU), 512 at depth
     // 2 (two per CU); fp8 caches at depth 2 fit three per CU (48 KB of LDS,
     // 168 VGPRs): 4 x 32K keys 79 -> 73 us, the combine 1 us longer
     const int64_t slots = sp.nst == 2 ? (fp8 ? 768 : 512) : 256;
-    const int64_t limit = std::min<int64_t>(kAttnMaxTarget, rounds_env * slots);
+    const int64_t limit = std::min<int64_t>(kAttnMaxTarget, slots);
     // items_of is non-increasing in the chunk: the smallest chunk (in units of
     // 64 keys) in [2, cap / 64] with items_of <= limit, else the cap
     int64_t lo = 2, hi = cap / 64;
@@ -199,15 +193,11 @@ struct SkinnyPlan {
 };
 
 
-// Whether a product may take gemm_slab_kernel: bf16 and K a multiple of 512
-// (DFLASH_GEMM_SLAB=0 turns it off).
-bool slab_eligible(int64_t K, size_t eb) {
-  static const int use_slab = env_int("DFLASH_GEMM_SLAB", 1, 0, 1);
-  return use_slab && eb == 2 && K % 512 == 0;
-}
+// Whether a product may take gemm_slab_kernel: bf16 and K a multiple of 512.
+bool slab_eligible(int64_t K, size_t eb) { return eb == 2 && K % 512 == 0; }
 
 // Rows per weight-streaming problem: 128 for slab-eligible products with K
-// up to 8192 (the kernel's row limit; DFLASH_GEMM_SLAB_ROWS lowers it), else
+// up to 8192 (the kernel's row limit), else
 // 64 for bf16 and 32 for fp32, whose staged activation rows take twice the
 // LDS (this keeps every gemm_lds_kernel plan within its 64 KB dynamic LDS
 // budget).  Above 64 rows the slab kernel's chunk is 512 wide, so its fp32
@@ -215,8 +205,7 @@ bool slab_eligible(int64_t K, size_t eb) {
 // stack's K/V product beats the tile kernel), not for the 20480-wide fc,
 // where the tile kernel takes 65+ rows (ragged batch fc: 64 -> 47 us).
 int64_t rows_per_problem(int64_t K, size_t eb) {
-  static const int slab_rows = env_int("DFLASH_GEMM_SLAB_ROWS", 128, 64, 128) / 16 * 16;
-  if (slab_eligible(K, eb)) return K <= 8192 ? slab_rows : kSkinnyMaxM;
+  if (slab_eligible(K, eb)) return K <= 8192 ? 128 : kSkinnyMaxM;
   return eb == 2 ? kSkinnyMaxM : kSkinnyMaxM / 2;
 }
 
@@ -227,17 +216,12 @@ int64_t rows_per_problem(int64_t K, size_t eb) {
 //  * otherwise gemm_lds_kernel, 64-column tiles, about 1024 workgroups with
 //    256-wide chunks, the staged activation slice within the LDS budget.
 SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, size_t eb) {
-  static const int wide_target = env_int("DFLASH_GEMM_WIDE_BLOCKS", 256, 1, 1 << 16);
-  static const int lds_target = env_int("DFLASH_GEMM_LDS_BLOCKS", 1024, 1, 1 << 16);
-  static const int wide_min_k = env_int("DFLASH_GEMM_WIDE_MIN_K", 8192, 0, 1 << 30);
-  static const int use_stream = env_int("DFLASH_GEMM_STREAM", 1, 0, 1);
-  static const int use_fullk = env_int("DFLASH_GEMM_FULLK", 1, 0, 1);
+  constexpr int wide_target = 256, lds_target = 1024, wide_min_k = 8192;
   SkinnyPlan p{};
   p.mt = (int32_t)std::max<int64_t>(1, cdiv(M, 16));
-  static const int use_resident = env_int("DFLASH_GEMM_RESIDENT", 1, 0, 1);
   // at most 16 rows and very many columns (a vocabulary): the rows stay in
   // LDS and each wave streams whole weight tiles, one result
-  if (use_resident && eb == 2 && p.mt == 1 && K % 64 == 0 && K <= kResMaxK && N % 4 == 0 && N >= 65536) {
+  if (eb == 2 && p.mt == 1 && K % 64 == 0 && K <= kResMaxK && N % 4 == 0 && N >= 65536) {
     p.resident = true;
     p.n_tiles = (int32_t)cdiv(N, 16);
     p.k_chunk = (int32_t)K;
@@ -245,7 +229,7 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, size_t eb) {
     return p;
   }
   // at most 16 rows: the whole K in one workgroup per 16 columns, one result
-  if (use_fullk && eb == 2 && p.mt == 1 && K % 512 == 0 && N % 4 == 0) {
+  if (eb == 2 && p.mt == 1 && K % 512 == 0 && N % 4 == 0) {
     p.fullk = true;
     p.n_tiles = (int32_t)cdiv(N, 16);
     p.k_chunk = (int32_t)K;
@@ -254,7 +238,7 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, size_t eb) {
   }
   // at most 32 rows, K below the wide kernel's range: per-wave weight streams
   // in 512-wide K-chunks
-  if (use_stream && eb == 2 && p.mt <= 2 && K < wide_min_k && K % 64 == 0 && N % 4 == 0) {
+  if (eb == 2 && p.mt <= 2 && K < wide_min_k && K % 64 == 0 && N % 4 == 0) {
     p.stream = true;
     p.n_tiles = (int32_t)cdiv(N, 16 * gemm_stream_waves(p.mt));
     p.k_chunk = 512;
@@ -264,9 +248,8 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, size_t eb) {
   // 33..128 rows (bf16, K a multiple of 512): the slice staged by direct
   // copies in up to 160 KB of LDS, which allows 1024-wide chunks at 64 rows
   // and 512-wide at 128; splits to about one workgroup per CU
-  static const int slab_min_mt = env_int("DFLASH_GEMM_SLAB_MIN_MT", 3, 1, 8);
-  if (slab_eligible(K, eb) && p.mt >= slab_min_mt && p.mt <= 8) {
-    static const int slab_target = env_int("DFLASH_GEMM_SLAB_BLOCKS", 256, 1, 1 << 16);
+  if (slab_eligible(K, eb) && p.mt >= 3 && p.mt <= 8) {
+    constexpr int slab_target = 256;
     p.slab = true;
     p.n_tiles = (int32_t)cdiv(N, 64);
     const int64_t kmax = std::max<int64_t>(512, ((int64_t)kSlabLdsBytes / (p.mt * 16 * 2) - 8) / 512 * 512);
@@ -307,10 +290,8 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, size_t eb) {
 // for 256-wide tiles, 55% for 128, 45% for 64), the partial traffic (8 bytes
 // per output and split at 5 TB/s) and the activation re-reads (2 bytes per
 // row, K-value and column tile at 20 TB/s from L2).  Chunks are whole 64-wide
-// K-steps.  DFLASH_GEMM_TILE_BN and DFLASH_GEMM_TILE_SPLITS force either.
+// K-steps.
 SkinnyPlan plan_tile(int64_t M, int64_t N, int64_t K) {
-  static const int forced = env_int("DFLASH_GEMM_TILE_SPLITS", 0, 0, 1 << 16);
-  static const int forced_bn = env_int("DFLASH_GEMM_TILE_BN", 0, 0, 256);
   SkinnyPlan p{};
   p.tile = true;
   p.m_tiles = (int32_t)cdiv(M, 256);
@@ -321,14 +302,12 @@ SkinnyPlan plan_tile(int64_t M, int64_t N, int64_t K) {
   double best_t = 0;
   bool first = true;
   for (int bn : {256, 128, 64}) {
-    if (forced_bn > 0 && bn != forced_bn) continue;
     const double eff = bn == 256 ? 0.6 : bn == 128 ? 0.55 : 0.45;
     const int64_t n_tiles = cdiv(N, bn);
     const int64_t tiles = (int64_t)p.m_tiles * n_tiles;
     const double tile_flops = 2.0 * 256 * bn * (double)K;
     const double reread = (double)n_tiles * p.m_tiles * 256 * K * 2 / l2;
     for (int64_t sp = 1; sp <= max_splits; ++sp) {
-      if (forced > 0 && sp != std::min<int64_t>(forced, max_splits)) continue;
       const double rounds = (double)cdiv(tiles * sp, 256);
       const double t = rounds * tile_flops / sp / (peak_cu * eff) + (double)sp * M * N * 8 / bw + reread;
       if (first || t < best_t) { best_bn = bn; best_sp = sp; best_t = t; first = false; }
@@ -349,8 +328,7 @@ SkinnyPlan plan_tile(int64_t M, int64_t N, int64_t K) {
 // Depends on shapes only, so that a workspace sized from the plan fits the
 // plan the call makes.
 bool tile_eligible(int64_t M, int64_t N, int64_t K, size_t eb) {
-  static const int min_rows = env_int("DFLASH_GEMM_TILE_MIN_ROWS", 0, 0, 1 << 30);
-  const int64_t lo = min_rows > 0 ? min_rows : rows_per_problem(K, eb) + 1;
+  const int64_t lo = rows_per_problem(K, eb) + 1;
   return eb == 2 && M >= lo && K % 64 == 0 && N % 4 == 0;
 }
 
@@ -917,6 +895,51 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t eb = elem_bytes(dt);
 
+  // the attention split, planned before anything is enqueued (every key of
+  // every sequence after this call's append)
+  AttnArgs aa{};
+  aa.q_ws = q_ws; aa.cache = view_of(c); aa.part_o = part_o; aa.part_ml = part_ml;
+  aa.R = R; aa.B = B; aa.n_kv = L->n_kv; aa.group = (int32_t)p.group; aa.qrows = (int32_t)p.qrows;
+  aa.d_h = L->d_h; aa.window = L->window;
+  // an fp8 cache's key scale multiplies every score: it joins the softmax
+  // scale; its value scale multiplies every output (applied to the partials)
+  aa.scale_log2 = (float)(1.0 / std::sqrt((double)L->d_h) * 1.4426950408889634 * (fp8 ? cd.k_scale : 1.0));
+  aa.v_scale = fp8 ? cd.v_scale : 1.f;
+  int64_t items = 0;
+  {
+    std::vector<int64_t> keys(R);
+    for (int r = 0; r < R; ++r) {
+      const int64_t hi = c->len[r] + n[r] + B;
+      const int64_t lo = L->window > 0 ? std::max<int64_t>(0, c->len[r] + n[r] - L->window + 1) : 0;
+      aa.key_hi[r] = (int32_t)hi;
+      aa.key_lo[r] = (int32_t)lo;
+      aa.qpos0[r] = (int32_t)(c->len[r] + n[r]);
+      keys[r] = hi - (lo & ~int64_t(63));
+    }
+    // an item's keys may span at most kAttnMaxChunkPages pages (its page list
+    // is staged in LDS); two pages go to a chunk that does not start on a page.
+    // A ring's positions wrap every `capacity` rows: each wrap an item spans
+    // takes one more entry of its page list.
+    int64_t cap = (int64_t)1 << 30;
+    if (cd.page_size > 0) cap = std::min<int64_t>(cap, (int64_t)(kAttnMaxChunkPages - 2) * cd.page_size);
+    if (cd.ring) cap = std::min<int64_t>(cap, (int64_t)(kAttnMaxChunkPages - 2) * cd.capacity);
+    const AttnSplit sp = plan_attn_split(keys, L->n_kv, cap, fp8);
+    aa.nst = sp.nst;
+    // each item starts its blocks at (item * 37) mod its block count: with
+    // every item starting at block 0, the items running at once stream
+    // regularly spaced addresses in step (a 4 x 33K batch: 125 -> 110 us)
+    aa.rot = 37;
+    aa.chunk_keys = (int32_t)sp.chunk;
+    for (int r = 0; r < R; ++r) {
+      aa.item_base[r] = (int32_t)items;
+      aa.chunks[r] = (int32_t)std::max<int64_t>(1, cdiv(keys[r], sp.chunk));
+      items += (int64_t)aa.chunks[r] * L->n_kv;
+    }
+    aa.item_base[R] = (int32_t)items;
+    // bounded by construction for the planner's splits; a forced split may not fit
+    if (items > p.max_items) return DFLASH_ERR_SHAPE;
+  }
+
   // 1. page table entries for the rows this call appends
   hipError_t e = enqueue_page_table(c, ap, s);
 
@@ -965,50 +988,8 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
     e = staged(DFLASH_STAGE_QKV_EPILOGUE, s, true, [&] { return launch_qkv_epilogue(dt, a, s); });
   }
 
-  // 4. attention over every cached key, split into chunks
-  AttnArgs aa{};
-  if (e == hipSuccess) {
-    aa.q_ws = q_ws; aa.cache = cv; aa.part_o = part_o; aa.part_ml = part_ml;
-    aa.R = R; aa.B = B; aa.n_kv = L->n_kv; aa.group = (int32_t)p.group; aa.qrows = (int32_t)p.qrows;
-    aa.d_h = L->d_h; aa.window = L->window;
-    // an fp8 cache's key scale multiplies every score: it joins the softmax
-    // scale; its value scale multiplies every output (applied to the partials)
-    aa.scale_log2 = (float)(1.0 / std::sqrt((double)L->d_h) * 1.4426950408889634 * (fp8 ? cd.k_scale : 1.0));
-    aa.v_scale = fp8 ? cd.v_scale : 1.f;
-    std::vector<int64_t> keys(R);
-    for (int r = 0; r < R; ++r) {
-      const int64_t hi = c->len[r] + n[r] + B;
-      const int64_t lo = L->window > 0 ? std::max<int64_t>(0, c->len[r] + n[r] - L->window + 1) : 0;
-      aa.key_hi[r] = (int32_t)hi;
-      aa.key_lo[r] = (int32_t)lo;
-      aa.qpos0[r] = (int32_t)(c->len[r] + n[r]);
-      keys[r] = hi - (lo & ~int64_t(63));
-    }
-    // an item's keys may span at most kAttnMaxChunkPages pages (its page list
-    // is staged in LDS); two pages go to a chunk that does not start on a page.
-    // A ring's positions wrap every `capacity` rows: each wrap an item spans
-    // takes one more entry of its page list.
-    int64_t cap = (int64_t)1 << 30;
-    if (cd.page_size > 0) cap = std::min<int64_t>(cap, (int64_t)(kAttnMaxChunkPages - 2) * cd.page_size);
-    if (cd.ring) cap = std::min<int64_t>(cap, (int64_t)(kAttnMaxChunkPages - 2) * cd.capacity);
-    const AttnSplit sp = plan_attn_split(keys, L->n_kv, cap, fp8);
-    const int64_t chunk = sp.chunk;
-    aa.nst = sp.nst;
-    // each item starts its blocks at (item * rot) mod its block count: with
-    // every item starting at block 0, the items running at once stream
-    // regularly spaced addresses in step (a 4 x 33K batch: 125 -> 110 us).
-    // DFLASH_ATTN_ROT=0 keeps the plain order.
-    static const int rot = env_int("DFLASH_ATTN_ROT", 37, 0, 1 << 20);
-    aa.rot = rot;
-    aa.chunk_keys = (int32_t)chunk;
-    int64_t items = 0;
-    for (int r = 0; r < R; ++r) {
-      aa.item_base[r] = (int32_t)items;
-      aa.chunks[r] = (int32_t)std::max<int64_t>(1, cdiv(keys[r], chunk));
-      items += (int64_t)aa.chunks[r] * L->n_kv;
-    }
-    aa.item_base[R] = (int32_t)items;
-    if (items > p.max_items) e = hipErrorInvalidValue;  // cannot happen: bounded by construction
+  // 4. attention over every cached key, split into chunks, and the merge
+  {
     if (e == hipSuccess)
       e = staged(DFLASH_STAGE_ATTN, s, items > 0, [&] {
         return fp8 ? launch_attn_fp8(aa, (int)items, s) : launch_attn_split(dt, aa, (int)items, s);
@@ -1200,6 +1181,12 @@ int dflash_attn_plan(const int64_t* keys, int32_t R, int32_t n_kv, int64_t chunk
   out[0] = sp.chunk;
   out[1] = sp.items;
   out[2] = sp.nst;
+  return DFLASH_OK;
+}
+
+int dflash_attn_force_chunk(int64_t chunk) {
+  if (chunk != 0 && (chunk < 64 || chunk % 64 != 0 || chunk > ((int64_t)1 << 30))) return DFLASH_ERR_SHAPE;
+  g_forced_chunk.store(chunk);
   return DFLASH_OK;
 }
 

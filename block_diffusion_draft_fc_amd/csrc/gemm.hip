@@ -691,16 +691,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_stream_kernel(TileProb p) {
 }
 
 // Configurations (measured): one 16-row tile: 8 waves, 4 stages; two tiles:
-// 16 waves, 3 stages (DFLASH_GEMM_STREAM_WAVES=12 takes 12).  p.n_tiles must
-// be ceil(N / (16 * waves)).
-int gemm_stream_waves(int mt) {
-  static const int w2 = [] {
-    const char* e = std::getenv("DFLASH_GEMM_STREAM_WAVES");
-    const int v = e ? std::atoi(e) : 16;
-    return v == 12 || v == 8 ? v : 16;
-  }();
-  return mt <= 1 ? 8 : w2;
-}
+// 16 waves, 3 stages.  p.n_tiles must be ceil(N / (16 * waves)).
+int gemm_stream_waves(int mt) { return mt <= 1 ? 8 : 16; }
 
 hipError_t launch_gemm_stream(const TileProb& p, int mt, hipStream_t s) {
   const int blocks = p.n_tiles * p.splits;
@@ -708,10 +700,6 @@ hipError_t launch_gemm_stream(const TileProb& p, int mt, hipStream_t s) {
   if (p.k_chunk != kStreamKC || mt < 1 || mt > 2) return hipErrorInvalidValue;
   if (mt == 1)
     launch((gemm_stream_kernel<1, 8, 4>), dim3(blocks), dim3(64 * 8), 0, s, p);
-  else if (gemm_stream_waves(2) == 12)
-    launch((gemm_stream_kernel<2, 12, 3>), dim3(blocks), dim3(64 * 12), 0, s, p);
-  else if (gemm_stream_waves(2) == 8)
-    launch((gemm_stream_kernel<2, 8, 4>), dim3(blocks), dim3(64 * 8), 0, s, p);
   else
     launch((gemm_stream_kernel<2, 16, 3>), dim3(blocks), dim3(64 * 16), 0, s, p);
   return hipGetLastError();

@@ -353,6 +353,19 @@ int dflash_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t *ou
 int dflash_attn_plan(const int64_t *keys, int32_t R, int32_t n_kv, int64_t chunk_cap, int32_t cache_dtype,
                      int64_t *out /* [3] */);
 
+/* ------------------------------------------------------------------------
+ * Attention split override (a diagnostic for tests of split invariance: the
+ * split is exact up to rounding order, so a layer's output must not depend on
+ * it).  chunk > 0 makes every later layer call and dflash_attn_plan split
+ * each (sequence, K/V head) into items of `chunk` keys (capped as the cache
+ * requires); 0 restores the planner.  Process-wide, not synchronised with
+ * calls in flight on other threads.  chunk must be 0 or a multiple of 64 in
+ * [64, 2^30] (else DFLASH_ERR_SHAPE).  A layer call whose forced split needs
+ * more work items than its workspace holds returns DFLASH_ERR_SHAPE with
+ * nothing enqueued.
+ * ---------------------------------------------------------------------- */
+int dflash_attn_force_chunk(int64_t chunk);
+
 #ifdef __cplusplus
 }
 #endif

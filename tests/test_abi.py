@@ -352,9 +352,6 @@ def _items(keys, n_kv, chunk):
     return sum(max(1, -(-k // chunk)) * n_kv for k in keys)
 
 
-_ATTN_KNOBS = ("DFLASH_ATTN_NST", "DFLASH_ATTN_ROUNDS", "DFLASH_ATTN_TARGET_ITEMS")
-
-
 # key counts of the named workloads: one 8K decode round (8192 cached + 16
 # block keys, plus the round's context rows), four 32K requests, a 4-request
 # stack, a 16-request ragged batch, a 4096-key sliding window on a ring of
@@ -368,7 +365,6 @@ ATTN_CASES = [
 ]
 
 
-@pytest.mark.skipif(any(v in os.environ for v in _ATTN_KNOBS), reason="attention split overridden by env")
 @pytest.mark.parametrize("dtype", [L.DFLASH_BF16, L.DFLASH_FP8_E4M3], ids=["bf16", "fp8"])
 @pytest.mark.parametrize("keys,n_kv,cap", ATTN_CASES, ids=[f"{len(k)}x{max(k)}-kv{g}-cap{c}" for k, g, c in ATTN_CASES])
 def test_attn_plan_invariants(keys, n_kv, cap, dtype):
@@ -398,13 +394,28 @@ def test_attn_plan_invariants(keys, n_kv, cap, dtype):
 def test_attn_plan_headline_split():
     """The 8K decode round: 8 heads x 26 chunks of 320 keys, one round of 256
     slots at ring depth 3."""
-    if any(v in os.environ for v in _ATTN_KNOBS):
-        pytest.skip("attention split overridden by env")
     assert _attn_plan([8216], 8) == (0, 320, 208, 3)
     assert _attn_plan([8216], 8, dtype=L.DFLASH_FP8_E4M3) == (0, 320, 208, 3)
     # four 32K requests: 512 items for bf16, 768 for fp8 caches
     assert _attn_plan([32792] * 4, 8)[2] == 512
     assert _attn_plan([32792] * 4, 8, dtype=L.DFLASH_FP8_E4M3)[2] == 768
+
+
+def test_attn_force_chunk():
+    """The split override: multiples of 64 from 64 up, 0 restores the planner;
+    the plan then reports the forced chunk (capped by the cache's limit)."""
+    f = L.LIB.dflash_attn_force_chunk
+    for bad in (-64, 32, 100, 1 << 31):
+        assert f(bad) == L.ERR_SHAPE
+    try:
+        assert f(128) == 0
+        assert _attn_plan([8216], 8) == (0, 128, 8 * 65, 3)
+        assert _attn_plan([33024] * 4, 8, 62 * 64 * 1) == (0, 128, 4 * 8 * 258, 2)
+        assert f(1 << 20) == 0
+        assert _attn_plan([33024] * 4, 8, 62 * 256)[1:3] == (62 * 256, 4 * 8 * 3)   # capped at 62 pages
+    finally:
+        assert f(0) == 0
+    assert _attn_plan([8216], 8) == (0, 320, 208, 3)
 
 
 def test_attn_plan_validation():

@@ -72,6 +72,8 @@ def run_rounds(wl, rounds, check_cache=True):
             assert err <= allow, f"round {rnd} layer {li}: |err| {err:.3e} > {allow:.3e} (|o| {o_norm:.3e})"
         for li, cache in enumerate(gm.caches):
             assert cache.lengths() == orc.lengths(li), f"round {rnd}: cache lengths"
+        if rounds > 8 or wl.R * wl.n_layers > 8:
+            say(f"  round {rnd}: worst rel-L2 so far {worst:.3e}")
     if check_cache:
         L0 = G.prefill_lengths(wl)
         for li, cache in enumerate(gm.caches):
@@ -191,8 +193,55 @@ def test_decode_8k_all_64_rounds():
 
 
 def test_ragged_paged_16_requests():
+    """16 rounds of the 16-request ragged paged workload, every round checked."""
     wl = configs.RAGGED_PAGED
+    run_rounds(wl, 16)
+
+
+@pytest.mark.timeout(900)
+def test_stack5_hybrid_full_size_4_rounds():
+    """The 5-layer hybrid stack at its full size: 4 requests on 32768-row
+    caches, sliding window 4096 on layers 0/2/4, one shared context, residual
+    chaining and per-layer crops, 4 rounds with every layer's output and
+    every round checked."""
+    wl = configs.STACK5_HYBRID
     run_rounds(wl, 4)
+
+
+def test_split_invariance_decode_8k():
+    """The split of the keys into work items is exact up to rounding order
+    (each item's online softmax is merged with its own maximum and sum), so a
+    round's output must not depend on it: the first 2 rounds of the decode
+    workload under the planner's split and forced chunks of 128, 256 and 1024
+    keys (520, 264 and 72 items instead of 208), each against the oracle and
+    against the planner's output."""
+    wl = configs.DECODE_8K
+    rounds = 2
+    kv = prefill_host(wl)
+    sched = G.schedule(wl)
+    orc = oracle_stack(wl, kv)
+    inputs = [G.round_inputs(wl, rnd, sched[rnd]) for rnd in range(rounds)]
+    refs = [orc.round(x, cu, H, wl.B)[0][0] for x, cu, H in inputs]
+    outs = {}
+    try:
+        for chunk in (0, 128, 256, 1024):
+            L.dflash_attn_force_chunk(chunk)
+            say(f"case split invariance chunk={chunk or 'planner'}")
+            gm = GpuModel(wl, rounds)
+            gm.prefill(kv)
+            outs[chunk] = [gm.round(x, cu, H)[0] for x, cu, H in inputs]
+            for rnd in range(rounds):
+                e = rel_l2(outs[chunk][rnd], refs[rnd])
+                assert e <= TOL["bf16"], f"chunk {chunk} round {rnd}: rel-L2 {e:.3e}"
+            del gm
+            torch.cuda.empty_cache()
+    finally:
+        L.dflash_attn_force_chunk(0)
+    for chunk in (128, 256, 1024):
+        for rnd in range(rounds):
+            e = rel_l2(outs[chunk][rnd], outs[0][rnd])
+            assert e <= 5e-3, f"chunk {chunk} round {rnd} differs from the planner's split by {e:.3e}"
+            say(f"  chunk {chunk} round {rnd}: {e:.2e} from the planner's split")
 
 
 def test_stack5_hybrid_ring_full_shapes():
