@@ -61,6 +61,7 @@ def _load() -> C.CDLL:
         "dflash_cache_crop": (C.c_int, [vp, p32, vp]),
         "dflash_kv_inject_attn_ws_bytes": (sz, [C.POINTER(LayerDesc), vp, i64, i32]),
         "dflash_kv_inject_attn": (C.c_int, [C.POINTER(LayerDesc), vp, vp, p32, vp, i32, vp, vp, sz, vp]),
+        "dflash_kv_inject_attn_noalloc": (C.c_int, [C.POINTER(LayerDesc), vp, vp, p32, vp, i32, vp, vp]),
         "dflash_draft_head_ws_bytes": (sz, [i64, i32, i64, i64, i32]),
         "dflash_draft_head": (C.c_int, [vp, i64, i32, i64, vp, C.c_float, vp, i64, i32, vp, vp, vp, sz, vp]),
         "dflash_timing_enable": (C.c_int, [C.c_int]),
@@ -235,6 +236,15 @@ def dflash_kv_inject_attn(layer: Layer, cache: Cache, C_rows, cu_ctx, H, B, out,
                                      _i32(cu_ctx), _ptr(H), int(B), _ptr(out), _ptr(ws),
                                      ws.numel() if ws is not None else 0, _stream(stream)),
            "dflash_kv_inject_attn")
+
+
+def dflash_kv_inject_attn_noalloc(layer: Layer, cache: Cache, C_rows, cu_ctx, H, B, out, stream=None) -> None:
+    """The layer call with the library's own per-GPU scratch buffer instead of
+    a caller workspace (allocates nothing)."""
+    _check(LIB.dflash_kv_inject_attn_noalloc(C.byref(layer.desc), cache.handle,
+                                             _ptr(C_rows) if C_rows is not None and C_rows.numel() else None,
+                                             _i32(cu_ctx), _ptr(H), int(B), _ptr(out), _stream(stream)),
+           "dflash_kv_inject_attn_noalloc")
 
 
 # --------------------------------------------------------------------- draft head

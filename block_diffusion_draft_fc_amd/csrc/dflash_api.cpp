@@ -86,11 +86,15 @@ namespace {
 // stage's kernels carry an event pair (hipExtLaunchKernel start/stop events,
 // stamped when the kernels themselves start and end on the GPU); a stage that
 // launched nothing records nothing.
+// Calls that must not create events (the scratch-buffer entry point) run
+// their stages without timing.
+thread_local bool t_untimed = false;
+
 template <class F>
 hipError_t staged(int stage, hipStream_t s, bool launches, F&& f) {
   (void)s;
   Timing& t = timing();
-  if (!launches) return f();
+  if (!launches || t_untimed) return f();
   bool on;
   hipEvent_t a = nullptr, b = nullptr;
   {
@@ -636,7 +640,10 @@ struct KvPlan {
   int64_t max_items;
 };
 
-KvPlan plan_kv(const dflash_layer_desc* L, const dflash_cache* c, int64_t T, int32_t B) {
+// items_exact >= 0 sizes the attention partials for exactly that many work
+// items (a call whose split is known); otherwise for the most any call with
+// these sizes may plan.
+KvPlan plan_kv(const dflash_layer_desc* L, const dflash_cache* c, int64_t T, int32_t B, int64_t items_exact = -1) {
   KvPlan p{};
   const size_t eb = elem_bytes(L->dtype);
   p.R = c->desc.n_seqs; p.B = B; p.T = T; p.RB = p.R * B;
@@ -664,6 +671,7 @@ KvPlan plan_kv(const dflash_layer_desc* L, const dflash_cache* c, int64_t T, int
   // pool, which bounds the extra items
   p.max_items = kAttnMaxTarget + 2 * p.R * L->n_kv;
   if (c->desc.page_size > 0) p.max_items += cdiv(c->desc.capacity * L->n_kv, kAttnMaxChunkPages - 2);
+  if (items_exact >= 0) p.max_items = items_exact;
   size_t o = 0;
   p.off_q = o;   o = align_up(o + (size_t)p.R * L->n_kv * p.qrows * L->d_h * eb);
   p.off_pq = o;  o = align_up(o + (p.fused_qkv ? 0 : job_part_bytes(p.gq)));
@@ -848,8 +856,15 @@ size_t dflash_kv_inject_attn_ws_bytes(const dflash_layer_desc* L, const dflash_c
   return max_over_rows(T, [&](int64_t t) { return plan_kv(L, c, t, B).total; });
 }
 
-int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const void* C, const int32_t* cu_ctx,
-                          const void* H, int32_t B, void* out, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// One layer call.  exact_ws: the workspace must hold this call's own needs
+// (the attention partials of its planned split), not the figure that holds
+// for every call with these sizes.
+int kv_inject_impl(const dflash_layer_desc* L, dflash_cache* c, const void* C, const int32_t* cu_ctx,
+                   const void* H, int32_t B, void* out, void* ws, size_t ws_bytes, void* stream, bool exact_ws) {
   int st = check_layer(L);
   if (st) return st;
   if (!c) return DFLASH_ERR_ARG;
@@ -864,8 +879,8 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
   const int64_t T = cu_ctx[cd.n_seqs];
   if (T > 0 && (!C || !aligned16(C))) return DFLASH_ERR_ARG;
   if (!H || !out || !ws || !aligned16(H) || !aligned16(out) || !aligned16(ws)) return DFLASH_ERR_ARG;
-  const KvPlan p = plan_kv(L, c, T, B);
-  if (ws_bytes < p.total) return DFLASH_ERR_WORKSPACE;
+  KvPlan p = plan_kv(L, c, T, B);
+  if (!exact_ws && ws_bytes < p.total) return DFLASH_ERR_WORKSPACE;
   std::vector<int64_t> rows(cd.n_seqs);
   for (int s = 0; s < cd.n_seqs; ++s) rows[s] = n[s] + B;
   if (cd.ring) {
@@ -884,21 +899,13 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
 
   const int32_t dt = L->dtype;
   const int R = cd.n_seqs;
-  char* w = static_cast<char*>(ws);
-  void* q_ws = w + p.off_q;
-  float* part_q = reinterpret_cast<float*>(w + p.off_pq);
-  float* part_kv = reinterpret_cast<float*>(w + p.off_pkv);
-  float* part_o = reinterpret_cast<float*>(w + p.off_po);
-  float* part_ml = reinterpret_cast<float*>(w + p.off_pml);
-  void* attn = w + p.off_attn;
-  float* part_out = reinterpret_cast<float*>(w + p.off_pout);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t eb = elem_bytes(dt);
 
   // the attention split, planned before anything is enqueued (every key of
   // every sequence after this call's append)
   AttnArgs aa{};
-  aa.q_ws = q_ws; aa.cache = view_of(c); aa.part_o = part_o; aa.part_ml = part_ml;
+  aa.cache = view_of(c);
   aa.R = R; aa.B = B; aa.n_kv = L->n_kv; aa.group = (int32_t)p.group; aa.qrows = (int32_t)p.qrows;
   aa.d_h = L->d_h; aa.window = L->window;
   // an fp8 cache's key scale multiplies every score: it joins the softmax
@@ -939,6 +946,19 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
     // bounded by construction for the planner's splits; a forced split may not fit
     if (items > p.max_items) return DFLASH_ERR_SHAPE;
   }
+  if (exact_ws) {
+    p = plan_kv(L, c, T, B, items);
+    if (ws_bytes < p.total) return DFLASH_ERR_WORKSPACE;
+  }
+  char* w = static_cast<char*>(ws);
+  void* q_ws = w + p.off_q;
+  float* part_q = reinterpret_cast<float*>(w + p.off_pq);
+  float* part_kv = reinterpret_cast<float*>(w + p.off_pkv);
+  float* part_o = reinterpret_cast<float*>(w + p.off_po);
+  float* part_ml = reinterpret_cast<float*>(w + p.off_pml);
+  void* attn = w + p.off_attn;
+  float* part_out = reinterpret_cast<float*>(w + p.off_pout);
+  aa.q_ws = q_ws; aa.part_o = part_o; aa.part_ml = part_ml;
 
   // 1. page table entries for the rows this call appends
   hipError_t e = enqueue_page_table(c, ap, s);
@@ -1023,6 +1043,56 @@ int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const voi
   if (e != hipSuccess) return DFLASH_ERR_HIP;
   commit_append(c, rows, ap);
   return DFLASH_OK;
+}
+
+// The scratch buffer of dflash_kv_inject_attn_noalloc: device memory of the
+// library's own, one copy per GPU for the life of the process.  In host code
+// `scratch` names a host-side stand-in; the device address of each GPU's copy
+// comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is ever handed to kernels.
+constexpr size_t kScratchBytes = (size_t)DFLASH_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+void* scratch_address(int* status) {
+  static std::mutex mu;
+  static void* ptr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    *status = DFLASH_ERR_HIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> g(mu);
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      *status = DFLASH_ERR_HIP;
+      return nullptr;
+    }
+    ptr[dev] = p;
+  }
+  *status = DFLASH_OK;
+  return ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const void* C, const int32_t* cu_ctx,
+                          const void* H, int32_t B, void* out, void* ws, size_t ws_bytes, void* stream) {
+  return kv_inject_impl(L, c, C, cu_ctx, H, B, out, ws, ws_bytes, stream, false);
+}
+
+int dflash_kv_inject_attn_noalloc(const dflash_layer_desc* L, dflash_cache* c, const void* C,
+                                  const int32_t* cu_ctx, const void* H, int32_t B, void* out, void* stream) {
+  int st = DFLASH_OK;
+  void* ws = scratch_address(&st);
+  if (st) return st;
+  const bool was = t_untimed;
+  t_untimed = true;
+  st = kv_inject_impl(L, c, C, cu_ctx, H, B, out, ws, kScratchBytes, stream, true);
+  t_untimed = was;
+  return st;
 }
 
 // ---------------------------------------------------------------- draft head

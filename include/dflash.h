@@ -225,6 +225,26 @@ int dflash_kv_inject_attn(const dflash_layer_desc *L, dflash_cache *c, const voi
                           void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * The same layer call without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Arguments, results and errors are those
+ * of dflash_kv_inject_attn; the workspace is a scratch buffer the library
+ * holds on each GPU it runs on, DFLASH_NOALLOC_SCRATCH_BYTES bytes from the
+ * first such call on that GPU until the process ends.  The call allocates
+ * nothing and creates no events (stage timing does not record it).  A call
+ * whose own needs (the q/k/v partial products of its rows, the attention
+ * partials of its planned split, the o_proj partials) exceed the buffer
+ * returns DFLASH_ERR_WORKSPACE with nothing enqueued; at the Qwen3-8B shapes a
+ * batch-1 decode round on caches of up to 64K keys needs about 15-30 MB.
+ * Every call on one GPU uses that GPU's one buffer: calls that overlap on a
+ * GPU (other streams or threads, or a graph replayed while another call runs)
+ * race.  Nothing in the buffer is expected to hold a value across calls.
+ * ---------------------------------------------------------------------- */
+#define DFLASH_NOALLOC_SCRATCH_BYTES (64u << 20)
+int dflash_kv_inject_attn_noalloc(const dflash_layer_desc *L, dflash_cache *c, const void *C,
+                                  const int32_t *cu_ctx, const void *H, int32_t B, void *out, void *stream);
+
+/* ------------------------------------------------------------------------
  * Draft head ("DFlash KV Injection Walkthrough", Step 5): after the last draft
  * layer, every request's block rows go through a final RMSNorm over d (gain
  * gamma_f, the formula of hidden_norm), the last B-1 of them (row 0 holds the
