@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  float* po = a.part_o + (int64_t)item * a.qrows * DH;
+  T* po = static_cast<T*>(a.part_o) + (int64_t)item * a.qrows * DH;
   const int rows_out = min(a.qrows, QS * QW);
   for (int idx = tid; idx < rows_out * DH; idx += 256) {
     const int qrow = idx / DH, d = idx - qrow * DH;
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     float acc = 0.f;
 #pragma unroll
     for (int st = 0; st < NS; ++st) acc += exp2f(s_m[st * QS + gq][row] - mu) * s_o[st * QS + gq][row][d];
-    po[idx] = acc;
+    po[idx] = from_f32<T>(acc);
   }
   if (tid < rows_out) {
     const int qrow = tid;
@@ -653,7 +653,7 @@ __global__ __launch_bounds__(256, 1) void attn_lds_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  float* po = a.part_o + (int64_t)item * a.qrows * DH;
+  bf16* po = static_cast<bf16*>(a.part_o) + (int64_t)item * a.qrows * DH;
   const int rows_out = min(a.qrows, QROWS);
   constexpr int C4 = DH / 4;
   for (int idx = tid; idx < rows_out * C4; idx += 256) {
@@ -661,7 +661,7 @@ __global__ __launch_bounds__(256, 1) void attn_lds_kernel(AttnArgs a) {
     f32x4 acc = *reinterpret_cast<const f32x4*>(s_ow(0) + row * LDO + 4 * c);
 #pragma unroll
     for (int w = 1; w < 4; ++w) acc += *reinterpret_cast<const f32x4*>(s_ow(w) + row * LDO + 4 * c);
-    *reinterpret_cast<f32x4*>(po + (int64_t)row * DH + 4 * c) = acc;
+    store4(po + (int64_t)row * DH + 4 * c, acc);
   }
   if (tid < rows_out) {
     const int row = tid;
@@ -958,9 +958,9 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_kernel(AttnArgs a) {
     m_run = m;
   }
 
-  float* po = a.part_o + (int64_t)item * a.qrows * DH;
+  bf16* po = static_cast<bf16*>(a.part_o) + (int64_t)item * a.qrows * DH;
 #pragma unroll
-  for (int d = 0; d < DT; ++d) *reinterpret_cast<f32x4*>(po + (int64_t)row * DH + 16 * d + 4 * q4) = o[d];
+  for (int d = 0; d < DT; ++d) store4(po + (int64_t)row * DH + 16 * d + 4 * q4, o[d]);
   float l = l_run;
   l += __shfl_xor(l, 16, kWave);
   l += __shfl_xor(l, 32, kWave);
@@ -1024,19 +1024,26 @@ hipError_t launch_attn_split(int dtype, const AttnArgs& a, int items, hipStream_
 // l = sum_c 2^(m_c - m) l_c, O = sum_c 2^(m_c - m) O_c / l, and stores O in the
 // row-major [R*B][n_h*d_h] order of the attention output (head h at columns
 // h*d_h .., "DFlash KV Injection Walkthrough" Step 4.5).
-// One wave per query row, lane l owning head dims 2l, 2l+1 (d_h <= 128).
+// One workgroup of one wave per query row (several per CU, so that every CU
+// streams a share of the partials), lane l owning head dims 2l, 2l+1
+// (d_h <= 128); the partials are in the layer's storage type.
 // Chunks go in groups of 32: every O load of the group and the group's (m, l)
 // loads (lane c % 32 loads chunk c's) are issued before any is used, so a row
 // costs one memory latency per 32 chunks; the group maximum and weights come
 // from wave reductions and readlane.  A group maximum above the running one
 // rescales the accumulators.
 
+__device__ __forceinline__ float2 load2f(const float* p) { return *reinterpret_cast<const float2*>(p); }
+__device__ __forceinline__ float2 load2f(const bf16* p) {
+  const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+  return float2{__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)};
+}
+
 template <typename T>
-__global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(64) void attn_combine_kernel(CombineArgs a) {
   constexpr int G = 32;
   const int lane = threadIdx.x & 63;
-  // uniform per wave (so the per-sequence tables are read with scalar loads)
-  const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row = blockIdx.x;
   const int per_seq = a.n_kv * a.group * a.B;
   if (row >= (int64_t)a.R * per_seq) return;
   const int r = (int)(row / per_seq);
@@ -1049,15 +1056,16 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
   const float* ml = a.part_ml + it0 * 2 * a.qrows + qrow;   // m_c at ml[c * mstride], l_c at + qrows
   const int64_t mstride = 2 * (int64_t)a.qrows;
   const bool act = 2 * lane < a.d_h;
-  const float* po = a.part_o + (it0 * a.qrows + qrow) * a.d_h + 2 * (act ? lane : 0);
+  const T* po = static_cast<const T*>(a.part_o) + (it0 * a.qrows + qrow) * a.d_h + 2 * (act ? lane : 0);
   const int64_t ostride = (int64_t)a.qrows * a.d_h;
 
   float mrun = -INFINITY, lrun = 0.f, o0 = 0.f, o1 = 0.f;
   for (int cb = 0; cb < n; cb += G) {
     float2 oc[G];
+    // chunks past n load chunk n - 1 again (their weight is 0): the loads
+    // stay unconditional, so all of them go out before the first is used
 #pragma unroll
-    for (int k = 0; k < G; ++k)
-      oc[k] = cb + k < n ? *reinterpret_cast<const float2*>(po + (int64_t)(cb + k) * ostride) : float2{0.f, 0.f};
+    for (int k = 0; k < G; ++k) oc[k] = load2f(po + (int64_t)min(cb + k, n - 1) * ostride);
     // issue the O loads before the (m, l) loads and their reductions
     asm volatile("" ::: "memory");
     const int c = cb + (lane & (G - 1));
@@ -1091,11 +1099,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
 hipError_t launch_attn_combine(int dtype, const CombineArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.R * a.n_kv * a.group * a.B;
   if (rows == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((rows + 3) / 4);
   if (dtype == 1)
-    launch(attn_combine_kernel<bf16>, dim3(blocks), dim3(256), 0, s, a);
+    launch(attn_combine_kernel<bf16>, dim3((unsigned)rows), dim3(64), 0, s, a);
   else
-    launch(attn_combine_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
+    launch(attn_combine_kernel<float>, dim3((unsigned)rows), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

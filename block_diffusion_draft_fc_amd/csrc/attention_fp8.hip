@@ -317,10 +317,9 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_fp8_kernel(AttnArgs a
   }
 
   if (!wave_rows) return;
-  float* po = a.part_o + (int64_t)item * a.qrows * DH;
+  bf16* po = static_cast<bf16*>(a.part_o) + (int64_t)item * a.qrows * DH;
 #pragma unroll
-  for (int d = 0; d < DT; ++d)
-    *reinterpret_cast<f32x4*>(po + (int64_t)row * DH + 16 * d + 4 * q4) = o[d] * a.v_scale;
+  for (int d = 0; d < DT; ++d) store4(po + (int64_t)row * DH + 16 * d + 4 * q4, o[d] * a.v_scale);
   float l = l_run;
   l += __shfl_xor(l, 16, kWave);
   l += __shfl_xor(l, 32, kWave);

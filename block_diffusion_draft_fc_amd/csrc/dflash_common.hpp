@@ -7,6 +7,7 @@ typedef __bf16 bf16;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(8 * sizeof(float)))) float f32x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 
 namespace dflash {
 
@@ -33,6 +34,11 @@ __device__ __forceinline__ void store8(float* p, f32x8 v) {
   *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
 }
 template <typename T> __device__ __forceinline__ vec8_t<T> zero8() { return vec8_t<T>{}; }
+// Four fp32 values stored in the storage type (rounded to nearest even for bf16).
+__device__ __forceinline__ void store4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+__device__ __forceinline__ void store4(bf16* p, f32x4 v) {
+  *reinterpret_cast<bf16x4*>(p) = __builtin_convertvector(v, bf16x4);
+}
 
 template <typename T> __device__ __forceinline__ float to_f32(T x) { return static_cast<float>(x); }
 template <typename T> __device__ __forceinline__ T from_f32(float x) { return static_cast<T>(x); }

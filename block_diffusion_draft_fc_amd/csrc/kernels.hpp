@@ -154,7 +154,8 @@ constexpr int kAttnMaxChunkPages = 64;
 struct AttnArgs {
   const void* q_ws;      // [R][n_kv][qrows][d_h]
   CacheView cache;
-  float* part_o;         // [items][qrows][d_h]
+  void* part_o;          // [items][qrows][d_h], unnormalised O in the layer's
+                         // storage type (bf16 or fp32)
   float* part_ml;        // [items][2][qrows]
   int32_t R, B, n_kv, group, qrows, d_h;
   int32_t chunk_keys;    // keys per work item (multiple of 64)
@@ -175,7 +176,7 @@ hipError_t launch_attn_split(int dtype, const AttnArgs& a, int items, hipStream_
 hipError_t launch_attn_fp8(const AttnArgs& a, int items, hipStream_t s);
 
 struct CombineArgs {
-  const float* part_o;
+  const void* part_o;    // the storage type of the layer
   const float* part_ml;
   void* attn;            // [R*B][n_h*d_h]
   int32_t R, B, n_kv, group, qrows, d_h;
