@@ -60,6 +60,10 @@ def parse():
                          "(bf16 or fp8) cache, print its JSON and exit (for profiling one kernel)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 8 times (scales HBM counters)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="no GPU work: read the rocprofv3 outputs under DIR (prof_decode/, pmc_FETCH_SIZE/, "
+                         "pmc_WRITE_SIZE/, pmc_copy_FETCH_SIZE/, pmc_copy_WRITE_SIZE/ as written by the commands "
+                         "in profiles/) and write the kernel-trace and HBM-traffic summaries into profiles/")
     return ap.parse_args()
 
 
@@ -118,33 +122,66 @@ def traffic_record():
 
 # ---------------------------------------------------------------------------- CPU oracle leg
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, budget_s):
     """The fp64 oracle on the host cores, over the first rounds of the same
-    schedule until `budget_s` seconds of round work have run."""
+    schedule until `budget_s` seconds of round work have run with every
+    BLAS thread, then a third of that budget on one thread.  The oracle's
+    prefill (building its cache of the 8192 prefilled rows) is timed apart."""
     from oracle import dflash_oracle as O
     from workloads import generate as G
 
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        blas = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = 1
+        threadpool_limits, blas = None, 1
+    cores = len(os.sched_getaffinity(0))
     fc, lw = G.fc_weights(wl), G.layer_weights(wl, 0)
     p = O.LayerParams(lw["w_qkv"].astype(np.float64), lw["w_o"].astype(np.float64), lw["gamma_q"],
                       lw["gamma_k"], wl.n_h, wl.n_kv, wl.d_h, wl.eps, wl.rope_theta, 0)
     K0, V0 = G.prefill_kv(wl, 0, 0, wl.prefill_len)
-    stack = O.OracleStack([p], fc["w_fc"].astype(np.float64), fc["gamma_h"], wl.eps, [[K0]], [[V0]])
     sched = G.schedule(wl)
-    done, spent = 0, 0.0
-    while spent < budget_s and done < wl.rounds:
-        x, cu, H = G.round_inputs(wl, done, sched[done])
-        t0 = time.perf_counter()
-        stack.round(x, cu, H, wl.B)
-        spent += time.perf_counter() - t0
-        done += 1
-    return {"value": done / spent, "unit": "draft blocks/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {done} of the {wl.rounds} seeded rounds (8192-row cache, 1-16 new rows, block 16), "
-                      f"fp64 NumPy, {spent:.1f} s of round work; weight set-up excluded"}
+
+    def run(budget):
+        """Rounds of the cycle in order (starting over from the prefill after
+        round 63) until `budget` seconds of round work."""
+        done, spent, prefill_s = 0, 0.0, 0.0
+        while spent < budget:
+            r = done % wl.rounds
+            if r == 0:
+                t0 = time.perf_counter()
+                stack = O.OracleStack([p], fc["w_fc"].astype(np.float64), fc["gamma_h"], wl.eps, [[K0]], [[V0]])
+                prefill_s = time.perf_counter() - t0
+            x, cu, H = G.round_inputs(wl, r, sched[r])
+            t0 = time.perf_counter()
+            stack.round(x, cu, H, wl.B)
+            spent += time.perf_counter() - t0
+            done += 1
+        return done, spent, prefill_s
+
+    done, spent, prefill_s = run(budget_s)
+    single = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            d1, s1, _ = run(budget_s / 3)
+        single = {"value": round(d1 / s1, 3), "unit": "draft blocks/s", "threads": 1,
+                  "sample": f"{d1} rounds of the cycle, {s1:.1f} s"}
+    return {"value": round(done / spent, 3), "unit": "draft blocks/s", "cores": cores, "kind": "oracle",
+            "blas_threads": blas, "cpu_model": _cpu_model(),
+            "sample": f"{done} rounds of the {wl.rounds}-round seeded cycle (8192-row cache, 1-16 new rows, block 16), "
+                      f"fp64 NumPy on {blas} BLAS threads of {cores} cores, {spent:.1f} s of round work; "
+                      f"weight set-up and the oracle's prefill excluded",
+            "prefill_s": round(prefill_s, 3), "single_thread": single}
 
 
 # ---------------------------------------------------------------------------- fresh-context projections
@@ -475,6 +512,176 @@ def draft_head_pass(iters):
     return res
 
 
+# ---------------------------------------------------------------------------- profile summaries
+
+PROFILE_CMDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_decode -o bench -- "
+             "python3 -u bench.py --no-fresh-ctx --no-batched --no-cpu-baseline",
+    "pmc": "rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{c} -o bench -- python3 -u bench.py "
+           "--no-fresh-ctx --no-batched --no-cpu-baseline --mode eager --steps 32 --warmup 4",
+    "copy": "rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_copy_{c} -o copy -- python3 -u bench.py "
+            "--copy-calibration",
+}
+ATTN_KERNELS = ("attn_ring64_kernel<128, 4, 2>", "attn_combine_kernel")
+
+
+def _short(name):
+    name = name.replace("void ", "")
+    return name.split("(")[0]
+
+
+def summarize_profiles(root):
+    """Kernel-trace and HBM-counter summaries of the 8K decode bench (the
+    commands in PROFILE_CMDS, run from the repository root with TMPDIR=/tmp),
+    written to profiles/.  FETCH_SIZE and WRITE_SIZE are per-dispatch KiB; each
+    is scaled by what it reads for a plain 256 MiB copy (262144 KiB each way)."""
+    import csv
+    import glob
+    import hashlib
+
+    def rows(pattern):
+        f = sorted(glob.glob(os.path.join(root, pattern)))
+        if not f:
+            raise SystemExit(f"no file matches {pattern} under {root}")
+        return list(csv.DictReader(open(f[0])))
+
+    stats = rows("prof_decode/*kernel_stats.csv")
+    lines = ["# Kernel trace: 8K decode round (decode_ctx8k_d4096_gqa32x8_dh128_block16_bf16), one MI355X", "",
+             "Command (from the repository root on the GPU box, `TMPDIR=/tmp`):", "", "```", PROFILE_CMDS["trace"],
+             "```", "",
+             "`bench.py` with only the headline workload: warmup, the timed steps as one graph and eagerly, "
+             "then the per-stage passes (one cache, then 16 cache replicas and 2 weight sets in rotation) and "
+             "the measured-peak copies and matrix product.  Durations are rocprofv3 kernel-trace begin/end "
+             "timestamps over all calls of the command.", "",
+             "| Kernel | Calls | Average µs | Min µs | Max µs | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in stats[:12]:
+        lines.append(f"| `{_short(r['Name'])[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    avg = {k: next(float(r["AverageNs"]) / 1e3 for r in stats if k in r["Name"]) for k in ATTN_KERNELS}
+    lines += ["", f"Attention launches of the round: `{ATTN_KERNELS[0]}` {avg[ATTN_KERNELS[0]]:.2f} µs + "
+                  f"`{ATTN_KERNELS[1]}` {avg[ATTN_KERNELS[1]]:.2f} µs = "
+                  f"{avg[ATTN_KERNELS[0]] + avg[ATTN_KERNELS[1]]:.2f} µs on average."]
+    open(os.path.join(ROOT, "profiles", "attn_decode_ctx8k_kernel_trace.md"), "w").write("\n".join(lines) + "\n")
+
+    def per_kernel(counter, prefix):
+        acc = {}
+        for r in rows(f"{prefix}_{counter}/*counter_collection.csv"):
+            k = _short(r["Kernel_Name"])
+            a = acc.setdefault(k, [0, 0.0])
+            a[0] += 1
+            a[1] += float(r["Counter_Value"])
+        return {k: (n, v / n) for k, (n, v) in acc.items()}
+
+    full = 262144.0
+    scale = {}
+    tables = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        cp = per_kernel(c, "pmc_copy")
+        big = max(v for _, v in cp.values())
+        scale[c] = full / big
+        tables[c] = per_kernel(c, "pmc")
+    lines = ["# HBM traffic counters: 8K decode round, one MI355X", "",
+             "Commands (one counter per run, each its own process, from the repository root, `TMPDIR=/tmp`):",
+             "", "```"] + [PROFILE_CMDS[k].format(c=c) for c in ("FETCH_SIZE", "WRITE_SIZE") for k in ("pmc", "copy")] + [
+             "```", "",
+             f"Calibration: a plain 256 MiB copy (262144 KiB read and written) reads FETCH_SIZE = "
+             f"{full / scale['FETCH_SIZE']:.1f} KiB and WRITE_SIZE = {full / scale['WRITE_SIZE']:.1f} KiB per "
+             f"dispatch, so FETCH_SIZE is scaled by {scale['FETCH_SIZE']:.3f} and WRITE_SIZE by "
+             f"{scale['WRITE_SIZE']:.3f} below.", "",
+             "| Kernel | Dispatches | FETCH KiB (raw) | Read MB (scaled) | WRITE KiB (raw) | Written MB (scaled) |",
+             "|---|---|---|---|---|---|"]
+    names = sorted(tables["FETCH_SIZE"], key=lambda k: -tables["FETCH_SIZE"][k][1] * tables["FETCH_SIZE"][k][0])
+    for k in names:
+        if not k.startswith(("dflash", "_ZN6dflash")):
+            continue
+        n, f = tables["FETCH_SIZE"][k]
+        w = tables["WRITE_SIZE"].get(k, (0, 0.0))[1]
+        lines.append(f"| `{k[:80]}` | {n} | {f:.1f} | {f * scale['FETCH_SIZE'] * 1024 / 1e6:.2f} | {w:.1f} | "
+                     f"{w * scale['WRITE_SIZE'] * 1024 / 1e6:.2f} |")
+
+    def bytes_of(c, key):
+        k = next(k for k in tables[c] if key in k)
+        return tables[c][k][1] * scale[c] * 1024
+
+    fetch = sum(bytes_of("FETCH_SIZE", k) for k in ATTN_KERNELS)
+    write = sum(bytes_of("WRITE_SIZE", k) for k in ATTN_KERNELS)
+    lines += ["", f"Attention of the round (`{ATTN_KERNELS[0]}` + `{ATTN_KERNELS[1]}`) per launch: "
+                  f"{fetch / 1e6:.2f} MB read + {write / 1e6:.2f} MB written = {(fetch + write) / 1e6:.2f} MB of "
+                  f"HBM traffic."]
+    open(os.path.join(ROOT, "profiles", "attn_decode_ctx8k_hbm_counters.md"), "w").write("\n".join(lines) + "\n")
+    src = os.path.join(ROOT, "block_diffusion_draft_fc_amd", "csrc", "attention.hip")
+    rec = {"kernels": list(ATTN_KERNELS), "workload": "decode_ctx8k_d4096_gqa32x8_dh128_block16_bf16",
+           "attention_source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+           "fetch_bytes_per_launch": int(fetch), "write_bytes_per_launch": int(write),
+           "fetch_scale": round(scale["FETCH_SIZE"], 4), "write_scale": round(scale["WRITE_SIZE"], 4),
+           "source": "profiles/attn_decode_ctx8k_hbm_counters.md",
+           "trace_us": {k: round(v, 3) for k, v in avg.items()}}
+    json.dump(rec, open(os.path.join(ROOT, "profiles", "attn_decode_ctx8k_traffic.json"), "w"), indent=1)
+    print(json.dumps(rec))
+    return 0
+
+
+# ---------------------------------------------------------------------------- measured peaks
+
+def measured_peaks(kv_bytes):
+    """The box's own figures beside the published peaks: the library's plain
+    streaming read (dflash_stream_read, timed by the same kernel-attached events
+    as the layer's kernels) of 1 GiB, and of the 8K round's K/V size over 17
+    rotated buffers (none re-read from the 256 MB Infinity Cache: what one
+    launch of that size streams from HBM); a plain 1 GiB device copy (bytes read
+    + written per second); and a large bf16 matrix product through torch
+    (hipBLASLt)."""
+    import torch
+
+    from block_diffusion_draft_fc_amd import _lib as L
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, iters):
+        fn(0)
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(iters):
+            fn(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / iters * 1e-3
+
+    def read_rate(bufs, iters):
+        L.dflash_stream_read(bufs[0])
+        torch.cuda.synchronize()
+        L.timing_reset()
+        L.timing_enable(True)
+        for i in range(iters):
+            L.dflash_stream_read(bufs[i % len(bufs)])
+        torch.cuda.synchronize()
+        st = L.timing_read()["stream_read"]
+        L.timing_enable(False)
+        return bufs[0].numel() / (st[1] * 1e-3 / st[0]) / 1e9, st[1] * 1e3 / st[0]
+
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    read_big, _ = read_rate([src], 10)
+    dst = torch.empty_like(src)
+    t = timed(lambda i: dst.copy_(src), 10)
+    copy_big = 2 * n / t / 1e9
+    del src, dst
+    m = (kv_bytes + 255) // 256 * 256
+    bufs = [torch.ones(m, dtype=torch.uint8, device="cuda") for _ in range(17)]
+    read_small, us_small = read_rate(bufs, 68)
+    del bufs
+    a = torch.randn((8192, 8192), device="cuda").to(torch.bfloat16)
+    b = torch.randn((8192, 8192), device="cuda").to(torch.bfloat16)
+    t = timed(lambda i: torch.matmul(a, b), 10)
+    mm = 2 * 8192 ** 3 / t / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    return {"hbm_read_1gib_gbps": round(read_big, 1), "hbm_copy_1gib_gbps": round(copy_big, 1),
+            "hbm_read_kv_size_cold_gbps": round(read_small, 1), "hbm_read_kv_size_cold_us": round(us_small, 3),
+            "kv_size_bytes": int(m), "bf16_matmul_8192_tflops": round(mm, 1),
+            "published": {"hbm_gbps": HBM_PEAK_GBPS, "bf16_dense_tflops": BF16_PEAK_TFLOPS}}
+
+
 # ---------------------------------------------------------------------------- GPU leg
 
 def main():
@@ -487,6 +694,8 @@ def main():
 
     if args.copy_calibration:
         return copy_calibration()
+    if args.summarize_profiles:
+        return summarize_profiles(args.summarize_profiles)
     if args.attn_pass:
         R, ctx, kv = args.attn_pass.split(",")
         if kv not in ("bf16", "fp8"):
@@ -506,16 +715,31 @@ def main():
     torch.cuda.set_device(0)
     log(f"bench: {wl.name}: generating weights and inputs")
     fc, lw = G.fc_weights(wl), G.layer_weights(wl, 0)
-    w_fc, gamma_h = to_device(fc["w_fc"], wl, dev), to_device(fc["gamma_h"], wl, dev)
-    layer = L.Layer(*(to_device(lw[k], wl, dev) for k in ("w_qkv", "w_o", "gamma_q", "gamma_k")),
-                    n_h=wl.n_h, n_kv=wl.n_kv, d_h=wl.d_h, eps=wl.eps, rope_theta=wl.rope_theta)
+
+    def weight_set():
+        w_fc, gamma_h = to_device(fc["w_fc"], wl, dev), to_device(fc["gamma_h"], wl, dev)
+        layer = L.Layer(*(to_device(lw[k], wl, dev) for k in ("w_qkv", "w_o", "gamma_q", "gamma_k")),
+                        n_h=wl.n_h, n_kv=wl.n_kv, d_h=wl.d_h, eps=wl.eps, rope_theta=wl.rope_theta)
+        return w_fc, gamma_h, layer
+
+    weights = [weight_set()]
     sched = G.schedule(wl)[:, 0]
     L0 = wl.prefill_len
-    cap = (L0 + int(sched.sum()) + wl.B + 63) // 64 * 64
-    cache = L.Cache(1, wl.n_kv, wl.d_h, torch.bfloat16, cap, device=dev)
+    grow = int(sched.sum())
+    cap = (L0 + grow + wl.B + 63) // 64 * 64
     K0, V0 = G.prefill_kv(wl, 0, 0, L0)
-    L.dflash_cache_append(cache, [0, L0], to_device(np.ascontiguousarray(K0.transpose(1, 0, 2)), wl, dev),
-                          to_device(np.ascontiguousarray(V0.transpose(1, 0, 2)), wl, dev))
+    # rows past the prefill (positions L0 .. L0 + grow) hold N(0,1) values too, so
+    # that every round's start length (up to L0 + grow) is reachable by a crop
+    K1, V1 = G.prefill_kv(wl, 0, 1, grow)
+    kr = to_device(np.ascontiguousarray(np.concatenate([K0, K1], axis=1).transpose(1, 0, 2)), wl, dev)
+    vr = to_device(np.ascontiguousarray(np.concatenate([V0, V1], axis=1).transpose(1, 0, 2)), wl, dev)
+
+    def new_cache():
+        c = L.Cache(1, wl.n_kv, wl.d_h, torch.bfloat16, cap, device=dev)
+        L.dflash_cache_append(c, [0, L0 + grow], kr, vr)
+        return c
+
+    cache = new_cache()
     xs, Hs = [], []
     for rnd in range(wl.rounds):
         x, _, H = G.round_inputs(wl, rnd, [int(sched[rnd])])
@@ -526,90 +750,65 @@ def main():
     out = torch.empty((wl.B, wl.d), dtype=torch.bfloat16, device=dev)
     ctx_ws = torch.empty(L.dflash_ctx_project_ws_bytes(max_n, wl.kd, wl.d, torch.bfloat16), dtype=torch.uint8,
                          device=dev)
-    layer_ws = torch.empty(L.dflash_kv_inject_attn_ws_bytes(layer, cache, max_n, wl.B), dtype=torch.uint8,
-                           device=dev)
+    layer_ws = torch.empty(L.dflash_kv_inject_attn_ws_bytes(weights[0][2], cache, max_n, wl.B),
+                           dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     # cache length at the start of round r of a 64-round cycle
     starts = L0 + np.concatenate([[0], np.cumsum(sched)[:-1]])
 
-    def step(i):
+    def step(i, c=None, w=None):
+        """Round i % 64 on cache c with weight set w: crop back to the round's
+        start, fc + hidden_norm, the layer, crop to the accepted prefix."""
+        c = cache if c is None else c
+        w_fc, gamma_h, layer = weights[0] if w is None else w
         r = i % wl.rounds
-        if cache.lengths()[0] != starts[r]:
-            L.dflash_cache_crop(cache, [int(starts[r])])
+        cur, st0 = c.lengths()[0], int(starts[r])
+        if cur < st0:
+            # a cold replica last ran an earlier round: bring it up to this
+            # round's start with the same rows the cache held there
+            L.dflash_cache_append(c, [0, st0 - cur], kr[cur:st0], vr[cur:st0])
+        L.dflash_cache_crop(c, [st0])
         n = int(sched[r])
         Cn = C[:n]
         L.dflash_ctx_project(xs[r], w_fc, gamma_h, wl.eps, Cn, ctx_ws)
-        L.dflash_kv_inject_attn(layer, cache, Cn, [0, n], Hs[r], wl.B, out, layer_ws)
-        L.dflash_cache_crop(cache, [int(starts[r]) + n])
+        L.dflash_kv_inject_attn(layer, c, Cn, [0, n], Hs[r], wl.B, out, layer_ws)
+        L.dflash_cache_crop(c, [st0 + n])
 
-    graphs = None
-    if args.mode in ("graph", "best"):
-        # HIP graphs of the cycle: one per round, and one holding all 64 rounds.
-        # Capture runs the library's host side (validation, planning, cache
-        # metadata) and records the kernels with their arguments; replaying
-        # round r's kernels re-writes the cache rows they wrote at capture, so
-        # the cache is cropped back first.  The crops of a round are host
-        # metadata only (nothing is enqueued), so a replay carries the whole
-        # GPU side of its rounds.  Steps replay in cycle order (every cache row
-        # is written before a later round reads it): single-round graphs up to
-        # a cycle boundary, the whole-cycle graph for each complete cycle, one
-        # launch per 64 rounds.
-        log("bench: capturing one graph per round and one per cycle")
-        s = torch.cuda.Stream()
-        graphs = []
-        torch.cuda.synchronize()
-        for r in range(wl.rounds):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=s):
-                step(r)
-            graphs.append(g)
-        cycle = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(cycle, stream=s):
-            for r in range(wl.rounds):
-                step(r)
-        torch.cuda.synchronize()
-
-        def run_steps(first, count):
-            i, end = first, first + count
-            while i < end:
-                if i % wl.rounds == 0 and end - i >= wl.rounds:
-                    cycle.replay()
-                    i += wl.rounds
-                else:
-                    graphs[i % wl.rounds].replay()
-                    i += 1
-    else:
-        run_steps = None
-
-    def eager_steps(first, count):
-        for i in range(first, first + count):
-            step(i)
-
-    # ---------------- timed regions: K steps after W warmup steps, bracketed by
-    # synchronisation; a step's time is the slower of HIP events and wall clock
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    # with graphs, the warmup steps end on a cycle boundary (the rounds still
-    # run in cycle order), so that graph replay times whole cycles; the
-    # captures have run every round's host side, so the cache's length is past
-    # every round's start and each step crops back to its own.  Eagerly alone,
-    # the cache starts at its prefill and the steps start at round 0.
-    first = (-args.warmup) % wl.rounds if graphs is not None else 0
-
-    def timed(fn):
-        fn(first, args.warmup)
+    def timed(run):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         ev0.record()
-        fn(first + args.warmup, args.steps)
+        run()
         ev1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         return max(ev0.elapsed_time(ev1), wall * 1e3) / args.steps
 
-    graph_ms = timed(run_steps) if graphs is not None else None
-    eager_ms = timed(eager_steps) if args.mode in ("eager", "best") else None
+    # W untimed warmup steps (rounds 0 .. W-1), then the K timed steps (rounds
+    # W .. W+K-1 of the cycle), eagerly and as one HIP graph of exactly those K
+    # steps.  Capture runs the library's host side (validation, planning, cache
+    # metadata) and records the kernels with their arguments; every round crops
+    # back to its own start first, so a replay rewrites the rows it wrote at
+    # capture and the cache metadata the capture left stays valid.
+    first = args.warmup
+    for i in range(args.warmup):
+        step(i)
+    eager_ms = graph_ms = None
+    if args.mode in ("eager", "best"):
+        eager_ms = timed(lambda: [step(first + i) for i in range(args.steps)])
+    if args.mode in ("graph", "best"):
+        log(f"bench: capturing the {args.steps} timed steps as one graph")
+        s = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(args.steps):
+                step(first + i)
+        g.replay()
+        graph_ms = timed(g.replay)
     if args.mode == "graph" or (args.mode == "best" and graph_ms <= eager_ms):
         ms_per_step, mode = graph_ms, "graph"
     else:
@@ -617,49 +816,71 @@ def main():
     fmt = lambda ms: "-" if ms is None else f"{ms * 1e3:.1f}"  # noqa: E731
     log(f"bench: graph {fmt(graph_ms)} us/step, eager {fmt(eager_ms)} us/step -> {mode}")
 
-    # ---------------- per-stage times: the same steps, eagerly, with the library's
-    # HIP events recorded on the launch stream around every stage
-    L.timing_reset()
-    L.timing_enable(True)
-    for i in range(args.steps):
-        step(first + args.warmup + i)
+    # ---------------- per-stage times from the library's kernel-attached HIP
+    # events on the launch stream, over the same K rounds issued eagerly.
+    #  warm: one cache and one weight set, as in the timed steps;
+    #  cold: 16 cache replicas (each 36 MB, 16 x 36 MB > 512 MB) and 2 weight
+    #  sets in rotation, so no kernel finds its K/V or weights among the last
+    #  256 MB of traffic (the size of the Infinity Cache): the attention reads
+    #  its K/V from HBM.
+    def stage_pass(pick):
+        L.timing_reset()
+        L.timing_enable(True)
+        for i in range(args.steps):
+            step(first + i, *pick(i))
+        torch.cuda.synchronize()
+        st = L.timing_read()
+        L.timing_enable(False)
+        return st
+
+    stages_warm = stage_pass(lambda i: (None, None))
+    log("bench: cold protocol (16 cache replicas, 2 weight sets)")
+    replicas = [new_cache() for _ in range(16)]
+    weights.append(weight_set())
     torch.cuda.synchronize()
-    stages = L.timing_read()
-    L.timing_enable(False)
+    stages = stage_pass(lambda i: (replicas[i % 16], weights[i % 2]))
+    replica_bytes = sum(c.k_pool.numel() * 2 * 2 for c in replicas)
+    del replicas
+    weights.pop()
+    torch.cuda.empty_cache()
 
     # algorithmic work of the timed steps
     work = {}
     for i in range(args.steps):
-        r = (first + args.warmup + i) % wl.rounds
+        r = (first + i) % wl.rounds
         for k, v in round_work(wl, int(starts[r]), int(sched[r])).items():
             a = work.setdefault(k, {"bytes": 0, "flops": 0})
             a["bytes"] += v["bytes"]
             a["flops"] += v["flops"]
 
-    def stage_entry(name, stage_names, bound):
-        n = stages[stage_names[0]][0]
-        ms = sum(stages[s][1] for s in stage_names)
+    def stage_entry(st, name, stage_names, bound):
+        n = st[stage_names[0]][0]
+        ms = sum(st[x][1] for x in stage_names)
         us = ms / max(n, 1) * 1e3
         b, f = work[name]["bytes"] / max(n, 1), work[name]["flops"] / max(n, 1)
         gbps = b / (us * 1e-6) / 1e9 if us > 0 else 0.0
         tflops = f / (us * 1e-6) / 1e12 if us > 0 else 0.0
-        e = {"stages": list(stage_names), "launches": n, "us_per_launch": round(us, 3),
-             "alg_bytes_per_launch": int(b), "alg_flops_per_launch": int(f),
-             "gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
-             "tflops": round(tflops, 2), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 5), "bound": bound}
-        return e
+        return {"stages": list(stage_names), "launches": n, "us_per_launch": round(us, 3),
+                "alg_bytes_per_launch": int(b), "alg_flops_per_launch": int(f),
+                "gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+                "tflops": round(tflops, 2), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 5), "bound": bound}
 
-    kernels = {
-        "attn": stage_entry("attn", ["attn"], "hbm"),
-        "attn+combine": stage_entry("attn", ["attn", "attn_combine"], "hbm"),
-        "ctx_project": stage_entry("ctx_gemm", ["ctx_gemm", "ctx_reduce", "ctx_norm"], "hbm"),
-        "qkv": stage_entry("qkv_gemm", ["qkv_gemm", "qkv_epilogue"], "hbm"),
-        "o_proj": stage_entry("o_gemm", ["o_gemm", "o_reduce"], "hbm"),
-    }
-    kernels["ctx_gemm_only"] = stage_entry("ctx_gemm", ["ctx_gemm"], "hbm")
+    def kernel_table(st):
+        return {
+            "attn+combine": stage_entry(st, "attn", ["attn", "attn_combine"], "hbm"),
+            "attn": stage_entry(st, "attn", ["attn"], "hbm"),
+            "ctx_project": stage_entry(st, "ctx_gemm", ["ctx_gemm", "ctx_reduce", "ctx_norm"], "hbm"),
+            "ctx_gemm_only": stage_entry(st, "ctx_gemm", ["ctx_gemm"], "hbm"),
+            "qkv": stage_entry(st, "qkv_gemm", ["qkv_gemm", "qkv_epilogue"], "hbm"),
+            "o_proj": stage_entry(st, "o_gemm", ["o_gemm", "o_reduce"], "hbm"),
+        }
+
+    kernels, kernels_warm = kernel_table(stages), kernel_table(stages_warm)
     stage_us = {k: round(v[1] / max(v[0], 1) * 1e3, 3) for k, v in stages.items() if v[0]}
+    stage_us_warm = {k: round(v[1] / max(v[0], 1) * 1e3, 3) for k, v in stages_warm.items() if v[0]}
+    peaks = measured_peaks(work["attn"]["bytes"] // args.steps)
 
-    att = kernels["attn"]
+    att = kernels["attn+combine"]
     round_bytes = work["round"]["bytes"] / args.steps
     blocks_per_s = 1e3 / ms_per_step
     res = {
@@ -683,12 +904,27 @@ def main():
         "attn_hbm_gbps": att["gbps"],
         "attn_hbm_frac_peak": att["hbm_frac"],
         "roofline": {"bound": "hbm", "achieved": att["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": att["hbm_frac"], "traffic": traffic_record(), "kernel": "attn_ring64_kernel<128,4,2> (split-context attention, two wave groups, 4-stage ring)",
-                     "us_per_launch": att["us_per_launch"], "alg_bytes_per_launch": att["alg_bytes_per_launch"]},
+                     "frac": att["hbm_frac"], "traffic": traffic_record(),
+                     "kernel": "attention (attn_ring64_kernel<128,4,2>: split-context attention, two wave groups, "
+                               "4-stage ring) + attn_combine_kernel, the two launches of G3 + G4",
+                     "protocol": "cold: 16 cache replicas and 2 weight sets in rotation",
+                     "us_per_launch": att["us_per_launch"], "alg_bytes_per_launch": att["alg_bytes_per_launch"],
+                     "attn_us": kernels["attn"]["us_per_launch"],
+                     "combine_us": round(att["us_per_launch"] - kernels["attn"]["us_per_launch"], 3),
+                     "frac_of_measured_read_peak": round(att["gbps"] / peaks["hbm_read_1gib_gbps"], 4),
+                     "frac_of_same_size_read": round(att["gbps"] / peaks["hbm_read_kv_size_cold_gbps"], 4),
+                     "warm": {"achieved": kernels_warm["attn+combine"]["gbps"],
+                              "frac": kernels_warm["attn+combine"]["hbm_frac"],
+                              "us_per_launch": kernels_warm["attn+combine"]["us_per_launch"],
+                              "attn_us": kernels_warm["attn"]["us_per_launch"]}},
+        "measured_peaks": peaks,
         "round_alg_bytes": int(round_bytes),
         "round_hbm_gbps": round(round_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "kernels": kernels,
+        "kernels_warm": kernels_warm,
         "stage_us": stage_us,
+        "stage_us_warm": stage_us_warm,
+        "cold_replica_bytes": int(replica_bytes),
     }
     if not args.no_fresh_ctx:
         log("bench: fresh-context projections")

@@ -71,6 +71,7 @@ def _load() -> C.CDLL:
         "dflash_accept": (C.c_int, [vp, vp, i64, i32, vp, vp, vp, vp]),
         "dflash_attn_plan": (C.c_int, [C.POINTER(C.c_int64), i32, i32, i64, i32, C.POINTER(C.c_int64)]),
         "dflash_attn_force_chunk": (C.c_int, [i64]),
+        "dflash_stream_read": (C.c_int, [vp, i64, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -275,7 +276,7 @@ def dflash_accept(draft_ids, posterior, acc, next_rows=None, next_anchor=None, s
 
 STAGES = ("ctx_gemm", "ctx_reduce", "ctx_norm", "qkv_gemm", "qkv_epilogue", "attn", "attn_combine",
           "o_gemm", "o_reduce", "cache_append", "page_table", "head_norm", "head_gemm", "head_argmax",
-          "accept")
+          "accept", "stream_read")
 
 
 def timing_enable(on: bool = True) -> None:
@@ -306,6 +307,11 @@ def dflash_attn_plan(keys, n_kv: int, chunk_cap: int = 1 << 30, cache_dtype: int
     _check(LIB.dflash_attn_plan(k, len(keys), int(n_kv), int(chunk_cap), int(cache_dtype), out),
            "dflash_attn_plan")
     return {"chunk": int(out[0]), "items": int(out[1]), "nst": int(out[2])}
+
+
+def dflash_stream_read(t, stream=None) -> None:
+    """A plain streaming read of the bytes of device tensor t (measurement)."""
+    _check(LIB.dflash_stream_read(_ptr(t), t.numel() * t.element_size(), None, _stream(stream)), "dflash_stream_read")
 
 
 def dflash_attn_force_chunk(chunk: int) -> None:

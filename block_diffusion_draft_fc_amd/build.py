@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdflash.so")
 
-SOURCES = ["gemm.hip", "qkv_epilogue.hip", "attention.hip", "attention_fp8.hip", "cache.hip", "head.hip", "dflash_api.cpp"]
+SOURCES = ["gemm.hip", "qkv_epilogue.hip", "attention.hip", "attention_fp8.hip", "cache.hip", "head.hip", "probe.hip", "dflash_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

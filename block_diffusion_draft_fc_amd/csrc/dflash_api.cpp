@@ -1254,6 +1254,15 @@ int dflash_attn_plan(const int64_t* keys, int32_t R, int32_t n_kv, int64_t chunk
   return DFLASH_OK;
 }
 
+int dflash_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+  if (bytes < 0) return DFLASH_ERR_SHAPE;
+  if (bytes == 0) return DFLASH_OK;
+  if (!src || !aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3)) return DFLASH_ERR_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(
+      staged(DFLASH_STAGE_STREAM_READ, s, bytes >= 16, [&] { return launch_stream_read(src, bytes, sink, s); }));
+}
+
 int dflash_attn_force_chunk(int64_t chunk) {
   if (chunk != 0 && (chunk < 64 || chunk % 64 != 0 || chunk > ((int64_t)1 << 30))) return DFLASH_ERR_SHAPE;
   g_forced_chunk.store(chunk);

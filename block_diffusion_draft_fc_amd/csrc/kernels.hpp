@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "dflash_common.hpp"
 
 namespace dflash {
@@ -202,6 +204,10 @@ hipError_t launch_accept(const int32_t* draft, const int32_t* post, int64_t R, i
                          int32_t* next_rows, int32_t* next_anchor, hipStream_t s);
 hipError_t launch_head_argmax(const float* part, int splits, int64_t M, int64_t vocab, float* seg_val,
                               int32_t* seg_idx, int32_t* ids, float* max_logit, hipStream_t s);
+
+// ---------------------------------------------------------------- measurement
+// Reads bytes / 16 16-byte words of src (nothing is written).
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s);
 
 // ---------------------------------------------------------------- cache
 struct AppendArgs {

@@ -318,12 +318,24 @@ typedef enum {
   DFLASH_STAGE_HEAD_GEMM = 12,   /* draft head: lm_head product */
   DFLASH_STAGE_HEAD_ARGMAX = 13, /* draft head: argmax over the vocabulary */
   DFLASH_STAGE_ACCEPT = 14,      /* acceptance of a round */
-  DFLASH_STAGE_COUNT = 15
+  DFLASH_STAGE_STREAM_READ = 15, /* dflash_stream_read (measurement) */
+  DFLASH_STAGE_COUNT = 16
 } dflash_stage;
 
 int dflash_timing_enable(int on);
 int dflash_timing_read(int32_t stage, int64_t *launches, double *total_ms);
 int dflash_timing_reset(void);
+
+/* ------------------------------------------------------------------------
+ * A plain streaming read (a measurement aid): reads the first bytes / 16
+ * 16-byte words at src (device memory, 16-byte aligned) and writes nothing
+ * (sink, a device word or NULL, is only written in a case no input meets in
+ * practice).  Timed as DFLASH_STAGE_STREAM_READ, it gives the HBM read rate
+ * one launch of that size reaches, beside which the layer's bandwidth-bound
+ * kernels are judged.  bytes < 0 -> DFLASH_ERR_SHAPE; misaligned src ->
+ * DFLASH_ERR_ARG.
+ * ---------------------------------------------------------------------- */
+int dflash_stream_read(const void *src, int64_t bytes, uint32_t *sink, void *stream);
 
 /* ------------------------------------------------------------------------
  * GEMM plan inspection (a diagnostic, host only: nothing is enqueued).  The

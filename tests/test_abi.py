@@ -401,6 +401,17 @@ def test_attn_plan_headline_split():
     assert _attn_plan([32792] * 4, 8, dtype=L.DFLASH_FP8_E4M3)[2] == 768
 
 
+def test_stream_read_validation():
+    """The measurement read refuses negative sizes and misaligned sources
+    before launching anything, and a zero-byte read is a no-op."""
+    f = L.LIB.dflash_stream_read
+    assert f(C.c_void_p(16), -1, None, None) == L.ERR_SHAPE
+    assert f(C.c_void_p(8), 64, None, None) == L.ERR_ARG
+    assert f(None, 64, None, None) == L.ERR_ARG
+    assert f(C.c_void_p(16), 64, C.c_void_p(2), None) == L.ERR_ARG
+    assert f(None, 0, None, None) == 0
+
+
 def test_attn_force_chunk():
     """The split override: multiples of 64 from 64 up, 0 restores the planner;
     the plan then reports the forced chunk (capped by the cache's limit)."""
