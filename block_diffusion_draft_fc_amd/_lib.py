@@ -62,6 +62,11 @@ def _load() -> C.CDLL:
         "dflash_kv_inject_attn_ws_bytes": (sz, [C.POINTER(LayerDesc), vp, i64, i32]),
         "dflash_kv_inject_attn": (C.c_int, [C.POINTER(LayerDesc), vp, vp, p32, vp, i32, vp, vp, sz, vp]),
         "dflash_kv_inject_attn_noalloc": (C.c_int, [C.POINTER(LayerDesc), vp, vp, p32, vp, i32, vp, vp]),
+        "dflash_cache_device_begin": (C.c_int, [vp, vp, vp]),
+        "dflash_kv_inject_attn_dev_ws_bytes": (sz, [C.POINTER(LayerDesc), vp, i32, i32]),
+        "dflash_kv_inject_attn_dev": (C.c_int, [C.POINTER(LayerDesc), vp, vp, i32, vp, vp, i32, vp, vp, sz, vp]),
+        "dflash_cache_crop_tail_dev": (C.c_int, [vp, i32, vp]),
+        "dflash_cache_device_end": (C.c_int, [vp, vp]),
         "dflash_draft_head_ws_bytes": (sz, [i64, i32, i64, i64, i32]),
         "dflash_draft_head": (C.c_int, [vp, i64, i32, i64, vp, C.c_float, vp, i64, i32, vp, vp, vp, sz, vp]),
         "dflash_timing_enable": (C.c_int, [C.c_int]),
@@ -246,6 +251,33 @@ def dflash_kv_inject_attn_noalloc(layer: Layer, cache: Cache, C_rows, cu_ctx, H,
                                              _ptr(C_rows) if C_rows is not None and C_rows.numel() else None,
                                              _i32(cu_ctx), _ptr(H), int(B), _ptr(out), _stream(stream)),
            "dflash_kv_inject_attn_noalloc")
+
+
+# --------------------------------------------------------------------- device-driven rounds
+
+def dflash_cache_device_begin(cache: Cache, d_len, stream=None) -> None:
+    """Device mode: the cache's lengths live in d_len (int32 [n_seqs] device tensor)."""
+    _check(LIB.dflash_cache_device_begin(cache.handle, _ptr(d_len), _stream(stream)), "dflash_cache_device_begin")
+
+
+def dflash_kv_inject_attn_dev_ws_bytes(layer: Layer, cache: Cache, n_max: int, B: int) -> int:
+    return int(LIB.dflash_kv_inject_attn_dev_ws_bytes(C.byref(layer.desc), cache.handle, int(n_max), int(B)))
+
+
+def dflash_kv_inject_attn_dev(layer: Layer, cache: Cache, C_rows, n_max, d_rows, H, B, out, ws, stream=None) -> None:
+    """A device-driven round: C_rows [n_seqs * n_max, d], d_rows int32 [n_seqs] device tensor."""
+    _check(LIB.dflash_kv_inject_attn_dev(C.byref(layer.desc), cache.handle, _ptr(C_rows), int(n_max), _ptr(d_rows),
+                                         _ptr(H), int(B), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
+           "dflash_kv_inject_attn_dev")
+
+
+def dflash_cache_crop_tail_dev(cache: Cache, drop: int, stream=None) -> None:
+    _check(LIB.dflash_cache_crop_tail_dev(cache.handle, int(drop), _stream(stream)), "dflash_cache_crop_tail_dev")
+
+
+def dflash_cache_device_end(cache: Cache, stream=None) -> None:
+    """Leave device mode (synchronises the stream and reads the lengths back)."""
+    _check(LIB.dflash_cache_device_end(cache.handle, _stream(stream)), "dflash_cache_device_end")
 
 
 # --------------------------------------------------------------------- draft head

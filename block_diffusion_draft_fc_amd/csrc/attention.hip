@@ -57,8 +57,9 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   const int local = item - a.item_base[r];
   const int g = local / a.chunks[r];
   const int chunk = local - g * a.chunks[r];
-  const int key_hi = a.key_hi[r];
-  const int kbeg = (a.key_lo[r] & ~63) + chunk * a.chunk_keys;
+  int key_lo, key_hi, qpos0;
+  attn_seq_keys(a, r, key_lo, key_hi, qpos0);
+  const int kbeg = (key_lo & ~63) + chunk * a.chunk_keys;
   const int kend = min(kbeg + a.chunk_keys, key_hi);
   const int nblk = kend > kbeg ? (kend - kbeg + 31) >> 5 : 0;
 
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
 #pragma unroll
   for (int t = 0; t < NQW; ++t) {
     const int qrow = qg * QW + t * 16 + j16;
-    vlo[t] = a.window > 0 ? a.qpos0[r] + qrow % a.B - a.window + 1 : INT_MIN;
+    vlo[t] = a.window > 0 ? qpos0 + qrow % a.B - a.window + 1 : INT_MIN;
     m_run[t] = -INFINITY;
     l_run[t] = 0.f;
 #pragma unroll
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   }
   const T* qlds = s_q + (qg * QW + j16) * LDQ + 8 * q4;
   // the largest lower bound among the rows (the last block row's)
-  const int vis_lo_max = a.qpos0[r] + a.B - 1 - a.window + 1;
+  const int vis_lo_max = qpos0 + a.B - 1 - a.window + 1;
 
   // physical pages of the chunk, read once: fetches then take their page from
   // LDS and never wait on a global load (vector loads complete in order, so a
@@ -346,8 +347,9 @@ __global__ __launch_bounds__(256, 1) void attn_lds_kernel(AttnArgs a) {
   const int local = item - a.item_base[r];
   const int g = local / a.chunks[r];
   const int chunk = local - g * a.chunks[r];
-  const int key_hi = a.key_hi[r];
-  const int kbeg = (a.key_lo[r] & ~63) + chunk * a.chunk_keys;
+  int key_lo, key_hi, qpos0;
+  attn_seq_keys(a, r, key_lo, key_hi, qpos0);
+  const int kbeg = (key_lo & ~63) + chunk * a.chunk_keys;
   const int kend = min(kbeg + a.chunk_keys, key_hi);
   const int nblk = kend > kbeg ? (kend - kbeg + 31) >> 5 : 0;
 
@@ -369,13 +371,13 @@ __global__ __launch_bounds__(256, 1) void attn_lds_kernel(AttnArgs a) {
   for (int t = 0; t < NQT; ++t) {
     const int qrow = t * 16 + j16;
     // keys visible to the row: [vlo, key_hi), vlo = pos - window + 1 on sliding layers
-    vlo[t] = a.window > 0 ? a.qpos0[r] + qrow % a.B - a.window + 1 : INT_MIN;
+    vlo[t] = a.window > 0 ? qpos0 + qrow % a.B - a.window + 1 : INT_MIN;
     m_run[t] = -INFINITY;
     l_run[t] = 0.f;
 #pragma unroll
     for (int d = 0; d < DT; ++d) o[t][d] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const int vis_lo_max = a.qpos0[r] + a.B - a.window;   // largest row bound (sliding layers)
+  const int vis_lo_max = qpos0 + a.B - a.window;   // largest row bound (sliding layers)
 
   // physical pages of the chunk, read once so that no load of the block loop
   // depends on another global load
@@ -728,8 +730,9 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_kernel(AttnArgs a) {
   const int local = item - a.item_base[r];
   const int g = local / a.chunks[r];
   const int chunk = local - g * a.chunks[r];
-  const int key_hi = a.key_hi[r];
-  const int kbeg = (a.key_lo[r] & ~63) + chunk * a.chunk_keys;
+  int key_lo, key_hi, qpos0;
+  attn_seq_keys(a, r, key_lo, key_hi, qpos0);
+  const int kbeg = (key_lo & ~63) + chunk * a.chunk_keys;
   const int kend = min(kbeg + a.chunk_keys, key_hi);
   const int nblk = kend > kbeg ? (kend - kbeg + 63) >> 6 : 0;
 
@@ -741,8 +744,8 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_kernel(AttnArgs a) {
 
   const int row = 16 * qt + j16;
   const bf16* qbase = static_cast<const bf16*>(a.q_ws) + (int64_t)(r * a.n_kv + g) * a.qrows * DH;
-  const int vlo = a.window > 0 ? a.qpos0[r] + row % a.B - a.window + 1 : INT_MIN;
-  const int vis_lo_max = a.qpos0[r] + a.B - a.window;   // largest row bound (sliding layers)
+  const int vlo = a.window > 0 ? qpos0 + row % a.B - a.window + 1 : INT_MIN;
+  const int vis_lo_max = qpos0 + a.B - a.window;   // largest row bound (sliding layers)
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[DT];
 #pragma unroll
@@ -1088,6 +1091,9 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(CombineArgs a) {
     }
   }
   const float inv = lrun > 0.f ? 1.0f / lrun : 0.f;
+  // device-driven rounds: the round's rows are now part of every sequence
+  if (a.d_len != nullptr && row == 0)
+    for (int q = lane; q < a.R; q += 64) a.d_len[q] += a.d_rows[q] + a.B;
   if (act) {
     const int h = g * a.group + hl;
     T* dst = static_cast<T*>(a.attn) + ((int64_t)r * a.B + b) * (a.n_kv * a.group * a.d_h) + h * a.d_h + 2 * lane;

@@ -96,8 +96,9 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_fp8_kernel(AttnArgs a
   const int local = item - a.item_base[r];
   const int g = local / a.chunks[r];
   const int chunk = local - g * a.chunks[r];
-  const int key_hi = a.key_hi[r];
-  const int kbeg = (a.key_lo[r] & ~63) + chunk * a.chunk_keys;
+  int key_lo, key_hi, qpos0;
+  attn_seq_keys(a, r, key_lo, key_hi, qpos0);
+  const int kbeg = (key_lo & ~63) + chunk * a.chunk_keys;
   const int kend = min(kbeg + a.chunk_keys, key_hi);
   const int nblk = kend > kbeg ? (kend - kbeg + 63) >> 6 : 0;
 
@@ -113,8 +114,8 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_fp8_kernel(AttnArgs a
 
   const int row = 16 * qt + j16;
   const bf16* qbase = static_cast<const bf16*>(a.q_ws) + (int64_t)(r * a.n_kv + g) * a.qrows * DH;
-  const int vlo = a.window > 0 ? a.qpos0[r] + row % a.B - a.window + 1 : INT_MIN;
-  const int vis_lo_max = a.qpos0[r] + a.B - a.window;
+  const int vlo = a.window > 0 ? qpos0 + row % a.B - a.window + 1 : INT_MIN;
+  const int vis_lo_max = qpos0 + a.B - a.window;
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[DT];
 #pragma unroll

@@ -62,4 +62,17 @@ hipError_t launch_bt_update(const BtUpdateArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- device-side lengths
+__global__ __launch_bounds__(64) void len_update_kernel(LenArgs a) {
+  const int r = threadIdx.x;
+  if (r >= a.R) return;
+  a.d_len[r] = a.set ? a.value[r] : max(0, a.d_len[r] + a.delta);
+}
+
+hipError_t launch_len_update(const LenArgs& a, hipStream_t s) {
+  if (a.R <= 0) return hipSuccess;
+  launch(len_update_kernel, dim3(1), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace dflash

@@ -24,6 +24,11 @@ struct dflash_cache {
   std::vector<int64_t> written_hi;          // ring: highest position ever written + 1
   std::vector<std::vector<int32_t>> pages;   // paged: physical page per logical page
   std::set<int32_t> free_pages;             // paged: lowest first
+  // device-driven rounds: the true lengths live in d_len on the device; len
+  // then holds upper bounds of them (every round counted with its largest
+  // possible number of new rows), and the pages cover the bounds
+  int32_t* d_len = nullptr;
+  bool dev = false;
 };
 
 namespace {
@@ -521,6 +526,19 @@ hipError_t run_gemms(int32_t dt, const std::vector<GemmJob>& jobs, hipStream_t s
 
 // ---------------------------------------------------------------- cache helpers
 
+// len_s = new_len[s] (0 <= new_len[s] <= len_s, checked by the caller);
+// pages at or past ceil(new_len / page_size) return to the free list.
+void crop_host(dflash_cache* c, const int32_t* new_len) {
+  for (int s = 0; s < c->desc.n_seqs; ++s) {
+    c->len[s] = new_len[s];
+    if (c->desc.page_size > 0) {
+      const size_t keep = (size_t)cdiv(new_len[s], c->desc.page_size);
+      for (size_t j = keep; j < c->pages[s].size(); ++j) c->free_pages.insert(c->pages[s][j]);
+      c->pages[s].resize(std::min(keep, c->pages[s].size()));
+    }
+  }
+}
+
 CacheView view_of(const dflash_cache* c) {
   CacheView v{};
   v.k_pool = c->desc.k_pool;
@@ -774,7 +792,7 @@ int64_t dflash_cache_free_pages(const dflash_cache* c) {
 
 int dflash_cache_append(dflash_cache* c, const int32_t* cu_rows, const void* k_rows, const void* v_rows,
                         void* stream) {
-  if (!c) return DFLASH_ERR_ARG;
+  if (!c || c->dev) return DFLASH_ERR_ARG;
   std::vector<int64_t> n;
   int st = check_cu(cu_rows, c->desc.n_seqs, &n);
   if (st) return st;
@@ -803,17 +821,10 @@ int dflash_cache_append(dflash_cache* c, const int32_t* cu_rows, const void* k_r
 }
 
 int dflash_cache_crop(dflash_cache* c, const int32_t* new_len, void* /*stream*/) {
-  if (!c || !new_len) return DFLASH_ERR_ARG;
+  if (!c || !new_len || c->dev) return DFLASH_ERR_ARG;
   for (int s = 0; s < c->desc.n_seqs; ++s)
     if (new_len[s] < 0 || new_len[s] > c->len[s]) return DFLASH_ERR_RANGE;
-  for (int s = 0; s < c->desc.n_seqs; ++s) {
-    c->len[s] = new_len[s];
-    if (c->desc.page_size > 0) {
-      const size_t keep = (size_t)cdiv(new_len[s], c->desc.page_size);
-      for (size_t j = keep; j < c->pages[s].size(); ++j) c->free_pages.insert(c->pages[s][j]);
-      c->pages[s].resize(std::min(keep, c->pages[s].size()));
-    }
-  }
+  crop_host(c, new_len);
   return DFLASH_OK;
 }
 
@@ -863,11 +874,18 @@ namespace {
 // One layer call.  exact_ws: the workspace must hold this call's own needs
 // (the attention partials of its planned split), not the figure that holds
 // for every call with these sizes.
+// dev_rows (device [n_seqs]): a device-driven round of the cache's device
+// mode; cu_ctx then holds the fixed stride n_max (cu_ctx[r] = r * n_max) and
+// every bound below is planned for n_max new rows per sequence.
 int kv_inject_impl(const dflash_layer_desc* L, dflash_cache* c, const void* C, const int32_t* cu_ctx,
-                   const void* H, int32_t B, void* out, void* ws, size_t ws_bytes, void* stream, bool exact_ws) {
+                   const void* H, int32_t B, void* out, void* ws, size_t ws_bytes, void* stream, bool exact_ws,
+                   const int32_t* dev_rows = nullptr) {
   int st = check_layer(L);
   if (st) return st;
   if (!c) return DFLASH_ERR_ARG;
+  // a cache in device mode takes device-driven rounds only (its host
+  // lengths are bounds), and device-driven rounds need device mode
+  if (c->dev != (dev_rows != nullptr)) return DFLASH_ERR_ARG;
   const auto& cd = c->desc;
   const bool fp8 = cd.dtype == DFLASH_FP8_E4M3;
   if (cd.dtype != L->dtype && !(fp8 && L->dtype == DFLASH_BF16)) return DFLASH_ERR_DTYPE;
@@ -883,6 +901,7 @@ int kv_inject_impl(const dflash_layer_desc* L, dflash_cache* c, const void* C, c
   if (!exact_ws && ws_bytes < p.total) return DFLASH_ERR_WORKSPACE;
   std::vector<int64_t> rows(cd.n_seqs);
   for (int s = 0; s < cd.n_seqs; ++s) rows[s] = n[s] + B;
+  if (cd.ring && dev_rows != nullptr) return DFLASH_ERR_SHAPE;
   if (cd.ring) {
     // a ring holds the last `capacity` positions: the window and the new rows
     // must fit, and every key the window reaches must still be held
@@ -912,6 +931,10 @@ int kv_inject_impl(const dflash_layer_desc* L, dflash_cache* c, const void* C, c
   // scale; its value scale multiplies every output (applied to the partials)
   aa.scale_log2 = (float)(1.0 / std::sqrt((double)L->d_h) * 1.4426950408889634 * (fp8 ? cd.k_scale : 1.0));
   aa.v_scale = fp8 ? cd.v_scale : 1.f;
+  if (dev_rows != nullptr) {
+    aa.d_len = c->d_len;
+    aa.d_rows = dev_rows;
+  }
   int64_t items = 0;
   {
     std::vector<int64_t> keys(R);
@@ -922,6 +945,10 @@ int kv_inject_impl(const dflash_layer_desc* L, dflash_cache* c, const void* C, c
       aa.key_lo[r] = (int32_t)lo;
       aa.qpos0[r] = (int32_t)(c->len[r] + n[r]);
       keys[r] = hi - (lo & ~int64_t(63));
+      // device-driven rounds: the true window start lies anywhere below the
+      // bound, and a window (from its block-aligned start) spans at most
+      // window + B + 62 keys
+      if (dev_rows != nullptr && L->window > 0) keys[r] = std::min<int64_t>(hi, (int64_t)L->window + B + 62);
     }
     // an item's keys may span at most kAttnMaxChunkPages pages (its page list
     // is staged in LDS); two pages go to a chunk that does not start on a page.
@@ -1005,6 +1032,11 @@ int kv_inject_impl(const dflash_layer_desc* L, dflash_cache* c, const void* C, c
     a.cache_fp8 = fp8 ? 1 : 0;
     a.k_scale = fp8 ? cd.k_scale : 1.f;
     a.v_scale = fp8 ? cd.v_scale : 1.f;
+    if (dev_rows != nullptr) {
+      a.d_len = c->d_len;
+      a.d_rows = dev_rows;
+      a.n_max = cu_ctx[1];
+    }
     e = staged(DFLASH_STAGE_QKV_EPILOGUE, s, true, [&] { return launch_qkv_epilogue(dt, a, s); });
   }
 
@@ -1019,6 +1051,10 @@ int kv_inject_impl(const dflash_layer_desc* L, dflash_cache* c, const void* C, c
       ca.part_o = part_o; ca.part_ml = part_ml; ca.attn = attn;
       ca.R = R; ca.B = B; ca.n_kv = L->n_kv; ca.group = (int32_t)p.group; ca.qrows = (int32_t)p.qrows;
       ca.d_h = L->d_h;
+      if (dev_rows != nullptr) {
+        ca.d_len = c->d_len;
+        ca.d_rows = dev_rows;
+      }
       for (int r = 0; r <= R; ++r) ca.item_base[r] = aa.item_base[r];
       for (int r = 0; r < R; ++r) ca.chunks[r] = aa.chunks[r];
       e = staged(DFLASH_STAGE_ATTN_COMBINE, s, true, [&] { return launch_attn_combine(dt, ca, s); });
@@ -1081,6 +1117,22 @@ extern "C" {
 int dflash_kv_inject_attn(const dflash_layer_desc* L, dflash_cache* c, const void* C, const int32_t* cu_ctx,
                           const void* H, int32_t B, void* out, void* ws, size_t ws_bytes, void* stream) {
   return kv_inject_impl(L, c, C, cu_ctx, H, B, out, ws, ws_bytes, stream, false);
+}
+
+size_t dflash_kv_inject_attn_dev_ws_bytes(const dflash_layer_desc* L, const dflash_cache* c, int32_t n_max,
+                                          int32_t B) {
+  if (!c || n_max < 0) return 0;
+  return dflash_kv_inject_attn_ws_bytes(L, c, (int64_t)c->desc.n_seqs * n_max, B);
+}
+
+int dflash_kv_inject_attn_dev(const dflash_layer_desc* L, dflash_cache* c, const void* C, int32_t n_max,
+                              const int32_t* d_rows, const void* H, int32_t B, void* out, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (!c || !d_rows || (reinterpret_cast<uintptr_t>(d_rows) & 3)) return DFLASH_ERR_ARG;
+  if (n_max < 0 || n_max > (1 << 20)) return DFLASH_ERR_SHAPE;
+  std::vector<int32_t> cu(c->desc.n_seqs + 1);
+  for (int r = 0; r <= c->desc.n_seqs; ++r) cu[r] = r * n_max;
+  return kv_inject_impl(L, c, C, cu.data(), H, B, out, ws, ws_bytes, stream, false, d_rows);
 }
 
 int dflash_kv_inject_attn_noalloc(const dflash_layer_desc* L, dflash_cache* c, const void* C,
@@ -1251,6 +1303,54 @@ int dflash_attn_plan(const int64_t* keys, int32_t R, int32_t n_kv, int64_t chunk
   out[0] = sp.chunk;
   out[1] = sp.items;
   out[2] = sp.nst;
+  return DFLASH_OK;
+}
+
+int dflash_cache_device_begin(dflash_cache* c, int32_t* d_len, void* stream) {
+  if (!c || !d_len || (reinterpret_cast<uintptr_t>(d_len) & 3) || c->dev) return DFLASH_ERR_ARG;
+  if (c->desc.ring) return DFLASH_ERR_SHAPE;
+  LenArgs a{};
+  a.d_len = d_len;
+  a.R = c->desc.n_seqs;
+  a.set = 1;
+  for (int r = 0; r < a.R; ++r) a.value[r] = c->len[r];
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = staged(DFLASH_STAGE_PAGE_TABLE, s, true, [&] { return launch_len_update(a, s); });
+  if (e != hipSuccess) return DFLASH_ERR_HIP;
+  c->d_len = d_len;
+  c->dev = true;
+  return DFLASH_OK;
+}
+
+int dflash_cache_crop_tail_dev(dflash_cache* c, int32_t drop, void* stream) {
+  if (!c || !c->dev) return DFLASH_ERR_ARG;
+  if (drop < 0) return DFLASH_ERR_RANGE;
+  LenArgs a{};
+  a.d_len = c->d_len;
+  a.R = c->desc.n_seqs;
+  a.delta = -drop;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = staged(DFLASH_STAGE_PAGE_TABLE, s, true, [&] { return launch_len_update(a, s); });
+  if (e != hipSuccess) return DFLASH_ERR_HIP;
+  // the bounds drop as the true lengths do; pages past the bounds hold no row
+  std::vector<int32_t> bound(c->desc.n_seqs);
+  for (int r = 0; r < c->desc.n_seqs; ++r) bound[r] = std::max(0, c->len[r] - drop);
+  crop_host(c, bound.data());
+  return DFLASH_OK;
+}
+
+int dflash_cache_device_end(dflash_cache* c, void* stream) {
+  if (!c || !c->dev) return DFLASH_ERR_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<int32_t> v(c->desc.n_seqs);
+  if (hipStreamSynchronize(s) != hipSuccess ||
+      hipMemcpy(v.data(), c->d_len, v.size() * sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess)
+    return DFLASH_ERR_HIP;
+  for (int r = 0; r < c->desc.n_seqs; ++r)
+    if (v[r] < 0 || v[r] > c->len[r]) return DFLASH_ERR_RANGE;
+  crop_host(c, v.data());
+  c->dev = false;
+  c->d_len = nullptr;
   return DFLASH_OK;
 }
 

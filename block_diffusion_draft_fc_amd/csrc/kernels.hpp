@@ -145,6 +145,13 @@ struct QkvEpiArgs {
   SeqTable seq;
   int32_t cache_fp8;     // 1: K/V go to the cache as E4M3 bytes of x / k_scale, x / v_scale
   float k_scale, v_scale;
+  // device-driven rounds (d_rows not null): sequence r's cache length is
+  // d_len[r] and its new context rows d_rows[r] <= n_max, at rows
+  // r * n_max .. of C (the context rows past d_rows[r] are skipped); seq is
+  // then unused
+  const int32_t* d_len;
+  const int32_t* d_rows;
+  int32_t n_max;
 };
 hipError_t launch_qkv_epilogue(int dtype, const QkvEpiArgs& a, hipStream_t s);
 
@@ -171,13 +178,36 @@ struct AttnArgs {
   int32_t key_lo[kMaxSeqs];         // first key any query may see
   int32_t key_hi[kMaxSeqs];         // keys in the cache after the append
   int32_t qpos0[kMaxSeqs];          // position of block row 0
+  // device-driven rounds (d_rows not null): the lengths and new rows of the
+  // round are read from device memory and key_lo / key_hi / qpos0 follow
+  // from them (the host planned the items for upper bounds: items past a
+  // sequence's keys hold no key)
+  const int32_t* d_len;
+  const int32_t* d_rows;
 };
+
+// Key range and block position of sequence r for one launch.
+__device__ __forceinline__ void attn_seq_keys(const AttnArgs& a, int r, int& lo, int& hi, int& q0) {
+  if (a.d_rows != nullptr) {
+    q0 = a.d_len[r] + a.d_rows[r];
+    hi = q0 + a.B;
+    lo = a.window > 0 ? max(0, q0 - a.window + 1) : 0;
+  } else {
+    q0 = a.qpos0[r];
+    hi = a.key_hi[r];
+    lo = a.key_lo[r];
+  }
+}
 hipError_t launch_attn_split(int dtype, const AttnArgs& a, int items, hipStream_t s);
 // bf16 queries over an fp8 (E4M3) cache, any d_h of 64 / 128 and up to four
 // 16-row query tiles; a.nst as for the bf16 64-key-block kernel.
 hipError_t launch_attn_fp8(const AttnArgs& a, int items, hipStream_t s);
 
 struct CombineArgs {
+  // device-driven rounds: after the merge, d_len[r] += d_rows[r] + B (the
+  // round's rows are in the cache); null otherwise
+  int32_t* d_len;
+  const int32_t* d_rows;
   const void* part_o;    // the storage type of the layer
   const float* part_ml;
   void* attn;            // [R*B][n_h*d_h]
@@ -204,6 +234,16 @@ hipError_t launch_accept(const int32_t* draft, const int32_t* post, int64_t R, i
                          int32_t* next_rows, int32_t* next_anchor, hipStream_t s);
 hipError_t launch_head_argmax(const float* part, int splits, int64_t M, int64_t vocab, float* seg_val,
                               int32_t* seg_idx, int32_t* ids, float* max_logit, hipStream_t s);
+
+// ---------------------------------------------------------------- device-side cache lengths
+// d_len[r] = max(0, d_len[r] + delta) for r < R; or, with set != 0,
+// d_len[r] = value[r].
+struct LenArgs {
+  int32_t* d_len;
+  int32_t R, delta, set;
+  int32_t value[kMaxSeqs];
+};
+hipError_t launch_len_update(const LenArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- measurement
 // Reads bytes / 16 16-byte words of src (nothing is written).

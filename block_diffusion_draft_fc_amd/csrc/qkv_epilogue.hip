@@ -66,19 +66,29 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvEpiArgs a) {
     for (int s = 0; s < splits; ++s) { x0 += src[s * stride]; x1 += src[s * stride + half]; }
   }
 
-  // sequence and position of this row
+  // sequence and position of this row (device-driven rounds: lengths and new
+  // rows from device memory, context rows at a fixed stride n_max, those past
+  // a sequence's new rows skipped; the whole wave shares the row)
   int r, pos;
+  const bool dev = a.d_rows != nullptr;
   if (kind == 0) {
     r = m / a.B;
-    pos = a.seq.L[r] + a.seq.n[r] + (m - r * a.B);
+    pos = (dev ? a.d_len[r] + a.d_rows[r] : a.seq.L[r] + a.seq.n[r]) + (m - r * a.B);
   } else if (m < a.T) {
-    r = 0;
-    while (r + 1 < a.R && m >= a.seq.cu[r + 1]) ++r;
-    pos = a.seq.L[r] + (m - a.seq.cu[r]);
+    if (dev) {
+      r = m / a.n_max;
+      const int j = m - r * a.n_max;
+      if (j >= a.d_rows[r]) return;
+      pos = a.d_len[r] + j;
+    } else {
+      r = 0;
+      while (r + 1 < a.R && m >= a.seq.cu[r + 1]) ++r;
+      pos = a.seq.L[r] + (m - a.seq.cu[r]);
+    }
   } else {
     const int bm = m - a.T;
     r = bm / a.B;
-    pos = a.seq.L[r] + a.seq.n[r] + (bm - r * a.B);
+    pos = (dev ? a.d_len[r] + a.d_rows[r] : a.seq.L[r] + a.seq.n[r]) + (bm - r * a.B);
   }
 
   if (kind != 2) {

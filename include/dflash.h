@@ -225,6 +225,54 @@ int dflash_kv_inject_attn(const dflash_layer_desc *L, dflash_cache *c, const voi
                           void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Device-driven rounds ("DFlash KV Injection Walkthrough", Steps 6 and 7: the
+ * acceptance of a round fixes how many context rows the next one injects and
+ * where the cache is cut back; here both stay in device memory, so a whole
+ * sequence of rounds runs without the host reading anything and can be
+ * captured in one HIP graph).
+ *
+ * dflash_cache_device_begin puts a contiguous or paged cache (not a ring:
+ * DFLASH_ERR_SHAPE) in device mode: its lengths are written to d_len
+ * (device int32 [n_seqs], caller-owned, 4-byte aligned) and from then on
+ * d_len holds them; the host keeps upper bounds of them, counting every
+ * round with its largest number of new rows.  In device mode the host-mode
+ * calls on the cache (dflash_cache_append, dflash_cache_crop and both
+ * dflash_kv_inject_attn forms) return DFLASH_ERR_ARG, and
+ * dflash_cache_lengths / dflash_cache_block_table report the bounds and the
+ * pages reserved for them.
+ *
+ * dflash_kv_inject_attn_dev is dflash_kv_inject_attn for a round whose new
+ * context row counts are d_rows (device int32 [n_seqs], each in 0..n_max,
+ * e.g. the next_rows of dflash_accept): C holds n_seqs * n_max rows, sequence
+ * r's at rows r * n_max .. r * n_max + d_rows[r] - 1 (the rest are read by the
+ * projection and otherwise ignored); the n + B new rows of each sequence take
+ * positions d_len[r] .. as in the host form, and d_len[r] grows by
+ * d_rows[r] + B.  Capacity, page reservation and the attention split are
+ * planned for the bounds: a call that would not fit if every sequence had
+ * n_max new rows returns DFLASH_ERR_CAPACITY with nothing enqueued.  Values
+ * of d_rows outside 0..n_max are not checked (they are on the device).
+ * Workspace: dflash_kv_inject_attn_dev_ws_bytes(L, c, n_max, B).
+ *
+ * dflash_cache_crop_tail_dev cuts `drop` rows off every sequence on the
+ * device (d_len[r] = max(0, d_len[r] - drop); drop = B after a layer call is
+ * the cut back to the block start, the accepted prefix) and the bounds with
+ * them.
+ *
+ * dflash_cache_device_end synchronises `stream`, reads d_len back, makes the
+ * host metadata exact (pages past the true lengths return to the free list)
+ * and leaves device mode; a length outside 0..bound reports
+ * DFLASH_ERR_RANGE and leaves the cache in device mode.
+ * ---------------------------------------------------------------------- */
+int dflash_cache_device_begin(dflash_cache *c, int32_t *d_len, void *stream);
+size_t dflash_kv_inject_attn_dev_ws_bytes(const dflash_layer_desc *L, const dflash_cache *c, int32_t n_max,
+                                          int32_t B);
+int dflash_kv_inject_attn_dev(const dflash_layer_desc *L, dflash_cache *c, const void *C, int32_t n_max,
+                              const int32_t *d_rows, const void *H, int32_t B, void *out, void *ws, size_t ws_bytes,
+                              void *stream);
+int dflash_cache_crop_tail_dev(dflash_cache *c, int32_t drop, void *stream);
+int dflash_cache_device_end(dflash_cache *c, void *stream);
+
+/* ------------------------------------------------------------------------
  * The same layer call without a caller workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  Arguments, results and errors are those
@@ -313,7 +361,7 @@ typedef enum {
   DFLASH_STAGE_O_GEMM = 7,       /* o_proj split-K partials */
   DFLASH_STAGE_O_REDUCE = 8,     /* o_proj reduction and store */
   DFLASH_STAGE_CACHE_APPEND = 9, /* dflash_cache_append copy */
-  DFLASH_STAGE_PAGE_TABLE = 10,  /* device page-table update */
+  DFLASH_STAGE_PAGE_TABLE = 10,  /* device page-table and device-length updates */
   DFLASH_STAGE_HEAD_NORM = 11,   /* draft head: final RMSNorm of the block tails */
   DFLASH_STAGE_HEAD_GEMM = 12,   /* draft head: lm_head product */
   DFLASH_STAGE_HEAD_ARGMAX = 13, /* draft head: argmax over the vocabulary */

@@ -401,6 +401,31 @@ def test_attn_plan_headline_split():
     assert _attn_plan([32792] * 4, 8, dtype=L.DFLASH_FP8_E4M3)[2] == 768
 
 
+def test_device_mode_validation():
+    """Device-driven rounds: a ring cannot enter device mode, a null or
+    misaligned length array is refused, and the device-round calls need device
+    mode; all checked before anything is enqueued."""
+    rc, ring = _cache(ring=1)
+    assert rc == 0
+    assert L.LIB.dflash_cache_device_begin(ring, FAKE, None) == L.ERR_SHAPE
+    rc, h = _cache()
+    assert rc == 0
+    assert L.LIB.dflash_cache_device_begin(h, None, None) == L.ERR_ARG
+    assert L.LIB.dflash_cache_device_begin(h, C.c_void_p(FAKE + 2), None) == L.ERR_ARG
+    assert L.LIB.dflash_cache_crop_tail_dev(h, 4, None) == L.ERR_ARG
+    assert L.LIB.dflash_cache_device_end(h, None) == L.ERR_ARG
+    lay = L.LayerDesc(512, 8, 2, 64, 1e-6, 1e6, 0, L.DFLASH_BF16, 0, FAKE, FAKE, FAKE, FAKE)
+    f = L.LIB.dflash_kv_inject_attn_dev
+    assert f(C.byref(lay), h, FAKE, 4, None, FAKE, 4, FAKE, FAKE, 1 << 30, None) == L.ERR_ARG
+    assert f(C.byref(lay), h, FAKE, -1, FAKE, FAKE, 4, FAKE, FAKE, 1 << 30, None) == L.ERR_SHAPE
+    # a cache in host mode takes no device-driven round
+    assert f(C.byref(lay), h, FAKE, 4, FAKE, FAKE, 4, FAKE, FAKE, 1 << 30, None) == L.ERR_ARG
+    assert L.LIB.dflash_kv_inject_attn_dev_ws_bytes(C.byref(lay), h, 4, 4) == \
+        L.LIB.dflash_kv_inject_attn_ws_bytes(C.byref(lay), h, 8, 4)
+    for c in (ring, h):
+        L.LIB.dflash_cache_destroy(c)
+
+
 def test_stream_read_validation():
     """The measurement read refuses negative sizes and misaligned sources
     before launching anything, and a zero-byte read is a no-op."""
