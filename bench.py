@@ -512,6 +512,88 @@ def draft_head_pass(iters):
     return res
 
 
+# ---------------------------------------------------------------------------- device-driven rounds
+
+def device_driven_pass(replays=3):
+    """The 8K decode layer's 64-round cycle as device-driven rounds in one HIP
+    graph: per round dflash_ctx_project (16 padded context rows),
+    dflash_kv_inject_attn_dev (new rows from device memory), the crop back to
+    the block start on the device, and dflash_accept on seeded draft/target
+    tokens whose next_rows drive the next round; the graph opens by setting the
+    device lengths and the first round's rows back, so every replay runs the
+    same 64 rounds with no host read."""
+    import torch
+
+    from block_diffusion_draft_fc_amd import _lib as L
+    from workloads import configs, generate as G
+    from workloads.device import to_device
+
+    wl = configs.DECODE_8K
+    dev = "cuda:0"
+    R, B, n_max, rounds, vocab = 1, wl.B, wl.B, wl.rounds, configs.QWEN3_VOCAB
+    fc, lw = G.fc_weights(wl), G.layer_weights(wl, 0)
+    w_fc, g_h = to_device(fc["w_fc"], wl, dev), to_device(fc["gamma_h"], wl, dev)
+    layer = L.Layer(*(to_device(lw[k], wl, dev) for k in ("w_qkv", "w_o", "gamma_q", "gamma_k")),
+                    n_h=wl.n_h, n_kv=wl.n_kv, d_h=wl.d_h, eps=wl.eps, rope_theta=wl.rope_theta)
+    L0 = wl.prefill_len
+    cap = (L0 + rounds * n_max + B + 63) // 64 * 64
+    cache = L.Cache(1, wl.n_kv, wl.d_h, torch.bfloat16, cap, device=dev)
+    K0, V0 = G.prefill_kv(wl, 0, 0, L0)
+    L.dflash_cache_append(cache, [0, L0], to_device(np.ascontiguousarray(K0.transpose(1, 0, 2)), wl, dev),
+                          to_device(np.ascontiguousarray(V0.transpose(1, 0, 2)), wl, dev))
+    toks = [G.accept_tokens(wl.seed, R, B, vocab, rnd=i) for i in range(rounds)]
+    n0 = int(G.schedule(wl)[0][0])
+    ns = [n0] + [int(t[2][0]) + 1 for t in toks[:-1]]
+    xs, Hs, drafts, posts = [], [], [], []
+    for i in range(rounds):
+        x, _, H = G.round_inputs(wl, i, [ns[i]])
+        pad = np.zeros((n_max, wl.kd), dtype=np.float32)
+        pad[:ns[i]] = x
+        xs.append(to_device(pad, wl, dev))
+        Hs.append(to_device(H, wl, dev))
+        drafts.append(torch.from_numpy(toks[i][0].reshape(-1).copy()).to(dev))
+        posts.append(torch.from_numpy(toks[i][1]).to(dev))
+    C = torch.empty((n_max, wl.d), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((B, wl.d), dtype=torch.bfloat16, device=dev)
+    cws = torch.empty(L.dflash_ctx_project_ws_bytes(n_max, wl.kd, wl.d, torch.bfloat16), dtype=torch.uint8,
+                      device=dev)
+    ws = torch.empty(L.dflash_kv_inject_attn_dev_ws_bytes(layer, cache, n_max, B), dtype=torch.uint8, device=dev)
+    d_len = torch.zeros((1,), dtype=torch.int32, device=dev)
+    d_rows = torch.zeros((1,), dtype=torch.int32, device=dev)
+    rows0 = torch.tensor([n0], dtype=torch.int32, device=dev)
+    acc = torch.empty((1,), dtype=torch.int32, device=dev)
+    L.dflash_cache_device_begin(cache, d_len)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        L.dflash_cache_device_reset(cache, [L0])
+        torch.mul(rows0, 1, out=d_rows)
+        for i in range(rounds):
+            L.dflash_ctx_project(xs[i], w_fc, g_h, wl.eps, C, cws)
+            L.dflash_kv_inject_attn_dev(layer, cache, C, n_max, d_rows, Hs[i], B, out, ws)
+            L.dflash_cache_crop_tail_dev(cache, B)
+            L.dflash_accept(drafts[i], posts[i], acc, d_rows)
+    g.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(replays):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = max(ev0.elapsed_time(ev1), (time.perf_counter() - t0) * 1e3) / (replays * rounds)
+    L.dflash_cache_device_end(cache)
+    length = cache.lengths()[0]
+    res = {"workload": wl.name, "rounds_per_graph": rounds, "replays": replays, "us_per_round": round(ms * 1e3, 2),
+           "draft_blocks_per_s": round(1e3 / ms, 1), "final_length": int(length),
+           "expected_length": int(L0 + sum(ns)), "accepted_rows_per_round": round(sum(ns) / rounds, 3)}
+    del cache, layer, xs, Hs, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 # ---------------------------------------------------------------------------- profile summaries
 
 PROFILE_CMDS = {
@@ -940,6 +1022,8 @@ def main():
         res["draft_head"] = draft_head_pass(20)
         log("bench: acceptance of a 16-request round")
         res["accept"] = accept_pass(100)
+        log("bench: device-driven rounds (64 in one graph, acceptance on the device)")
+        res["device_driven_graph"] = device_driven_pass()
         log("bench: ragged 16-request paged batch")
         res["ragged_paged"] = batched_rounds(configs.RAGGED_PAGED, 16)
         log("bench: 5-layer hybrid stack, ring caches on the sliding layers")

@@ -67,6 +67,7 @@ def _load() -> C.CDLL:
         "dflash_kv_inject_attn_dev": (C.c_int, [C.POINTER(LayerDesc), vp, vp, i32, vp, vp, i32, vp, vp, sz, vp]),
         "dflash_cache_crop_tail_dev": (C.c_int, [vp, i32, vp]),
         "dflash_cache_device_end": (C.c_int, [vp, vp]),
+        "dflash_cache_device_reset": (C.c_int, [vp, p32, vp]),
         "dflash_draft_head_ws_bytes": (sz, [i64, i32, i64, i64, i32]),
         "dflash_draft_head": (C.c_int, [vp, i64, i32, i64, vp, C.c_float, vp, i64, i32, vp, vp, vp, sz, vp]),
         "dflash_timing_enable": (C.c_int, [C.c_int]),
@@ -273,6 +274,11 @@ def dflash_kv_inject_attn_dev(layer: Layer, cache: Cache, C_rows, n_max, d_rows,
 
 def dflash_cache_crop_tail_dev(cache: Cache, drop: int, stream=None) -> None:
     _check(LIB.dflash_cache_crop_tail_dev(cache.handle, int(drop), _stream(stream)), "dflash_cache_crop_tail_dev")
+
+
+def dflash_cache_device_reset(cache: Cache, host_len, stream=None) -> None:
+    """Device-side lengths set back to host_len (each at most the host bound)."""
+    _check(LIB.dflash_cache_device_reset(cache.handle, _i32(host_len), _stream(stream)), "dflash_cache_device_reset")
 
 
 def dflash_cache_device_end(cache: Cache, stream=None) -> None:

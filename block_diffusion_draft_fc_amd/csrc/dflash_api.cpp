@@ -1322,6 +1322,20 @@ int dflash_cache_device_begin(dflash_cache* c, int32_t* d_len, void* stream) {
   return DFLASH_OK;
 }
 
+int dflash_cache_device_reset(dflash_cache* c, const int32_t* host_len, void* stream) {
+  if (!c || !c->dev || !host_len) return DFLASH_ERR_ARG;
+  for (int r = 0; r < c->desc.n_seqs; ++r)
+    if (host_len[r] < 0 || host_len[r] > c->len[r]) return DFLASH_ERR_RANGE;
+  LenArgs a{};
+  a.d_len = c->d_len;
+  a.R = c->desc.n_seqs;
+  a.set = 1;
+  for (int r = 0; r < a.R; ++r) a.value[r] = host_len[r];
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = staged(DFLASH_STAGE_PAGE_TABLE, s, true, [&] { return launch_len_update(a, s); });
+  return hip_status(e);
+}
+
 int dflash_cache_crop_tail_dev(dflash_cache* c, int32_t drop, void* stream) {
   if (!c || !c->dev) return DFLASH_ERR_ARG;
   if (drop < 0) return DFLASH_ERR_RANGE;

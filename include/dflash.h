@@ -258,6 +258,11 @@ int dflash_kv_inject_attn(const dflash_layer_desc *L, dflash_cache *c, const voi
  * the cut back to the block start, the accepted prefix) and the bounds with
  * them.
  *
+ * dflash_cache_device_reset writes host_len (host [n_seqs]) into d_len on
+ * the device, each at most the current bound (else DFLASH_ERR_RANGE, nothing
+ * enqueued); the bounds stay.  Captured at the start of a graph of rounds, it
+ * makes every replay start from the same lengths.
+ *
  * dflash_cache_device_end synchronises `stream`, reads d_len back, makes the
  * host metadata exact (pages past the true lengths return to the free list)
  * and leaves device mode; a length outside 0..bound reports
@@ -270,6 +275,7 @@ int dflash_kv_inject_attn_dev(const dflash_layer_desc *L, dflash_cache *c, const
                               const int32_t *d_rows, const void *H, int32_t B, void *out, void *ws, size_t ws_bytes,
                               void *stream);
 int dflash_cache_crop_tail_dev(dflash_cache *c, int32_t drop, void *stream);
+int dflash_cache_device_reset(dflash_cache *c, const int32_t *host_len, void *stream);
 int dflash_cache_device_end(dflash_cache *c, void *stream);
 
 /* ------------------------------------------------------------------------
