@@ -607,6 +607,23 @@ PROFILE_CMDS = {
 ATTN_KERNELS = ("attn_ring64_kernel<128, 4, 2>", "attn_combine_kernel")
 
 
+def attn_kernel_name(nst, d_h):
+    """The attention kernel instance the library launches for a plan's ring
+    depth and head dim (bf16 layers), as rocprofv3 names it."""
+    if d_h == 128:
+        return "attn_ring64_kernel<128, 4, 2>" if nst >= 3 else "attn_ring64_kernel<128, 2>"
+    return "attn_ring64_kernel<64, 4>"
+
+
+def attn_kernel_label(L, keys, n_kv, d_h):
+    plan = L.dflash_attn_plan(keys, n_kv)
+    name = attn_kernel_name(plan["nst"], d_h)
+    shape = ("two wave groups, 4-stage ring" if "4, 2>" in name else
+             "one wave group, 2-stage ring" if "128, 2>" in name else "one wave group")
+    return (f"attention ({name}: split-context attention, {shape}, {plan['items']} items of "
+            f"{plan['chunk']} keys) + attn_combine_kernel, the two launches of G3 + G4")
+
+
 def _short(name):
     name = name.replace("void ", "")
     return name.split("(")[0]
@@ -987,8 +1004,7 @@ def main():
         "attn_hbm_frac_peak": att["hbm_frac"],
         "roofline": {"bound": "hbm", "achieved": att["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": att["hbm_frac"], "traffic": traffic_record(),
-                     "kernel": "attention (attn_ring64_kernel<128,4,2>: split-context attention, two wave groups, "
-                               "4-stage ring) + attn_combine_kernel, the two launches of G3 + G4",
+                     "kernel": attn_kernel_label(L, [L0 + wl.B + 8] * wl.R, wl.n_kv, wl.d_h),
                      "protocol": "cold: 16 cache replicas and 2 weight sets in rotation",
                      "us_per_launch": att["us_per_launch"], "alg_bytes_per_launch": att["alg_bytes_per_launch"],
                      "attn_us": kernels["attn"]["us_per_launch"],

@@ -911,9 +911,11 @@ hipError_t launch_gemm_resident(const FullkArgs& p, hipStream_t s) {
 // together.
 
 template <typename Tout>
+// add and out carry no __restrict__: a residual layer may write its output over
+// the block rows it adds (out == add); each element is read, then written, by
+// the same thread.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits,
-                                                            int64_t MN, const Tout* __restrict__ add,
-                                                            Tout* __restrict__ out) {
+                                                            int64_t MN, const Tout* add, Tout* out) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= MN) return;
   f32x4 s = *reinterpret_cast<const f32x4*>(part + i);
