@@ -187,8 +187,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
       float mx = sv[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      mx = max_xor32(max_xor16(mx));
       // Lazy rescale: the reference max only moves when the block max exceeds
       // it by more than 8 (log2 units), so every p <= 256, and O is rescaled
       // only on those rare blocks (wave-uniform branch), which keeps the
@@ -253,8 +252,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
 #pragma unroll
   for (int t = 0; t < NQW; ++t) {
     float l = l_run[t];
-    l += __shfl_xor(l, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
+    l = sum_xor32(sum_xor16(l));
     const int row = t * 16 + j16;
     if (q4 == 0) {
       s_m[wave][row] = m_run[t];
@@ -466,8 +464,7 @@ __global__ __launch_bounds__(256, 1) void attn_lds_kernel(AttnArgs a) {
       float mx = sv[t][0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[t][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      mx = max_xor32(max_xor16(mx));
       // a row's first visible key sets its reference (its sums are still zero)
       if (m_run[t] == -INFINITY) m_run[t] = mx;
       over |= mx > m_run[t] + 64.f;
@@ -541,8 +538,7 @@ __global__ __launch_bounds__(256, 1) void attn_lds_kernel(AttnArgs a) {
       float mx = sv[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      mx = max_xor32(max_xor16(mx));
       // Lazy rescale: the reference max only moves when the block max exceeds
       // it by more than 8 (log2 units), so every p <= 256 and O is rescaled on
       // those rare blocks only (wave-uniform branch).
@@ -646,8 +642,7 @@ __global__ __launch_bounds__(256, 1) void attn_lds_kernel(AttnArgs a) {
     for (int w = 1; w < 4; ++w) mm = fmaxf(mm, s_m[w * QROWS + row]);
     const float f = m_run[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[t] - mm);
     float l = l_run[t];
-    l += __shfl_xor(l, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
+    l = sum_xor32(sum_xor16(l));
     if (q4 == 0) s_l[wave * QROWS + row] = l * f;
 #pragma unroll
     for (int d = 0; d < DT; ++d)
@@ -858,8 +853,7 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_kernel(AttnArgs a) {
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sv[hh][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    mx = max_xor32(max_xor16(mx));
     // the reference maximum moves only when the block maximum exceeds it by
     // more than 8 (log2 units): every p <= 256, O rescaled on those blocks only
     const bool need = mx > m_run + 8.f;
@@ -964,9 +958,7 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_kernel(AttnArgs a) {
   bf16* po = static_cast<bf16*>(a.part_o) + (int64_t)item * a.qrows * DH;
 #pragma unroll
   for (int d = 0; d < DT; ++d) store4(po + (int64_t)row * DH + 16 * d + 4 * q4, o[d]);
-  float l = l_run;
-  l += __shfl_xor(l, 16, kWave);
-  l += __shfl_xor(l, 32, kWave);
+  const float l = sum_xor32(sum_xor16(l_run));
   if (q4 == 0) {
     float* pml = a.part_ml + (int64_t)item * 2 * a.qrows;
     pml[row] = m_run;
@@ -1023,18 +1015,16 @@ hipError_t launch_attn_split(int dtype, const AttnArgs& a, int items, hipStream_
 }
 
 // ---------------------------------------------------------------- combine
-// Merges the chunk partials of one query row: m = max_c m_c,
-// l = sum_c 2^(m_c - m) l_c, O = sum_c 2^(m_c - m) O_c / l, and stores O in the
+// One query row's chunk partials merged: m = max_c m_c,
+// l = sum_c 2^(m_c - m) l_c, O = sum_c 2^(m_c - m) O_c / l, stored in the
 // row-major [R*B][n_h*d_h] order of the attention output (head h at columns
-// h*d_h .., "DFlash KV Injection Walkthrough" Step 4.5).
-// One workgroup of one wave per query row (several per CU, so that every CU
-// streams a share of the partials), lane l owning head dims 2l, 2l+1
-// (d_h <= 128); the partials are in the layer's storage type.
-// Chunks go in groups of 32: every O load of the group and the group's (m, l)
-// loads (lane c % 32 loads chunk c's) are issued before any is used, so a row
-// costs one memory latency per 32 chunks; the group maximum and weights come
-// from wave reductions and readlane.  A group maximum above the running one
-// rescales the accumulators.
+// h*d_h .., "DFlash KV Injection Walkthrough" Step 4.5).  One wave per row,
+// lane l owning head dims 2l, 2l+1 (d_h <= 128); the partials are in the
+// layer's storage type.  Chunks go in groups of 32: every O load of the group
+// and the group's (m, l) loads (lane c % 32 loads chunk c's) are issued before
+// any is used, so a row costs one memory latency per 32 chunks; the group
+// maximum and weights come from wave reductions and readlane.  A group maximum
+// above the running one rescales the accumulators.
 
 __device__ __forceinline__ float2 load2f(const float* p) { return *reinterpret_cast<const float2*>(p); }
 __device__ __forceinline__ float2 load2f(const bf16* p) {
@@ -1042,42 +1032,36 @@ __device__ __forceinline__ float2 load2f(const bf16* p) {
   return float2{__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)};
 }
 
+// Row qrow of the n items it0 .. it0 + n - 1 (one (sequence, K/V head)):
+// returns this lane's two normalised output values.
 template <typename T>
-__global__ __launch_bounds__(64) void attn_combine_kernel(CombineArgs a) {
+__device__ __forceinline__ float2 merge_partials_row(const T* part_o, const float* part_ml, int64_t it0, int n,
+                                                     int qrows, int qrow, int d_h, int lane) {
   constexpr int G = 32;
-  const int lane = threadIdx.x & 63;
-  const int64_t row = blockIdx.x;
-  const int per_seq = a.n_kv * a.group * a.B;
-  if (row >= (int64_t)a.R * per_seq) return;
-  const int r = (int)(row / per_seq);
-  const int rem = (int)(row - (int64_t)r * per_seq);
-  const int g = rem / (a.group * a.B);
-  const int qrow = rem - g * a.group * a.B;
-  const int hl = qrow / a.B, b = qrow - hl * a.B;
-  const int n = a.chunks[r];
-  const int64_t it0 = a.item_base[r] + (int64_t)g * n;
-  const float* ml = a.part_ml + it0 * 2 * a.qrows + qrow;   // m_c at ml[c * mstride], l_c at + qrows
-  const int64_t mstride = 2 * (int64_t)a.qrows;
-  const bool act = 2 * lane < a.d_h;
-  const T* po = static_cast<const T*>(a.part_o) + (it0 * a.qrows + qrow) * a.d_h + 2 * (act ? lane : 0);
-  const int64_t ostride = (int64_t)a.qrows * a.d_h;
-
+  const float* ml = part_ml + it0 * 2 * qrows + qrow;   // m_c at ml[c * mstride], l_c at + qrows
+  const int mstride = 2 * qrows;
+  const bool act = 2 * lane < d_h;
+  const T* po = part_o + (it0 * qrows + qrow) * d_h + 2 * (act ? lane : 0);
+  const int ostride = qrows * d_h;
   float mrun = -INFINITY, lrun = 0.f, o0 = 0.f, o1 = 0.f;
   for (int cb = 0; cb < n; cb += G) {
     float2 oc[G];
     // chunks past n load chunk n - 1 again (their weight is 0): the loads
-    // stay unconditional, so all of them go out before the first is used
+    // stay unconditional, so all of them go out before the first is used;
+    // 32-bit offsets within a group of 32 chunks (qrows * d_h <= 64 * 128)
+    const T* pb = po + (int64_t)cb * ostride;
+    const int last = n - 1 - cb;
 #pragma unroll
-    for (int k = 0; k < G; ++k) oc[k] = load2f(po + (int64_t)min(cb + k, n - 1) * ostride);
+    for (int k = 0; k < G; ++k) oc[k] = load2f(pb + min(k, last) * ostride);
     // issue the O loads before the (m, l) loads and their reductions
     asm volatile("" ::: "memory");
     const int c = cb + (lane & (G - 1));
-    const float mc = c < n ? ml[c * mstride] : -INFINITY;
-    const float lc = c < n ? ml[c * mstride + a.qrows] : 0.f;
+    const float mc = c < n ? ml[(int64_t)c * mstride] : -INFINITY;
+    const float lc = c < n ? ml[(int64_t)c * mstride + qrows] : 0.f;
     const float mg = fmaxf(wave_max(mc), mrun);
     const float mu = mg == -INFINITY ? 0.f : mg;
-    const float wc = exp2f(mc - mu);            // weight of chunk cb + lane % 32
-    const float sa = exp2f(mrun - mu);          // rescale of the groups before
+    const float wc = __builtin_amdgcn_exp2f(mc - mu);     // weight of chunk cb + lane % 32 (0 for -inf)
+    const float sa = __builtin_amdgcn_exp2f(mrun - mu);   // rescale of the groups before
     // lanes 32..63 repeat lanes 0..31: half the wave sum is the group's
     lrun = lrun * sa + 0.5f * wave_sum(wc * lc);
     o0 *= sa;
@@ -1091,15 +1075,41 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(CombineArgs a) {
     }
   }
   const float inv = lrun > 0.f ? 1.0f / lrun : 0.f;
+  return float2{o0 * inv, o1 * inv};
+}
+
+template <typename T>
+__device__ __forceinline__ void store_merged_row(T* attn, float2 o, int r, int g, int qrow, int B, int group,
+                                                 int n_kv, int d_h, int lane) {
+  if (2 * lane >= d_h) return;
+  const int hl = qrow / B, b = qrow - hl * B;
+  const int h = g * group + hl;
+  T* dst = attn + ((int64_t)r * B + b) * (n_kv * group * d_h) + h * d_h + 2 * lane;
+  dst[0] = from_f32<T>(o.x);
+  dst[1] = from_f32<T>(o.y);
+}
+
+// The combine launch: one workgroup of one wave per query row (several per
+// CU, so that every CU streams a share of the partials).
+
+template <typename T>
+__global__ __launch_bounds__(64) void attn_combine_kernel(CombineArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x;
+  const int per_seq = a.n_kv * a.group * a.B;
+  if (row >= a.R * per_seq) return;
+  const int r = row / per_seq;
+  const int rem = row - r * per_seq;
+  const int g = rem / (a.group * a.B);
+  const int qrow = rem - g * a.group * a.B;
+  const int n = a.chunks[r];
+  const int64_t it0 = a.item_base[r] + (int64_t)g * n;
+  const float2 o = merge_partials_row(static_cast<const T*>(a.part_o), a.part_ml, it0, n, a.qrows, qrow, a.d_h,
+                                      lane);
   // device-driven rounds: the round's rows are now part of every sequence
   if (a.d_len != nullptr && row == 0)
     for (int q = lane; q < a.R; q += 64) a.d_len[q] += a.d_rows[q] + a.B;
-  if (act) {
-    const int h = g * a.group + hl;
-    T* dst = static_cast<T*>(a.attn) + ((int64_t)r * a.B + b) * (a.n_kv * a.group * a.d_h) + h * a.d_h + 2 * lane;
-    dst[0] = from_f32<T>(o0 * inv);
-    dst[1] = from_f32<T>(o1 * inv);
-  }
+  store_merged_row(static_cast<T*>(a.attn), o, r, g, qrow, a.B, a.group, a.n_kv, a.d_h, lane);
 }
 
 hipError_t launch_attn_combine(int dtype, const CombineArgs& a, hipStream_t s) {

@@ -227,8 +227,7 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_fp8_kernel(AttnArgs a
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sv[hh][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    mx = max_xor32(max_xor16(mx));
     // lazy maximum, as in the bf16 kernels: moved only when the block's
     // exceeds it by more than 8 (log2 units), so every p <= 256
     const bool need = mx > m_run + 8.f;
@@ -322,8 +321,7 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_fp8_kernel(AttnArgs a
 #pragma unroll
   for (int d = 0; d < DT; ++d) store4(po + (int64_t)row * DH + 16 * d + 4 * q4, o[d] * a.v_scale);
   float l = l_run;
-  l += __shfl_xor(l, 16, kWave);
-  l += __shfl_xor(l, 32, kWave);
+  l = sum_xor32(sum_xor16(l));
   if (q4 == 0) {
     float* pml = a.part_ml + (int64_t)item * 2 * a.qrows;
     pml[row] = m_run;

@@ -64,15 +64,43 @@ __device__ __forceinline__ f32x4 mma32(f32x8 a, f32x8 b, f32x4 c) {
   return c;
 }
 
+// Cross-lane exchanges without the LDS crossbar (a ds_bpermute shuffle costs
+// ~100 clocks of latency per step): v_permlane16_swap / v_permlane32_swap
+// with both operands x give each lane {x, x of lane ^ 16} (^ 32) in some
+// order, and DPP row_mirror, row_half_mirror and quad_perm pair lanes within
+// a row of 16.  Every step pairs lanes symmetrically, so all lanes of a
+// reduction end with the same bits.
+__device__ __forceinline__ float2 lane_swap16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return float2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float2 lane_swap32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return float2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float max_xor16(float x) { const float2 s = lane_swap16(x); return fmaxf(s.x, s.y); }
+__device__ __forceinline__ float max_xor32(float x) { const float2 s = lane_swap32(x); return fmaxf(s.x, s.y); }
+__device__ __forceinline__ float sum_xor16(float x) { const float2 s = lane_swap16(x); return s.x + s.y; }
+__device__ __forceinline__ float sum_xor32(float x) { const float2 s = lane_swap32(x); return s.x + s.y; }
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppRowMirror = 0x140, kDppRowHalfMirror = 0x141, kDppXor2 = 0x4e, kDppXor1 = 0xb1;
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_f<kDppRowMirror>(v);       // lane i + lane 15 - i (row of 16)
+  v += dpp_f<kDppRowHalfMirror>(v);   // + lane 7 - i (half row)
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppXor1>(v);            // the row's sum
+  return sum_xor32(sum_xor16(v));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, dpp_f<kDppRowMirror>(v));
+  v = fmaxf(v, dpp_f<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  return max_xor32(max_xor16(v));
 }
 
 // One direct-to-LDS copy of 16 bytes per lane (lane l's bytes land at
