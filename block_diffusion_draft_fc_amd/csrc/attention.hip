@@ -380,9 +380,14 @@ __global__ __launch_bounds__(256, 1) void attn_lds_kernel(AttnArgs a) {
   // physical pages of the chunk, read once so that no load of the block loop
   // depends on another global load
   const int pg0 = kbeg / a.cache.page_rows;
-  const int npg = nblk > 0 ? (kend - 1) / a.cache.page_rows - pg0 + 1 : 0;
-  for (int i = tid; i < npg; i += 256) s_page[i] = (int32_t)cache_page(a.cache, r, (pg0 + i) * a.cache.page_rows);
-  __syncthreads();
+  // a contiguous or ring cache holds sequence r at page r: no page list, and
+  // no barrier before the first copies go out
+  const bool paged = a.cache.block_table != nullptr;
+  if (paged) {
+    const int npg = nblk > 0 ? (kend - 1) / a.cache.page_rows - pg0 + 1 : 0;
+    for (int i = tid; i < npg; i += 256) s_page[i] = (int32_t)cache_page(a.cache, r, (pg0 + i) * a.cache.page_rows);
+    __syncthreads();
+  }
 
   const bf16* kpool = static_cast<const bf16*>(a.cache.k_pool);
   const bf16* vpool = static_cast<const bf16*>(a.cache.v_pool);
@@ -395,7 +400,7 @@ __global__ __launch_bounds__(256, 1) void attn_lds_kernel(AttnArgs a) {
   // capacities are multiples of 64 rows): rows past key_hi are stale rows
   // inside the allocation, masked below.
   auto issue = [&](int blk, int st) {
-    const int64_t page = s_page[blk / a.cache.page_rows - pg0];
+    const int64_t page = paged ? (int64_t)s_page[blk / a.cache.page_rows - pg0] : (int64_t)r;
     const int slot = blk % a.cache.page_rows;
     const bf16* kb = kpool + k_offset(a.cache, page, g, slot);
     const bf16* vb = vpool + v_offset(a.cache, page, g, slot);
@@ -747,9 +752,14 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_kernel(AttnArgs a) {
   for (int d = 0; d < DT; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int pg0 = kbeg / a.cache.page_rows;
-  const int npg = nblk > 0 ? (kend - 1) / a.cache.page_rows - pg0 + 1 : 0;
-  for (int i = tid; i < npg; i += 256) s_page[i] = (int32_t)cache_page(a.cache, r, (pg0 + i) * a.cache.page_rows);
-  __syncthreads();
+  // a contiguous or ring cache holds sequence r at page r: no page list, and
+  // no barrier before the first copies go out
+  const bool paged = a.cache.block_table != nullptr;
+  if (paged) {
+    const int npg = nblk > 0 ? (kend - 1) / a.cache.page_rows - pg0 + 1 : 0;
+    for (int i = tid; i < npg; i += 256) s_page[i] = (int32_t)cache_page(a.cache, r, (pg0 + i) * a.cache.page_rows);
+    __syncthreads();
+  }
   // The queries go to LDS by direct copies issued before the first blocks',
   // so the wait for block 0 covers them too and their latency overlaps the
   // blocks' (a register load would be waited for on its own: the compiler
@@ -792,7 +802,7 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_kernel(AttnArgs a) {
   auto rot_blk = [&](int b) { const int x = b + rot0; return x >= nblk ? x - nblk : x; };
   auto issue = [&](int b) {
     const int blk = kbeg + 64 * rot_blk(b);
-    const int64_t page = s_page[blk / a.cache.page_rows - pg0];
+    const int64_t page = paged ? (int64_t)s_page[blk / a.cache.page_rows - pg0] : (int64_t)r;
     const int slot = blk % a.cache.page_rows;
     const bf16* kb = kpool + k_offset(a.cache, page, g, slot);
     const bf16* vb = vpool + v_offset(a.cache, page, g, slot);

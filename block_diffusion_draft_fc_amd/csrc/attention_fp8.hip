@@ -122,9 +122,14 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_fp8_kernel(AttnArgs a
   for (int d = 0; d < DT; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int pg0 = kbeg / a.cache.page_rows;
-  const int npg = nblk > 0 ? (kend - 1) / a.cache.page_rows - pg0 + 1 : 0;
-  for (int i = tid; i < npg; i += 256) s_page[i] = (int32_t)cache_page(a.cache, r, (pg0 + i) * a.cache.page_rows);
-  __syncthreads();
+  // a contiguous or ring cache holds sequence r at page r: no page list, and
+  // no barrier before the first copies go out
+  const bool paged = a.cache.block_table != nullptr;
+  if (paged) {
+    const int npg = nblk > 0 ? (kend - 1) / a.cache.page_rows - pg0 + 1 : 0;
+    for (int i = tid; i < npg; i += 256) s_page[i] = (int32_t)cache_page(a.cache, r, (pg0 + i) * a.cache.page_rows);
+    __syncthreads();
+  }
   // Queries: direct copies into the last stage ahead of the first blocks'
   // (as in the bf16 ring kernel); step s of lane (j16, q4) holds head dims
   // QSPAN q4 + 8 s .. + 7 of row 16 wave + j16, at 16 * lane of slab s.
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_fp8_kernel(AttnArgs a
   auto rot_blk = [&](int b) { const int x = b + rot0; return x >= nblk ? x - nblk : x; };
   auto issue = [&](int b) {
     const int blk = kbeg + 64 * rot_blk(b);
-    const int64_t page = s_page[blk / a.cache.page_rows - pg0];
+    const int64_t page = paged ? (int64_t)s_page[blk / a.cache.page_rows - pg0] : (int64_t)r;
     const int slot = blk % a.cache.page_rows;
     const unsigned char* kb = kpool + k_offset(a.cache, page, g, slot);
     const unsigned char* vb = vpool + v_offset(a.cache, page, g, slot);

@@ -98,9 +98,15 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvEpiArgs a) {
     if (act) {
       x0 = x0 * rr * to_f32(gam[lane]);
       x1 = x1 * rr * to_f32(gam[lane + half]);
-      double sn, cs;
-      sincos((double)pos * a.inv_freq[lane], &sn, &cs);
-      const float c = (float)cs, sv = (float)sn;
+      // the angle pos * w in fp64 (positions reach tens of thousands: its
+      // fp32 rounding alone would shift it by ~1e-3 rad), reduced to
+      // [-pi, pi] in fp64 (k * 2pi exact to ~1e-11 rad for any position
+      // here), then sine and cosine of the reduced angle in fp32
+      const double ang = (double)pos * a.inv_freq[lane];
+      const double kr = rint(ang * 0.15915494309189535);   // 1 / (2 pi)
+      const float red = (float)fma(-kr, 6.283185307179586, ang);
+      float sv, c;
+      sincosf(red, &sv, &c);
       const float y0 = x0 * c - x1 * sv;
       const float y1 = x1 * c + x0 * sv;
       x0 = y0; x1 = y1;
