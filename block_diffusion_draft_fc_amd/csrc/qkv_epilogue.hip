@@ -28,8 +28,11 @@ __device__ __forceinline__ uint8_t to_e4m3(float x) {
   return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xff);
 }
 
+// Each wave is one short chain of loads, a reduction and stores: at most 64
+// VGPRs, so that eight waves per SIMD cover the load latency of the large rounds
+// (17152 waves for 1024 fresh context rows).
 template <typename T, bool F8>
-__global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvEpiArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void qkv_epilogue_kernel(QkvEpiArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int RB = a.R * a.B;
@@ -62,7 +65,7 @@ __global__ __launch_bounds__(256) void qkv_epilogue_kernel(QkvEpiArgs a) {
   float x0 = 0.f, x1 = 0.f;
   if (act) {
     const float* src = part + (int64_t)m * row_stride + col + lane;
-#pragma unroll 8
+#pragma unroll 4
     for (int s = 0; s < splits; ++s) { x0 += src[s * stride]; x1 += src[s * stride + half]; }
   }
 
