@@ -1118,7 +1118,7 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(CombineArgs a) {
                                       lane);
   // device-driven rounds: the round's rows are now part of every sequence
   if (a.d_len != nullptr && row == 0)
-    for (int q = lane; q < a.R; q += 64) a.d_len[q] += a.d_rows[q] + a.B;
+    for (int q = lane; q < a.R; q += 64) a.d_len[q] += dev_rows_of(a.d_rows, q, a.n_max) + a.B;
   store_merged_row(static_cast<T*>(a.attn), o, r, g, qrow, a.B, a.group, a.n_kv, a.d_h, lane);
 }
 

@@ -934,6 +934,7 @@ int kv_inject_impl(const dflash_layer_desc* L, dflash_cache* c, const void* C, c
   if (dev_rows != nullptr) {
     aa.d_len = c->d_len;
     aa.d_rows = dev_rows;
+    aa.n_max = cu_ctx[1];
   }
   int64_t items = 0;
   {
@@ -1054,6 +1055,7 @@ int kv_inject_impl(const dflash_layer_desc* L, dflash_cache* c, const void* C, c
       if (dev_rows != nullptr) {
         ca.d_len = c->d_len;
         ca.d_rows = dev_rows;
+        ca.n_max = cu_ctx[1];
       }
       for (int r = 0; r <= R; ++r) ca.item_base[r] = aa.item_base[r];
       for (int r = 0; r < R; ++r) ca.chunks[r] = aa.chunks[r];

@@ -127,6 +127,13 @@ struct SeqTable {
   int32_t n[kMaxSeqs];       // new context rows
   int32_t cu[kMaxSeqs + 1];  // context row offsets
 };
+// A device-driven round's new context rows of sequence r, clamped to the
+// 0..n_max the host planned capacity, pages and the attention split for: a
+// row count out of range then cannot move a read or write past those bounds.
+__device__ __forceinline__ int dev_rows_of(const int32_t* d_rows, int r, int n_max) {
+  return min(max(d_rows[r], 0), n_max);
+}
+
 struct QkvEpiArgs {
   // Split-K partials: Q of block row b (0 <= b < R*B), split s, column c at
   // part_q[s * q_split + b * q_row + c]; K/V of row m of [C; H] (K columns
@@ -181,15 +188,16 @@ struct AttnArgs {
   // device-driven rounds (d_rows not null): the lengths and new rows of the
   // round are read from device memory and key_lo / key_hi / qpos0 follow
   // from them (the host planned the items for upper bounds: items past a
-  // sequence's keys hold no key)
+  // sequence's keys hold no key); row counts are clamped to 0..n_max
   const int32_t* d_len;
   const int32_t* d_rows;
+  int32_t n_max;
 };
 
 // Key range and block position of sequence r for one launch.
 __device__ __forceinline__ void attn_seq_keys(const AttnArgs& a, int r, int& lo, int& hi, int& q0) {
   if (a.d_rows != nullptr) {
-    q0 = a.d_len[r] + a.d_rows[r];
+    q0 = a.d_len[r] + dev_rows_of(a.d_rows, r, a.n_max);
     hi = q0 + a.B;
     lo = a.window > 0 ? max(0, q0 - a.window + 1) : 0;
   } else {
@@ -205,9 +213,10 @@ hipError_t launch_attn_fp8(const AttnArgs& a, int items, hipStream_t s);
 
 struct CombineArgs {
   // device-driven rounds: after the merge, d_len[r] += d_rows[r] + B (the
-  // round's rows are in the cache); null otherwise
+  // round's rows are in the cache; d_rows clamped to 0..n_max); null otherwise
   int32_t* d_len;
   const int32_t* d_rows;
+  int32_t n_max;
   const void* part_o;    // the storage type of the layer
   const float* part_ml;
   void* attn;            // [R*B][n_h*d_h]

@@ -76,12 +76,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void q
   const bool dev = a.d_rows != nullptr;
   if (kind == 0) {
     r = m / a.B;
-    pos = (dev ? a.d_len[r] + a.d_rows[r] : a.seq.L[r] + a.seq.n[r]) + (m - r * a.B);
+    pos = (dev ? a.d_len[r] + dev_rows_of(a.d_rows, r, a.n_max) : a.seq.L[r] + a.seq.n[r]) + (m - r * a.B);
   } else if (m < a.T) {
     if (dev) {
       r = m / a.n_max;
       const int j = m - r * a.n_max;
-      if (j >= a.d_rows[r]) return;
+      if (j >= dev_rows_of(a.d_rows, r, a.n_max)) return;
       pos = a.d_len[r] + j;
     } else {
       r = 0;
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void q
   } else {
     const int bm = m - a.T;
     r = bm / a.B;
-    pos = (dev ? a.d_len[r] + a.d_rows[r] : a.seq.L[r] + a.seq.n[r]) + (bm - r * a.B);
+    pos = (dev ? a.d_len[r] + dev_rows_of(a.d_rows, r, a.n_max) : a.seq.L[r] + a.seq.n[r]) + (bm - r * a.B);
   }
 
   if (kind != 2) {

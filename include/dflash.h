@@ -249,8 +249,9 @@ int dflash_kv_inject_attn(const dflash_layer_desc *L, dflash_cache *c, const voi
  * positions d_len[r] .. as in the host form, and d_len[r] grows by
  * d_rows[r] + B.  Capacity, page reservation and the attention split are
  * planned for the bounds: a call that would not fit if every sequence had
- * n_max new rows returns DFLASH_ERR_CAPACITY with nothing enqueued.  Values
- * of d_rows outside 0..n_max are not checked (they are on the device).
+ * n_max new rows returns DFLASH_ERR_CAPACITY with nothing enqueued.  The
+ * kernels clamp each d_rows value to 0..n_max (it is on the device, so the
+ * host cannot check it): a count out of range acts as the nearest bound.
  * Workspace: dflash_kv_inject_attn_dev_ws_bytes(L, c, n_max, B).
  *
  * dflash_cache_crop_tail_dev cuts `drop` rows off every sequence on the

@@ -161,3 +161,47 @@ def test_device_mode_refuses_host_calls():
     assert cache.lengths() == [0]
     assert L.LIB.dflash_cache_crop_tail_dev(cache.handle, 4, None) == L.ERR_ARG
     assert L.LIB.dflash_cache_device_end(cache.handle, None) == L.ERR_ARG
+
+
+def test_device_rows_out_of_range_act_as_the_bounds():
+    """Row counts on the device are clamped to 0..n_max by every kernel that
+    reads them: a round given [n_max + 7, -3] matches the round given
+    [n_max, 0] (outputs bit for bit, lengths), so a bad count cannot move a
+    read or write past the planned bounds."""
+    wl = configs.WALKTHROUGH.scaled(name="device_rows_clamped", d=256, n_h=8, n_kv=2, d_h=64, k_layers=2, B=4,
+                                    R=2, rounds=1, dtype="bf16", seed=17, prefill="fixed", prefill_len=100,
+                                    n_new="fixed", n_fixed=4, block_rows="anchor_mask")
+    R, B, n_max = wl.R, wl.B, 4
+    kv = prefill_host(wl)
+    fc, lw = G.fc_weights(wl), G.layer_weights(wl, 0)
+    w_fc, g_h = to_device(fc["w_fc"], wl), to_device(fc["gamma_h"], wl)
+    layer = L.Layer(*(to_device(lw[k], wl) for k in ("w_qkv", "w_o", "gamma_q", "gamma_k")),
+                    n_h=wl.n_h, n_kv=wl.n_kv, d_h=wl.d_h, eps=wl.eps, rope_theta=wl.rope_theta)
+    x, _, H = G.round_inputs(wl, 0, [n_max] * R)
+    xd, Hd = to_device(x, wl), to_device(H, wl)
+    kr = np.concatenate([kv[0][r][0].transpose(1, 0, 2) for r in range(R)], axis=0)
+    vr = np.concatenate([kv[0][r][1].transpose(1, 0, 2) for r in range(R)], axis=0)
+    results = []
+    for rows in ([n_max + 7, -3], [n_max, 0]):
+        say(f"case {wl.name}: d_rows {rows}")
+        cache = L.Cache(R, wl.n_kv, wl.d_h, torch.bfloat16, 256, device="cuda")
+        L.dflash_cache_append(cache, [0, 100, 200], to_device(kr, wl), to_device(vr, wl))
+        C = torch.empty((R * n_max, wl.d), dtype=torch.bfloat16, device="cuda")
+        cws = torch.empty(L.dflash_ctx_project_ws_bytes(R * n_max, wl.kd, wl.d, torch.bfloat16),
+                          dtype=torch.uint8, device="cuda")
+        ws = torch.empty(L.dflash_kv_inject_attn_dev_ws_bytes(layer, cache, n_max, B), dtype=torch.uint8,
+                         device="cuda")
+        out = torch.empty((R * B, wl.d), dtype=torch.bfloat16, device="cuda")
+        d_len = torch.zeros((R,), dtype=torch.int32, device="cuda")
+        d_rows = torch.tensor(rows, dtype=torch.int32, device="cuda")
+        L.dflash_cache_device_begin(cache, d_len)
+        L.dflash_ctx_project(xd, w_fc, g_h, wl.eps, C, cws)
+        L.dflash_kv_inject_attn_dev(layer, cache, C, n_max, d_rows, Hd, B, out, ws)
+        torch.cuda.synchronize()
+        lengths = d_len.cpu().tolist()
+        L.dflash_cache_device_end(cache)
+        K, V = cache_rows(cache, 0)
+        results.append((out.cpu(), lengths, K, V))
+    assert results[0][1] == results[1][1] == [100 + n_max + B, 100 + B]
+    assert torch.equal(results[0][0], results[1][0])
+    assert np.array_equal(results[0][2], results[1][2]) and np.array_equal(results[0][3], results[1][3])
