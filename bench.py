@@ -728,8 +728,10 @@ def measured_peaks(kv_bytes):
     as the layer's kernels) of 1 GiB, and of the 8K round's K/V size over 17
     rotated buffers (none re-read from the 256 MB Infinity Cache: what one
     launch of that size streams from HBM); a plain 1 GiB device copy (bytes read
-    + written per second); and a large bf16 matrix product through torch
-    (hipBLASLt)."""
+    + written per second); a large bf16 matrix product through torch
+    (hipBLASLt); and the library's matrix-core probe (dflash_mfma_peak:
+    back-to-back bf16 MFMAs on register operands, 16 waves per CU), the rate the
+    matrix cores sustain at this GPU's clocks under load."""
     import torch
 
     from block_diffusion_draft_fc_amd import _lib as L
@@ -775,9 +777,21 @@ def measured_peaks(kv_bytes):
     mm = 2 * 8192 ** 3 / t / 1e12
     del a, b
     torch.cuda.empty_cache()
+    iters, wgs = 4096, 1024
+    L.dflash_mfma_peak(64, wgs)
+    torch.cuda.synchronize()
+    L.timing_reset()
+    L.timing_enable(True)
+    for _ in range(5):
+        L.dflash_mfma_peak(iters, wgs)
+    torch.cuda.synchronize()
+    st = L.timing_read()["mfma_peak"]
+    L.timing_enable(False)
+    mfma = wgs * 4 * 8 * iters * 16384 / (st[1] * 1e-3 / st[0]) / 1e12
     return {"hbm_read_1gib_gbps": round(read_big, 1), "hbm_copy_1gib_gbps": round(copy_big, 1),
             "hbm_read_kv_size_cold_gbps": round(read_small, 1), "hbm_read_kv_size_cold_us": round(us_small, 3),
             "kv_size_bytes": int(m), "bf16_matmul_8192_tflops": round(mm, 1),
+            "bf16_mfma_probe_tflops": round(mfma, 1),
             "published": {"hbm_gbps": HBM_PEAK_GBPS, "bf16_dense_tflops": BF16_PEAK_TFLOPS}}
 
 
@@ -1026,7 +1040,13 @@ def main():
     }
     if not args.no_fresh_ctx:
         log("bench: fresh-context projections")
-        res["fresh_ctx_projections"] = fresh_ctx_projections(20)
+        fc = fresh_ctx_projections(20)
+        # the same rates against what the matrix cores sustain on this GPU
+        probe = peaks["bf16_mfma_probe_tflops"]
+        fc["mfma_probe_tflops"] = probe
+        for k in ("ctx_gemm", "qkv_gemm", "gemms"):
+            fc[k]["frac_of_mfma_probe"] = round(fc[k]["tflops"] / probe, 4)
+        res["fresh_ctx_projections"] = fc
     if not args.no_batched:
         log("bench: attention kernel on the stack's full-attention layer shape")
         res["attn_at_scale"] = attn_pass(30, 4, 32768, "bf16")

@@ -78,6 +78,7 @@ def _load() -> C.CDLL:
         "dflash_attn_plan": (C.c_int, [C.POINTER(C.c_int64), i32, i32, i64, i32, C.POINTER(C.c_int64)]),
         "dflash_attn_force_chunk": (C.c_int, [i64]),
         "dflash_stream_read": (C.c_int, [vp, i64, vp, vp]),
+        "dflash_mfma_peak": (C.c_int, [i32, i64, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -314,7 +315,7 @@ def dflash_accept(draft_ids, posterior, acc, next_rows=None, next_anchor=None, s
 
 STAGES = ("ctx_gemm", "ctx_reduce", "ctx_norm", "qkv_gemm", "qkv_epilogue", "attn", "attn_combine",
           "o_gemm", "o_reduce", "cache_append", "page_table", "head_norm", "head_gemm", "head_argmax",
-          "accept", "stream_read")
+          "accept", "stream_read", "mfma_peak")
 
 
 def timing_enable(on: bool = True) -> None:
@@ -350,6 +351,12 @@ def dflash_attn_plan(keys, n_kv: int, chunk_cap: int = 1 << 30, cache_dtype: int
 def dflash_stream_read(t, stream=None) -> None:
     """A plain streaming read of the bytes of device tensor t (measurement)."""
     _check(LIB.dflash_stream_read(_ptr(t), t.numel() * t.element_size(), None, _stream(stream)), "dflash_stream_read")
+
+
+def dflash_mfma_peak(iters: int, workgroups: int, stream=None) -> None:
+    """Back-to-back bf16 MFMAs on register operands (measurement): 8 * iters
+    16x16x32 products per wave, four waves per workgroup."""
+    _check(LIB.dflash_mfma_peak(int(iters), int(workgroups), None, _stream(stream)), "dflash_mfma_peak")
 
 
 def dflash_attn_force_chunk(chunk: int) -> None:

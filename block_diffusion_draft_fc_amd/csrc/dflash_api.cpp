@@ -1379,6 +1379,14 @@ int dflash_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* str
       staged(DFLASH_STAGE_STREAM_READ, s, bytes >= 16, [&] { return launch_stream_read(src, bytes, sink, s); }));
 }
 
+int dflash_mfma_peak(int32_t iters, int64_t workgroups, float* sink, void* stream) {
+  if (iters < 1 || iters > (1 << 24) || workgroups < 1 || workgroups > (1 << 20)) return DFLASH_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(sink) & 3) return DFLASH_ERR_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(
+      staged(DFLASH_STAGE_MFMA_PEAK, s, true, [&] { return launch_mfma_peak(iters, workgroups, sink, s); }));
+}
+
 int dflash_attn_force_chunk(int64_t chunk) {
   if (chunk != 0 && (chunk < 64 || chunk % 64 != 0 || chunk > ((int64_t)1 << 30))) return DFLASH_ERR_SHAPE;
   g_forced_chunk.store(chunk);

@@ -257,6 +257,7 @@ hipError_t launch_len_update(const LenArgs& a, hipStream_t s);
 // ---------------------------------------------------------------- measurement
 // Reads bytes / 16 16-byte words of src (nothing is written).
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s);
+hipError_t launch_mfma_peak(int iters, int64_t workgroups, float* sink, hipStream_t s);
 
 // ---------------------------------------------------------------- cache
 struct AppendArgs {

@@ -374,7 +374,8 @@ typedef enum {
   DFLASH_STAGE_HEAD_ARGMAX = 13, /* draft head: argmax over the vocabulary */
   DFLASH_STAGE_ACCEPT = 14,      /* acceptance of a round */
   DFLASH_STAGE_STREAM_READ = 15, /* dflash_stream_read (measurement) */
-  DFLASH_STAGE_COUNT = 16
+  DFLASH_STAGE_MFMA_PEAK = 16,   /* dflash_mfma_peak (measurement) */
+  DFLASH_STAGE_COUNT = 17
 } dflash_stage;
 
 int dflash_timing_enable(int on);
@@ -391,6 +392,17 @@ int dflash_timing_reset(void);
  * DFLASH_ERR_ARG.
  * ---------------------------------------------------------------------- */
 int dflash_stream_read(const void *src, int64_t bytes, uint32_t *sink, void *stream);
+
+/* ------------------------------------------------------------------------
+ * A matrix-core rate probe (a measurement aid): `workgroups` workgroups of
+ * four waves, each wave 8 * iters bf16 16x16x32 MFMAs on register operands
+ * (16384 flops each), nothing read and nothing written (sink, a device float
+ * or NULL, is only written in a case no run meets).  Timed as
+ * DFLASH_STAGE_MFMA_PEAK, it gives the bf16 MFMA rate this GPU sustains at its
+ * clocks under load, beside which the projections' TFLOP/s are judged.
+ * iters in 1..2^24 and workgroups in 1..2^20 (else DFLASH_ERR_SHAPE).
+ * ---------------------------------------------------------------------- */
+int dflash_mfma_peak(int32_t iters, int64_t workgroups, float *sink, void *stream);
 
 /* ------------------------------------------------------------------------
  * GEMM plan inspection (a diagnostic, host only: nothing is enqueued).  The

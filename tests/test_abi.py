@@ -437,6 +437,15 @@ def test_stream_read_validation():
     assert f(None, 0, None, None) == 0
 
 
+def test_mfma_peak_validation():
+    """The matrix-core probe refuses out-of-range sizes and misaligned sinks
+    before launching anything."""
+    f = L.LIB.dflash_mfma_peak
+    for it, wg in ((0, 1), (1 << 25, 1), (1, 0), (1, (1 << 20) + 1)):
+        assert f(it, wg, None, None) == L.ERR_SHAPE
+    assert f(1, 1, C.c_void_p(2), None) == L.ERR_ARG
+
+
 def test_attn_force_chunk():
     """The split override: multiples of 64 from 64 up, 0 restores the planner;
     the plan then reports the forced chunk (capped by the cache's limit)."""

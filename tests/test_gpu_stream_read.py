@@ -1,4 +1,5 @@
-"""GPU: dflash_stream_read, the plain read the bench sets the attention against.
+"""GPU: dflash_stream_read, the plain read the bench sets the attention against,
+and dflash_mfma_peak, the matrix-core probe beside the projections.
 
 The kernel folds every 16-byte word a lane reads into one value by XOR and
 stores it only when it equals one constant.  A buffer of zeros holding that
@@ -43,3 +44,19 @@ def test_stream_read_covers_its_range(n16):
     # the word just past the range is never read (nor a partial last word)
     assert _read(nbytes, n16) == 0
     assert _read(nbytes + 15, n16) == 0
+
+
+def test_mfma_peak_runs_and_writes_nothing():
+    """The probe's accumulators never reach the stored value: the sink keeps
+    its bits, and a timed run reports a positive rate."""
+    sink = torch.full((1,), -7.0, dtype=torch.float32, device="cuda")
+    assert L.LIB.dflash_mfma_peak(64, 512, C.c_void_p(sink.data_ptr()), None) == 0
+    torch.cuda.synchronize()
+    assert sink.item() == -7.0
+    L.timing_reset()
+    L.timing_enable(True)
+    L.dflash_mfma_peak(256, 1024)
+    torch.cuda.synchronize()
+    n, ms = L.timing_read()["mfma_peak"]
+    L.timing_enable(False)
+    assert n == 1 and ms > 0
