@@ -70,9 +70,10 @@ __device__ __forceinline__ u32x4 keep_bytes(u32x4 w, int n) {
 // NG = 2: two groups of four waves on alternate blocks with an exact merge of
 // their states at the end, as in the bf16 ring kernel; group 0 copies the
 // queries (the last stage holds one copy per tile) and group 1 reads them
-// after a barrier.
+// after a barrier.  The two-stage one-group form runs four workgroups per CU
+// (32 KB of LDS each): at most 128 VGPRs, i.e. four waves per SIMD.
 template <int DH, int NST, int NG = 1>
-__global__ __launch_bounds__(256 * NG, 1) void attn_ring64_fp8_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256 * NG, (NG == 1 && NST == 2) ? 4 : 1) void attn_ring64_fp8_kernel(AttnArgs a) {
   using V8 = bf16x8;
   static_assert(DH == 64 || DH == 128, "layouts defined for d_h 64 and 128");
   static_assert(NST >= 2 && NST <= 7, "blocks in flight are counted by wait_vm_blocks (up to 6 after the current)");
@@ -336,7 +337,9 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_fp8_kernel(AttnArgs a
 
 // Ring depth: the host plans for the bf16 kernel's depths (3 stages of 32 KB:
 // one workgroup per CU; 2: several per CU).  fp8 stages are half as large:
-// plan 2 takes 3 stages (48 KB; the host fits three workgroups per CU to it);
+// plan 2 takes 2 stages at d_h 128 (32 KB, four workgroups per CU, which the
+// host fits its items to: 4 x 32K keys 67 us against 71 with three stages and
+// three per CU) and 3 at d_h 64;
 // plan 3 takes two wave groups with 6 stages (96 KB) at d_h 128 (8K decode
 // cache: 12.3-12.6 us; 12.6-13.0 with 4 stages; one group of four waves
 // 13.6-14.4) and one group with 4 stages (64 KB) at d_h 64.  With one group,
@@ -350,7 +353,7 @@ hipError_t launch_attn_fp8(const AttnArgs& a, int items, hipStream_t s) {
     if (a.d_h == 128) launch((attn_ring64_fp8_kernel<128, 6, 2>), dim3(items), dim3(512), 0, s, a);
     else launch((attn_ring64_fp8_kernel<64, 4>), dim3(items), dim3(256), 0, s, a);
   } else {
-    if (a.d_h == 128) launch((attn_ring64_fp8_kernel<128, 3>), dim3(items), dim3(256), 0, s, a);
+    if (a.d_h == 128) launch((attn_ring64_fp8_kernel<128, 2>), dim3(items), dim3(256), 0, s, a);
     else launch((attn_ring64_fp8_kernel<64, 3>), dim3(items), dim3(256), 0, s, a);
   }
   return hipGetLastError();

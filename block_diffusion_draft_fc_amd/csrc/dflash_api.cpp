@@ -166,9 +166,10 @@ AttnSplit plan_attn_split(const std::vector<int64_t>& keys, int n_kv, int64_t ch
     sp.chunk = std::min(cap, forced);
   } else {
     // workgroup slots of one round: 256 at depth 3 (one per CU), 512 at depth
-    // 2 (two per CU); fp8 caches at depth 2 fit three per CU (48 KB of LDS,
-    // 168 VGPRs): 4 x 32K keys 79 -> 73 us, the combine 1 us longer
-    const int64_t slots = sp.nst == 2 ? (fp8 ? 768 : 512) : 256;
+    // 2 (two per CU); fp8 caches at depth 2 fit four per CU (32 KB of LDS and
+    // at most 128 VGPRs each): 4 x 32K keys 79 us with two per CU, 73 with
+    // three, 67 with four
+    const int64_t slots = sp.nst == 2 ? (fp8 ? 1024 : 512) : 256;
     const int64_t limit = std::min<int64_t>(kAttnMaxTarget, slots);
     // items_of is non-increasing in the chunk: the smallest chunk (in units of
     // 64 keys) in [2, cap / 64] with items_of <= limit, else the cap

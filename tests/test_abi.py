@@ -371,7 +371,7 @@ def test_attn_plan_invariants(keys, n_kv, cap, dtype):
     """The chunk is a whole number of 64-key blocks, at least 128 and within
     the cap; the item count is what the chunk gives; the ring depth follows the
     total key count; and the chunk is the smallest that brings the items into
-    one round of launch slots (256 workgroups at depth 3, 512 at depth 2, 768
+    one round of launch slots (256 workgroups at depth 3, 512 at depth 2, 1024
     at depth 2 for fp8 caches), or the cap when no chunk within it does."""
     rc, chunk, items, nst = _attn_plan(keys, n_kv, cap, dtype)
     assert rc == 0
@@ -380,7 +380,7 @@ def test_attn_plan_invariants(keys, n_kv, cap, dtype):
     capc = max(128, cap // 64 * 64)
     assert chunk % 64 == 0 and 128 <= chunk <= capc
     assert items == _items(keys, n_kv, chunk)
-    limit = (768 if dtype == L.DFLASH_FP8_E4M3 else 512) if nst == 2 else 256
+    limit = (1024 if dtype == L.DFLASH_FP8_E4M3 else 512) if nst == 2 else 256
     if _items(keys, n_kv, capc) <= limit:
         assert items <= limit
         assert chunk == 128 or _items(keys, n_kv, chunk - 64) > limit
@@ -396,9 +396,9 @@ def test_attn_plan_headline_split():
     slots at ring depth 3."""
     assert _attn_plan([8216], 8) == (0, 320, 208, 3)
     assert _attn_plan([8216], 8, dtype=L.DFLASH_FP8_E4M3) == (0, 320, 208, 3)
-    # four 32K requests: 512 items for bf16, 768 for fp8 caches
+    # four 32K requests: 512 items for bf16, 992 for fp8 caches (chunks of 1088)
     assert _attn_plan([32792] * 4, 8)[2] == 512
-    assert _attn_plan([32792] * 4, 8, dtype=L.DFLASH_FP8_E4M3)[2] == 768
+    assert _attn_plan([32792] * 4, 8, dtype=L.DFLASH_FP8_E4M3)[1:3] == (1088, 992)
 
 
 def test_device_mode_validation():
