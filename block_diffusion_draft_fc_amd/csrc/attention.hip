@@ -9,29 +9,38 @@
 // pos_q - pos_k >= window.  Query head h reads K/V head h / (n_h / n_kv)
 // ("KV Cache + Speculative Decoding 面试 Cheat Sheet" 6.3).
 //
-// Layout of the work on gfx950:
-//  * The g = n_h/n_kv query heads that share a K/V head contribute g*B query
-//    rows (64 for 32/8 heads and B = 16).  They stay in VGPRs for the whole
-//    chunk as the B operand of S^T = K Q^T, so each K/V byte is read from HBM
-//    once and feeds all of them.
-//  * Keys go through in blocks of 32 per wavefront, the four waves of a
-//    workgroup taking every fourth block.  K rows load straight into the A
-//    operand of 16x16x32 MFMAs (16-byte loads, 64 contiguous bytes per key per
-//    instruction).  The two 16-key tiles of a block use the key order
-//    tile kt, row i -> key 8*(i/4) + 4*kt + i%4, so after the S^T products each
-//    lane holds the scores of 8 consecutive keys for one query row: exactly the
-//    B operand of O^T = V^T P^T.
-//  * V is stored transposed in the cache (tiles of 64 slots, head dim-major
-//    within a tile), so the A operand of that product (16 head dims x 32 keys)
-//    is 16 contiguous bytes per lane as well.  No LDS and no lane shuffles sit
-//    in the key loop; the row max needs two xor shuffles.
-//  * The running max, sum and output stay per lane in the log2 domain; the
-//    four waves merge through LDS at the end and the workgroup writes one
-//    partial (m, l, unnormalised O) per query row.
+// The kernels (all one workgroup per (sequence, K/V head, key chunk); the g =
+// n_h/n_kv query heads that share a K/V head contribute g*B query rows - 64
+// for 32/8 heads and B = 16 - which stay resident for the whole chunk, so each
+// K/V byte is read from HBM once and feeds all of them):
+//  * attn_ring64_kernel (bf16, four 16-row query tiles: the layer shapes of
+//    the workloads): 64-key blocks through a ring of LDS stages filled by
+//    direct-to-LDS copies, one query tile per wave; two wave groups on
+//    alternate blocks where one workgroup holds a CU.  Its own comment below
+//    gives the layout.
+//  * attn_lds_kernel (bf16, one to three query tiles): 32-key blocks through
+//    per-wave LDS rings.
+//  * attn_split_kernel (fp32 layers): K and V^T rows loaded straight into
+//    MFMA operands (16-byte loads), the four waves of a workgroup on every
+//    fourth 32-key block, merged through LDS at the end.
+// Every kernel keeps the running max, sum and output per lane in the log2
+// domain and writes one partial (m, l, unnormalised O) per query row and item;
+// attn_combine_kernel merges the partials of a row.
 #include "kernels.hpp"
 
 namespace dflash {
 
+// ---------------------------------------------------------------- fp32: register-fed blocks
+// Keys go through in blocks of 32 per wavefront, the four waves of a
+// workgroup taking every fourth block.  K rows load straight into the A
+// operand of 16x16x32 MFMAs (16-byte loads, 64 contiguous bytes per key per
+// instruction).  The two 16-key tiles of a block use the key order
+// tile kt, row i -> key 8*(i/4) + 4*kt + i%4, so after the S^T = K Q^T
+// products each lane holds the scores of 8 consecutive keys for one query row:
+// exactly the B operand of O^T = V^T P^T.  V is stored transposed in the cache
+// (tiles of 64 slots, head dim-major within a tile), so the A operand of that
+// product (16 head dims x 32 keys) is 16 contiguous bytes per lane as well.
+// No LDS sits in the key loop; the four waves merge through LDS at the end.
 template <typename T, int DH, int NQW, int QS>
 __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   using V8 = vec8_t<T>;
