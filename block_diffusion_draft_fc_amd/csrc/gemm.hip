@@ -691,8 +691,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_stream_kernel(TileProb p) {
 }
 
 // Configurations (measured): one 16-row tile: 8 waves, 4 stages; two tiles:
-// 16 waves, 3 stages.  p.n_tiles must be ceil(N / (16 * waves)).
-int gemm_stream_waves(int mt) { return mt <= 1 ? 8 : 16; }
+// 12 waves, 4 stages (the 8K round's q/k/v product: 32 column tiles x 8
+// splits = 256 workgroups, one per CU; 16 waves and 3 stages gave 192
+// workgroups, 12.6 us against 12.0 on average).  p.n_tiles must be
+// ceil(N / (16 * waves)).
+int gemm_stream_waves(int mt) { return mt <= 1 ? 8 : 12; }
 
 hipError_t launch_gemm_stream(const TileProb& p, int mt, hipStream_t s) {
   const int blocks = p.n_tiles * p.splits;
@@ -701,7 +704,7 @@ hipError_t launch_gemm_stream(const TileProb& p, int mt, hipStream_t s) {
   if (mt == 1)
     launch((gemm_stream_kernel<1, 8, 4>), dim3(blocks), dim3(64 * 8), 0, s, p);
   else
-    launch((gemm_stream_kernel<2, 16, 3>), dim3(blocks), dim3(64 * 16), 0, s, p);
+    launch((gemm_stream_kernel<2, 12, 4>), dim3(blocks), dim3(64 * 12), 0, s, p);
   return hipGetLastError();
 }
 
