@@ -194,7 +194,7 @@ struct SkinnyPlan {
   int32_t k_chunk, splits, mt, n_tiles;
   bool wide;         // gemm_wide_kernel (256-column tiles) instead of gemm_lds_kernel
   bool tile;         // gemm_tile_kernel (256x256 MFMA tiles) for many rows
-  bool stream;       // gemm_stream_kernel (per-wave weight streams) for at most 32 rows
+  bool stream;       // gemm_stream_kernel (per-wave weight streams) for at most 64 rows
   bool fullk;        // gemm_fullk_kernel (no split-K partials) for at most 16 rows
   bool resident;     // gemm_resident_kernel: at most 16 rows kept in LDS, very many columns
   bool slab;         // gemm_slab_kernel: bf16, up to 128 rows, slice staged in up to 160 KB of LDS
@@ -246,18 +246,19 @@ SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K, size_t eb) {
     p.splits = 1;
     return p;
   }
-  // at most 32 rows, K below the wide kernel's range: per-wave weight streams
+  // at most 64 rows, K below the wide kernel's range: per-wave weight streams
   // in 512-wide K-chunks
-  if (eb == 2 && p.mt <= 2 && K < wide_min_k && K % 64 == 0 && N % 4 == 0) {
+  if (eb == 2 && p.mt <= 4 && K < wide_min_k && K % 64 == 0 && N % 4 == 0) {
     p.stream = true;
     p.n_tiles = (int32_t)cdiv(N, 16 * gemm_stream_waves(p.mt));
     p.k_chunk = 512;
     p.splits = (int32_t)cdiv(K, 512);
     return p;
   }
-  // 33..128 rows (bf16, K a multiple of 512): the slice staged by direct
-  // copies in up to 160 KB of LDS, which allows 1024-wide chunks at 64 rows
-  // and 512-wide at 128; splits to about one workgroup per CU
+  // 65..128 rows, or 33..64 with a long K (bf16, K a multiple of 512): the
+  // slice staged by direct copies in up to 160 KB of LDS, which allows
+  // 1024-wide chunks at 64 rows and 512-wide at 128; splits to about one
+  // workgroup per CU
   if (slab_eligible(K, eb) && p.mt >= 3 && p.mt <= 8) {
     constexpr int slab_target = 256;
     p.slab = true;

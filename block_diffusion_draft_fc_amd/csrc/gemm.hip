@@ -13,11 +13,12 @@
 //    over the whole K, no partials;
 //  * gemm_resident_kernel (<= 16 rows, a vocabulary of columns) - the rows
 //    kept in LDS, whole-K weight tiles streamed per wave;
-//  * gemm_stream_kernel (<= 32 rows) - per-wave weight rings of 64-wide
+//  * gemm_stream_kernel (<= 64 rows, K < 8192) - per-wave weight rings of 64-wide
 //    K-steps, 512-wide chunks;
 //  * gemm_wide_kernel (<= 32 rows, K >= 8192) - each wave streams 64 weight
 //    rows and reads the activation rows straight from L2;
-//  * gemm_slab_kernel (33..128 rows, K a multiple of 512) - the chunk's
+//  * gemm_slab_kernel (65..128 rows, or 33..64 with K >= 8192; K a multiple
+//    of 512) - the chunk's
 //    activation slice staged by direct copies in up to 160 KB of LDS, waves
 //    stream 16 weight rows each;
 //  * gemm_lds_kernel (fp32, and bf16 with other K) - the same scheme within
@@ -590,14 +591,14 @@ hipError_t launch_gemm_tile(const TileProb& p, int bn, hipStream_t s) {
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- weight streaming (bf16, at most 32 rows)
+// ---------------------------------------------------------------- weight streaming (bf16, at most 64 rows)
 // part[split][m][n] = sum over the split's K-chunk of x[m][k] w[n][k], for the
-// q/k/v and o projections of a draft round (16..32 rows): the product is the
+// q/k/v and o projections of a draft round (16..64 rows): the product is the
 // weight stream, so each wave owns 16 weight rows and streams them through its
 // own direct-to-LDS ring of 64-wide K-steps - 16 rows x 128 bytes per step,
 // two copies of 8 whole rows (whole cache lines), chunks XOR-swizzled so that
 // the MFMA fragment reads are conflict free - with no barrier in the loop.  The
-// workgroup's activation chunk (at most 32 rows x 512) is staged once in LDS in
+// workgroup's activation chunk (at most 64 rows x 512) is staged once in LDS in
 // MFMA operand order by direct copies issued together with the first weight
 // steps, so its latency overlaps theirs.  Products are taken as W x^T, so each
 // lane ends with four consecutive columns of one row (16-byte partial stores).
@@ -693,18 +694,23 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_stream_kernel(TileProb p) {
 // Configurations (measured): one 16-row tile: 8 waves, 4 stages; two tiles:
 // 12 waves, 4 stages (the 8K round's q/k/v product: 32 column tiles x 8
 // splits = 256 workgroups, one per CU; 16 waves and 3 stages gave 192
-// workgroups, 12.6 us against 12.0 on average).  p.n_tiles must be
+// workgroups, 12.6 us against 12.0 on average); three or four tiles: 8
+// waves, 4 stages, 128 KB of LDS (a 64-row 4096 x 4096 product: 32 x 8
+// workgroups, 10.5 us against 12.4 for the slab kernel; at 128 rows, 4 waves
+// and 160 KB took 12.9 us against the slab kernel's 11.0).  p.n_tiles must be
 // ceil(N / (16 * waves)).
-int gemm_stream_waves(int mt) { return mt <= 1 ? 8 : 12; }
+int gemm_stream_waves(int mt) { return mt == 2 ? 12 : 8; }
 
 hipError_t launch_gemm_stream(const TileProb& p, int mt, hipStream_t s) {
   const int blocks = p.n_tiles * p.splits;
   if (blocks == 0) return hipSuccess;
-  if (p.k_chunk != kStreamKC || mt < 1 || mt > 2) return hipErrorInvalidValue;
+  if (p.k_chunk != kStreamKC || mt < 1 || mt > 4) return hipErrorInvalidValue;
   if (mt == 1)
     launch((gemm_stream_kernel<1, 8, 4>), dim3(blocks), dim3(64 * 8), 0, s, p);
-  else
+  else if (mt == 2)
     launch((gemm_stream_kernel<2, 12, 4>), dim3(blocks), dim3(64 * 12), 0, s, p);
+  else
+    launch((gemm_stream_kernel<4, 8, 4>), dim3(blocks), dim3(64 * 8), 0, s, p);
   return hipGetLastError();
 }
 

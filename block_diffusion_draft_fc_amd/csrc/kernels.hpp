@@ -73,7 +73,7 @@ struct TileProb {
 };
 // bn: output columns per tile, 256, 128 or 64 (n_tiles = ceil(N / bn)).
 hipError_t launch_gemm_tile(const TileProb& p, int bn, hipStream_t s);
-// Weight-streaming product for at most 32 rows (mt = ceil(M / 16) of 1 or 2):
+// Weight-streaming product for at most 64 rows (mt = ceil(M / 16) of 1 to 4):
 // bf16, K a multiple of 64, N of 4, k_chunk == 512; the TileProb's n_tiles is
 // ceil(N / (16 * gemm_stream_waves(mt))) and m_tiles is unused.
 int gemm_stream_waves(int mt);

@@ -423,10 +423,10 @@ int dflash_mfma_peak(int32_t iters, int64_t workgroups, float *sink, void *strea
 typedef enum {
   DFLASH_GEMM_LDS = 0,       /* activation slice in up to 64 KB of LDS, fp32 or other K */
   DFLASH_GEMM_WIDE = 1,      /* <= 32 rows, K >= 8192: activation from L2 */
-  DFLASH_GEMM_STREAM = 2,    /* <= 32 rows: per-wave weight rings */
+  DFLASH_GEMM_STREAM = 2,    /* <= 64 rows, K < 8192: per-wave weight rings */
   DFLASH_GEMM_FULLK = 3,     /* <= 16 rows: whole K per workgroup, no partials */
   DFLASH_GEMM_RESIDENT = 4,  /* <= 16 rows, >= 65536 columns: rows kept in LDS */
-  DFLASH_GEMM_SLAB = 5,      /* 33..128 rows: slice staged in up to 160 KB of LDS */
+  DFLASH_GEMM_SLAB = 5,      /* 65..128 rows (33..64 at K >= 8192): slice staged in up to 160 KB of LDS */
   DFLASH_GEMM_TILE = 6       /* many rows: 256 x 256/128/64 MFMA tiles */
 } dflash_gemm_kernel;
 int dflash_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t *out /* [6] */);

@@ -270,7 +270,7 @@ def _plan(M, N, K, dt):
 # the fresh 1024-row context and the draft head over the Qwen3 vocabulary
 ROUTES = [
     ((16, 4096, 20480), "fullk"), ((16, 4096, 4096), "fullk"), ((32, 6144, 4096), "stream"),
-    ((24, 6144, 4096), "stream"), ((64, 4096, 4096), "slab"), ((128, 2048, 4096), "slab"),
+    ((24, 6144, 4096), "stream"), ((64, 4096, 4096), "stream"), ((128, 2048, 4096), "slab"),
     ((48, 4096, 20480), "slab"), ((100, 4096, 20480), "tile"), ((256, 4096, 4096), "tile"),
     ((392, 2048, 4096), "tile"), ((1024, 2560, 12800), "tile"), ((15, 151936, 4096), "resident"),
     ((20, 4096, 20480), "wide"),
@@ -302,11 +302,16 @@ def test_gemm_plan_invariants():
                     rows = min(M, p["rows_per_problem"]) if kind != "tile" else M
                     if kind in ("fullk", "resident"):
                         assert rows <= 16 and sp == 1 and kc == K, where
-                    if kind in ("stream", "wide"):
+                    if kind == "wide":
                         assert rows <= 32, where
+                    if kind == "stream":
+                        assert rows <= 64 and K < 8192 and K % 64 == 0 and kc == 512, where
+                        waves = 12 if -(-rows // 16) == 2 else 8
+                        assert p["n_tiles"] == -(-N // (16 * waves)), where
                     if kind == "slab":
                         mt = -(-rows // 16)
                         assert 3 <= mt <= 8 and K % 512 == 0 and kc % 512 == 0, where
+                        assert mt >= 5 or K >= 8192, where
                         assert mt * 16 * (kc + 8) * 2 <= 160 * 1024, where
                         assert p["n_tiles"] == -(-N // 64), where
                     if kind == "tile":

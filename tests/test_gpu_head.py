@@ -94,14 +94,17 @@ def test_qwen3_vocab_bf16():
     _check(configs.DECODE_8K, configs.QWEN3_VOCAB)
 
 
-@pytest.mark.parametrize("R,B,d,vocab", [(4, 16, 512, 32000), (16, 16, 512, 12000), (2, 16, 4096, 20000),
-                                         (3, 2, 256, 4096), (1, 16, 1024, 8196), (1, 4, 512, 70004),
-                                         (1, 16, 2048, 65540)])
+@pytest.mark.parametrize("R,B,d,vocab", [(4, 16, 512, 32000), (8, 16, 512, 32000), (16, 16, 512, 12000),
+                                         (2, 16, 4096, 20000), (2, 16, 520, 5000), (3, 2, 256, 4096),
+                                         (1, 16, 1024, 8196), (1, 4, 512, 70004), (1, 16, 2048, 65540)])
 def test_batched_heads_bf16(R, B, d, vocab):
-    """Several requests (60, 240, 30, 3 and 15 rows: the LDS, tile, stream and
-    full-K products), a vocabulary that is not a multiple of the argmax
-    segment, B = 2; vocabularies of 64 K and more take the resident-rows
-    product (3 and 15 rows, a last 16-column tile holding 4 columns)."""
+    """Several requests (60 and 30 rows: the per-wave stream product; 120: the
+    LDS-slab product; 240: the tile product; 30 rows over d = 520, not a
+    multiple of 64: the register-staged LDS product; 3 and 15 rows: the
+    stream and full-K products), a vocabulary that is not a multiple of the
+    argmax segment, B = 2; vocabularies of 64 K and more take the
+    resident-rows product (3 and 15 rows, a last 16-column tile holding 4
+    columns)."""
     wl = configs.DECODE_8K.scaled(name=f"head_R{R}_B{B}_d{d}", R=R, B=B, d=d)
     _check(wl, vocab)
 
