@@ -191,9 +191,11 @@ def fresh_ctx_projections(iters):
     Qwen3-4B-shaped layer: d 2560, 32/8 heads of 128, k = 5 -> 12800-wide raw
     context, 1024 new context rows plus a block of 16, bf16): the layer call on
     an empty cache, timed per stage with the library's kernel-attached events.
-    The fc GEMM (1024 x 12800 -> 2560) and the K/V GEMM of [C; H] (1040 x 2560 ->
-    2048) run on the MFMA tile kernel; Q (16 rows) and o_proj (16 rows) stream
-    their weights and are HBM-bound."""
+    The fc GEMM (1024 x 12800 -> 2560) and the K/V GEMM of C (1024 x 2560 ->
+    2048) run on the MFMA tile kernel; Q/K/V of the 16 block rows (one product)
+    and o_proj (16 rows) stream their weights and are HBM-bound.  Beside them,
+    as context, torch.matmul (hipBLASLt) on the two tile-GEMM shapes, timed the
+    same way (back-to-back calls between two events)."""
     import torch
 
     from block_diffusion_draft_fc_amd import _lib as L
@@ -246,6 +248,23 @@ def fresh_ctx_projections(iters):
     res["gemms+reductions"] = {"us": round(all_us, 2), "tflops": round(tot / all_us / 1e6, 1),
                                "mfma_frac": round(tot / all_us / 1e6 / BF16_PEAK_TFLOPS, 4)}
     res["stage_us"] = {k: round(v, 2) for k, v in us.items() if st[k][0]}
+    res["vendor_matmul"] = {}
+    for name, (M, K, N) in (("ctx_gemm", (n, kd, d)), ("kv_gemm_of_C", (n, d, 2 * kvd))):
+        a = torch.randn((M, K), device=dev).to(torch.bfloat16)
+        w = torch.randn((N, K), device=dev).to(torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a, w.t())
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(iters):
+            torch.matmul(a, w.t())
+        ev1.record()
+        torch.cuda.synchronize()
+        t = ev0.elapsed_time(ev1) / iters * 1e3
+        res["vendor_matmul"][name] = {"shape": f"{M} x {K} -> {N}", "us": round(t, 2),
+                                      "tflops": round(2 * M * K * N / t / 1e6, 1)}
+        del a, w
     return res
 
 

@@ -654,7 +654,12 @@ struct KvPlan {
   // rows are computed and ignored) when every row fits one weight-streaming
   // problem - the weights are then streamed once, in one launch; otherwise Q
   // of H and K/V of [C; H] as two products (gq, gkv).
+  // block_rows_apart: instead, Q, K and V of H in one weight-streaming
+  // product (gq) and K/V of C alone (gkv), when the block rows would add a
+  // 256-row tile to a tile-GEMM K/V product (1024 fresh context rows + 16
+  // block rows: 5 row tiles, the fifth holding 16 rows).
   bool fused_qkv;
+  bool block_rows_apart;
   GemmJob gq, gkv, go;
   size_t off_q, off_pq, off_pkv, off_po, off_pml, off_attn, off_pout, total;
   int64_t max_items;
@@ -681,8 +686,16 @@ KvPlan plan_kv(const dflash_layer_desc* L, const dflash_cache* c, int64_t T, int
     p.gq = p.gkv;
     p.gq.plan.splits = 0;   // no separate partials
   } else {
-    p.gq = make_job(nullptr, 0, nullptr, p.RB, L->w_qkv, p.qd, L->d, eb);
-    p.gkv = make_job(nullptr, T, nullptr, p.RB, nullptr, 2 * p.kvd, L->d, eb);
+    constexpr int64_t kTileRows = 256;
+    p.block_rows_apart = p.RB <= kSkinnyMaxM && tile_eligible(T, 2 * p.kvd, L->d, eb) &&
+                         cdiv(T + p.RB, kTileRows) > cdiv(T, kTileRows);
+    if (p.block_rows_apart) {
+      p.gq = make_job(nullptr, 0, nullptr, p.RB, L->w_qkv, p.qd + 2 * p.kvd, L->d, eb);
+      p.gkv = make_job(nullptr, T, nullptr, 0, nullptr, 2 * p.kvd, L->d, eb);
+    } else {
+      p.gq = make_job(nullptr, 0, nullptr, p.RB, L->w_qkv, p.qd, L->d, eb);
+      p.gkv = make_job(nullptr, T, nullptr, p.RB, nullptr, 2 * p.kvd, L->d, eb);
+    }
   }
   p.go = make_job(nullptr, p.RB, nullptr, 0, L->w_o, L->d, p.qd, eb);
   // work items of one attention launch: at most the target count plus one
@@ -994,6 +1007,7 @@ int kv_inject_impl(const dflash_layer_desc* L, dflash_cache* c, const void* C, c
   hipError_t e = enqueue_page_table(c, ap, s);
 
   // 2. q/k/v projection: Q from the block rows, K/V from [C; H] with one weight
+  //    (the block rows' K/V in their Q product when block_rows_apart)
   GemmJob gq = p.gq, gkv = p.gkv;
   gkv.x0 = C; gkv.x1 = H; gkv.part = part_kv;
   if (p.fused_qkv) {
@@ -1016,12 +1030,26 @@ int kv_inject_impl(const dflash_layer_desc* L, dflash_cache* c, const void* C, c
       a.part_kv = part_kv + p.qd;
       a.kv_row = w; a.kv_split = split;
       a.sq = a.skv = gkv.plan.splits;
+      a.part_kvh = a.part_kv + T * w;
+      a.kvh_row = w; a.kvh_split = split; a.skvh = a.skv;
+    } else if (p.block_rows_apart) {
+      // [splits][RB][qd + 2 kvd] for the block rows, [splits][T][2 kvd] for C
+      const int64_t w = p.qd + 2 * p.kvd;
+      a.part_q = part_q;
+      a.q_row = w; a.q_split = p.RB * w;
+      a.part_kv = part_kv;
+      a.kv_row = 2 * p.kvd; a.kv_split = T * 2 * p.kvd;
+      a.sq = gq.plan.splits; a.skv = gkv.plan.splits;
+      a.part_kvh = part_q + p.qd;
+      a.kvh_row = w; a.kvh_split = p.RB * w; a.skvh = gq.plan.splits;
     } else {
       a.part_q = part_q;
       a.q_row = p.qd; a.q_split = p.RB * p.qd;
       a.part_kv = part_kv;
       a.kv_row = 2 * p.kvd; a.kv_split = (T + p.RB) * 2 * p.kvd;
       a.sq = gq.plan.splits; a.skv = gkv.plan.splits;
+      a.part_kvh = part_kv + T * a.kv_row;
+      a.kvh_row = a.kv_row; a.kvh_split = a.kv_split; a.skvh = a.skv;
     }
     a.gamma_q = L->gamma_q; a.gamma_k = L->gamma_k;
     a.q_ws = q_ws;

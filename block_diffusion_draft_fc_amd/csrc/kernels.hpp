@@ -136,12 +136,14 @@ __device__ __forceinline__ int dev_rows_of(const int32_t* d_rows, int r, int n_m
 
 struct QkvEpiArgs {
   // Split-K partials: Q of block row b (0 <= b < R*B), split s, column c at
-  // part_q[s * q_split + b * q_row + c]; K/V of row m of [C; H] (K columns
-  // first, then V) at part_kv[s * kv_split + m * kv_row + c].
+  // part_q[s * q_split + b * q_row + c]; K/V of context row m < T (K columns
+  // first, then V) at part_kv[s * kv_split + m * kv_row + c], and of block
+  // row b at part_kvh[s * kvh_split + b * kvh_row + c] (skvh splits).
   const float* part_q;
   const float* part_kv;
-  int64_t q_row, q_split, kv_row, kv_split;
-  int32_t sq, skv;
+  const float* part_kvh;
+  int64_t q_row, q_split, kv_row, kv_split, kvh_row, kvh_split;
+  int32_t sq, skv, skvh;
   const void* gamma_q;
   const void* gamma_k;
   void* q_ws;            // [R][n_kv][qrows][d_h]

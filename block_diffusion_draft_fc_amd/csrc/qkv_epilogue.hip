@@ -55,16 +55,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void q
   }
 
   // split-K reduction of the two elements of this lane's rotation pair
-  const float* part;
-  int splits, col;
-  int64_t row_stride, stride;
-  if (kind == 0) { part = a.part_q; splits = a.sq; row_stride = a.q_row; stride = a.q_split; col = head * a.d_h; }
-  else { part = a.part_kv; splits = a.skv; row_stride = a.kv_row; stride = a.kv_split;
-         col = (kind == 2 ? kvd : 0) + head * a.d_h; }
+  // (block rows' K/V from their own source: sel 2)
+  const int sel = kind == 0 ? 0 : m < a.T ? 1 : 2;
+  const float* part = sel == 0 ? a.part_q : sel == 1 ? a.part_kv : a.part_kvh;
+  const int splits = sel == 0 ? a.sq : sel == 1 ? a.skv : a.skvh;
+  const int64_t row_stride = sel == 0 ? a.q_row : sel == 1 ? a.kv_row : a.kvh_row;
+  const int64_t stride = sel == 0 ? a.q_split : sel == 1 ? a.kv_split : a.kvh_split;
+  const int col = (kind == 2 ? kvd : 0) + head * a.d_h;
+  const int pm = sel == 2 ? m - a.T : m;
   const bool act = lane < half;
   float x0 = 0.f, x1 = 0.f;
   if (act) {
-    const float* src = part + (int64_t)m * row_stride + col + lane;
+    const float* src = part + (int64_t)pm * row_stride + col + lane;
 #pragma unroll 4
     for (int s = 0; s < splits; ++s) { x0 += src[s * stride]; x1 += src[s * stride + half]; }
   }

@@ -342,6 +342,12 @@ SMALL = [
            rounds=1),
     _small("fresh_ctx2x200_tile_gemm_r2", d=512, k_layers=2, d_h=128, B=16, R=2, prefill="none",
            n_new="fixed", n_fixed=200, rounds=1),
+    # context rows that fill whole 256-row tiles, so the block rows would add
+    # a tile: Q/K/V of the block rows in one streaming product, K/V of C alone
+    _small("fresh_ctx256_block_rows_apart", d=512, k_layers=2, B=16, prefill="none", n_new="fixed", n_fixed=256,
+           rounds=1),
+    _small("ctx2x250_block_rows_apart_r2", d=512, k_layers=2, d_h=128, B=16, R=2, prefill="uniform",
+           prefill_range=(0, 300), n_new="fixed", n_fixed=250, rounds=2),
     # the library's limits: 64 requests per cache (ragged, some empty), and
     # 64 query rows per K/V head from an MHA layer with B = 64
     _small("max_seqs_r64", R=64, d_h=128, B=16, prefill="uniform", prefill_range=(0, 300), n_range=(0, 4),
