@@ -419,9 +419,12 @@ hipError_t launch_gemm_wide(const GemmProb& p, hipStream_t s) {
 // many K-splits to fill the CUs, and their partials cost more than the
 // product): 64x64 / 32x64 blocks per wave.
 //
-// The K loop steps by 64 through two LDS stages of 64 KB; the copies of step
-// s + 1 are issued right after the barrier of step s and land while step s
-// computes.  Operands reach LDS by direct-to-LDS copies that each move 8 rows
+// The K loop steps by 64 through LDS stages: two of 64 KB for BN = 256 (a
+// third would not fit), the copies of step s + 1 issued right after the
+// barrier of step s and landing while step s computes; three of 48 / 40 KB for
+// BN = 128 / 64, the copies of step s + 2 issued after the barrier of step s,
+// so that they have two steps to land (the 16-request batch's 256-row q/k/v
+// and o products 39 -> 36 us and 20 -> 17 us).  Operands reach LDS by direct-to-LDS copies that each move 8 rows
 // x 128 bytes (whole cache lines: copies of half lines run at well under half
 // the rate), so a stage holds each tile row's 64 K-values contiguously, in
 // 1 KB blocks of 8 rows.  An MFMA fragment read (16 rows, one 16-byte chunk of
@@ -450,14 +453,15 @@ constexpr int kXcds = 8;
 
 template <int BN>
 __global__ __launch_bounds__(512, 1) void gemm_tile_kernel(TileProb p) {
+  constexpr int NST = BN == 256 ? 2 : 3;   // LDS stages
   constexpr int BBLOCKS = BN / 8;          // 1 KB blocks of B per stage
   constexpr int WN = BN / 64;              // waves along N
   constexpr int WM = kTileWaves / WN;      // waves along M
   constexpr int RM = kTileBM / WM;         // rows per wave
   constexpr int FM = RM / 16;              // 16-row fragments per wave
-  // one array per stage and operand, so that each stage is named statically
-  __shared__ __align__(16) unsigned char sa0[kTileBlocks * 1024], sb0[BBLOCKS * 1024];
-  __shared__ __align__(16) unsigned char sa1[kTileBlocks * 1024], sb1[BBLOCKS * 1024];
+  // stage arrays, always indexed by a compile-time stage number
+  __shared__ __align__(16) unsigned char sa[NST][kTileBlocks * 1024];
+  __shared__ __align__(16) unsigned char sb[NST][BBLOCKS * 1024];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -482,6 +486,7 @@ __global__ __launch_bounds__(512, 1) void gemm_tile_kernel(TileProb p) {
 
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
 
   // Copies of one K-step: block b of a stage holds tile rows 8 b .. 8 b + 7;
   // wave w copies blocks w, w + 8, w + 16, w + 24 of A and w, w + 8, .. of B.
@@ -492,8 +497,8 @@ __global__ __launch_bounds__(512, 1) void gemm_tile_kernel(TileProb p) {
   const int crow = lane >> 3;
   const int cchunk = (lane & 7) ^ crow ^ (wave & 1);   // blocks w + 8 i all have parity w & 1
   auto issue = [&](int step, auto st) {
-    unsigned char* da = st.value ? sa1 : sa0;
-    unsigned char* db = st.value ? sb1 : sb0;
+    unsigned char* da = sa[st.value];
+    unsigned char* db = sb[st.value];
     const int k = k_begin + step * kTileBK + 8 * cchunk;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
@@ -530,8 +535,8 @@ __global__ __launch_bounds__(512, 1) void gemm_tile_kernel(TileProb p) {
   // The products are taken as W x^T (B fragments in the MFMA's first operand)
   // so that each lane ends up with four consecutive output columns of a row.
   auto compute = [&](auto st) {
-    const unsigned char* ga = (st.value ? sa1 : sa0) + (FM * wm) * 2048;
-    const unsigned char* gb = (st.value ? sb1 : sb0) + (4 * wn) * 2048;
+    const unsigned char* ga = sa[st.value] + (FM * wm) * 2048;
+    const unsigned char* gb = sb[st.value] + (4 * wn) * 2048;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int off = kk ? foff1 : foff0;
@@ -547,19 +552,38 @@ __global__ __launch_bounds__(512, 1) void gemm_tile_kernel(TileProb p) {
     }
   };
 
-  // Step s: wait for this wave's copies of step s (the only ones in flight),
-  // barrier, refill the stage of step s - 1 with step s + 1, compute.  The
-  // barrier is s_barrier in asm, a compiler memory barrier as well;
-  // __syncthreads() would add a release fence that waits for every copy.
-  auto step = [&](int s, auto st, auto st_next) {
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    if (s + 1 < nsteps) issue(s + 1, st_next);
-    compute(st);
-  };
-  issue(0, S0{});
-  for (int s = 0; s < nsteps; s += 2) {
-    step(s, S0{}, S1{});
-    if (s + 1 < nsteps) step(s + 1, S1{}, S0{});
+  // Step s: wait for this wave's copies of step s, barrier, refill the stage
+  // of step s - 1 with step s + NST - 1, compute.  The barrier is s_barrier in
+  // asm, a compiler memory barrier as well; __syncthreads() would add a
+  // release fence that waits for every copy.
+  if constexpr (NST == 2) {
+    // the copies of step s are the only ones in flight
+    auto step = [&](int s, auto st, auto st_next) {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      if (s + 1 < nsteps) issue(s + 1, st_next);
+      compute(st);
+    };
+    issue(0, S0{});
+    for (int s = 0; s < nsteps; s += 2) {
+      step(s, S0{}, S1{});
+      if (s + 1 < nsteps) step(s + 1, S1{}, S0{});
+    }
+  } else {
+    // those of step s + 1 (PER_WAVE + PER_WAVE_B per wave) may still be
+    constexpr int CPS = PER_WAVE + PER_WAVE_B;
+    auto step = [&](int s, auto st, auto st_issue) {
+      wait_vm_blocks<CPS>(s + 1 < nsteps ? 1 : 0);
+      asm volatile("s_barrier" ::: "memory");
+      if (s + 2 < nsteps) issue(s + 2, st_issue);
+      compute(st);
+    };
+    issue(0, S0{});
+    if (nsteps > 1) issue(1, S1{});
+    for (int s = 0; s < nsteps; s += 3) {
+      step(s, S0{}, S2{});
+      if (s + 1 < nsteps) step(s + 1, S1{}, S0{});
+      if (s + 2 < nsteps) step(s + 2, S2{}, S1{});
+    }
   }
 
   // lane l holds, for row m = 16 i + l % 16 of the wave's block, the four
