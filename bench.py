@@ -446,7 +446,9 @@ def attn_pass(iters, R=4, ctx=32768, kv="bf16"):
            "launches": st["attn"][0], "us_per_launch": round(us, 2), "alg_bytes_per_launch": int(alg),
            "gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
            "keys_per_us": round(R * keys / us, 1),
-           "combine_us": round(st["attn_combine"][1] * 1e3 / st["attn_combine"][0], 2)}
+           "combine_us": round(st["attn_combine"][1] * 1e3 / st["attn_combine"][0], 2) if st["attn_combine"][0]
+           else None,
+           "split_merged_in_launch": st["attn_combine"][0] == 0}
     del cache, layer, C, H, out, ws
     torch.cuda.empty_cache()
     return res
@@ -623,22 +625,29 @@ PROFILE_CMDS = {
     "copy": "rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_copy_{c} -o copy -- python3 -u bench.py "
             "--copy-calibration",
 }
-ATTN_KERNELS = ("attn_ring64_kernel<128, 4, 2>", "attn_combine_kernel")
+# The 8K decode's attention launches (G3 with the split merge G4 in the same
+# launch: one sequence, 8 K/V heads, one item per compute unit).
+ATTN_KERNELS = ("attn_ring64_kernel<128, 4, 2, true>",)
 
 
-def attn_kernel_name(nst, d_h):
+def attn_kernel_name(nst, d_h, merged=False):
     """The attention kernel instance the library launches for a plan's ring
     depth and head dim (bf16 layers), as rocprofv3 names it."""
     if d_h == 128:
-        return "attn_ring64_kernel<128, 4, 2>" if nst >= 3 else "attn_ring64_kernel<128, 2>"
+        if nst >= 3:
+            return "attn_ring64_kernel<128, 4, 2, true>" if merged else "attn_ring64_kernel<128, 4, 2>"
+        return "attn_ring64_kernel<128, 2>"
     return "attn_ring64_kernel<64, 4>"
 
 
-def attn_kernel_label(L, keys, n_kv, d_h):
+def attn_kernel_label(L, keys, n_kv, d_h, merged):
     plan = L.dflash_attn_plan(keys, n_kv)
-    name = attn_kernel_name(plan["nst"], d_h)
-    shape = ("two wave groups, 4-stage ring" if "4, 2>" in name else
+    name = attn_kernel_name(plan["nst"], d_h, merged)
+    shape = ("two wave groups, 4-stage ring" if "4, 2" in name else
              "one wave group, 2-stage ring" if "128, 2>" in name else "one wave group")
+    if merged:
+        return (f"attention ({name}: split-context attention, {shape}, {plan['items']} items of "
+                f"{plan['chunk']} keys, the split merged in the same launch): G3 + G4 in one launch")
     return (f"attention ({name}: split-context attention, {shape}, {plan['items']} items of "
             f"{plan['chunk']} keys) + attn_combine_kernel, the two launches of G3 + G4")
 
@@ -676,9 +685,8 @@ def summarize_profiles(root):
         lines.append(f"| `{_short(r['Name'])[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
     avg = {k: next(float(r["AverageNs"]) / 1e3 for r in stats if k in r["Name"]) for k in ATTN_KERNELS}
-    lines += ["", f"Attention launches of the round: `{ATTN_KERNELS[0]}` {avg[ATTN_KERNELS[0]]:.2f} µs + "
-                  f"`{ATTN_KERNELS[1]}` {avg[ATTN_KERNELS[1]]:.2f} µs = "
-                  f"{avg[ATTN_KERNELS[0]] + avg[ATTN_KERNELS[1]]:.2f} µs on average."]
+    lines += ["", "Attention launches of the round: " + " + ".join(f"`{k}` {avg[k]:.2f} µs" for k in ATTN_KERNELS)
+              + f" = {sum(avg.values()):.2f} µs on average (the split's merge runs inside the attention launch)."]
     open(os.path.join(ROOT, "profiles", "attn_decode_ctx8k_kernel_trace.md"), "w").write("\n".join(lines) + "\n")
 
     def per_kernel(counter, prefix):
@@ -723,7 +731,7 @@ def summarize_profiles(root):
 
     fetch = sum(bytes_of("FETCH_SIZE", k) for k in ATTN_KERNELS)
     write = sum(bytes_of("WRITE_SIZE", k) for k in ATTN_KERNELS)
-    lines += ["", f"Attention of the round (`{ATTN_KERNELS[0]}` + `{ATTN_KERNELS[1]}`) per launch: "
+    lines += ["", "Attention of the round (" + " + ".join(f"`{k}`" for k in ATTN_KERNELS) + ") per launch: "
                   f"{fetch / 1e6:.2f} MB read + {write / 1e6:.2f} MB written = {(fetch + write) / 1e6:.2f} MB of "
                   f"HBM traffic."]
     open(os.path.join(ROOT, "profiles", "attn_decode_ctx8k_hbm_counters.md"), "w").write("\n".join(lines) + "\n")
@@ -1037,7 +1045,8 @@ def main():
         "attn_hbm_frac_peak": att["hbm_frac"],
         "roofline": {"bound": "hbm", "achieved": att["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": att["hbm_frac"], "traffic": traffic_record(),
-                     "kernel": attn_kernel_label(L, [L0 + wl.B + 8] * wl.R, wl.n_kv, wl.d_h),
+                     "kernel": attn_kernel_label(L, [L0 + wl.B + 8] * wl.R, wl.n_kv, wl.d_h,
+                                                 stages["attn_combine"][0] == 0),
                      "protocol": "cold: 16 cache replicas and 2 weight sets in rotation",
                      "us_per_launch": att["us_per_launch"], "alg_bytes_per_launch": att["alg_bytes_per_launch"],
                      "attn_us": kernels["attn"]["us_per_launch"],

@@ -77,6 +77,7 @@ def _load() -> C.CDLL:
         "dflash_accept": (C.c_int, [vp, vp, i64, i32, vp, vp, vp, vp]),
         "dflash_attn_plan": (C.c_int, [C.POINTER(C.c_int64), i32, i32, i64, i32, C.POINTER(C.c_int64)]),
         "dflash_attn_force_chunk": (C.c_int, [i64]),
+        "dflash_attn_sync_timeouts": (C.c_int, [vp]),
         "dflash_stream_read": (C.c_int, [vp, i64, vp, vp]),
         "dflash_mfma_peak": (C.c_int, [i32, i64, vp, vp]),
     }
@@ -363,6 +364,14 @@ def dflash_attn_force_chunk(chunk: int) -> None:
     """Force the attention split of later layer calls to `chunk` keys per
     item (0: the planner's split); a diagnostic for split-invariance tests."""
     _check(LIB.dflash_attn_force_chunk(int(chunk)), "dflash_attn_force_chunk")
+
+
+def dflash_attn_sync_timeouts() -> int:
+    """Attention workgroups whose in-launch merge wait timed out on the
+    current device since the library was loaded (0 in every correct run)."""
+    n = C.c_uint32(0)
+    _check(LIB.dflash_attn_sync_timeouts(C.byref(n)), "dflash_attn_sync_timeouts")
+    return int(n.value)
 
 
 def timing_read() -> dict:

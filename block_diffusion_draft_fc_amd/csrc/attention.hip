@@ -685,6 +685,151 @@ __global__ __launch_bounds__(256, 1) void attn_lds_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- merge of a row's partials
+// One query row's chunk partials merged: m = max_c m_c,
+// l = sum_c 2^(m_c - m) l_c, O = sum_c 2^(m_c - m) O_c / l, stored in the
+// row-major [R*B][n_h*d_h] order of the attention output (head h at columns
+// h*d_h .., "DFlash KV Injection Walkthrough" Step 4.5).  One wave per row,
+// lane l owning head dims 2l, 2l+1 (d_h <= 128); the partials are in the
+// layer's storage type.  Chunks go in groups of 32: every O load of the group
+// and the group's (m, l) loads (lane c % 32 loads chunk c's) are issued before
+// any is used, so a row costs one memory latency per 32 chunks; the group
+// maximum and weights come from wave reductions and readlane.  A group maximum
+// above the running one rescales the accumulators.
+
+__device__ __forceinline__ float2 load2f(const float* p) { return *reinterpret_cast<const float2*>(p); }
+__device__ __forceinline__ float2 load2f(const bf16* p) {
+  const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+  return float2{__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)};
+}
+
+// Row qrow of the n items it0 .. it0 + n - 1 (one (sequence, K/V head)):
+// returns this lane's two normalised output values.
+template <typename T>
+__device__ __forceinline__ float2 merge_partials_row(const T* part_o, const float* part_ml, int64_t it0, int n,
+                                                     int qrows, int qrow, int d_h, int lane) {
+  constexpr int G = 32;
+  const float* ml = part_ml + it0 * 2 * qrows + qrow;   // m_c at ml[c * mstride], l_c at + qrows
+  const int mstride = 2 * qrows;
+  const bool act = 2 * lane < d_h;
+  const T* po = part_o + (it0 * qrows + qrow) * d_h + 2 * (act ? lane : 0);
+  const int ostride = qrows * d_h;
+  float mrun = -INFINITY, lrun = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int cb = 0; cb < n; cb += G) {
+    float2 oc[G];
+    // chunks past n load chunk n - 1 again (their weight is 0): the loads
+    // stay unconditional, so all of them go out before the first is used;
+    // 32-bit offsets within a group of 32 chunks (qrows * d_h <= 64 * 128)
+    const T* pb = po + (int64_t)cb * ostride;
+    const int last = n - 1 - cb;
+#pragma unroll
+    for (int k = 0; k < G; ++k) oc[k] = load2f(pb + min(k, last) * ostride);
+    // issue the O loads before the (m, l) loads and their reductions
+    asm volatile("" ::: "memory");
+    const int c = cb + (lane & (G - 1));
+    const float mc = c < n ? ml[(int64_t)c * mstride] : -INFINITY;
+    const float lc = c < n ? ml[(int64_t)c * mstride + qrows] : 0.f;
+    const float mg = fmaxf(wave_max(mc), mrun);
+    const float mu = mg == -INFINITY ? 0.f : mg;
+    const float wc = __builtin_amdgcn_exp2f(mc - mu);     // weight of chunk cb + lane % 32 (0 for -inf)
+    const float sa = __builtin_amdgcn_exp2f(mrun - mu);   // rescale of the groups before
+    // lanes 32..63 repeat lanes 0..31: half the wave sum is the group's
+    lrun = lrun * sa + 0.5f * wave_sum(wc * lc);
+    o0 *= sa;
+    o1 *= sa;
+    mrun = mg;
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wc), k));
+      o0 += w * oc[k].x;
+      o1 += w * oc[k].y;
+    }
+  }
+  const float inv = lrun > 0.f ? 1.0f / lrun : 0.f;
+  return float2{o0 * inv, o1 * inv};
+}
+
+template <typename T>
+__device__ __forceinline__ void store_merged_row(T* attn, float2 o, int r, int g, int qrow, int B, int group,
+                                                 int n_kv, int d_h, int lane) {
+  if (2 * lane >= d_h) return;
+  const int hl = qrow / B, b = qrow - hl * B;
+  const int h = g * group + hl;
+  T* dst = attn + ((int64_t)r * B + b) * (n_kv * group * d_h) + h * d_h + 2 * lane;
+  dst[0] = from_f32<T>(o.x);
+  dst[1] = from_f32<T>(o.y);
+}
+
+// ---------------------------------------------------------------- in-launch merge: a head's arrivals
+// The items of one K/V head meet at a word of device memory (one atomic add
+// per item, polled by loads that reach past the CU's L1, which observe the
+// atomics), then merge the head's rows from each other's partials.  Items of
+// a head whose workgroup indices agree mod 8 sit on one XCD, so their
+// partials are in that XCD's L2 and no cache write-back is needed; the
+// arrival word counts arrivals per XCD, and if a head's items came from
+// several XCDs every item writes its L2 back and invalidates its caches
+// before the merge (slow, but exact).  Waits are bounded: a workgroup whose
+// wait runs out counts itself in g_attn_sync_timeouts and writes its rows as
+// NaN rather than hang.
+
+__device__ uint32_t g_attn_sync_timeouts = 0;
+constexpr int kAttnSpinLimit = 1 << 18;   // polls (each a memory round trip): ~0.3 s
+
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 0xf;
+}
+// loads that miss the CU's L1, waited for in the same asm block
+__device__ __forceinline__ uint64_t load_sync64(const uint64_t* p) {
+  uint64_t v;
+  asm volatile("global_load_dwordx2 %0, %1, off sc0 sc1\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ uint32_t load_sync32(const uint32_t* p) {
+  uint32_t v;
+  asm volatile("global_load_dword %0, %1, off sc0 sc1\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ int byte_sum(uint64_t v) {
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += (int)((v >> (8 * i)) & 0xff);
+  return s;
+}
+
+// One thread per workgroup, after the workgroup's partial stores have
+// completed: arrive at head word w (kAttnSyncWords u32: the u64 arrival word,
+// the fallback count) and wait for the head's n items.  Returns 0 when all n
+// came from this XCD, 1 when they came from several (every item's L2 is then
+// written back and this CU's caches invalidated), 2 when a wait timed out.
+__device__ __forceinline__ int attn_head_arrive(uint32_t* w, int n) {
+  const uint32_t x = xcc_id() & 7;
+  uint64_t* word = reinterpret_cast<uint64_t*>(w);
+  __hip_atomic_fetch_add(reinterpret_cast<unsigned long long*>(word), 1ull << (8 * x), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
+  uint64_t v = 0;
+  for (int i = 0;; ++i) {
+    v = load_sync64(word);
+    if (byte_sum(v) >= n) break;
+    if (i > kAttnSpinLimit) return 2;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if ((int)((v >> (8 * x)) & 0xff) == n) return 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __hip_atomic_fetch_add(w + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  for (int i = 0; (int)load_sync32(w + 2) < n; ++i) {
+    if (i > kAttnSpinLimit) return 2;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return 1;
+}
+
+hipError_t attn_sync_timeouts(uint32_t* count) {
+  return hipMemcpyFromSymbol(count, HIP_SYMBOL(g_attn_sync_timeouts), sizeof(uint32_t), 0, hipMemcpyDeviceToHost);
+}
+
 // ---------------------------------------------------------------- bf16: shared ring of 64-key blocks
 // For work items with four 16-row query tiles (g*B of 49..64 rows): wave t
 // owns query tile t, and the four waves share one ring of NST 64-key blocks in
@@ -715,7 +860,7 @@ __global__ __launch_bounds__(256, 1) void attn_lds_kernel(AttnArgs a) {
 // an item's chain of dependent blocks is half as long, and at the end group 1
 // hands its (m, l, O) to group 0 through LDS for an exact merge.  The ring
 // then holds the two blocks in work plus NST - 2 in flight.
-template <int DH, int NST, int NG = 1>
+template <int DH, int NST, int NG = 1, bool MERGE = false>
 __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_kernel(AttnArgs a) {
   using V8 = bf16x8;
   static_assert(NST >= 2 && NST <= 8, "blocks in flight are counted by wait_vm_blocks (up to 6 after the current)");
@@ -730,15 +875,25 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_kernel(AttnArgs a) {
   constexpr int PER_WAVE = COPIES / (4 * NG);
   static_assert(PER_WAVE * 4 * NG == COPIES, "copies split evenly over the waves");
   constexpr int STAGE = COPIES * 1024;
+  static_assert(!MERGE || NG == 2, "the in-launch merge runs on the one-workgroup-per-CU plans");
   __shared__ __align__(16) unsigned char ring[NST * STAGE];
   __shared__ int32_t s_page[kAttnMaxChunkPages];
 
   const int item = blockIdx.x;
-  int r = 0;
-  while (r + 1 < a.R && item >= a.item_base[r + 1]) ++r;
-  const int local = item - a.item_base[r];
-  const int g = local / a.chunks[r];
-  const int chunk = local - g * a.chunks[r];
+  int r = 0, g, chunk;
+  if constexpr (MERGE) {
+    // one sequence: item x is chunk x / n_kv of K/V head x % n_kv (the
+    // sequence index is then a constant, and so are the argument offsets)
+    g = item % a.n_kv;
+    chunk = item / a.n_kv;
+  } else {
+    while (r + 1 < a.R && item >= a.item_base[r + 1]) ++r;
+    const int local = item - a.item_base[r];
+    g = local / a.chunks[r];
+    chunk = local - g * a.chunks[r];
+  }
+  // the partial's slot: items of one (sequence, head) in chunk order
+  const int pitem = a.item_base[r] + g * a.chunks[r] + chunk;
   int key_lo, key_hi, qpos0;
   attn_seq_keys(a, r, key_lo, key_hi, qpos0);
   const int kbeg = (key_lo & ~63) + chunk * a.chunk_keys;
@@ -807,7 +962,7 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_kernel(AttnArgs a) {
   // blocks in a rotated order (the online softmax does not depend on it): the
   // items that run at once then do not all stream the same offsets of their
   // chunks at the same time
-  const int rot0 = a.rot > 0 && nblk > 0 ? (int)(((unsigned)item * (unsigned)a.rot) % (unsigned)nblk) : 0;
+  const int rot0 = a.rot > 0 && nblk > 0 ? (int)(((unsigned)pitem * (unsigned)a.rot) % (unsigned)nblk) : 0;
   auto rot_blk = [&](int b) { const int x = b + rot0; return x >= nblk ? x - nblk : x; };
   auto issue = [&](int b) {
     const int blk = kbeg + 64 * rot_blk(b);
@@ -960,28 +1115,52 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_kernel(AttnArgs a) {
       reinterpret_cast<float*>(xb + DT * 1024 + 256)[lane] = l_run;
     }
     __syncthreads();
-    if (grp == 1) return;
-    // exact merge of two online-softmax states with reference maxima m0, m1
-    const float m1 = reinterpret_cast<const float*>(xb + DT * 1024)[lane];
-    const float l1 = reinterpret_cast<const float*>(xb + DT * 1024 + 256)[lane];
-    const float m = fmaxf(m_run, m1);
-    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
-    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+    if (grp == 0) {
+      // exact merge of two online-softmax states with reference maxima m0, m1
+      const float m1 = reinterpret_cast<const float*>(xb + DT * 1024)[lane];
+      const float l1 = reinterpret_cast<const float*>(xb + DT * 1024 + 256)[lane];
+      const float m = fmaxf(m_run, m1);
+      const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+      const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
 #pragma unroll
-    for (int d = 0; d < DT; ++d)
-      o[d] = o[d] * a0 + *reinterpret_cast<const f32x4*>(xb + d * 1024 + 16 * lane) * a1;
-    l_run = l_run * a0 + l1 * a1;
-    m_run = m;
+      for (int d = 0; d < DT; ++d)
+        o[d] = o[d] * a0 + *reinterpret_cast<const f32x4*>(xb + d * 1024 + 16 * lane) * a1;
+      l_run = l_run * a0 + l1 * a1;
+      m_run = m;
+    }
   }
 
-  bf16* po = static_cast<bf16*>(a.part_o) + (int64_t)item * a.qrows * DH;
+  if (grp == 0) {
+    bf16* po = static_cast<bf16*>(a.part_o) + (int64_t)pitem * a.qrows * DH;
 #pragma unroll
-  for (int d = 0; d < DT; ++d) store4(po + (int64_t)row * DH + 16 * d + 4 * q4, o[d]);
-  const float l = sum_xor32(sum_xor16(l_run));
-  if (q4 == 0) {
-    float* pml = a.part_ml + (int64_t)item * 2 * a.qrows;
-    pml[row] = m_run;
-    pml[a.qrows + row] = l;
+    for (int d = 0; d < DT; ++d) store4(po + (int64_t)row * DH + 16 * d + 4 * q4, o[d]);
+    const float l = sum_xor32(sum_xor16(l_run));
+    if (q4 == 0) {
+      float* pml = a.part_ml + (int64_t)pitem * 2 * a.qrows;
+      pml[row] = m_run;
+      pml[a.qrows + row] = l;
+    }
+  }
+
+  if constexpr (MERGE) {
+    // every partial store of the workgroup has reached L2, then one thread
+    // arrives for the workgroup and waits for the head's other items
+    __shared__ int s_status;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int nch = a.chunks[0];
+    if (tid == 0) s_status = attn_head_arrive(a.sync + kAttnSyncStride * g, nch);
+    __syncthreads();
+    const int status = s_status;
+    if (status == 2 && tid == 0) atomicAdd(&g_attn_sync_timeouts, 1u);
+    // rows chunk, chunk + nch, ... of the head, one per wave
+    const int valid = a.group * a.B;
+    for (int qr = chunk + wave * nch; qr < valid; qr += 4 * NG * nch) {
+      float2 ov = merge_partials_row(static_cast<const bf16*>(a.part_o), a.part_ml, (int64_t)g * nch, nch, a.qrows,
+                                     qr, DH, lane);
+      if (status == 2) ov = float2{__builtin_nanf(""), __builtin_nanf("")};
+      store_merged_row(static_cast<bf16*>(a.attn), ov, 0, g, qr, a.B, a.group, a.n_kv, DH, lane);
+    }
   }
 }
 
@@ -1000,7 +1179,9 @@ static hipError_t launch_attn_t(const AttnArgs& a, int items, hipStream_t s) {
     // us against 14.2 us for one group of four); plans of several workgroups
     // per CU two stages and one group.
     if (nqt == 4) {
-      if (a.d_h == 128 && a.nst >= 3) {
+      if (a.d_h == 128 && a.nst >= 3 && a.sync != nullptr) {
+        launch((attn_ring64_kernel<128, 4, 2, true>), dim3(items), dim3(512), 0, s, a);
+      } else if (a.d_h == 128 && a.nst >= 3) {
         launch((attn_ring64_kernel<128, 4, 2>), dim3(items), dim3(512), 0, s, a);
       } else if (a.d_h == 128) {
         launch((attn_ring64_kernel<128, 2>), dim3(items), dim3(256), 0, s, a);
@@ -1034,80 +1215,6 @@ hipError_t launch_attn_split(int dtype, const AttnArgs& a, int items, hipStream_
 }
 
 // ---------------------------------------------------------------- combine
-// One query row's chunk partials merged: m = max_c m_c,
-// l = sum_c 2^(m_c - m) l_c, O = sum_c 2^(m_c - m) O_c / l, stored in the
-// row-major [R*B][n_h*d_h] order of the attention output (head h at columns
-// h*d_h .., "DFlash KV Injection Walkthrough" Step 4.5).  One wave per row,
-// lane l owning head dims 2l, 2l+1 (d_h <= 128); the partials are in the
-// layer's storage type.  Chunks go in groups of 32: every O load of the group
-// and the group's (m, l) loads (lane c % 32 loads chunk c's) are issued before
-// any is used, so a row costs one memory latency per 32 chunks; the group
-// maximum and weights come from wave reductions and readlane.  A group maximum
-// above the running one rescales the accumulators.
-
-__device__ __forceinline__ float2 load2f(const float* p) { return *reinterpret_cast<const float2*>(p); }
-__device__ __forceinline__ float2 load2f(const bf16* p) {
-  const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
-  return float2{__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)};
-}
-
-// Row qrow of the n items it0 .. it0 + n - 1 (one (sequence, K/V head)):
-// returns this lane's two normalised output values.
-template <typename T>
-__device__ __forceinline__ float2 merge_partials_row(const T* part_o, const float* part_ml, int64_t it0, int n,
-                                                     int qrows, int qrow, int d_h, int lane) {
-  constexpr int G = 32;
-  const float* ml = part_ml + it0 * 2 * qrows + qrow;   // m_c at ml[c * mstride], l_c at + qrows
-  const int mstride = 2 * qrows;
-  const bool act = 2 * lane < d_h;
-  const T* po = part_o + (it0 * qrows + qrow) * d_h + 2 * (act ? lane : 0);
-  const int ostride = qrows * d_h;
-  float mrun = -INFINITY, lrun = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int cb = 0; cb < n; cb += G) {
-    float2 oc[G];
-    // chunks past n load chunk n - 1 again (their weight is 0): the loads
-    // stay unconditional, so all of them go out before the first is used;
-    // 32-bit offsets within a group of 32 chunks (qrows * d_h <= 64 * 128)
-    const T* pb = po + (int64_t)cb * ostride;
-    const int last = n - 1 - cb;
-#pragma unroll
-    for (int k = 0; k < G; ++k) oc[k] = load2f(pb + min(k, last) * ostride);
-    // issue the O loads before the (m, l) loads and their reductions
-    asm volatile("" ::: "memory");
-    const int c = cb + (lane & (G - 1));
-    const float mc = c < n ? ml[(int64_t)c * mstride] : -INFINITY;
-    const float lc = c < n ? ml[(int64_t)c * mstride + qrows] : 0.f;
-    const float mg = fmaxf(wave_max(mc), mrun);
-    const float mu = mg == -INFINITY ? 0.f : mg;
-    const float wc = __builtin_amdgcn_exp2f(mc - mu);     // weight of chunk cb + lane % 32 (0 for -inf)
-    const float sa = __builtin_amdgcn_exp2f(mrun - mu);   // rescale of the groups before
-    // lanes 32..63 repeat lanes 0..31: half the wave sum is the group's
-    lrun = lrun * sa + 0.5f * wave_sum(wc * lc);
-    o0 *= sa;
-    o1 *= sa;
-    mrun = mg;
-#pragma unroll
-    for (int k = 0; k < G; ++k) {
-      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wc), k));
-      o0 += w * oc[k].x;
-      o1 += w * oc[k].y;
-    }
-  }
-  const float inv = lrun > 0.f ? 1.0f / lrun : 0.f;
-  return float2{o0 * inv, o1 * inv};
-}
-
-template <typename T>
-__device__ __forceinline__ void store_merged_row(T* attn, float2 o, int r, int g, int qrow, int B, int group,
-                                                 int n_kv, int d_h, int lane) {
-  if (2 * lane >= d_h) return;
-  const int hl = qrow / B, b = qrow - hl * B;
-  const int h = g * group + hl;
-  T* dst = attn + ((int64_t)r * B + b) * (n_kv * group * d_h) + h * d_h + 2 * lane;
-  dst[0] = from_f32<T>(o.x);
-  dst[1] = from_f32<T>(o.y);
-}
-
 // The combine launch: one workgroup of one wave per query row (several per
 // CU, so that every CU streams a share of the partials).
 

@@ -661,7 +661,7 @@ struct KvPlan {
   bool fused_qkv;
   bool block_rows_apart;
   GemmJob gq, gkv, go;
-  size_t off_q, off_pq, off_pkv, off_po, off_pml, off_attn, off_pout, total;
+  size_t off_q, off_pq, off_pkv, off_po, off_pml, off_attn, off_pout, off_sync, total;
   int64_t max_items;
 };
 
@@ -713,6 +713,7 @@ KvPlan plan_kv(const dflash_layer_desc* L, const dflash_cache* c, int64_t T, int
   p.off_pml = o; o = align_up(o + (size_t)p.max_items * 2 * p.qrows * sizeof(float));
   p.off_attn = o; o = align_up(o + (size_t)p.RB * p.qd * eb);
   p.off_pout = o; o = align_up(o + job_part_bytes(p.go));
+  p.off_sync = o; o = align_up(o + (size_t)kAttnSyncStride * sizeof(uint32_t) * L->n_kv);
   p.total = o;
   return p;
 }
@@ -886,6 +887,22 @@ size_t dflash_kv_inject_attn_ws_bytes(const dflash_layer_desc* L, const dflash_c
 
 namespace {
 
+// Compute units of the current device (0 if it cannot be queried), read once
+// per device.
+int device_cus() {
+  static std::mutex mu;
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> g(mu);
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 // One layer call.  exact_ws: the workspace must hold this call's own needs
 // (the attention partials of its planned split), not the figure that holds
 // for every call with these sizes.
@@ -989,6 +1006,16 @@ int kv_inject_impl(const dflash_layer_desc* L, dflash_cache* c, const void* C, c
     // bounded by construction for the planner's splits; a forced split may not fit
     if (items > p.max_items) return DFLASH_ERR_SHAPE;
   }
+  // The split merges in the attention launch itself (no combine launch) for
+  // one sequence of bf16 rows over a bf16 cache with 49..64 query rows per
+  // K/V head at d_h 128, on the one-workgroup-per-CU plans: the items of a
+  // head wait for each other, so every item must be resident at once (at
+  // most one per compute unit), and a head's items must share an XCD (n_kv
+  // a multiple of the 8 XCDs; item x takes head x % n_kv).  Device-driven
+  // rounds keep the combine launch, which also advances the device lengths.
+  const bool merge_in_attn = dt == DFLASH_BF16 && !fp8 && L->d_h == 128 && cdiv(p.qrows, 16) == 4 &&
+                             aa.nst >= 3 && R == 1 && L->n_kv % 8 == 0 && L->n_kv <= 64 && dev_rows == nullptr && items > 0 &&
+                             items <= device_cus() && aa.chunks[0] <= 255;
   if (exact_ws) {
     p = plan_kv(L, c, T, B, items);
     if (ws_bytes < p.total) return DFLASH_ERR_WORKSPACE;
@@ -1002,6 +1029,11 @@ int kv_inject_impl(const dflash_layer_desc* L, dflash_cache* c, const void* C, c
   void* attn = w + p.off_attn;
   float* part_out = reinterpret_cast<float*>(w + p.off_pout);
   aa.q_ws = q_ws; aa.part_o = part_o; aa.part_ml = part_ml;
+  uint32_t* attn_sync = reinterpret_cast<uint32_t*>(w + p.off_sync);
+  if (merge_in_attn) {
+    aa.sync = attn_sync;
+    aa.attn = attn;
+  }
 
   // 1. page table entries for the rows this call appends
   hipError_t e = enqueue_page_table(c, ap, s);
@@ -1068,6 +1100,10 @@ int kv_inject_impl(const dflash_layer_desc* L, dflash_cache* c, const void* C, c
       a.d_rows = dev_rows;
       a.n_max = cu_ctx[1];
     }
+    if (merge_in_attn) {
+      a.attn_sync = attn_sync;
+      a.n_sync = L->n_kv;
+    }
     e = staged(DFLASH_STAGE_QKV_EPILOGUE, s, true, [&] { return launch_qkv_epilogue(dt, a, s); });
   }
 
@@ -1077,7 +1113,7 @@ int kv_inject_impl(const dflash_layer_desc* L, dflash_cache* c, const void* C, c
       e = staged(DFLASH_STAGE_ATTN, s, items > 0, [&] {
         return fp8 ? launch_attn_fp8(aa, (int)items, s) : launch_attn_split(dt, aa, (int)items, s);
       });
-    if (e == hipSuccess) {
+    if (e == hipSuccess && !merge_in_attn) {
       CombineArgs ca{};
       ca.part_o = part_o; ca.part_ml = part_ml; ca.attn = attn;
       ca.R = R; ca.B = B; ca.n_kv = L->n_kv; ca.group = (int32_t)p.group; ca.qrows = (int32_t)p.qrows;
@@ -1415,6 +1451,11 @@ int dflash_mfma_peak(int32_t iters, int64_t workgroups, float* sink, void* strea
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(
       staged(DFLASH_STAGE_MFMA_PEAK, s, true, [&] { return launch_mfma_peak(iters, workgroups, sink, s); }));
+}
+
+int dflash_attn_sync_timeouts(uint32_t* count) {
+  if (!count) return DFLASH_ERR_ARG;
+  return hip_status(attn_sync_timeouts(count));
 }
 
 int dflash_attn_force_chunk(int64_t chunk) {

@@ -161,6 +161,10 @@ struct QkvEpiArgs {
   const int32_t* d_len;
   const int32_t* d_rows;
   int32_t n_max;
+  // the arrival words of an in-launch attention merge (n_sync heads), zeroed
+  // here so that the attention launch that follows starts from zero
+  uint32_t* attn_sync;
+  int32_t n_sync;
 };
 hipError_t launch_qkv_epilogue(int dtype, const QkvEpiArgs& a, hipStream_t s);
 
@@ -194,7 +198,22 @@ struct AttnArgs {
   const int32_t* d_len;
   const int32_t* d_rows;
   int32_t n_max;
+  // In-launch merge (sync not null; one sequence, n_kv a multiple of 8, at
+  // most one item per CU): item x takes K/V head x % n_kv, chunk x / n_kv, so
+  // the items of a head share an XCD (workgroups are dealt to the XCDs in
+  // turn); once all of a head's items have stored their partials they merge
+  // its rows and write the normalised output to `attn` ([B][n_h*d_h]).
+  // sync[kAttnSyncStride * g ..]: head g's arrival word (u64: a byte per XCD,
+  // each arrival adding one to its XCD's byte) and the fallback count (u32),
+  // zeroed by the q/k/v epilogue before every launch.
+  uint32_t* sync;
+  void* attn;
 };
+constexpr int kAttnSyncStride = 64;   // u32 words between heads' arrival words (256 bytes)
+constexpr int kAttnSyncWords = 4;     // words of a head that the epilogue zeroes
+// Workgroups whose wait for the other items of their head timed out since the
+// library was loaded (their rows are written as NaN); 0 in every correct run.
+hipError_t attn_sync_timeouts(uint32_t* count);
 
 // Key range and block position of sequence r for one launch.
 __device__ __forceinline__ void attn_seq_keys(const AttnArgs& a, int r, int& lo, int& hi, int& q0) {

@@ -465,6 +465,21 @@ int dflash_attn_plan(const int64_t *keys, int32_t R, int32_t n_kv, int64_t chunk
  * ---------------------------------------------------------------------- */
 int dflash_attn_force_chunk(int64_t chunk);
 
+/* ------------------------------------------------------------------------
+ * In-launch merge watchdog.  When a layer call of one sequence (bf16, d_h 128,
+ * 49..64 query rows per K/V head, n_kv a multiple of 8, at most one attention
+ * work item per compute unit) merges its attention split inside the
+ * attention launch, the items of a K/V head wait for each other there.  Each
+ * wait is bounded: a workgroup that gives up writes its rows as NaN and is
+ * counted here.  *count receives the number of such workgroups on the
+ * current device since the library was loaded (0 in every correct run; a
+ * non-zero count means some attention work item could not become resident,
+ * e.g. because other work held the compute units).  Synchronous with the
+ * device.  Returns DFLASH_ERR_ARG for a null pointer, DFLASH_ERR_HIP if the
+ * read fails.
+ * ---------------------------------------------------------------------- */
+int dflash_attn_sync_timeouts(uint32_t *count);
+
 #ifdef __cplusplus
 }
 #endif

@@ -187,9 +187,11 @@ def test_fresh_context_1024_bf16():
 
 
 def test_decode_8k_all_64_rounds():
-    """Every round of the decode workload at full size, as the benchmark runs it."""
+    """Every round of the decode workload at full size, as the benchmark runs
+    it (the attention merges its split in its own launch)."""
     wl = configs.DECODE_8K
     run_rounds(wl, wl.rounds)
+    assert L.dflash_attn_sync_timeouts() == 0
 
 
 def test_ragged_paged_16_requests():
@@ -361,6 +363,50 @@ SMALL = [
 @pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
 def test_small_case(wl):
     run_rounds(wl, wl.rounds)
+
+
+# One sequence with n_kv a multiple of 8 (bf16, d_h 128, 49..64 query rows
+# per K/V head, at most one attention item per compute unit): the attention
+# launch merges its own split, and no combine launch follows.  The cases span
+# one to tens of chunks per head (rows per merging item from 64 down to 2),
+# padded query rows (B = 13: 52 of 64), two query heads per K/V head, 16 K/V
+# heads, a sliding window, paged and ring caches and a residual stack; the
+# two-request batch keeps the combine launch.
+MERGE = [
+    (_small("merge_g4_b16_n8", d=512, n_h=32, n_kv=8, d_h=128, B=16, prefill_len=300, n_range=(1, 16)), True),
+    (_small("merge_g4_b13_padded_rows", d=512, n_h=32, n_kv=8, d_h=128, B=13, prefill_len=700, rounds=2), True),
+    (_small("merge_one_chunk_per_head", d=512, n_h=32, n_kv=8, d_h=128, B=16, prefill_len=40, rounds=2), True),
+    (_small("merge_long_cache", d=512, n_h=32, n_kv=8, d_h=128, B=16, prefill_len=5000, rounds=2), True),
+    (_small("merge_g2_b32", d=512, n_h=16, n_kv=8, d_h=128, B=32, prefill_len=900, rounds=2), True),
+    (_small("merge_n_kv16", d=512, n_h=64, n_kv=16, d_h=128, B=16, prefill_len=600, rounds=2), True),
+    (_small("merge_window_100", d=512, n_h=32, n_kv=8, d_h=128, B=16, prefill_len=500, window=100,
+            sliding_layers=(0,)), True),
+    (_small("merge_paged", d=512, n_h=32, n_kv=8, d_h=128, B=16, prefill_len=800, page_size=64), True),
+    (_small("merge_ring_window_100", d=512, n_h=32, n_kv=8, d_h=128, B=16, prefill_len=500, window=100,
+            sliding_layers=(0,), ring=True, rounds=4), True),
+    (_small("merge_stack3_residual", n_layers=3, d=512, n_h=32, n_kv=8, d_h=128, B=16, prefill_len=600,
+            window=256, sliding_layers=(0, 2)), True),
+    (_small("combine_r2_n8", R=2, d=512, n_h=32, n_kv=8, d_h=128, B=16, prefill="uniform",
+            prefill_range=(100, 900), rounds=2), False),
+]
+
+
+@pytest.mark.parametrize("wl,merged", MERGE, ids=[w.name for w, _ in MERGE])
+def test_in_launch_merge(wl, merged):
+    L.timing_enable(True)
+    L.timing_reset()
+    try:
+        run_rounds(wl, wl.rounds)
+        t = L.timing_read()
+    finally:
+        L.timing_enable(False)
+        L.timing_reset()
+    assert t["attn"][0] > 0
+    if merged:
+        assert t["attn_combine"][0] == 0, "the split should merge inside the attention launch"
+    else:
+        assert t["attn_combine"][0] > 0, "batches of several sequences keep the combine launch"
+    assert L.dflash_attn_sync_timeouts() == 0
 
 
 # ------------------------------------------------------------------ fp8 (E4M3) caches
