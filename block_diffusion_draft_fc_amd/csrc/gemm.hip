@@ -748,12 +748,15 @@ hipError_t launch_gemm_stream(const TileProb& p, int mt, hipStream_t s) {
 // the storage type with the residual added (out may alias add: each element
 // is read and written by the same lane).
 // Requirements (checked by the planner): bf16, K a multiple of 512, N of 4.
-constexpr int kFullkWaves = 8, kFullkStages = 4;
+constexpr int kFullkWaves = 8, kFullkStages = 5;
 
 __global__ __launch_bounds__(64 * kFullkWaves) void gemm_fullk_kernel(FullkArgs p) {
   constexpr int STAGE = 4 * 1024;   // 16 weight rows + 16 activation rows, 128 bytes each
+  // the rings fill the CU's 160 KB; the waves' sums meet in the first ring
+  // once every wave is past its last step
   __shared__ __align__(16) unsigned char ring[kFullkWaves][kFullkStages * STAGE];
-  __shared__ f32x4 red[kFullkWaves][64];
+  static_assert(kFullkWaves * 64 * sizeof(f32x4) <= kFullkStages * STAGE, "the reduction fits one wave's ring");
+  f32x4 (*red)[64] = reinterpret_cast<f32x4 (*)[64]>(&ring[0][0]);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * 16;
@@ -803,6 +806,7 @@ __global__ __launch_bounds__(64 * kFullkWaves) void gemm_fullk_kernel(FullkArgs 
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (t + AHEAD < nsteps) issue(t + AHEAD);
   }
+  __syncthreads();   // every wave's ring reads are done before ring 0 takes the sums
   red[wave][lane] = acc;
   __syncthreads();
   if (wave != 0) return;
