@@ -78,6 +78,7 @@ def _load() -> C.CDLL:
         "dflash_attn_plan": (C.c_int, [C.POINTER(C.c_int64), i32, i32, i64, i32, C.POINTER(C.c_int64)]),
         "dflash_attn_force_chunk": (C.c_int, [i64]),
         "dflash_attn_sync_timeouts": (C.c_int, [vp]),
+        "dflash_attn_force_merge_spread": (C.c_int, [i32]),
         "dflash_stream_read": (C.c_int, [vp, i64, vp, vp]),
         "dflash_mfma_peak": (C.c_int, [i32, i64, vp, vp]),
     }
@@ -364,6 +365,13 @@ def dflash_attn_force_chunk(chunk: int) -> None:
     """Force the attention split of later layer calls to `chunk` keys per
     item (0: the planner's split); a diagnostic for split-invariance tests."""
     _check(LIB.dflash_attn_force_chunk(int(chunk)), "dflash_attn_force_chunk")
+
+
+def dflash_attn_force_merge_spread(on: bool) -> None:
+    """Deal each K/V head's attention items to consecutive workgroups where the
+    split merges in the attention launch (a diagnostic: the merge then takes
+    its write-back path across XCDs)."""
+    _check(LIB.dflash_attn_force_merge_spread(1 if on else 0), "dflash_attn_force_merge_spread")
 
 
 def dflash_attn_sync_timeouts() -> int:

@@ -884,8 +884,13 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_kernel(AttnArgs a) {
   if constexpr (MERGE) {
     // one sequence: item x is chunk x / n_kv of K/V head x % n_kv (the
     // sequence index is then a constant, and so are the argument offsets)
-    g = item % a.n_kv;
-    chunk = item / a.n_kv;
+    if (a.merge_spread) {
+      g = item / a.chunks[0];
+      chunk = item - g * a.chunks[0];
+    } else {
+      g = item % a.n_kv;
+      chunk = item / a.n_kv;
+    }
   } else {
     while (r + 1 < a.R && item >= a.item_base[r + 1]) ++r;
     const int local = item - a.item_base[r];

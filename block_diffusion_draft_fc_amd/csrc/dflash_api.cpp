@@ -149,6 +149,7 @@ struct AttnSplit {
 };
 
 std::atomic<int64_t> g_forced_chunk{0};
+std::atomic<int> g_merge_spread{0};   // dflash_attn_force_merge_spread
 
 AttnSplit plan_attn_split(const std::vector<int64_t>& keys, int n_kv, int64_t chunk_cap, bool fp8) {
   int64_t total = 0;
@@ -1033,6 +1034,7 @@ int kv_inject_impl(const dflash_layer_desc* L, dflash_cache* c, const void* C, c
   if (merge_in_attn) {
     aa.sync = attn_sync;
     aa.attn = attn;
+    aa.merge_spread = g_merge_spread.load();
   }
 
   // 1. page table entries for the rows this call appends
@@ -1456,6 +1458,12 @@ int dflash_mfma_peak(int32_t iters, int64_t workgroups, float* sink, void* strea
 int dflash_attn_sync_timeouts(uint32_t* count) {
   if (!count) return DFLASH_ERR_ARG;
   return hip_status(attn_sync_timeouts(count));
+}
+
+int dflash_attn_force_merge_spread(int32_t on) {
+  if (on != 0 && on != 1) return DFLASH_ERR_ARG;
+  g_merge_spread.store(on);
+  return DFLASH_OK;
 }
 
 int dflash_attn_force_chunk(int64_t chunk) {

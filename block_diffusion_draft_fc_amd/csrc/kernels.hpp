@@ -208,6 +208,10 @@ struct AttnArgs {
   // zeroed by the q/k/v epilogue before every launch.
   uint32_t* sync;
   void* attn;
+  // a diagnostic item order for the in-launch merge: chunk x % chunks of head
+  // x / chunks, which deals a head's items to several XCDs (the merge's
+  // write-back path); 0 in every ordinary call
+  int32_t merge_spread;
 };
 constexpr int kAttnSyncStride = 64;   // u32 words between heads' arrival words (256 bytes)
 constexpr int kAttnSyncWords = 4;     // words of a head that the epilogue zeroes

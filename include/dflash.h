@@ -480,6 +480,19 @@ int dflash_attn_force_chunk(int64_t chunk);
  * ---------------------------------------------------------------------- */
 int dflash_attn_sync_timeouts(uint32_t *count);
 
+/* ------------------------------------------------------------------------
+ * In-launch merge item order (a diagnostic for tests of the merge's
+ * write-back path).  Where a layer call merges its attention split inside
+ * the attention launch (see dflash_attn_sync_timeouts), on = 1 deals each
+ * K/V head's work items to consecutive workgroups, so that a head's items
+ * run on several XCDs and merge through the path that writes every XCD's L2
+ * back first (slower; results equal up to rounding order); 0 restores the
+ * order that keeps a head on one XCD.  Process-wide, not synchronised with
+ * calls in flight on other threads.  Returns DFLASH_ERR_ARG unless on is 0
+ * or 1.
+ * ---------------------------------------------------------------------- */
+int dflash_attn_force_merge_spread(int32_t on);
+
 #ifdef __cplusplus
 }
 #endif

@@ -246,6 +246,47 @@ def test_split_invariance_decode_8k():
             say(f"  chunk {chunk} round {rnd}: {e:.2e} from the planner's split")
 
 
+def test_in_launch_merge_across_xcds_decode_8k():
+    """The in-launch merge with each K/V head's items on consecutive
+    workgroups (so a head's 26 items run on several XCDs): every item writes
+    its L2 back and meets the others at a second count before merging.  The
+    first 2 rounds of the decode workload against the oracle and against the
+    ordinary order, no combine launch, no wait timed out."""
+    wl = configs.DECODE_8K
+    rounds = 2
+    kv = prefill_host(wl)
+    sched = G.schedule(wl)
+    orc = oracle_stack(wl, kv)
+    inputs = [G.round_inputs(wl, rnd, sched[rnd]) for rnd in range(rounds)]
+    refs = [orc.round(x, cu, H, wl.B)[0][0] for x, cu, H in inputs]
+    outs = {}
+    try:
+        for spread in (False, True):
+            L.dflash_attn_force_merge_spread(spread)
+            say(f"case in-launch merge spread={spread}")
+            gm = GpuModel(wl, rounds)
+            gm.prefill(kv)
+            L.timing_enable(True)
+            L.timing_reset()
+            outs[spread] = [gm.round(x, cu, H)[0] for x, cu, H in inputs]
+            t = L.timing_read()
+            L.timing_enable(False)
+            assert t["attn"][0] == rounds and t["attn_combine"][0] == 0
+            for rnd in range(rounds):
+                e = rel_l2(outs[spread][rnd], refs[rnd])
+                assert e <= TOL["bf16"], f"spread {spread} round {rnd}: rel-L2 {e:.3e}"
+            del gm
+            torch.cuda.empty_cache()
+    finally:
+        L.dflash_attn_force_merge_spread(False)
+        L.timing_enable(False)
+        L.timing_reset()
+    for rnd in range(rounds):
+        e = rel_l2(outs[True][rnd], outs[False][rnd])
+        assert e <= 5e-3, f"round {rnd}: the spread order differs by {e:.3e}"
+    assert L.dflash_attn_sync_timeouts() == 0
+
+
 def test_stack5_hybrid_ring_full_shapes():
     """The same stack with bounded ring caches on the sliding layers (4160
     rows instead of the whole context): 2 requests on 8192-row contexts, so
