@@ -132,11 +132,17 @@ def _cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(wl, budget_s):
+PARITY_ROUNDS = 8   # rounds of the cycle the CPU leg also checks against the GPU's outputs
+
+
+def cpu_baseline(wl, budget_s, gpu_outs=()):
     """The fp64 oracle on the host cores, over the first rounds of the same
     schedule until `budget_s` seconds of round work have run with every
     BLAS thread, then a third of that budget on one thread.  The oracle's
-    prefill (building its cache of the 8192 prefilled rows) is timed apart."""
+    prefill (building its cache of the 8192 prefilled rows) is timed apart.
+    gpu_outs[r]: the layer output of round r from the GPU (rounds in order
+    from the same prefill); their rel-L2 against the oracle's outputs of the
+    same rounds is reported as `parity` (outside the timed round work)."""
     from oracle import dflash_oracle as O
     from workloads import generate as G
 
@@ -152,7 +158,9 @@ def cpu_baseline(wl, budget_s):
     K0, V0 = G.prefill_kv(wl, 0, 0, wl.prefill_len)
     sched = G.schedule(wl)
 
-    def run(budget):
+    errs = []
+
+    def run(budget, check=False):
         """Rounds of the cycle in order (starting over from the prefill after
         round 63) until `budget` seconds of round work."""
         done, spent, prefill_s = 0, 0.0, 0.0
@@ -164,12 +172,15 @@ def cpu_baseline(wl, budget_s):
                 prefill_s = time.perf_counter() - t0
             x, cu, H = G.round_inputs(wl, r, sched[r])
             t0 = time.perf_counter()
-            stack.round(x, cu, H, wl.B)
+            outs, _ = stack.round(x, cu, H, wl.B)
             spent += time.perf_counter() - t0
+            if check and done < len(gpu_outs):
+                ref, got = outs[0], np.asarray(gpu_outs[done], dtype=np.float64)
+                errs.append(float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)))
             done += 1
         return done, spent, prefill_s
 
-    done, spent, prefill_s = run(budget_s)
+    done, spent, prefill_s = run(budget_s, check=True)
     single = None
     if threadpool_limits is not None:
         with threadpool_limits(limits=1):
@@ -181,7 +192,12 @@ def cpu_baseline(wl, budget_s):
             "sample": f"{done} rounds of the {wl.rounds}-round seeded cycle (8192-row cache, 1-16 new rows, block 16), "
                       f"fp64 NumPy on {blas} BLAS threads of {cores} cores, {spent:.1f} s of round work; "
                       f"weight set-up and the oracle's prefill excluded",
-            "prefill_s": round(prefill_s, 3), "single_thread": single}
+            "prefill_s": round(prefill_s, 3), "single_thread": single,
+            "parity": {"rounds": len(errs), "rel_l2_max": max(errs) if errs else None,
+                       "rel_l2_mean": float(np.mean(errs)) if errs else None, "tolerance": 1e-2,
+                       "pass": bool(errs) and max(errs) <= 1e-2,
+                       "what": "the GPU's layer output of each of the cycle's first rounds (in order on a fresh "
+                               "copy of the prefilled cache) against the oracle's"}}
 
 
 # ---------------------------------------------------------------------------- fresh-context projections
@@ -1095,8 +1111,19 @@ def main():
         log("bench: 5-layer hybrid stack, unbounded caches")
         res["stack5_hybrid_full_caches"] = batched_rounds(configs.STACK5_HYBRID, 8, ring=False)
     if not args.no_cpu_baseline:
+        # rounds 0 .. PARITY_ROUNDS - 1 in order on a fresh copy of the prefilled
+        # cache: the outputs the CPU leg sets against the oracle's
+        log("bench: the cycle's first rounds in order, for the parity check")
+        pc = new_cache()
+        L.dflash_cache_crop(pc, [L0])
+        par_outs = []
+        for r in range(PARITY_ROUNDS):
+            step(r, pc)
+            par_outs.append(out.float().cpu().numpy())
+        del pc
+        torch.cuda.empty_cache()
         log("bench: timing the fp64 oracle on the host")
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, par_outs)
     print(json.dumps(res), flush=True)
     return 0
 
