@@ -860,7 +860,10 @@ hipError_t attn_sync_timeouts(uint32_t* count) {
 // an item's chain of dependent blocks is half as long, and at the end group 1
 // hands its (m, l, O) to group 0 through LDS for an exact merge.  The ring
 // then holds the two blocks in work plus NST - 2 in flight.
-template <int DH, int NST, int NG = 1, bool MERGE = false>
+// MERGE: 0 = partials for the combine launch; 1 = the split merged in the
+// launch, item x on K/V head x % n_kv; 2 = the same with a head's items on
+// consecutive workgroups (the diagnostic order that spreads a head over XCDs).
+template <int DH, int NST, int NG = 1, int MERGE = 0>
 __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_kernel(AttnArgs a) {
   using V8 = bf16x8;
   static_assert(NST >= 2 && NST <= 8, "blocks in flight are counted by wait_vm_blocks (up to 6 after the current)");
@@ -875,32 +878,41 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_kernel(AttnArgs a) {
   constexpr int PER_WAVE = COPIES / (4 * NG);
   static_assert(PER_WAVE * 4 * NG == COPIES, "copies split evenly over the waves");
   constexpr int STAGE = COPIES * 1024;
-  static_assert(!MERGE || NG == 2, "the in-launch merge runs on the one-workgroup-per-CU plans");
+  static_assert(MERGE == 0 || NG == 2, "the in-launch merge runs on the one-workgroup-per-CU plans");
   __shared__ __align__(16) unsigned char ring[NST * STAGE];
   __shared__ int32_t s_page[kAttnMaxChunkPages];
 
   const int item = blockIdx.x;
   int r = 0, g, chunk;
-  if constexpr (MERGE) {
-    // one sequence: item x is chunk x / n_kv of K/V head x % n_kv (the
-    // sequence index is then a constant, and so are the argument offsets)
-    if (a.merge_spread) {
-      g = item / a.chunks[0];
-      chunk = item - g * a.chunks[0];
+  int key_lo, key_hi, qpos0;
+  if constexpr (MERGE != 0) {
+    // one sequence of a host-driven round: item x is chunk x / n_kv of K/V
+    // head x % n_kv.  Every argument the start needs sits at a fixed offset
+    // and nothing here branches on an argument, so they are read in one
+    // batch (a chain of dependent argument reads, each an L2 round trip on
+    // first touch, held back the first K/V copies by ~2 us).
+    if constexpr (MERGE == 2) {
+      g = item / a.seq0[3];
+      chunk = item - g * a.seq0[3];
     } else {
       g = item % a.n_kv;
       chunk = item / a.n_kv;
     }
+    key_lo = a.seq0[0];
+    key_hi = a.seq0[1];
+    qpos0 = a.seq0[2];
+    // the cache's head count and head dim in the same batch (the compiler
+    // would read them where the first addresses are formed, a wait later)
+    asm volatile("" ::"s"(a.cache.n_kv), "s"(a.cache.d_h));
   } else {
     while (r + 1 < a.R && item >= a.item_base[r + 1]) ++r;
     const int local = item - a.item_base[r];
     g = local / a.chunks[r];
     chunk = local - g * a.chunks[r];
+    attn_seq_keys(a, r, key_lo, key_hi, qpos0);
   }
   // the partial's slot: items of one (sequence, head) in chunk order
-  const int pitem = a.item_base[r] + g * a.chunks[r] + chunk;
-  int key_lo, key_hi, qpos0;
-  attn_seq_keys(a, r, key_lo, key_hi, qpos0);
+  const int pitem = MERGE != 0 ? g * a.seq0[3] + chunk : a.item_base[r] + g * a.chunks[r] + chunk;
   const int kbeg = (key_lo & ~63) + chunk * a.chunk_keys;
   const int kend = min(kbeg + a.chunk_keys, key_hi);
   const int nblk = kend > kbeg ? (kend - kbeg + 63) >> 6 : 0;
@@ -1147,13 +1159,13 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_kernel(AttnArgs a) {
     }
   }
 
-  if constexpr (MERGE) {
+  if constexpr (MERGE != 0) {
     // every partial store of the workgroup has reached L2, then one thread
     // arrives for the workgroup and waits for the head's other items
     __shared__ int s_status;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const int nch = a.chunks[0];
+    const int nch = a.seq0[3];
     if (tid == 0) s_status = attn_head_arrive(a.sync + kAttnSyncStride * g, nch);
     __syncthreads();
     const int status = s_status;
@@ -1184,8 +1196,10 @@ static hipError_t launch_attn_t(const AttnArgs& a, int items, hipStream_t s) {
     // us against 14.2 us for one group of four); plans of several workgroups
     // per CU two stages and one group.
     if (nqt == 4) {
-      if (a.d_h == 128 && a.nst >= 3 && a.sync != nullptr) {
-        launch((attn_ring64_kernel<128, 4, 2, true>), dim3(items), dim3(512), 0, s, a);
+      if (a.d_h == 128 && a.nst >= 3 && a.sync != nullptr && a.merge_spread) {
+        launch((attn_ring64_kernel<128, 4, 2, 2>), dim3(items), dim3(512), 0, s, a);
+      } else if (a.d_h == 128 && a.nst >= 3 && a.sync != nullptr) {
+        launch((attn_ring64_kernel<128, 4, 2, 1>), dim3(items), dim3(512), 0, s, a);
       } else if (a.d_h == 128 && a.nst >= 3) {
         launch((attn_ring64_kernel<128, 4, 2>), dim3(items), dim3(512), 0, s, a);
       } else if (a.d_h == 128) {

@@ -1004,6 +1004,10 @@ int kv_inject_impl(const dflash_layer_desc* L, dflash_cache* c, const void* C, c
       items += (int64_t)aa.chunks[r] * L->n_kv;
     }
     aa.item_base[R] = (int32_t)items;
+    aa.seq0[0] = aa.key_lo[0];
+    aa.seq0[1] = aa.key_hi[0];
+    aa.seq0[2] = aa.qpos0[0];
+    aa.seq0[3] = aa.chunks[0];
     // bounded by construction for the planner's splits; a forced split may not fit
     if (items > p.max_items) return DFLASH_ERR_SHAPE;
   }

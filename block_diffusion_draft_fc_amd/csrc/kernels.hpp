@@ -186,6 +186,10 @@ struct AttnArgs {
   int32_t window;
   float scale_log2;      // d_h^-0.5 * log2(e) (times the key scale of an fp8 cache)
   float v_scale;         // value scale of an fp8 cache (the fp8 kernel scales its partial O)
+  // sequence 0's key_lo, key_hi, qpos0 and chunks beside the scalars above,
+  // so that a one-sequence launch reads everything its start needs from one
+  // span of the arguments
+  int32_t seq0[4];
   int32_t item_base[kMaxSeqs + 1];  // items of sequence r: [item_base[r], item_base[r+1])
   int32_t chunks[kMaxSeqs];         // items per (sequence, K/V head)
   int32_t key_lo[kMaxSeqs];         // first key any query may see
