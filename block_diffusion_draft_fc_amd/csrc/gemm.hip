@@ -634,6 +634,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_stream_kernel(TileProb p) {
   constexpr int XS = kStreamKC / 32;                         // activation slabs per 16-row tile
   __shared__ __align__(16) unsigned char sx[MT * XS * 1024];
   __shared__ __align__(16) unsigned char ring[WAVES][NST * 2048];
+  // the operand pointers in the same batch of argument reads as the sizes
+  asm volatile("" ::"s"(p.x0), "s"(p.x1), "s"(p.w));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nt = blockIdx.x % p.n_tiles, split = blockIdx.x / p.n_tiles;
@@ -757,6 +759,10 @@ __global__ __launch_bounds__(64 * kFullkWaves) void gemm_fullk_kernel(FullkArgs 
   __shared__ __align__(16) unsigned char ring[kFullkWaves][kFullkStages * STAGE];
   static_assert(kFullkWaves * 64 * sizeof(f32x4) <= kFullkStages * STAGE, "the reduction fits one wave's ring");
   f32x4 (*red)[64] = reinterpret_cast<f32x4 (*)[64]>(&ring[0][0]);
+  // the operand pointers in the same batch of argument reads as the sizes
+  // (read where they are first used, they would add a round trip before the
+  // first copies)
+  asm volatile("" ::"s"(p.x0), "s"(p.x1), "s"(p.w));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * 16;

@@ -33,6 +33,13 @@ __device__ __forceinline__ uint8_t to_e4m3(float x) {
 // (17152 waves for 1024 fresh context rows).
 template <typename T, bool F8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void qkv_epilogue_kernel(QkvEpiArgs a) {
+  // the scalar arguments in one batch of reads (left to itself the compiler
+  // reads them behind the branches that use them, a round trip each, before
+  // the first partial load)
+  asm volatile("" ::"s"(a.part_q), "s"(a.part_kv), "s"(a.part_kvh), "s"(a.q_row), "s"(a.q_split), "s"(a.kv_row),
+               "s"(a.kv_split), "s"(a.kvh_row), "s"(a.kvh_split));
+  asm volatile("" ::"s"(a.sq), "s"(a.skv), "s"(a.skvh), "s"(a.R), "s"(a.B), "s"(a.T), "s"(a.n_h), "s"(a.n_kv),
+               "s"(a.d_h), "s"(a.n_sync), "s"(a.attn_sync), "s"(a.d_rows));
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int RB = a.R * a.B;
@@ -70,9 +77,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void q
   const bool act = lane < half;
   float x0 = 0.f, x1 = 0.f;
   if (act) {
+    // every split's loads of a group of 8 go out before the first is added
+    // (one memory latency per 8 splits), then the sums in split order
     const float* src = part + (int64_t)pm * row_stride + col + lane;
-#pragma unroll 4
-    for (int s = 0; s < splits; ++s) { x0 += src[s * stride]; x1 += src[s * stride + half]; }
+    for (int s0 = 0; s0 < splits; s0 += 8) {
+      float v0[8], v1[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int sj = min(s0 + j, splits - 1);
+        v0[j] = src[sj * stride];
+        v1[j] = src[sj * stride + half];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (s0 + j < splits) { x0 += v0[j]; x1 += v1[j]; }
+    }
   }
 
   // sequence and position of this row (device-driven rounds: lengths and new
