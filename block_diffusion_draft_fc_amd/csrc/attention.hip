@@ -26,7 +26,7 @@
 // Every kernel keeps the running max, sum and output per lane in the log2
 // domain and writes one partial (m, l, unnormalised O) per query row and item;
 // attn_combine_kernel merges the partials of a row.
-#include "kernels.hpp"
+#include "attn_merge.hpp"
 
 namespace dflash {
 
@@ -685,146 +685,8 @@ __global__ __launch_bounds__(256, 1) void attn_lds_kernel(AttnArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- merge of a row's partials
-// One query row's chunk partials merged: m = max_c m_c,
-// l = sum_c 2^(m_c - m) l_c, O = sum_c 2^(m_c - m) O_c / l, stored in the
-// row-major [R*B][n_h*d_h] order of the attention output (head h at columns
-// h*d_h .., "DFlash KV Injection Walkthrough" Step 4.5).  One wave per row,
-// lane l owning head dims 2l, 2l+1 (d_h <= 128); the partials are in the
-// layer's storage type.  Chunks go in groups of 32: every O load of the group
-// and the group's (m, l) loads (lane c % 32 loads chunk c's) are issued before
-// any is used, so a row costs one memory latency per 32 chunks; the group
-// maximum and weights come from wave reductions and readlane.  A group maximum
-// above the running one rescales the accumulators.
-
-__device__ __forceinline__ float2 load2f(const float* p) { return *reinterpret_cast<const float2*>(p); }
-__device__ __forceinline__ float2 load2f(const bf16* p) {
-  const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
-  return float2{__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)};
-}
-
-// Row qrow of the n items it0 .. it0 + n - 1 (one (sequence, K/V head)):
-// returns this lane's two normalised output values.
-template <typename T>
-__device__ __forceinline__ float2 merge_partials_row(const T* part_o, const float* part_ml, int64_t it0, int n,
-                                                     int qrows, int qrow, int d_h, int lane) {
-  constexpr int G = 32;
-  const float* ml = part_ml + it0 * 2 * qrows + qrow;   // m_c at ml[c * mstride], l_c at + qrows
-  const int mstride = 2 * qrows;
-  const bool act = 2 * lane < d_h;
-  const T* po = part_o + (it0 * qrows + qrow) * d_h + 2 * (act ? lane : 0);
-  const int ostride = qrows * d_h;
-  float mrun = -INFINITY, lrun = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int cb = 0; cb < n; cb += G) {
-    float2 oc[G];
-    // chunks past n load chunk n - 1 again (their weight is 0): the loads
-    // stay unconditional, so all of them go out before the first is used;
-    // 32-bit offsets within a group of 32 chunks (qrows * d_h <= 64 * 128)
-    const T* pb = po + (int64_t)cb * ostride;
-    const int last = n - 1 - cb;
-#pragma unroll
-    for (int k = 0; k < G; ++k) oc[k] = load2f(pb + min(k, last) * ostride);
-    // issue the O loads before the (m, l) loads and their reductions
-    asm volatile("" ::: "memory");
-    const int c = cb + (lane & (G - 1));
-    const float mc = c < n ? ml[(int64_t)c * mstride] : -INFINITY;
-    const float lc = c < n ? ml[(int64_t)c * mstride + qrows] : 0.f;
-    const float mg = fmaxf(wave_max(mc), mrun);
-    const float mu = mg == -INFINITY ? 0.f : mg;
-    const float wc = __builtin_amdgcn_exp2f(mc - mu);     // weight of chunk cb + lane % 32 (0 for -inf)
-    const float sa = __builtin_amdgcn_exp2f(mrun - mu);   // rescale of the groups before
-    // lanes 32..63 repeat lanes 0..31: half the wave sum is the group's
-    lrun = lrun * sa + 0.5f * wave_sum(wc * lc);
-    o0 *= sa;
-    o1 *= sa;
-    mrun = mg;
-#pragma unroll
-    for (int k = 0; k < G; ++k) {
-      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wc), k));
-      o0 += w * oc[k].x;
-      o1 += w * oc[k].y;
-    }
-  }
-  const float inv = lrun > 0.f ? 1.0f / lrun : 0.f;
-  return float2{o0 * inv, o1 * inv};
-}
-
-template <typename T>
-__device__ __forceinline__ void store_merged_row(T* attn, float2 o, int r, int g, int qrow, int B, int group,
-                                                 int n_kv, int d_h, int lane) {
-  if (2 * lane >= d_h) return;
-  const int hl = qrow / B, b = qrow - hl * B;
-  const int h = g * group + hl;
-  T* dst = attn + ((int64_t)r * B + b) * (n_kv * group * d_h) + h * d_h + 2 * lane;
-  dst[0] = from_f32<T>(o.x);
-  dst[1] = from_f32<T>(o.y);
-}
-
-// ---------------------------------------------------------------- in-launch merge: a head's arrivals
-// The items of one K/V head meet at a word of device memory (one atomic add
-// per item, polled by loads that reach past the CU's L1, which observe the
-// atomics), then merge the head's rows from each other's partials.  Items of
-// a head whose workgroup indices agree mod 8 sit on one XCD, so their
-// partials are in that XCD's L2 and no cache write-back is needed; the
-// arrival word counts arrivals per XCD, and if a head's items came from
-// several XCDs every item writes its L2 back and invalidates its caches
-// before the merge (slow, but exact).  Waits are bounded: a workgroup whose
-// wait runs out counts itself in g_attn_sync_timeouts and writes its rows as
-// NaN rather than hang.
-
+// Workgroups of this file's kernels whose in-launch merge wait timed out.
 __device__ uint32_t g_attn_sync_timeouts = 0;
-constexpr int kAttnSpinLimit = 1 << 18;   // polls (each a memory round trip): ~0.3 s
-
-__device__ __forceinline__ uint32_t xcc_id() {
-  uint32_t v;
-  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
-  return v & 0xf;
-}
-// loads that miss the CU's L1, waited for in the same asm block
-__device__ __forceinline__ uint64_t load_sync64(const uint64_t* p) {
-  uint64_t v;
-  asm volatile("global_load_dwordx2 %0, %1, off sc0 sc1\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(p) : "memory");
-  return v;
-}
-__device__ __forceinline__ uint32_t load_sync32(const uint32_t* p) {
-  uint32_t v;
-  asm volatile("global_load_dword %0, %1, off sc0 sc1\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(p) : "memory");
-  return v;
-}
-__device__ __forceinline__ int byte_sum(uint64_t v) {
-  int s = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s += (int)((v >> (8 * i)) & 0xff);
-  return s;
-}
-
-// One thread per workgroup, after the workgroup's partial stores have
-// completed: arrive at head word w (kAttnSyncWords u32: the u64 arrival word,
-// the fallback count) and wait for the head's n items.  Returns 0 when all n
-// came from this XCD, 1 when they came from several (every item's L2 is then
-// written back and this CU's caches invalidated), 2 when a wait timed out.
-__device__ __forceinline__ int attn_head_arrive(uint32_t* w, int n) {
-  const uint32_t x = xcc_id() & 7;
-  uint64_t* word = reinterpret_cast<uint64_t*>(w);
-  __hip_atomic_fetch_add(reinterpret_cast<unsigned long long*>(word), 1ull << (8 * x), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_SYSTEM);
-  uint64_t v = 0;
-  for (int i = 0;; ++i) {
-    v = load_sync64(word);
-    if (byte_sum(v) >= n) break;
-    if (i > kAttnSpinLimit) return 2;
-    __builtin_amdgcn_s_sleep(1);
-  }
-  if ((int)((v >> (8 * x)) & 0xff) == n) return 0;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __hip_atomic_fetch_add(w + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  for (int i = 0; (int)load_sync32(w + 2) < n; ++i) {
-    if (i > kAttnSpinLimit) return 2;
-    __builtin_amdgcn_s_sleep(1);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return 1;
-}
 
 hipError_t attn_sync_timeouts(uint32_t* count) {
   return hipMemcpyFromSymbol(count, HIP_SYMBOL(g_attn_sync_timeouts), sizeof(uint32_t), 0, hipMemcpyDeviceToHost);

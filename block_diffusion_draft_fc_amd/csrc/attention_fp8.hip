@@ -33,7 +33,7 @@
 //    c ^ ((R / 4) % 4).  Each operand read (16 lanes, 16 bytes each) then
 //    covers all 256 bytes of the banks.
 
-#include "kernels.hpp"
+#include "attn_merge.hpp"
 
 namespace dflash {
 
@@ -72,7 +72,18 @@ __device__ __forceinline__ u32x4 keep_bytes(u32x4 w, int n) {
 // queries (the last stage holds one copy per tile) and group 1 reads them
 // after a barrier.  The two-stage one-group form runs four workgroups per CU
 // (32 KB of LDS each): at most 128 VGPRs, i.e. four waves per SIMD.
-template <int DH, int NST, int NG = 1>
+// Workgroups of this file's kernels whose in-launch merge wait timed out.
+__device__ uint32_t g_attn_fp8_sync_timeouts = 0;
+
+hipError_t attn_fp8_sync_timeouts(uint32_t* count) {
+  return hipMemcpyFromSymbol(count, HIP_SYMBOL(g_attn_fp8_sync_timeouts), sizeof(uint32_t), 0,
+                             hipMemcpyDeviceToHost);
+}
+
+// MERGE: as in the bf16 ring kernel (0: partials for the combine launch; 1:
+// the split merged in the launch, item x on K/V head x % n_kv; 2: the
+// diagnostic order with a head's items on consecutive workgroups).
+template <int DH, int NST, int NG = 1, int MERGE = 0>
 __global__ __launch_bounds__(256 * NG, (NG == 1 && NST == 2) ? 4 : 1) void attn_ring64_fp8_kernel(AttnArgs a) {
   using V8 = bf16x8;
   static_assert(DH == 64 || DH == 128, "layouts defined for d_h 64 and 128");
@@ -88,17 +99,36 @@ __global__ __launch_bounds__(256 * NG, (NG == 1 && NST == 2) ? 4 : 1) void attn_
   static_assert(PER_WAVE * 4 * NG == COPIES, "copies split evenly over the waves");
   constexpr int STAGE = COPIES * 1024;
   constexpr int QSPAN = DH / 4;        // head dims of a lane group in the QK contraction
+  static_assert(MERGE == 0 || NG == 2, "the in-launch merge runs on the one-workgroup-per-CU plans");
   __shared__ __align__(16) unsigned char ring[NST * STAGE];
   __shared__ int32_t s_page[kAttnMaxChunkPages];
 
   const int item = blockIdx.x;
-  int r = 0;
-  while (r + 1 < a.R && item >= a.item_base[r + 1]) ++r;
-  const int local = item - a.item_base[r];
-  const int g = local / a.chunks[r];
-  const int chunk = local - g * a.chunks[r];
+  int r = 0, g, chunk;
   int key_lo, key_hi, qpos0;
-  attn_seq_keys(a, r, key_lo, key_hi, qpos0);
+  if constexpr (MERGE != 0) {
+    // one sequence of a host-driven round, every argument of the start at a
+    // fixed offset and read in one batch (as in the bf16 ring kernel)
+    if constexpr (MERGE == 2) {
+      g = item / a.seq0[3];
+      chunk = item - g * a.seq0[3];
+    } else {
+      g = item % a.n_kv;
+      chunk = item / a.n_kv;
+    }
+    key_lo = a.seq0[0];
+    key_hi = a.seq0[1];
+    qpos0 = a.seq0[2];
+    asm volatile("" ::"s"(a.cache.n_kv), "s"(a.cache.d_h));
+  } else {
+    while (r + 1 < a.R && item >= a.item_base[r + 1]) ++r;
+    const int local = item - a.item_base[r];
+    g = local / a.chunks[r];
+    chunk = local - g * a.chunks[r];
+    attn_seq_keys(a, r, key_lo, key_hi, qpos0);
+  }
+  // the partial's slot: items of one (sequence, head) in chunk order
+  const int pitem = MERGE != 0 ? g * a.seq0[3] + chunk : a.item_base[r] + g * a.chunks[r] + chunk;
   const int kbeg = (key_lo & ~63) + chunk * a.chunk_keys;
   const int kend = min(kbeg + a.chunk_keys, key_hi);
   const int nblk = kend > kbeg ? (kend - kbeg + 63) >> 6 : 0;
@@ -164,7 +194,7 @@ __global__ __launch_bounds__(256 * NG, (NG == 1 && NST == 2) ? 4 : 1) void attn_
   const int kkey_in = lane / KCH, kslot = lane % KCH;
   const int vrow_in = lane >> 2, vslot = lane & 3;
 
-  const int rot0 = a.rot > 0 && nblk > 0 ? (int)(((unsigned)item * (unsigned)a.rot) % (unsigned)nblk) : 0;
+  const int rot0 = a.rot > 0 && nblk > 0 ? (int)(((unsigned)pitem * (unsigned)a.rot) % (unsigned)nblk) : 0;
   auto rot_blk = [&](int b) { const int x = b + rot0; return x >= nblk ? x - nblk : x; };
   auto issue = [&](int b) {
     const int blk = kbeg + 64 * rot_blk(b);
@@ -309,29 +339,52 @@ __global__ __launch_bounds__(256 * NG, (NG == 1 && NST == 2) ? 4 : 1) void attn_
       reinterpret_cast<float*>(xb + DT * 1024 + 256)[lane] = l_run;
     }
     __syncthreads();
-    if (grp == 1) return;
-    const float m1 = reinterpret_cast<const float*>(xb + DT * 1024)[lane];
-    const float l1 = reinterpret_cast<const float*>(xb + DT * 1024 + 256)[lane];
-    const float m = fmaxf(m_run, m1);
-    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
-    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+    if (grp == 0) {
+      const float m1 = reinterpret_cast<const float*>(xb + DT * 1024)[lane];
+      const float l1 = reinterpret_cast<const float*>(xb + DT * 1024 + 256)[lane];
+      const float m = fmaxf(m_run, m1);
+      const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+      const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
 #pragma unroll
-    for (int d = 0; d < DT; ++d)
-      o[d] = o[d] * a0 + *reinterpret_cast<const f32x4*>(xb + d * 1024 + 16 * lane) * a1;
-    l_run = l_run * a0 + l1 * a1;
-    m_run = m;
+      for (int d = 0; d < DT; ++d)
+        o[d] = o[d] * a0 + *reinterpret_cast<const f32x4*>(xb + d * 1024 + 16 * lane) * a1;
+      l_run = l_run * a0 + l1 * a1;
+      m_run = m;
+    }
   }
 
-  if (!wave_rows) return;
-  bf16* po = static_cast<bf16*>(a.part_o) + (int64_t)item * a.qrows * DH;
+  if (wave_rows && grp == 0) {
+    bf16* po = static_cast<bf16*>(a.part_o) + (int64_t)pitem * a.qrows * DH;
 #pragma unroll
-  for (int d = 0; d < DT; ++d) store4(po + (int64_t)row * DH + 16 * d + 4 * q4, o[d] * a.v_scale);
-  float l = l_run;
-  l = sum_xor32(sum_xor16(l));
-  if (q4 == 0) {
-    float* pml = a.part_ml + (int64_t)item * 2 * a.qrows;
-    pml[row] = m_run;
-    pml[a.qrows + row] = l;
+    for (int d = 0; d < DT; ++d) store4(po + (int64_t)row * DH + 16 * d + 4 * q4, o[d] * a.v_scale);
+    float l = l_run;
+    l = sum_xor32(sum_xor16(l));
+    if (q4 == 0) {
+      float* pml = a.part_ml + (int64_t)pitem * 2 * a.qrows;
+      pml[row] = m_run;
+      pml[a.qrows + row] = l;
+    }
+  }
+
+  if constexpr (MERGE != 0) {
+    // every partial store of the workgroup has reached L2, then one thread
+    // arrives for the workgroup and waits for the head's other items; then
+    // rows chunk, chunk + nch, ... of the head, one per wave
+    __shared__ int s_status;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int nch = a.seq0[3];
+    if (tid == 0) s_status = attn_head_arrive(a.sync + kAttnSyncStride * g, nch);
+    __syncthreads();
+    const int status = s_status;
+    if (status == 2 && tid == 0) atomicAdd(&g_attn_fp8_sync_timeouts, 1u);
+    const int valid = a.group * a.B;
+    for (int qr = chunk + wave * nch; qr < valid; qr += 4 * NG * nch) {
+      float2 ov = merge_partials_row(static_cast<const bf16*>(a.part_o), a.part_ml, (int64_t)g * nch, nch, a.qrows,
+                                     qr, DH, lane);
+      if (status == 2) ov = float2{__builtin_nanf(""), __builtin_nanf("")};
+      store_merged_row(static_cast<bf16*>(a.attn), ov, 0, g, qr, a.B, a.group, a.n_kv, DH, lane);
+    }
   }
 }
 
@@ -350,7 +403,11 @@ hipError_t launch_attn_fp8(const AttnArgs& a, int items, hipStream_t s) {
   if (items == 0) return hipSuccess;
   if ((a.qrows + 15) / 16 > 4) return hipErrorInvalidValue;
   if (a.nst >= 3) {
-    if (a.d_h == 128) launch((attn_ring64_fp8_kernel<128, 6, 2>), dim3(items), dim3(512), 0, s, a);
+    if (a.d_h == 128 && a.sync != nullptr && a.merge_spread)
+      launch((attn_ring64_fp8_kernel<128, 6, 2, 2>), dim3(items), dim3(512), 0, s, a);
+    else if (a.d_h == 128 && a.sync != nullptr)
+      launch((attn_ring64_fp8_kernel<128, 6, 2, 1>), dim3(items), dim3(512), 0, s, a);
+    else if (a.d_h == 128) launch((attn_ring64_fp8_kernel<128, 6, 2>), dim3(items), dim3(512), 0, s, a);
     else launch((attn_ring64_fp8_kernel<64, 4>), dim3(items), dim3(256), 0, s, a);
   } else {
     if (a.d_h == 128) launch((attn_ring64_fp8_kernel<128, 2>), dim3(items), dim3(256), 0, s, a);

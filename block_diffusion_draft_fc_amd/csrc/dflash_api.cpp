@@ -1012,13 +1012,13 @@ int kv_inject_impl(const dflash_layer_desc* L, dflash_cache* c, const void* C, c
     if (items > p.max_items) return DFLASH_ERR_SHAPE;
   }
   // The split merges in the attention launch itself (no combine launch) for
-  // one sequence of bf16 rows over a bf16 cache with 49..64 query rows per
-  // K/V head at d_h 128, on the one-workgroup-per-CU plans: the items of a
+  // one sequence of bf16 rows over a bf16 or fp8 cache with 49..64 query rows
+  // per K/V head at d_h 128, on the one-workgroup-per-CU plans: the items of a
   // head wait for each other, so every item must be resident at once (at
   // most one per compute unit), and a head's items must share an XCD (n_kv
   // a multiple of the 8 XCDs; item x takes head x % n_kv).  Device-driven
   // rounds keep the combine launch, which also advances the device lengths.
-  const bool merge_in_attn = dt == DFLASH_BF16 && !fp8 && L->d_h == 128 && cdiv(p.qrows, 16) == 4 &&
+  const bool merge_in_attn = dt == DFLASH_BF16 && L->d_h == 128 && cdiv(p.qrows, 16) == 4 &&
                              aa.nst >= 3 && R == 1 && L->n_kv % 8 == 0 && L->n_kv <= 64 && dev_rows == nullptr && items > 0 &&
                              items <= device_cus() && aa.chunks[0] <= 255;
   if (exact_ws) {
@@ -1461,7 +1461,12 @@ int dflash_mfma_peak(int32_t iters, int64_t workgroups, float* sink, void* strea
 
 int dflash_attn_sync_timeouts(uint32_t* count) {
   if (!count) return DFLASH_ERR_ARG;
-  return hip_status(attn_sync_timeouts(count));
+  uint32_t bf = 0, f8 = 0;
+  hipError_t e = attn_sync_timeouts(&bf);
+  if (e == hipSuccess) e = attn_fp8_sync_timeouts(&f8);
+  if (e != hipSuccess) return DFLASH_ERR_HIP;
+  *count = bf + f8;
+  return DFLASH_OK;
 }
 
 int dflash_attn_force_merge_spread(int32_t on) {

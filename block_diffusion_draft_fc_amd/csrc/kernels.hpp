@@ -222,6 +222,7 @@ constexpr int kAttnSyncWords = 4;     // words of a head that the epilogue zeroe
 // Workgroups whose wait for the other items of their head timed out since the
 // library was loaded (their rows are written as NaN); 0 in every correct run.
 hipError_t attn_sync_timeouts(uint32_t* count);
+hipError_t attn_fp8_sync_timeouts(uint32_t* count);   // the fp8-cache kernels' count
 
 // Key range and block position of sequence r for one launch.
 __device__ __forceinline__ void attn_seq_keys(const AttnArgs& a, int r, int& lo, int& hi, int& q0) {

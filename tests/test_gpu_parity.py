@@ -246,26 +246,29 @@ def test_split_invariance_decode_8k():
             say(f"  chunk {chunk} round {rnd}: {e:.2e} from the planner's split")
 
 
-def test_in_launch_merge_across_xcds_decode_8k():
-    """The in-launch merge with each K/V head's items on consecutive
-    workgroups (so a head's 26 items run on several XCDs): every item writes
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_in_launch_merge_across_xcds_decode_8k(kv):
+    """The in-launch merge (bf16 and fp8 caches) with each K/V head's items
+    on consecutive workgroups (so a head's 26 items run on several XCDs): every item writes
     its L2 back and meets the others at a second count before merging.  The
     first 2 rounds of the decode workload against the oracle and against the
     ordinary order, no combine launch, no wait timed out."""
     wl = configs.DECODE_8K
+    if kv == "fp8":
+        wl = wl.scaled(name="decode_ctx8k_fp8_cache", kv_dtype="fp8", k_scale=1.0, v_scale=1.0)
     rounds = 2
-    kv = prefill_host(wl)
+    kvh = prefill_host(wl)
     sched = G.schedule(wl)
-    orc = oracle_stack(wl, kv)
+    orc = oracle_stack(wl, kvh)
     inputs = [G.round_inputs(wl, rnd, sched[rnd]) for rnd in range(rounds)]
     refs = [orc.round(x, cu, H, wl.B)[0][0] for x, cu, H in inputs]
     outs = {}
     try:
         for spread in (False, True):
             L.dflash_attn_force_merge_spread(spread)
-            say(f"case in-launch merge spread={spread}")
+            say(f"case in-launch merge {kv} cache spread={spread}")
             gm = GpuModel(wl, rounds)
-            gm.prefill(kv)
+            gm.prefill(kvh)
             L.timing_enable(True)
             L.timing_reset()
             outs[spread] = [gm.round(x, cu, H)[0] for x, cu, H in inputs]
@@ -406,13 +409,20 @@ def test_small_case(wl):
     run_rounds(wl, wl.rounds)
 
 
-# One sequence with n_kv a multiple of 8 (bf16, d_h 128, 49..64 query rows
-# per K/V head, at most one attention item per compute unit): the attention
-# launch merges its own split, and no combine launch follows.  The cases span
-# one to tens of chunks per head (rows per merging item from 64 down to 2),
-# padded query rows (B = 13: 52 of 64), two query heads per K/V head, 16 K/V
-# heads, a sliding window, paged and ring caches and a residual stack; the
-# two-request batch keeps the combine launch.
+def _fp8(name, **kw):
+    base = dict(kv_dtype="fp8", k_scale=1.5, v_scale=0.5)
+    base.update(kw)
+    return _small("fp8_" + name, **base)
+
+
+# One sequence with n_kv a multiple of 8 (bf16 layers over bf16 or fp8
+# caches, d_h 128, 49..64 query rows per K/V head, at most one attention item
+# per compute unit): the attention launch merges its own split, and no
+# combine launch follows.  The cases span one to tens of chunks per head (rows
+# per merging item from 64 down to 2), padded query rows (B = 13: 52 of 64),
+# two query heads per K/V head, 16 K/V heads, a sliding window, paged and ring
+# caches and a residual stack; the two-request batches keep the combine
+# launch.
 MERGE = [
     (_small("merge_g4_b16_n8", d=512, n_h=32, n_kv=8, d_h=128, B=16, prefill_len=300, n_range=(1, 16)), True),
     (_small("merge_g4_b13_padded_rows", d=512, n_h=32, n_kv=8, d_h=128, B=13, prefill_len=700, rounds=2), True),
@@ -429,6 +439,15 @@ MERGE = [
             window=256, sliding_layers=(0, 2)), True),
     (_small("combine_r2_n8", R=2, d=512, n_h=32, n_kv=8, d_h=128, B=16, prefill="uniform",
             prefill_range=(100, 900), rounds=2), False),
+    # the same over fp8 caches (the fp8 kernel merges its split the same way)
+    (_fp8("merge_g4_b16_n8", d=512, n_h=32, n_kv=8, d_h=128, B=16, prefill_len=300, n_range=(1, 16)), True),
+    (_fp8("merge_g4_b13_padded_rows", d=512, n_h=32, n_kv=8, d_h=128, B=13, prefill_len=700, rounds=2), True),
+    (_fp8("merge_one_chunk_per_head", d=512, n_h=32, n_kv=8, d_h=128, B=16, prefill_len=40, rounds=2), True),
+    (_fp8("merge_long_cache", d=512, n_h=32, n_kv=8, d_h=128, B=16, prefill_len=5000, rounds=2), True),
+    (_fp8("merge_window_100_paged", d=512, n_h=32, n_kv=8, d_h=128, B=16, prefill_len=500, window=100,
+          sliding_layers=(0,), page_size=64), True),
+    (_fp8("combine_r2_n8", R=2, d=512, n_h=32, n_kv=8, d_h=128, B=16, prefill="uniform",
+          prefill_range=(100, 900), rounds=2), False),
 ]
 
 
@@ -451,12 +470,6 @@ def test_in_launch_merge(wl, merged):
 
 
 # ------------------------------------------------------------------ fp8 (E4M3) caches
-
-def _fp8(name, **kw):
-    base = dict(kv_dtype="fp8", k_scale=1.5, v_scale=0.5)
-    base.update(kw)
-    return _small("fp8_" + name, **base)
-
 
 # every query-tile count and head dim of the fp8 kernel, ragged tails, empty
 # caches, windows, paged and ring caches, stacks, and scales that are and are
