@@ -643,7 +643,7 @@ PROFILE_CMDS = {
 }
 # The 8K decode's attention launches (G3 with the split merge G4 in the same
 # launch: one sequence, 8 K/V heads, one item per compute unit).
-ATTN_KERNELS = ("attn_ring64_kernel<128, 4, 2, true>",)
+ATTN_KERNELS = ("attn_ring64_kernel<128, 4, 2, 1>",)
 
 
 def attn_kernel_name(nst, d_h, merged=False):
@@ -651,7 +651,7 @@ def attn_kernel_name(nst, d_h, merged=False):
     depth and head dim (bf16 layers), as rocprofv3 names it."""
     if d_h == 128:
         if nst >= 3:
-            return "attn_ring64_kernel<128, 4, 2, true>" if merged else "attn_ring64_kernel<128, 4, 2>"
+            return "attn_ring64_kernel<128, 4, 2, 1>" if merged else "attn_ring64_kernel<128, 4, 2>"
         return "attn_ring64_kernel<128, 2>"
     return "attn_ring64_kernel<64, 4>"
 
