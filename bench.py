@@ -36,6 +36,23 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 METRIC = "draft blocks/sec + attn HBM GB/s (% peak), ctx 8K, block 16, GQA 32/8"
 
 
+def head_start(calls: int, us_per_call: float = 100.0) -> None:
+    """Enqueue register-only MFMA work (no memory traffic) before an
+    event-timed eager loop of `calls` library calls: while it runs, the host
+    enqueues the loop ahead of the GPU.  A kernel-attached event pair stamps
+    its start when the stream reaches the launch, so a host that falls behind
+    the GPU adds its submission gap to the kernel's time; with the head start
+    the loop's kernels run back to back and the events bracket the kernels
+    alone (the rocprofv3 kernel trace measures the same launches the same).
+    About us_per_call of head start per call, at most 40 ms; ~13000
+    iterations of the 256-workgroup MFMA loop take a millisecond."""
+    from block_diffusion_draft_fc_amd import _lib as L
+
+    ms = min(40.0, calls * us_per_call * 1e-3)
+    if ms > 0:
+        L.dflash_mfma_peak(max(1, int(ms * 13000)), 256)
+
+
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
@@ -243,6 +260,7 @@ def fresh_ctx_projections(iters):
         call()
     torch.cuda.synchronize()
     L.timing_reset()
+    head_start(iters, 300.0)
     L.timing_enable(True)
     for _ in range(iters):
         call()
@@ -375,6 +393,7 @@ def batched_rounds(wl, rounds, ring=False):
     torch.cuda.synchronize()
     ms = max(ev0.elapsed_time(ev1), (time.perf_counter() - t0) * 1e3) / rounds
     L.timing_reset()
+    head_start(rounds, 2000.0)
     L.timing_enable(True)
     cycle()
     torch.cuda.synchronize()
@@ -446,6 +465,7 @@ def attn_pass(iters, R=4, ctx=32768, kv="bf16"):
         call()
     torch.cuda.synchronize()
     L.timing_reset()
+    head_start(iters)
     L.timing_enable(True)
     for _ in range(iters):
         call()
@@ -491,6 +511,7 @@ def accept_pass(iters):
         L.dflash_accept(d_draft, d_post, acc, rows, anchor)
     torch.cuda.synchronize()
     L.timing_reset()
+    head_start(iters, 30.0)
     L.timing_enable(True)
     for _ in range(iters):
         L.dflash_accept(d_draft, d_post, acc, rows, anchor)
@@ -532,6 +553,7 @@ def draft_head_pass(iters):
     torch.cuda.synchronize()
     us = ev0.elapsed_time(ev1) * 1e3 / iters
     L.timing_reset()
+    head_start(iters, 50.0)
     L.timing_enable(True)
     for _ in range(iters):
         L.dflash_draft_head(h, B, gam, wl.eps, w, ids, ws)
@@ -694,8 +716,9 @@ def summarize_profiles(root):
              "```", "",
              "`bench.py` with only the headline workload: warmup, the timed steps as one graph and eagerly, "
              "then the per-stage passes (one cache, then 16 cache replicas and 2 weight sets in rotation) and "
-             "the measured-peak copies and matrix product.  Durations are rocprofv3 kernel-trace begin/end "
-             "timestamps over all calls of the command.", "",
+             "the measured-peak copies and matrix product.  `mfma_peak_kernel` is mostly the register-only head "
+             "start enqueued before each event-timed pass (so the host runs ahead of the GPU).  Durations are "
+             "rocprofv3 kernel-trace begin/end timestamps over all calls of the command.", "",
              "| Kernel | Calls | Average µs | Min µs | Max µs | % of GPU time |", "|---|---|---|---|---|---|"]
     for r in stats[:12]:
         lines.append(f"| `{_short(r['Name'])[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
@@ -981,6 +1004,7 @@ def main():
     #  its K/V from HBM.
     def stage_pass(pick):
         L.timing_reset()
+        head_start(args.steps)
         L.timing_enable(True)
         for i in range(args.steps):
             step(first + i, *pick(i))
