@@ -1022,13 +1022,16 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_kernel(AttnArgs a) {
   }
 
   if constexpr (MERGE != 0) {
-    // every partial store of the workgroup has reached L2, then one thread
+    // every partial store of the workgroup has reached L2, then wave 0
     // arrives for the workgroup and waits for the head's other items
     __shared__ int s_status;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const int nch = a.seq0[3];
-    if (tid == 0) s_status = attn_head_arrive(a.sync + kAttnSyncStride * g, nch);
+    if (tid < 64) {
+      const int st = attn_head_arrive(a.sync + kAttnSyncStride * g, nch, chunk, lane);
+      if (tid == 0) s_status = st;
+    }
     __syncthreads();
     const int status = s_status;
     if (status == 2 && tid == 0) atomicAdd(&g_attn_sync_timeouts, 1u);

@@ -82,17 +82,24 @@ __device__ __forceinline__ void store_merged_row(T* attn, float2 o, int r, int g
 }
 
 // ---------------------------------------------------------------- in-launch merge: a head's arrivals
-// The items of one K/V head meet at a word of device memory (one
-// system-scope atomic add per item, polled by loads that reach past every
-// cache: a load that stops at L2 can be served a stale copy of the word),
-// then merge the head's rows from each other's partials.  Items of a head
-// whose workgroup indices agree mod 8 sit on one XCD, so their partials are
-// in that XCD's L2 and no cache write-back is needed; the arrival word counts
-// arrivals per XCD, and if a head's items came from several XCDs every item
-// writes its L2 back and invalidates its caches before the merge (slow, but
-// exact).  Waits are bounded: a workgroup whose wait runs out counts itself
-// in its kernel file's timeout counter (read by dflash_attn_sync_timeouts)
-// and writes its rows as NaN rather than hang.
+// The items of one K/V head meet before merging the head's rows from each
+// other's partials.  Items of a head whose workgroup indices agree mod 8 sit
+// on one XCD, so their partials are in that XCD's L2 and no cache write-back
+// is needed.  Each item, once its partial stores are complete, stores a flag
+// (1 + its XCD) in its slot of the head's flag line with a plain store, which
+// lands in its XCD's L2, and adds 1 << (8 * XCD) to the head's arrival word
+// with a system-scope atomic.  The waiting wave polls the flag line with loads
+// that miss its CU's L1 and are served by the L2 (one round trip of the L2,
+// ~0.4 us from the last arrival to the release): when all n flags carry its
+// own XCD, every item ran beside it.  A flag stored on another XCD stays in
+// that XCD's L2 and never shows as this XCD's, so a head whose items came
+// from several XCDs never completes its flags; every 8th poll therefore also
+// reads the arrival word past every cache, and once its bytes count all n
+// items without this XCD's byte doing so, every item writes its L2 back,
+// meets the others at a second count and invalidates its caches before the
+// merge (slow, but exact).  Waits are bounded: a workgroup whose wait runs out
+// counts itself in its kernel file's timeout counter (read by
+// dflash_attn_sync_timeouts) and writes its rows as NaN rather than hang.
 
 constexpr int kAttnSpinLimit = 1 << 18;   // polls (each a memory round trip): ~0.3 s
 
@@ -101,7 +108,7 @@ __device__ __forceinline__ uint32_t xcc_id() {
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
   return v & 0xf;
 }
-// loads that miss the CU's L1, waited for in the same asm block
+// loads that miss the CU's L1 and every cache past it, waited for in the same asm block
 __device__ __forceinline__ uint64_t load_sync64(const uint64_t* p) {
   uint64_t v;
   asm volatile("global_load_dwordx2 %0, %1, off sc0 sc1\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(p) : "memory");
@@ -112,6 +119,12 @@ __device__ __forceinline__ uint32_t load_sync32(const uint32_t* p) {
   asm volatile("global_load_dword %0, %1, off sc0 sc1\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(p) : "memory");
   return v;
 }
+// a load that misses the CU's L1 and is served by the XCD's L2 (device scope)
+__device__ __forceinline__ uint32_t load_l2_32(const uint32_t* p) {
+  uint32_t v;
+  asm volatile("global_load_dword %0, %1, off sc1\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
 __device__ __forceinline__ int byte_sum(uint64_t v) {
   int s = 0;
 #pragma unroll
@@ -119,26 +132,34 @@ __device__ __forceinline__ int byte_sum(uint64_t v) {
   return s;
 }
 
-// One thread per workgroup, after the workgroup's partial stores have
-// completed: arrive at head word w (kAttnSyncWords u32: the u64 arrival word,
-// the fallback count) and wait for the head's n items.  Returns 0 when all n
-// came from this XCD, 1 when they came from several (every item's L2 is then
-// written back and this CU's caches invalidated), 2 when a wait timed out.
-__device__ __forceinline__ int attn_head_arrive(uint32_t* w, int n) {
+// One wave per workgroup (all 64 lanes), after the workgroup's partial stores
+// have completed: item `slot` of its head arrives at head words w (the u64
+// arrival word, the fallback count, and the flags at w + kAttnSyncFlags) and
+// waits for the head's n items (n <= kAttnMergeMaxItems).  Returns, in every
+// lane, 0 when all n came from this XCD, 1 when they came from several (every
+// item's L2 is then written back and this CU's caches invalidated), 2 when a
+// wait timed out.
+__device__ __forceinline__ int attn_head_arrive(uint32_t* w, int n, int slot, int lane) {
   const uint32_t x = xcc_id() & 7;
+  uint32_t* flags = w + kAttnSyncFlags;
   uint64_t* word = reinterpret_cast<uint64_t*>(w);
-  __hip_atomic_fetch_add(reinterpret_cast<unsigned long long*>(word), 1ull << (8 * x), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_SYSTEM);
-  uint64_t v = 0;
+  if (lane == 0) {
+    flags[slot] = 1u + x;
+    __hip_atomic_fetch_add(reinterpret_cast<unsigned long long*>(word), 1ull << (8 * x), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
+  }
   for (int i = 0;; ++i) {
-    v = load_sync64(word);
-    if (byte_sum(v) >= n) break;
+    const uint32_t f = load_l2_32(flags + (lane < n ? lane : 0));
+    if (__all(lane >= n || f == 1u + x)) return 0;
+    if ((i & 7) == 7) {
+      const uint64_t v = load_sync64(word);
+      if (byte_sum(v) >= n && (int)((v >> (8 * x)) & 0xff) != n) break;
+    }
     if (i > kAttnSpinLimit) return 2;
     __builtin_amdgcn_s_sleep(1);
   }
-  if ((int)((v >> (8 * x)) & 0xff) == n) return 0;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __hip_atomic_fetch_add(w + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (lane == 0) __hip_atomic_fetch_add(w + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   for (int i = 0; (int)load_sync32(w + 2) < n; ++i) {
     if (i > kAttnSpinLimit) return 2;
     __builtin_amdgcn_s_sleep(1);

@@ -1016,11 +1016,12 @@ int kv_inject_impl(const dflash_layer_desc* L, dflash_cache* c, const void* C, c
   // per K/V head at d_h 128, on the one-workgroup-per-CU plans: the items of a
   // head wait for each other, so every item must be resident at once (at
   // most one per compute unit), and a head's items must share an XCD (n_kv
-  // a multiple of the 8 XCDs; item x takes head x % n_kv).  Device-driven
+  // a multiple of the 8 XCDs; item x takes head x % n_kv), at most
+  // kAttnMergeMaxItems of them (one arrival flag each).  Device-driven
   // rounds keep the combine launch, which also advances the device lengths.
   const bool merge_in_attn = dt == DFLASH_BF16 && L->d_h == 128 && cdiv(p.qrows, 16) == 4 &&
                              aa.nst >= 3 && R == 1 && L->n_kv % 8 == 0 && L->n_kv <= 64 && dev_rows == nullptr && items > 0 &&
-                             items <= device_cus() && aa.chunks[0] <= 255;
+                             items <= device_cus() && aa.chunks[0] <= kAttnMergeMaxItems;
   if (exact_ws) {
     p = plan_kv(L, c, T, B, items);
     if (ws_bytes < p.total) return DFLASH_ERR_WORKSPACE;

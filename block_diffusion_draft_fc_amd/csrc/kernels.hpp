@@ -208,7 +208,8 @@ struct AttnArgs {
   // turn); once all of a head's items have stored their partials they merge
   // its rows and write the normalised output to `attn` ([B][n_h*d_h]).
   // sync[kAttnSyncStride * g ..]: head g's arrival word (u64: a byte per XCD,
-  // each arrival adding one to its XCD's byte) and the fallback count (u32),
+  // each arrival adding one to its XCD's byte), the fallback count (u32) and,
+  // in the next 128-byte line, one arrival flag per item of the head, all
   // zeroed by the q/k/v epilogue before every launch.
   uint32_t* sync;
   void* attn;
@@ -218,7 +219,9 @@ struct AttnArgs {
   int32_t merge_spread;
 };
 constexpr int kAttnSyncStride = 64;   // u32 words between heads' arrival words (256 bytes)
-constexpr int kAttnSyncWords = 4;     // words of a head that the epilogue zeroes
+constexpr int kAttnSyncWords = 4;     // a head's words 0..3: arrival word, fallback count
+constexpr int kAttnSyncFlags = 32;    // a head's words 32..63: the items' arrival flags
+constexpr int kAttnMergeMaxItems = kAttnSyncStride - kAttnSyncFlags;   // items of a head merged in the launch
 // Workgroups whose wait for the other items of their head timed out since the
 // library was loaded (their rows are written as NaN); 0 in every correct run.
 hipError_t attn_sync_timeouts(uint32_t* count);

@@ -48,10 +48,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void q
   const int kvd = a.n_kv * a.d_h;
   const int64_t n_q_items = (int64_t)RB * a.n_h;
   const int64_t n_kv_items = (int64_t)Mkv * a.n_kv;
-  // the next attention launch's arrival words (a plain store: the kernel
-  // boundary makes it visible to that launch)
-  if (a.attn_sync != nullptr && blockIdx.x == 0 && (int)threadIdx.x < a.n_sync * kAttnSyncWords)
-    a.attn_sync[kAttnSyncStride * (threadIdx.x / kAttnSyncWords) + threadIdx.x % kAttnSyncWords] = 0u;
+  // the next attention launch's arrival words and flags (plain stores: the
+  // kernel boundary makes them visible to that launch)
+  if (a.attn_sync != nullptr && blockIdx.x == 0) {
+    constexpr int per_head = kAttnSyncWords + kAttnMergeMaxItems;
+    for (int t = threadIdx.x; t < a.n_sync * per_head; t += blockDim.x) {
+      const int h = t / per_head, wd = t - h * per_head;
+      a.attn_sync[kAttnSyncStride * h + (wd < kAttnSyncWords ? wd : kAttnSyncFlags + wd - kAttnSyncWords)] = 0u;
+    }
+  }
   if (item >= n_q_items + 2 * n_kv_items) return;
 
   int kind;   // 0 = Q, 1 = K, 2 = V
