@@ -468,7 +468,7 @@ int dflash_attn_force_chunk(int64_t chunk);
 /* ------------------------------------------------------------------------
  * In-launch merge watchdog.  When a layer call of one sequence (bf16, d_h 128,
  * 49..64 query rows per K/V head, n_kv a multiple of 8, at most one attention
- * work item per compute unit) merges its attention split inside the
+ * work item per compute unit and 32 per K/V head) merges its attention split inside the
  * attention launch, the items of a K/V head wait for each other there.  Each
  * wait is bounded: a workgroup that gives up writes its rows as NaN and is
  * counted here.  *count receives the number of such workgroups on the
