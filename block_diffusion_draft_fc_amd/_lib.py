@@ -79,6 +79,7 @@ def _load() -> C.CDLL:
         "dflash_attn_force_chunk": (C.c_int, [i64]),
         "dflash_attn_sync_timeouts": (C.c_int, [vp]),
         "dflash_attn_force_merge_spread": (C.c_int, [i32]),
+        "dflash_attn_set_spin_limit": (C.c_int, [i32]),
         "dflash_stream_read": (C.c_int, [vp, i64, vp, vp]),
         "dflash_mfma_peak": (C.c_int, [i32, i64, vp, vp]),
     }
@@ -372,6 +373,16 @@ def dflash_attn_force_merge_spread(on: bool) -> None:
     split merges in the attention launch (a diagnostic: the merge then takes
     its write-back path across XCDs)."""
     _check(LIB.dflash_attn_force_merge_spread(1 if on else 0), "dflash_attn_force_merge_spread")
+
+
+ATTN_SPIN_LIMIT = 1 << 18
+
+
+def dflash_attn_set_spin_limit(polls: int) -> None:
+    """Polls before an in-launch merge wait gives up (0: at once; the default
+    ATTN_SPIN_LIMIT restores ordinary calls); a diagnostic for tests of the
+    time-out path."""
+    _check(LIB.dflash_attn_set_spin_limit(int(polls)), "dflash_attn_set_spin_limit")
 
 
 def dflash_attn_sync_timeouts() -> int:

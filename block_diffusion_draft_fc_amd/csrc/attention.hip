@@ -1029,7 +1029,7 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_kernel(AttnArgs a) {
     __syncthreads();
     const int nch = a.seq0[3];
     if (tid < 64) {
-      const int st = attn_head_arrive(a.sync + kAttnSyncStride * g, nch, chunk, lane);
+      const int st = attn_head_arrive(a.sync + kAttnSyncStride * g, nch, chunk, lane, a.spin_limit);
       if (tid == 0) s_status = st;
     }
     __syncthreads();

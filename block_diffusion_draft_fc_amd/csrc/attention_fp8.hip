@@ -375,7 +375,7 @@ __global__ __launch_bounds__(256 * NG, (NG == 1 && NST == 2) ? 4 : 1) void attn_
     __syncthreads();
     const int nch = a.seq0[3];
     if (tid < 64) {
-      const int st = attn_head_arrive(a.sync + kAttnSyncStride * g, nch, chunk, lane);
+      const int st = attn_head_arrive(a.sync + kAttnSyncStride * g, nch, chunk, lane, a.spin_limit);
       if (tid == 0) s_status = st;
     }
     __syncthreads();

@@ -101,8 +101,6 @@ __device__ __forceinline__ void store_merged_row(T* attn, float2 o, int r, int g
 // counts itself in its kernel file's timeout counter (read by
 // dflash_attn_sync_timeouts) and writes its rows as NaN rather than hang.
 
-constexpr int kAttnSpinLimit = 1 << 18;   // polls (each a memory round trip): ~0.3 s
-
 __device__ __forceinline__ uint32_t xcc_id() {
   uint32_t v;
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
@@ -135,11 +133,12 @@ __device__ __forceinline__ int byte_sum(uint64_t v) {
 // One wave per workgroup (all 64 lanes), after the workgroup's partial stores
 // have completed: item `slot` of its head arrives at head words w (the u64
 // arrival word, the fallback count, and the flags at w + kAttnSyncFlags) and
-// waits for the head's n items (n <= kAttnMergeMaxItems).  Returns, in every
-// lane, 0 when all n came from this XCD, 1 when they came from several (every
-// item's L2 is then written back and this CU's caches invalidated), 2 when a
-// wait timed out.
-__device__ __forceinline__ int attn_head_arrive(uint32_t* w, int n, int slot, int lane) {
+// waits for the head's n items (n <= kAttnMergeMaxItems), giving up after
+// `polls` polls of a wait (0: without polling).  Returns, in every lane, 0
+// when all n came from this XCD, 1 when they came from several (every item's
+// L2 is then written back and this CU's caches invalidated), 2 when a wait
+// timed out.
+__device__ __forceinline__ int attn_head_arrive(uint32_t* w, int n, int slot, int lane, int polls) {
   const uint32_t x = xcc_id() & 7;
   uint32_t* flags = w + kAttnSyncFlags;
   uint64_t* word = reinterpret_cast<uint64_t*>(w);
@@ -149,19 +148,19 @@ __device__ __forceinline__ int attn_head_arrive(uint32_t* w, int n, int slot, in
                            __HIP_MEMORY_SCOPE_SYSTEM);
   }
   for (int i = 0;; ++i) {
+    if (i >= polls) return 2;
     const uint32_t f = load_l2_32(flags + (lane < n ? lane : 0));
     if (__all(lane >= n || f == 1u + x)) return 0;
     if ((i & 7) == 7) {
       const uint64_t v = load_sync64(word);
       if (byte_sum(v) >= n && (int)((v >> (8 * x)) & 0xff) != n) break;
     }
-    if (i > kAttnSpinLimit) return 2;
     __builtin_amdgcn_s_sleep(1);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   if (lane == 0) __hip_atomic_fetch_add(w + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   for (int i = 0; (int)load_sync32(w + 2) < n; ++i) {
-    if (i > kAttnSpinLimit) return 2;
+    if (i >= polls) return 2;
     __builtin_amdgcn_s_sleep(1);
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");

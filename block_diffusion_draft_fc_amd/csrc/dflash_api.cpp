@@ -150,6 +150,7 @@ struct AttnSplit {
 
 std::atomic<int64_t> g_forced_chunk{0};
 std::atomic<int> g_merge_spread{0};   // dflash_attn_force_merge_spread
+std::atomic<int> g_spin_limit{kAttnSpinLimit};   // dflash_attn_set_spin_limit
 
 AttnSplit plan_attn_split(const std::vector<int64_t>& keys, int n_kv, int64_t chunk_cap, bool fp8) {
   int64_t total = 0;
@@ -1040,6 +1041,7 @@ int kv_inject_impl(const dflash_layer_desc* L, dflash_cache* c, const void* C, c
     aa.sync = attn_sync;
     aa.attn = attn;
     aa.merge_spread = g_merge_spread.load();
+    aa.spin_limit = g_spin_limit.load();
   }
 
   // 1. page table entries for the rows this call appends
@@ -1473,6 +1475,12 @@ int dflash_attn_sync_timeouts(uint32_t* count) {
 int dflash_attn_force_merge_spread(int32_t on) {
   if (on != 0 && on != 1) return DFLASH_ERR_ARG;
   g_merge_spread.store(on);
+  return DFLASH_OK;
+}
+
+int dflash_attn_set_spin_limit(int32_t polls) {
+  if (polls < 0 || polls > kAttnSpinLimit) return DFLASH_ERR_ARG;
+  g_spin_limit.store(polls);
   return DFLASH_OK;
 }
 

@@ -217,7 +217,12 @@ struct AttnArgs {
   // x / chunks, which deals a head's items to several XCDs (the merge's
   // write-back path); 0 in every ordinary call
   int32_t merge_spread;
+  // polls before a wait of the in-launch merge gives up (kAttnSpinLimit in
+  // every ordinary call; dflash_attn_set_spin_limit lowers it for tests of the
+  // time-out path)
+  int32_t spin_limit;
 };
+constexpr int kAttnSpinLimit = 1 << 18;   // polls (each a memory round trip): ~0.3 s
 constexpr int kAttnSyncStride = 64;   // u32 words between heads' arrival words (256 bytes)
 constexpr int kAttnSyncWords = 4;     // a head's words 0..3: arrival word, fallback count
 constexpr int kAttnSyncFlags = 32;    // a head's words 32..63: the items' arrival flags

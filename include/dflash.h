@@ -493,6 +493,18 @@ int dflash_attn_sync_timeouts(uint32_t *count);
  * ---------------------------------------------------------------------- */
 int dflash_attn_force_merge_spread(int32_t on);
 
+/* ------------------------------------------------------------------------
+ * In-launch merge wait bound (a diagnostic for tests of the time-out path).
+ * Each wait of a work item for the other items of its K/V head gives up
+ * after `polls` polls of the device memory it waits on (0: at once, without
+ * polling); a work item that gives up writes its rows as NaN and is counted
+ * by dflash_attn_sync_timeouts.  The default, restored by passing 262144, is
+ * about 0.3 s per wait.  Applies to later layer calls; process-wide, not
+ * synchronised with calls in flight on other threads.  Returns
+ * DFLASH_ERR_ARG unless 0 <= polls <= 262144.
+ * ---------------------------------------------------------------------- */
+int dflash_attn_set_spin_limit(int32_t polls);
+
 #ifdef __cplusplus
 }
 #endif

@@ -468,6 +468,22 @@ def test_attn_force_chunk():
     assert _attn_plan([8216], 8) == (0, 320, 208, 3)
 
 
+def test_attn_merge_diagnostics_validation():
+    """The merge's item-order switch takes 0 or 1, its wait bound 0 .. 2^18
+    polls; both only set process-wide values (no device call)."""
+    spread = L.LIB.dflash_attn_force_merge_spread
+    for bad in (-1, 2, 7):
+        assert spread(bad) == L.ERR_ARG
+    assert spread(0) == 0
+    spin = L.LIB.dflash_attn_set_spin_limit
+    for bad in (-1, (1 << 18) + 1, 1 << 30):
+        assert spin(bad) == L.ERR_ARG
+    try:
+        assert spin(0) == 0 and spin(5) == 0
+    finally:
+        assert spin(L.ATTN_SPIN_LIMIT) == 0
+
+
 def test_attn_plan_validation():
     k = (C.c_int64 * 2)(100, 200)
     out = (C.c_int64 * 3)()

@@ -190,8 +190,9 @@ def test_decode_8k_all_64_rounds():
     """Every round of the decode workload at full size, as the benchmark runs
     it (the attention merges its split in its own launch)."""
     wl = configs.DECODE_8K
+    t0 = L.dflash_attn_sync_timeouts()
     run_rounds(wl, wl.rounds)
-    assert L.dflash_attn_sync_timeouts() == 0
+    assert L.dflash_attn_sync_timeouts() == t0
 
 
 def test_ragged_paged_16_requests():
@@ -263,6 +264,7 @@ def test_in_launch_merge_across_xcds_decode_8k(kv):
     inputs = [G.round_inputs(wl, rnd, sched[rnd]) for rnd in range(rounds)]
     refs = [orc.round(x, cu, H, wl.B)[0][0] for x, cu, H in inputs]
     outs = {}
+    t0 = L.dflash_attn_sync_timeouts()
     try:
         for spread in (False, True):
             L.dflash_attn_force_merge_spread(spread)
@@ -287,7 +289,7 @@ def test_in_launch_merge_across_xcds_decode_8k(kv):
     for rnd in range(rounds):
         e = rel_l2(outs[True][rnd], outs[False][rnd])
         assert e <= 5e-3, f"round {rnd}: the spread order differs by {e:.3e}"
-    assert L.dflash_attn_sync_timeouts() == 0
+    assert L.dflash_attn_sync_timeouts() == t0
 
 
 def test_stack5_hybrid_ring_full_shapes():
@@ -453,6 +455,7 @@ MERGE = [
 
 @pytest.mark.parametrize("wl,merged", MERGE, ids=[w.name for w, _ in MERGE])
 def test_in_launch_merge(wl, merged):
+    t0 = L.dflash_attn_sync_timeouts()
     L.timing_enable(True)
     L.timing_reset()
     try:
@@ -466,7 +469,40 @@ def test_in_launch_merge(wl, merged):
         assert t["attn_combine"][0] == 0, "the split should merge inside the attention launch"
     else:
         assert t["attn_combine"][0] > 0, "batches of several sequences keep the combine launch"
-    assert L.dflash_attn_sync_timeouts() == 0
+    assert L.dflash_attn_sync_timeouts() == t0
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_in_launch_merge_forced_timeouts(kv):
+    """The time-out path of the in-launch merge, forced from the host: with
+    the wait bound at 0 polls every work item gives up at once, writes its
+    rows as NaN (so the layer output is NaN throughout) and is counted once;
+    with the bound restored the same round matches the oracle and nothing
+    more is counted.  No wait is left running: giving up takes no poll."""
+    kw = dict(d=512, n_h=32, n_kv=8, d_h=128, B=16, prefill_len=5000, rounds=1)
+    wl = _fp8("merge_forced_timeouts", **kw) if kv == "fp8" else _small("merge_forced_timeouts", **kw)
+    kvh = prefill_host(wl)
+    x, cu, H = G.round_inputs(wl, 0, G.schedule(wl)[0])
+    keys = int(G.prefill_lengths(wl)[0]) + int(cu[1] - cu[0]) + wl.B
+    items = L.dflash_attn_plan([keys], wl.n_kv)["items"]
+    t0 = L.dflash_attn_sync_timeouts()
+    say(f"case forced time-outs {kv} items={items}")
+    try:
+        L.dflash_attn_set_spin_limit(0)
+        gm = GpuModel(wl, 1)
+        gm.prefill(kvh)
+        got = gm.round(x, cu, H)[0]
+    finally:
+        L.dflash_attn_set_spin_limit(L.ATTN_SPIN_LIMIT)
+    assert np.isnan(got).all()
+    assert L.dflash_attn_sync_timeouts() - t0 == items
+    del gm
+    gm = GpuModel(wl, 1)
+    gm.prefill(kvh)
+    got = gm.round(x, cu, H)[0]
+    ref, _ = oracle_stack(wl, kvh).round(x, cu, H, wl.B)
+    assert rel_l2(got, ref[0]) <= TOL["bf16"]
+    assert L.dflash_attn_sync_timeouts() - t0 == items
 
 
 # ------------------------------------------------------------------ fp8 (E4M3) caches
