@@ -981,12 +981,18 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_kernel(AttnArgs a) {
   }
 
   if constexpr (NG == 2) {
-    // group 1's state through LDS (the ring is free once every wave is past
-    // its last block): lane l of tile t at [t][d][l] for O, then m and l
+    // Group 1's state through LDS: lane l of tile t at [t][d][l] for O, then
+    // m and l.  The last step works on blocks b0 = 2 ((nblk - 1) / 2) and
+    // b0 + 1, in stages b0 % 4 and b0 % 4 + 1 (b0 is even); once past that
+    // step's barrier every other block is done with, so the other two
+    // stages are free.  Group 1 writes there as soon as it leaves the loop
+    // (while group 0 may still be on its last block), and one barrier
+    // hands the state to group 0.
+    static_assert(NST == 4, "the exchange uses the two stages the last step leaves free");
     constexpr int XB = DT * 1024 + 512;
-    static_assert(4 * XB <= NST * STAGE, "the merge fits the ring");
-    unsigned char* xb = ring + qt * XB;
-    __syncthreads();
+    static_assert(4 * XB <= 2 * STAGE, "the exchange fits two stages");
+    const int b0 = 2 * ((nblk - 1) / 2);
+    unsigned char* xb = ring + ((b0 & 3) == 0 ? 2 * STAGE : 0) + qt * XB;
     if (grp == 1) {
 #pragma unroll
       for (int d = 0; d < DT; ++d) *reinterpret_cast<f32x4*>(xb + d * 1024 + 16 * lane) = o[d];
