@@ -980,6 +980,7 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_kernel(AttnArgs a) {
     if (NG * i + grp < nblk) process(NG * i + grp);
   }
 
+  uint32_t pre = 0;   // a preloaded word of the partial (kept until the end)
   if constexpr (NG == 2) {
     // Group 1's state through LDS: lane l of tile t at [t][d][l] for O, then
     // m and l.  The last step works on blocks b0 = 2 ((nblk - 1) / 2) and
@@ -993,6 +994,7 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_kernel(AttnArgs a) {
     static_assert(4 * XB <= 2 * STAGE, "the exchange fits two stages");
     const int b0 = 2 * ((nblk - 1) / 2);
     unsigned char* xb = ring + ((b0 & 3) == 0 ? 2 * STAGE : 0) + qt * XB;
+    if (MERGE != 0 && grp == 1) pre = attn_partial_preload(a.part_o, a.part_ml, pitem, a.qrows, DH, tid - 256);
     if (grp == 1) {
 #pragma unroll
       for (int d = 0; d < DT; ++d) *reinterpret_cast<f32x4*>(xb + d * 1024 + 16 * lane) = o[d];
@@ -1050,6 +1052,7 @@ __global__ __launch_bounds__(256 * NG, 1) void attn_ring64_kernel(AttnArgs a) {
       store_merged_row(static_cast<bf16*>(a.attn), ov, 0, g, qr, a.B, a.group, a.n_kv, DH, lane);
     }
   }
+  asm volatile("" ::"v"(pre));
 }
 
 template <typename T>

@@ -325,12 +325,14 @@ __global__ __launch_bounds__(256 * NG, (NG == 1 && NST == 2) ? 4 : 1) void attn_
     if (NG * i + grp < nblk) process(NG * i + grp);
   }
 
+  uint32_t pre = 0;   // a preloaded word of the partial (kept until the end)
   if constexpr (NG == 2) {
     // group 1's (m, l, O) to group 0 through LDS, lane l of tile t at
     // [t][d][l] for O, then m and l; exact merge with reference maxima
     constexpr int XB = DT * 1024 + 512;
     static_assert(4 * XB <= NST * STAGE, "the merge fits the ring");
     unsigned char* xb = ring + qt * XB;
+    if (MERGE != 0 && grp == 1) pre = attn_partial_preload(a.part_o, a.part_ml, pitem, a.qrows, DH, tid - 256);
     __syncthreads();
     if (grp == 1) {
 #pragma unroll
@@ -389,6 +391,7 @@ __global__ __launch_bounds__(256 * NG, (NG == 1 && NST == 2) ? 4 : 1) void attn_
       store_merged_row(static_cast<bf16*>(a.attn), ov, 0, g, qr, a.B, a.group, a.n_kv, DH, lane);
     }
   }
+  asm volatile("" ::"v"(pre));
 }
 
 // Ring depth: the host plans for the bf16 kernel's depths (3 stages of 32 KB:

@@ -81,6 +81,25 @@ __device__ __forceinline__ void store_merged_row(T* attn, float2 o, int r, int g
   dst[1] = from_f32<T>(o.y);
 }
 
+// Lines of one item's partial (O rows, then m and l) brought into the XCD's
+// L2 before the item writes them, by one line per thread t (t < 132 for 64
+// query rows of 128 dims; others load nothing).  A store that misses the L2
+// does not leave its line there, so the other items' first reads of a freshly
+// written partial would wait on memory (a row merge 1.7 against 1.3 us with
+// the lines brought in first).  The word returned is unused; the caller keeps
+// it live until its loads may complete in the background.
+__device__ __forceinline__ uint32_t attn_partial_preload(const void* part_o, const float* part_ml, int64_t item,
+                                                         int qrows, int d_h, int t) {
+  const int olines = qrows * d_h * 2 / 128;
+  const int mlines = (qrows * 2 * 4 + 127) / 128;
+  const unsigned char* p = nullptr;
+  if (t >= 0 && t < olines)
+    p = static_cast<const unsigned char*>(part_o) + item * qrows * d_h * 2 + 128 * t;
+  else if (t >= olines && t < olines + mlines)
+    p = reinterpret_cast<const unsigned char*>(part_ml + item * 2 * qrows) + 128 * (t - olines);
+  return p != nullptr ? *reinterpret_cast<const uint32_t*>(p) : 0u;
+}
+
 // ---------------------------------------------------------------- in-launch merge: a head's arrivals
 // The items of one K/V head meet before merging the head's rows from each
 // other's partials.  Items of a head whose workgroup indices agree mod 8 sit
