@@ -120,16 +120,27 @@ def round_work(wl, L, n):
 
 # ---------------------------------------------------------------------------- HBM traffic record
 
+ATTN_SOURCES = ("attention.hip", "attn_merge.hpp")
+
+
+def attention_source_sha256():
+    """SHA-256 over the bf16 attention kernel's sources (the kernel file and
+    the merge helpers it includes), in that order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        h.update(open(os.path.join(ROOT, "block_diffusion_draft_fc_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
 def traffic_record():
     """Measured HBM bytes per attention launch (rocprofv3 FETCH_SIZE + WRITE_SIZE,
     scaled by a plain copy's reading), from the record kept with the profiles -
     or None when the attention kernel's source has changed since it was taken."""
-    import hashlib
     rec_path = os.path.join(ROOT, "profiles", "attn_decode_ctx8k_traffic.json")
-    src_path = os.path.join(ROOT, "block_diffusion_draft_fc_amd", "csrc", "attention.hip")
     try:
         rec = json.load(open(rec_path))
-        sha = hashlib.sha256(open(src_path, "rb").read()).hexdigest()
+        sha = attention_source_sha256()
     except (OSError, ValueError):
         return None
     if rec.get("attention_source_sha256") != sha:
@@ -702,7 +713,6 @@ def summarize_profiles(root):
     is scaled by what it reads for a plain 256 MiB copy (262144 KiB each way)."""
     import csv
     import glob
-    import hashlib
 
     def rows(pattern):
         f = sorted(glob.glob(os.path.join(root, pattern)))
@@ -774,9 +784,9 @@ def summarize_profiles(root):
                   f"{fetch / 1e6:.2f} MB read + {write / 1e6:.2f} MB written = {(fetch + write) / 1e6:.2f} MB of "
                   f"HBM traffic."]
     open(os.path.join(ROOT, "profiles", "attn_decode_ctx8k_hbm_counters.md"), "w").write("\n".join(lines) + "\n")
-    src = os.path.join(ROOT, "block_diffusion_draft_fc_amd", "csrc", "attention.hip")
     rec = {"kernels": list(ATTN_KERNELS), "workload": "decode_ctx8k_d4096_gqa32x8_dh128_block16_bf16",
-           "attention_source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+           "attention_sources": ["block_diffusion_draft_fc_amd/csrc/" + f for f in ATTN_SOURCES],
+           "attention_source_sha256": attention_source_sha256(),
            "fetch_bytes_per_launch": int(fetch), "write_bytes_per_launch": int(write),
            "fetch_scale": round(scale["FETCH_SIZE"], 4), "write_scale": round(scale["WRITE_SIZE"], 4),
            "source": "profiles/attn_decode_ctx8k_hbm_counters.md",
