@@ -328,12 +328,19 @@ __global__ __launch_bounds__(256 * NG, (NG == 1 && NST == 2) ? 4 : 1) void attn_
   uint32_t pre = 0;   // a preloaded word of the partial (kept until the end)
   if constexpr (NG == 2) {
     // group 1's (m, l, O) to group 0 through LDS, lane l of tile t at
-    // [t][d][l] for O, then m and l; exact merge with reference maxima
+    // [t][d][l] for O, then m and l; exact merge with reference maxima.
+    // The last step works on blocks b0 = 2 ((nblk - 1) / 2) and b0 + 1, in
+    // the stage pair (b0 % 6) / 2 (b0 is even); once past that step's
+    // barrier the other two pairs are free.  Query tiles 0-1 use one of them
+    // and 2-3 the other, so group 1 writes as soon as it leaves the loop
+    // and one barrier hands the state to group 0.
+    static_assert(NST == 6, "the exchange uses the two stage pairs the last step leaves free");
     constexpr int XB = DT * 1024 + 512;
-    static_assert(4 * XB <= NST * STAGE, "the merge fits the ring");
-    unsigned char* xb = ring + qt * XB;
+    static_assert(2 * XB <= 2 * STAGE, "two query tiles fit a stage pair");
+    const int busy = (2 * ((nblk - 1) / 2) % 6) / 2;
+    const int pair = (busy + (qt < 2 ? 1 : 2)) % 3;
+    unsigned char* xb = ring + pair * 2 * STAGE + (qt & 1) * XB;
     if (MERGE != 0 && grp == 1) pre = attn_partial_preload(a.part_o, a.part_ml, pitem, a.qrows, DH, tid - 256);
-    __syncthreads();
     if (grp == 1) {
 #pragma unroll
       for (int d = 0; d < DT; ++d) *reinterpret_cast<f32x4*>(xb + d * 1024 + 16 * lane) = o[d];
